@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Paged-attention decode benchmark on one MI355X.
+
+One step = one decode layer of the Llama-7B-shaped workload (B = 32 sequences, 32 query
+heads = 32 kv heads, head_dim 128, block_size 16, bf16, kv lengths U{512..2048} before
+the step, physical blocks shuffled in a pool of total need + 10 %):
+    slot_mapping -> cache write of the new K/V rows -> split-KV attention -> combine,
+all through the C ABI of libpagedkv.so on torch's current stream, with every input
+already resident in HBM.  Several copies of the K/V pool are rotated so that each step
+reads a pool that left the 256 MB Infinity Cache long ago.
+
+Prints one JSON line: KV-read GB/s (value), µs per step, the roofline of the dominant
+kernel (the split-KV attention pass, timed with HIP events around its launch on the
+same stream) and the fp64 CPU oracle timed on this host as a baseline.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--seed S]
+  python bench.py --calibrate-copy MIB     # plain copy of known size, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged-decode KV-read HBM GB/s (% of peak) + µs/step, Llama-7B-shape B=32, 1 GPU"
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E, vendor figure
+DOMINANT_KERNEL = "decode_split_kernel"
+KERNEL_SOURCES = ["paged_kv_cache_133_amd/csrc/decode.hip", "paged_kv_cache_133_amd/csrc/pkv_device.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama7b_mha_bf16")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--replicas", type=int, default=0, help="K/V pool copies rotated (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=5.0,
+                    help="minimum wall time of the CPU-oracle sample")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="omit the per-kernel HIP events inside the timed region")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (for counter scaling)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary,
+    or None if the summary is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{DOMINANT_KERNEL}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def algorithmic_bytes(case):
+    """(kv_read, split_kernel, step) algorithmic bytes of one step."""
+    w = case.w
+    e = w.elem_bytes
+    Lp = case.lens_after.astype("int64")
+    B, T = w.batch, case.num_tokens
+    if w.mode == "mla":
+        row = w.head_dim + w.head_dim_rope          # nope read once (key and value) + rope
+        new_rows = T * (w.head_dim + w.head_dim_rope) * e
+    else:
+        row = w.num_kv_heads * (w.head_dim + w.head_dim_v)
+        new_rows = T * w.num_kv_heads * (w.head_dim + w.head_dim_v) * e
+    kv = int(Lp.sum()) * row * e
+    q_bytes = T * w.num_q_heads * (w.head_dim + w.head_dim_rope) * e
+    out_bytes = T * w.num_q_heads * w.head_dim_v * e
+    table = 4 * int((-(-Lp // w.block_size)).sum())
+    split = kv + q_bytes + out_bytes + table + 4 * B
+    # slot_mapping: table entry, L_b, cu; slot written; write: new rows read + written
+    step = split + 2 * new_rows + 4 * B * 3 + 8 * T
+    return kv, split, step
+
+
+def calibrate_copy(mib: int):
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
+
+
+def cpu_baseline(case, kv_bytes, min_seconds):
+    """The fp64 oracle on this host: the whole step (slot_mapping, writes, attention) on
+    host copies of the same inputs, repeated until min_seconds of wall time."""
+    from oracle import oracle
+    from paged_kv_cache_133_amd import workloads as wl  # noqa: F401
+    import numpy as np
+    import torch
+
+    def host(t):
+        if t is None:
+            return None
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    c = case
+    h = {"block_table": c.block_table, "lens_before": c.lens_before, "cu_q": c.cu_q,
+         "lens_after": c.lens_after, "cache_k": host(c.cache_k), "cache_v": host(c.cache_v),
+         "cache_rope": host(c.cache_rope), "q": host(c.q), "q_rope": host(c.q_rope),
+         "new_k": host(c.new_k), "new_v": host(c.new_v), "new_rope": host(c.new_rope),
+         "block_size": c.w.block_size, "num_blocks": c.num_blocks, "scale": c.w.scale}
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.decode_step(h, causal=(c.w.mode == "varlen"))
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= min_seconds and len(times) >= 3:
+            break
+    med = statistics.median(times)
+    return {"value": round(kv_bytes / med / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": (f"whole {c.w.name} step (slot_mapping, K/V writes, fp64 attention over "
+                       f"all {c.w.batch} sequences), median of {len(times)} runs, "
+                       f"{med * 1e3:.1f} ms/step")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import paged_kv_cache_133_amd as pkv
+    from paged_kv_cache_133_amd import _lib
+    from paged_kv_cache_133_amd import workloads as wl
+
+    pkv.lib()   # fails loudly if the HIP library is missing
+    w = wl.WORKLOADS[args.workload]
+    if w.mode == "varlen":
+        print("bench.py times the decode workloads", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    case = wl.make_workload_case(w, seed=args.seed, device=dev)
+    kv_bytes, split_bytes, step_bytes = algorithmic_bytes(case)
+    pool_bytes = sum(t.numel() * t.element_size()
+                     for t in {id(x): x for x in (case.cache_k, case.cache_v, case.cache_rope)
+                               if x is not None}.values())
+    R = args.replicas or max(2, min(64, math.ceil(2.0e9 / pool_bytes)))
+    mla = w.mode == "mla"
+
+    table = case.table_tensor(dev)
+    lb = case.lens_before_tensor(dev)
+    la = case.lens_after_tensor(dev)
+    cu = case.cu_q_tensor(dev)
+    T = case.num_tokens
+    slots = torch.empty(T, dtype=torch.int64, device=dev)
+    out = torch.empty((T, w.num_q_heads, w.head_dim_v), dtype=w.torch_dtype, device=dev)
+    lse = torch.empty((T, w.num_q_heads), dtype=torch.float32, device=dev)
+    need = pkv.decode_workspace_size(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim_v,
+                                     case.max_len_after)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    slot_call = _lib.prepare_slot_mapping(table, lb, cu, w.block_size, T, slots)
+    reps = []
+    for r in range(R):
+        k = case.cache_k if r == 0 else case.cache_k.clone()
+        rope = None
+        if mla:
+            v = k
+            rope = case.cache_rope if r == 0 else case.cache_rope.clone()
+            write = _lib.prepare_kv_cache_write(case.new_k, case.new_rope, k, rope, slots)
+        else:
+            v = case.cache_v if r == 0 else case.cache_v.clone()
+            write = _lib.prepare_kv_cache_write(case.new_k, case.new_v, k, v, slots)
+        split, combine, _, _ = _lib.prepare_decode(case.q, k, v, table, la, case.max_len_after,
+                                                   w.scale, q_rope=case.q_rope, k_rope_cache=rope,
+                                                   out=out, lse=lse, workspace=ws)
+        reps.append((write, split, combine))
+    torch.cuda.synchronize()
+
+    events = not args.no_kernel_events
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)] if events else None
+
+    def step(i, timed):
+        write, split, combine = reps[i % R]
+        slot_call()
+        write()
+        if timed and events:
+            ev[i][0].record()
+        split()
+        if timed and events:
+            ev[i][1].record()
+        combine()
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        step(i, True)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    us_step = ms_step * 1e3
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+
+    roofline = None
+    if events:
+        durs = [a.elapsed_time(b) for a, b in ev]
+        split_ms = statistics.mean(durs)
+        achieved = split_bytes / (split_ms * 1e-3) / 1e9
+        traffic = read_traffic(w.name)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                    "traffic": traffic, "kernel": DOMINANT_KERNEL,
+                    "kernel_us": round(split_ms * 1e3, 2),
+                    "algorithmic_bytes_per_launch": split_bytes}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, kv_bytes, args.cpu_seconds)
+
+    cfg = {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
+           "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "head_dim_v": w.head_dim_v,
+           "head_dim_rope": w.head_dim_rope, "block_size": w.block_size,
+           "num_blocks": case.num_blocks, "seed": args.seed,
+           "kv_tokens": int(case.lens_after.sum()), "max_kv_len": case.max_len_after,
+           "pool_replicas": R, "step": "slot_mapping + kv_cache_write + decode split + combine"}
+    line = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": w.dtype, "data": "synthetic", "config": cfg,
+            "us_per_step": round(us_step, 2),
+            "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBPS, 2),
+            "algorithmic_bytes_per_step": step_bytes, "kv_read_bytes_per_step": kv_bytes,
+            "roofline": roofline, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,216 @@
+/*
+ * pagedkv.h — C ABI of libpagedkv.so: paged KV-cache write and block-table
+ * attention decode for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  - Every pointer is a DEVICE pointer (memory on the current HIP device) unless it is
+ *    marked [host].  Tensors are dense, row-major and contiguous in the shapes given.
+ *  - The caller owns every buffer: caches, tables, queries, outputs and workspace.
+ *    The library allocates nothing, keeps no state besides a thread-local error
+ *    string, never synchronises, and enqueues work only on `stream` (a hipStream_t;
+ *    NULL is the default stream).  The call returns once the work is enqueued.
+ *  - Arguments are checked on the host before anything is enqueued.  A non-zero
+ *    return is one of the PKV_ERR_* codes; nothing was enqueued then, and
+ *    pkv_last_error() describes the problem.  PKV_ERR_HIP reports a launch failure.
+ *  - Every argument is required: no size, count or scale has a default (the pages
+ *    warn that a misnamed attention argument silently falls back to scale 1.0 or one
+ *    head: "KVCache Optimization Skill", Appendix A, parameter-name table).
+ *  - Device-side preconditions that the host cannot check without reading device
+ *    memory are listed per call.  The kernels clamp every index they derive from
+ *    device data into its buffer, so a violated precondition gives unspecified
+ *    values, never an out-of-bounds access.
+ *
+ * Cache layout ("KVCache Optimization Skill", Layer 3, 3.1; ai6s.net KVCache article,
+ * section 4.1, ND branch; hotelren.com "Paged KV Cache and Packed Sequence", 2.1):
+ *     cache[num_blocks][block_size][num_kv_heads][head_dim]
+ * The flat row index of (physical block P, offset o) is the slot P * block_size + o;
+ * logical position p of sequence b lives in slot
+ *     block_table[b][p / block_size] * block_size + p % block_size.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef PKV_API
+#define PKV_API __attribute__((visibility("default")))
+#endif
+
+/* Return codes. */
+enum {
+    PKV_OK = 0,
+    PKV_ERR_NULL = -1,         /* a required pointer is NULL */
+    PKV_ERR_SHAPE = -2,        /* a size or count is negative or inconsistent */
+    PKV_ERR_DTYPE = -3,        /* unknown dtype code */
+    PKV_ERR_UNSUPPORTED = -4,  /* a valid combination this library does not implement */
+    PKV_ERR_ALIGN = -5,        /* a pointer is not 16-byte aligned */
+    PKV_ERR_SCALE = -6,        /* softmax_scale is NaN, infinite or <= 0 */
+    PKV_ERR_WORKSPACE = -7,    /* workspace NULL or smaller than required */
+    PKV_ERR_HIP = -8           /* the HIP runtime reported an error at launch */
+};
+
+/* Element types of caches, queries and outputs. */
+enum { PKV_F32 = 0, PKV_BF16 = 1 };
+
+/* Library version (major * 100 + minor). */
+PKV_API int pkv_version(void);
+
+/* Text describing the last non-OK status returned on the calling thread. */
+PKV_API const char* pkv_last_error(void);
+
+/*
+ * slot_mapping for one step: sequence b already holds lens_before[b] tokens and appends
+ * n_b = cu_new[b+1] - cu_new[b] tokens, packed in order.  Token t of sequence b is at
+ * logical position lens_before[b] + (t - cu_new[b]) and gets
+ *     slot_mapping[t] = block_table[b][pos / block_size] * block_size + pos % block_size.
+ * ("KVCache Optimization Skill", Layer 3, 3.1 mapping formula and 3.3 slot_mapping
+ * construction, of which the sequential form b * max_seq_len + pos is the special case
+ * of the identity table; "Paged KV Cache and Packed Sequence", 2.2, index snippet.)
+ *
+ *   slot_mapping  [num_tokens] int64, written
+ *   block_table   [batch][max_blocks_per_seq] int32
+ *   lens_before   [batch] int32
+ *   cu_new        [batch + 1] int32, cu_new[0] = 0, non-decreasing, cu_new[batch] = num_tokens
+ *   block_size    power of two in [1, 256]
+ * Device preconditions: each position's logical block < max_blocks_per_seq (else the
+ * slot is written as -1, which pkv_kv_cache_write skips).
+ */
+PKV_API int pkv_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
+                     const int32_t* lens_before, const int32_t* cu_new,
+                     int32_t batch, int64_t num_tokens, int32_t max_blocks_per_seq,
+                     int32_t block_size, void* stream);
+
+/*
+ * Cache write by slot_mapping: for each token t,
+ *     k_cache.view(num_blocks * block_size, num_kv_heads, head_dim_k)[slot_mapping[t]] = k_new[t]
+ *     v_cache.view(num_blocks * block_size, num_kv_heads, head_dim_v)[slot_mapping[t]] = v_new[t]
+ * A byte copy with no conversion ("KVCache Optimization Skill", Mode 2 step 3 and the
+ * division of labour after 3.3: slot_mapping drives writes, block_table drives reads;
+ * ai6s.net article, 4.2, cache write loop).
+ *
+ *   k_new [num_tokens][num_kv_heads][head_dim_k], v_new [num_tokens][num_kv_heads][head_dim_v]
+ *   k_cache [num_blocks][block_size][num_kv_heads][head_dim_k], v_cache likewise with head_dim_v
+ *   slot_mapping [num_tokens] int64
+ * For the MLA latent cache pass (kv_nope, k_rope, cache_nope, cache_rope) with
+ * num_kv_heads = 1, head_dim_k = 512, head_dim_v = 64: the two caches share slots.
+ * num_tokens = 0 enqueues nothing.
+ * Device preconditions: slots in [0, num_blocks * block_size) and distinct within one
+ * call (a slot outside the range is skipped; duplicated slots leave either row).
+ */
+PKV_API int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                       const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                       int32_t head_dim_k, int32_t head_dim_v, int32_t block_size,
+                       int64_t num_blocks, int32_t dtype, void* stream);
+
+/*
+ * Bytes of workspace pkv_paged_attn_decode needs for these sizes (0 if none).  The
+ * workspace holds split-KV partial results; its contents need no initialisation.
+ */
+PKV_API size_t pkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim_v, int32_t max_seq_len_kv);
+
+/*
+ * Paged-attention decode: one query row per sequence and head attends to all
+ * seq_lens_kv[b] cached tokens of its sequence, read through block_table
+ * ("KVCache Optimization Skill", Mode 2 step 4, 3.6 data flow — the decode reads
+ * kv_len + 1 tokens, the token just written included — and Appendix E, decode uses no
+ * mask; Mode 3 for MLA; "Paged KV Cache and Packed Sequence", 3.3 and 4.2).
+ *
+ *   out [batch][num_q_heads][head_dim_v], same dtype as q, written
+ *   lse_out [batch][num_q_heads] fp32 natural-log sum-exp of the scaled scores, or NULL
+ *   q [batch][num_q_heads][head_dim_qk]
+ *   q_rope [batch][num_q_heads][head_dim_rope] or NULL
+ *   k_cache [num_blocks][block_size][num_kv_heads][head_dim_qk]
+ *   v_cache [num_blocks][block_size][num_kv_heads][head_dim_v]  (MLA: the same pointer
+ *           as k_cache — value = cache_nope)
+ *   k_rope_cache [num_blocks][block_size][num_kv_heads][head_dim_rope] or NULL; given
+ *           exactly when q_rope is (skill page, Mode 3 constraints)
+ *   block_table [batch][max_blocks_per_seq] int32; seq_lens_kv [batch] int32 (= L'_b)
+ *   max_seq_len_kv [host] an upper bound of seq_lens_kv, <= max_blocks_per_seq * block_size
+ *   softmax_scale [host] > 0 (e.g. 1/sqrt(head_dim); MLA 1/sqrt(512 + 64))
+ *   workspace: at least pkv_decode_workspace_size(...) bytes, 16-byte aligned (may be
+ *           NULL when that size is 0)
+ * score(h, p) = softmax_scale * (q[h] . K_p + q_rope[h] . Krope_p) with K/V of kv head
+ * h / (num_q_heads / num_kv_heads); out[h] = sum_p softmax(score)_p * V_p.
+ * Supported: MHA/GQA with head_dim_qk = head_dim_v in {64, 128}, 1 <= q heads per kv
+ * head <= 16, f32 or bf16; MLA with num_kv_heads = 1, head_dim_qk = head_dim_v = 512,
+ * head_dim_rope = 64, bf16, num_q_heads a multiple of 16.  block_size a power of two in
+ * [1, 256].  Accumulation is fp32; out is rounded once to its dtype.
+ * Device preconditions: 1 <= seq_lens_kv[b] <= max_seq_len_kv; block_table entries for
+ * the logical blocks in use lie in [0, num_blocks); entries past them are never read.
+ */
+PKV_API int pkv_paged_attn_decode(void* out, float* lse_out, const void* q, const void* q_rope,
+                          const void* k_cache, const void* v_cache, const void* k_rope_cache,
+                          const int32_t* block_table, const int32_t* seq_lens_kv,
+                          int32_t batch, int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim_qk,
+                          int32_t head_dim_v, int32_t head_dim_rope, int32_t block_size,
+                          int64_t num_blocks, float softmax_scale, int32_t dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two launches pkv_paged_attn_decode makes, exposed separately (same arguments, same
+ * checks) so a caller can time or schedule them on their own.  _split runs the split-KV
+ * pass: rows of sequences that fit one split are finished in `out`/`lse_out`, the others
+ * leave partial softmax states (max, sum, unnormalised output per split) in `workspace`.
+ * _combine then merges those states (out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s,
+ * lse = M + log of that sum, M = max_s m_s) and enqueues nothing when no row was split.
+ * Calling _split then _combine on one stream equals pkv_paged_attn_decode.
+ */
+PKV_API int pkv_paged_attn_decode_split(void* out, float* lse_out, const void* q, const void* q_rope,
+                                const void* k_cache, const void* v_cache,
+                                const void* k_rope_cache, const int32_t* block_table,
+                                const int32_t* seq_lens_kv, int32_t batch,
+                                int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim_qk,
+                                int32_t head_dim_v, int32_t head_dim_rope, int32_t block_size,
+                                int64_t num_blocks, float softmax_scale, int32_t dtype,
+                                void* workspace, size_t workspace_bytes, void* stream);
+PKV_API int pkv_paged_attn_decode_combine(void* out, float* lse_out, const void* q, const void* q_rope,
+                                  const void* k_cache, const void* v_cache,
+                                  const void* k_rope_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens_kv, int32_t batch,
+                                  int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim_qk, int32_t head_dim_v,
+                                  int32_t head_dim_rope, int32_t block_size, int64_t num_blocks,
+                                  float softmax_scale, int32_t dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
+ * Packed varlen attention over the paged cache: sequence b owns query rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) of the packed stream (n_b rows) and
+ * seq_lens_kv[b] = L'_b cached tokens, its own new rows included (they were written
+ * with pkv_kv_cache_write first).  With causal != 0, row i of sequence b sees keys
+ * p <= L'_b - n_b + i (bottom-right causal, the query's own token included); with
+ * causal = 0 it sees all L'_b keys.  Queries of different sequences never see each
+ * other ("Paged KV Cache and Packed Sequence", 3.1-3.3 and 4.1; "KVCache Optimization
+ * Skill", Appendix C, sparse_mode 3, and Appendix E).
+ *
+ *   out [total_q][num_q_heads][head_dim], q [total_q][num_q_heads][head_dim]
+ *   lse_out [total_q][num_q_heads] fp32 or NULL
+ *   cu_seqlens_q [batch + 1] int32 (cu_seqlens_q[0] = 0); seq_lens_kv [batch] int32
+ *   max_seqlen_q [host] >= every n_b
+ * Supported: head_dim in {64, 128}, 1 <= q heads per kv head <= 16, bf16;
+ * block_size a power of two in [16, 256].
+ * Device preconditions: n_b <= seq_lens_kv[b]; table entries as for decode.
+ */
+PKV_API int pkv_paged_attn_varlen(void* out, float* lse_out, const void* q,
+                          const int32_t* cu_seqlens_q, const int32_t* seq_lens_kv,
+                          const void* k_cache, const void* v_cache, const int32_t* block_table,
+                          int32_t batch, int64_t total_q, int32_t max_seqlen_q,
+                          int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                          float softmax_scale, int32_t causal, int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

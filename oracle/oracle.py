@@ -58,6 +58,8 @@ def lib():
                 build(force=True)
             L = ctypes.CDLL(LIB)
         p, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.orc_max_threads.restype = ctypes.c_int
+        L.orc_max_threads.argtypes = []
         L.orc_slot_of.restype = i64
         L.orc_slot_of.argtypes = [p, i32, i32, i64, i32, i64]
         L.orc_slot_mapping.argtypes = [p, i32, i32, p, p, i32, i64, p]
@@ -92,6 +94,11 @@ def _storage(a: np.ndarray) -> tuple[np.ndarray, int]:
     if a.dtype in (np.uint16, np.int16):
         return a.view(np.uint16), BF16
     raise TypeError(f"oracle takes float32 or bf16-as-uint16 arrays, got {a.dtype}")
+
+
+def max_threads() -> int:
+    """Threads the oracle's parallel loop uses."""
+    return int(lib().orc_max_threads())
 
 
 # --------------------------------------------------------------------------- index map

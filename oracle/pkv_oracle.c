@@ -49,6 +49,15 @@
 
 int orc_version(void) { return 1; }
 
+/* Threads an OpenMP region of the oracle will use (1 without OpenMP). */
+int orc_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 /* One element of a stored tensor, widened exactly to double. */
 static double load_elem(const void* base, int64_t idx, int dtype) {
     if (dtype == ORC_F32) {

@@ -1,5 +1,8 @@
 """MI355X-native paged KV cache: slot_mapping write and block-table attention decode.
 
 The compute lives in the HIP library libpagedkv.so (built by
-paged_kv_cache_133_amd.build); this package only marshals torch tensors to its C ABI.
+`python -m paged_kv_cache_133_amd.build`); this package only marshals torch tensors
+to its C ABI (include/pagedkv.h).  Calls raise if the library is missing.
 """
+from ._lib import (PagedKVError, decode_workspace_size, kv_cache_write, lib,  # noqa: F401
+                   paged_attn_decode, paged_attn_varlen, slot_mapping, version)

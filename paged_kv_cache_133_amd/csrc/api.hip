@@ -1,0 +1,288 @@
+// C-ABI front end of libpagedkv.so: host-side argument checks, then one or two kernel
+// launches on the caller's stream.  No allocation, no synchronisation, no state except
+// the thread-local text of the last error.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/pagedkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return PKV_OK;
+    return fail(PKV_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool pow2_in(int32_t v, int32_t lo, int32_t hi) {
+    return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+int log2i(int32_t v) {
+    int r = 0;
+    while ((1 << r) < v) ++r;
+    return r;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+int pkv_version(void) { return 100; }
+
+const char* pkv_last_error(void) { return g_err; }
+
+int pkv_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
+                     const int32_t* lens_before, const int32_t* cu_new, int32_t batch,
+                     int64_t num_tokens, int32_t max_blocks_per_seq, int32_t block_size,
+                     void* stream) {
+    if (batch < 0 || num_tokens < 0) return fail(PKV_ERR_SHAPE, "slot_mapping: negative batch or num_tokens");
+    if (max_blocks_per_seq <= 0) return fail(PKV_ERR_SHAPE, "slot_mapping: max_blocks_per_seq must be > 0");
+    if (!pow2_in(block_size, 1, 256))
+        return fail(PKV_ERR_UNSUPPORTED, "slot_mapping: block_size %d is not a power of two in [1, 256]", block_size);
+    if (batch == 0 || num_tokens == 0) return PKV_OK;
+    if (!slot_mapping || !block_table || !lens_before || !cu_new)
+        return fail(PKV_ERR_NULL, "slot_mapping: NULL pointer argument");
+    pkv::SlotParams p{slot_mapping, block_table, lens_before, cu_new, num_tokens, batch,
+                      max_blocks_per_seq, log2i(block_size)};
+    return hip_status(pkv::launch_slot_mapping(p, (hipStream_t)stream), "slot_mapping launch");
+}
+
+int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                       const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                       int32_t head_dim_k, int32_t head_dim_v, int32_t block_size,
+                       int64_t num_blocks, int32_t dtype, void* stream) {
+    if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "kv_cache_write: unknown dtype %d", dtype);
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim_k <= 0 || head_dim_v <= 0 || num_blocks <= 0)
+        return fail(PKV_ERR_SHAPE, "kv_cache_write: sizes must be positive (num_tokens >= 0)");
+    if (!pow2_in(block_size, 1, 256))
+        return fail(PKV_ERR_UNSUPPORTED, "kv_cache_write: block_size %d is not a power of two in [1, 256]", block_size);
+    if (num_tokens > 0x7fffffffLL) return fail(PKV_ERR_SHAPE, "kv_cache_write: num_tokens too large");
+    if (num_tokens == 0) return PKV_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping)
+        return fail(PKV_ERR_NULL, "kv_cache_write: NULL pointer argument");
+    if (k_cache == v_cache) return fail(PKV_ERR_SHAPE, "kv_cache_write: k_cache and v_cache must differ");
+    const int eb = elem_bytes(dtype);
+    pkv::WriteParams p{};
+    p.src[0] = static_cast<const uint8_t*>(k_new);
+    p.src[1] = static_cast<const uint8_t*>(v_new);
+    p.dst[0] = static_cast<uint8_t*>(k_cache);
+    p.dst[1] = static_cast<uint8_t*>(v_cache);
+    p.row_bytes[0] = (int64_t)num_kv_heads * head_dim_k * eb;
+    p.row_bytes[1] = (int64_t)num_kv_heads * head_dim_v * eb;
+    p.slots = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.num_slots = num_blocks * block_size;
+    for (int i = 0; i < 2; ++i) {
+        if ((reinterpret_cast<uintptr_t>(p.src[i]) | reinterpret_cast<uintptr_t>(p.dst[i])) % eb)
+            return fail(PKV_ERR_ALIGN, "kv_cache_write: pointers must be aligned to the element size");
+    }
+    return hip_status(pkv::launch_kv_write(p, (hipStream_t)stream), "kv_cache_write launch");
+}
+
+size_t pkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim_v, int32_t max_seq_len_kv) {
+    if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim_v <= 0 ||
+        max_seq_len_kv <= 0 || num_q_heads % num_kv_heads)
+        return 0;
+    return pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim_v, max_seq_len_kv).ws_bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Host-side checks shared by the decode entry points; fills the kernel parameters.
+int prepare_decode(pkv::DecodeParams& p, pkv::DecodePlan& plan, void* out, float* lse_out,
+                   const void* q, const void* q_rope, const void* k_cache, const void* v_cache,
+                   const void* k_rope_cache, const int32_t* block_table,
+                   const int32_t* seq_lens_kv, int32_t batch, int32_t max_blocks_per_seq,
+                   int32_t max_seq_len_kv, int32_t num_q_heads, int32_t num_kv_heads,
+                   int32_t head_dim_qk, int32_t head_dim_v, int32_t head_dim_rope,
+                   int32_t block_size, int64_t num_blocks, float softmax_scale, int32_t dtype,
+                   void* workspace, size_t workspace_bytes, bool* nothing_to_do) {
+    *nothing_to_do = false;
+    if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "decode: unknown dtype %d", dtype);
+    if (batch < 0) return fail(PKV_ERR_SHAPE, "decode: negative batch");
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+        return fail(PKV_ERR_SHAPE, "decode: num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                    num_q_heads, num_kv_heads);
+    if (head_dim_qk <= 0 || head_dim_v <= 0 || head_dim_rope < 0 || max_blocks_per_seq <= 0 ||
+        num_blocks <= 0)
+        return fail(PKV_ERR_SHAPE, "decode: head dims, max_blocks_per_seq and num_blocks must be positive");
+    if (!pow2_in(block_size, 1, 256))
+        return fail(PKV_ERR_UNSUPPORTED, "decode: block_size %d is not a power of two in [1, 256]", block_size);
+    if ((int64_t)max_seq_len_kv > (int64_t)max_blocks_per_seq * block_size || max_seq_len_kv <= 0)
+        return fail(PKV_ERR_SHAPE, "decode: max_seq_len_kv %d must be in [1, max_blocks_per_seq * block_size]",
+                    max_seq_len_kv);
+    if (!isfinite(softmax_scale) || !(softmax_scale > 0.0f))
+        return fail(PKV_ERR_SCALE, "decode: softmax_scale must be finite and > 0");
+    if ((q_rope == nullptr) != (k_rope_cache == nullptr))
+        return fail(PKV_ERR_NULL, "decode: q_rope and k_rope_cache must be given together or not at all");
+    const bool mla = q_rope != nullptr;
+    if (!mla && head_dim_rope != 0)
+        return fail(PKV_ERR_SHAPE, "decode: head_dim_rope must be 0 without rope inputs");
+    if (mla) {
+        return fail(PKV_ERR_UNSUPPORTED, "decode: the MLA (rope) path is not built yet");
+    }
+    const int group = num_q_heads / num_kv_heads;
+    if (head_dim_qk != head_dim_v || (head_dim_qk != 64 && head_dim_qk != 128))
+        return fail(PKV_ERR_UNSUPPORTED, "decode: head_dim %d/%d not supported (64 or 128, equal)",
+                    head_dim_qk, head_dim_v);
+    if (group > 16)
+        return fail(PKV_ERR_UNSUPPORTED, "decode: %d query heads per kv head (max 16)", group);
+    if (batch == 0) {
+        *nothing_to_do = true;
+        return PKV_OK;
+    }
+    if (!out || !q || !k_cache || !v_cache || !block_table || !seq_lens_kv)
+        return fail(PKV_ERR_NULL, "decode: NULL pointer argument");
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PKV_ERR_ALIGN, "decode: out, q and caches must be 16-byte aligned");
+    plan = pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim_v, max_seq_len_kv);
+    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))
+        return fail(PKV_ERR_WORKSPACE, "decode: workspace needs %zu bytes (16-byte aligned), got %zu",
+                    plan.ws_bytes, workspace ? workspace_bytes : (size_t)0);
+    if ((int64_t)num_kv_heads * batch * plan.max_splits > 0x7fffffffLL)
+        return fail(PKV_ERR_SHAPE, "decode: grid too large");
+
+    p = pkv::DecodeParams{};
+    p.out = out;
+    p.lse = lse_out;
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.table = block_table;
+    p.seq_lens = seq_lens_kv;
+    p.ws_o = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
+    p.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + plan.ws_ml_offset)
+                            : nullptr;
+    p.batch = batch;
+    p.mbs = max_blocks_per_seq;
+    p.hq = num_q_heads;
+    p.hkv = num_kv_heads;
+    p.group = group;
+    p.bs_log2 = log2i(block_size);
+    p.split_tokens = plan.split_tokens;
+    p.max_splits = plan.max_splits;
+    p.len_cap = max_seq_len_kv;
+    p.num_blocks = num_blocks;
+    p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+    return PKV_OK;
+}
+
+int launch_combine_for(const pkv::DecodeParams& p, int32_t head_dim_v, int32_t dtype,
+                       hipStream_t s) {
+    pkv::CombineParams c{};
+    c.out = p.out;
+    c.lse = p.lse;
+    c.ws_o = p.ws_o;
+    c.ws_ml = p.ws_ml;
+    c.seq_lens = p.seq_lens;
+    c.batch = p.batch;
+    c.hq = p.hq;
+    c.dim = head_dim_v;
+    c.split_tokens = p.split_tokens;
+    c.max_splits = p.max_splits;
+    c.len_cap = p.len_cap;
+    return hip_status(pkv::launch_combine(c, dtype, s), "decode combine launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+#define PKV_DECODE_ARGS                                                                    \
+    out, lse_out, q, q_rope, k_cache, v_cache, k_rope_cache, block_table, seq_lens_kv, batch, \
+        max_blocks_per_seq, max_seq_len_kv, num_q_heads, num_kv_heads, head_dim_qk,           \
+        head_dim_v, head_dim_rope, block_size, num_blocks, softmax_scale, dtype, workspace,   \
+        workspace_bytes
+
+int pkv_paged_attn_decode(void* out, float* lse_out, const void* q, const void* q_rope,
+                          const void* k_cache, const void* v_cache, const void* k_rope_cache,
+                          const int32_t* block_table, const int32_t* seq_lens_kv,
+                          int32_t batch, int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim_qk,
+                          int32_t head_dim_v, int32_t head_dim_rope, int32_t block_size,
+                          int64_t num_blocks, float softmax_scale, int32_t dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    pkv::DecodeParams p;
+    pkv::DecodePlan plan{};
+    bool idle = false;
+    int rc = prepare_decode(p, plan, PKV_DECODE_ARGS, &idle);
+    if (rc != PKV_OK || idle) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    rc = hip_status(pkv::launch_decode(p, dtype, head_dim_qk, s), "decode split launch");
+    if (rc != PKV_OK || plan.max_splits <= 1) return rc;
+    return launch_combine_for(p, head_dim_v, dtype, s);
+}
+
+int pkv_paged_attn_decode_split(void* out, float* lse_out, const void* q, const void* q_rope,
+                                const void* k_cache, const void* v_cache,
+                                const void* k_rope_cache, const int32_t* block_table,
+                                const int32_t* seq_lens_kv, int32_t batch,
+                                int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim_qk,
+                                int32_t head_dim_v, int32_t head_dim_rope, int32_t block_size,
+                                int64_t num_blocks, float softmax_scale, int32_t dtype,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    pkv::DecodeParams p;
+    pkv::DecodePlan plan{};
+    bool idle = false;
+    int rc = prepare_decode(p, plan, PKV_DECODE_ARGS, &idle);
+    if (rc != PKV_OK || idle) return rc;
+    return hip_status(pkv::launch_decode(p, dtype, head_dim_qk, (hipStream_t)stream),
+                      "decode split launch");
+}
+
+int pkv_paged_attn_decode_combine(void* out, float* lse_out, const void* q, const void* q_rope,
+                                  const void* k_cache, const void* v_cache,
+                                  const void* k_rope_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens_kv, int32_t batch,
+                                  int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim_qk, int32_t head_dim_v,
+                                  int32_t head_dim_rope, int32_t block_size, int64_t num_blocks,
+                                  float softmax_scale, int32_t dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    pkv::DecodeParams p;
+    pkv::DecodePlan plan{};
+    bool idle = false;
+    int rc = prepare_decode(p, plan, PKV_DECODE_ARGS, &idle);
+    if (rc != PKV_OK || idle || plan.max_splits <= 1) return rc;
+    return launch_combine_for(p, head_dim_v, dtype, (hipStream_t)stream);
+}
+
+#undef PKV_DECODE_ARGS
+
+int pkv_paged_attn_varlen(void* out, float* lse_out, const void* q, const int32_t* cu_seqlens_q,
+                          const int32_t* seq_lens_kv, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, int32_t batch, int64_t total_q,
+                          int32_t max_seqlen_q, int32_t max_blocks_per_seq, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int64_t num_blocks, float softmax_scale, int32_t causal, int32_t dtype,
+                          void* stream) {
+    (void)out; (void)lse_out; (void)q; (void)cu_seqlens_q; (void)seq_lens_kv; (void)k_cache;
+    (void)v_cache; (void)block_table; (void)batch; (void)total_q; (void)max_seqlen_q;
+    (void)max_blocks_per_seq; (void)num_q_heads; (void)num_kv_heads; (void)head_dim;
+    (void)block_size; (void)num_blocks; (void)softmax_scale; (void)causal; (void)dtype; (void)stream;
+    return fail(PKV_ERR_UNSUPPORTED, "varlen: not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,342 @@
+// Paged-attention decode for MHA/GQA on gfx950 ("KVCache Optimization Skill", Mode 2
+// step 4 and 3.6; "Paged KV Cache and Packed Sequence", 3.3 and 4.2: the kernel walks
+// each sequence's physical blocks through block_table).
+//
+// Decode reads every cached K/V byte once and does about one flop per byte, so the
+// kernel is bound by HBM bandwidth.  Design:
+//  * one workgroup (4 wave64s) per (kv head, sequence, split of split_tokens tokens);
+//    the kv head varies fastest in blockIdx, so workgroups in flight together read
+//    neighbouring head slices of the same physical blocks;
+//  * each workgroup computes all G = Hq / Hkv query heads of its kv head, so a K/V row
+//    is read from HBM once however many query heads share it (GQA);
+//  * a token's K (or V) row of one head is D * elem bytes, loaded as 16-byte vectors by
+//    LPT = D * elem / 16 lanes; a wave covers TPW = 64 / LPT tokens per load and issues
+//    all K and V loads of a 32-token step before using any of them;
+//  * each lane looks up its token's physical block itself (block_table row of the
+//    sequence, cached), so any power-of-two block size works;
+//  * rows of the wave keep their own online-softmax state (max, sum, output), merged
+//    across rows with shuffles and across waves in LDS at the end;
+//  * tokens past the sequence length are never loaded (masked by selection), so stale
+//    or NaN rows in a block's tail cannot leak into the sum.
+// A second kernel merges the per-split partial states (log-sum-exp rule).
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kWaves = 4;
+constexpr int kStepTokens = 32;   // tokens a wave loads per step
+
+template <typename T> struct ElemBytes;
+template <> struct ElemBytes<float> { static constexpr int v = 4; };
+template <> struct ElemBytes<bf16_t> { static constexpr int v = 2; };
+
+template <typename T, int D>
+struct Shape {
+    static constexpr int kEpl = 16 / ElemBytes<T>::v;  // elements per lane per load
+    static constexpr int kLpt = D / kEpl;              // lanes per token row
+    static constexpr int kTpw = kWave / kLpt;          // tokens per wave load
+    static constexpr int kNj = kStepTokens / kTpw;     // loads per step (each of K, V)
+    static_assert(kLpt >= 1 && kLpt <= 64 && kTpw * kLpt == kWave, "bad shape");
+};
+
+// q . k over the lane's EPL elements (fp32 accumulate).
+template <typename T>
+__device__ __forceinline__ float lane_dot(const u32x4& q, const u32x4& k);
+template <>
+__device__ __forceinline__ float lane_dot<bf16_t>(const u32x4& q, const u32x4& k) {
+    float a = dot2_bf16(q[0], k[0], 0.0f);
+    a = dot2_bf16(q[1], k[1], a);
+    a = dot2_bf16(q[2], k[2], a);
+    return dot2_bf16(q[3], k[3], a);
+}
+template <>
+__device__ __forceinline__ float lane_dot<float>(const u32x4& q, const u32x4& k) {
+    float a = __uint_as_float(q[0]) * __uint_as_float(k[0]);
+    a = fmaf(__uint_as_float(q[1]), __uint_as_float(k[1]), a);
+    a = fmaf(__uint_as_float(q[2]), __uint_as_float(k[2]), a);
+    return fmaf(__uint_as_float(q[3]), __uint_as_float(k[3]), a);
+}
+
+// Widen a 16-byte vector to EPL floats.
+template <typename T>
+__device__ __forceinline__ void widen(const u32x4& v, float* f);
+template <>
+__device__ __forceinline__ void widen<bf16_t>(const u32x4& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_lo(v[i]); f[2 * i + 1] = bf16_hi(v[i]); }
+}
+template <>
+__device__ __forceinline__ void widen<float>(const u32x4& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float v);
+template <>
+__device__ __forceinline__ void store_out<bf16_t>(void* out, int64_t idx, float v) {
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16(v);
+}
+template <>
+__device__ __forceinline__ void store_out<float>(void* out, int64_t idx, float v) {
+    reinterpret_cast<float*>(out)[idx] = v;
+}
+
+template <typename T, int D, int GP>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
+    using S = Shape<T, D>;
+    constexpr int EPL = S::kEpl, LPT = S::kLpt, TPW = S::kTpw, NJ = S::kNj;
+    constexpr int EB = ElemBytes<T>::v;
+    __shared__ float sm_m[kWaves][GP];
+    __shared__ float sm_l[kWaves][GP];
+    __shared__ float sm_o[kWaves][GP][D];
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int row = lane / LPT;
+    const int col = lane % LPT;
+
+    int id = blockIdx.x;
+    const int kvh = id % p.hkv;
+    id /= p.hkv;
+    const int b = id % p.batch;
+    const int split = id / p.batch;
+    const int L = min(p.seq_lens[b], p.len_cap);
+    const int t0 = split * p.split_tokens;
+    if (L <= 0) {   // no visible key: output 0, lse -inf
+        if (split == 0) {
+            for (int i = threadIdx.x; i < p.group * D; i += blockDim.x) {
+                const int h = kvh * p.group + i / D;
+                store_out<T>(p.out, ((int64_t)b * p.hq + h) * D + i % D, 0.0f);
+                if (p.lse && i % D == 0) p.lse[(int64_t)b * p.hq + h] = -INFINITY;
+            }
+        }
+        return;
+    }
+    if (t0 >= L) return;
+    const int t1 = min(L, t0 + p.split_tokens);
+    const int nsplit = (L + p.split_tokens - 1) / p.split_tokens;
+    const int per_wave = p.split_tokens / kWaves;
+    const int w0 = t0 + wave * per_wave;
+    const int w1 = min(t1, w0 + per_wave);
+
+    // Queries of the group (padded heads repeat the last real one and are not stored).
+    u32x4 qv[GP];
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+        const int h = kvh * p.group + min(g, p.group - 1);
+        const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) +
+                            (((int64_t)b * p.hq + h) * D + col * EPL) * EB;
+        qv[g] = ld16(qp);
+    }
+    float m[GP], l[GP], o[GP][EPL];
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[g][e] = 0.0f;
+    }
+
+    const int32_t* trow = p.table + (int64_t)b * p.mbs;
+    const int64_t slot_stride = (int64_t)p.hkv * D * EB;      // bytes per cache row
+    const int64_t head_off = ((int64_t)kvh * D + col * EPL) * EB;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k_cache) + head_off;
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v_cache) + head_off;
+    const int bs_mask = (1 << p.bs_log2) - 1;
+    const int32_t last_block = (int32_t)(p.num_blocks - 1);
+
+    for (int base = w0; base < w1; base += kStepTokens) {
+        u32x4 kr[NJ], vr[NJ];
+        bool valid[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int tok = base + j * TPW + row;
+            valid[j] = tok < w1;
+            kr[j] = u32x4{0u, 0u, 0u, 0u};
+            vr[j] = u32x4{0u, 0u, 0u, 0u};
+            if (valid[j]) {
+                int32_t phys = trow[tok >> p.bs_log2];
+                phys = min(max(phys, 0), last_block);
+                const int64_t slot = ((int64_t)phys << p.bs_log2) | (tok & bs_mask);
+                kr[j] = ld16(kbase + slot * slot_stride);
+                vr[j] = ld16(vbase + slot * slot_stride);
+            }
+        }
+        float vf[NJ][EPL];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) widen<T>(vr[j], vf[j]);
+
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+            if (g >= p.group) break;
+            float s[NJ];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const float dotp = group_sum<LPT>(lane_dot<T>(qv[g], kr[j]));
+                s[j] = valid[j] ? dotp * p.scale_log2 : -INFINITY;
+                mx = fmaxf(mx, s[j]);
+            }
+            const float mnew = fmaxf(m[g], mx);
+            if (mnew != -INFINITY) {
+                const float alpha = fast_exp2(m[g] - mnew);
+                l[g] *= alpha;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[g][e] *= alpha;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const float pj = fast_exp2(s[j] - mnew);
+                    l[g] += pj;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) o[g][e] = fmaf(pj, vf[j][e], o[g][e]);
+                }
+                m[g] = mnew;
+            }
+        }
+    }
+
+    // Merge the rows of this wave, then the waves of the workgroup.
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+        if (g >= p.group) break;
+        const float mw = cross_row_max<LPT>(m[g]);
+        const float f = (m[g] == -INFINITY) ? 0.0f : fast_exp2(m[g] - mw);
+        const float lw = cross_row_sum<LPT>(l[g] * f);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[g][e] = cross_row_sum<LPT>(o[g][e] * f);
+        if (row == 0) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sm_o[wave][g][col * EPL + e] = o[g][e];
+            if (col == 0) {
+                sm_m[wave][g] = mw;
+                sm_l[wave][g] = lw;
+            }
+        }
+    }
+    __syncthreads();
+
+    for (int i = threadIdx.x; i < p.group * D; i += blockDim.x) {
+        const int g = i / D;
+        const int d = i % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][g]);
+        float acc = 0.0f, lsum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = (sm_m[w][g] == -INFINITY) ? 0.0f : fast_exp2(sm_m[w][g] - M);
+            acc = fmaf(f, sm_o[w][g][d], acc);
+            lsum = fmaf(f, sm_l[w][g], lsum);
+        }
+        const int h = kvh * p.group + g;
+        const int64_t bh = (int64_t)b * p.hq + h;
+        if (nsplit == 1) {
+            store_out<T>(p.out, bh * D + d, acc / lsum);
+            if (p.lse && d == 0) p.lse[bh] = (M + __log2f(lsum)) * kLn2;
+        } else {
+            const int64_t ps = bh * p.max_splits + split;
+            p.ws_o[ps * D + d] = acc;
+            if (d == 0) {
+                p.ws_ml[ps * 2] = M;
+                p.ws_ml[ps * 2 + 1] = lsum;
+            }
+        }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+    extern __shared__ float sm_w[];   // [max_splits] weights
+    __shared__ float sm_inv;
+    __shared__ float sm_lse;
+    const int64_t bh = blockIdx.x;
+    const int b = (int)(bh / p.hq);
+    const int L = min(p.seq_lens[b], p.len_cap);
+    const int ns = L > 0 ? (L + p.split_tokens - 1) / p.split_tokens : 0;
+    if (ns <= 1) return;   // the split kernel wrote this row directly
+    const float* ml = p.ws_ml + bh * p.max_splits * 2;
+    if (threadIdx.x == 0) {
+        float M = -INFINITY;
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+        float lsum = 0.0f;
+        for (int s = 0; s < ns; ++s) {
+            const float w = fast_exp2(ml[2 * s] - M);
+            sm_w[s] = w;
+            lsum = fmaf(w, ml[2 * s + 1], lsum);
+        }
+        sm_inv = 1.0f / lsum;
+        sm_lse = (M + __log2f(lsum)) * kLn2;
+    }
+    __syncthreads();
+    const float* o = p.ws_o + bh * p.max_splits * p.dim;
+    for (int d = threadIdx.x; d < p.dim; d += blockDim.x) {
+        float acc = 0.0f;
+        for (int s = 0; s < ns; ++s) acc = fmaf(sm_w[s], o[(int64_t)s * p.dim + d], acc);
+        store_out<T>(p.out, bh * p.dim + d, acc * sm_inv);
+    }
+    if (p.lse && threadIdx.x == 0) p.lse[bh] = sm_lse;
+}
+
+template <typename T, int D>
+hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
+    const int G = p.group;
+    const int gp = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
+    const dim3 grid((unsigned)((int64_t)p.hkv * p.batch * p.max_splits));
+    switch (gp) {
+        case 1: hipLaunchKernelGGL((decode_split_kernel<T, D, 1>), grid, dim3(256), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((decode_split_kernel<T, D, 2>), grid, dim3(256), 0, s, p); break;
+        case 4: hipLaunchKernelGGL((decode_split_kernel<T, D, 4>), grid, dim3(256), 0, s, p); break;
+        case 8: hipLaunchKernelGGL((decode_split_kernel<T, D, 8>), grid, dim3(256), 0, s, p); break;
+        default: hipLaunchKernelGGL((decode_split_kernel<T, D, 16>), grid, dim3(256), 0, s, p); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim_v, int32_t max_seq_len_kv) {
+    DecodePlan pl{};
+    const int G = num_q_heads / num_kv_heads;
+    // Larger groups carry more partial state per split: use longer splits for them.
+    int split = G <= 2 ? 256 : G <= 4 ? 512 : 1024;
+    const int64_t pairs = (int64_t)batch * num_kv_heads;
+    auto nsplits = [&](int sp) { return (int64_t)(max_seq_len_kv + sp - 1) / sp; };
+    // Keep at least ~4 workgroups per compute unit in flight on long sequences.
+    while (split > kWaves * kStepTokens && pairs * nsplits(split) < 1024) split /= 2;
+    pl.split_tokens = split;
+    pl.max_splits = (int32_t)(max_seq_len_kv > 0 ? nsplits(split) : 1);
+    if (pl.max_splits <= 1) {
+        pl.ws_bytes = 0;
+        pl.ws_ml_offset = 0;
+        return pl;
+    }
+    const size_t rows = (size_t)batch * num_q_heads * pl.max_splits;
+    const size_t o_bytes = (rows * head_dim_v * sizeof(float) + 255) & ~(size_t)255;
+    pl.ws_ml_offset = o_bytes;
+    pl.ws_bytes = o_bytes + rows * 2 * sizeof(float);
+    return pl;
+}
+
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, hipStream_t s) {
+    if (dtype == 1) {
+        return head_dim == 64 ? launch_decode_t<bf16_t, 64>(p, s) : launch_decode_t<bf16_t, 128>(p, s);
+    }
+    return head_dim == 64 ? launch_decode_t<float, 64>(p, s) : launch_decode_t<float, 128>(p, s);
+}
+
+hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)p.batch * p.hq));
+    const int threads = p.dim >= 256 ? 256 : (p.dim >= 128 ? 128 : 64);
+    const size_t shm = (size_t)p.max_splits * sizeof(float);
+    if (dtype == 1) hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(threads), shm, s, p);
+    else hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(threads), shm, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,79 @@
+// Host-side declarations shared by the C-ABI front end (api.hip) and the kernel files.
+// Each launcher enqueues on the given stream and returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// ------------------------------------------------------------------ slot_mapping + write
+struct SlotParams {
+    int64_t* slots;
+    const int32_t* table;
+    const int32_t* lens_before;
+    const int32_t* cu_new;
+    int64_t num_tokens;
+    int32_t batch;
+    int32_t mbs;
+    int32_t bs_log2;
+};
+hipError_t launch_slot_mapping(const SlotParams& p, hipStream_t s);
+
+struct WriteParams {
+    const uint8_t* src[2];   // k_new, v_new
+    uint8_t* dst[2];         // k_cache, v_cache
+    int64_t row_bytes[2];
+    const int64_t* slots;
+    int64_t num_tokens;
+    int64_t num_slots;       // num_blocks * block_size
+};
+hipError_t launch_kv_write(const WriteParams& p, hipStream_t s);
+
+// ------------------------------------------------------------------ decode (MHA / GQA)
+// Split-KV plan: sequence b's tokens are cut into ceil(L'_b / split_tokens) chunks; one
+// workgroup handles (kv head, sequence, chunk).  Partial states go to the workspace and
+// a second kernel merges them.  The plan depends on host-known sizes only, so results
+// do not depend on where blocks sit.
+struct DecodePlan {
+    int32_t split_tokens;
+    int32_t max_splits;
+    size_t ws_bytes;
+    size_t ws_ml_offset;     // byte offset of the (m, l) array inside the workspace
+};
+DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim_v, int32_t max_seq_len_kv);
+
+struct DecodeParams {
+    void* out;
+    float* lse;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* table;
+    const int32_t* seq_lens;
+    float* ws_o;             // [B][Hq][max_splits][D]
+    float* ws_ml;            // [B][Hq][max_splits][2]
+    int32_t batch, mbs, hq, hkv, group;
+    int32_t bs_log2;
+    int32_t split_tokens, max_splits;
+    int32_t len_cap;         // min(max_seq_len_kv, mbs * block_size)
+    int64_t num_blocks;
+    float scale_log2;        // softmax_scale * log2(e)
+};
+// dtype: 0 f32, 1 bf16; head_dim 64 or 128.
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, hipStream_t s);
+
+// Merge of split partials (shared by decode kernels of every shape).
+struct CombineParams {
+    void* out;
+    float* lse;
+    const float* ws_o;
+    const float* ws_ml;
+    const int32_t* seq_lens;
+    int32_t batch, hq, dim, split_tokens, max_splits, len_cap;
+};
+hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t s);
+
+}  // namespace pkv

@@ -1,0 +1,90 @@
+// slot_mapping and the cache write ("KVCache Optimization Skill", Layer 3, 3.1 and 3.3;
+// "Paged KV Cache and Packed Sequence", 2.2; ai6s.net KVCache article, 4.2).
+//
+// Both are tiny next to the attention read: the write moves 2 x T rows (8 KiB each for
+// a 32-head, 128-dim bf16 layer).  The copy uses 16-byte vector loads/stores, one
+// workgroup per (token, K-or-V) row, so rows of both caches are written in one launch.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+namespace {
+
+// One workgroup per sequence; threads walk that sequence's new tokens.
+__global__ __launch_bounds__(256) void slot_mapping_kernel(SlotParams p) {
+    const int b = blockIdx.x;
+    // cu_new comes from device memory: clamp it into [0, num_tokens]
+    const int32_t first = max(p.cu_new[b], 0);
+    const int32_t last = (int32_t)min((int64_t)p.cu_new[b + 1], p.num_tokens);
+    const int64_t before = p.lens_before[b];
+    const int32_t bs_mask = (1 << p.bs_log2) - 1;
+    for (int32_t t = first + (int32_t)threadIdx.x; t < last; t += blockDim.x) {
+        const int64_t pos = before + (t - first);
+        const int64_t logical = pos >> p.bs_log2;
+        int64_t slot = -1;
+        if (logical >= 0 && logical < p.mbs) {
+            const int64_t phys = p.table[(int64_t)b * p.mbs + logical];
+            slot = (phys << p.bs_log2) | (pos & bs_mask);
+        }
+        p.slots[t] = slot;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_slot_mapping(const SlotParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(slot_mapping_kernel, dim3(p.batch), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+namespace {
+
+// blockIdx.x = token, blockIdx.y = 0 (K) / 1 (V).  VEC = bytes per access (16 when the
+// row size and both base pointers allow it, else 4 or 2).
+template <int VEC>
+__global__ __launch_bounds__(256) void kv_write_kernel(WriteParams p) {
+    const int64_t t = blockIdx.x;
+    const int which = blockIdx.y;
+    const int64_t slot = p.slots[t];
+    if (slot < 0 || slot >= p.num_slots) return;   // outside the pool: skipped
+    const int64_t rb = p.row_bytes[which];
+    const uint8_t* src = p.src[which] + t * rb;
+    uint8_t* dst = p.dst[which] + slot * rb;
+    for (int64_t off = (int64_t)threadIdx.x * VEC; off < rb; off += (int64_t)blockDim.x * VEC) {
+        if constexpr (VEC == 16) {
+            st16(dst + off, ld16(src + off));
+        } else if constexpr (VEC == 4) {
+            *reinterpret_cast<uint32_t*>(dst + off) = *reinterpret_cast<const uint32_t*>(src + off);
+        } else {
+            *reinterpret_cast<uint16_t*>(dst + off) = *reinterpret_cast<const uint16_t*>(src + off);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_kv_write(const WriteParams& p, hipStream_t s) {
+    auto aligned = [&](int v) {
+        for (int i = 0; i < 2; ++i) {
+            if (p.row_bytes[i] % v) return false;
+            if (reinterpret_cast<uintptr_t>(p.src[i]) % v) return false;
+            if (reinterpret_cast<uintptr_t>(p.dst[i]) % v) return false;
+        }
+        return true;
+    };
+    const int64_t widest = p.row_bytes[0] > p.row_bytes[1] ? p.row_bytes[0] : p.row_bytes[1];
+    int threads = 256;
+    dim3 grid((unsigned)p.num_tokens, 2);
+    if (aligned(16)) {
+        while (threads > 64 && (int64_t)(threads / 2) * 16 >= widest) threads /= 2;
+        hipLaunchKernelGGL(kv_write_kernel<16>, grid, dim3(threads), 0, s, p);
+    } else if (aligned(4)) {
+        hipLaunchKernelGGL(kv_write_kernel<4>, grid, dim3(threads), 0, s, p);
+    } else {
+        hipLaunchKernelGGL(kv_write_kernel<2>, grid, dim3(threads), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pkv

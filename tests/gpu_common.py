@@ -1,0 +1,104 @@
+"""Shared pieces of the GPU tests: run one step through the C ABI, run the oracle on
+host copies of the same inputs, and compare to the stated tolerances."""
+import sys
+
+import numpy as np
+import torch
+
+import paged_kv_cache_133_amd as pkv
+from oracle import oracle
+from tests.helpers import case_numpy, host
+
+# Tolerances on outputs (max-abs, fp32 accumulation on the GPU)
+ATOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_step(c, causal=False, want_lse=True):
+    """slot_mapping, cache write and attention for case `c` (tensors on the GPU)."""
+    w = c.w
+    dev = c.q.device
+    table = c.table_tensor(dev)
+    lb = c.lens_before_tensor(dev)
+    la = c.lens_after_tensor(dev)
+    cu = c.cu_q_tensor(dev)
+    T = c.num_tokens
+    slots = pkv.slot_mapping(table, lb, cu, w.block_size, T)
+    k = c.cache_k.clone()
+    rope = None
+    if w.mode == "mla":
+        v = k
+        rope = c.cache_rope.clone()
+        pkv.kv_cache_write(c.new_k, c.new_rope, k, rope, slots)
+    else:
+        v = c.cache_v.clone()
+        pkv.kv_cache_write(c.new_k, c.new_v, k, v, slots)
+    lse = torch.empty((T, w.num_q_heads), dtype=torch.float32, device=dev) if want_lse else None
+    if w.mode == "varlen":
+        out, _ = pkv.paged_attn_varlen(c.q, k, v, table, cu, la, c.max_new, w.scale,
+                                       causal=causal, lse=lse)
+    else:
+        out, _ = pkv.paged_attn_decode(c.q, k, v, table, la, c.max_len_after, w.scale,
+                                       q_rope=c.q_rope, k_rope_cache=rope, lse=lse)
+    torch.cuda.synchronize()
+    return {"slots": slots, "cache_k": k, "cache_v": v, "cache_rope": rope, "out": out,
+            "lse": lse}
+
+
+def oracle_step(c, causal=False, rows=None):
+    """The oracle on host copies: slot_mapping and writes for the whole step, then
+    attention for every sequence, or only for the sequences in `rows` (a sample)."""
+    h = case_numpy(c)
+    slots = oracle.slot_mapping(h["block_table"], h["lens_before"], h["cu_q"], h["block_size"],
+                                h["num_blocks"])
+    k = oracle.kv_write(h["cache_k"], h["new_k"], slots)
+    if c.w.mode == "mla":
+        v = k
+        rope = oracle.kv_write(h["cache_rope"], h["new_rope"], slots)
+    else:
+        v = oracle.kv_write(h["cache_v"], h["new_v"], slots)
+        rope = None
+    idx = np.arange(c.w.batch) if rows is None else np.asarray(rows)
+    tok = np.concatenate([np.arange(h["cu_q"][b], h["cu_q"][b + 1]) for b in idx]).astype(np.int64)
+    n = h["cu_q"][idx + 1] - h["cu_q"][idx]
+    cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    q_rope = h["q_rope"][tok] if h["q_rope"] is not None else None
+    out, lse = oracle.paged_attention(h["q"][tok], k, v, h["block_table"][idx], cu,
+                                      h["lens_after"][idx], h["scale"], causal,
+                                      q_rope=q_rope, k_rope=rope)
+    return {"slots": slots, "cache_k": k, "cache_v": v, "cache_rope": rope, "out": out,
+            "lse": lse, "tokens": tok}
+
+
+def compare_outputs(c, g, o, tokens=None, label=""):
+    """Max-abs check of out (and lse) against the oracle; returns the max error."""
+    w = c.w
+    out = g["out"].detach().float().cpu().numpy().astype(np.float64)
+    lse = g["lse"].cpu().numpy().astype(np.float64) if g["lse"] is not None else None
+    if tokens is not None:
+        out = out[tokens]
+        lse = lse[tokens] if lse is not None else None
+    err = np.abs(out - o["out"])
+    assert np.isfinite(out).all(), f"{label}: non-finite GPU output"
+    worst = np.unravel_index(int(np.argmax(err)), err.shape)
+    emax = float(err.max()) if err.size else 0.0
+    assert emax <= ATOL[w.dtype], (f"{label}: max-abs error {emax:.3e} > {ATOL[w.dtype]} at "
+                                   f"(row, head, d) = {worst}")
+    if lse is not None:
+        lerr = np.abs(lse - o["lse"]) / np.maximum(1.0, np.abs(o["lse"]))
+        assert float(lerr.max()) <= 1e-4, f"{label}: lse error {float(lerr.max()):.3e}"
+    return emax
+
+
+def compare_writes(c, g, o):
+    """The written pools must equal the oracle's byte for byte."""
+    assert np.array_equal(g["slots"].cpu().numpy(), o["slots"])
+    assert host(g["cache_k"]).tobytes() == o["cache_k"].tobytes()
+    if c.w.mode == "mla":
+        assert host(g["cache_rope"]).tobytes() == o["cache_rope"].tobytes()
+    else:
+        assert host(g["cache_v"]).tobytes() == o["cache_v"].tobytes()
