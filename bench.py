@@ -4,14 +4,17 @@
 One step = one decode layer of the Llama-7B-shaped workload (B = 32 sequences, 32 query
 heads = 32 kv heads, head_dim 128, block_size 16, bf16, kv lengths U{512..2048} before
 the step, physical blocks shuffled in a pool of total need + 10 %):
-    slot_mapping -> cache write of the new K/V rows -> split-KV attention -> combine,
+    slot_mapping + cache write of the new K/V rows + split-KV attention (one launch,
+    pkv_paged_attn_decode_append), then the split combine (second launch),
 all through the C ABI of libpagedkv.so on torch's current stream, with every input
-already resident in HBM.  Several copies of the K/V pool are rotated so that each step
+already resident in HBM.  --path append / separate time the same step as three / four
+launches (kv_cache_append or slot_mapping + kv_cache_write, split, combine).  Several copies of the K/V pool are rotated so that each step
 reads a pool that left the 256 MB Infinity Cache long ago.
 
 Prints one JSON line: KV-read GB/s (value), µs per step, the roofline of the dominant
-kernel (the split-KV attention pass, timed with HIP events around its launch on the
-same stream) and the fp64 CPU oracle timed on this host as a baseline.
+kernel (the split-KV attention pass, timed with HIP events around each of its launches
+on the stream it runs on, in a second pass of the same steps so the events do not
+perturb the step time) and the fp64 CPU oracle timed on this host as a baseline.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--seed S]
   python bench.py --calibrate-copy MIB     # plain copy of known size, for counter scaling
@@ -50,6 +53,10 @@ def parse():
                     help="minimum wall time of the CPU-oracle sample")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="omit the per-kernel HIP events inside the timed region")
+    ap.add_argument("--path", choices=("fused", "append", "separate"), default="fused",
+                    help="fused: decode_append (write folded into the split pass), combine; "
+                         "append: kv_cache_append (slot_mapping + write), split, combine; "
+                         "separate: slot_mapping, write, split, combine")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for counter scaling)")
     return ap.parse_args()
@@ -193,22 +200,36 @@ def main():
     lse = torch.empty((T, w.num_q_heads), dtype=torch.float32, device=dev)
     need = pkv.decode_workspace_size(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim_v,
                                      case.max_len_after)
-    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
     slot_call = _lib.prepare_slot_mapping(table, lb, cu, w.block_size, T, slots)
+    fused = args.path == "fused"
     reps = []
+    slot_first = args.path == "separate"
     for r in range(R):
         k = case.cache_k if r == 0 else case.cache_k.clone()
         rope = None
         if mla:
             v = k
             rope = case.cache_rope if r == 0 else case.cache_rope.clone()
-            write = _lib.prepare_kv_cache_write(case.new_k, case.new_rope, k, rope, slots)
+            pair = (case.new_k, case.new_rope, k, rope)
         else:
             v = case.cache_v if r == 0 else case.cache_v.clone()
-            write = _lib.prepare_kv_cache_write(case.new_k, case.new_v, k, v, slots)
-        split, combine, _, _ = _lib.prepare_decode(case.q, k, v, table, la, case.max_len_after,
-                                                   w.scale, q_rope=case.q_rope, k_rope_cache=rope,
-                                                   out=out, lse=lse, workspace=ws)
+            pair = (case.new_k, case.new_v, k, v)
+        if fused and not mla:
+            split, combine, _ = _lib.prepare_decode_append(case.q, case.new_k, case.new_v, k, v,
+                                                           table, la, case.max_len_after, w.scale,
+                                                           out=out, lse=lse, workspace=ws,
+                                                           slots_out=slots)
+            reps.append((None, split, combine))
+            continue
+        if args.path == "separate":
+            write = _lib.prepare_kv_cache_write(*pair, slots)
+        else:
+            write = _lib.prepare_kv_cache_append(*pair, table, lb, cu, case.max_new, slots)
+        split, combine, whole, _ = _lib.prepare_decode(case.q, k, v, table, la,
+                                                       case.max_len_after, w.scale,
+                                                       q_rope=case.q_rope, k_rope_cache=rope,
+                                                       out=out, lse=lse, workspace=ws)
         reps.append((write, split, combine))
     torch.cuda.synchronize()
 
@@ -216,25 +237,29 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)] if events else None
 
-    def step(i, timed):
-        write, split, combine = reps[i % R]
-        slot_call()
-        write()
-        if timed and events:
+    def step(i, with_events):
+        write, attn, combine = reps[i % R]
+        if slot_first:
+            slot_call()
+        if write is not None:
+            write()
+        if with_events:
             ev[i][0].record()
-        split()
-        if timed and events:
+        attn()
+        if with_events:
             ev[i][1].record()
-        combine()
+        if combine is not None:
+            combine()
 
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
+    # Timed region: K whole steps, events only at its two ends.
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(args.steps):
-        step(i, True)
+        step(i, False)
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
@@ -243,6 +268,11 @@ def main():
 
     roofline = None
     if events:
+        # Second pass of the same K steps with a pair of HIP events around every launch of
+        # the dominant kernel, recorded on the stream it runs on (torch's current stream).
+        for i in range(args.steps):
+            step(i, True)
+        torch.cuda.synchronize()
         durs = [a.elapsed_time(b) for a, b in ev]
         split_ms = statistics.mean(durs)
         achieved = split_bytes / (split_ms * 1e-3) / 1e9
@@ -262,7 +292,12 @@ def main():
            "head_dim_rope": w.head_dim_rope, "block_size": w.block_size,
            "num_blocks": case.num_blocks, "seed": args.seed,
            "kv_tokens": int(case.lens_after.sum()), "max_kv_len": case.max_len_after,
-           "pool_replicas": R, "step": "slot_mapping + kv_cache_write + decode split + combine"}
+           "pool_replicas": R,
+           "path": args.path,
+           "step": {"fused": "paged_attn_decode_append: split pass that also writes the new "
+                             "token (slot_mapping + write + split-KV attention), then combine",
+                    "append": "kv_cache_append (slot_mapping + write), decode split, combine",
+                    "separate": "slot_mapping, kv_cache_write, decode split, combine"}[args.path]}
     line = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

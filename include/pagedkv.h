@@ -109,8 +109,25 @@ PKV_API int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_cac
                        int64_t num_blocks, int32_t dtype, void* stream);
 
 /*
+ * slot_mapping and the cache write in one launch (the two calls above, fused): token i
+ * of sequence b (packed row t = cu_new[b] + i) is written to slot
+ * block_table[b][pos / block_size] * block_size + pos % block_size, pos = lens_before[b] + i,
+ * and that slot is stored in slot_mapping_out[t] when slot_mapping_out is not NULL (so
+ * later layers of the same step can call pkv_kv_cache_write with it).
+ *   max_new_tokens [host] >= every n_b = cu_new[b+1] - cu_new[b]; batch <= 65535.
+ * Other arguments and preconditions as for pkv_slot_mapping and pkv_kv_cache_write.
+ */
+PKV_API int pkv_kv_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                        const int32_t* block_table, const int32_t* lens_before,
+                        const int32_t* cu_new, int64_t* slot_mapping_out, int32_t batch,
+                        int64_t num_tokens, int32_t max_new_tokens, int32_t max_blocks_per_seq,
+                        int32_t num_kv_heads, int32_t head_dim_k, int32_t head_dim_v,
+                        int32_t block_size, int64_t num_blocks, int32_t dtype, void* stream);
+
+/*
  * Bytes of workspace pkv_paged_attn_decode needs for these sizes (0 if none).  The
- * workspace holds split-KV partial results; its contents need no initialisation.
+ * workspace holds split-KV partial results; its contents need no initialisation, and
+ * calls that may run at the same time need separate workspaces.
  */
 PKV_API size_t pkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim_v, int32_t max_seq_len_kv);
@@ -161,7 +178,7 @@ PKV_API int pkv_paged_attn_decode(void* out, float* lse_out, const void* q, cons
  * leave partial softmax states (max, sum, unnormalised output per split) in `workspace`.
  * _combine then merges those states (out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s,
  * lse = M + log of that sum, M = max_s m_s) and enqueues nothing when no row was split.
- * Calling _split then _combine on one stream equals pkv_paged_attn_decode.
+ * Calling _split then _combine on one stream equals pkv_paged_attn_decode, bit for bit.
  */
 PKV_API int pkv_paged_attn_decode_split(void* out, float* lse_out, const void* q, const void* q_rope,
                                 const void* k_cache, const void* v_cache,
@@ -182,6 +199,32 @@ PKV_API int pkv_paged_attn_decode_combine(void* out, float* lse_out, const void*
                                   int32_t head_dim_rope, int32_t block_size, int64_t num_blocks,
                                   float softmax_scale, int32_t dtype, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step of one layer with the cache write folded into the attention pass:
+ * for each sequence b, the new K/V row of this step (k_new[b], v_new[b]) is stored at
+ * logical position seq_lens_kv[b] - 1, and query b attends to all seq_lens_kv[b] tokens,
+ * that one included.  Equal to pkv_kv_cache_append (one token per sequence,
+ * lens_before = seq_lens_kv - 1) followed by pkv_paged_attn_decode, in one pass over the
+ * cache: the new token's K/V are taken from k_new/v_new instead of being read back
+ * ("KVCache Optimization Skill", 3.6: write by slot_mapping, then attention reads
+ * kv_len + 1 tokens).
+ *   k_new, v_new [batch][num_kv_heads][head_dim], 16-byte aligned
+ *   slot_mapping_out [batch] int64 or NULL: the slot written for each sequence
+ *   stages: 1 = the split pass only (writes, single-split rows, partial states),
+ *           2 = the combine pass only, 3 = both.  1 then 2 on one stream equals 3.
+ * MHA/GQA only (no rope); other arguments, workspace and preconditions as for
+ * pkv_paged_attn_decode (with head_dim_qk = head_dim_v = head_dim).
+ */
+PKV_API int pkv_paged_attn_decode_append(void* out, float* lse_out, const void* q, const void* k_new,
+                                 const void* v_new, void* k_cache, void* v_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens_kv,
+                                 int64_t* slot_mapping_out, int32_t batch,
+                                 int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int64_t num_blocks, float softmax_scale,
+                                 int32_t dtype, int32_t stages, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /*
  * Packed varlen attention over the paged cache: sequence b owns query rows

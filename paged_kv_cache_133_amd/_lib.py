@@ -22,8 +22,9 @@ STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_SHAPE", -3: "PKV_ERR_DTY
           -4: "PKV_ERR_UNSUPPORTED", -5: "PKV_ERR_ALIGN", -6: "PKV_ERR_SCALE",
           -7: "PKV_ERR_WORKSPACE", -8: "PKV_ERR_HIP"}
 EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_write",
-           "pkv_decode_workspace_size", "pkv_paged_attn_decode", "pkv_paged_attn_decode_split",
-           "pkv_paged_attn_decode_combine", "pkv_paged_attn_varlen")
+           "pkv_kv_cache_append", "pkv_decode_workspace_size", "pkv_paged_attn_decode", "pkv_paged_attn_decode_split",
+           "pkv_paged_attn_decode_combine", "pkv_paged_attn_decode_append",
+           "pkv_paged_attn_varlen")
 
 
 class PagedKVError(RuntimeError):
@@ -54,6 +55,9 @@ def lib() -> ctypes.CDLL:
     L.pkv_slot_mapping.argtypes = [p, p, p, p, i32, i64, i32, i32, p]
     L.pkv_kv_cache_write.restype = ctypes.c_int
     L.pkv_kv_cache_write.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i32, i64, i32, p]
+    L.pkv_kv_cache_append.restype = ctypes.c_int
+    L.pkv_kv_cache_append.argtypes = [p, p, p, p, p, p, p, p, i32, i64, i32, i32, i32, i32, i32,
+                                      i32, i64, i32, p]
     L.pkv_decode_workspace_size.restype = sz
     L.pkv_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     for name in ("pkv_paged_attn_decode", "pkv_paged_attn_decode_split",
@@ -62,6 +66,9 @@ def lib() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
         fn.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                        i64, f32, i32, p, sz, p]
+    L.pkv_paged_attn_decode_append.restype = ctypes.c_int
+    L.pkv_paged_attn_decode_append.argtypes = [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
+                                               i32, i32, i32, i64, f32, i32, i32, p, sz, p]
     L.pkv_paged_attn_varlen.restype = ctypes.c_int
     L.pkv_paged_attn_varlen.argtypes = [p, p, p, p, p, p, p, p, i32, i64, i32, i32, i32, i32,
                                         i32, i32, i64, f32, i32, i32, p]
@@ -128,6 +135,44 @@ def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tens
                                     _dtype_code(k_cache), _stream(k_cache.device)))
 
 
+def _append_args(k_new, v_new, k_cache, v_cache, block_table, lens_before, cu_new,
+                 max_new_tokens, slots_out):
+    _dev(k_new, v_new, k_cache, v_cache, block_table, lens_before, cu_new, slots_out)
+    nb, bs, hkv, dk = k_cache.shape
+    dv = v_cache.shape[-1]
+    return (_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(lens_before), _ptr(cu_new), _ptr(slots_out), lens_before.shape[0],
+            k_new.shape[0], max_new_tokens, block_table.shape[1], hkv, dk, dv, bs, nb,
+            _dtype_code(k_cache), _stream(k_cache.device))
+
+
+def kv_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                    v_cache: torch.Tensor, block_table: torch.Tensor, lens_before: torch.Tensor,
+                    cu_new: torch.Tensor, max_new_tokens: int,
+                    slots_out: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """slot_mapping + write in one launch (see pkv_kv_cache_append)."""
+    _check(lib().pkv_kv_cache_append(*_append_args(k_new, v_new, k_cache, v_cache, block_table,
+                                                   lens_before, cu_new, max_new_tokens,
+                                                   slots_out)))
+    return slots_out
+
+
+def prepare_kv_cache_append(k_new, v_new, k_cache, v_cache, block_table, lens_before, cu_new,
+                            max_new_tokens, slots_out=None):
+    args = _append_args(k_new, v_new, k_cache, v_cache, block_table, lens_before, cu_new,
+                        max_new_tokens, slots_out)
+    return PreparedCall(lib().pkv_kv_cache_append, args,
+                        (k_new, v_new, k_cache, v_cache, block_table, lens_before, cu_new,
+                         slots_out))
+
+
+def new_decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_dim_v: int,
+                         max_seq_len_kv: int, device) -> torch.Tensor:
+    """A zero-filled decode workspace of the required size (at least 16 bytes)."""
+    need = decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim_v, max_seq_len_kv)
+    return torch.zeros(max(need, 16), dtype=torch.uint8, device=device)
+
+
 def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, head_dim_v: int,
                           max_seq_len_kv: int) -> int:
     return int(lib().pkv_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim_v,
@@ -144,8 +189,7 @@ def _decode_args(q, k_cache, v_cache, block_table, seq_lens_kv, max_seq_len_kv, 
     if out is None:
         out = torch.empty((B, hq, dv), dtype=q.dtype, device=q.device)
     if workspace is None:
-        need = decode_workspace_size(B, hq, hkv, dv, max_seq_len_kv)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = new_decode_workspace(B, hq, hkv, dv, max_seq_len_kv, q.device)
     args = (_ptr(out), _ptr(lse), _ptr(q), _ptr(q_rope), _ptr(k_cache), _ptr(v_cache),
             _ptr(k_rope_cache), _ptr(block_table), _ptr(seq_lens_kv), B, block_table.shape[1],
             max_seq_len_kv, hq, hkv, dqk, dv, dr, bs, nb, float(softmax_scale), _dtype_code(q),
@@ -192,6 +236,50 @@ def prepare_decode(q, k_cache, v_cache, block_table, seq_lens_kv, max_seq_len_kv
     return (PreparedCall(L.pkv_paged_attn_decode_split, args, keep),
             PreparedCall(L.pkv_paged_attn_decode_combine, args, keep),
             PreparedCall(L.pkv_paged_attn_decode, args, keep), out)
+
+
+def _decode_append_args(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
+                        max_seq_len_kv, softmax_scale, stages, out, lse, workspace, slots_out):
+    _dev(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv, out, lse, workspace,
+         slots_out)
+    B, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = new_decode_workspace(B, hq, hkv, d, max_seq_len_kv, q.device)
+    args = (_ptr(out), _ptr(lse), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_table), _ptr(seq_lens_kv), _ptr(slots_out), B, block_table.shape[1],
+            max_seq_len_kv, hq, hkv, d, bs, nb, float(softmax_scale), _dtype_code(q), stages,
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device))
+    return args, out, workspace
+
+
+def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
+                             max_seq_len_kv, softmax_scale, out=None, lse=None, workspace=None,
+                             slots_out=None):
+    """Write this step's token and attend, in one pass (see pkv_paged_attn_decode_append)."""
+    args, out, _ = _decode_append_args(q, k_new, v_new, k_cache, v_cache, block_table,
+                                       seq_lens_kv, max_seq_len_kv, softmax_scale, 3, out, lse,
+                                       workspace, slots_out)
+    _check(lib().pkv_paged_attn_decode_append(*args))
+    return out, lse
+
+
+def prepare_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
+                          max_seq_len_kv, softmax_scale, out=None, lse=None, workspace=None,
+                          slots_out=None):
+    """(split pass, combine pass) prepared calls of pkv_paged_attn_decode_append."""
+    calls = []
+    for stages in (1, 2):
+        args, out, workspace = _decode_append_args(q, k_new, v_new, k_cache, v_cache,
+                                                   block_table, seq_lens_kv, max_seq_len_kv,
+                                                   softmax_scale, stages, out, lse, workspace,
+                                                   slots_out)
+        calls.append(PreparedCall(lib().pkv_paged_attn_decode_append, args,
+                                  (q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
+                                   out, lse, workspace, slots_out)))
+    return calls[0], calls[1], out
 
 
 def prepare_slot_mapping(block_table, lens_before, cu_new, block_size, num_tokens, out):

@@ -96,6 +96,49 @@ int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_cache, void
     return hip_status(pkv::launch_kv_write(p, (hipStream_t)stream), "kv_cache_write launch");
 }
 
+int pkv_kv_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                        const int32_t* block_table, const int32_t* lens_before,
+                        const int32_t* cu_new, int64_t* slot_mapping_out, int32_t batch,
+                        int64_t num_tokens, int32_t max_new_tokens, int32_t max_blocks_per_seq,
+                        int32_t num_kv_heads, int32_t head_dim_k, int32_t head_dim_v,
+                        int32_t block_size, int64_t num_blocks, int32_t dtype, void* stream) {
+    if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "kv_cache_append: unknown dtype %d", dtype);
+    if (batch < 0 || num_tokens < 0 || max_new_tokens < 0 || num_kv_heads <= 0 || head_dim_k <= 0 ||
+        head_dim_v <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+        return fail(PKV_ERR_SHAPE, "kv_cache_append: sizes must be positive (batch, num_tokens, max_new_tokens >= 0)");
+    if (!pow2_in(block_size, 1, 256))
+        return fail(PKV_ERR_UNSUPPORTED, "kv_cache_append: block_size %d is not a power of two in [1, 256]", block_size);
+    if (num_tokens > 0x7fffffffLL || batch > 65535)
+        return fail(PKV_ERR_UNSUPPORTED, "kv_cache_append: at most 65535 sequences and 2^31 - 1 tokens");
+    if (batch == 0 || num_tokens == 0 || max_new_tokens == 0) return PKV_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !lens_before || !cu_new)
+        return fail(PKV_ERR_NULL, "kv_cache_append: NULL pointer argument");
+    if (k_cache == v_cache) return fail(PKV_ERR_SHAPE, "kv_cache_append: k_cache and v_cache must differ");
+    const int eb = elem_bytes(dtype);
+    pkv::AppendParams p{};
+    p.src[0] = static_cast<const uint8_t*>(k_new);
+    p.src[1] = static_cast<const uint8_t*>(v_new);
+    p.dst[0] = static_cast<uint8_t*>(k_cache);
+    p.dst[1] = static_cast<uint8_t*>(v_cache);
+    p.row_bytes[0] = (int64_t)num_kv_heads * head_dim_k * eb;
+    p.row_bytes[1] = (int64_t)num_kv_heads * head_dim_v * eb;
+    for (int i = 0; i < 2; ++i) {
+        if ((reinterpret_cast<uintptr_t>(p.src[i]) | reinterpret_cast<uintptr_t>(p.dst[i])) % eb)
+            return fail(PKV_ERR_ALIGN, "kv_cache_append: pointers must be aligned to the element size");
+    }
+    p.table = block_table;
+    p.lens_before = lens_before;
+    p.cu_new = cu_new;
+    p.slots_out = slot_mapping_out;
+    p.num_tokens = num_tokens;
+    p.num_slots = num_blocks * block_size;
+    p.batch = batch;
+    p.max_new = max_new_tokens;
+    p.mbs = max_blocks_per_seq;
+    p.bs_log2 = log2i(block_size);
+    return hip_status(pkv::launch_kv_append(p, (hipStream_t)stream), "kv_cache_append launch");
+}
+
 size_t pkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim_v, int32_t max_seq_len_kv) {
     if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim_v <= 0 ||
@@ -170,9 +213,9 @@ int prepare_decode(pkv::DecodeParams& p, pkv::DecodePlan& plan, void* out, float
     p.v_cache = v_cache;
     p.table = block_table;
     p.seq_lens = seq_lens_kv;
-    p.ws_o = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
-    p.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + plan.ws_ml_offset)
-                            : nullptr;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    p.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.ws_o_offset) : nullptr;
+    p.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.ws_ml_offset) : nullptr;
     p.batch = batch;
     p.mbs = max_blocks_per_seq;
     p.hq = num_q_heads;
@@ -270,6 +313,42 @@ int pkv_paged_attn_decode_combine(void* out, float* lse_out, const void* q, cons
 }
 
 #undef PKV_DECODE_ARGS
+
+int pkv_paged_attn_decode_append(void* out, float* lse_out, const void* q, const void* k_new,
+                                 const void* v_new, void* k_cache, void* v_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens_kv,
+                                 int64_t* slot_mapping_out, int32_t batch,
+                                 int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int64_t num_blocks, float softmax_scale,
+                                 int32_t dtype, int32_t stages, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    if (stages < 1 || stages > 3) return fail(PKV_ERR_SHAPE, "decode_append: stages must be 1, 2 or 3");
+    pkv::DecodeParams p;
+    pkv::DecodePlan plan{};
+    bool idle = false;
+    int rc = prepare_decode(p, plan, out, lse_out, q, nullptr, k_cache, v_cache, nullptr,
+                            block_table, seq_lens_kv, batch, max_blocks_per_seq, max_seq_len_kv,
+                            num_q_heads, num_kv_heads, head_dim, head_dim, 0, block_size,
+                            num_blocks, softmax_scale, dtype, workspace, workspace_bytes, &idle);
+    if (rc != PKV_OK || idle) return rc;
+    if (!k_new || !v_new) return fail(PKV_ERR_NULL, "decode_append: NULL k_new or v_new");
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return fail(PKV_ERR_ALIGN, "decode_append: k_new and v_new must be 16-byte aligned");
+    if (k_cache == v_cache) return fail(PKV_ERR_SHAPE, "decode_append: k_cache and v_cache must differ");
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.k_cache_w = k_cache;
+    p.v_cache_w = v_cache;
+    p.slots_out = slot_mapping_out;
+    hipStream_t s = (hipStream_t)stream;
+    if (stages & 1) {
+        rc = hip_status(pkv::launch_decode(p, dtype, head_dim, s), "decode_append split launch");
+        if (rc != PKV_OK) return rc;
+    }
+    if ((stages & 2) && plan.max_splits > 1) return launch_combine_for(p, head_dim, dtype, s);
+    return PKV_OK;
+}
 
 int pkv_paged_attn_varlen(void* out, float* lse_out, const void* q, const int32_t* cu_seqlens_q,
                           const int32_t* seq_lens_kv, const void* k_cache, const void* v_cache,

@@ -9,16 +9,20 @@
 //    neighbouring head slices of the same physical blocks;
 //  * each workgroup computes all G = Hq / Hkv query heads of its kv head, so a K/V row
 //    is read from HBM once however many query heads share it (GQA);
-//  * a token's K (or V) row of one head is D * elem bytes, loaded as 16-byte vectors by
-//    LPT = D * elem / 16 lanes; a wave covers TPW = 64 / LPT tokens per load and issues
-//    all K and V loads of a 32-token step before using any of them;
-//  * each lane looks up its token's physical block itself (block_table row of the
-//    sequence, cached), so any power-of-two block size works;
+//  * a token's K (or V) row of one head is D * elem bytes, loaded as 16-byte
+//    non-temporal vectors by LPT = D * elem / 16 lanes; a wave covers TPW = 64 / LPT
+//    tokens per load and issues all K and V loads of a 32-token step before using any;
+//  * block-table entries of the next step are fetched one step ahead, one entry per
+//    lane, and handed to the lanes that need them with a cross-lane shuffle, so address
+//    translation never waits on memory; any power-of-two block size works;
 //  * rows of the wave keep their own online-softmax state (max, sum, output), merged
 //    across rows with shuffles and across waves in LDS at the end;
 //  * tokens past the sequence length are never loaded (masked by selection), so stale
 //    or NaN rows in a block's tail cannot leak into the sum.
-// A second kernel merges the per-split partial states (log-sum-exp rule).
+// A second kernel merges the splits of each (sequence, head) with the log-sum-exp rule.
+// (Merging in the same launch, by the last workgroup to arrive, needs a device-scope
+// release/acquire per workgroup; on gfx950 that write-back of the L2 made the decode
+// about ten times slower than the extra launch.)
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -86,7 +90,7 @@ __device__ __forceinline__ void store_out<float>(void* out, int64_t idx, float v
     reinterpret_cast<float*>(out)[idx] = v;
 }
 
-template <typename T, int D, int GP>
+template <typename T, int D, int GP, bool APPEND>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     using S = Shape<T, D>;
     constexpr int EPL = S::kEpl, LPT = S::kLpt, TPW = S::kTpw, NJ = S::kNj;
@@ -123,6 +127,29 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int per_wave = p.split_tokens / kWaves;
     const int w0 = t0 + wave * per_wave;
     const int w1 = min(t1, w0 + per_wave);
+    const int bs_mask = (1 << p.bs_log2) - 1;
+    const int32_t last_block = (int32_t)(p.num_blocks - 1);
+    const int32_t* trow = p.table + (int64_t)b * p.mbs;
+
+    // Append mode: this step's token sits at L - 1; its K/V come from the new rows.
+    const int pos_new = APPEND ? L - 1 : -1;
+    const int64_t new_off = ((int64_t)b * p.hkv + kvh) * D * EB;
+    if (APPEND && pos_new >= t0 && pos_new < t1) {
+        int32_t phys = trow[pos_new >> p.bs_log2];
+        phys = min(max(phys, 0), last_block);
+        const int64_t slot = ((int64_t)phys << p.bs_log2) | (pos_new & bs_mask);
+        const int64_t dst = (slot * p.hkv + kvh) * D * EB;
+        constexpr int kChunks = D * EB / 16;
+        const int i = threadIdx.x;
+        if (i < 2 * kChunks) {
+            const int which = i / kChunks;
+            const int64_t off = (int64_t)(i % kChunks) * 16;
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(which ? p.v_new : p.k_new) + new_off;
+            uint8_t* dstp = reinterpret_cast<uint8_t*>(which ? p.v_cache_w : p.k_cache_w) + dst;
+            st16(dstp + off, ld16(src + off));
+        }
+        if (p.slots_out && kvh == 0 && threadIdx.x == 0) p.slots_out[b] = slot;
+    }
 
     // Queries of the group (padded heads repeat the last real one and are not stored).
     u32x4 qv[GP];
@@ -142,29 +169,47 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         for (int e = 0; e < EPL; ++e) o[g][e] = 0.0f;
     }
 
-    const int32_t* trow = p.table + (int64_t)b * p.mbs;
     const int64_t slot_stride = (int64_t)p.hkv * D * EB;      // bytes per cache row
     const int64_t head_off = ((int64_t)kvh * D + col * EPL) * EB;
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k_cache) + head_off;
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v_cache) + head_off;
-    const int bs_mask = (1 << p.bs_log2) - 1;
-    const int32_t last_block = (int32_t)(p.num_blocks - 1);
+    const uint8_t* knew =
+        APPEND ? reinterpret_cast<const uint8_t*>(p.k_new) + new_off + col * EPL * EB : nullptr;
+    const uint8_t* vnew =
+        APPEND ? reinterpret_cast<const uint8_t*>(p.v_new) + new_off + col * EPL * EB : nullptr;
 
+    // Table entries of the blocks a step touches: lane i holds entry (first block + i).
+    // Steps start at multiples of 32 tokens, so a step spans at most 32 blocks.
+    auto load_table = [&](int base) -> int32_t {
+        const int blk0 = base >> p.bs_log2;
+        const int nblk = ((min(base + kStepTokens, w1) - 1) >> p.bs_log2) - blk0 + 1;
+        return (base < w1 && lane < nblk) ? trow[blk0 + lane] : 0;
+    };
+
+    int32_t tbl = load_table(w0);
     for (int base = w0; base < w1; base += kStepTokens) {
+        const int32_t tbl_next = load_table(base + kStepTokens);
+        const int blk0 = base >> p.bs_log2;
         u32x4 kr[NJ], vr[NJ];
         bool valid[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int tok = base + j * TPW + row;
             valid[j] = tok < w1;
+            int32_t phys = __shfl(tbl, (tok >> p.bs_log2) - blk0, 64);
+            phys = min(max(phys, 0), last_block);
+            const int64_t slot = ((int64_t)phys << p.bs_log2) | (tok & bs_mask);
             kr[j] = u32x4{0u, 0u, 0u, 0u};
             vr[j] = u32x4{0u, 0u, 0u, 0u};
             if (valid[j]) {
-                int32_t phys = trow[tok >> p.bs_log2];
-                phys = min(max(phys, 0), last_block);
-                const int64_t slot = ((int64_t)phys << p.bs_log2) | (tok & bs_mask);
-                kr[j] = ld16(kbase + slot * slot_stride);
-                vr[j] = ld16(vbase + slot * slot_stride);
+                const uint8_t* kp = kbase + slot * slot_stride;
+                const uint8_t* vp = vbase + slot * slot_stride;
+                if (APPEND && tok == pos_new) {
+                    kp = knew;
+                    vp = vnew;
+                }
+                kr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp));
+                vr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp));
             }
         }
         float vf[NJ][EPL];
@@ -198,6 +243,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
                 m[g] = mnew;
             }
         }
+        tbl = tbl_next;
     }
 
     // Merge the rows of this wave, then the waves of the workgroup.
@@ -282,20 +328,27 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     if (p.lse && threadIdx.x == 0) p.lse[bh] = sm_lse;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool APPEND>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
     const int G = p.group;
     const int gp = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
     const dim3 grid((unsigned)((int64_t)p.hkv * p.batch * p.max_splits));
     switch (gp) {
-        case 1: hipLaunchKernelGGL((decode_split_kernel<T, D, 1>), grid, dim3(256), 0, s, p); break;
-        case 2: hipLaunchKernelGGL((decode_split_kernel<T, D, 2>), grid, dim3(256), 0, s, p); break;
-        case 4: hipLaunchKernelGGL((decode_split_kernel<T, D, 4>), grid, dim3(256), 0, s, p); break;
-        case 8: hipLaunchKernelGGL((decode_split_kernel<T, D, 8>), grid, dim3(256), 0, s, p); break;
-        default: hipLaunchKernelGGL((decode_split_kernel<T, D, 16>), grid, dim3(256), 0, s, p); break;
+        case 1: hipLaunchKernelGGL((decode_split_kernel<T, D, 1, APPEND>), grid, dim3(256), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((decode_split_kernel<T, D, 2, APPEND>), grid, dim3(256), 0, s, p); break;
+        case 4: hipLaunchKernelGGL((decode_split_kernel<T, D, 4, APPEND>), grid, dim3(256), 0, s, p); break;
+        case 8: hipLaunchKernelGGL((decode_split_kernel<T, D, 8, APPEND>), grid, dim3(256), 0, s, p); break;
+        default: hipLaunchKernelGGL((decode_split_kernel<T, D, 16, APPEND>), grid, dim3(256), 0, s, p); break;
     }
     return hipGetLastError();
 }
+
+template <typename T, int D>
+hipError_t launch_decode_d(const DecodeParams& p, hipStream_t s) {
+    return p.k_new ? launch_decode_t<T, D, true>(p, s) : launch_decode_t<T, D, false>(p, s);
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -311,23 +364,19 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
     while (split > kWaves * kStepTokens && pairs * nsplits(split) < 1024) split /= 2;
     pl.split_tokens = split;
     pl.max_splits = (int32_t)(max_seq_len_kv > 0 ? nsplits(split) : 1);
-    if (pl.max_splits <= 1) {
-        pl.ws_bytes = 0;
-        pl.ws_ml_offset = 0;
-        return pl;
-    }
+    if (pl.max_splits <= 1) return pl;   // no workspace needed
     const size_t rows = (size_t)batch * num_q_heads * pl.max_splits;
-    const size_t o_bytes = (rows * head_dim_v * sizeof(float) + 255) & ~(size_t)255;
-    pl.ws_ml_offset = o_bytes;
-    pl.ws_bytes = o_bytes + rows * 2 * sizeof(float);
+    pl.ws_o_offset = 0;
+    pl.ws_ml_offset = align256(rows * head_dim_v * sizeof(float));
+    pl.ws_bytes = pl.ws_ml_offset + rows * 2 * sizeof(float);
     return pl;
 }
 
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, hipStream_t s) {
     if (dtype == 1) {
-        return head_dim == 64 ? launch_decode_t<bf16_t, 64>(p, s) : launch_decode_t<bf16_t, 128>(p, s);
+        return head_dim == 64 ? launch_decode_d<bf16_t, 64>(p, s) : launch_decode_d<bf16_t, 128>(p, s);
     }
-    return head_dim == 64 ? launch_decode_t<float, 64>(p, s) : launch_decode_t<float, 128>(p, s);
+    return head_dim == 64 ? launch_decode_d<float, 64>(p, s) : launch_decode_d<float, 128>(p, s);
 }
 
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t s) {

@@ -31,16 +31,35 @@ struct WriteParams {
 };
 hipError_t launch_kv_write(const WriteParams& p, hipStream_t s);
 
+// slot_mapping and write in one launch: workgroup (b, i, K-or-V) appends new token i of
+// sequence b.
+struct AppendParams {
+    const uint8_t* src[2];
+    uint8_t* dst[2];
+    int64_t row_bytes[2];
+    const int32_t* table;
+    const int32_t* lens_before;
+    const int32_t* cu_new;
+    int64_t* slots_out;      // may be null
+    int64_t num_tokens;
+    int64_t num_slots;
+    int32_t batch, max_new, mbs, bs_log2;
+};
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
+
 // ------------------------------------------------------------------ decode (MHA / GQA)
 // Split-KV plan: sequence b's tokens are cut into ceil(L'_b / split_tokens) chunks; one
 // workgroup handles (kv head, sequence, chunk).  Partial states go to the workspace and
 // a second kernel merges them.  The plan depends on host-known sizes only, so results
 // do not depend on where blocks sit.
+// Workspace layout (each part 256-byte aligned):
+//   [o fp32 B*Hq*max_splits*Dv][(m, l) fp32 B*Hq*max_splits*2]
 struct DecodePlan {
     int32_t split_tokens;
     int32_t max_splits;
     size_t ws_bytes;
-    size_t ws_ml_offset;     // byte offset of the (m, l) array inside the workspace
+    size_t ws_o_offset;
+    size_t ws_ml_offset;
 };
 DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t head_dim_v, int32_t max_seq_len_kv);
@@ -61,11 +80,19 @@ struct DecodeParams {
     int32_t len_cap;         // min(max_seq_len_kv, mbs * block_size)
     int64_t num_blocks;
     float scale_log2;        // softmax_scale * log2(e)
+    // Append mode (decode step that also writes this step's token): the token at
+    // position seq_lens[b] - 1 is read from k_new/v_new rows [B][Hkv][D] instead of the
+    // cache, and the workgroup whose split holds it writes its head slice to the cache.
+    const void* k_new;       // null: plain decode
+    const void* v_new;
+    void* k_cache_w;         // writable views of the caches (append mode)
+    void* v_cache_w;
+    int64_t* slots_out;      // [B] or null
 };
 // dtype: 0 f32, 1 bf16; head_dim 64 or 128.
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, hipStream_t s);
 
-// Merge of split partials (shared by decode kernels of every shape).
+// Merge of split partials (second launch of a split decode).
 struct CombineParams {
     void* out;
     float* lse;

@@ -87,4 +87,64 @@ hipError_t launch_kv_write(const WriteParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+namespace {
+
+// blockIdx = (new-token index i within its sequence, sequence b, K or V).
+template <int VEC>
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
+    const int i = blockIdx.x;
+    const int b = blockIdx.y;
+    const int which = blockIdx.z;
+    const int64_t first = max(p.cu_new[b], 0);
+    const int64_t last = min((int64_t)p.cu_new[b + 1], p.num_tokens);
+    const int64_t t = first + i;
+    if (t >= last) return;
+    const int64_t pos = (int64_t)p.lens_before[b] + i;
+    const int64_t logical = pos >> p.bs_log2;
+    int64_t slot = -1;
+    if (pos >= 0 && logical < p.mbs) {
+        const int64_t phys = p.table[(int64_t)b * p.mbs + logical];
+        slot = (phys << p.bs_log2) | (pos & ((1 << p.bs_log2) - 1));
+    }
+    if (which == 0 && threadIdx.x == 0 && p.slots_out) p.slots_out[t] = slot;
+    if (slot < 0 || slot >= p.num_slots) return;
+    const int64_t rb = p.row_bytes[which];
+    const uint8_t* src = p.src[which] + t * rb;
+    uint8_t* dst = p.dst[which] + slot * rb;
+    for (int64_t off = (int64_t)threadIdx.x * VEC; off < rb; off += (int64_t)blockDim.x * VEC) {
+        if constexpr (VEC == 16) {
+            st16(dst + off, ld16(src + off));
+        } else if constexpr (VEC == 4) {
+            *reinterpret_cast<uint32_t*>(dst + off) = *reinterpret_cast<const uint32_t*>(src + off);
+        } else {
+            *reinterpret_cast<uint16_t*>(dst + off) = *reinterpret_cast<const uint16_t*>(src + off);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t s) {
+    auto aligned = [&](int v) {
+        for (int i = 0; i < 2; ++i) {
+            if (p.row_bytes[i] % v) return false;
+            if (reinterpret_cast<uintptr_t>(p.src[i]) % v) return false;
+            if (reinterpret_cast<uintptr_t>(p.dst[i]) % v) return false;
+        }
+        return true;
+    };
+    const int64_t widest = p.row_bytes[0] > p.row_bytes[1] ? p.row_bytes[0] : p.row_bytes[1];
+    int threads = 256;
+    const dim3 grid((unsigned)p.max_new, (unsigned)p.batch, 2);
+    if (aligned(16)) {
+        while (threads > 64 && (int64_t)(threads / 2) * 16 >= widest) threads /= 2;
+        hipLaunchKernelGGL(kv_append_kernel<16>, grid, dim3(threads), 0, s, p);
+    } else if (aligned(4)) {
+        hipLaunchKernelGGL(kv_append_kernel<4>, grid, dim3(threads), 0, s, p);
+    } else {
+        hipLaunchKernelGGL(kv_append_kernel<2>, grid, dim3(threads), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace pkv

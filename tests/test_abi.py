@@ -132,6 +132,31 @@ def test_write_rejects():
     assert call(T=0, k=None, v=None, kc=None, vc=None, s=None) == 0
 
 
+def test_append_rejects():
+    L = _lib().lib()
+    f = L.pkv_kv_cache_append
+
+    def call(**kw):
+        a = dict(k=FAKE, v=FAKE, kc=FAKE, vc=ctypes.c_void_p(0x200000), t=FAKE, lb=FAKE, cu=FAKE,
+                 so=None, B=2, T=2, mx=1, mbs=4, h=1, dk=64, dv=64, bs=16, nb=8, dt=1)
+        a.update(kw)
+        return f(a["k"], a["v"], a["kc"], a["vc"], a["t"], a["lb"], a["cu"], a["so"], a["B"],
+                 a["T"], a["mx"], a["mbs"], a["h"], a["dk"], a["dv"], a["bs"], a["nb"], a["dt"],
+                 None)
+    assert call(dt=2) == -3
+    assert call(B=-1) == -2
+    assert call(mx=-1) == -2
+    assert call(mbs=0) == -2
+    assert call(bs=48) == -4
+    assert call(B=70000) == -4
+    assert call(t=None) == -1
+    assert call(cu=None) == -1
+    assert call(vc=FAKE) == -2
+    assert call(k=ctypes.c_void_p(0x100001)) == -5
+    assert call(B=0, k=None) == 0
+    assert call(mx=0, k=None) == 0
+
+
 def test_slot_mapping_rejects():
     L = _lib().lib()
     f = L.pkv_slot_mapping
