@@ -36,7 +36,10 @@ if ROOT not in sys.path:
 
 METRIC = "paged-decode KV-read HBM GB/s (% of peak) + µs/step, Llama-7B-shape B=32, 1 GPU"
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E, vendor figure
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, vendor figure
 DOMINANT_KERNEL = "decode_split_kernel"
+KERNEL_NAME = {"decode": "decode_split_kernel", "mla": "mfma_attn_kernel<0, 512>",
+               "varlen": "mfma_attn_kernel<1, 128>"}
 KERNEL_SOURCES = ["paged_kv_cache_133_amd/csrc/decode.hip", "paged_kv_cache_133_amd/csrc/pkv_device.h"]
 
 
@@ -88,6 +91,18 @@ def read_traffic(workload: str):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def algorithmic_flops(case):
+    """Flops of the attention kernel: 2 (Dqk + Dv) per visible (query row, key) pair."""
+    w = case.w
+    L = case.lens_before.astype("int64")
+    n = case.n_new.astype("int64")
+    if w.mode == "varlen":
+        pairs = int((n * L + n * (n + 1) // 2).sum())          # bottom-right causal
+    else:
+        pairs = int((L + n).sum())                             # decode: every key
+    return pairs * w.num_q_heads * 2 * (w.head_dim + w.head_dim_rope + w.head_dim_v)
 
 
 def algorithmic_bytes(case):
@@ -178,9 +193,6 @@ def main():
 
     pkv.lib()   # fails loudly if the HIP library is missing
     w = wl.WORKLOADS[args.workload]
-    if w.mode == "varlen":
-        print("bench.py times the decode workloads", file=sys.stderr)
-        sys.exit(2)
     dev = torch.device("cuda:0")
     case = wl.make_workload_case(w, seed=args.seed, device=dev)
     kv_bytes, split_bytes, step_bytes = algorithmic_bytes(case)
@@ -215,6 +227,12 @@ def main():
         else:
             v = case.cache_v if r == 0 else case.cache_v.clone()
             pair = (case.new_k, case.new_v, k, v)
+        if w.mode == "varlen":
+            write = _lib.prepare_kv_cache_append(*pair, table, lb, cu, case.max_new, slots)
+            attn = _lib.prepare_varlen(case.q, k, v, table, cu, la, case.max_new, w.scale,
+                                       causal=True, out=out, lse=lse)
+            reps.append((write, attn, None))
+            continue
         if fused and not mla:
             split, combine, _ = _lib.prepare_decode_append(case.q, case.new_k, case.new_v, k, v,
                                                            table, la, case.max_len_after, w.scale,
@@ -267,6 +285,7 @@ def main():
     value = kv_bytes / (ms_step * 1e-3) / 1e9
 
     roofline = None
+    flops = algorithmic_flops(case)
     if events:
         # Second pass of the same K steps with a pair of HIP events around every launch of
         # the dominant kernel, recorded on the stream it runs on (torch's current stream).
@@ -275,13 +294,24 @@ def main():
         torch.cuda.synchronize()
         durs = [a.elapsed_time(b) for a, b in ev]
         split_ms = statistics.mean(durs)
-        achieved = split_bytes / (split_ms * 1e-3) / 1e9
+        gbps = split_bytes / (split_ms * 1e-3) / 1e9
+        tflops = flops / (split_ms * 1e-3) / 1e12
+        # The bound is whichever resource the launch would saturate first at peak.
+        mfma_bound = flops / (PEAK_BF16_TFLOPS * 1e12) > split_bytes / (PEAK_HBM_GBPS * 1e9)
         traffic = read_traffic(w.name)
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                    "traffic": traffic, "kernel": DOMINANT_KERNEL,
-                    "kernel_us": round(split_ms * 1e3, 2),
-                    "algorithmic_bytes_per_launch": split_bytes}
+        kname = KERNEL_NAME["mla" if mla else w.mode if w.mode == "varlen" else "decode"]
+        if mfma_bound:
+            roofline = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+        else:
+            roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                        "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+        roofline.update({"traffic": traffic, "kernel": kname,
+                         "kernel_us": round(split_ms * 1e3, 2),
+                         "algorithmic_bytes_per_launch": split_bytes,
+                         "algorithmic_flops_per_launch": flops,
+                         "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+                         "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)})
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -298,20 +298,35 @@ def prepare_kv_cache_write(k_new, v_new, k_cache, v_cache, slots):
     return PreparedCall(lib().pkv_kv_cache_write, args, (k_new, v_new, k_cache, v_cache, slots))
 
 
+def _varlen_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, max_seqlen_q,
+                 softmax_scale, causal, out, lse):
+    _dev(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, out, lse)
+    T, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    args = (_ptr(out), _ptr(lse), _ptr(q), _ptr(cu_seqlens_q), _ptr(seq_lens_kv), _ptr(k_cache),
+            _ptr(v_cache), _ptr(block_table), seq_lens_kv.shape[0], T, max_seqlen_q,
+            block_table.shape[1], hq, hkv, d, bs, nb, float(softmax_scale), int(bool(causal)),
+            _dtype_code(q), _stream(q.device))
+    return args, out
+
+
 def paged_attn_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                       block_table: torch.Tensor, cu_seqlens_q: torch.Tensor,
                       seq_lens_kv: torch.Tensor, max_seqlen_q: int, softmax_scale: float,
                       causal: bool = True, out: Optional[torch.Tensor] = None,
                       lse: Optional[torch.Tensor] = None):
     """Packed varlen attention over the paged cache (see pkv_paged_attn_varlen)."""
-    _dev(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, out, lse)
-    T, hq, d = q.shape
-    nb, bs, hkv, _ = k_cache.shape
-    if out is None:
-        out = torch.empty_like(q)
-    _check(lib().pkv_paged_attn_varlen(
-        _ptr(out), _ptr(lse), _ptr(q), _ptr(cu_seqlens_q), _ptr(seq_lens_kv), _ptr(k_cache),
-        _ptr(v_cache), _ptr(block_table), seq_lens_kv.shape[0], T, max_seqlen_q,
-        block_table.shape[1], hq, hkv, d, bs, nb, float(softmax_scale), int(bool(causal)),
-        _dtype_code(q), _stream(q.device)))
+    args, out = _varlen_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv,
+                             max_seqlen_q, softmax_scale, causal, out, lse)
+    _check(lib().pkv_paged_attn_varlen(*args))
     return out, lse
+
+
+def prepare_varlen(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, max_seqlen_q,
+                   softmax_scale, causal=True, out=None, lse=None):
+    args, out = _varlen_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv,
+                             max_seqlen_q, softmax_scale, causal, out, lse)
+    return PreparedCall(lib().pkv_paged_attn_varlen, args,
+                        (q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, out, lse))

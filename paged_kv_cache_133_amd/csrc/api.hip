@@ -144,6 +144,8 @@ size_t pkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num
     if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim_v <= 0 ||
         max_seq_len_kv <= 0 || num_q_heads % num_kv_heads)
         return 0;
+    if (num_kv_heads == 1 && head_dim_v == 512)   // the MLA-absorbed shape
+        return pkv::plan_mla(batch, num_q_heads, head_dim_v, max_seq_len_kv).ws_bytes;
     return pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim_v, max_seq_len_kv).ws_bytes;
 }
 
@@ -182,7 +184,7 @@ int prepare_decode(pkv::DecodeParams& p, pkv::DecodePlan& plan, void* out, float
     if (!mla && head_dim_rope != 0)
         return fail(PKV_ERR_SHAPE, "decode: head_dim_rope must be 0 without rope inputs");
     if (mla) {
-        return fail(PKV_ERR_UNSUPPORTED, "decode: the MLA (rope) path is not built yet");
+        return fail(PKV_ERR_UNSUPPORTED, "decode: internal: MLA arguments reached the MHA path");
     }
     const int group = num_q_heads / num_kv_heads;
     if (head_dim_qk != head_dim_v || (head_dim_qk != 64 && head_dim_qk != 128))
@@ -249,6 +251,116 @@ int launch_combine_for(const pkv::DecodeParams& p, int32_t head_dim_v, int32_t d
 
 }  // namespace
 
+namespace {
+
+// MLA-absorbed decode: checks and launch (split pass, then combine when stages ask).
+int run_mla_decode(void* out, float* lse_out, const void* q, const void* q_rope,
+                   const void* k_cache, const void* v_cache, const void* k_rope_cache,
+                   const int32_t* block_table, const int32_t* seq_lens_kv, int32_t batch,
+                   int32_t max_blocks_per_seq, int32_t max_seq_len_kv, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim_qk, int32_t head_dim_v,
+                   int32_t head_dim_rope, int32_t block_size, int64_t num_blocks,
+                   float softmax_scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+                   int stages, hipStream_t s) {
+    if (num_kv_heads != 1 || head_dim_qk != 512 || head_dim_v != 512 || head_dim_rope != 64)
+        return fail(PKV_ERR_UNSUPPORTED,
+                    "decode (MLA): needs 1 kv head, head_dim_qk = head_dim_v = 512, head_dim_rope = 64");
+    if (dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "decode (MLA): bf16 only");
+    if (v_cache != k_cache)
+        return fail(PKV_ERR_UNSUPPORTED, "decode (MLA): v_cache must be k_cache (value = cache_nope)");
+    if (batch == 0) return PKV_OK;
+    if (!out || !q || !k_cache || !block_table || !seq_lens_kv)
+        return fail(PKV_ERR_NULL, "decode: NULL pointer argument");
+    if (!aligned16(out) || !aligned16(q) || !aligned16(q_rope) || !aligned16(k_cache) ||
+        !aligned16(k_rope_cache))
+        return fail(PKV_ERR_ALIGN, "decode: out, q, q_rope and caches must be 16-byte aligned");
+    const pkv::DecodePlan plan = pkv::plan_mla(batch, num_q_heads, head_dim_v, max_seq_len_kv);
+    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))
+        return fail(PKV_ERR_WORKSPACE, "decode: workspace needs %zu bytes (16-byte aligned), got %zu",
+                    plan.ws_bytes, workspace ? workspace_bytes : (size_t)0);
+    const int64_t hgs = pkv::mla_head_groups(num_q_heads);
+    if (hgs * ((int64_t)batch * plan.max_splits + 7) > 0x7fffffffLL)
+        return fail(PKV_ERR_SHAPE, "decode: grid too large");
+    pkv::MfmaParams p{};
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    p.out = out;
+    p.lse = lse_out;
+    p.q = q;
+    p.q_rope = q_rope;
+    p.k_cache = k_cache;
+    p.v_cache = nullptr;
+    p.k_rope = k_rope_cache;
+    p.table = block_table;
+    p.seq_lens = seq_lens_kv;
+    p.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.ws_o_offset) : nullptr;
+    p.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.ws_ml_offset) : nullptr;
+    p.batch = batch;
+    p.mbs = max_blocks_per_seq;
+    p.hq = num_q_heads;
+    p.hkv = 1;
+    p.group = num_q_heads;
+    p.bs_log2 = log2i(block_size);
+    p.split_tokens = plan.split_tokens;
+    p.max_splits = plan.max_splits;
+    p.len_cap = max_seq_len_kv;
+    p.num_blocks = num_blocks;
+    p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+    int rc = PKV_OK;
+    if (stages & 1) {
+        rc = hip_status(pkv::launch_mla_decode(p, s), "decode (MLA) launch");
+        if (rc != PKV_OK) return rc;
+    }
+    if ((stages & 2) && plan.max_splits > 1) {
+        pkv::CombineParams c{};
+        c.out = out;
+        c.lse = lse_out;
+        c.ws_o = p.ws_o;
+        c.ws_ml = p.ws_ml;
+        c.seq_lens = seq_lens_kv;
+        c.batch = batch;
+        c.hq = num_q_heads;
+        c.dim = head_dim_v;
+        c.split_tokens = plan.split_tokens;
+        c.max_splits = plan.max_splits;
+        c.len_cap = max_seq_len_kv;
+        rc = hip_status(pkv::launch_combine(c, dtype, s), "decode (MLA) combine launch");
+    }
+    return rc;
+}
+
+// Checks common to every decode entry before the MHA/MLA split.  Returns PKV_OK and sets
+// *mla when the rope inputs select the MLA path.
+int check_decode_common(const void* q_rope, const void* k_rope_cache, int32_t dtype, int32_t batch,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim_qk,
+                        int32_t head_dim_v, int32_t head_dim_rope, int32_t max_blocks_per_seq,
+                        int32_t max_seq_len_kv, int32_t block_size, int64_t num_blocks,
+                        float softmax_scale, bool* mla) {
+    *mla = false;
+    if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "decode: unknown dtype %d", dtype);
+    if (batch < 0) return fail(PKV_ERR_SHAPE, "decode: negative batch");
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+        return fail(PKV_ERR_SHAPE, "decode: num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                    num_q_heads, num_kv_heads);
+    if (head_dim_qk <= 0 || head_dim_v <= 0 || head_dim_rope < 0 || max_blocks_per_seq <= 0 ||
+        num_blocks <= 0)
+        return fail(PKV_ERR_SHAPE, "decode: head dims, max_blocks_per_seq and num_blocks must be positive");
+    if (!pow2_in(block_size, 1, 256))
+        return fail(PKV_ERR_UNSUPPORTED, "decode: block_size %d is not a power of two in [1, 256]", block_size);
+    if ((int64_t)max_seq_len_kv > (int64_t)max_blocks_per_seq * block_size || max_seq_len_kv <= 0)
+        return fail(PKV_ERR_SHAPE, "decode: max_seq_len_kv %d must be in [1, max_blocks_per_seq * block_size]",
+                    max_seq_len_kv);
+    if (!isfinite(softmax_scale) || !(softmax_scale > 0.0f))
+        return fail(PKV_ERR_SCALE, "decode: softmax_scale must be finite and > 0");
+    if ((q_rope == nullptr) != (k_rope_cache == nullptr))
+        return fail(PKV_ERR_NULL, "decode: q_rope and k_rope_cache must be given together or not at all");
+    *mla = q_rope != nullptr;
+    if (!*mla && head_dim_rope != 0)
+        return fail(PKV_ERR_SHAPE, "decode: head_dim_rope must be 0 without rope inputs");
+    return PKV_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 #define PKV_DECODE_ARGS                                                                    \
@@ -265,10 +377,16 @@ int pkv_paged_attn_decode(void* out, float* lse_out, const void* q, const void* 
                           int32_t head_dim_v, int32_t head_dim_rope, int32_t block_size,
                           int64_t num_blocks, float softmax_scale, int32_t dtype,
                           void* workspace, size_t workspace_bytes, void* stream) {
+    bool mla = false;
+    int rc = check_decode_common(q_rope, k_rope_cache, dtype, batch, num_q_heads, num_kv_heads,
+                                 head_dim_qk, head_dim_v, head_dim_rope, max_blocks_per_seq,
+                                 max_seq_len_kv, block_size, num_blocks, softmax_scale, &mla);
+    if (rc != PKV_OK) return rc;
+    if (mla) return run_mla_decode(PKV_DECODE_ARGS, 3, (hipStream_t)stream);
     pkv::DecodeParams p;
     pkv::DecodePlan plan{};
     bool idle = false;
-    int rc = prepare_decode(p, plan, PKV_DECODE_ARGS, &idle);
+    rc = prepare_decode(p, plan, PKV_DECODE_ARGS, &idle);
     if (rc != PKV_OK || idle) return rc;
     hipStream_t s = (hipStream_t)stream;
     rc = hip_status(pkv::launch_decode(p, dtype, head_dim_qk, s), "decode split launch");
@@ -285,10 +403,16 @@ int pkv_paged_attn_decode_split(void* out, float* lse_out, const void* q, const 
                                 int32_t head_dim_v, int32_t head_dim_rope, int32_t block_size,
                                 int64_t num_blocks, float softmax_scale, int32_t dtype,
                                 void* workspace, size_t workspace_bytes, void* stream) {
+    bool mla = false;
+    int rc = check_decode_common(q_rope, k_rope_cache, dtype, batch, num_q_heads, num_kv_heads,
+                                 head_dim_qk, head_dim_v, head_dim_rope, max_blocks_per_seq,
+                                 max_seq_len_kv, block_size, num_blocks, softmax_scale, &mla);
+    if (rc != PKV_OK) return rc;
+    if (mla) return run_mla_decode(PKV_DECODE_ARGS, 1, (hipStream_t)stream);
     pkv::DecodeParams p;
     pkv::DecodePlan plan{};
     bool idle = false;
-    int rc = prepare_decode(p, plan, PKV_DECODE_ARGS, &idle);
+    rc = prepare_decode(p, plan, PKV_DECODE_ARGS, &idle);
     if (rc != PKV_OK || idle) return rc;
     return hip_status(pkv::launch_decode(p, dtype, head_dim_qk, (hipStream_t)stream),
                       "decode split launch");
@@ -304,10 +428,16 @@ int pkv_paged_attn_decode_combine(void* out, float* lse_out, const void* q, cons
                                   int32_t head_dim_rope, int32_t block_size, int64_t num_blocks,
                                   float softmax_scale, int32_t dtype, void* workspace,
                                   size_t workspace_bytes, void* stream) {
+    bool mla = false;
+    int rc = check_decode_common(q_rope, k_rope_cache, dtype, batch, num_q_heads, num_kv_heads,
+                                 head_dim_qk, head_dim_v, head_dim_rope, max_blocks_per_seq,
+                                 max_seq_len_kv, block_size, num_blocks, softmax_scale, &mla);
+    if (rc != PKV_OK) return rc;
+    if (mla) return run_mla_decode(PKV_DECODE_ARGS, 2, (hipStream_t)stream);
     pkv::DecodeParams p;
     pkv::DecodePlan plan{};
     bool idle = false;
-    int rc = prepare_decode(p, plan, PKV_DECODE_ARGS, &idle);
+    rc = prepare_decode(p, plan, PKV_DECODE_ARGS, &idle);
     if (rc != PKV_OK || idle || plan.max_splits <= 1) return rc;
     return launch_combine_for(p, head_dim_v, dtype, (hipStream_t)stream);
 }
@@ -357,11 +487,54 @@ int pkv_paged_attn_varlen(void* out, float* lse_out, const void* q, const int32_
                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                           int64_t num_blocks, float softmax_scale, int32_t causal, int32_t dtype,
                           void* stream) {
-    (void)out; (void)lse_out; (void)q; (void)cu_seqlens_q; (void)seq_lens_kv; (void)k_cache;
-    (void)v_cache; (void)block_table; (void)batch; (void)total_q; (void)max_seqlen_q;
-    (void)max_blocks_per_seq; (void)num_q_heads; (void)num_kv_heads; (void)head_dim;
-    (void)block_size; (void)num_blocks; (void)softmax_scale; (void)causal; (void)dtype; (void)stream;
-    return fail(PKV_ERR_UNSUPPORTED, "varlen: not built yet");
+    if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "varlen: unknown dtype %d", dtype);
+    if (batch < 0 || total_q < 0 || max_seqlen_q < 0)
+        return fail(PKV_ERR_SHAPE, "varlen: negative batch, total_q or max_seqlen_q");
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+        return fail(PKV_ERR_SHAPE, "varlen: num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                    num_q_heads, num_kv_heads);
+    if (max_blocks_per_seq <= 0 || num_blocks <= 0 || head_dim <= 0)
+        return fail(PKV_ERR_SHAPE, "varlen: head_dim, max_blocks_per_seq and num_blocks must be positive");
+    if (!isfinite(softmax_scale) || !(softmax_scale > 0.0f))
+        return fail(PKV_ERR_SCALE, "varlen: softmax_scale must be finite and > 0");
+    if (!pow2_in(block_size, 1, 256))
+        return fail(PKV_ERR_UNSUPPORTED, "varlen: block_size %d is not a power of two in [1, 256]", block_size);
+    if (dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "varlen: bf16 only");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PKV_ERR_UNSUPPORTED, "varlen: head_dim %d not supported (64 or 128)", head_dim);
+    const int group = num_q_heads / num_kv_heads;
+    if (group > 16) return fail(PKV_ERR_UNSUPPORTED, "varlen: %d query heads per kv head (max 16)", group);
+    if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return PKV_OK;
+    if (!out || !q || !cu_seqlens_q || !seq_lens_kv || !k_cache || !v_cache || !block_table)
+        return fail(PKV_ERR_NULL, "varlen: NULL pointer argument");
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PKV_ERR_ALIGN, "varlen: out, q and caches must be 16-byte aligned");
+    const int tpb = pkv::varlen_tokens_per_block(group);
+    const int64_t qblocks = (max_seqlen_q + tpb - 1) / tpb;
+    if ((int64_t)num_kv_heads * qblocks * batch > 0x7fffffffLL)
+        return fail(PKV_ERR_SHAPE, "varlen: grid too large");
+    pkv::MfmaParams p{};
+    p.out = out;
+    p.lse = lse_out;
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.table = block_table;
+    p.seq_lens = seq_lens_kv;
+    p.cu_q = cu_seqlens_q;
+    p.batch = batch;
+    p.mbs = max_blocks_per_seq;
+    p.hq = num_q_heads;
+    p.hkv = num_kv_heads;
+    p.group = group;
+    p.bs_log2 = log2i(block_size);
+    p.len_cap = (int32_t)((int64_t)max_blocks_per_seq * block_size > 0x7fffffffLL
+                              ? 0x7fffffff : (int64_t)max_blocks_per_seq * block_size);
+    p.q_blocks = (int32_t)qblocks;
+    p.causal = causal ? 1 : 0;
+    p.num_blocks = num_blocks;
+    p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+    return hip_status(pkv::launch_varlen(p, head_dim, (hipStream_t)stream), "varlen launch");
 }
 
 }  // extern "C"

@@ -19,12 +19,9 @@ struct bf16_t { uint16_t bits; };  // storage tag for bf16 tensors
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN).
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32; NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // 2-term bf16 dot product accumulated in fp32 (v_dot2_f32_bf16).

@@ -103,4 +103,39 @@ struct CombineParams {
 };
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t s);
 
+// ------------------------------------------------------------------ MFMA attention
+// One core for the two dense-contraction paths: the MLA-absorbed decode (rows = query
+// heads of one token, key = nope || rope, value = nope) and the packed varlen causal
+// chunk (rows = (query token, query head) pairs of one kv head).  Rows are grouped 32 per
+// wave, 4 waves per workgroup; the workgroup walks a key range in 32-key tiles.
+struct MfmaParams {
+    void* out;               // [rows][Dv] in q's dtype (decode: [B][Hq][Dv]; varlen: [T][Hq][Dv])
+    float* lse;              // [rows] or null
+    const void* q;           // [.., Hq, Dqk main part]
+    const void* q_rope;      // MLA: [B][Hq][Dr]; else null
+    const void* k_cache;     // [nb][bs][Hkv][Dk]
+    const void* v_cache;     // varlen: [nb][bs][Hkv][Dv]; MLA: unused (value = nope part of K)
+    const void* k_rope;      // MLA: [nb][bs][1][Dr]
+    const int32_t* table;
+    const int32_t* seq_lens;  // L'_b
+    const int32_t* cu_q;      // varlen: [B+1]
+    float* ws_o;             // MLA splits: [B][Hq][max_splits][Dv]
+    float* ws_ml;            // [B][Hq][max_splits][2]
+    int32_t batch, mbs, hq, hkv, group;
+    int32_t bs_log2;
+    int32_t split_tokens, max_splits;   // MLA
+    int32_t len_cap;
+    int32_t q_blocks;        // varlen: query blocks per sequence in the grid
+    int32_t causal;
+    int64_t num_blocks;
+    float scale_log2;
+};
+// MLA decode: Dqk = 512 + Dr 64, Dv = 512, bf16.  Returns the launch status.
+DecodePlan plan_mla(int32_t batch, int32_t num_q_heads, int32_t head_dim_v, int32_t max_seq_len_kv);
+int32_t mla_head_groups(int32_t num_q_heads);
+hipError_t launch_mla_decode(const MfmaParams& p, hipStream_t s);
+// Varlen chunk: head_dim 64 or 128, bf16.
+hipError_t launch_varlen(const MfmaParams& p, int head_dim, hipStream_t s);
+int32_t varlen_tokens_per_block(int32_t group);
+
 }  // namespace pkv

@@ -11,6 +11,12 @@ from tests.helpers import case_numpy, host
 
 # Tolerances on outputs (max-abs, fp32 accumulation on the GPU)
 ATOL = {"f32": 1e-5, "bf16": 2e-2}
+# lse: the MHA/GQA decode keeps softmax weights in fp32 (relative 1e-4 covers fp32 sums);
+# the MFMA paths (MLA, varlen) feed bf16-rounded weights to the matrix cores and sum the
+# same rounded weights, each within 2^-9 relative of the exact one, so ln(sum) may move
+# by up to 2^-9 ~ 1.95e-3: allow 4e-3 absolute there.
+LSE_REL_DECODE = 1e-4
+LSE_ABS_MFMA = 4e-3
 
 
 def say(msg):
@@ -89,8 +95,13 @@ def compare_outputs(c, g, o, tokens=None, label=""):
     assert emax <= ATOL[w.dtype], (f"{label}: max-abs error {emax:.3e} > {ATOL[w.dtype]} at "
                                    f"(row, head, d) = {worst}")
     if lse is not None:
-        lerr = np.abs(lse - o["lse"]) / np.maximum(1.0, np.abs(o["lse"]))
-        assert float(lerr.max()) <= 1e-4, f"{label}: lse error {float(lerr.max()):.3e}"
+        if w.mode == "decode":
+            lerr = np.abs(lse - o["lse"]) / np.maximum(1.0, np.abs(o["lse"]))
+            bound = LSE_REL_DECODE
+        else:
+            lerr = np.abs(lse - o["lse"])
+            bound = LSE_ABS_MFMA
+        assert float(lerr.max()) <= bound, f"{label}: lse error {float(lerr.max()):.3e} > {bound}"
     return emax
 
 

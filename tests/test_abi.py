@@ -167,12 +167,45 @@ def test_slot_mapping_rejects():
     assert f(None, None, None, None, 0, 0, 4, 16, None) == 0
 
 
-def test_varlen_rejects_bad_arguments():
-    L = _lib().lib()
-    f = L.pkv_paged_attn_varlen
-    rc = f(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 4, 4, 4, 1, 64, 16, 32,
-           float("nan"), 1, 1, None)
-    assert rc != 0
+def test_mla_decode_rejects():
+    L = _lib()
+    mla = dict(q_rope=FAKE, kr=FAKE, hq=128, hkv=1, dqk=512, dv=512, dr=64, dtype=1, bs=128,
+               mbs=64, maxlen=8192)
+    assert decode(L, **dict(mla, dtype=0)) == -4            # fp32 MLA not built
+    assert decode(L, **dict(mla, dr=32)) == -4              # rope width must be 64
+    assert decode(L, **dict(mla, dqk=128, dv=128)) == -4
+    assert decode(L, **dict(mla, hkv=2, hq=128)) == -4
+    assert decode(L, **dict(mla, v=ctypes.c_void_p(0x300000))) == -4   # value must be cache_nope
+    assert decode(L, **dict(mla, ws=None)) == -7
+    assert decode(L, **dict(mla, out=None)) == -1
+    assert decode(L, **dict(mla, B=0)) == 0
+
+
+def varlen(L, **kw):
+    a = dict(out=FAKE, lse=None, q=FAKE, cu=FAKE, lens=FAKE, k=FAKE, v=FAKE, t=FAKE, B=2, T=8,
+             maxq=4, mbs=4, hq=4, hkv=1, d=64, bs=16, nb=32, scale=0.125, causal=1, dtype=1)
+    a.update(kw)
+    return L.lib().pkv_paged_attn_varlen(a["out"], a["lse"], a["q"], a["cu"], a["lens"], a["k"],
+                                         a["v"], a["t"], a["B"], a["T"], a["maxq"], a["mbs"],
+                                         a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"],
+                                         a["causal"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=4), -3), (dict(dtype=0), -4), (dict(d=96), -4), (dict(hq=34, hkv=2), -4),
+    (dict(hq=6, hkv=4), -2), (dict(B=-1), -2), (dict(scale=float("nan")), -6),
+    (dict(scale=-2.0), -6), (dict(bs=3), -4), (dict(q=None), -1), (dict(cu=None), -1),
+    (dict(out=ctypes.c_void_p(0x100008)), -5), (dict(mbs=0), -2),
+])
+def test_varlen_rejects(kw, code):
+    L = _lib()
+    assert varlen(L, **kw) == code, L.lib().pkv_last_error()
+
+
+def test_varlen_empty_is_ok():
+    L = _lib()
+    assert varlen(L, B=0, out=None, q=None) == 0
+    assert varlen(L, T=0, out=None, q=None) == 0
 
 
 def test_binding_refuses_cpu_tensors():
