@@ -18,14 +18,15 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.hip", "write.hip", "decode.hip", "mfma_attn.hip"]
+SOURCES = ["api.hip", "write.hip", "decode.hip", "mla_attn.hip", "varlen_attn.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]
 # The MFMA attention kernels keep their accumulators in ordinary VGPRs: with the default
 # choice (AGPRs) the online-softmax rescale copies every accumulator out and back each tile.
-EXTRA = {"mfma_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"varlen_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "mla_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

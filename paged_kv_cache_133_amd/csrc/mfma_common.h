@@ -1,0 +1,141 @@
+// Device pieces shared by the MFMA attention kernels for gfx950 (MLA-absorbed decode
+// and packed varlen chunk): vector types, the explicit wait and barrier of the tile
+// pipeline, loads from global memory straight into LDS, transposing LDS reads, the
+// block-table chunks staged in LDS, and the chunk swizzle of unpadded LDS rows.
+//
+// Tile pipeline.  The K/V rows of a tile of 32 keys go from global memory straight into
+// LDS (global_load_lds_dwordx4: each lane names its own 16-byte source, the destination
+// is 16 bytes per lane after a wave-uniform base), into one of four LDS stages, three
+// tiles ahead of the tile being computed: no registers hold data in flight, so the loads
+// of three tiles overlap the math.  Their completion is waited for explicitly (the
+// vector-memory counter, per wave) followed by one workgroup barrier per tile.  The
+// block-table entries of the next 1024 keys are staged in LDS 512 keys before they are
+// needed, so no load of the table sits in the in-order counter between the K/V loads.
+// Keys past the range are read from the range's last key (a real, finite row) and get
+// weight 0.
+#pragma once
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace mfma {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2f = 0.69314718055994530942f;
+constexpr float kRescaleSlack = 8.0f;           // log2 units a row max may grow before rescaling
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // bf16 pair (1, 1)
+constexpr int kKeys = 32;                       // keys per tile
+constexpr int kStages = 4;                      // LDS stages of the tile pipeline
+constexpr int kChunkTiles = 32;                 // tiles per staged chunk of the block table
+constexpr int kChunkKeys = kChunkTiles * kKeys;
+constexpr int kTabEntries = kChunkKeys + 16;    // entries per chunk buffer (>= 1024 + 1)
+
+// s_waitcnt immediate (gfx9 layout): vmcnt in bits 3:0 and 15:14, expcnt in 6:4,
+// lgkmcnt in 11:8; expcnt and lgkmcnt at their maxima do not wait.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Wait for this wave's loads into LDS of tile t, with n in {0, 1, 2} later tiles (each
+// of at least PER loads) allowed to stay in flight.
+template <int PER>
+__device__ __forceinline__ void wait_tile(int n) {
+    static_assert(kStages == 4, "waits cover up to two later tiles");
+    if (n >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * PER));
+    else if (n == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
+// Workgroup barrier after this wave's LDS writes have completed.  No memory fence: a
+// fence would also wait for the loads still in flight into LDS.
+__device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// 16 bytes per lane from src into LDS at lds_base + 16 * lane (lds_base wave-uniform, in
+// M0).  Written as inline asm on purpose: the compiler then does not know that LDS is
+// written here and does not make every later LDS read wait for all of these loads (it
+// cannot tell the stages of one LDS array apart); the kernels wait for them explicitly.
+// s_nop: an SALU write of M0 needs one wait state before a load that writes LDS.
+__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds_base) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_base;
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m0) : "memory");
+}
+
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit offset per lane (the
+// saddr form), for loads whose addresses differ from lane to lane only by constants.
+// s_nop 4: an SGPR or M0 written by a VALU instruction needs five wait states before a
+// vector-memory instruction reads it.
+__device__ __forceinline__ void lds_dma16_s(const uint8_t* sbase, uint32_t voff, uint8_t* lds_base) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_base;
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+
+// Read of a wave-uniform int32 through the scalar data cache (a load from the constant
+// address space; p must be the same in every lane).
+__device__ __forceinline__ int32_t uniform_load(const int32_t* p) {
+    return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(reinterpret_cast<uintptr_t>(p));
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr(const uint8_t* lds_addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(lds_addr));
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
+}
+
+// ------------------------------------------------------------------ block-table chunks
+// Chunk c holds the entries of keys [k_begin + 1024 c, k_begin + 1024 (c + 1)) in LDS
+// buffer c & 1.  Entries are loaded into registers when the chunk before it starts to
+// be used and stored 16 tiles later; the barrier of every tile publishes them.
+template <int NT>
+struct TableChunks {
+    static constexpr int kRegs = (kChunkKeys + 1 + NT - 1) / NT;
+    int32_t* lds;            // [2][kTabEntries]
+    const int32_t* row;      // this sequence's block-table row
+    int k_begin, k_end, bs_log2, tid;
+    int32_t last_block;
+
+    __device__ int first_entry(int c) const { return (k_begin + c * kChunkKeys) >> bs_log2; }
+    __device__ bool exists(int c) const { return k_begin + c * kChunkKeys < k_end; }
+    __device__ void load(int c, int32_t* regs) const {
+        const int e0 = first_entry(c);
+        const int e1 = (min(k_end, k_begin + (c + 1) * kChunkKeys) - 1) >> bs_log2;
+#pragma unroll
+        for (int j = 0; j < kRegs; ++j) regs[j] = row[min(e0 + tid + j * NT, e1)];
+    }
+    __device__ void store(int c, const int32_t* regs) const {
+        int32_t* dst = lds + (c & 1) * kTabEntries;
+#pragma unroll
+        for (int j = 0; j < kRegs; ++j)
+            if (tid + j * NT < kTabEntries) dst[tid + j * NT] = min(max(regs[j], 0), last_block);
+    }
+    // Physical block of key (all keys of one tile lie in one chunk).
+    __device__ uint32_t block_of(int key, int chunk) const {
+        return (uint32_t)lds[(chunk & 1) * kTabEntries + (key >> bs_log2) - first_entry(chunk)];
+    }
+};
+
+// ------------------------------------------------------------------ online softmax state
+struct RowState {
+    float m = -INFINITY;     // running max (log2 units), equal in every lane of the row
+    float l = 0.0f;          // this lane's part of the running sum
+};
+
+// Physical 16-byte chunk of logical chunk c in LDS row r (an involution).  Rows sharing
+// a 256-byte bank line (x = r >> SHIFT) get distinct XOR patterns: 16 consecutive rows
+// land on 16 different chunks, and any 4 consecutive rows map a chunk pair {2i, 2i+1}
+// to 8 different chunks.
+template <int CPR, int SHIFT>
+__device__ __forceinline__ int swz(int r, int c) {
+    const int x = r >> SHIFT;
+    return c ^ ((2 * (x & (CPR / 2 - 1))) ^ ((x / (CPR / 2)) & 1));
+}
+
+}  // namespace mfma
+}  // namespace pkv

@@ -1,0 +1,363 @@
+// MLA-absorbed decode over the paged cache with MFMA for gfx950 ("KVCache Optimization
+// Skill", Mode 3: key = cache_nope || cache_rope, value = cache_nope, rope passed
+// separately): all query heads of a sequence share one latent head, so a tile of keys
+// read once serves every head.
+//
+// A workgroup of four waves owns 64 heads (16 per wave) of one (sequence, split) and walks
+// its keys in tiles of 32 (the tile pipeline of mfma_common.h), each wave over the whole
+// 576-wide contraction, with v_mfma_f32_16x16x32_bf16.  The two head groups of 128 heads
+// are launched onto the same XCD so that the second read of a K tile comes from its L2.
+//  * S^T (16 keys x 16 heads, two per tile) = K . Q^T: K rows from LDS as the A operand,
+//    Q^T of the wave's 16 heads in registers as the B operand (72 registers);
+//  * lane (g, n) (g = lane / 16) holds 8 keys of head n: the head's max and sum take two
+//    cross-lane steps, and P^T (bf16) is the B operand of the next product with k-slot
+//    8 g + 4 h + r standing for accumulator entry r of key half h;
+//  * O^T (512 x 16 heads, 128 registers) += V^T . P^T, the A operand built by two
+//    ds_read_b64_tr_b16 per product (four keys at one value column per lane and read)
+//    from the nope part of the same LDS rows;
+//  * O^T keeps one head per lane column, so the online-softmax rescale is lane-local; it
+//    is applied only when a head's max grows by more than 2^8 (P <= 256 in between),
+//    which after the first tiles almost never happens.  Full tiles skip the masking.
+// One wave per SIMD: O^T lives in VGPRs (the rescale multiplies it in place) and Q^T in
+// the accumulation registers.
+#include "mfma_common.h"
+
+namespace pkv {
+
+namespace {
+
+using namespace mfma;
+
+struct MlaCfg {
+    static constexpr int kWaves = 4;
+    static constexpr int kThreads = kWaves * 64;
+    static constexpr int kHeads = kWaves * 16;              // query heads per workgroup
+    // LDS stage: 32 nope rows of 1024 bytes padded to 1040 (one wave load each), then 32
+    // rope rows of 128 bytes (eight per wave load) with their chunks XOR-swizzled by row.
+    static constexpr int kNopeRow = 1024 + 16;
+    static constexpr int kRopeBase = kKeys * kNopeRow;
+    static constexpr int kStage = kRopeBase + kKeys * 128;
+    static constexpr int kDma = kKeys / kWaves + 1;         // wave loads per tile: 8 nope + 1 rope
+    static constexpr int kSteps = 576 / 32;                 // S^T k-steps (16 nope, 2 rope)
+    static constexpr int kDTiles = 512 / 16;                // 16-row tiles of O^T
+    static constexpr int kSmem = kStages * kStage + 2 * kTabEntries * 4;
+    static_assert(kSmem <= 160 * 1024, "LDS");
+    static_assert(kKeys * 128 == kWaves * 1024, "one rope load per wave");
+};
+
+// LDS row (within a 16-key half) of the key behind accumulator row 4 g + r: the four keys
+// of one transposing read (r = 0..3) sit two LDS rows apart, which with 16-byte row
+// padding puts both the 16-row K reads and the 4-row V reads on distinct banks.
+__device__ __forceinline__ int mla_row(int g, int r) { return (g & 2) * 4 + (g & 1) + 2 * r; }
+// Physical 16-byte chunk of rope chunk c in rope row r.
+__device__ __forceinline__ int rope_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+__global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams p) {
+    using C = MlaCfg;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::kSmem];
+
+    const int tid = threadIdx.x;
+    const int wid = tid >> 6;
+    const int lane = tid & 63;
+    const int n = lane & 15;          // head of this lane inside the wave; A-operand row
+    const int g = lane >> 4;          // k-slot group
+
+    // Workgroups are dealt to the 8 XCDs round-robin; the head groups of one work unit
+    // take ids that differ by a multiple of 8 and follow each other on one XCD.
+    const int hgs = (p.hq + C::kHeads - 1) / C::kHeads;
+    const int id = blockIdx.x;
+    const int hg = (id >> 3) % hgs;
+    const int unit = ((id >> 3) / hgs) * 8 + (id & 7);
+    const int b = unit % p.batch;
+    const int split = unit / p.batch;
+    if (split >= p.max_splits) return;
+    const int L = min(p.seq_lens[b], p.len_cap);
+    const int k_begin = split * p.split_tokens;
+    if (k_begin >= L) return;
+    const int k_end = min(L, k_begin + p.split_tokens);
+    const int ntiles = (k_end - k_begin + kKeys - 1) / kKeys;
+
+    const int head = hg * C::kHeads + wid * 16 + n;
+    const bool valid = head < p.hq;
+    const int64_t row = (int64_t)b * p.hq + min(head, p.hq - 1);
+
+    // Q^T fragments: k-step s covers dims 32 s .. 32 s + 31; this lane holds 8 of them.
+    bf16x8_t qf[C::kSteps];
+    {
+        const uint8_t* qn = reinterpret_cast<const uint8_t*>(p.q) + row * 512 * 2;
+        const uint8_t* qr = reinterpret_cast<const uint8_t*>(p.q_rope) + row * 64 * 2;
+#pragma unroll
+        for (int s = 0; s < C::kSteps; ++s) {
+            const int dim = 32 * s + 8 * g;
+            qf[s] = __builtin_bit_cast(bf16x8_t, ld16(dim < 512 ? qn + dim * 2 : qr + (dim - 512) * 2));
+            // Keep Q^T in the accumulation registers (the products read their B operand
+            // from there directly), leaving the VGPRs to O^T and the operands in flight.
+            asm volatile("" : "+a"(qf[s]));
+        }
+    }
+
+    TableChunks<C::kThreads> tab;
+    tab.lds = reinterpret_cast<int32_t*>(smem + kStages * C::kStage);
+    tab.row = p.table + (int64_t)b * p.mbs;
+    tab.k_begin = k_begin;
+    tab.k_end = k_end;
+    tab.bs_log2 = p.bs_log2;
+    tab.tid = tid;
+    tab.last_block = (int32_t)(p.num_blocks - 1);
+    int32_t treg[TableChunks<C::kThreads>::kRegs];
+    tab.load(0, treg);
+    tab.store(0, treg);
+    // Q and the first chunk must be resident before the loop: otherwise the wait for
+    // them, placed inside the loop, would also wait for the tile loads issued there.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    block_sync();
+
+    // Loads of one tile: wave w fills nope rows 8 w .. 8 w + 7 (one load per row, lane =
+    // 16-byte chunk; the row's slot is the same for the whole wave) and rope rows
+    // 8 w .. 8 w + 7 (one load, lane = row 8 w + lane / 8, physical chunk lane % 8).
+    const int bs_mask = (1 << p.bs_log2) - 1;
+    const uint32_t nope_block = (uint32_t)(1024u << p.bs_log2);   // bytes per block
+    const uint32_t rope_block = (uint32_t)(128u << p.bs_log2);
+    const uint8_t* nope_src = reinterpret_cast<const uint8_t*>(p.k_cache) + lane * 16;
+    const int rope_r = wid * 8 + (lane >> 3);
+    const uint8_t* rope_src = reinterpret_cast<const uint8_t*>(p.k_rope) + rope_chunk(rope_r, lane & 7) * 16;
+    // Full tiles with blocks of at least 8 keys: the wave's 8 rows are consecutive slots of
+    // one block, found with one scalar read of the block table; every load then uses that
+    // row base in SGPRs and a constant offset per lane.
+    const int wid_u = __builtin_amdgcn_readfirstlane(wid);
+    const bool fast_rows = p.bs_log2 >= 3;
+    const uint32_t rope_voff = (uint32_t)((lane >> 3) * 128 + rope_chunk(rope_r, lane & 7) * 16);
+    auto issue_tile = [&](int u) {
+        const int kb = k_begin + u * kKeys;
+        const int chunk = u / kChunkTiles;
+        uint8_t* stage = smem + (u % kStages) * C::kStage;
+        if (fast_rows && kb + kKeys <= k_end) {
+            const int key0 = kb + 8 * wid_u;
+            const int32_t blk = min(max(uniform_load(tab.row + (key0 >> p.bs_log2)), 0), tab.last_block);
+            const uint64_t slot0 = ((uint64_t)(uint32_t)blk << p.bs_log2) | (uint32_t)(key0 & bs_mask);
+            const uint8_t* nb = reinterpret_cast<const uint8_t*>(p.k_cache) + slot0 * 1024u;
+#pragma unroll
+            for (int j = 0; j < kKeys / C::kWaves; ++j)
+                lds_dma16_s(nb + j * 1024, (uint32_t)lane * 16u, stage + (8 * wid_u + j) * C::kNopeRow);
+            lds_dma16_s(reinterpret_cast<const uint8_t*>(p.k_rope) + slot0 * 128u, rope_voff,
+                        stage + C::kRopeBase + wid_u * 1024);
+            return;
+        }
+#pragma unroll
+        for (int j = 0; j < kKeys / C::kWaves; ++j) {
+            const int r = wid * (kKeys / C::kWaves) + j;
+            const int key = min(kb + r, k_end - 1);
+            const uint32_t blk = __builtin_amdgcn_readfirstlane(tab.block_of(key, chunk));
+            lds_dma16(nope_src + ((uint64_t)blk * nope_block + (uint32_t)(key & bs_mask) * 1024u),
+                      stage + r * C::kNopeRow);
+        }
+        const int key = min(kb + rope_r, k_end - 1);
+        const uint32_t blk = tab.block_of(key, chunk);
+        lds_dma16(rope_src + ((uint64_t)blk * rope_block + (uint32_t)(key & bs_mask) * 128u),
+                  stage + C::kRopeBase + wid * 1024);
+    };
+
+    // S^T reads: A-operand row n of key half h is LDS row 16 h + mla_row(n / 4, n % 4);
+    // k-step s < 16 reads nope chunk 4 s + g, k-step 16 + i rope chunk 4 i + g.
+    const int krow = mla_row(n >> 2, n & 3);
+    int k_off[2], rope_off[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = 16 * h + krow;
+        k_off[h] = r * C::kNopeRow + 16 * g;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) rope_off[h][i] = C::kRopeBase + r * 128 + rope_chunk(r, 4 * i + g) * 16;
+    }
+    // O^T reads: lane (g, n) reads LDS rows 16 h + mla_row(g, n / 4), value columns
+    // 16 dt + 4 (n % 4) .. + 3.
+    int v_off[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) v_off[h] = (16 * h + mla_row(g, n >> 2)) * C::kNopeRow + 8 * (n & 3);
+
+    RowState st;
+    f32x4 oacc[C::kDTiles];
+#pragma unroll
+    for (int dt = 0; dt < C::kDTiles; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Scores of tile t: full tiles keep the raw S^T entries; the last tile of a range scales
+    // them and sets keys past the range (and all keys of heads past num_q_heads) to -inf.
+    // Entry (h, r) of lane (g, n) is key 16 h + mla_row(g, r) of the tile.  Returns the
+    // head's max over the tile (scaled, log2 units).
+    auto scores = [&](int t, bool full, float* sv) -> float {
+        const uint8_t* stage = smem + (t % kStages) * C::kStage;
+        f32x4 sacc[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            sacc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < C::kSteps; ++s) {
+                const uint8_t* src = s < 16 ? stage + k_off[h] + 64 * s : stage + rope_off[h][s - 16];
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(src));
+                sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], sacc[h], 0, 0, 0);
+            }
+        }
+        float tmax;
+        if (full) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][e & 3];
+            tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+            tmax *= p.scale_log2;
+        } else {
+            const int kb = k_begin + t * kKeys;
+            tmax = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int key = kb + 16 * (e >> 2) + mla_row(g, e & 3);
+                sv[e] = (valid && key < k_end) ? sacc[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
+                tmax = fmaxf(tmax, sv[e]);
+            }
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        return fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    };
+
+    // P^T of tile t against the running max (k-slot 8 g + 4 h + r is entry (h, r); the sum
+    // adds the rounded weights), then O^T += V^T . P^T.
+    auto probs_pv = [&](int t, bool full, const float* sv) {
+        u32x4 pw;
+        if (full) {
+            const float mneg = -st.m;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const uint32_t w = pack_bf16(fast_exp2(__builtin_fmaf(sv[e], p.scale_log2, mneg)),
+                                             fast_exp2(__builtin_fmaf(sv[e + 1], p.scale_log2, mneg)));
+                st.l = dot2_bf16(w, kOnesBf16x2, st.l);
+                pw[e >> 1] = w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float e0 = sv[e] == -INFINITY ? 0.0f : fast_exp2(sv[e] - st.m);
+                const float e1 = sv[e + 1] == -INFINITY ? 0.0f : fast_exp2(sv[e + 1] - st.m);
+                const uint32_t w = pack_bf16(e0, e1);
+                st.l = dot2_bf16(w, kOnesBf16x2, st.l);
+                pw[e >> 1] = w;
+            }
+        }
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+        const uint8_t* stage = smem + (t % kStages) * C::kStage;
+        const uint8_t* v0 = stage + v_off[0];
+        const uint8_t* v1 = stage + v_off[1];
+#pragma unroll
+        for (int dt = 0; dt < C::kDTiles; ++dt) {
+            // Assemble the operand from whole dwords: extracting the 16-bit elements one
+            // by one made the compiler keep only the first dword of each read.
+            const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(v0 + 32 * dt));
+            const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(v1 + 32 * dt));
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, oacc[dt], 0, 0, 0);
+        }
+    };
+
+    // Table chunks and the loads of tile u (issued kStages - 1 tiles ahead).
+    auto feed = [&](int u) {
+        if (u >= ntiles) return;
+        const int c = u / kChunkTiles;
+        if (u % kChunkTiles == 0 && tab.exists(c + 1)) tab.load(c + 1, treg);
+        if (u % kChunkTiles == kChunkTiles / 2 && tab.exists(c + 1)) tab.store(c + 1, treg);
+        issue_tile(u);
+    };
+#pragma unroll
+    for (int u = 0; u < kStages - 1; ++u) feed(u);
+
+    // Tile t: wait for its loads, barrier (tile t visible, the stage of tile t - 1 free,
+    // staged table entries visible), issue tile t + 3, scores, then P and O.  A tile that
+    // raises some head's max by more than the slack leaves the loop to rescale O^T, so that
+    // inside the loop the accumulators are only touched by the products.
+    int t = 0;
+    float sv[8];
+    float tmax = 0.0f;
+    bool full = false;
+    while (t < ntiles) {
+        for (; t < ntiles; ++t) {
+            wait_tile<C::kDma>(min(ntiles - 1 - t, kStages - 2));
+            block_sync();
+            feed(t + kStages - 1);
+            full = k_begin + (t + 1) * kKeys <= k_end;
+            tmax = scores(t, full, sv);
+            const bool grow = tmax > st.m + kRescaleSlack || (st.m == -INFINITY && tmax != -INFINITY);
+            if (__any(grow)) break;
+            probs_pv(t, full, sv);
+        }
+        if (t >= ntiles) break;
+        {
+            const bool grow = tmax > st.m + kRescaleSlack || (st.m == -INFINITY && tmax != -INFINITY);
+            const float mnew = grow ? tmax : st.m;
+            const float alpha = !grow ? 1.0f : (st.m == -INFINITY ? 0.0f : fast_exp2(st.m - mnew));
+            st.l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < C::kDTiles; ++dt) oacc[dt] *= alpha;
+            st.m = mnew;
+        }
+        probs_pv(t, full, sv);
+        ++t;
+    }
+
+    // ---------------------------------------------------------------- epilogue
+    float l_tot = st.l + __shfl_xor(st.l, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (!valid) return;
+    const int nsplit = (L + p.split_tokens - 1) / p.split_tokens;
+    if (nsplit == 1) {
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + row * 512 + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < C::kDTiles; ++dt) {
+            const uint32_t w0 = bf16_bits(oacc[dt][0] * inv) | ((uint32_t)bf16_bits(oacc[dt][1] * inv) << 16);
+            const uint32_t w1 = bf16_bits(oacc[dt][2] * inv) | ((uint32_t)bf16_bits(oacc[dt][3] * inv) << 16);
+            *reinterpret_cast<uint2*>(out + 16 * dt) = make_uint2(w0, w1);
+        }
+        if (p.lse && g == 0) p.lse[row] = l_tot > 0.0f ? (st.m + __log2f(l_tot)) * kLn2f : -INFINITY;
+    } else {
+        const int64_t ps = row * p.max_splits + split;
+        float* o = p.ws_o + ps * 512 + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < C::kDTiles; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = oacc[dt];
+        if (g == 0) {
+            p.ws_ml[ps * 2] = st.m;
+            p.ws_ml[ps * 2 + 1] = l_tot;
+        }
+    }
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+int32_t mla_head_groups(int32_t num_q_heads) {
+    return (num_q_heads + MlaCfg::kHeads - 1) / MlaCfg::kHeads;
+}
+
+DecodePlan plan_mla(int32_t batch, int32_t num_q_heads, int32_t head_dim_v, int32_t max_seq_len_kv) {
+    DecodePlan pl{};
+    const int64_t hgs = mla_head_groups(num_q_heads);
+    auto nsplits = [&](int sp) { return (int64_t)(max_seq_len_kv + sp - 1) / sp; };
+    // A split's partial state is Hq x Dv fp32 (256 KiB at 128 x 512): long splits keep that
+    // traffic small; shorten them only while the grid would leave compute units idle.
+    int split = 1024;
+    while (split > 256 && batch * hgs * nsplits(split) < 512) split /= 2;
+    pl.split_tokens = split;
+    pl.max_splits = (int32_t)(max_seq_len_kv > 0 ? nsplits(split) : 1);
+    if (pl.max_splits <= 1) return pl;
+    const size_t rows = (size_t)batch * num_q_heads * pl.max_splits;
+    pl.ws_o_offset = 0;
+    pl.ws_ml_offset = align256(rows * head_dim_v * sizeof(float));
+    pl.ws_bytes = pl.ws_ml_offset + rows * 2 * sizeof(float);
+    return pl;
+}
+
+hipError_t launch_mla_decode(const MfmaParams& p, hipStream_t s) {
+    // ids: (unit / 8, head group, unit % 8) with units = batch * max_splits rounded up to 8
+    const int64_t hgs = mla_head_groups(p.hq);
+    const int64_t units = ((int64_t)p.batch * p.max_splits + 7) / 8 * 8;
+    const dim3 grid((unsigned)(hgs * units));
+    hipLaunchKernelGGL(mla_decode_kernel, grid, dim3(MlaCfg::kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace pkv
