@@ -37,6 +37,10 @@ constexpr int kTabEntries = kChunkKeys + 16;    // entries per chunk buffer (>= 
 
 // s_waitcnt immediate (gfx9 layout): vmcnt in bits 3:0 and 15:14, expcnt in 6:4,
 // lgkmcnt in 11:8; expcnt and lgkmcnt at their maxima do not wait.
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Wait for this wave's loads into LDS of tile t, with n in {0, 1, 2} later tiles (each
@@ -120,6 +124,76 @@ struct TableChunks {
         return (uint32_t)lds[(chunk & 1) * kTabEntries + (key >> bs_log2) - first_entry(chunk)];
     }
 };
+
+// ------------------------------------------------------------------ work order
+// Work item `item` of a launch in which sequence b contributes count(b, L_b) items.  Up
+// to NT sequences are taken longest first (ties: lower index first), so that the longest
+// work starts first and the live items are numbered without gaps (and so spread evenly
+// over the XCDs); more sequences than that are taken in index order.  Sets seq and j
+// (the item's index within its sequence); false if item is past the last item.  All NT
+// threads of the workgroup must call it; lds needs 3 NT + 24 ints and is free afterwards.
+template <int NT, typename Count>
+__device__ bool find_item(int item, int batch, const int32_t* seq_lens, int len_cap, Count count,
+                          int32_t* lds, int& seq, int& j) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    int32_t* s_len = lds;                 // [NT] lengths of the chunk's sequences
+    int32_t* s_cnt = lds + NT;            // [NT] item counts by position in the order
+    int32_t* s_seq = lds + 2 * NT;        // [NT] sequence at each position
+    int32_t* s_wave = lds + 3 * NT;       // [NT / 64] per-wave sums
+    int32_t* s_res = lds + 3 * NT + 16;   // found, sequence, index
+    const bool ranked = batch <= NT;
+    if (tid == 0) s_res[0] = 0;
+    int base = 0;                         // items of the chunks before
+    for (int c0 = 0; c0 < batch; c0 += NT) {
+        const int bb = c0 + tid;
+        int len = 0, cnt = 0;
+        if (bb < batch) {
+            len = min(seq_lens[bb], len_cap);
+            cnt = count(bb, len);
+        }
+        int pos = tid;
+        if (ranked) {
+            s_len[tid] = bb < batch ? len : -1;
+            __syncthreads();
+            if (bb < batch) {
+                pos = 0;
+                for (int o = 0; o < batch; ++o) {
+                    const int lo = s_len[o];
+                    pos += (lo > len) || (lo == len && o < tid);
+                }
+            }
+        }
+        s_cnt[pos] = bb < batch ? cnt : 0;
+        s_seq[pos] = bb;
+        __syncthreads();
+        int v = s_cnt[tid];
+        const int own = v;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(v, d, 64);
+            if (lane >= d) v += u;
+        }
+        if (lane == 63) s_wave[wid] = v;
+        __syncthreads();
+        int incl = base + v;
+        for (int w = 0; w < wid; ++w) incl += s_wave[w];
+        if (item >= incl - own && item < incl) {
+            s_res[0] = 1;
+            s_res[1] = s_seq[tid];
+            s_res[2] = item - (incl - own);
+        }
+        for (int w = 0; w < NT / 64; ++w) base += s_wave[w];
+        __syncthreads();
+        if (s_res[0]) break;
+    }
+    const bool found = s_res[0] != 0;
+    seq = s_res[1];
+    j = s_res[2];
+    __syncthreads();
+    return found;
+}
 
 // ------------------------------------------------------------------ online softmax state
 struct RowState {

@@ -63,13 +63,19 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
     const int g = lane >> 4;          // k-slot group
 
     // Workgroups are dealt to the 8 XCDs round-robin; the head groups of one work unit
-    // take ids that differ by a multiple of 8 and follow each other on one XCD.
+    // take ids that differ by a multiple of 8 and follow each other on one XCD.  Units
+    // (sequence, split) are numbered without gaps, the longest sequences first.
     const int hgs = (p.hq + C::kHeads - 1) / C::kHeads;
     const int id = blockIdx.x;
     const int hg = (id >> 3) % hgs;
     const int unit = ((id >> 3) / hgs) * 8 + (id & 7);
-    const int b = unit % p.batch;
-    const int split = unit / p.batch;
+    int b, split;
+    {
+        auto nsplits = [&](int, int len) { return len > 0 ? (len + p.split_tokens - 1) / p.split_tokens : 0; };
+        if (!find_item<C::kThreads>(unit, p.batch, p.seq_lens, p.len_cap, nsplits,
+                                    reinterpret_cast<int32_t*>(smem + kStages * C::kStage), b, split))
+            return;
+    }
     if (split >= p.max_splits) return;
     const int L = min(p.seq_lens[b], p.len_cap);
     const int k_begin = split * p.split_tokens;
@@ -196,6 +202,15 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
                 sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], sacc[h], 0, 0, 0);
             }
         }
+        // Keep six K reads in flight ahead of the products (left alone, the compiler
+        // issues each read just before its product and waits out the LDS latency).
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * C::kSteps - 6; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
         float tmax;
         if (full) {
 #pragma unroll
@@ -252,6 +267,14 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
             const bf16x8_t a = __builtin_bit_cast(bf16x8_t, u32x4{lo[0], lo[1], hi[0], hi[1]});
             oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, oacc[dt], 0, 0, 0);
         }
+        // Twelve transposing reads (six products) in flight ahead of the products.
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 0);
+#pragma unroll
+        for (int i = 0; i < C::kDTiles - 6; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
     };
 
     // Table chunks and the loads of tile u (issued kStages - 1 tiles ahead).

@@ -52,14 +52,24 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
     const int lrow = lane & 31;        // query row of this lane inside the wave
     const int lhalf = lane >> 5;       // which half of the k-slots / keys
 
-    int id = blockIdx.x;
-    const int kvh = id % p.hkv;
-    id /= p.hkv;
-    const int qb = id % p.q_blocks;
-    const int b = id / p.q_blocks;
     const int G = p.group;
     const int tw = 32 / G;                         // query tokens per wave
     const int tpb = C::kWaves * tw;                // query tokens per workgroup
+    // Work items (sequence, query block), the longest sequences first and, within one,
+    // the last query blocks (most keys) first; the kv head varies fastest.
+    const int kvh = blockIdx.x % p.hkv;
+    int b, qb;
+    {
+        int j;
+        auto qblocks = [&](int s, int len) {
+            const int n = p.cu_q[s + 1] - p.cu_q[s];
+            return (n > 0 && len > 0) ? (n + tpb - 1) / tpb : 0;
+        };
+        if (!find_item<C::kThreads>(blockIdx.x / p.hkv, p.batch, p.seq_lens, p.len_cap, qblocks,
+                                    reinterpret_cast<int32_t*>(smem + kStages * C::kStage), b, j))
+            return;
+        qb = qblocks(b, min(p.seq_lens[b], p.len_cap)) - 1 - j;
+    }
     const int q0 = p.cu_q[b];
     const int nq = p.cu_q[b + 1] - q0;
     const int L = min(p.seq_lens[b], p.len_cap);
@@ -170,6 +180,10 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
             const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(krow + pos));
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc, 0, 0, 0);
         }
+        // All K reads of the tile in flight before the products (left alone, the compiler
+        // issues each read just before its product and waits out the LDS latency).
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::kSteps, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, C::kSteps, 0);
         float tmax;
         if (full) {
 #pragma unroll
@@ -237,6 +251,16 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
                     a, __builtin_bit_cast(bf16x8_t, pw[ks]), oacc[mt], 0, 0, 0);
             }
         }
+        // Eight transposing reads (four products) in flight ahead of the products.
+        constexpr int kPv = 2 * C::kMTiles;
+        constexpr int kAhead = kPv < 4 ? kPv : 4;
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kAhead, 0);
+#pragma unroll
+        for (int i = 0; i < kPv - kAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAhead, 0);
     };
 
     // Table chunks and the loads of tile u (issued kStages - 1 tiles ahead).
