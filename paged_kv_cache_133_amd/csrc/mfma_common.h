@@ -82,6 +82,17 @@ __device__ __forceinline__ int32_t uniform_load(const int32_t* p) {
     return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(reinterpret_cast<uintptr_t>(p));
 }
 
+// max(x, x of lane ^ 32) and max(x, x of lane ^ 16) with the gfx950 lane-swap
+// instructions (fmax of the two swapped copies), instead of LDS-routed shuffles.
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ s16x4 lds_read_tr(const uint8_t* lds_addr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4*)(lds_addr));

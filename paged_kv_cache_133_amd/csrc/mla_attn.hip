@@ -133,13 +133,19 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
     const int wid_u = __builtin_amdgcn_readfirstlane(wid);
     const bool fast_rows = p.bs_log2 >= 3;
     const uint32_t rope_voff = (uint32_t)((lane >> 3) * 128 + rope_chunk(rope_r, lane & 7) * 16);
+    // The table entry of the next tile is read one tile ahead, off the critical path.
+    auto fast_tile = [&](int u) { return fast_rows && k_begin + (u + 1) * kKeys <= k_end; };
+    auto entry_of = [&](int u) { return uniform_load(tab.row + ((k_begin + u * kKeys + 8 * wid_u) >> p.bs_log2)); };
+    int32_t next_entry = fast_tile(0) ? entry_of(0) : 0;
     auto issue_tile = [&](int u) {
         const int kb = k_begin + u * kKeys;
         const int chunk = u / kChunkTiles;
         uint8_t* stage = smem + (u % kStages) * C::kStage;
-        if (fast_rows && kb + kKeys <= k_end) {
+        const int32_t entry = next_entry;
+        if (u + 1 < ntiles && fast_tile(u + 1)) next_entry = entry_of(u + 1);
+        if (fast_tile(u)) {
             const int key0 = kb + 8 * wid_u;
-            const int32_t blk = min(max(uniform_load(tab.row + (key0 >> p.bs_log2)), 0), tab.last_block);
+            const int32_t blk = min(max(entry, 0), tab.last_block);
             const uint64_t slot0 = ((uint64_t)(uint32_t)blk << p.bs_log2) | (uint32_t)(key0 & bs_mask);
             const uint8_t* nb = reinterpret_cast<const uint8_t*>(p.k_cache) + slot0 * 1024u;
 #pragma unroll
@@ -227,8 +233,7 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
                 tmax = fmaxf(tmax, sv[e]);
             }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        return fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        return max_xor32(max_xor16(tmax));
     };
 
     // P^T of tile t against the running max (k-slot 8 g + 4 h + r is entry (h, r); the sum

@@ -134,13 +134,19 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
         fast_voff[j] = (uint32_t)(r - 16 * (wid & 1)) * row_bytes +
                        (uint32_t)swz<C::kRowChunks, C::kRowShift>(r, q % C::kRowChunks) * 16u;
     }
+    // The table entry of the next tile is read one tile ahead, off the critical path.
+    auto fast_tile = [&](int u) { return fast_rows && (u + 1) * kKeys <= k_end; };
+    auto entry_of = [&](int u) { return uniform_load(tab.row + ((u * kKeys + 16 * (wid_u & 1)) >> p.bs_log2)); };
+    int32_t next_entry = fast_tile(0) ? entry_of(0) : 0;
     auto issue_tile = [&](int u) {
         const int kb = u * kKeys;
         const int chunk = u / kChunkTiles;
         uint8_t* stage = smem + (u % kStages) * C::kStage;
-        if (fast_rows && kb + kKeys <= k_end) {
+        const int32_t entry = next_entry;
+        if (u + 1 < ntiles && fast_tile(u + 1)) next_entry = entry_of(u + 1);
+        if (fast_tile(u)) {
             const int key0 = kb + 16 * (wid_u & 1);
-            const int32_t blk = min(max(uniform_load(tab.row + (key0 >> p.bs_log2)), 0), tab.last_block);
+            const int32_t blk = min(max(entry, 0), tab.last_block);
             const uint64_t slot0 = ((uint64_t)(uint32_t)blk << p.bs_log2) | (uint32_t)(key0 & bs_mask);
             const uint8_t* sb = cache_u + slot0 * row_bytes;
 #pragma unroll
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
                 tmax = fmaxf(tmax, sv[r]);
             }
         }
-        return fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        return max_xor32(tmax);
     };
 
     // P^T of tile t against the running max (B-operand layout: k-slot j of k-step ks is
