@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.hip", "write.hip", "decode.hip", "mla_attn.hip", "varlen_attn.hip"]
+SOURCES = ["api.hip", "write.hip", "decode.hip", "mla_attn.hip", "varlen_attn.hip", "gqa_attn.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -26,7 +26,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={
 # The MFMA attention kernels keep their accumulators in ordinary VGPRs: with the default
 # choice (AGPRs) the online-softmax rescale copies every accumulator out and back each tile.
 EXTRA = {"varlen_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "mla_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "mla_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "gqa_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

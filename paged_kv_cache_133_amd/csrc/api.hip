@@ -229,11 +229,24 @@ int prepare_decode(pkv::DecodeParams& p, pkv::DecodePlan& plan, void* out, float
     p.len_cap = max_seq_len_kv;
     p.num_blocks = num_blocks;
     p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+    if (pkv::gqa_stream_supported(dtype, group, head_dim_v, p.bs_log2, batch)) {
+        p.parts = plan.parts;
+        p.ws_o = reinterpret_cast<float*>(ws + plan.st_o_offset);
+        p.ws_ml = reinterpret_cast<float*>(ws + plan.st_ml_offset);
+        p.tile_prefix = reinterpret_cast<int32_t*>(ws + plan.st_pre_offset);
+    }
     return PKV_OK;
+}
+
+// Whether the split pass can leave partial states: several splits per sequence, or
+// several ranges per kv head for the range-streaming kernel.
+bool needs_combine(const pkv::DecodeParams& p, const pkv::DecodePlan& plan) {
+    return p.parts > 0 ? p.parts > 1 : plan.max_splits > 1;
 }
 
 int launch_combine_for(const pkv::DecodeParams& p, int32_t head_dim_v, int32_t dtype,
                        hipStream_t s) {
+    if (p.parts > 0) return hip_status(pkv::launch_gqa_stream_combine(p, head_dim_v, s), "decode combine launch");
     pkv::CombineParams c{};
     c.out = p.out;
     c.lse = p.lse;
@@ -390,7 +403,7 @@ int pkv_paged_attn_decode(void* out, float* lse_out, const void* q, const void* 
     if (rc != PKV_OK || idle) return rc;
     hipStream_t s = (hipStream_t)stream;
     rc = hip_status(pkv::launch_decode(p, dtype, head_dim_qk, s), "decode split launch");
-    if (rc != PKV_OK || plan.max_splits <= 1) return rc;
+    if (rc != PKV_OK || !needs_combine(p, plan)) return rc;
     return launch_combine_for(p, head_dim_v, dtype, s);
 }
 
@@ -438,7 +451,7 @@ int pkv_paged_attn_decode_combine(void* out, float* lse_out, const void* q, cons
     pkv::DecodePlan plan{};
     bool idle = false;
     rc = prepare_decode(p, plan, PKV_DECODE_ARGS, &idle);
-    if (rc != PKV_OK || idle || plan.max_splits <= 1) return rc;
+    if (rc != PKV_OK || idle || !needs_combine(p, plan)) return rc;
     return launch_combine_for(p, head_dim_v, dtype, (hipStream_t)stream);
 }
 
@@ -476,7 +489,7 @@ int pkv_paged_attn_decode_append(void* out, float* lse_out, const void* q, const
         rc = hip_status(pkv::launch_decode(p, dtype, head_dim, s), "decode_append split launch");
         if (rc != PKV_OK) return rc;
     }
-    if ((stages & 2) && plan.max_splits > 1) return launch_combine_for(p, head_dim, dtype, s);
+    if ((stages & 2) && needs_combine(p, plan)) return launch_combine_for(p, head_dim, dtype, s);
     return PKV_OK;
 }
 

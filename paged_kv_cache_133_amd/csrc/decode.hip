@@ -364,15 +364,26 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
     while (split > kWaves * kStepTokens && pairs * nsplits(split) < 1024) split /= 2;
     pl.split_tokens = split;
     pl.max_splits = (int32_t)(max_seq_len_kv > 0 ? nsplits(split) : 1);
-    if (pl.max_splits <= 1) return pl;   // no workspace needed
-    const size_t rows = (size_t)batch * num_q_heads * pl.max_splits;
-    pl.ws_o_offset = 0;
-    pl.ws_ml_offset = align256(rows * head_dim_v * sizeof(float));
-    pl.ws_bytes = pl.ws_ml_offset + rows * 2 * sizeof(float);
+    if (pl.max_splits > 1) {
+        const size_t rows = (size_t)batch * num_q_heads * pl.max_splits;
+        pl.ws_o_offset = 0;
+        pl.ws_ml_offset = align256(rows * head_dim_v * sizeof(float));
+        pl.ws_bytes = pl.ws_ml_offset + rows * 2 * sizeof(float);
+    }
+    if (gqa_mfma_supported(1, G)) {      // the range-streaming layout, if that kernel runs
+        pl.parts = gqa_stream_parts(num_kv_heads);
+        const size_t parts = (size_t)num_kv_heads * pl.parts * 2 * G;
+        pl.st_o_offset = 0;
+        pl.st_ml_offset = align256(parts * head_dim_v * sizeof(float));
+        pl.st_pre_offset = align256(pl.st_ml_offset + parts * 2 * sizeof(float));
+        const size_t st_bytes = pl.st_pre_offset + ((size_t)batch + 1) * sizeof(int32_t);
+        if (st_bytes > pl.ws_bytes) pl.ws_bytes = st_bytes;
+    }
     return pl;
 }
 
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, hipStream_t s) {
+    if (gqa_mfma_supported(dtype, p.group)) return launch_gqa_decode(p, head_dim, s);
     if (dtype == 1) {
         return head_dim == 64 ? launch_decode_d<bf16_t, 64>(p, s) : launch_decode_d<bf16_t, 128>(p, s);
     }

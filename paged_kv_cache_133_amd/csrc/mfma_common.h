@@ -73,13 +73,21 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds_base) {
 // vector-memory instruction reads it.
 __device__ __forceinline__ void lds_dma16_s(const uint8_t* sbase, uint32_t voff, uint8_t* lds_base) {
     const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_base;
-    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+    // The base is the same in every lane; reading it from the first lane puts it in SGPRs
+    // also where the compiler cannot prove that (it is then a no-op where it can).
+    const uint64_t a = reinterpret_cast<uintptr_t>(sbase);
+    const uint64_t sa = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32);
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sa), "{m0}"(m0) : "memory");
 }
 
 // Read of a wave-uniform int32 through the scalar data cache (a load from the constant
 // address space; p must be the same in every lane).
 __device__ __forceinline__ int32_t uniform_load(const int32_t* p) {
-    return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(reinterpret_cast<uintptr_t>(p));
+    const uint64_t a = reinterpret_cast<uintptr_t>(p);
+    const uint64_t sa = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32);
+    return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(sa);
 }
 
 // max(x, x of lane ^ 32) and max(x, x of lane ^ 16) with the gfx950 lane-swap

@@ -71,13 +71,24 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
     const int unit = ((id >> 3) / hgs) * 8 + (id & 7);
     int b, split;
     {
-        auto nsplits = [&](int, int len) { return len > 0 ? (len + p.split_tokens - 1) / p.split_tokens : 0; };
+        auto nsplits = [&](int, int len) { return len > 0 ? (len + p.split_tokens - 1) / p.split_tokens : 1; };
         if (!find_item<C::kThreads>(unit, p.batch, p.seq_lens, p.len_cap, nsplits,
                                     reinterpret_cast<int32_t*>(smem + kStages * C::kStage), b, split))
             return;
+        b = __builtin_amdgcn_readfirstlane(b);          // the same in every lane
+        split = __builtin_amdgcn_readfirstlane(split);
     }
     if (split >= p.max_splits) return;
     const int L = min(p.seq_lens[b], p.len_cap);
+    if (L <= 0) {   // no visible key: output 0, lse -inf (one unit per such sequence)
+        const int h0 = hg * C::kHeads + wid * 16 + (lane & 15);
+        if (h0 < p.hq) {
+            uint16_t* o0 = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)b * p.hq + h0) * 512 + 4 * (lane >> 4);
+            for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<uint2*>(o0 + 16 * dt) = make_uint2(0u, 0u);
+            if (p.lse && lane < 16) p.lse[(int64_t)b * p.hq + h0] = -INFINITY;
+        }
+        return;
+    }
     const int k_begin = split * p.split_tokens;
     if (k_begin >= L) return;
     const int k_end = min(L, k_begin + p.split_tokens);

@@ -54,12 +54,19 @@ hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
 // do not depend on where blocks sit.
 // Workspace layout (each part 256-byte aligned):
 //   [o fp32 B*Hq*max_splits*Dv][(m, l) fp32 B*Hq*max_splits*2]
+// With 4..16 query heads per kv head the bf16 path may instead run the range-streaming
+// kernel (gqa_stream_supported): `parts` workgroups per kv head, each leaving at most two
+// partial states; its workspace is laid out from offset 0 as
+//   [o fp32 Hkv*parts*2*G*Dv][(m, l) fp32 Hkv*parts*2*G*2][tile prefix int32 B+1]
+// and ws_bytes covers both layouts.
 struct DecodePlan {
     int32_t split_tokens;
     int32_t max_splits;
     size_t ws_bytes;
     size_t ws_o_offset;
     size_t ws_ml_offset;
+    int32_t parts;
+    size_t st_o_offset, st_ml_offset, st_pre_offset;
 };
 DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t head_dim_v, int32_t max_seq_len_kv);
@@ -88,9 +95,20 @@ struct DecodeParams {
     void* k_cache_w;         // writable views of the caches (append mode)
     void* v_cache_w;
     int64_t* slots_out;      // [B] or null
+    // Range-streaming kernel (parts > 0): workgroups per kv head, and the tile prefix
+    // [B + 1] it leaves for its combine; ws_o / ws_ml then hold its partial states.
+    int32_t parts;
+    int32_t* tile_prefix;
 };
-// dtype: 0 f32, 1 bf16; head_dim 64 or 128.
+// dtype: 0 f32, 1 bf16; head_dim 64 or 128.  bf16 with 4..16 query heads per kv head runs
+// on the matrix cores (launch_gqa_decode: the range-streaming kernel when p.parts > 0,
+// else the per-split one), everything else on the vector ALU.
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, hipStream_t s);
+bool gqa_mfma_supported(int dtype, int group);
+bool gqa_stream_supported(int dtype, int group, int head_dim, int bs_log2, int batch);
+int gqa_stream_parts(int num_kv_heads);
+hipError_t launch_gqa_decode(const DecodeParams& p, int head_dim, hipStream_t s);
+hipError_t launch_gqa_stream_combine(const DecodeParams& p, int head_dim, hipStream_t s);
 
 // Merge of split partials (second launch of a split decode).
 struct CombineParams {

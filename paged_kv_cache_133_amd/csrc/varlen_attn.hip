@@ -68,7 +68,8 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
         if (!find_item<C::kThreads>(blockIdx.x / p.hkv, p.batch, p.seq_lens, p.len_cap, qblocks,
                                     reinterpret_cast<int32_t*>(smem + kStages * C::kStage), b, j))
             return;
-        qb = qblocks(b, min(p.seq_lens[b], p.len_cap)) - 1 - j;
+        b = __builtin_amdgcn_readfirstlane(b);          // the same in every lane
+        qb = __builtin_amdgcn_readfirstlane(qblocks(b, min(p.seq_lens[b], p.len_cap)) - 1 - j);
     }
     const int q0 = p.cu_q[b];
     const int nq = p.cu_q[b + 1] - q0;
