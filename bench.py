@@ -37,10 +37,24 @@ if ROOT not in sys.path:
 METRIC = "paged-decode KV-read HBM GB/s (% of peak) + µs/step, Llama-7B-shape B=32, 1 GPU"
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E, vendor figure
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, vendor figure
-DOMINANT_KERNEL = "decode_split_kernel"
-KERNEL_NAME = {"decode": "decode_split_kernel", "mla": "mla_decode_kernel",
-               "varlen": "varlen_kernel<128>"}
-KERNEL_SOURCES = ["paged_kv_cache_133_amd/csrc/decode.hip", "paged_kv_cache_133_amd/csrc/pkv_device.h"]
+CSRC = "paged_kv_cache_133_amd/csrc/"
+MFMA_SOURCES = [CSRC + "mfma_common.h", CSRC + "pkv_device.h"]
+
+
+def dominant_kernel(w):
+    """The attention kernel a workload's step runs (the library's dispatch rule) and the
+    sources its traffic counters depend on."""
+    if w.mode == "mla":
+        return "mla_decode_kernel", [CSRC + "mla_attn.hip"] + MFMA_SOURCES
+    if w.mode == "varlen":
+        return "varlen_kernel<128>", [CSRC + "varlen_attn.hip"] + MFMA_SOURCES
+    group = w.num_q_heads // w.num_kv_heads
+    if w.dtype == "bf16" and 4 <= group <= 16:
+        rows_per_wave_load = 1024 // (2 * w.head_dim)
+        name = ("gqa_stream_kernel" if w.block_size >= rows_per_wave_load and w.batch <= 1024
+                else "gqa_decode_kernel")
+        return name, [CSRC + "gqa_attn.hip"] + MFMA_SOURCES
+    return "decode_split_kernel", [CSRC + "decode.hip", CSRC + "pkv_device.h"]
 
 
 def parse():
@@ -65,18 +79,18 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, kernel: str, sources):
     """HBM bytes per launch of the dominant kernel from the committed counter summary,
     or None if the summary is missing or was taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{DOMINANT_KERNEL}_{workload}.txt")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel.split('<')[0]}_{workload}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -85,7 +99,7 @@ def read_traffic(workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -298,8 +312,8 @@ def main():
         tflops = flops / (split_ms * 1e-3) / 1e12
         # The bound is whichever resource the launch would saturate first at peak.
         mfma_bound = flops / (PEAK_BF16_TFLOPS * 1e12) > split_bytes / (PEAK_HBM_GBPS * 1e9)
-        traffic = read_traffic(w.name)
-        kname = KERNEL_NAME["mla" if mla else w.mode if w.mode == "varlen" else "decode"]
+        kname, ksources = dominant_kernel(w)
+        traffic = read_traffic(w.name, kname, ksources)
         if mfma_bound:
             roofline = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}

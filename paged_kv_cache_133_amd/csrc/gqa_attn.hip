@@ -482,9 +482,15 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
 // Merge of the partial states of sequences that cross range ends: workgroup (b, kv head),
 // parts from the non-empty ranges first .. last of that kv head (part of the first range:
 // its last segment unless the sequence starts exactly at the range start; ranges are
-// empty when there are fewer tiles than ranges).
+// empty when there are fewer tiles than ranges).  The (m, l) of all parts are staged in
+// LDS with one round of loads, then every o element is read once.
+constexpr int kCombineMaxParts = kStreamWgs;
+
 template <int D>
 __global__ __launch_bounds__(256) void gqa_stream_combine_kernel(DecodeParams p) {
+    __shared__ float s_w[16][kCombineMaxParts];   // m, then the weight e^(m - M)
+    __shared__ float s_l[16][kCombineMaxParts];
+    __shared__ float s_inv[16];
     const int b = blockIdx.x / p.hkv;
     const int kvh = blockIdx.x % p.hkv;
     const int T = p.tile_prefix[p.batch];
@@ -496,29 +502,50 @@ __global__ __launch_bounds__(256) void gqa_stream_combine_kernel(DecodeParams p)
     const int wl = range_of(end - 1, T, P);
     if (wf == wl) return;
     const int G = p.group;
+    const int np = wl - wf + 1;
     const int first_slot = range_start(wf, T, P) == pre ? 0 : 1;
-    for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-        const int n = i / D;
-        const int d = i % D;
-        auto part = [&](int wr) {
-            return ((int64_t)(kvh * P + wr) * 2 + (wr == wf ? first_slot : 0)) * G + n;
-        };
-        auto empty = [&](int wr) { return range_start(wr, T, P) == range_start(wr + 1, T, P); };
+    auto part = [&](int j, int n) {   // partial index of part j (range wf + j), head n
+        return ((int64_t)(kvh * P + wf + j) * 2 + (j == 0 ? first_slot : 0)) * G + n;
+    };
+    for (int i = threadIdx.x; i < np * G; i += blockDim.x) {
+        const int j = i / G, n = i % G;
+        const bool empty = range_start(wf + j, T, P) == range_start(wf + j + 1, T, P);
+        const int64_t ps = part(j, n);
+        s_w[n][j] = empty ? -INFINITY : p.ws_ml[ps * 2];
+        s_l[n][j] = empty ? 0.0f : p.ws_ml[ps * 2 + 1];
+    }
+    __syncthreads();
+    if (threadIdx.x < G) {
+        const int n = threadIdx.x;
         float M = -INFINITY;
-        for (int wr = wf; wr <= wl; ++wr)
-            if (!empty(wr)) M = fmaxf(M, p.ws_ml[part(wr) * 2]);
-        float acc = 0.0f, lsum = 0.0f;
-        for (int wr = wf; wr <= wl; ++wr) {
-            if (empty(wr)) continue;
-            const int64_t ps = part(wr);
-            const float m = p.ws_ml[ps * 2];
-            const float f = m == -INFINITY ? 0.0f : fast_exp2(m - M);
-            acc = fmaf(f, p.ws_o[ps * D + d], acc);
-            lsum = fmaf(f, p.ws_ml[ps * 2 + 1], lsum);
+        for (int j = 0; j < np; ++j) M = fmaxf(M, s_w[n][j]);
+        float lsum = 0.0f;
+        for (int j = 0; j < np; ++j) {
+            const float f = s_w[n][j] == -INFINITY ? 0.0f : fast_exp2(s_w[n][j] - M);
+            s_w[n][j] = f;
+            lsum = fmaf(f, s_l[n][j], lsum);
         }
+        s_inv[n] = lsum > 0.0f ? 1.0f / lsum : 0.0f;
         const int64_t row = (int64_t)b * p.hq + kvh * G + n;
-        reinterpret_cast<uint16_t*>(p.out)[row * D + d] = bf16_bits(lsum > 0.0f ? acc / lsum : 0.0f);
-        if (p.lse && d == 0) p.lse[row] = lsum > 0.0f ? (M + __log2f(lsum)) * kLn2f : -INFINITY;
+        if (p.lse) p.lse[row] = lsum > 0.0f ? (M + __log2f(lsum)) * kLn2f : -INFINITY;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * (D / 4); i += blockDim.x) {
+        const int n = i / (D / 4);
+        const int d = (i % (D / 4)) * 4;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int j = 0; j < np; ++j) {
+            const float f = s_w[n][j];
+            if (f == 0.0f) continue;
+            const f32x4 o = *reinterpret_cast<const f32x4*>(p.ws_o + part(j, n) * D + d);
+            acc += f * o;
+        }
+        const float inv = s_inv[n];
+        const int64_t row = (int64_t)b * p.hq + kvh * G + n;
+        const uint32_t w0 = bf16_bits(acc[0] * inv) | ((uint32_t)bf16_bits(acc[1] * inv) << 16);
+        const uint32_t w1 = bf16_bits(acc[2] * inv) | ((uint32_t)bf16_bits(acc[3] * inv) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * D + d) = make_uint2(w0, w1);
     }
 }
 
