@@ -305,9 +305,11 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
     for (int u = 0; u < kStages - 1; ++u) feed(u);
 
     // Tile t: wait for its loads, barrier (tile t visible, the stage of tile t - 1 free,
-    // staged table entries visible), issue tile t + 3, scores, then P and O.  A tile that
-    // raises some head's max by more than the slack leaves the loop to rescale O^T, so that
-    // inside the loop the accumulators are only touched by the products.
+    // staged table entries visible), issue tile t + 3 (two waves before their scores, two
+    // after, so that the four waves do not queue their 36 loads on the compute unit at
+    // once), scores, then P and O.  A tile that raises some head's max by more than the
+    // slack leaves the loop to rescale O^T, so that inside the loop the accumulators are
+    // only touched by the products.
     int t = 0;
     float sv[8];
     float tmax = 0.0f;
@@ -316,9 +318,10 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
         for (; t < ntiles; ++t) {
             wait_tile<C::kDma>(min(ntiles - 1 - t, kStages - 2));
             block_sync();
-            feed(t + kStages - 1);
+            if (wid_u < 2) feed(t + kStages - 1);
             full = k_begin + (t + 1) * kKeys <= k_end;
             tmax = scores(t, full, sv);
+            if (wid_u >= 2) feed(t + kStages - 1);
             const bool grow = tmax > st.m + kRescaleSlack || (st.m == -INFINITY && tmax != -INFINITY);
             if (__any(grow)) break;
             probs_pv(t, full, sv);
