@@ -66,7 +66,8 @@ def lib():
         L.orc_kv_write.argtypes = [p, i64, i64, p, p, i64]
         L.orc_kv_write_contiguous.argtypes = [p, i32, i64, i64, p, p, p]
         L.orc_paged_attention.argtypes = [p, p, i32, p, p, p, p, i32, i32, p, p, i32, i32,
-                                          i32, i32, i32, i32, i64, f64, i32, p, p, p, i32]
+                                          i32, i32, i32, i32, i64, f64, i32, i32, p, p, p,
+                                          i32]
         L.orc_merge_states.argtypes = [p, p, p, i32, i64, i32, p, p]
         _lib = L
     return _lib
@@ -146,8 +147,10 @@ def kv_write_contiguous(cache: np.ndarray, newkv: np.ndarray, seqlen, token_offs
 # --------------------------------------------------------------------------- attention
 def paged_attention(q, k_cache, v_cache, block_table, cu_q, seq_lens_kv, scale: float,
                     causal: bool, q_rope=None, k_rope=None, want_touched: bool = False,
-                    threads: int = 0):
-    """fp64 paged attention; returns (out [T,Hq,Dv] f64, lse [T,Hq] f64[, touched])."""
+                    threads: int = 0, window: int = 0):
+    """fp64 paged attention; returns (out [T,Hq,Dv] f64, lse [T,Hq] f64[, touched]).
+    window > 0: each row sees only its `window` most recent visible positions (the band of
+    sparse_mode 4 with pre_tokens = window - 1; "KVCache Optimization Skill", Appendix C)."""
     qs, dt = _storage(q)
     ks, dk = _storage(k_cache)
     vs, dv = _storage(v_cache)
@@ -171,7 +174,8 @@ def paged_attention(q, k_cache, v_cache, block_table, cu_q, seq_lens_kv, scale: 
     _check(lib().orc_paged_attention(_ptr(qs), _ptr(qr), dt, _ptr(ks), _ptr(vs), _ptr(kr),
                                      _ptr(t), len(sl), t.shape[1], _ptr(cu), _ptr(sl), Hq, Hkv,
                                      Dqk, Dv, Dr, bs, nb, float(scale), int(bool(causal)),
-                                     _ptr(out), _ptr(lse), _ptr(touched), int(threads)))
+                                     int(window), _ptr(out), _ptr(lse), _ptr(touched),
+                                     int(threads)))
     if want_touched:
         return out, lse, touched
     return out, lse
@@ -206,7 +210,7 @@ def kv_cache_bytes(layers: int, tokens: int, heads: int, head_dim: int, elem_byt
 
 
 # --------------------------------------------------------------------------- one step
-def decode_step(case_np: dict, causal: bool, threads: int = 0):
+def decode_step(case_np: dict, causal: bool, threads: int = 0, window: int = 0):
     """Whole step on host arrays: slot_mapping, cache writes, then attention.
 
     case_np holds numpy arrays: block_table, lens_before, cu_q, lens_after, cache_k,
@@ -227,6 +231,6 @@ def decode_step(case_np: dict, causal: bool, threads: int = 0):
         v = kv_write(c["cache_v"], c["new_v"], slots)
     out, lse = paged_attention(c["q"], k, v, c["block_table"], c["cu_q"], c["lens_after"],
                                c["scale"], causal, q_rope=c.get("q_rope"), k_rope=rope,
-                               threads=threads)
+                               threads=threads, window=window)
     return {"slots": slots, "cache_k": k, "cache_v": v, "cache_rope": rope, "out": out,
             "lse": lse}

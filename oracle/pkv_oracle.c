@@ -176,9 +176,11 @@ int orc_kv_write_contiguous(uint8_t* cache, int32_t batch, int64_t max_seq_len,
  *            cache_nope for both, so Dv = Dqk there)
  *   k_rope   [nb, bs, Hkv, Dr] or NULL, present iff q_rope is
  *   seq_lens_kv[b] = L'_b, the number of cached tokens of sequence b after the write.
- * Row i of sequence b (n_b = cu_q[b+1]-cu_q[b] rows) sees positions p in
- *   [0, L'_b)                 if causal == 0   (decode, sparse_mode 0)
- *   [0, L'_b - n_b + i]       if causal != 0   (bottom-right causal, self included)
+ * Row i of sequence b (n_b = cu_q[b+1]-cu_q[b] rows) sees positions p in [lo, hi] with
+ *   hi = L'_b - 1             if causal == 0   (decode, sparse_mode 0)
+ *   hi = L'_b - n_b + i       if causal != 0   (bottom-right causal, self included)
+ *   lo = max(0, hi - window + 1) if window > 0 (band / sliding window: the `window` most
+ *        recent positions up to hi, the row's own included), else lo = 0.
  * score_p = scale * (q . K_p + q_rope . Krope_p); out = sum_p softmax_p * V_p;
  * lse = max + log(sum exp(score - max)).  Empty rows: out 0, lse -inf.
  * `touched` (nb*bs bytes, or NULL) marks every cache row read.
@@ -190,7 +192,8 @@ int orc_paged_attention(const void* q, const void* q_rope, int32_t dtype,
                         int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t head_dim_qk, int32_t head_dim_v, int32_t head_dim_rope,
                         int32_t block_size, int64_t num_blocks, double scale, int32_t causal,
-                        double* out, double* lse, uint8_t* touched, int32_t num_threads) {
+                        int32_t window, double* out, double* lse, uint8_t* touched,
+                        int32_t num_threads) {
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0) return ORC_ERR_ARG;
     if (num_q_heads % num_kv_heads != 0) return ORC_ERR_ARG;
     if ((q_rope == NULL) != (k_rope == NULL)) return ORC_ERR_ARG;
@@ -237,9 +240,11 @@ int orc_paged_attention(const void* q, const void* q_rope, int32_t dtype,
             const int64_t i = t - cu_q[b];
             const int64_t n = cu_q[b + 1] - cu_q[b];
             const int64_t visible = causal ? (seq_lens_kv[b] - n + i + 1) : seq_lens_kv[b];
+            int64_t lo = 0;                    /* first visible position */
+            if (window > 0 && visible - window > 0) lo = visible - window;
 
             double m = -INFINITY;
-            for (int64_t p = 0; p < visible; ++p) {
+            for (int64_t p = lo; p < visible; ++p) {
                 int64_t slot = orc_slot_of(block_table, max_blocks_per_seq, b, p,
                                            block_size, num_blocks);
                 double s = 0.0;
@@ -258,7 +263,7 @@ int orc_paged_attention(const void* q, const void* q_rope, int32_t dtype,
             }
             double z = 0.0;
             for (int32_t d = 0; d < head_dim_v; ++d) acc[d] = 0.0;
-            for (int64_t p = 0; p < visible; ++p) {
+            for (int64_t p = lo; p < visible; ++p) {
                 int64_t slot = orc_slot_of(block_table, max_blocks_per_seq, b, p,
                                            block_size, num_blocks);
                 double w = exp(score[p] - m);

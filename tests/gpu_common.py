@@ -56,7 +56,7 @@ def gpu_step(c, causal=False, want_lse=True):
             "lse": lse}
 
 
-def oracle_step(c, causal=False, rows=None):
+def oracle_step(c, causal=False, rows=None, window=0):
     """The oracle on host copies: slot_mapping and writes for the whole step, then
     attention for every sequence, or only for the sequences in `rows` (a sample)."""
     h = case_numpy(c)
@@ -76,7 +76,7 @@ def oracle_step(c, causal=False, rows=None):
     q_rope = h["q_rope"][tok] if h["q_rope"] is not None else None
     out, lse = oracle.paged_attention(h["q"][tok], k, v, h["block_table"][idx], cu,
                                       h["lens_after"][idx], h["scale"], causal,
-                                      q_rope=q_rope, k_rope=rope)
+                                      q_rope=q_rope, k_rope=rope, window=window)
     return {"slots": slots, "cache_k": k, "cache_v": v, "cache_rope": rope, "out": out,
             "lse": lse, "tokens": tok}
 

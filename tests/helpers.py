@@ -49,8 +49,9 @@ def logical_rows(pool, table_row, need, prefix_len, new_rows):
     return np.concatenate([flat, new_rows], axis=0)
 
 
-def brute_attention(case, causal):
-    """Textbook attention in fp64 over contiguous per-sequence K/V.  Returns (out, lse)."""
+def brute_attention(case, causal, window=0):
+    """Textbook attention in fp64 over contiguous per-sequence K/V.  Returns (out, lse).
+    window > 0 keeps, for each row, only the `window` most recent of its visible keys."""
     c = case
     w = c.w
     kp = as_f64(c.cache_k)
@@ -79,10 +80,12 @@ def brute_attention(case, causal):
             if R is not None:
                 s = s + qr[a:e, h, :] @ R[:, g, :].T
             s = s * w.scale
-            if causal:
-                # row i may see keys 0 .. Lp - n + i
-                keep = np.arange(Lp)[None, :] <= (Lp - n + np.arange(n))[:, None]
-                s = np.where(keep, s, -np.inf)
+            # row i may see keys 0 .. hi_i: hi_i = Lp - n + i (causal) or Lp - 1
+            hi = (Lp - n + np.arange(n)) if causal else np.full(n, Lp - 1)
+            keep = np.arange(Lp)[None, :] <= hi[:, None]
+            if window > 0:
+                keep &= np.arange(Lp)[None, :] > (hi - window)[:, None]
+            s = np.where(keep, s, -np.inf)
             z = logsumexp(s, axis=1)
             p = np.exp(s - z[:, None])
             out[a:e, h, :] = p @ V[:, g, :w.head_dim_v]

@@ -209,3 +209,58 @@ def test_oracle_rejects_bad_lengths():
     with pytest.raises(oracle.OracleError):     # more query rows than keys
         oracle.paged_attention(h["q"], h["cache_k"], h["cache_v"], h["block_table"],
                                [0, 1], [0], w.scale, False)
+
+
+# ------------------------------------------------------------------ band (sliding window)
+# "KVCache Optimization Skill", Appendix C: sparse_mode 4 is a band (sliding window) used
+# with pre_tokens; the LLM-serving page keeps only the most recent N tokens.  Reading: a row
+# sees the `window` most recent of its visible positions, its own included.
+
+@pytest.mark.parametrize("shape", SHAPES[:4])
+@pytest.mark.parametrize("window", [1, 3, 16, 40])
+def test_decode_window_matches_brute_force(shape, window):
+    Hq, Hkv, D, bs, dt = shape
+    w = wl.custom(batch=4, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                  dtype=dt)
+    c = wl.make_case(w, [0, 2, 39, 70], [1] * 4, seed=window)
+    r = oracle.decode_step(case_numpy(c), causal=False, window=window)
+    out, lse = brute_attention(c, causal=False, window=window)
+    np.testing.assert_allclose(r["out"], out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["lse"], lse, rtol=1e-13, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("window", [1, 5, 12])
+def test_varlen_window_matches_brute_force(causal, window):
+    w = wl.custom(mode="varlen", batch=4, num_q_heads=4, num_kv_heads=2, head_dim=16,
+                  block_size=4, dtype="f32")
+    c = wl.make_case(w, [0, 5, 4, 20], [7, 1, 13, 6], seed=window)
+    r = oracle.decode_step(case_numpy(c), causal=causal, window=window)
+    out, lse = brute_attention(c, causal=causal, window=window)
+    np.testing.assert_allclose(r["out"], out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["lse"], lse, rtol=1e-13, atol=1e-12)
+
+
+def test_window_of_one_returns_the_rows_own_value():
+    """Decode with window 1 sees only the token just written: out = its V exactly and
+    lse = its score."""
+    w = wl.custom(batch=3, num_q_heads=4, num_kv_heads=2, head_dim=8, block_size=4)
+    c = wl.make_case(w, [9, 0, 30], [1, 1, 1], seed=5)
+    r = oracle.decode_step(case_numpy(c), causal=False, window=1)
+    q = c.q.double().numpy()
+    k = c.new_k.double().numpy()
+    v = c.new_v.double().numpy()
+    for h in range(4):
+        g = h // 2
+        assert np.array_equal(r["out"][:, h, :], v[:, g, :])
+        np.testing.assert_allclose(r["lse"][:, h], (q[:, h] * k[:, g]).sum(-1) * w.scale,
+                                   rtol=0, atol=1e-12)
+
+
+def test_window_covering_the_sequence_changes_nothing():
+    w = wl.custom(mode="varlen", batch=2, num_q_heads=2, num_kv_heads=1, head_dim=8,
+                  block_size=4)
+    c = wl.make_case(w, [3, 10], [5, 2], seed=6)
+    a = oracle.decode_step(case_numpy(c), causal=True, window=0)
+    b = oracle.decode_step(case_numpy(c), causal=True, window=12)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"])

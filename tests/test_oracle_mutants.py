@@ -37,6 +37,8 @@ MUTANTS = {
     "write_wrong_row": ("memcpy(cache + slots[t] * row_bytes, rows + t * row_bytes,",
                         "memcpy(cache + slots[t] * row_bytes, rows + 0 * row_bytes,"),
     "dup_not_detected": ("if (seen[slots_out[t]]) { rc = ORC_ERR_DUP; break; }", ""),
+    "window_ignored": ("if (window > 0 && visible - window > 0) lo = visible - window;", ""),
+    "window_off_by_one": ("lo = visible - window;", "lo = visible - window + 1;"),
 }
 
 
