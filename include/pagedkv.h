@@ -241,7 +241,7 @@ PKV_API int pkv_paged_attn_decode_append(void* out, float* lse_out, const void* 
  *   cu_seqlens_q [batch + 1] int32 (cu_seqlens_q[0] = 0); seq_lens_kv [batch] int32
  *   max_seqlen_q [host] >= every n_b
  * Supported: head_dim in {64, 128}, 1 <= q heads per kv head <= 16, bf16;
- * block_size a power of two in [16, 256].
+ * block_size a power of two in [1, 256].
  * Device preconditions: n_b <= seq_lens_kv[b]; table entries as for decode.
  */
 PKV_API int pkv_paged_attn_varlen(void* out, float* lse_out, const void* q,
@@ -251,6 +251,42 @@ PKV_API int pkv_paged_attn_varlen(void* out, float* lse_out, const void* q,
                           int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
                           int32_t head_dim, int32_t block_size, int64_t num_blocks,
                           float softmax_scale, int32_t causal, int32_t dtype, void* stream);
+
+/*
+ * Sliding-window (band) forms.  The band is sparse_mode 4 with pre_tokens ("KVCache
+ * Optimization Skill", Appendix C: sliding-window models), read as: a query row sees only
+ * the `window` most recent of the keys it would otherwise see, its own position included,
+ * i.e. positions [hi - window + 1, hi] with hi its last visible position (pre_tokens =
+ * window - 1; the LLM-serving page's "keep only the latest N tokens" is window = N).
+ * window = 0 keeps every key (the forms above); window < 0 is PKV_ERR_SHAPE.
+ *
+ * pkv_paged_attn_decode_ex: MHA/GQA decode (no rope) with the window; with k_new and v_new
+ * given it is pkv_paged_attn_decode_append (the new row of each sequence is written at
+ * position seq_lens_kv[b] - 1 and read from k_new/v_new), with both NULL a plain decode
+ * over the cache (slot_mapping_out then unused).  stages as for decode_append; workspace:
+ * pkv_decode_workspace_size(...) bytes suffice for any window.  Other arguments, support
+ * and preconditions as for pkv_paged_attn_decode_append / pkv_paged_attn_decode.
+ * MTP decode (next_n + 1 query tokens per sequence, causal) goes through
+ * pkv_paged_attn_varlen(_ex) with n_b = next_n + 1 (skill page, Appendix E).
+ */
+PKV_API int pkv_paged_attn_decode_ex(void* out, float* lse_out, const void* q, const void* k_new,
+                             const void* v_new, void* k_cache, void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens_kv,
+                             int64_t* slot_mapping_out, int32_t batch, int32_t max_blocks_per_seq,
+                             int32_t max_seq_len_kv, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                             float softmax_scale, int32_t dtype, int32_t window, int32_t stages,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* pkv_paged_attn_varlen with the window (causal or not: hi = the row's last visible key). */
+PKV_API int pkv_paged_attn_varlen_ex(void* out, float* lse_out, const void* q,
+                             const int32_t* cu_seqlens_q, const int32_t* seq_lens_kv,
+                             const void* k_cache, const void* v_cache, const int32_t* block_table,
+                             int32_t batch, int64_t total_q, int32_t max_seqlen_q,
+                             int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                             float softmax_scale, int32_t causal, int32_t window, int32_t dtype,
+                             void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,9 +22,10 @@ STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_SHAPE", -3: "PKV_ERR_DTY
           -4: "PKV_ERR_UNSUPPORTED", -5: "PKV_ERR_ALIGN", -6: "PKV_ERR_SCALE",
           -7: "PKV_ERR_WORKSPACE", -8: "PKV_ERR_HIP"}
 EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_write",
-           "pkv_kv_cache_append", "pkv_decode_workspace_size", "pkv_paged_attn_decode", "pkv_paged_attn_decode_split",
-           "pkv_paged_attn_decode_combine", "pkv_paged_attn_decode_append",
-           "pkv_paged_attn_varlen")
+           "pkv_kv_cache_append", "pkv_decode_workspace_size", "pkv_paged_attn_decode",
+           "pkv_paged_attn_decode_split", "pkv_paged_attn_decode_combine",
+           "pkv_paged_attn_decode_append", "pkv_paged_attn_decode_ex", "pkv_paged_attn_varlen",
+           "pkv_paged_attn_varlen_ex")
 
 
 class PagedKVError(RuntimeError):
@@ -69,9 +70,15 @@ def lib() -> ctypes.CDLL:
     L.pkv_paged_attn_decode_append.restype = ctypes.c_int
     L.pkv_paged_attn_decode_append.argtypes = [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
                                                i32, i32, i32, i64, f32, i32, i32, p, sz, p]
+    L.pkv_paged_attn_decode_ex.restype = ctypes.c_int
+    L.pkv_paged_attn_decode_ex.argtypes = [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
+                                           i32, i32, i32, i64, f32, i32, i32, i32, p, sz, p]
     L.pkv_paged_attn_varlen.restype = ctypes.c_int
     L.pkv_paged_attn_varlen.argtypes = [p, p, p, p, p, p, p, p, i32, i64, i32, i32, i32, i32,
                                         i32, i32, i64, f32, i32, i32, p]
+    L.pkv_paged_attn_varlen_ex.restype = ctypes.c_int
+    L.pkv_paged_attn_varlen_ex.argtypes = [p, p, p, p, p, p, p, p, i32, i64, i32, i32, i32, i32,
+                                           i32, i32, i64, f32, i32, i32, i32, p]
     _lib = L
     return L
 
@@ -203,8 +210,17 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       q_rope: Optional[torch.Tensor] = None,
                       k_rope_cache: Optional[torch.Tensor] = None,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                      workspace: Optional[torch.Tensor] = None):
-    """Decode attention (see pkv_paged_attn_decode).  Returns (out, lse or None)."""
+                      workspace: Optional[torch.Tensor] = None, window: int = 0):
+    """Decode attention (see pkv_paged_attn_decode; window > 0: the sliding-window form
+    pkv_paged_attn_decode_ex, MHA/GQA only).  Returns (out, lse or None)."""
+    if window:
+        if q_rope is not None or k_rope_cache is not None:
+            raise ValueError("a sliding window is supported for MHA/GQA decode only")
+        args, out, _ = _decode_append_args(q, None, None, k_cache, v_cache, block_table,
+                                           seq_lens_kv, max_seq_len_kv, softmax_scale, 3, out,
+                                           lse, workspace, None, window)
+        _check(lib().pkv_paged_attn_decode_ex(*args))
+        return out, lse
     args, out, _ = _decode_args(q, k_cache, v_cache, block_table, seq_lens_kv, max_seq_len_kv,
                                 softmax_scale, q_rope, k_rope_cache, out, lse, workspace)
     _check(lib().pkv_paged_attn_decode(*args))
@@ -239,7 +255,9 @@ def prepare_decode(q, k_cache, v_cache, block_table, seq_lens_kv, max_seq_len_kv
 
 
 def _decode_append_args(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
-                        max_seq_len_kv, softmax_scale, stages, out, lse, workspace, slots_out):
+                        max_seq_len_kv, softmax_scale, stages, out, lse, workspace, slots_out,
+                        window=0):
+    """Arguments of pkv_paged_attn_decode_ex (k_new/v_new None: plain decode)."""
     _dev(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv, out, lse, workspace,
          slots_out)
     B, hq, d = q.shape
@@ -250,33 +268,38 @@ def _decode_append_args(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens
         workspace = new_decode_workspace(B, hq, hkv, d, max_seq_len_kv, q.device)
     args = (_ptr(out), _ptr(lse), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
             _ptr(block_table), _ptr(seq_lens_kv), _ptr(slots_out), B, block_table.shape[1],
-            max_seq_len_kv, hq, hkv, d, bs, nb, float(softmax_scale), _dtype_code(q), stages,
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device))
+            max_seq_len_kv, hq, hkv, d, bs, nb, float(softmax_scale), _dtype_code(q), int(window),
+            stages, _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(q.device))
     return args, out, workspace
 
 
 def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
                              max_seq_len_kv, softmax_scale, out=None, lse=None, workspace=None,
-                             slots_out=None):
-    """Write this step's token and attend, in one pass (see pkv_paged_attn_decode_append)."""
+                             slots_out=None, window=0):
+    """Write this step's token and attend, in one pass (pkv_paged_attn_decode_ex with the new
+    rows; window > 0 keeps each sequence's `window` most recent keys)."""
+    if k_new is None or v_new is None:
+        raise ValueError("paged_attn_decode_append needs k_new and v_new")
     args, out, _ = _decode_append_args(q, k_new, v_new, k_cache, v_cache, block_table,
                                        seq_lens_kv, max_seq_len_kv, softmax_scale, 3, out, lse,
-                                       workspace, slots_out)
-    _check(lib().pkv_paged_attn_decode_append(*args))
+                                       workspace, slots_out, window)
+    _check(lib().pkv_paged_attn_decode_ex(*args))
     return out, lse
 
 
 def prepare_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
                           max_seq_len_kv, softmax_scale, out=None, lse=None, workspace=None,
-                          slots_out=None):
-    """(split pass, combine pass) prepared calls of pkv_paged_attn_decode_append."""
+                          slots_out=None, window=0):
+    """(split pass, combine pass) prepared calls of the write-and-attend decode
+    (pkv_paged_attn_decode_ex with the new rows)."""
     calls = []
     for stages in (1, 2):
         args, out, workspace = _decode_append_args(q, k_new, v_new, k_cache, v_cache,
                                                    block_table, seq_lens_kv, max_seq_len_kv,
                                                    softmax_scale, stages, out, lse, workspace,
-                                                   slots_out)
-        calls.append(PreparedCall(lib().pkv_paged_attn_decode_append, args,
+                                                   slots_out, window)
+        calls.append(PreparedCall(lib().pkv_paged_attn_decode_ex, args,
                                   (q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
                                    out, lse, workspace, slots_out)))
     return calls[0], calls[1], out
@@ -299,7 +322,8 @@ def prepare_kv_cache_write(k_new, v_new, k_cache, v_cache, slots):
 
 
 def _varlen_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, max_seqlen_q,
-                 softmax_scale, causal, out, lse):
+                 softmax_scale, causal, out, lse, window=0):
+    """Arguments of pkv_paged_attn_varlen_ex."""
     _dev(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, out, lse)
     T, hq, d = q.shape
     nb, bs, hkv, _ = k_cache.shape
@@ -308,7 +332,7 @@ def _varlen_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, ma
     args = (_ptr(out), _ptr(lse), _ptr(q), _ptr(cu_seqlens_q), _ptr(seq_lens_kv), _ptr(k_cache),
             _ptr(v_cache), _ptr(block_table), seq_lens_kv.shape[0], T, max_seqlen_q,
             block_table.shape[1], hq, hkv, d, bs, nb, float(softmax_scale), int(bool(causal)),
-            _dtype_code(q), _stream(q.device))
+            int(window), _dtype_code(q), _stream(q.device))
     return args, out
 
 
@@ -316,17 +340,18 @@ def paged_attn_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       block_table: torch.Tensor, cu_seqlens_q: torch.Tensor,
                       seq_lens_kv: torch.Tensor, max_seqlen_q: int, softmax_scale: float,
                       causal: bool = True, out: Optional[torch.Tensor] = None,
-                      lse: Optional[torch.Tensor] = None):
-    """Packed varlen attention over the paged cache (see pkv_paged_attn_varlen)."""
+                      lse: Optional[torch.Tensor] = None, window: int = 0):
+    """Packed varlen attention over the paged cache (pkv_paged_attn_varlen_ex; window > 0
+    keeps each row's `window` most recent visible keys)."""
     args, out = _varlen_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv,
-                             max_seqlen_q, softmax_scale, causal, out, lse)
-    _check(lib().pkv_paged_attn_varlen(*args))
+                             max_seqlen_q, softmax_scale, causal, out, lse, window)
+    _check(lib().pkv_paged_attn_varlen_ex(*args))
     return out, lse
 
 
 def prepare_varlen(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, max_seqlen_q,
-                   softmax_scale, causal=True, out=None, lse=None):
+                   softmax_scale, causal=True, out=None, lse=None, window=0):
     args, out = _varlen_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv,
-                             max_seqlen_q, softmax_scale, causal, out, lse)
-    return PreparedCall(lib().pkv_paged_attn_varlen, args,
+                             max_seqlen_q, softmax_scale, causal, out, lse, window)
+    return PreparedCall(lib().pkv_paged_attn_varlen_ex, args,
                         (q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, out, lse))

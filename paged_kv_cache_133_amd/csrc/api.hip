@@ -161,8 +161,10 @@ int prepare_decode(pkv::DecodeParams& p, pkv::DecodePlan& plan, void* out, float
                    int32_t max_seq_len_kv, int32_t num_q_heads, int32_t num_kv_heads,
                    int32_t head_dim_qk, int32_t head_dim_v, int32_t head_dim_rope,
                    int32_t block_size, int64_t num_blocks, float softmax_scale, int32_t dtype,
-                   void* workspace, size_t workspace_bytes, bool* nothing_to_do) {
+                   void* workspace, size_t workspace_bytes, bool* nothing_to_do,
+                   int32_t window = 0) {
     *nothing_to_do = false;
+    if (window < 0) return fail(PKV_ERR_SHAPE, "decode: window must be >= 0 (0: no window)");
     if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "decode: unknown dtype %d", dtype);
     if (batch < 0) return fail(PKV_ERR_SHAPE, "decode: negative batch");
     if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
@@ -200,7 +202,10 @@ int prepare_decode(pkv::DecodeParams& p, pkv::DecodePlan& plan, void* out, float
         return fail(PKV_ERR_NULL, "decode: NULL pointer argument");
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return fail(PKV_ERR_ALIGN, "decode: out, q and caches must be 16-byte aligned");
-    plan = pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim_v, max_seq_len_kv);
+    // With a window a sequence's splits cover at most window + 31 keys (they start at the
+    // window start rounded down to 32): plan for that length.
+    const int32_t plan_len = window > 0 && window < max_seq_len_kv - 31 ? window + 31 : max_seq_len_kv;
+    plan = pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim_v, plan_len);
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))
         return fail(PKV_ERR_WORKSPACE, "decode: workspace needs %zu bytes (16-byte aligned), got %zu",
                     plan.ws_bytes, workspace ? workspace_bytes : (size_t)0);
@@ -229,6 +234,7 @@ int prepare_decode(pkv::DecodeParams& p, pkv::DecodePlan& plan, void* out, float
     p.len_cap = max_seq_len_kv;
     p.num_blocks = num_blocks;
     p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+    p.window = window;
     if (pkv::gqa_stream_supported(dtype, group, head_dim_v, p.bs_log2, batch)) {
         p.parts = plan.parts;
         p.ws_o = reinterpret_cast<float*>(ws + plan.st_o_offset);
@@ -259,6 +265,7 @@ int launch_combine_for(const pkv::DecodeParams& p, int32_t head_dim_v, int32_t d
     c.split_tokens = p.split_tokens;
     c.max_splits = p.max_splits;
     c.len_cap = p.len_cap;
+    c.window = p.window;
     return hip_status(pkv::launch_combine(c, dtype, s), "decode combine launch");
 }
 
@@ -457,6 +464,53 @@ int pkv_paged_attn_decode_combine(void* out, float* lse_out, const void* q, cons
 
 #undef PKV_DECODE_ARGS
 
+}  // extern "C"
+
+namespace {
+
+// MHA/GQA decode with an optional sliding window and an optional new token per sequence
+// (k_new/v_new given: written at position seq_lens_kv[b] - 1 in the same pass).
+int run_decode_mha(void* out, float* lse_out, const void* q, const void* k_new, const void* v_new,
+                   void* k_cache, void* v_cache, const int32_t* block_table,
+                   const int32_t* seq_lens_kv, int64_t* slot_mapping_out, int32_t batch,
+                   int32_t max_blocks_per_seq, int32_t max_seq_len_kv, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                   float softmax_scale, int32_t dtype, int32_t window, int32_t stages,
+                   void* workspace, size_t workspace_bytes, hipStream_t s, const char* who) {
+    if (stages < 1 || stages > 3) return fail(PKV_ERR_SHAPE, "%s: stages must be 1, 2 or 3", who);
+    pkv::DecodeParams p;
+    pkv::DecodePlan plan{};
+    bool idle = false;
+    int rc = prepare_decode(p, plan, out, lse_out, q, nullptr, k_cache, v_cache, nullptr,
+                            block_table, seq_lens_kv, batch, max_blocks_per_seq, max_seq_len_kv,
+                            num_q_heads, num_kv_heads, head_dim, head_dim, 0, block_size,
+                            num_blocks, softmax_scale, dtype, workspace, workspace_bytes, &idle,
+                            window);
+    if (rc != PKV_OK || idle) return rc;
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return fail(PKV_ERR_NULL, "%s: k_new and v_new must be given together or not at all", who);
+    if (k_new) {
+        if (!aligned16(k_new) || !aligned16(v_new))
+            return fail(PKV_ERR_ALIGN, "%s: k_new and v_new must be 16-byte aligned", who);
+        if (k_cache == v_cache) return fail(PKV_ERR_SHAPE, "%s: k_cache and v_cache must differ", who);
+        p.k_new = k_new;
+        p.v_new = v_new;
+        p.k_cache_w = k_cache;
+        p.v_cache_w = v_cache;
+        p.slots_out = slot_mapping_out;
+    }
+    if (stages & 1) {
+        rc = hip_status(pkv::launch_decode(p, dtype, head_dim, s), "decode split launch");
+        if (rc != PKV_OK) return rc;
+    }
+    if ((stages & 2) && needs_combine(p, plan)) return launch_combine_for(p, head_dim, dtype, s);
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int pkv_paged_attn_decode_append(void* out, float* lse_out, const void* q, const void* k_new,
                                  const void* v_new, void* k_cache, void* v_cache,
                                  const int32_t* block_table, const int32_t* seq_lens_kv,
@@ -466,31 +520,26 @@ int pkv_paged_attn_decode_append(void* out, float* lse_out, const void* q, const
                                  int32_t block_size, int64_t num_blocks, float softmax_scale,
                                  int32_t dtype, int32_t stages, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-    if (stages < 1 || stages > 3) return fail(PKV_ERR_SHAPE, "decode_append: stages must be 1, 2 or 3");
-    pkv::DecodeParams p;
-    pkv::DecodePlan plan{};
-    bool idle = false;
-    int rc = prepare_decode(p, plan, out, lse_out, q, nullptr, k_cache, v_cache, nullptr,
-                            block_table, seq_lens_kv, batch, max_blocks_per_seq, max_seq_len_kv,
-                            num_q_heads, num_kv_heads, head_dim, head_dim, 0, block_size,
-                            num_blocks, softmax_scale, dtype, workspace, workspace_bytes, &idle);
-    if (rc != PKV_OK || idle) return rc;
     if (!k_new || !v_new) return fail(PKV_ERR_NULL, "decode_append: NULL k_new or v_new");
-    if (!aligned16(k_new) || !aligned16(v_new))
-        return fail(PKV_ERR_ALIGN, "decode_append: k_new and v_new must be 16-byte aligned");
-    if (k_cache == v_cache) return fail(PKV_ERR_SHAPE, "decode_append: k_cache and v_cache must differ");
-    p.k_new = k_new;
-    p.v_new = v_new;
-    p.k_cache_w = k_cache;
-    p.v_cache_w = v_cache;
-    p.slots_out = slot_mapping_out;
-    hipStream_t s = (hipStream_t)stream;
-    if (stages & 1) {
-        rc = hip_status(pkv::launch_decode(p, dtype, head_dim, s), "decode_append split launch");
-        if (rc != PKV_OK) return rc;
-    }
-    if ((stages & 2) && needs_combine(p, plan)) return launch_combine_for(p, head_dim, dtype, s);
-    return PKV_OK;
+    return run_decode_mha(out, lse_out, q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
+                          slot_mapping_out, batch, max_blocks_per_seq, max_seq_len_kv, num_q_heads,
+                          num_kv_heads, head_dim, block_size, num_blocks, softmax_scale, dtype, 0,
+                          stages, workspace, workspace_bytes, (hipStream_t)stream, "decode_append");
+}
+
+int pkv_paged_attn_decode_ex(void* out, float* lse_out, const void* q, const void* k_new,
+                             const void* v_new, void* k_cache, void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens_kv,
+                             int64_t* slot_mapping_out, int32_t batch, int32_t max_blocks_per_seq,
+                             int32_t max_seq_len_kv, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                             float softmax_scale, int32_t dtype, int32_t window, int32_t stages,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    return run_decode_mha(out, lse_out, q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
+                          slot_mapping_out, batch, max_blocks_per_seq, max_seq_len_kv, num_q_heads,
+                          num_kv_heads, head_dim, block_size, num_blocks, softmax_scale, dtype,
+                          window, stages, workspace, workspace_bytes, (hipStream_t)stream,
+                          "decode_ex");
 }
 
 int pkv_paged_attn_varlen(void* out, float* lse_out, const void* q, const int32_t* cu_seqlens_q,
@@ -500,6 +549,20 @@ int pkv_paged_attn_varlen(void* out, float* lse_out, const void* q, const int32_
                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                           int64_t num_blocks, float softmax_scale, int32_t causal, int32_t dtype,
                           void* stream) {
+    return pkv_paged_attn_varlen_ex(out, lse_out, q, cu_seqlens_q, seq_lens_kv, k_cache, v_cache,
+                                    block_table, batch, total_q, max_seqlen_q, max_blocks_per_seq,
+                                    num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                    softmax_scale, causal, 0, dtype, stream);
+}
+
+int pkv_paged_attn_varlen_ex(void* out, float* lse_out, const void* q, const int32_t* cu_seqlens_q,
+                             const int32_t* seq_lens_kv, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, int32_t batch, int64_t total_q,
+                             int32_t max_seqlen_q, int32_t max_blocks_per_seq, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int64_t num_blocks, float softmax_scale, int32_t causal, int32_t window,
+                             int32_t dtype, void* stream) {
+    if (window < 0) return fail(PKV_ERR_SHAPE, "varlen: window must be >= 0 (0: no window)");
     if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "varlen: unknown dtype %d", dtype);
     if (batch < 0 || total_q < 0 || max_seqlen_q < 0)
         return fail(PKV_ERR_SHAPE, "varlen: negative batch, total_q or max_seqlen_q");
@@ -545,6 +608,7 @@ int pkv_paged_attn_varlen(void* out, float* lse_out, const void* q, const int32_
                               ? 0x7fffffff : (int64_t)max_blocks_per_seq * block_size);
     p.q_blocks = (int32_t)qblocks;
     p.causal = causal ? 1 : 0;
+    p.window = window;
     p.num_blocks = num_blocks;
     p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
     return hip_status(pkv::launch_varlen(p, head_dim, (hipStream_t)stream), "varlen launch");

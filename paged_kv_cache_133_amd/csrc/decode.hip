@@ -110,7 +110,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int b = id % p.batch;
     const int split = id / p.batch;
     const int L = min(p.seq_lens[b], p.len_cap);
-    const int t0 = split * p.split_tokens;
+    // Keys [ks, L) are visible (a sliding window moves ks up); the splits start at ks
+    // rounded down to a step, and the keys below ks in the first one are not loaded.
+    const int ks = window_start(L, p.window);
+    const int ksa = ks & ~(kStepTokens - 1);
+    const int t0 = ksa + split * p.split_tokens;
     if (L <= 0) {   // no visible key: output 0, lse -inf
         if (split == 0) {
             for (int i = threadIdx.x; i < p.group * D; i += blockDim.x) {
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     }
     if (t0 >= L) return;
     const int t1 = min(L, t0 + p.split_tokens);
-    const int nsplit = (L + p.split_tokens - 1) / p.split_tokens;
+    const int nsplit = (L - ksa + p.split_tokens - 1) / p.split_tokens;
     const int per_wave = p.split_tokens / kWaves;
     const int w0 = t0 + wave * per_wave;
     const int w1 = min(t1, w0 + per_wave);
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int tok = base + j * TPW + row;
-            valid[j] = tok < w1;
+            valid[j] = tok >= ks && tok < w1;
             int32_t phys = __shfl(tbl, (tok >> p.bs_log2) - blk0, 64);
             phys = min(max(phys, 0), last_block);
             const int64_t slot = ((int64_t)phys << p.bs_log2) | (tok & bs_mask);
@@ -303,7 +307,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     const int64_t bh = blockIdx.x;
     const int b = (int)(bh / p.hq);
     const int L = min(p.seq_lens[b], p.len_cap);
-    const int ns = L > 0 ? (L + p.split_tokens - 1) / p.split_tokens : 0;
+    const int ns = L > 0 ? (L - window_start32(L, p.window) + p.split_tokens - 1) / p.split_tokens : 0;
     if (ns <= 1) return;   // the split kernel wrote this row directly
     const float* ml = p.ws_ml + bh * p.max_splits * 2;
     if (threadIdx.x == 0) {

@@ -56,13 +56,14 @@ struct GqaCfg {
 };
 
 // ------------------------------------------------------------------ per-tile math
-// Scores of the tile in `stage`: full tiles keep the raw S^T entries; a tile that runs
-// past the key range (kb + 32 > k_end) scales them and sets keys past it to -inf.  Entry
-// (h, r) of lane (g, n) is key kb + 16 h + 4 g + r.  Returns the head's max over the tile
-// (scaled, log2 units).
+// Scores of the tile in `stage`: full tiles keep the raw S^T entries; a tile that is not
+// wholly inside the key range [k_lo, k_end) scales them and sets keys outside it to -inf.
+// Entry (h, r) of lane (g, n) is key kb + 16 h + 4 g + r.  Returns the head's max over the
+// tile (scaled, log2 units).
 template <int D>
 __device__ __forceinline__ float tile_scores(const uint8_t* stage, const bf16x8_t* qf, int n, int g,
-                                             bool full, int kb, int k_end, float scale_log2, float* sv) {
+                                             bool full, int kb, int k_lo, int k_end, float scale_log2,
+                                             float* sv) {
     using C = GqaCfg<D>;
     f32x4 sacc[2];
 #pragma unroll
@@ -89,7 +90,7 @@ __device__ __forceinline__ float tile_scores(const uint8_t* stage, const bf16x8_
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int key = kb + 16 * (e >> 2) + 4 * g + (e & 3);
-            sv[e] = key < k_end ? sacc[e >> 2][e & 3] * scale_log2 : -INFINITY;
+            sv[e] = (key >= k_lo && key < k_end) ? sacc[e >> 2][e & 3] * scale_log2 : -INFINITY;
             tmax = fmaxf(tmax, sv[e]);
         }
     }
@@ -223,9 +224,10 @@ __device__ __forceinline__ int range_start(int w, int T, int P) { return (int)((
 __device__ __forceinline__ int range_of(int x, int T, int P) { return (int)(((int64_t)(x + 1) * P - 1) / T); }
 
 // Position in the end-to-end tile order: sequence b holds tiles [pre, end) and has
-// length L; seg counts the sequences with tiles entered so far.
+// length L; its visible keys start at ks (a sliding window moves it up) and its tiles at
+// ksa = ks rounded down to a tile; seg counts the sequences with tiles entered so far.
 struct Cursor {
-    int b, pre, end, L, seg;
+    int b, pre, end, L, ks, ksa, seg;
 };
 
 template <int D, bool APPEND>
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
     for (int c0 = 0; c0 < p.batch; c0 += 64) {
         const int b = c0 + lane;
         const int L = b < p.batch ? min(p.seq_lens[b], p.len_cap) : 0;
-        const int nt = L > 0 ? (L + kKeys - 1) / kKeys : 0;
+        const int nt = L > 0 ? (L - window_start32(L, p.window) + kKeys - 1) / kKeys : 0;
         int v = nt;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -320,6 +322,8 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         c.pre = __builtin_amdgcn_readfirstlane(s_pre[b]);
         c.end = __builtin_amdgcn_readfirstlane(s_pre[b + 1]);
         c.L = __builtin_amdgcn_readfirstlane(s_len[b]);
+        c.ks = window_start(c.L, p.window);
+        c.ksa = c.ks & ~(kKeys - 1);
         c.seg = 0;
         return c;
     };
@@ -332,6 +336,8 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
             c.end = __builtin_amdgcn_readfirstlane(s_pre[c.b + 1]);
         } while (x >= c.end);
         c.L = __builtin_amdgcn_readfirstlane(s_len[c.b]);
+        c.ks = window_start(c.L, p.window);
+        c.ksa = c.ks & ~(kKeys - 1);
         ++c.seg;
     };
 
@@ -359,7 +365,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
     int32_t pe_last = 0;              // entry of the block of the sequence's last key
     auto prep = [&](int u) {          // entries of local tile u
         advance(ic, x0 + u);
-        const int kb = (x0 + u - ic.pre) * kKeys;
+        const int kb = ic.ksa + (x0 + u - ic.pre) * kKeys;
         const int32_t* trow = p.table + (int64_t)ic.b * p.mbs;
         const int last_idx = (ic.L - 1) >> p.bs_log2;
 #pragma unroll
@@ -368,7 +374,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
     };
     auto issue = [&](int u) {         // loads of local tile u (prep(u) done)
         const int x = x0 + u;
-        const int kb = (x - ic.pre) * kKeys;
+        const int kb = ic.ksa + (x - ic.pre) * kKeys;
         uint8_t* stage = smem + (u % kStg) * C::kStage;
         if (x == ic.pre || u == 0) {  // first tile of a segment: its query rows first
             const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(p.q) + ((int64_t)ic.b * p.hq + kvh * G) * D * 2;
@@ -449,9 +455,10 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
                 wait_tile<C::kDma>(min(ntw - 1 - t, kStg - 2));
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 feed(t + kStg - 1);
-                const int kb = (x0 + t - cc.pre) * kKeys;
-                full = kb + kKeys <= cc.L;
-                tmax = tile_scores<D>(smem + (t % kStg) * C::kStage, qf, n, g, full, kb, cc.L, p.scale_log2, sv);
+                const int kb = cc.ksa + (x0 + t - cc.pre) * kKeys;
+                full = kb >= cc.ks && kb + kKeys <= cc.L;
+                tmax = tile_scores<D>(smem + (t % kStg) * C::kStage, qf, n, g, full, kb, cc.ks, cc.L,
+                                      p.scale_log2, sv);
                 if (__any(must_rescale(st, tmax))) break;
                 tile_pv<D>(smem + (t % kStg) * C::kStage, st, full, sv, p.scale_log2, n, g, oacc);
             }
@@ -570,7 +577,9 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
     const int kvh = blockIdx.x % p.hkv;
     int b, split;
     {
-        auto nsplits = [&](int, int len) { return len > 0 ? (len + p.split_tokens - 1) / p.split_tokens : 1; };
+        auto nsplits = [&](int, int len) {
+            return len > 0 ? (len - window_start32(len, p.window) + p.split_tokens - 1) / p.split_tokens : 1;
+        };
         if (!find_item<64>(blockIdx.x / p.hkv, p.batch, p.seq_lens, p.len_cap, nsplits,
                            reinterpret_cast<int32_t*>(smem + kStages * C::kStage), b, split))
             return;
@@ -585,7 +594,9 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
         if (valid) store_empty<D>(p, row, g);
         return;
     }
-    const int k_begin = split * p.split_tokens;
+    const int ks = window_start(L, p.window);                         // first visible key
+    const int ksa = ks & ~(kKeys - 1);
+    const int k_begin = ksa + split * p.split_tokens;
     if (k_begin >= L) return;
     const int k_end = min(L, k_begin + p.split_tokens);
     const int ntiles = (k_end - k_begin + kKeys - 1) / kKeys;
@@ -702,8 +713,9 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             feed(t + kStages - 1);
             const int kb = k_begin + t * kKeys;
-            full = kb + kKeys <= k_end;
-            tmax = tile_scores<D>(smem + (t % kStages) * C::kStage, qf, n, g, full, kb, k_end, p.scale_log2, sv);
+            full = kb >= ks && kb + kKeys <= k_end;
+            tmax = tile_scores<D>(smem + (t % kStages) * C::kStage, qf, n, g, full, kb, ks, k_end, p.scale_log2,
+                                  sv);
             if (__any(must_rescale(st, tmax))) break;
             tile_pv<D>(smem + (t % kStages) * C::kStage, st, full, sv, p.scale_log2, n, g, oacc);
         }
@@ -717,7 +729,7 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
     float l_tot = st.l + __shfl_xor(st.l, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
     if (!valid) return;
-    const int nsplit = (L + p.split_tokens - 1) / p.split_tokens;
+    const int nsplit = (L - ksa + p.split_tokens - 1) / p.split_tokens;
     if (nsplit == 1) {
         store_final<D>(p, row, g, st.m, l_tot, oacc);
     } else {

@@ -71,6 +71,12 @@ __device__ __forceinline__ float cross_row_sum(float v) {
 // 2^x in fp32 (v_exp_f32).  Arguments here are <= 0 or -inf; 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// First key a decode query at position L - 1 sees under a sliding window of `window` keys
+// (the band of "KVCache Optimization Skill", Appendix C, sparse_mode 4; window <= 0: none).
+__device__ __forceinline__ int window_start(int L, int window) { return window > 0 ? max(0, L - window) : 0; }
+// The same rounded down to a multiple of 32 keys: where a sequence's splits and tiles begin.
+__device__ __forceinline__ int window_start32(int L, int window) { return window_start(L, window) & ~31; }
+
 // 16-byte global load / store.
 __device__ __forceinline__ u32x4 ld16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);

@@ -99,6 +99,10 @@ struct DecodeParams {
     // [B + 1] it leaves for its combine; ws_o / ws_ml then hold its partial states.
     int32_t parts;
     int32_t* tile_prefix;
+    // Sliding window (band): > 0 keeps the `window` most recent keys of each sequence
+    // (window_start below); 0 keeps all of them.  Splits and tiles then start at the
+    // window start rounded down to a multiple of 32 keys.
+    int32_t window;
 };
 // dtype: 0 f32, 1 bf16; head_dim 64 or 128.  bf16 with 4..16 query heads per kv head runs
 // on the matrix cores (launch_gqa_decode: the range-streaming kernel when p.parts > 0,
@@ -118,6 +122,7 @@ struct CombineParams {
     const float* ws_ml;
     const int32_t* seq_lens;
     int32_t batch, hq, dim, split_tokens, max_splits, len_cap;
+    int32_t window;          // as DecodeParams::window (the splits start where the pass put them)
 };
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t s);
 
@@ -145,6 +150,7 @@ struct MfmaParams {
     int32_t len_cap;
     int32_t q_blocks;        // varlen: query blocks per sequence in the grid
     int32_t causal;
+    int32_t window;          // varlen: > 0 keeps each row's `window` most recent visible keys
     int64_t num_blocks;
     float scale_log2;
 };

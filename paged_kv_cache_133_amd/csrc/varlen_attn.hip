@@ -86,7 +86,13 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
     const int k_end = p.causal ? min(L, L - nq + i_last + 1) : L;
     // keys below full_end are visible to every row of the workgroup
     const int full_end = p.causal ? min(k_end, L - nq + i_first + 1) : k_end;
-    const int ntiles = (k_end + kKeys - 1) / kKeys;
+    // Sliding window: a row sees keys [vis - window + 1, vis]; the workgroup's tiles start
+    // at its first row's lower bound rounded down to a tile, and keys from full_lo on are
+    // above every row's lower bound.
+    const int lo_row = p.window > 0 ? vis - p.window + 1 : 0;
+    const int kstart = p.window > 0 ? max(0, (p.causal ? L - nq + i_first : L - 1) - p.window + 1) & ~(kKeys - 1) : 0;
+    const int full_lo = p.window > 0 ? (p.causal ? L - nq + i_last : L - 1) - p.window + 1 : 0;
+    const int ntiles = (k_end - kstart + kKeys - 1) / kKeys;
 
     bf16x8_t qf[C::kSteps];
     {
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
     TableChunks<C::kThreads> tab;
     tab.lds = reinterpret_cast<int32_t*>(smem + kStages * C::kStage);
     tab.row = p.table + (int64_t)b * p.mbs;
-    tab.k_begin = 0;
+    tab.k_begin = kstart;
     tab.k_end = k_end;
     tab.bs_log2 = p.bs_log2;
     tab.tid = tid;
@@ -136,11 +142,11 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
                        (uint32_t)swz<C::kRowChunks, C::kRowShift>(r, q % C::kRowChunks) * 16u;
     }
     // The table entry of the next tile is read one tile ahead, off the critical path.
-    auto fast_tile = [&](int u) { return fast_rows && (u + 1) * kKeys <= k_end; };
-    auto entry_of = [&](int u) { return uniform_load(tab.row + ((u * kKeys + 16 * (wid_u & 1)) >> p.bs_log2)); };
+    auto fast_tile = [&](int u) { return fast_rows && kstart + (u + 1) * kKeys <= k_end; };
+    auto entry_of = [&](int u) { return uniform_load(tab.row + ((kstart + u * kKeys + 16 * (wid_u & 1)) >> p.bs_log2)); };
     int32_t next_entry = fast_tile(0) ? entry_of(0) : 0;
     auto issue_tile = [&](int u) {
-        const int kb = u * kKeys;
+        const int kb = kstart + u * kKeys;
         const int chunk = u / kChunkTiles;
         uint8_t* stage = smem + (u % kStages) * C::kStage;
         const int32_t entry = next_entry;
@@ -200,12 +206,12 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
             for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sv[r]);
             tmax *= p.scale_log2;
         } else {
-            const int kb = t * kKeys;
+            const int kb = kstart + t * kKeys;
             tmax = -INFINITY;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = kb + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-                const bool ok = valid && key < k_end && key <= vis;
+                const bool ok = valid && key >= lo_row && key < k_end && key <= vis;
                 sv[r] = ok ? sacc[r] * p.scale_log2 : -INFINITY;
                 tmax = fmaxf(tmax, sv[r]);
             }
@@ -294,7 +300,7 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
             wait_tile<C::kDma>(min(ntiles - 1 - t, kStages - 2));
             block_sync();
             feed(t + kStages - 1);
-            full = t * kKeys + kKeys <= full_end;
+            full = kstart + t * kKeys >= full_lo && kstart + t * kKeys + kKeys <= full_end;
             tmax = scores(t, full, sv);
             const bool grow = tmax > st.m + kRescaleSlack || (st.m == -INFINITY && tmax != -INFINITY);
             if (__any(grow)) break;

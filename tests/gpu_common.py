@@ -25,7 +25,7 @@ def say(msg):
     sys.stdout.flush()
 
 
-def gpu_step(c, causal=False, want_lse=True):
+def gpu_step(c, causal=False, want_lse=True, window=0):
     """slot_mapping, cache write and attention for case `c` (tensors on the GPU)."""
     w = c.w
     dev = c.q.device
@@ -47,10 +47,10 @@ def gpu_step(c, causal=False, want_lse=True):
     lse = torch.empty((T, w.num_q_heads), dtype=torch.float32, device=dev) if want_lse else None
     if w.mode == "varlen":
         out, _ = pkv.paged_attn_varlen(c.q, k, v, table, cu, la, c.max_new, w.scale,
-                                       causal=causal, lse=lse)
+                                       causal=causal, lse=lse, window=window)
     else:
         out, _ = pkv.paged_attn_decode(c.q, k, v, table, la, c.max_len_after, w.scale,
-                                       q_rope=c.q_rope, k_rope_cache=rope, lse=lse)
+                                       q_rope=c.q_rope, k_rope_cache=rope, lse=lse, window=window)
     torch.cuda.synchronize()
     return {"slots": slots, "cache_k": k, "cache_v": v, "cache_rope": rope, "out": out,
             "lse": lse}

@@ -214,3 +214,36 @@ def test_binding_refuses_cpu_tensors():
     t = torch.zeros(4)
     with pytest.raises(ValueError):
         L.kv_cache_write(t, t, t, t, t)
+
+
+def test_window_forms_reject_bad_arguments():
+    """The sliding-window entry points check their extra arguments on the host."""
+    L = _lib().lib()
+
+    def dec(**kw):
+        a = dict(out=FAKE, lse=None, q=FAKE, kn=None, vn=None, kc=FAKE, vc=ctypes.c_void_p(0x200000),
+                 t=FAKE, lens=FAKE, so=None, B=2, mbs=4, mx=64, hq=8, hkv=2, d=128, bs=16, nb=8,
+                 scale=0.1, dt=1, win=16, st=3)
+        a.update(kw)
+        return L.pkv_paged_attn_decode_ex(a["out"], a["lse"], a["q"], a["kn"], a["vn"], a["kc"],
+                                          a["vc"], a["t"], a["lens"], a["so"], a["B"], a["mbs"],
+                                          a["mx"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"],
+                                          a["scale"], a["dt"], a["win"], a["st"], FAKE, 1 << 30,
+                                          None)
+    assert dec(win=-1) == -2
+    assert dec(st=0) == -2
+    assert dec(st=4) == -2
+    assert dec(kn=FAKE) == -1                    # k_new without v_new
+    assert dec(kn=FAKE, vn=FAKE, vc=FAKE) == -2  # append into one cache for K and V
+    assert dec(d=96) == -4
+    assert dec(B=0) == 0
+
+    def var(**kw):
+        a = dict(win=8, causal=1, dtype=1, d=64, B=2)
+        a.update(kw)
+        return L.pkv_paged_attn_varlen_ex(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], 8,
+                                          4, 4, 4, 1, a["d"], 16, 32, 0.125, a["causal"], a["win"],
+                                          a["dtype"], None)
+    assert var(win=-3) == -2
+    assert var(d=96) == -4
+    assert var(B=0) == 0
