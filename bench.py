@@ -107,15 +107,32 @@ def read_traffic(workload: str, kernel: str, sources):
         return None
 
 
-def algorithmic_flops(case):
-    """Flops of the attention kernel: 2 (Dqk + Dv) per visible (query row, key) pair."""
+def visible_keys(case):
+    """Per sequence: (keys some query row sees, visible (query row, key) pairs), with
+    bottom-right causal rows for varlen and the workload's sliding window."""
+    import numpy as np
     w = case.w
     L = case.lens_before.astype("int64")
     n = case.n_new.astype("int64")
+    Lp = L + n
     if w.mode == "varlen":
-        pairs = int((n * L + n * (n + 1) // 2).sum())          # bottom-right causal
+        # row i sees keys [0, L + i]: i + L + 1 of them, at most `window`
+        rows = [np.arange(int(k)) + int(b) + 1 for b, k in zip(L, n)]
+        if w.window:
+            rows = [np.minimum(r, w.window) for r in rows]
+        pairs = np.array([int(r.sum()) for r in rows], np.int64)
+        first = np.maximum(0, L + 1 - w.window) if w.window else np.zeros_like(L)
+        keys = Lp - first
     else:
-        pairs = int((L + n).sum())                             # decode: every key
+        keys = np.minimum(Lp, w.window) if w.window else Lp
+        pairs = keys.copy()
+    return keys, pairs
+
+
+def algorithmic_flops(case):
+    """Flops of the attention kernel: 2 (Dqk + Dv) per visible (query row, key) pair."""
+    w = case.w
+    pairs = int(visible_keys(case)[1].sum())
     return pairs * w.num_q_heads * 2 * (w.head_dim + w.head_dim_rope + w.head_dim_v)
 
 
@@ -123,7 +140,7 @@ def algorithmic_bytes(case):
     """(kv_read, split_kernel, step) algorithmic bytes of one step."""
     w = case.w
     e = w.elem_bytes
-    Lp = case.lens_after.astype("int64")
+    Lp = visible_keys(case)[0]                     # keys some row of the sequence sees
     B, T = w.batch, case.num_tokens
     if w.mode == "mla":
         row = w.head_dim + w.head_dim_rope          # nope read once (key and value) + rope
@@ -176,7 +193,7 @@ def cpu_baseline(case, kv_bytes, min_seconds):
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        oracle.decode_step(h, causal=(c.w.mode == "varlen"))
+        oracle.decode_step(h, causal=(c.w.mode == "varlen"), window=c.w.window)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start >= min_seconds and len(times) >= 3:
             break
@@ -244,16 +261,19 @@ def main():
         if w.mode == "varlen":
             write = _lib.prepare_kv_cache_append(*pair, table, lb, cu, case.max_new, slots)
             attn = _lib.prepare_varlen(case.q, k, v, table, cu, la, case.max_new, w.scale,
-                                       causal=True, out=out, lse=lse)
+                                       causal=True, out=out, lse=lse, window=w.window)
             reps.append((write, attn, None))
             continue
         if fused and not mla:
             split, combine, _ = _lib.prepare_decode_append(case.q, case.new_k, case.new_v, k, v,
                                                            table, la, case.max_len_after, w.scale,
                                                            out=out, lse=lse, workspace=ws,
-                                                           slots_out=slots)
+                                                           slots_out=slots, window=w.window)
             reps.append((None, split, combine))
             continue
+        if w.window:
+            print("bench.py: sliding-window workloads run the fused path only", file=sys.stderr)
+            sys.exit(2)
         if args.path == "separate":
             write = _lib.prepare_kv_cache_write(*pair, slots)
         else:
@@ -333,7 +353,7 @@ def main():
 
     cfg = {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "head_dim_v": w.head_dim_v,
-           "head_dim_rope": w.head_dim_rope, "block_size": w.block_size,
+           "head_dim_rope": w.head_dim_rope, "block_size": w.block_size, "window": w.window,
            "num_blocks": case.num_blocks, "seed": args.seed,
            "kv_tokens": int(case.lens_after.sum()), "max_kv_len": case.max_len_after,
            "pool_replicas": R,

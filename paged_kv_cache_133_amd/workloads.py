@@ -52,6 +52,7 @@ class Workload:
     scale: float
     max_blocks_per_seq: int
     description: str = ""
+    window: int = 0           # sliding window (keys each query row sees; 0: all)
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -84,7 +85,20 @@ VARLEN = Workload("varlen_causal_bf16", "varlen", 16, 32, 8, 128, 128, 0, 128, "
                   "(median 300, sigma 1, clipped [50,3000]), prefix U{0..4096}, "
                   "32 q / 8 kv heads, head_dim 128, bs 128, bf16")
 
-WORKLOADS = {w.name: w for w in (TINY, LLAMA7B, GQA_LONG, MLA, VARLEN)}
+# Two more for the band and MTP rows (beyond the five above): a Mistral-7B-shaped
+# sliding-window decode (window 4096 on long contexts) and an MTP decode step with
+# next_n = 1 (two causal query tokens per sequence through the varlen path).
+SWA_DECODE = Workload("swa_decode_bf16", "decode", 32, 32, 8, 128, 128, 0, 16, "bf16",
+                      1.0 / math.sqrt(128.0), 2049,
+                      "sliding-window GQA decode: B=32, 32 q / 8 kv heads, head_dim 128, bs 16, "
+                      "kv lengths log-uniform [1024, 32768], window 4096, bf16", window=4096)
+MTP_DECODE = Workload("mtp_decode_bf16", "varlen", 32, 32, 8, 128, 128, 0, 16, "bf16",
+                      1.0 / math.sqrt(128.0), 129,
+                      "MTP decode (next_n = 1): B=32, 2 causal query tokens per sequence, "
+                      "32 q / 8 kv heads, head_dim 128, bs 16, kv lengths U{512..2048} before "
+                      "the step, bf16")
+
+WORKLOADS = {w.name: w for w in (TINY, LLAMA7B, GQA_LONG, MLA, VARLEN, SWA_DECODE, MTP_DECODE)}
 
 
 def sample_lengths(w: Workload, seed: int) -> tuple[np.ndarray, np.ndarray]:
@@ -100,6 +114,11 @@ def sample_lengths(w: Workload, seed: int) -> tuple[np.ndarray, np.ndarray]:
         return np.clip(np.round(np.exp(u)), 1024, 32768).astype(np.int64), np.ones(B, np.int64)
     if w.name == MLA.name:
         return rng.integers(2048, 8192, size=B, endpoint=True), np.ones(B, np.int64)
+    if w.name == SWA_DECODE.name:
+        u = rng.uniform(math.log(1024.0), math.log(32768.0), size=B)
+        return np.clip(np.round(np.exp(u)), 1024, 32768).astype(np.int64), np.ones(B, np.int64)
+    if w.name == MTP_DECODE.name:
+        return rng.integers(512, 2048, size=B, endpoint=True), np.full(B, 2, np.int64)
     if w.name == VARLEN.name:
         n = np.clip(np.round(rng.lognormal(math.log(300.0), 1.0, size=B)), 50, 3000)
         L = rng.integers(0, 4096, size=B, endpoint=True)

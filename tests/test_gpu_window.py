@@ -83,3 +83,30 @@ def test_mtp_decode_through_varlen():
         o = oracle_step(c, causal=True, window=window)
         compare_writes(c, g, o)
         compare_outputs(c, g, o, tokens=o["tokens"], label=f"mtp window {window}")
+
+
+@pytest.mark.parametrize("name", ["swa_decode_bf16", "mtp_decode_bf16"])
+def test_window_and_mtp_workloads_sampled(name):
+    """The full-size band and MTP workloads as the bench runs them (write-and-attend for the
+    band, write + varlen for MTP); the oracle checks the longest, the shortest and two other
+    sequences."""
+    w = wl.WORKLOADS[name]
+    say(f"full workload {name} (sampled sequences)")
+    c = wl.make_workload_case(w, seed=0, device=DEV)
+    order = np.argsort(c.lens_after)
+    rows = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 3})
+    o = oracle_step(c, causal=w.mode == "varlen", rows=rows, window=w.window)
+    if w.mode == "varlen":
+        g = gpu_step(c, causal=True, window=w.window)
+    else:
+        B = w.batch
+        k, v = c.cache_k.clone(), c.cache_v.clone()
+        slots = torch.full((B,), -3, dtype=torch.int64, device=DEV)
+        lse = torch.empty((B, w.num_q_heads), dtype=torch.float32, device=DEV)
+        out, _ = pkv.paged_attn_decode_append(c.q, c.new_k, c.new_v, k, v, c.table_tensor(DEV),
+                                              c.lens_after_tensor(DEV), c.max_len_after, w.scale,
+                                              lse=lse, slots_out=slots, window=w.window)
+        torch.cuda.synchronize()
+        g = {"slots": slots, "cache_k": k, "cache_v": v, "out": out, "lse": lse}
+    compare_writes(c, g, o)
+    compare_outputs(c, g, o, tokens=o["tokens"], label=name)
