@@ -2,8 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's CPU-baseline
 leg may import this module; the product path never does.  It shares no code with
-the HIP library.  Arithmetic lives in pkv_oracle.c; this file marshals arrays and
-holds the two host-side formulas the pages print in Python form:
+the HIP library.  The hot-path arithmetic lives in pkv_oracle.c; this file marshals
+arrays, computes the upstream RMSNorm + RoPE of the MLA latent row in numpy fp64
+(rmsnorm_rope), and holds the two host-side formulas the pages print in Python form:
 
   * packing (hotelren.com source note "Paged KV Cache and Packed Sequence",
     section 3.1): seq_offset is the prefix sum of the lengths with a leading 0,
@@ -191,6 +192,37 @@ def merge_states(m, l, o):
     lse = np.zeros(rows, np.float64)
     _check(lib().orc_merge_states(_ptr(m), _ptr(l), _ptr(o), S, rows, D, _ptr(out), _ptr(lse)))
     return out, lse
+
+
+# --------------------------------------------------------------------------- upstream of the write
+def widen(a: np.ndarray) -> np.ndarray:
+    """fp64 copy of fp32 values or of bf16 bit patterns (uint16 storage; exact)."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def rmsnorm_rope(kv, gamma, cos, sin, head_dim_nope: int, eps: float):
+    """The fused normalise-rotate step in front of the MLA cache write ("KVCache
+    Optimization Skill", Mode 3 and its fused write npu_kv_rmsnorm_rope_cache, which the
+    pages name without defining; the readings below are this build's).  For every token
+    row kv[t] = [c (head_dim_nope) | k_pe (head_dim_rope)]:
+      nope[t] = c / sqrt(mean(c^2) + eps) * gamma                         (RMSNorm)
+      rope[t] = [x1 cos - x2 sin | x2 cos + x1 sin], x1 = k_pe[:Dr/2], x2 = k_pe[Dr/2:]
+    (rotary embedding in the half-split form: pair (x1[i], x2[i]) turned by the angle whose
+    cosine and sine are cos[t, i] and sin[t, i]).  fp64, unrounded; returns (nope, rope)."""
+    x = widen(kv)
+    g = widen(gamma)
+    c = np.asarray(cos, np.float64)
+    s_ = np.asarray(sin, np.float64)
+    xn, xr = x[:, :head_dim_nope], x[:, head_dim_nope:]
+    rms = np.sqrt((xn * xn).mean(axis=1) + float(eps))
+    nope = xn / rms[:, None] * g[None, :]
+    h = xr.shape[1] // 2
+    x1, x2 = xr[:, :h], xr[:, h:]
+    rope = np.concatenate([x1 * c - x2 * s_, x2 * c + x1 * s_], axis=1)
+    return nope, rope
 
 
 # --------------------------------------------------------------------------- host formulas
