@@ -125,6 +125,30 @@ PKV_API int pkv_kv_cache_append(const void* k_new, const void* v_new, void* k_ca
                         int32_t block_size, int64_t num_blocks, int32_t dtype, void* stream);
 
 /*
+ * The MLA latent row normalised, rotated and written in one launch: the fused writer the
+ * pages place in front of the MLA cache (npu_kv_rmsnorm_rope_cache, keyed by slot_mapping;
+ * "KVCache Optimization Skill", Mode 3 and its cache-write fusion note), which they name
+ * without defining.  Readings taken: for token t with kv[t] = [c | k_pe],
+ *   cache_nope[slot_t] = c / sqrt(mean(c^2) + eps) * gamma                 (RMSNorm)
+ *   cache_rope[slot_t] = [x1 cos - x2 sin | x2 cos + x1 sin]                (rotary, half-split)
+ * with x1 = k_pe[:Dr/2], x2 = k_pe[Dr/2:], cos = cos[t], sin = sin[t] (the caller's angles for
+ * the token's position).  fp32 arithmetic, one rounding to the cache dtype.
+ *   kv [num_tokens][head_dim_nope + head_dim_rope], gamma [head_dim_nope], both in dtype
+ *   cos, sin [num_tokens][head_dim_rope / 2] fp32
+ *   cache_nope [num_blocks][block_size][1][head_dim_nope], cache_rope [...][1][head_dim_rope]
+ *   slot_mapping [num_tokens] int64 (as for pkv_kv_cache_write; slots outside the pool are
+ *   skipped)
+ * Supported: f32 or bf16; head_dim_nope a multiple of 16 bytes' worth of elements, at most
+ * 1024 (bf16) / 512 (f32); head_dim_rope a multiple of 32 bytes' worth, at most 256 / 128.
+ * All arrays 16-byte aligned.
+ */
+PKV_API int pkv_kv_rmsnorm_rope_cache(const void* kv, const void* gamma, const float* cos,
+                              const float* sin, void* cache_nope, void* cache_rope,
+                              const int64_t* slot_mapping, int64_t num_tokens,
+                              int32_t head_dim_nope, int32_t head_dim_rope, int32_t block_size,
+                              int64_t num_blocks, float eps, int32_t dtype, void* stream);
+
+/*
  * Bytes of workspace pkv_paged_attn_decode needs for these sizes (0 if none).  The
  * workspace holds split-KV partial results; its contents need no initialisation, and
  * calls that may run at the same time need separate workspaces.

@@ -22,7 +22,8 @@ STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_SHAPE", -3: "PKV_ERR_DTY
           -4: "PKV_ERR_UNSUPPORTED", -5: "PKV_ERR_ALIGN", -6: "PKV_ERR_SCALE",
           -7: "PKV_ERR_WORKSPACE", -8: "PKV_ERR_HIP"}
 EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_write",
-           "pkv_kv_cache_append", "pkv_decode_workspace_size", "pkv_paged_attn_decode",
+           "pkv_kv_cache_append", "pkv_kv_rmsnorm_rope_cache", "pkv_decode_workspace_size",
+           "pkv_paged_attn_decode",
            "pkv_paged_attn_decode_split", "pkv_paged_attn_decode_combine",
            "pkv_paged_attn_decode_append", "pkv_paged_attn_decode_ex", "pkv_paged_attn_varlen",
            "pkv_paged_attn_varlen_ex")
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.pkv_kv_cache_append.restype = ctypes.c_int
     L.pkv_kv_cache_append.argtypes = [p, p, p, p, p, p, p, p, i32, i64, i32, i32, i32, i32, i32,
                                       i32, i64, i32, p]
+    L.pkv_kv_rmsnorm_rope_cache.restype = ctypes.c_int
+    L.pkv_kv_rmsnorm_rope_cache.argtypes = [p, p, p, p, p, p, p, i64, i32, i32, i32, i64, f32, i32, p]
     L.pkv_decode_workspace_size.restype = sz
     L.pkv_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     for name in ("pkv_paged_attn_decode", "pkv_paged_attn_decode_split",
@@ -171,6 +174,20 @@ def prepare_kv_cache_append(k_new, v_new, k_cache, v_cache, block_table, lens_be
     return PreparedCall(lib().pkv_kv_cache_append, args,
                         (k_new, v_new, k_cache, v_cache, block_table, lens_before, cu_new,
                          slots_out))
+
+
+def kv_rmsnorm_rope_cache(kv: torch.Tensor, gamma: torch.Tensor, cos: torch.Tensor,
+                          sin: torch.Tensor, cache_nope: torch.Tensor, cache_rope: torch.Tensor,
+                          slot_mapping: torch.Tensor, eps: float = 1e-6):
+    """RMSNorm + RoPE + write of the MLA latent row (see pkv_kv_rmsnorm_rope_cache).
+    kv [T, Dn + Dr], gamma [Dn], cos/sin [T, Dr/2] fp32, caches [nb, bs, 1, Dn/Dr]."""
+    _dev(kv, gamma, cos, sin, cache_nope, cache_rope, slot_mapping)
+    nb, bs, _, dn = cache_nope.shape
+    dr = cache_rope.shape[-1]
+    _check(lib().pkv_kv_rmsnorm_rope_cache(_ptr(kv), _ptr(gamma), _ptr(cos), _ptr(sin),
+                                           _ptr(cache_nope), _ptr(cache_rope), _ptr(slot_mapping),
+                                           slot_mapping.shape[0], dn, dr, bs, nb, float(eps),
+                                           _dtype_code(kv), _stream(kv.device)))
 
 
 def new_decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_dim_v: int,

@@ -139,6 +139,51 @@ int pkv_kv_cache_append(const void* k_new, const void* v_new, void* k_cache, voi
     return hip_status(pkv::launch_kv_append(p, (hipStream_t)stream), "kv_cache_append launch");
 }
 
+int pkv_kv_rmsnorm_rope_cache(const void* kv, const void* gamma, const float* cos, const float* sin,
+                              void* cache_nope, void* cache_rope, const int64_t* slot_mapping,
+                              int64_t num_tokens, int32_t head_dim_nope, int32_t head_dim_rope,
+                              int32_t block_size, int64_t num_blocks, float eps, int32_t dtype,
+                              void* stream) {
+    if (dtype != PKV_F32 && dtype != PKV_BF16)
+        return fail(PKV_ERR_DTYPE, "kv_rmsnorm_rope_cache: unknown dtype %d", dtype);
+    if (num_tokens < 0 || head_dim_nope <= 0 || head_dim_rope <= 0 || num_blocks <= 0)
+        return fail(PKV_ERR_SHAPE, "kv_rmsnorm_rope_cache: head dims and num_blocks must be positive");
+    if (!pow2_in(block_size, 1, 256))
+        return fail(PKV_ERR_UNSUPPORTED, "kv_rmsnorm_rope_cache: block_size %d is not a power of two in [1, 256]",
+                    block_size);
+    const int per16 = 16 / elem_bytes(dtype);
+    if (head_dim_nope % per16 || head_dim_nope / per16 > 128 || head_dim_rope % (2 * per16) ||
+        head_dim_rope / 2 / per16 > 64)
+        return fail(PKV_ERR_UNSUPPORTED,
+                    "kv_rmsnorm_rope_cache: head_dim_nope must be a multiple of %d up to %d and head_dim_rope "
+                    "a multiple of %d up to %d",
+                    per16, 128 * per16, 2 * per16, 128 * per16);
+    if (!isfinite(eps) || eps < 0.0f) return fail(PKV_ERR_SHAPE, "kv_rmsnorm_rope_cache: eps must be finite and >= 0");
+    if (num_tokens > 0x7fffffffLL * 4) return fail(PKV_ERR_UNSUPPORTED, "kv_rmsnorm_rope_cache: too many tokens");
+    if (num_tokens == 0) return PKV_OK;
+    if (!kv || !gamma || !cos || !sin || !cache_nope || !cache_rope || !slot_mapping)
+        return fail(PKV_ERR_NULL, "kv_rmsnorm_rope_cache: NULL pointer argument");
+    if (!aligned16(kv) || !aligned16(gamma) || !aligned16(cos) || !aligned16(sin) || !aligned16(cache_nope) ||
+        !aligned16(cache_rope))
+        return fail(PKV_ERR_ALIGN, "kv_rmsnorm_rope_cache: kv, gamma, cos, sin and caches must be 16-byte aligned");
+    if (cache_nope == cache_rope)
+        return fail(PKV_ERR_SHAPE, "kv_rmsnorm_rope_cache: cache_nope and cache_rope must differ");
+    pkv::NormRopeParams p{};
+    p.kv = kv;
+    p.gamma = gamma;
+    p.cos = cos;
+    p.sin = sin;
+    p.cache_nope = cache_nope;
+    p.cache_rope = cache_rope;
+    p.slots = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.num_slots = num_blocks * block_size;
+    p.dn = head_dim_nope;
+    p.dr = head_dim_rope;
+    p.eps = eps;
+    return hip_status(pkv::launch_norm_rope_write(p, dtype, (hipStream_t)stream), "kv_rmsnorm_rope_cache launch");
+}
+
 size_t pkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim_v, int32_t max_seq_len_kv) {
     if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim_v <= 0 ||

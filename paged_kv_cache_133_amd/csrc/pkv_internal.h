@@ -47,6 +47,21 @@ struct AppendParams {
 };
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
 
+// RMSNorm + RoPE + write of the MLA latent row (one wave per token).
+struct NormRopeParams {
+    const void* kv;          // [T][dn + dr]
+    const void* gamma;       // [dn]
+    const float* cos;        // [T][dr / 2]
+    const float* sin;
+    void* cache_nope;        // [nb * bs][dn]
+    void* cache_rope;        // [nb * bs][dr]
+    const int64_t* slots;
+    int64_t num_tokens, num_slots;
+    int32_t dn, dr;
+    float eps;
+};
+hipError_t launch_norm_rope_write(const NormRopeParams& p, int dtype, hipStream_t s);
+
 // ------------------------------------------------------------------ decode (MHA / GQA)
 // Split-KV plan: sequence b's tokens are cut into ceil(L'_b / split_tokens) chunks; one
 // workgroup handles (kv head, sequence, chunk).  Partial states go to the workspace and

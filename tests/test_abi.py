@@ -247,3 +247,29 @@ def test_window_forms_reject_bad_arguments():
     assert var(win=-3) == -2
     assert var(d=96) == -4
     assert var(B=0) == 0
+
+
+def test_norm_rope_write_rejects():
+    L = _lib().lib()
+
+    def call(**kw):
+        a = dict(kv=FAKE, g=FAKE, c=FAKE, s=FAKE, cn=FAKE, cr=ctypes.c_void_p(0x200000), sl=FAKE,
+                 T=4, dn=512, dr=64, bs=16, nb=8, eps=1e-6, dt=1)
+        a.update(kw)
+        return L.pkv_kv_rmsnorm_rope_cache(a["kv"], a["g"], a["c"], a["s"], a["cn"], a["cr"], a["sl"],
+                                           a["T"], a["dn"], a["dr"], a["bs"], a["nb"], a["eps"],
+                                           a["dt"], None)
+    assert call(dt=5) == -3
+    assert call(T=-1) == -2
+    assert call(dn=0) == -2
+    assert call(bs=24) == -4
+    assert call(dn=500) == -4                    # not a multiple of 8 bf16
+    assert call(dr=40) == -4                     # half not a multiple of 8 bf16
+    assert call(dn=2048) == -4
+    assert call(eps=-1.0) == -2
+    assert call(eps=float("inf")) == -2
+    assert call(sl=None) == -1
+    assert call(c=None) == -1
+    assert call(kv=ctypes.c_void_p(0x100008)) == -5
+    assert call(cr=FAKE) == -2                   # one pool for both parts
+    assert call(T=0, kv=None) == 0
