@@ -27,7 +27,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 # The mutation test points this at a deliberately broken build of the oracle.
 _LIB_OVERRIDE = os.environ.get("PKV_ORACLE_LIB_OVERRIDE")
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 ERRORS = {-1: "bad argument", -2: "block table cannot serve a position",
           -3: "slot out of range", -4: "duplicate slot", -5: "bad lengths", -6: "out of memory"}
 
@@ -89,13 +89,16 @@ def _c(a, dtype=None):
 
 
 def _storage(a: np.ndarray) -> tuple[np.ndarray, int]:
-    """Raw storage of a value array and its dtype code: float32, or bf16 as uint16 bits."""
+    """Raw storage of a value array and its dtype code: float32, bf16 as uint16 bits, or
+    float64 (values widened on the host, e.g. dequantized int8)."""
     a = np.ascontiguousarray(a)
     if a.dtype == np.float32:
         return a, F32
+    if a.dtype == np.float64:
+        return a, F64
     if a.dtype in (np.uint16, np.int16):
         return a.view(np.uint16), BF16
-    raise TypeError(f"oracle takes float32 or bf16-as-uint16 arrays, got {a.dtype}")
+    raise TypeError(f"oracle takes float32, float64 or bf16-as-uint16 arrays, got {a.dtype}")
 
 
 def max_threads() -> int:
@@ -223,6 +226,30 @@ def rmsnorm_rope(kv, gamma, cos, sin, head_dim_nope: int, eps: float):
     x1, x2 = xr[:, :h], xr[:, h:]
     rope = np.concatenate([x1 * c - x2 * s_, x2 * c + x1 * s_], axis=1)
     return nope, rope
+
+
+# --------------------------------------------------------------------------- int8 cache
+def quantize_rows(x):
+    """Symmetric int8 codes of each row (last axis) with one fp32 scale per row: the INT8
+    KV cache with per-(token, kv head) scales.  The pages name the knobs (antiquant_scale,
+    dequant_scale_key/value: "KVCache Optimization Skill", Layer 3 notes; ai6s.net article,
+    low-precision and quantized caches) but not the scheme; the reading taken:
+      s = max|x| / 127            (fp32 division)
+      q = round_half_even(x / s)  (fp32 division), clamped to [-127, 127];  s = 0 -> q = 0
+    The codes are integers decided in floating point, so this follows the fp32 operations
+    of the GPU writer exactly (IEEE division, ties to even).  Returns (q int8, s float32)."""
+    xf = widen(x).astype(np.float32)          # exact for fp32 and bf16 inputs
+    amax = np.max(np.abs(xf), axis=-1)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    q = np.rint((xf / safe[..., None]).astype(np.float32))
+    q = np.where((s > 0)[..., None], q, 0.0)
+    return np.clip(q, -127, 127).astype(np.int8), s
+
+
+def dequantize_rows(q, s):
+    """q * s in fp64 (exact: a 7-bit code times a 24-bit mantissa)."""
+    return np.asarray(q, np.float64) * np.asarray(s, np.float64)[..., None]
 
 
 # --------------------------------------------------------------------------- host formulas

@@ -46,6 +46,7 @@
 
 #define ORC_F32 0
 #define ORC_BF16 1
+#define ORC_F64 2   /* values already widened (e.g. int8 codes times their scale) */
 
 int orc_version(void) { return 1; }
 
@@ -62,6 +63,8 @@ int orc_max_threads(void) {
 static double load_elem(const void* base, int64_t idx, int dtype) {
     if (dtype == ORC_F32) {
         return (double)((const float*)base)[idx];
+    } else if (dtype == ORC_F64) {
+        return ((const double*)base)[idx];
     } else {
         /* bf16 is the top half of an fp32: put the 16 bits back on top. */
         uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
@@ -197,7 +200,7 @@ int orc_paged_attention(const void* q, const void* q_rope, int32_t dtype,
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0) return ORC_ERR_ARG;
     if (num_q_heads % num_kv_heads != 0) return ORC_ERR_ARG;
     if ((q_rope == NULL) != (k_rope == NULL)) return ORC_ERR_ARG;
-    if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_ARG;
+    if (dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_F64) return ORC_ERR_ARG;
     if (batch > 0 && cu_q[0] != 0) return ORC_ERR_LEN;
     for (int32_t b = 0; b < batch; ++b) {
         int32_t n = cu_q[b + 1] - cu_q[b];
