@@ -48,6 +48,8 @@ def dominant_kernel(w):
         return "mla_decode_kernel", [CSRC + "mla_attn.hip"] + MFMA_SOURCES
     if w.mode == "varlen":
         return "varlen_kernel<128>", [CSRC + "varlen_attn.hip"] + MFMA_SOURCES
+    if w.kv_dtype == "int8":
+        return "decode_int8_kernel", [CSRC + "int8_kv.hip", CSRC + "pkv_device.h"]
     group = w.num_q_heads // w.num_kv_heads
     if w.dtype == "bf16" and 4 <= group <= 16:
         rows_per_wave_load = 1024 // (2 * w.head_dim)
@@ -145,10 +147,17 @@ def algorithmic_bytes(case):
     if w.mode == "mla":
         row = w.head_dim + w.head_dim_rope          # nope read once (key and value) + rope
         new_rows = T * (w.head_dim + w.head_dim_rope) * e
+        kv = int(Lp.sum()) * row * e
+    elif w.kv_dtype == "int8":
+        # one-byte codes of K and V plus one fp32 scale each per (token, kv head)
+        row = w.num_kv_heads * (w.head_dim + w.head_dim_v + 8)
+        kv = int(Lp.sum()) * row
+        # the quantizing write reads the new rows in the query dtype, writes codes and scales
+        new_rows = (T * w.num_kv_heads * (w.head_dim + w.head_dim_v) * e + T * row) // 2
     else:
         row = w.num_kv_heads * (w.head_dim + w.head_dim_v)
         new_rows = T * w.num_kv_heads * (w.head_dim + w.head_dim_v) * e
-    kv = int(Lp.sum()) * row * e
+        kv = int(Lp.sum()) * row * e
     q_bytes = T * w.num_q_heads * (w.head_dim + w.head_dim_rope) * e
     out_bytes = T * w.num_q_heads * w.head_dim_v * e
     table = 4 * int((-(-Lp // w.block_size)).sum())
@@ -189,11 +198,34 @@ def cpu_baseline(case, kv_bytes, min_seconds):
          "cache_rope": host(c.cache_rope), "q": host(c.q), "q_rope": host(c.q_rope),
          "new_k": host(c.new_k), "new_v": host(c.new_v), "new_rope": host(c.new_rope),
          "block_size": c.w.block_size, "num_blocks": c.num_blocks, "scale": c.w.scale}
+    int8 = c.w.kv_dtype == "int8"
+    if int8:
+        # the oracle's own quantization of the pools (outside the timed step)
+        pk, sk = oracle.quantize_rows(h["cache_k"])
+        pv, sv = oracle.quantize_rows(h["cache_v"])
+
+    def int8_step():
+        # slot_mapping, quantize and write the new rows, attend over the dequantized pools
+        slots = oracle.slot_mapping(h["block_table"], h["lens_before"], h["cu_q"],
+                                    h["block_size"], h["num_blocks"])
+        caches = []
+        for pool, scale, new in ((pk, sk, h["new_k"]), (pv, sv, h["new_v"])):
+            qn, sn = oracle.quantize_rows(new)
+            codes = oracle.kv_write(pool, qn, slots)
+            scales = oracle.kv_write(scale, sn, slots)
+            caches.append(oracle.dequantize_rows(codes, scales))
+        return oracle.paged_attention(oracle.widen(h["q"]), caches[0], caches[1], h["block_table"],
+                                      h["cu_q"], h["lens_after"], h["scale"], False,
+                                      window=c.w.window)
+
     times = []
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        oracle.decode_step(h, causal=(c.w.mode == "varlen"), window=c.w.window)
+        if int8:
+            int8_step()
+        else:
+            oracle.decode_step(h, causal=(c.w.mode == "varlen"), window=c.w.window)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start >= min_seconds and len(times) >= 3:
             break
@@ -227,9 +259,22 @@ def main():
     dev = torch.device("cuda:0")
     case = wl.make_workload_case(w, seed=args.seed, device=dev)
     kv_bytes, split_bytes, step_bytes = algorithmic_bytes(case)
-    pool_bytes = sum(t.numel() * t.element_size()
-                     for t in {id(x): x for x in (case.cache_k, case.cache_v, case.cache_rope)
-                               if x is not None}.values())
+    int8 = w.kv_dtype == "int8"
+    if int8:
+        # The INT8 pools: every row of the bf16 pool quantized by the library's writer.
+        nbs = case.num_blocks * w.block_size
+        pool_i8 = {n: torch.empty(case.cache_k.shape, dtype=torch.int8, device=dev) for n in ("k", "v")}
+        pool_sc = {n: torch.empty(case.cache_k.shape[:3], dtype=torch.float32, device=dev)
+                   for n in ("k", "v")}
+        pkv.kv_cache_write_int8(case.cache_k.reshape(nbs, w.num_kv_heads, w.head_dim),
+                                case.cache_v.reshape(nbs, w.num_kv_heads, w.head_dim_v),
+                                pool_i8["k"], pool_i8["v"], pool_sc["k"], pool_sc["v"],
+                                torch.arange(nbs, dtype=torch.int64, device=dev))
+        pool_bytes = sum(t.numel() * t.element_size() for t in (*pool_i8.values(), *pool_sc.values()))
+    else:
+        pool_bytes = sum(t.numel() * t.element_size()
+                         for t in {id(x): x for x in (case.cache_k, case.cache_v, case.cache_rope)
+                                   if x is not None}.values())
     R = args.replicas or max(2, min(64, math.ceil(2.0e9 / pool_bytes)))
     mla = w.mode == "mla"
 
@@ -247,8 +292,17 @@ def main():
     slot_call = _lib.prepare_slot_mapping(table, lb, cu, w.block_size, T, slots)
     fused = args.path == "fused"
     reps = []
-    slot_first = args.path == "separate"
+    slot_first = args.path == "separate" or int8
     for r in range(R):
+        if int8:
+            ki8, vi8, ksc, vsc = (pool_i8["k"], pool_i8["v"], pool_sc["k"], pool_sc["v"]) if r == 0 else (
+                pool_i8["k"].clone(), pool_i8["v"].clone(), pool_sc["k"].clone(), pool_sc["v"].clone())
+            write = _lib.prepare_kv_cache_write_int8(case.new_k, case.new_v, ki8, vi8, ksc, vsc, slots)
+            split, combine, _ = _lib.prepare_decode_int8(case.q, ki8, vi8, ksc, vsc, table, la,
+                                                         case.max_len_after, w.scale, out=out,
+                                                         lse=lse, workspace=ws, window=w.window)
+            reps.append((write, split, combine))
+            continue
         k = case.cache_k if r == 0 else case.cache_k.clone()
         rope = None
         if mla:
@@ -354,6 +408,7 @@ def main():
     cfg = {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "head_dim_v": w.head_dim_v,
            "head_dim_rope": w.head_dim_rope, "block_size": w.block_size, "window": w.window,
+           "kv_dtype": w.kv_dtype or w.dtype,
            "num_blocks": case.num_blocks, "seed": args.seed,
            "kv_tokens": int(case.lens_after.sum()), "max_kv_len": case.max_len_after,
            "pool_replicas": R,

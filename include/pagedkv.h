@@ -125,6 +125,43 @@ PKV_API int pkv_kv_cache_append(const void* k_new, const void* v_new, void* k_ca
                         int32_t block_size, int64_t num_blocks, int32_t dtype, void* stream);
 
 /*
+ * INT8 KV cache.  The pages name the knobs of a quantized cache (antiquant_scale,
+ * dequant_scale_key/value: "KVCache Optimization Skill", Layer 3 notes; the ai6s.net article
+ * on low-precision caches) but not the scheme.  The one taken: symmetric int8 codes with one
+ * fp32 scale per (token, kv head) row,
+ *   s = max|x| / 127,  q = round_half_even(x / s) clamped to [-127, 127]  (IEEE fp32 divisions;
+ *   a zero row has s = 0 and zero codes),  x ~ q * s.
+ * Caches: codes k_cache, v_cache [num_blocks][block_size][num_kv_heads][head_dim] int8 and
+ * scales k_scale, v_scale [num_blocks][block_size][num_kv_heads] fp32.
+ *
+ * pkv_kv_cache_write_int8: quantize k_new, v_new [num_tokens][num_kv_heads][head_dim]
+ * (dtype f32 or bf16) row by row and store codes and scales at slot_mapping[t] (int64;
+ * slots outside the pool are skipped).  head_dim 64 or 128; all arrays 16-byte aligned;
+ * K and V arrays distinct.
+ */
+PKV_API int pkv_kv_cache_write_int8(const void* k_new, const void* v_new, void* k_cache,
+                            void* v_cache, float* k_scale, float* v_scale,
+                            const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                            int32_t dtype, void* stream);
+
+/*
+ * Decode over the INT8 caches: as pkv_paged_attn_decode_ex without the new-token write (write
+ * it first with pkv_kv_cache_write_int8), with bf16 q and out, 1..4 query heads per kv head,
+ * head_dim 64 or 128.  score = scale * s_k * (q . q_k), out = sum softmax * s_v * q_v, in fp32.
+ * window, stages and workspace as for pkv_paged_attn_decode_ex (pkv_decode_workspace_size
+ * bytes suffice).
+ */
+PKV_API int pkv_paged_attn_decode_int8(void* out, float* lse_out, const void* q, const void* k_cache,
+                               const void* v_cache, const float* k_scale, const float* v_scale,
+                               const int32_t* block_table, const int32_t* seq_lens_kv,
+                               int32_t batch, int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int64_t num_blocks, float softmax_scale,
+                               int32_t window, int32_t stages, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
  * The MLA latent row normalised, rotated and written in one launch: the fused writer the
  * pages place in front of the MLA cache (npu_kv_rmsnorm_rope_cache, keyed by slot_mapping;
  * "KVCache Optimization Skill", Mode 3 and its cache-write fusion note), which they name

@@ -22,7 +22,8 @@ STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_SHAPE", -3: "PKV_ERR_DTY
           -4: "PKV_ERR_UNSUPPORTED", -5: "PKV_ERR_ALIGN", -6: "PKV_ERR_SCALE",
           -7: "PKV_ERR_WORKSPACE", -8: "PKV_ERR_HIP"}
 EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_write",
-           "pkv_kv_cache_append", "pkv_kv_rmsnorm_rope_cache", "pkv_decode_workspace_size",
+           "pkv_kv_cache_append", "pkv_kv_cache_write_int8", "pkv_kv_rmsnorm_rope_cache",
+           "pkv_decode_workspace_size", "pkv_paged_attn_decode_int8",
            "pkv_paged_attn_decode",
            "pkv_paged_attn_decode_split", "pkv_paged_attn_decode_combine",
            "pkv_paged_attn_decode_append", "pkv_paged_attn_decode_ex", "pkv_paged_attn_varlen",
@@ -60,6 +61,11 @@ def lib() -> ctypes.CDLL:
     L.pkv_kv_cache_append.restype = ctypes.c_int
     L.pkv_kv_cache_append.argtypes = [p, p, p, p, p, p, p, p, i32, i64, i32, i32, i32, i32, i32,
                                       i32, i64, i32, p]
+    L.pkv_kv_cache_write_int8.restype = ctypes.c_int
+    L.pkv_kv_cache_write_int8.argtypes = [p, p, p, p, p, p, p, i64, i32, i32, i32, i64, i32, p]
+    L.pkv_paged_attn_decode_int8.restype = ctypes.c_int
+    L.pkv_paged_attn_decode_int8.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32,
+                                             i32, i32, i64, f32, i32, i32, p, sz, p]
     L.pkv_kv_rmsnorm_rope_cache.restype = ctypes.c_int
     L.pkv_kv_rmsnorm_rope_cache.argtypes = [p, p, p, p, p, p, p, i64, i32, i32, i32, i64, f32, i32, p]
     L.pkv_decode_workspace_size.restype = sz
@@ -188,6 +194,69 @@ def kv_rmsnorm_rope_cache(kv: torch.Tensor, gamma: torch.Tensor, cos: torch.Tens
                                            _ptr(cache_nope), _ptr(cache_rope), _ptr(slot_mapping),
                                            slot_mapping.shape[0], dn, dr, bs, nb, float(eps),
                                            _dtype_code(kv), _stream(kv.device)))
+
+
+def kv_cache_write_int8(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                        v_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                        slot_mapping: torch.Tensor):
+    """Quantize and write one step's K/V rows into the INT8 cache (see
+    pkv_kv_cache_write_int8).  Caches [nb, bs, Hkv, D] int8, scales [nb, bs, Hkv] fp32."""
+    _dev(k_new, v_new, k_cache, v_cache, k_scale, v_scale, slot_mapping)
+    nb, bs, hkv, d = k_cache.shape
+    _check(lib().pkv_kv_cache_write_int8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping),
+                                         slot_mapping.shape[0], hkv, d, bs, nb, _dtype_code(k_new),
+                                         _stream(k_new.device)))
+
+
+def _decode_int8_args(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens_kv,
+                      max_seq_len_kv, softmax_scale, stages, out, lse, workspace, window):
+    _dev(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens_kv, out, lse, workspace)
+    B, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = new_decode_workspace(B, hq, hkv, d, max_seq_len_kv, q.device)
+    args = (_ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+            _ptr(v_scale), _ptr(block_table), _ptr(seq_lens_kv), B, block_table.shape[1],
+            max_seq_len_kv, hq, hkv, d, bs, nb, float(softmax_scale), int(window), stages,
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device))
+    return args, out, workspace
+
+
+def paged_attn_decode_int8(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens_kv,
+                           max_seq_len_kv, softmax_scale, out=None, lse=None, workspace=None,
+                           window=0):
+    """Decode over the INT8 cache (see pkv_paged_attn_decode_int8).  Returns (out, lse)."""
+    args, out, _ = _decode_int8_args(q, k_cache, v_cache, k_scale, v_scale, block_table,
+                                     seq_lens_kv, max_seq_len_kv, softmax_scale, 3, out, lse,
+                                     workspace, window)
+    _check(lib().pkv_paged_attn_decode_int8(*args))
+    return out, lse
+
+
+def prepare_decode_int8(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens_kv,
+                        max_seq_len_kv, softmax_scale, out=None, lse=None, workspace=None, window=0):
+    """(split pass, combine pass) prepared calls of pkv_paged_attn_decode_int8."""
+    calls = []
+    for stages in (1, 2):
+        args, out, workspace = _decode_int8_args(q, k_cache, v_cache, k_scale, v_scale, block_table,
+                                                 seq_lens_kv, max_seq_len_kv, softmax_scale, stages,
+                                                 out, lse, workspace, window)
+        calls.append(PreparedCall(lib().pkv_paged_attn_decode_int8, args,
+                                  (q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens_kv,
+                                   out, lse, workspace)))
+    return calls[0], calls[1], out
+
+
+def prepare_kv_cache_write_int8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, slots):
+    _dev(k_new, v_new, k_cache, v_cache, k_scale, v_scale, slots)
+    nb, bs, hkv, d = k_cache.shape
+    args = (_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+            _ptr(slots), slots.shape[0], hkv, d, bs, nb, _dtype_code(k_new), _stream(k_new.device))
+    return PreparedCall(lib().pkv_kv_cache_write_int8, args,
+                        (k_new, v_new, k_cache, v_cache, k_scale, v_scale, slots))
 
 
 def new_decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_dim_v: int,

@@ -207,7 +207,7 @@ int prepare_decode(pkv::DecodeParams& p, pkv::DecodePlan& plan, void* out, float
                    int32_t head_dim_qk, int32_t head_dim_v, int32_t head_dim_rope,
                    int32_t block_size, int64_t num_blocks, float softmax_scale, int32_t dtype,
                    void* workspace, size_t workspace_bytes, bool* nothing_to_do,
-                   int32_t window = 0) {
+                   int32_t window = 0, bool allow_stream = true, bool byte_rows = false) {
     *nothing_to_do = false;
     if (window < 0) return fail(PKV_ERR_SHAPE, "decode: window must be >= 0 (0: no window)");
     if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "decode: unknown dtype %d", dtype);
@@ -250,7 +250,7 @@ int prepare_decode(pkv::DecodeParams& p, pkv::DecodePlan& plan, void* out, float
     // With a window a sequence's splits cover at most window + 31 keys (they start at the
     // window start rounded down to 32): plan for that length.
     const int32_t plan_len = window > 0 && window < max_seq_len_kv - 31 ? window + 31 : max_seq_len_kv;
-    plan = pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim_v, plan_len);
+    plan = pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim_v, plan_len, byte_rows);
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))
         return fail(PKV_ERR_WORKSPACE, "decode: workspace needs %zu bytes (16-byte aligned), got %zu",
                     plan.ws_bytes, workspace ? workspace_bytes : (size_t)0);
@@ -280,7 +280,7 @@ int prepare_decode(pkv::DecodeParams& p, pkv::DecodePlan& plan, void* out, float
     p.num_blocks = num_blocks;
     p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
     p.window = window;
-    if (pkv::gqa_stream_supported(dtype, group, head_dim_v, p.bs_log2, batch)) {
+    if (allow_stream && pkv::gqa_stream_supported(dtype, group, head_dim_v, p.bs_log2, batch)) {
         p.parts = plan.parts;
         p.ws_o = reinterpret_cast<float*>(ws + plan.st_o_offset);
         p.ws_ml = reinterpret_cast<float*>(ws + plan.st_ml_offset);
@@ -585,6 +585,78 @@ int pkv_paged_attn_decode_ex(void* out, float* lse_out, const void* q, const voi
                           num_kv_heads, head_dim, block_size, num_blocks, softmax_scale, dtype,
                           window, stages, workspace, workspace_bytes, (hipStream_t)stream,
                           "decode_ex");
+}
+
+int pkv_kv_cache_write_int8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            float* k_scale, float* v_scale, const int64_t* slot_mapping,
+                            int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int64_t num_blocks, int32_t dtype, void* stream) {
+    if (dtype != PKV_F32 && dtype != PKV_BF16)
+        return fail(PKV_ERR_DTYPE, "kv_cache_write_int8: unknown input dtype %d", dtype);
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0)
+        return fail(PKV_ERR_SHAPE, "kv_cache_write_int8: num_kv_heads and num_blocks must be positive");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PKV_ERR_UNSUPPORTED, "kv_cache_write_int8: head_dim %d not supported (64 or 128)", head_dim);
+    if (!pow2_in(block_size, 1, 256))
+        return fail(PKV_ERR_UNSUPPORTED, "kv_cache_write_int8: block_size %d is not a power of two in [1, 256]",
+                    block_size);
+    if (num_tokens * num_kv_heads > 0x7fffffffLL * 16)
+        return fail(PKV_ERR_UNSUPPORTED, "kv_cache_write_int8: too many rows");
+    if (num_tokens == 0) return PKV_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache || !k_scale || !v_scale || !slot_mapping)
+        return fail(PKV_ERR_NULL, "kv_cache_write_int8: NULL pointer argument");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(k_scale) || !aligned16(v_scale))
+        return fail(PKV_ERR_ALIGN, "kv_cache_write_int8: arrays must be 16-byte aligned");
+    if (k_cache == v_cache || k_scale == v_scale)
+        return fail(PKV_ERR_SHAPE, "kv_cache_write_int8: K and V need their own codes and scales");
+    pkv::QuantWriteParams p{};
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.k_cache = static_cast<int8_t*>(k_cache);
+    p.v_cache = static_cast<int8_t*>(v_cache);
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.slots = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.num_slots = num_blocks * block_size;
+    p.hkv = num_kv_heads;
+    return hip_status(pkv::launch_kv_write_int8(p, dtype, head_dim, (hipStream_t)stream),
+                      "kv_cache_write_int8 launch");
+}
+
+int pkv_paged_attn_decode_int8(void* out, float* lse_out, const void* q, const void* k_cache,
+                               const void* v_cache, const float* k_scale, const float* v_scale,
+                               const int32_t* block_table, const int32_t* seq_lens_kv, int32_t batch,
+                               int32_t max_blocks_per_seq, int32_t max_seq_len_kv, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, float softmax_scale, int32_t window, int32_t stages,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    if (stages < 1 || stages > 3) return fail(PKV_ERR_SHAPE, "decode_int8: stages must be 1, 2 or 3");
+    if (num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 && num_q_heads / num_kv_heads > 4)
+        return fail(PKV_ERR_UNSUPPORTED, "decode_int8: %d query heads per kv head (max 4)",
+                    num_q_heads / num_kv_heads);
+    pkv::DecodeParams p;
+    pkv::DecodePlan plan{};
+    bool idle = false;
+    // The codes are one byte per element; the host checks run on the bf16 query shape.
+    int rc = prepare_decode(p, plan, out, lse_out, q, nullptr, k_cache, v_cache, nullptr, block_table,
+                            seq_lens_kv, batch, max_blocks_per_seq, max_seq_len_kv, num_q_heads,
+                            num_kv_heads, head_dim, head_dim, 0, block_size, num_blocks, softmax_scale,
+                            PKV_BF16, workspace, workspace_bytes, &idle, window, false, true);
+    if (rc != PKV_OK || idle) return rc;
+    if (!k_scale || !v_scale) return fail(PKV_ERR_NULL, "decode_int8: NULL scale array");
+    if (!aligned16(k_scale) || !aligned16(v_scale))
+        return fail(PKV_ERR_ALIGN, "decode_int8: scale arrays must be 16-byte aligned");
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    hipStream_t s = (hipStream_t)stream;
+    if (stages & 1) {
+        rc = hip_status(pkv::launch_decode_int8(p, head_dim, s), "decode_int8 split launch");
+        if (rc != PKV_OK) return rc;
+    }
+    if ((stages & 2) && needs_combine(p, plan)) return launch_combine_for(p, head_dim, PKV_BF16, s);
+    return PKV_OK;
 }
 
 int pkv_paged_attn_varlen(void* out, float* lse_out, const void* q, const int32_t* cu_seqlens_q,

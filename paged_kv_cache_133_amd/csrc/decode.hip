@@ -357,11 +357,13 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
 
 DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t head_dim_v, int32_t max_seq_len_kv) {
+                       int32_t head_dim_v, int32_t max_seq_len_kv, bool byte_rows) {
     DecodePlan pl{};
     const int G = num_q_heads / num_kv_heads;
-    // Larger groups carry more partial state per split: use longer splits for them.
+    // Larger groups carry more partial state per split: use longer splits for them (and
+    // twice as long over one-byte INT8 rows, for the same bytes per workgroup).
     int split = G <= 2 ? 256 : G <= 4 ? 512 : 1024;
+    if (byte_rows) split *= 2;
     const int64_t pairs = (int64_t)batch * num_kv_heads;
     auto nsplits = [&](int sp) { return (int64_t)(max_seq_len_kv + sp - 1) / sp; };
     // Keep at least ~4 workgroups per compute unit in flight on long sequences.

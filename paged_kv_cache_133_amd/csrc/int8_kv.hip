@@ -1,0 +1,344 @@
+// INT8 KV cache: the quantizing write and the decode that reads it.  The pages name the
+// knobs of a quantized cache (antiquant_scale, dequant_scale_key/value: "KVCache
+// Optimization Skill", Layer 3 notes; the ai6s.net article on low-precision caches) but
+// not the scheme.  The one taken: symmetric int8 codes with one fp32 scale per (token, kv
+// head) row, s = max|x| / 127 and q = round_half_even(x / s) (IEEE fp32 divisions; a zero
+// row has s = 0 and zero codes).  The caches hold the codes [nb][bs][Hkv][D] int8 and the
+// scales [nb][bs][Hkv] fp32, one pair for K and one for V.
+//
+// Decode is bound by HBM bytes, and int8 rows are half the bf16 bytes (plus 4 bytes of
+// scale per row): the same split-KV schedule as decode_split_kernel on the vector ALU.
+//  * a token's row of one head is D bytes, 16 codes per lane and 16-byte load: D / 16
+//    lanes per row, 64 / (D / 16) tokens per wave load;
+//  * K codes go to bf16 pairs (exact for |q| <= 127) for v_dot2_f32_bf16 against the bf16
+//    query; the row's K scale multiplies the finished dot product;
+//  * V codes are widened once per token and shared by the group's heads; the row's V scale
+//    is folded into the softmax weight: o += (p s_v) q_v, l += p;
+//  * the 64 scales of a 32-token step (K and V) come in one 4-byte-per-lane load and reach
+//    the lanes of each token through LDS, each row of lanes taking consecutive tokens so
+//    that it reads its scales in one access (a scale load per token row cost a sixth of the
+//    kernel's time, shuffles per token most of that);
+//  * splits are twice as long as for bf16 rows, for the same bytes per workgroup.
+// Keys below the window start are not loaded; the new token is written beforehand by the
+// quantizing write (the attention reads the same codes later steps will).
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr float kLn2i8 = 0.69314718055994530942f;
+constexpr int kWavesI8 = 4;
+constexpr int kStepTokensI8 = 32;
+
+// Signed byte k of a dword as float.
+__device__ __forceinline__ float sbyte(uint32_t w, int k) { return (float)(int)(int8_t)(w >> (8 * k)); }
+// Two floats as a bf16 pair (exact for the codes, |q| <= 127).
+__device__ __forceinline__ uint32_t pack_bf16_pair(float a, float b) {
+    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// ------------------------------------------------------------------ quantizing write
+// One group of D / 8 lanes per (token, kv head) row: 8 values per lane.  blockIdx.y picks K
+// or V.  Rows whose slot lies outside the pool are skipped.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void kv_write_int8_kernel(QuantWriteParams p) {
+    constexpr int kLpr = D / 8;                       // lanes per row
+    constexpr int kRpw = 64 / kLpr;                   // rows per wave
+    const int which = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRpw + lane / kLpr;
+    const int c = lane % kLpr;
+    const int64_t rows = p.num_tokens * p.hkv;
+    const bool live = row < rows;
+    const int64_t t = live ? row / p.hkv : 0;
+    const int h = live ? (int)(row % p.hkv) : 0;
+    const int64_t slot = live ? p.slots[t] : -1;
+    float x[8];
+    float amax = 0.0f;
+    if (live) {
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(which ? p.v_new : p.k_new) +
+                             (row * D + c * 8) * (int64_t)sizeof(T);
+        if constexpr (sizeof(T) == 2) {
+            const u32x4 v = ld16(src);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { x[2 * i] = bf16_lo(v[i]); x[2 * i + 1] = bf16_hi(v[i]); }
+        } else {
+            const u32x4 a = ld16(src), b = ld16(src + 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { x[i] = __uint_as_float(a[i]); x[4 + i] = __uint_as_float(b[i]); }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    }
+#pragma unroll
+    for (int s = 1; s < kLpr; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 64));
+    if (!live || slot < 0 || slot >= p.num_slots) return;
+    const float sc = __fdiv_rn(amax, 127.0f);
+    uint32_t w[2] = {0u, 0u};
+    if (sc > 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float qf = fminf(fmaxf(rintf(__fdiv_rn(x[i], sc)), -127.0f), 127.0f);
+            w[i >> 2] |= ((uint32_t)(int)qf & 0xffu) << (8 * (i & 3));
+        }
+    }
+    uint8_t* dst = reinterpret_cast<uint8_t*>(which ? p.v_cache : p.k_cache) + (slot * p.hkv + h) * D + c * 8;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    if (c == 0) (which ? p.v_scale : p.k_scale)[slot * p.hkv + h] = sc;
+}
+
+// ------------------------------------------------------------------ int8 decode
+template <int D, int GP>
+__global__ __launch_bounds__(256) void decode_int8_kernel(DecodeParams p) {
+    constexpr int EPL = 16;                           // codes per lane per load
+    constexpr int LPT = D / EPL;                      // lanes per token row
+    constexpr int TPW = 64 / LPT;                     // tokens per wave load
+    constexpr int NJ = kStepTokensI8 / TPW;           // loads per step (each of K, V)
+    __shared__ float sm_m[kWavesI8][GP];
+    __shared__ float sm_l[kWavesI8][GP];
+    __shared__ float sm_o[kWavesI8][GP][D];
+    __shared__ __attribute__((aligned(16))) float sm_sc[kWavesI8][2 * kStepTokensI8];   // a step's K, V scales
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int row = lane / LPT;
+    const int col = lane % LPT;
+
+    int id = blockIdx.x;
+    const int kvh = id % p.hkv;
+    id /= p.hkv;
+    const int b = id % p.batch;
+    const int split = id / p.batch;
+    const int L = min(p.seq_lens[b], p.len_cap);
+    const int ks = window_start(L, p.window);
+    const int ksa = ks & ~(kStepTokensI8 - 1);
+    const int t0 = ksa + split * p.split_tokens;
+    if (L <= 0) {   // no visible key: output 0, lse -inf
+        if (split == 0) {
+            for (int i = threadIdx.x; i < p.group * D; i += blockDim.x) {
+                const int h = kvh * p.group + i / D;
+                reinterpret_cast<uint16_t*>(p.out)[((int64_t)b * p.hq + h) * D + i % D] = 0;
+                if (p.lse && i % D == 0) p.lse[(int64_t)b * p.hq + h] = -INFINITY;
+            }
+        }
+        return;
+    }
+    if (t0 >= L) return;
+    const int t1 = min(L, t0 + p.split_tokens);
+    const int nsplit = (L - ksa + p.split_tokens - 1) / p.split_tokens;
+    const int per_wave = p.split_tokens / kWavesI8;
+    const int w0 = t0 + wave * per_wave;
+    const int w1 = min(t1, w0 + per_wave);
+    const int bs_mask = (1 << p.bs_log2) - 1;
+    const int32_t last_block = (int32_t)(p.num_blocks - 1);
+    const int32_t* trow = p.table + (int64_t)b * p.mbs;
+
+    // Queries of the group (bf16; padded heads repeat the last real one, not stored): the
+    // lane's 16 elements as 8 bf16 pairs.
+    uint32_t qv[GP][8];
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+        const int h = kvh * p.group + min(g, p.group - 1);
+        const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + (((int64_t)b * p.hq + h) * D + col * EPL) * 2;
+        const u32x4 a = ld16(qp), c = ld16(qp + 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { qv[g][i] = a[i]; qv[g][4 + i] = c[i]; }
+    }
+    float m[GP], l[GP], o[GP][EPL];
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[g][e] = 0.0f;
+    }
+
+    const int64_t slot_stride = (int64_t)p.hkv * D;               // bytes per cache row
+    const int64_t head_off = (int64_t)kvh * D + col * EPL;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k_cache) + head_off;
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v_cache) + head_off;
+
+    // Table entries of the blocks a step touches: lane i holds entry (first block + i).
+    auto load_table = [&](int base) -> int32_t {
+        const int blk0 = base >> p.bs_log2;
+        const int nblk = ((min(base + kStepTokensI8, w1) - 1) >> p.bs_log2) - blk0 + 1;
+        return (base < w1 && lane < nblk) ? trow[blk0 + lane] : 0;
+    };
+
+    int32_t tbl = load_table(w0);
+    for (int base = w0; base < w1; base += kStepTokensI8) {
+        const int32_t tbl_next = load_table(base + kStepTokensI8);
+        const int blk0 = base >> p.bs_log2;
+        // Scales of the step's 32 tokens in one load (lane i < 32: the K scale of token
+        // base + i; lane 32 + i: its V scale), through this wave's LDS slots to the lanes of
+        // row r, which take tokens NJ r .. NJ r + NJ - 1 and read their NJ scales at once.
+        {
+            const int tk = base + (lane & 31);
+            int32_t phys = __shfl(tbl, (tk >> p.bs_log2) - blk0, 64);
+            phys = min(max(phys, 0), last_block);
+            const int64_t slot = ((int64_t)phys << p.bs_log2) | (tk & bs_mask);
+            const float* sp = lane < 32 ? p.k_scale : p.v_scale;
+            sm_sc[wave][lane] = (tk >= ks && tk < w1) ? sp[slot * p.hkv + kvh] : 0.0f;
+        }
+        u32x4 kr[NJ], vr[NJ];
+        float ksc[NJ], vsc[NJ];
+        bool valid[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int tok = base + row * NJ + j;
+            valid[j] = tok >= ks && tok < w1;
+            int32_t phys = __shfl(tbl, (tok >> p.bs_log2) - blk0, 64);
+            phys = min(max(phys, 0), last_block);
+            const int64_t slot = ((int64_t)phys << p.bs_log2) | (tok & bs_mask);
+            kr[j] = u32x4{0u, 0u, 0u, 0u};
+            vr[j] = u32x4{0u, 0u, 0u, 0u};
+            if (valid[j]) {
+                kr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + slot * slot_stride));
+                vr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + slot * slot_stride));
+            }
+        }
+        // The row's NJ consecutive K and V scales (written by this wave above; LDS accesses
+        // of one wave complete in order).
+        if constexpr (NJ == 4) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&sm_sc[wave][row * NJ]);
+            const f32x4 c = *reinterpret_cast<const f32x4*>(&sm_sc[wave][kStepTokensI8 + row * NJ]);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) { ksc[j] = a[j]; vsc[j] = c[j]; }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                ksc[j] = sm_sc[wave][row * NJ + j];
+                vsc[j] = sm_sc[wave][kStepTokensI8 + row * NJ + j];
+            }
+        }
+        // K codes as bf16 pairs; V codes widened once for all heads of the group.
+        uint32_t kb[NJ][8];
+        float vf[NJ][EPL];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kb[j][2 * i] = pack_bf16_pair(sbyte(kr[j][i], 0), sbyte(kr[j][i], 1));
+                kb[j][2 * i + 1] = pack_bf16_pair(sbyte(kr[j][i], 2), sbyte(kr[j][i], 3));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) vf[j][4 * i + k] = sbyte(vr[j][i], k);
+            }
+        }
+
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+            if (g >= p.group) break;
+            float s[NJ];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                float a = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) a = dot2_bf16(qv[g][i], kb[j][i], a);
+                const float dotp = group_sum<LPT>(a) * ksc[j];
+                s[j] = valid[j] ? dotp * p.scale_log2 : -INFINITY;
+                mx = fmaxf(mx, s[j]);
+            }
+            const float mnew = fmaxf(m[g], mx);
+            if (mnew != -INFINITY) {
+                const float alpha = fast_exp2(m[g] - mnew);
+                l[g] *= alpha;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[g][e] *= alpha;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const float pj = fast_exp2(s[j] - mnew);
+                    l[g] += pj;
+                    const float pv = pj * vsc[j];
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) o[g][e] = fmaf(pv, vf[j][e], o[g][e]);
+                }
+                m[g] = mnew;
+            }
+        }
+        tbl = tbl_next;
+    }
+
+    // Merge the rows of this wave, then the waves of the workgroup.
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+        if (g >= p.group) break;
+        const float mw = cross_row_max<LPT>(m[g]);
+        const float f = (m[g] == -INFINITY) ? 0.0f : fast_exp2(m[g] - mw);
+        const float lw = cross_row_sum<LPT>(l[g] * f);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[g][e] = cross_row_sum<LPT>(o[g][e] * f);
+        if (row == 0) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sm_o[wave][g][col * EPL + e] = o[g][e];
+            if (col == 0) {
+                sm_m[wave][g] = mw;
+                sm_l[wave][g] = lw;
+            }
+        }
+    }
+    __syncthreads();
+
+    for (int i = threadIdx.x; i < p.group * D; i += blockDim.x) {
+        const int g = i / D;
+        const int d = i % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWavesI8; ++w) M = fmaxf(M, sm_m[w][g]);
+        float acc = 0.0f, lsum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWavesI8; ++w) {
+            const float f = (sm_m[w][g] == -INFINITY) ? 0.0f : fast_exp2(sm_m[w][g] - M);
+            acc = fmaf(f, sm_o[w][g][d], acc);
+            lsum = fmaf(f, sm_l[w][g], lsum);
+        }
+        const int h = kvh * p.group + g;
+        const int64_t bh = (int64_t)b * p.hq + h;
+        if (nsplit == 1) {
+            reinterpret_cast<uint16_t*>(p.out)[bh * D + d] = f32_to_bf16(acc / lsum);
+            if (p.lse && d == 0) p.lse[bh] = (M + __log2f(lsum)) * kLn2i8;
+        } else {
+            const int64_t ps = bh * p.max_splits + split;
+            p.ws_o[ps * D + d] = acc;
+            if (d == 0) {
+                p.ws_ml[ps * 2] = M;
+                p.ws_ml[ps * 2 + 1] = lsum;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_kv_write_int8(const QuantWriteParams& p, int in_dtype, int head_dim, hipStream_t s) {
+    const int rpw = 64 / (head_dim / 8);
+    const int64_t rows = p.num_tokens * p.hkv;
+    const dim3 grid((unsigned)((rows + 4 * rpw - 1) / (4 * rpw)), 2);
+    if (in_dtype == 1) {
+        if (head_dim == 64) hipLaunchKernelGGL((kv_write_int8_kernel<bf16_t, 64>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((kv_write_int8_kernel<bf16_t, 128>), grid, dim3(256), 0, s, p);
+    } else {
+        if (head_dim == 64) hipLaunchKernelGGL((kv_write_int8_kernel<float, 64>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((kv_write_int8_kernel<float, 128>), grid, dim3(256), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_int8(const DecodeParams& p, int head_dim, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)p.hkv * p.batch * p.max_splits));
+    const int gp = p.group <= 1 ? 1 : (p.group <= 2 ? 2 : 4);
+    if (head_dim == 64) {
+        if (gp == 1) hipLaunchKernelGGL((decode_int8_kernel<64, 1>), grid, dim3(256), 0, s, p);
+        else if (gp == 2) hipLaunchKernelGGL((decode_int8_kernel<64, 2>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((decode_int8_kernel<64, 4>), grid, dim3(256), 0, s, p);
+    } else {
+        if (gp == 1) hipLaunchKernelGGL((decode_int8_kernel<128, 1>), grid, dim3(256), 0, s, p);
+        else if (gp == 2) hipLaunchKernelGGL((decode_int8_kernel<128, 2>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((decode_int8_kernel<128, 4>), grid, dim3(256), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -47,6 +47,21 @@ struct AppendParams {
 };
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
 
+// Quantizing write of the INT8 cache: per (token, kv head) row, s = max|x| / 127 and
+// q = round_half_even(x / s) into the int8 caches and the fp32 scale arrays.
+struct QuantWriteParams {
+    const void* k_new;       // [T][Hkv][D] in the input dtype
+    const void* v_new;
+    int8_t* k_cache;         // [nb * bs][Hkv][D]
+    int8_t* v_cache;
+    float* k_scale;          // [nb * bs][Hkv]
+    float* v_scale;
+    const int64_t* slots;
+    int64_t num_tokens, num_slots;
+    int32_t hkv;
+};
+hipError_t launch_kv_write_int8(const QuantWriteParams& p, int in_dtype, int head_dim, hipStream_t s);
+
 // RMSNorm + RoPE + write of the MLA latent row (one wave per token).
 struct NormRopeParams {
     const void* kv;          // [T][dn + dr]
@@ -84,7 +99,7 @@ struct DecodePlan {
     size_t st_o_offset, st_ml_offset, st_pre_offset;
 };
 DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t head_dim_v, int32_t max_seq_len_kv);
+                       int32_t head_dim_v, int32_t max_seq_len_kv, bool byte_rows = false);
 
 struct DecodeParams {
     void* out;
@@ -114,6 +129,9 @@ struct DecodeParams {
     // [B + 1] it leaves for its combine; ws_o / ws_ml then hold its partial states.
     int32_t parts;
     int32_t* tile_prefix;
+    // INT8 caches (launch_decode_int8): one fp32 scale per (slot, kv head) row, else null.
+    const float* k_scale;
+    const float* v_scale;
     // Sliding window (band): > 0 keeps the `window` most recent keys of each sequence
     // (window_start below); 0 keeps all of them.  Splits and tiles then start at the
     // window start rounded down to a multiple of 32 keys.
@@ -128,6 +146,9 @@ bool gqa_stream_supported(int dtype, int group, int head_dim, int bs_log2, int b
 int gqa_stream_parts(int num_kv_heads);
 hipError_t launch_gqa_decode(const DecodeParams& p, int head_dim, hipStream_t s);
 hipError_t launch_gqa_stream_combine(const DecodeParams& p, int head_dim, hipStream_t s);
+// Decode over the INT8 caches (p.k_scale / p.v_scale set): bf16 queries and output,
+// 1..4 query heads per kv head, split-KV with the generic combine.
+hipError_t launch_decode_int8(const DecodeParams& p, int head_dim, hipStream_t s);
 
 // Merge of split partials (second launch of a split decode).
 struct CombineParams {

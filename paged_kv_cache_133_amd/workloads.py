@@ -53,6 +53,7 @@ class Workload:
     max_blocks_per_seq: int
     description: str = ""
     window: int = 0           # sliding window (keys each query row sees; 0: all)
+    kv_dtype: str = ""        # "int8": the cache holds int8 codes + fp32 row scales
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -98,7 +99,15 @@ MTP_DECODE = Workload("mtp_decode_bf16", "varlen", 32, 32, 8, 128, 128, 0, 16, "
                       "32 q / 8 kv heads, head_dim 128, bs 16, kv lengths U{512..2048} before "
                       "the step, bf16")
 
-WORKLOADS = {w.name: w for w in (TINY, LLAMA7B, GQA_LONG, MLA, VARLEN, SWA_DECODE, MTP_DECODE)}
+# The headline shape over an INT8 cache (the same lengths as the bf16 headline).
+LLAMA7B_INT8 = Workload("llama7b_mha_int8", "decode", 32, 32, 32, 128, 128, 0, 16, "bf16",
+                        1.0 / math.sqrt(128.0), 129,
+                        "Llama-7B-shaped MHA decode layer over an INT8 KV cache (codes + fp32 "
+                        "scale per token and head): B=32, 32 heads, head_dim 128, bs 16, kv "
+                        "lengths U{512..2048}, bf16 queries", kv_dtype="int8")
+
+WORKLOADS = {w.name: w for w in (TINY, LLAMA7B, GQA_LONG, MLA, VARLEN, SWA_DECODE, MTP_DECODE,
+                                 LLAMA7B_INT8)}
 
 
 def sample_lengths(w: Workload, seed: int) -> tuple[np.ndarray, np.ndarray]:
@@ -107,7 +116,7 @@ def sample_lengths(w: Workload, seed: int) -> tuple[np.ndarray, np.ndarray]:
     B = w.batch
     if w is TINY or w.name == TINY.name:
         return np.array([37, 130], np.int64), np.ones(2, np.int64)
-    if w.name == LLAMA7B.name:
+    if w.name in (LLAMA7B.name, "llama7b_mha_int8"):
         return rng.integers(512, 2048, size=B, endpoint=True), np.ones(B, np.int64)
     if w.name == GQA_LONG.name:
         u = rng.uniform(math.log(1024.0), math.log(32768.0), size=B)

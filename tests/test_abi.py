@@ -273,3 +273,42 @@ def test_norm_rope_write_rejects():
     assert call(kv=ctypes.c_void_p(0x100008)) == -5
     assert call(cr=FAKE) == -2                   # one pool for both parts
     assert call(T=0, kv=None) == 0
+
+
+def test_int8_forms_reject_bad_arguments():
+    L = _lib().lib()
+
+    def wr(**kw):
+        a = dict(kn=FAKE, vn=FAKE, kc=FAKE, vc=ctypes.c_void_p(0x200000), ks=ctypes.c_void_p(0x300000),
+                 vs=ctypes.c_void_p(0x400000), sl=FAKE, T=4, h=2, d=128, bs=16, nb=8, dt=1)
+        a.update(kw)
+        return L.pkv_kv_cache_write_int8(a["kn"], a["vn"], a["kc"], a["vc"], a["ks"], a["vs"], a["sl"],
+                                         a["T"], a["h"], a["d"], a["bs"], a["nb"], a["dt"], None)
+    assert wr(dt=3) == -3
+    assert wr(T=-1) == -2
+    assert wr(h=0) == -2
+    assert wr(d=96) == -4
+    assert wr(bs=12) == -4
+    assert wr(sl=None) == -1
+    assert wr(ks=None) == -1
+    assert wr(kc=ctypes.c_void_p(0x100004)) == -5
+    assert wr(vc=FAKE) == -2
+    assert wr(vs=ctypes.c_void_p(0x300000)) == -2
+    assert wr(T=0, kn=None) == 0
+
+    def dec(**kw):
+        a = dict(out=FAKE, lse=None, q=FAKE, kc=FAKE, vc=ctypes.c_void_p(0x200000),
+                 ks=ctypes.c_void_p(0x300000), vs=ctypes.c_void_p(0x400000), t=FAKE, lens=FAKE,
+                 B=2, mbs=4, mx=64, hq=8, hkv=2, d=128, bs=16, nb=8, scale=0.1, win=0, st=3)
+        a.update(kw)
+        return L.pkv_paged_attn_decode_int8(a["out"], a["lse"], a["q"], a["kc"], a["vc"], a["ks"], a["vs"],
+                                            a["t"], a["lens"], a["B"], a["mbs"], a["mx"], a["hq"],
+                                            a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["win"],
+                                            a["st"], FAKE, 1 << 30, None)
+    assert dec(hq=16, hkv=2) == -4               # more than 4 query heads per kv head
+    assert dec(st=0) == -2
+    assert dec(win=-1) == -2
+    assert dec(d=96) == -4
+    assert dec(ks=None) == -1
+    assert dec(vs=ctypes.c_void_p(0x400004)) == -5
+    assert dec(B=0) == 0

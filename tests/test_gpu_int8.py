@@ -1,0 +1,133 @@
+"""GPU parity of the INT8 KV cache against the oracle, through the C ABI: the quantizing
+write bit for bit (codes and fp32 scales, all other bytes unchanged, out-of-pool slots
+skipped), and decode over the int8 caches against fp64 attention over the exactly
+dequantized rows.  Needs an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_133_amd as pkv
+from oracle import oracle
+from paged_kv_cache_133_amd import workloads as wl
+from tests.gpu_common import say
+from tests.helpers import host
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.mark.parametrize("dtype,hkv,d,bs", [("bf16", 8, 128, 16), ("f32", 1, 64, 1),
+                                            ("bf16", 4, 64, 128), ("f32", 2, 128, 32)])
+def test_int8_write_bit_exact(dtype, hkv, d, bs):
+    td = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    g = torch.Generator().manual_seed(hkv * d + bs)
+    T = 29
+    nb = max(8, (2 * T + bs - 1) // bs)
+    k_new = (torch.randn(T, hkv, d, generator=g) * torch.rand(T, hkv, 1, generator=g) * 50).to(td)
+    v_new = (torch.randn(T, hkv, d, generator=g) * 0.01).to(td)
+    k_new[3] = 0                                   # zero rows: scale 0, zero codes
+    v_new[7, 0] = 0
+    slots = torch.randperm(nb * bs, generator=g)[:T].to(torch.int64)
+    slots[11] = -1
+    slots[12] = nb * bs
+    kc = torch.randint(-128, 128, (nb, bs, hkv, d), generator=g, dtype=torch.int8)
+    vc = torch.randint(-128, 128, (nb, bs, hkv, d), generator=g, dtype=torch.int8)
+    ks = torch.randn(nb, bs, hkv, generator=g)
+    vs = torch.randn(nb, bs, hkv, generator=g)
+    say(f"int8 write {dtype} hkv={hkv} d={d} bs={bs}")
+    dk, dv, dks, dvs = kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV)
+    pkv.kv_cache_write_int8(k_new.to(DEV), v_new.to(DEV), dk, dv, dks, dvs, slots.to(DEV))
+    torch.cuda.synchronize()
+    ok = ((slots >= 0) & (slots < nb * bs)).numpy()
+    sl = slots.numpy()[ok]
+    for new, cache, scale, gc, gs in ((k_new, kc, ks, dk, dks), (v_new, vc, vs, dv, dvs)):
+        q, s = oracle.quantize_rows(host(new))                     # [T, hkv, d], [T, hkv]
+        exp_c = cache.numpy().reshape(nb * bs, hkv, d).copy()
+        exp_s = scale.numpy().reshape(nb * bs, hkv).copy()
+        exp_c[sl] = q[ok]
+        exp_s[sl] = s[ok]
+        assert np.array_equal(gc.cpu().numpy().reshape(nb * bs, hkv, d), exp_c)
+        assert np.array_equal(gs.cpu().numpy().reshape(nb * bs, hkv).view(np.uint32), exp_s.view(np.uint32))
+
+
+def _int8_case(Hq, Hkv, D, bs, L, seed):
+    """A decode case whose pool rows are int8 codes and scales (the oracle's quantization of
+    a bf16 pool), with the step's new rows written by the GPU's quantizing write."""
+    w = wl.custom(batch=len(L), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                  dtype="bf16")
+    c = wl.make_case(w, np.array(L) - 1, [1] * len(L), seed=seed, device=DEV, poison=False)
+    nb = c.num_blocks
+    kq, ksc = oracle.quantize_rows(host(c.cache_k))
+    vq, vsc = oracle.quantize_rows(host(c.cache_v))
+    dev = {"kc": torch.from_numpy(kq).to(DEV), "vc": torch.from_numpy(vq).to(DEV),
+           "ks": torch.from_numpy(ksc).to(DEV), "vs": torch.from_numpy(vsc).to(DEV)}
+    table = c.table_tensor(DEV)
+    slots = pkv.slot_mapping(table, c.lens_before_tensor(DEV), c.cu_q_tensor(DEV), bs, c.num_tokens)
+    pkv.kv_cache_write_int8(c.new_k, c.new_v, dev["kc"], dev["vc"], dev["ks"], dev["vs"], slots)
+    torch.cuda.synchronize()
+    # the oracle's view of the written caches
+    sl = slots.cpu().numpy()
+    nq, ns = oracle.quantize_rows(host(c.new_k))
+    kq = kq.reshape(nb * bs, Hkv, D)
+    kq[sl] = nq
+    ksc = ksc.reshape(nb * bs, Hkv)
+    ksc[sl] = ns
+    nq, ns = oracle.quantize_rows(host(c.new_v))
+    vq = vq.reshape(nb * bs, Hkv, D)
+    vq[sl] = nq
+    vsc = vsc.reshape(nb * bs, Hkv)
+    vsc[sl] = ns
+    assert np.array_equal(dev["kc"].cpu().numpy().reshape(nb * bs, Hkv, D), kq)
+    assert np.array_equal(dev["vs"].cpu().numpy().reshape(nb * bs, Hkv), vsc)
+    kdeq = oracle.dequantize_rows(kq, ksc).reshape(nb, bs, Hkv, D)
+    vdeq = oracle.dequantize_rows(vq, vsc).reshape(nb, bs, Hkv, D)
+    return c, dev, table, kdeq, vdeq
+
+
+def _check(c, out, lse, kdeq, vdeq, window, rows=None):
+    idx = np.arange(c.w.batch) if rows is None else np.asarray(rows)
+    q = oracle.widen(host(c.q))[idx]
+    cu = np.arange(len(idx) + 1, dtype=np.int32)
+    o, ol = oracle.paged_attention(q, kdeq, vdeq, c.block_table[idx], cu, c.lens_after[idx],
+                                   c.w.scale, False, window=window)
+    got = out.float().cpu().numpy()[idx]
+    err = np.abs(got - o).max()
+    assert err <= 2e-2, f"max-abs error {err:.3e}"
+    lerr = (np.abs(lse.cpu().numpy()[idx] - ol) / np.maximum(1.0, np.abs(ol))).max()
+    assert lerr <= 1e-4, f"lse error {lerr:.3e}"
+    return err
+
+
+@pytest.mark.parametrize("shape", [(32, 32, 128, 16), (8, 2, 64, 1), (16, 4, 128, 128),
+                                   (4, 1, 128, 32), (12, 4, 64, 64)],
+                         ids=lambda s: "hq%d_hkv%d_d%d_bs%d" % s)
+@pytest.mark.parametrize("window", [0, 100])
+def test_int8_decode(shape, window):
+    Hq, Hkv, D, bs = shape
+    L = [1, 31, 32, 33, 300, 1500, 3000]
+    say(f"int8 decode {shape} window {window}")
+    c, dev, table, kdeq, vdeq = _int8_case(Hq, Hkv, D, bs, L, seed=Hq + bs + window)
+    lse = torch.empty((len(L), Hq), dtype=torch.float32, device=DEV)
+    out, _ = pkv.paged_attn_decode_int8(c.q, dev["kc"], dev["vc"], dev["ks"], dev["vs"], table,
+                                        c.lens_after_tensor(DEV), c.max_len_after, c.w.scale,
+                                        lse=lse, window=window)
+    torch.cuda.synchronize()
+    say(f"  max-abs error {_check(c, out, lse, kdeq, vdeq, window):.3e}")
+
+
+def test_int8_headline_workload_sampled():
+    """The INT8 headline workload at full size (B = 32, 32 heads, lengths 513..2049): the
+    whole pool quantized by the oracle, the step's rows by the GPU writer, decode on the GPU;
+    eight sequences checked in full."""
+    w = wl.WORKLOADS["llama7b_mha_int8"]
+    L, _ = wl.sample_lengths(w, 0)
+    say("int8 headline workload (sampled sequences)")
+    c, dev, table, kdeq, vdeq = _int8_case(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                           list(np.asarray(L) + 1), seed=0)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=DEV)
+    out, _ = pkv.paged_attn_decode_int8(c.q, dev["kc"], dev["vc"], dev["ks"], dev["vs"], table,
+                                        c.lens_after_tensor(DEV), c.max_len_after, c.w.scale,
+                                        lse=lse)
+    torch.cuda.synchronize()
+    _check(c, out, lse, kdeq, vdeq, 0, rows=list(range(0, 32, 4)))
