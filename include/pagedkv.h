@@ -7,9 +7,13 @@
  *  - Every pointer is a DEVICE pointer (memory on the current HIP device) unless it is
  *    marked [host].  Tensors are dense, row-major and contiguous in the shapes given.
  *  - The caller owns every buffer: caches, tables, queries, outputs and workspace.
- *    The library allocates nothing, keeps no state besides a thread-local error
- *    string, never synchronises, and enqueues work only on `stream` (a hipStream_t;
- *    NULL is the default stream).  The call returns once the work is enqueued.
+ *    The write, copy and attention calls allocate nothing, keep no state besides a
+ *    thread-local error string, never synchronise, and enqueue work only on `stream`
+ *    (a hipStream_t; NULL is the default stream); each returns once its work is
+ *    enqueued, so any of them may be recorded into a captured graph (pkv_graph_*).
+ *    The exceptions, all marked below: the host block manager (pkv_bm_*), which owns
+ *    host memory between its create and destroy, and pkv_graph_end, which instantiates
+ *    an executable graph.
  *  - Arguments are checked on the host before anything is enqueued.  A non-zero
  *    return is one of the PKV_ERR_* codes; nothing was enqueued then, and
  *    pkv_last_error() describes the problem.  PKV_ERR_HIP reports a launch failure.
@@ -220,8 +224,12 @@ PKV_API size_t pkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int
  * head <= 16, f32 or bf16; MLA with num_kv_heads = 1, head_dim_qk = head_dim_v = 512,
  * head_dim_rope = 64, bf16, num_q_heads a multiple of 16.  block_size a power of two in
  * [1, 256].  Accumulation is fp32; out is rounded once to its dtype.
- * Device preconditions: 1 <= seq_lens_kv[b] <= max_seq_len_kv; block_table entries for
+ * Device preconditions: 0 <= seq_lens_kv[b] <= max_seq_len_kv; block_table entries for
  * the logical blocks in use lie in [0, num_blocks); entries past them are never read.
+ * Padding rows: seq_lens_kv[b] = 0 marks a row with no sequence (a batch kept at a fixed
+ * size, as a captured step needs): its out is 0 and its lse -inf, and no block_table
+ * entry of it is read.  The same holds for every decode entry point below; the append
+ * forms also write no cache row for it and report slot -1 in slot_mapping_out[b].
  */
 PKV_API int pkv_paged_attn_decode(void* out, float* lse_out, const void* q, const void* q_rope,
                           const void* k_cache, const void* v_cache, const void* k_rope_cache,
@@ -348,6 +356,100 @@ PKV_API int pkv_paged_attn_varlen_ex(void* out, float* lse_out, const void* q,
                              int32_t head_dim, int32_t block_size, int64_t num_blocks,
                              float softmax_scale, int32_t causal, int32_t window, int32_t dtype,
                              void* stream);
+
+/*
+ * ---------------------------------------------------------------- block management
+ * Host block manager of one cache pool ("Paged KV Cache and Packed Sequence", 2.1-2.2,
+ * 5.2 and 5.3).  [host] only: no call touches the GPU.  A manager owns num_blocks
+ * physical blocks of block_size slots, a free list, a reference count per block, and per
+ * sequence (a caller-chosen int64 id) its length and logical -> physical block list.
+ *  - Blocks are taken from the end of the free list (the block freed last is reused
+ *    first) and only when a token crosses into a new logical block.
+ *  - pkv_bm_fork gives `child` the blocks of `parent` and raises each block's count
+ *    (prefix sharing: beam search, parallel sampling).
+ *  - pkv_bm_free lowers the counts of all of a sequence's blocks, then returns the
+ *    blocks whose count reached 0 to the free list in the sequence's block order.
+ *  - Copy on write: when pkv_bm_append must write into a partly filled last block that
+ *    another sequence shares, it takes a fresh block in its place and reports the pair
+ *    (shared block, fresh block) in copy_out; the caller copies that block's rows
+ *    (pkv_kv_cache_copy_blocks, once per cache array) before writing the new rows.
+ * Calls return PKV_OK or a PKV_ERR_* code and then change nothing: PKV_ERR_SHAPE for an
+ * unknown or duplicate id, or a sequence longer than max_blocks_per_seq blocks;
+ * PKV_ERR_WORKSPACE when the free list cannot cover an append (the cache is full).
+ * A manager is not thread safe; calls on one manager must not overlap.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* New manager with every block free; NULL (and pkv_last_error) on invalid sizes. */
+PKV_API pkv_block_manager* pkv_bm_create(int64_t num_blocks, int32_t block_size,
+                                         int32_t max_blocks_per_seq);
+/* Frees the manager and all it holds (NULL is a no-op). */
+PKV_API void pkv_bm_destroy(pkv_block_manager* bm);
+/* Blocks on the free list (-1 for NULL). */
+PKV_API int64_t pkv_bm_num_free(const pkv_block_manager* bm);
+/* Registers an empty sequence. */
+PKV_API int pkv_bm_add(pkv_block_manager* bm, int64_t seq);
+/* Registers `child` sharing every block of `parent` (same length). */
+PKV_API int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
+/*
+ * Extends `seq` by num_tokens >= 0 tokens.  slots_out [host] [num_tokens] int64 or NULL:
+ * the slot of each new token (block * block_size + offset), in order, ready for
+ * pkv_kv_cache_write.  copy_out [host] [2] int64 and num_copies [host]: *num_copies is
+ * set to 0 or 1, and to 1 with copy_out = {source block, destination block} when a shared
+ * last block was copied on write; both may be NULL only when no copy is needed (else
+ * PKV_ERR_NULL and nothing changes).
+ */
+PKV_API int pkv_bm_append(pkv_block_manager* bm, int64_t seq, int32_t num_tokens,
+                          int64_t* slots_out, int64_t* copy_out, int32_t* num_copies);
+/* Releases `seq` (counts first, then blocks at count 0 back to the free list). */
+PKV_API int pkv_bm_free(pkv_block_manager* bm, int64_t seq);
+/* [host] *len = tokens of `seq`. */
+PKV_API int pkv_bm_length(const pkv_block_manager* bm, int64_t seq, int64_t* len);
+/* [host] *count = sequences holding physical block `block` (0 when free). */
+PKV_API int pkv_bm_ref_count(const pkv_block_manager* bm, int32_t block, int32_t* count);
+/*
+ * [host] Batch view for one step: row i of table [n][max_blocks_per_seq] int32 gets the
+ * blocks of seqs[i] followed by pad_block in every unused entry; seq_lens [n] int32 (or
+ * NULL) gets their lengths.  The two arrays are what the decode calls take as
+ * block_table and seq_lens_kv once copied to the device (pkv_upload).
+ */
+PKV_API int pkv_bm_table(const pkv_block_manager* bm, const int64_t* seqs, int32_t n,
+                         int32_t* table, int32_t* seq_lens, int32_t pad_block);
+
+/*
+ * Copies whole blocks inside one cache array: for i < num_pairs, block pairs[2i] of
+ * pool [num_blocks][block_bytes] is copied to block pairs[2i+1] (the copy-on-write pairs
+ * of pkv_bm_append; call once per cache array: K, V, and the scale arrays of an INT8
+ * cache).  pairs [num_pairs][2] int64 on the device; a pair naming a block outside
+ * [0, num_blocks), or the same block twice, is skipped.  block_bytes a positive multiple
+ * of 4 and pool 4-byte aligned (16 for the fast path).  Precondition: no destination
+ * block is the source or destination of another pair.
+ */
+PKV_API int pkv_kv_cache_copy_blocks(void* pool, int64_t block_bytes, int64_t num_blocks,
+                                     const int64_t* pairs, int32_t num_pairs, void* stream);
+
+/*
+ * ---------------------------------------------------------------- captured steps
+ * A decode step (uploads of the host-built tables, the cache write, the attention) can be
+ * recorded once and replayed on `stream`, so a step costs one launch instead of several
+ * ("Paged KV Cache and Packed Sequence", 5.3: the block table stays a host-built tensor
+ * whose new contents are copied in before each replay).  Host arguments (sizes, pointers,
+ * max_seq_len_kv) are fixed at capture; device data (tables, lengths, inputs) is read at
+ * each replay.  Keep the batch fixed with padding rows (seq_lens_kv = 0).
+ */
+/* Copies `bytes` from host memory to the device on `stream`.  In a captured step the copy
+ * reads src_host at each replay; src_host must then be pinned (hipHostMalloc) and must not
+ * be rewritten until that replay has run (double-buffer it). */
+PKV_API int pkv_upload(void* dst, const void* src_host, size_t bytes, void* stream);
+/* Starts recording the work enqueued on `stream` by this thread (a created stream, not
+ * NULL) into a graph; nothing runs until the graph is launched. */
+PKV_API int pkv_graph_begin(void* stream);
+/* Ends the recording and instantiates it: *graph_out is an executable graph handle. */
+PKV_API int pkv_graph_end(void* stream, void** graph_out);
+/* Replays a graph on `stream` (asynchronous, like the calls it recorded). */
+PKV_API int pkv_graph_launch(void* graph, void* stream);
+/* Destroys a graph handle (NULL is a no-op); no replay of it may still be pending. */
+PKV_API int pkv_graph_destroy(void* graph);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,10 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_paged_attn_decode",
            "pkv_paged_attn_decode_split", "pkv_paged_attn_decode_combine",
            "pkv_paged_attn_decode_append", "pkv_paged_attn_decode_ex", "pkv_paged_attn_varlen",
-           "pkv_paged_attn_varlen_ex")
+           "pkv_paged_attn_varlen_ex", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
+           "pkv_bm_add", "pkv_bm_fork", "pkv_bm_append", "pkv_bm_free", "pkv_bm_length",
+           "pkv_bm_ref_count", "pkv_bm_table", "pkv_kv_cache_copy_blocks", "pkv_upload",
+           "pkv_graph_begin", "pkv_graph_end", "pkv_graph_launch", "pkv_graph_destroy")
 
 
 class PagedKVError(RuntimeError):
@@ -88,6 +91,37 @@ def lib() -> ctypes.CDLL:
     L.pkv_paged_attn_varlen_ex.restype = ctypes.c_int
     L.pkv_paged_attn_varlen_ex.argtypes = [p, p, p, p, p, p, p, p, i32, i64, i32, i32, i32, i32,
                                            i32, i32, i64, f32, i32, i32, i32, p]
+    L.pkv_bm_create.restype = p
+    L.pkv_bm_create.argtypes = [i64, i32, i32]
+    L.pkv_bm_destroy.restype = None
+    L.pkv_bm_destroy.argtypes = [p]
+    L.pkv_bm_num_free.restype = i64
+    L.pkv_bm_num_free.argtypes = [p]
+    for name in ("pkv_bm_add", "pkv_bm_free"):
+        getattr(L, name).restype = ctypes.c_int
+        getattr(L, name).argtypes = [p, i64]
+    L.pkv_bm_fork.restype = ctypes.c_int
+    L.pkv_bm_fork.argtypes = [p, i64, i64]
+    L.pkv_bm_append.restype = ctypes.c_int
+    L.pkv_bm_append.argtypes = [p, i64, i32, p, p, p]
+    L.pkv_bm_length.restype = ctypes.c_int
+    L.pkv_bm_length.argtypes = [p, i64, p]
+    L.pkv_bm_ref_count.restype = ctypes.c_int
+    L.pkv_bm_ref_count.argtypes = [p, i32, p]
+    L.pkv_bm_table.restype = ctypes.c_int
+    L.pkv_bm_table.argtypes = [p, p, i32, p, p, i32]
+    L.pkv_kv_cache_copy_blocks.restype = ctypes.c_int
+    L.pkv_kv_cache_copy_blocks.argtypes = [p, i64, i64, p, i32, p]
+    L.pkv_upload.restype = ctypes.c_int
+    L.pkv_upload.argtypes = [p, p, sz, p]
+    L.pkv_graph_begin.restype = ctypes.c_int
+    L.pkv_graph_begin.argtypes = [p]
+    L.pkv_graph_end.restype = ctypes.c_int
+    L.pkv_graph_end.argtypes = [p, p]
+    L.pkv_graph_launch.restype = ctypes.c_int
+    L.pkv_graph_launch.argtypes = [p, p]
+    L.pkv_graph_destroy.restype = ctypes.c_int
+    L.pkv_graph_destroy.argtypes = [p]
     _lib = L
     return L
 
@@ -441,3 +475,152 @@ def prepare_varlen(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, 
                              max_seqlen_q, softmax_scale, causal, out, lse, window)
     return PreparedCall(lib().pkv_paged_attn_varlen_ex, args,
                         (q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, out, lse))
+
+
+# ---------------------------------------------------------------------- block management
+class BlockManager:
+    """Host block manager of one cache pool (pkv_bm_*): LIFO free list, per-block reference
+    counts, copy on write of a shared partly filled last block.  Sequences are int ids."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_blocks_per_seq: int):
+        self._h = lib().pkv_bm_create(num_blocks, block_size, max_blocks_per_seq)
+        if not self._h:
+            msg = lib().pkv_last_error()
+            raise PagedKVError(-2, msg.decode() if msg else "")
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.max_blocks_per_seq = max_blocks_per_seq
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().pkv_bm_destroy(self._h)
+            self._h = None
+
+    __del__ = close
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    @property
+    def num_free(self) -> int:
+        return int(lib().pkv_bm_num_free(self._h))
+
+    def add(self, seq: int):
+        _check(lib().pkv_bm_add(self._h, seq))
+
+    def fork(self, parent: int, child: int):
+        _check(lib().pkv_bm_fork(self._h, parent, child))
+
+    def append(self, seq: int, num_tokens: int = 1):
+        """Extend seq; returns (slots int64 [num_tokens], copy) with copy = (src, dst) block
+        of a copy on write, or None."""
+        import numpy as np
+        slots = np.empty(max(num_tokens, 0), dtype=np.int64)
+        copy = np.empty(2, dtype=np.int64)
+        n = ctypes.c_int32(0)
+        _check(lib().pkv_bm_append(self._h, seq, num_tokens, slots.ctypes.data_as(ctypes.c_void_p),
+                                   copy.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n)))
+        return slots, ((int(copy[0]), int(copy[1])) if n.value else None)
+
+    def free(self, seq: int):
+        _check(lib().pkv_bm_free(self._h, seq))
+
+    def length(self, seq: int) -> int:
+        v = ctypes.c_int64(0)
+        _check(lib().pkv_bm_length(self._h, seq, ctypes.byref(v)))
+        return int(v.value)
+
+    def ref_count(self, block: int) -> int:
+        v = ctypes.c_int32(0)
+        _check(lib().pkv_bm_ref_count(self._h, block, ctypes.byref(v)))
+        return int(v.value)
+
+    def table(self, seqs, pad_block: int = 0, table=None, seq_lens=None):
+        """Fixed-width int32 block table [len(seqs)][max_blocks_per_seq] and int32 lengths
+        (numpy arrays, or the caller's writable C-contiguous int32 arrays)."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        n = ids.shape[0]
+        if table is None:
+            table = np.empty((n, self.max_blocks_per_seq), dtype=np.int32)
+        if seq_lens is None:
+            seq_lens = np.empty(n, dtype=np.int32)
+        for a, shape in ((table, (n, self.max_blocks_per_seq)), (seq_lens, (n,))):
+            if a.dtype != np.int32 or tuple(a.shape) != shape or not a.flags["C_CONTIGUOUS"]:
+                raise ValueError(f"expected a C-contiguous int32 array of shape {shape}")
+        _check(lib().pkv_bm_table(self._h, ids.ctypes.data_as(ctypes.c_void_p), n,
+                                  table.ctypes.data_as(ctypes.c_void_p),
+                                  seq_lens.ctypes.data_as(ctypes.c_void_p), pad_block))
+        return table, seq_lens
+
+
+def kv_cache_copy_blocks(pool: torch.Tensor, pairs: torch.Tensor):
+    """Copy whole blocks of pool [num_blocks][...] (pkv_kv_cache_copy_blocks); pairs is an
+    int64 [n][2] device tensor of (source, destination) blocks."""
+    _dev(pool, pairs)
+    if pairs.dtype != torch.int64 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be an int64 [n][2] tensor")
+    block_bytes = pool[0].numel() * pool.element_size()
+    _check(lib().pkv_kv_cache_copy_blocks(_ptr(pool), block_bytes, pool.shape[0], _ptr(pairs),
+                                          pairs.shape[0], _stream(pool.device)))
+
+
+def upload(dst: torch.Tensor, src: torch.Tensor):
+    """Host -> device copy on the current stream (pkv_upload); src pinned for capture."""
+    _dev(dst)
+    if src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous host tensor")
+    nbytes = src.numel() * src.element_size()
+    if nbytes > dst.numel() * dst.element_size():
+        raise ValueError("dst is smaller than src")
+    _check(lib().pkv_upload(_ptr(dst), _ptr(src), nbytes, _stream(dst.device)))
+
+
+class CapturedStep:
+    """Graph of the library calls made inside `with step.capture(): ...` on a created
+    stream (pkv_graph_*); replay() launches it on that stream."""
+
+    def __init__(self, device=None):
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+        self.stream = torch.cuda.Stream(self.device)
+        self._g = None
+
+    def capture(self):
+        import contextlib
+
+        @contextlib.contextmanager
+        def cm():
+            if self._g is not None:
+                raise RuntimeError("already captured")
+            s = ctypes.c_void_p(self.stream.cuda_stream)
+            self.stream.wait_stream(torch.cuda.current_stream(self.device))
+            with torch.cuda.stream(self.stream):
+                _check(lib().pkv_graph_begin(s))
+                try:
+                    yield self
+                except BaseException:
+                    g = ctypes.c_void_p()
+                    lib().pkv_graph_end(s, ctypes.byref(g))
+                    lib().pkv_graph_destroy(g)
+                    raise
+                g = ctypes.c_void_p()
+                _check(lib().pkv_graph_end(s, ctypes.byref(g)))
+                self._g = g
+        return cm()
+
+    def replay(self):
+        """Launch on the step's stream after the current stream's prior work; the current
+        stream then waits for it."""
+        cur = torch.cuda.current_stream(self.device)
+        self.stream.wait_stream(cur)
+        _check(lib().pkv_graph_launch(self._g, ctypes.c_void_p(self.stream.cuda_stream)))
+        cur.wait_stream(self.stream)
+
+    def close(self):
+        if getattr(self, "_g", None) is not None:
+            lib().pkv_graph_destroy(self._g)
+            self._g = None
+
+    __del__ = close

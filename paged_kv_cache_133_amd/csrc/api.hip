@@ -10,13 +10,22 @@
 #include "pkv_internal.h"
 
 namespace {
-
 thread_local char g_err[512] = "";
+}  // namespace
+
+namespace pkv {
+int set_error_v(int code, const char* fmt, va_list ap) {
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    return code;
+}
+}  // namespace pkv
+
+namespace {
 
 int fail(int code, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    pkv::set_error_v(code, fmt, ap);
     va_end(ap);
     return code;
 }
@@ -94,6 +103,60 @@ int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_cache, void
             return fail(PKV_ERR_ALIGN, "kv_cache_write: pointers must be aligned to the element size");
     }
     return hip_status(pkv::launch_kv_write(p, (hipStream_t)stream), "kv_cache_write launch");
+}
+
+int pkv_kv_cache_copy_blocks(void* pool, int64_t block_bytes, int64_t num_blocks,
+                             const int64_t* pairs, int32_t num_pairs, void* stream) {
+    if (num_pairs < 0 || block_bytes <= 0 || num_blocks <= 0)
+        return fail(PKV_ERR_SHAPE, "kv_cache_copy_blocks: sizes must be positive (num_pairs >= 0)");
+    if (block_bytes % 4) return fail(PKV_ERR_ALIGN, "kv_cache_copy_blocks: block_bytes must be a multiple of 4");
+    if (num_blocks > INT64_MAX / block_bytes) return fail(PKV_ERR_SHAPE, "kv_cache_copy_blocks: pool size overflows");
+    if (num_pairs == 0) return PKV_OK;
+    if (!pool || !pairs) return fail(PKV_ERR_NULL, "kv_cache_copy_blocks: NULL pointer argument");
+    if (reinterpret_cast<uintptr_t>(pool) % 4) return fail(PKV_ERR_ALIGN, "kv_cache_copy_blocks: pool must be 4-byte aligned");
+    pkv::CopyBlocksParams p{};
+    p.pool = static_cast<uint8_t*>(pool);
+    p.pairs = pairs;
+    p.block_bytes = block_bytes;
+    p.num_blocks = num_blocks;
+    p.num_pairs = num_pairs;
+    return hip_status(pkv::launch_copy_blocks(p, (hipStream_t)stream), "kv_cache_copy_blocks launch");
+}
+
+int pkv_upload(void* dst, const void* src_host, size_t bytes, void* stream) {
+    if (bytes == 0) return PKV_OK;
+    if (!dst || !src_host) return fail(PKV_ERR_NULL, "upload: NULL pointer argument");
+    return hip_status(hipMemcpyAsync(dst, src_host, bytes, hipMemcpyHostToDevice, (hipStream_t)stream),
+                      "upload");
+}
+
+int pkv_graph_begin(void* stream) {
+    if (!stream) return fail(PKV_ERR_NULL, "graph_begin: capture needs a created stream, not the NULL stream");
+    return hip_status(hipStreamBeginCapture((hipStream_t)stream, hipStreamCaptureModeThreadLocal),
+                      "graph_begin");
+}
+
+int pkv_graph_end(void* stream, void** graph_out) {
+    if (!stream || !graph_out) return fail(PKV_ERR_NULL, "graph_end: NULL stream or graph_out");
+    *graph_out = nullptr;
+    hipGraph_t g = nullptr;
+    int rc = hip_status(hipStreamEndCapture((hipStream_t)stream, &g), "graph_end: end capture");
+    if (rc != PKV_OK) return rc;
+    hipGraphExec_t exec = nullptr;
+    rc = hip_status(hipGraphInstantiate(&exec, g, nullptr, nullptr, 0), "graph_end: instantiate");
+    (void)hipGraphDestroy(g);
+    if (rc == PKV_OK) *graph_out = exec;
+    return rc;
+}
+
+int pkv_graph_launch(void* graph, void* stream) {
+    if (!graph) return fail(PKV_ERR_NULL, "graph_launch: NULL graph");
+    return hip_status(hipGraphLaunch((hipGraphExec_t)graph, (hipStream_t)stream), "graph_launch");
+}
+
+int pkv_graph_destroy(void* graph) {
+    if (!graph) return PKV_OK;
+    return hip_status(hipGraphExecDestroy((hipGraphExec_t)graph), "graph_destroy");
 }
 
 int pkv_kv_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

@@ -115,8 +115,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int ks = window_start(L, p.window);
     const int ksa = ks & ~(kStepTokens - 1);
     const int t0 = ksa + split * p.split_tokens;
-    if (L <= 0) {   // no visible key: output 0, lse -inf
+    if (L <= 0) {   // no visible key (a padding row): output 0, lse -inf, nothing written
         if (split == 0) {
+            if (APPEND && p.slots_out && kvh == 0 && threadIdx.x == 0) p.slots_out[b] = -1;
             for (int i = threadIdx.x; i < p.group * D; i += blockDim.x) {
                 const int h = kvh * p.group + i / D;
                 store_out<T>(p.out, ((int64_t)b * p.hq + h) * D + i % D, 0.0f);

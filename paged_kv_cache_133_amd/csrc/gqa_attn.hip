@@ -287,6 +287,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
             const int e = s_pre[b + 1];
             empty = s_len[b] <= 0;
             mine = e > s_pre[b] && e - 1 >= x0 && e - 1 < x1;
+            if (APPEND && empty && p.slots_out && w == 0 && kvh == 0) p.slots_out[b] = -1;
         }
         uint64_t em = w == 0 ? __ballot(empty) : 0ull;
         while (em) {
@@ -590,8 +591,9 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
     const int L = min(p.seq_lens[b], p.len_cap);
     const bool valid = n < G;
     const int64_t row = (int64_t)b * p.hq + kvh * G + min(n, G - 1);
-    if (L <= 0) {
+    if (L <= 0) {   // a padding row: output 0, lse -inf, nothing written
         if (valid) store_empty<D>(p, row, g);
+        if (APPEND && p.slots_out && kvh == 0 && split == 0 && threadIdx.x == 0) p.slots_out[b] = -1;
         return;
     }
     const int ks = window_start(L, p.window);                         // first visible key

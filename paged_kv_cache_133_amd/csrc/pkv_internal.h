@@ -3,10 +3,14 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdarg.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace pkv {
+
+// Sets the calling thread's pkv_last_error() text; returns code.
+int set_error_v(int code, const char* fmt, va_list ap);
 
 // ------------------------------------------------------------------ slot_mapping + write
 struct SlotParams {
@@ -46,6 +50,18 @@ struct AppendParams {
     int32_t batch, max_new, mbs, bs_log2;
 };
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
+
+// Block copies inside one pool (copy on write of a shared block): pair i copies block
+// pairs[2i] to block pairs[2i+1]; pairs naming a block outside the pool, or the same block
+// twice, are skipped.
+struct CopyBlocksParams {
+    uint8_t* pool;
+    const int64_t* pairs;
+    int64_t block_bytes;
+    int64_t num_blocks;
+    int32_t num_pairs;
+};
+hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t s);
 
 // Quantizing write of the INT8 cache: per (token, kv head) row, s = max|x| / 127 and
 // q = round_half_even(x / s) into the int8 caches and the fp32 scale arrays.

@@ -147,4 +147,36 @@ hipError_t launch_kv_append(const AppendParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+namespace {
+
+// blockIdx.x = pair, blockIdx.y strides over the block's bytes.
+template <int VEC>
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksParams p) {
+    const int64_t src = p.pairs[2 * (int64_t)blockIdx.x];
+    const int64_t dst = p.pairs[2 * (int64_t)blockIdx.x + 1];
+    if (src < 0 || src >= p.num_blocks || dst < 0 || dst >= p.num_blocks || src == dst) return;
+    const uint8_t* s = p.pool + src * p.block_bytes;
+    uint8_t* d = p.pool + dst * p.block_bytes;
+    const int64_t step = (int64_t)gridDim.y * blockDim.x * VEC;
+    for (int64_t off = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * VEC; off < p.block_bytes; off += step) {
+        if constexpr (VEC == 16) {
+            st16(d + off, ld16(s + off));
+        } else {
+            *reinterpret_cast<uint32_t*>(d + off) = *reinterpret_cast<const uint32_t*>(s + off);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t s) {
+    const bool v16 = p.block_bytes % 16 == 0 && reinterpret_cast<uintptr_t>(p.pool) % 16 == 0;
+    const int64_t per_wg = 256LL * (v16 ? 16 : 4);
+    const int64_t chunks = (p.block_bytes + per_wg - 1) / per_wg;
+    const dim3 grid((unsigned)p.num_pairs, (unsigned)(chunks < 16 ? chunks : 16));
+    if (v16) hipLaunchKernelGGL(copy_blocks_kernel<16>, grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(copy_blocks_kernel<4>, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 }  // namespace pkv
