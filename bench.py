@@ -76,6 +76,11 @@ def parse():
                     help="fused: decode_append (write folded into the split pass), combine; "
                          "append: kv_cache_append (slot_mapping + write), split, combine; "
                          "separate: slot_mapping, write, split, combine")
+    ap.add_argument("--serving", action="store_true",
+                    help="serving loop instead: host block manager, recorded decode step "
+                         "replayed with double-buffered table uploads, per block size")
+    ap.add_argument("--block-sizes", default="16,32,64,128",
+                    help="block sizes of the --serving sweep")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for counter scaling)")
     return ap.parse_args()
@@ -237,6 +242,115 @@ def cpu_baseline(case, kv_bytes, min_seconds):
                        f"{med * 1e3:.1f} ms/step")}
 
 
+def serving(args):
+    """--serving: the decode layer of a workload as a serving loop runs it, once per block
+    size ("Paged KV Cache and Packed Sequence", 5.3-5.4).  The sequences start at the
+    workload's lengths, their blocks taken from the host block manager one block per
+    sequence in turn (so that neighbouring blocks belong to different sequences, as under
+    continuous batching).  Each step: pkv_bm_decode_step writes the next table into a pinned
+    buffer (host time), the buffer is uploaded on a copy stream (upload time), and the
+    recorded write-and-attend step is replayed (graph time); the same step run eagerly is
+    timed beside it.  Prints one JSON line with a row per block size."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_133_amd as pkv
+    from paged_kv_cache_133_amd import workloads as wl
+    from paged_kv_cache_133_amd.step import GraphDecodeStep
+
+    w = wl.WORKLOADS[args.workload]
+    if w.mode != "decode" or w.kv_dtype:
+        print("bench.py --serving runs MHA/GQA decode workloads", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    L0, _ = wl.sample_lengths(w, args.seed)
+    B, hq, hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    row_bytes = hkv * d * w.elem_bytes
+    gen = torch.Generator(device=dev).manual_seed(args.seed)
+    total = args.warmup + args.steps
+    rows = []
+    for bs in [int(x) for x in args.block_sizes.split(",")]:
+        final = L0 + total + 1
+        mbs = int(math.ceil(final.max() / bs))
+        nb = int(sum(math.ceil(x / bs) for x in final)) + 8
+        k = torch.randn(nb, bs, hkv, d, generator=gen, device=dev).to(w.torch_dtype)
+        v = torch.randn(nb, bs, hkv, d, generator=gen, device=dev).to(w.torch_dtype)
+        bm = pkv.BlockManager(nb, bs, mbs)
+        left = [int(x) for x in L0]
+        for b in range(B):
+            bm.add(b)
+        while any(left):
+            for b in range(B):
+                n = min(left[b], bs)
+                if n:
+                    bm.append(b, n)
+                    left[b] -= n
+        step = GraphDecodeStep(k, v, B, mbs, hq, w.scale, window=w.window)
+        step.q.copy_(torch.randn(B, hq, d, generator=gen, device=dev).to(w.torch_dtype))
+        step.k_new.copy_(torch.randn(B, hkv, d, generator=gen, device=dev).to(w.torch_dtype))
+        step.v_new.copy_(step.k_new)
+        ids = np.arange(B, dtype=np.int64)
+        for _ in range(args.warmup):
+            tab, lens = step.host_tables()
+            bm.decode_step(ids, table=tab, seq_lens=lens)
+            step.launch()
+        torch.cuda.synchronize()
+        kv_tokens = int(L0.sum()) + B * (args.warmup + 1) + B * (args.steps - 1) // 2
+        ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+        timing = [{"upload": (ev(), ev()), "graph": (ev(), ev())} for _ in range(args.steps)]
+        t0, t1 = ev(), ev()
+        host_s = 0.0
+        t0.record()
+        wall0 = time.perf_counter()
+        for i in range(args.steps):
+            h0 = time.perf_counter()
+            tab, lens = step.host_tables()
+            _, _, _, cp = bm.decode_step(ids, table=tab, seq_lens=lens)
+            host_s += time.perf_counter() - h0
+            step.launch(timing[i])
+        t1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        up = statistics.mean(a.elapsed_time(b) for a, b in (x["upload"] for x in timing)) * 1e3
+        gr = statistics.mean(a.elapsed_time(b) for a, b in (x["graph"] for x in timing)) * 1e3
+        # The same step eagerly (two launches) on the tables of the last step.
+        table_d, lens_d = (x.clone() for x in step.device_views((step.t - 1) % 2))
+        ws = pkv.new_decode_workspace(B, hq, hkv, d, mbs * bs, dev)
+        out = torch.empty_like(step.out)
+        e0, e1 = ev(), ev()
+        for it in range(2):
+            if it:
+                e0.record()
+            for _ in range(args.steps):
+                pkv.paged_attn_decode_append(step.q, step.k_new, step.v_new, k, v, table_d, lens_d,
+                                             mbs * bs, w.scale, out=out, workspace=ws)
+            if it:
+                e1.record()
+        torch.cuda.synchronize()
+        eager = e0.elapsed_time(e1) / args.steps * 1e3
+        held = sum(math.ceil(bm.length(b) / bs) for b in range(B))
+        rows.append({"block_size": bs, "max_blocks_per_seq": mbs,
+                     "table_bytes": B * (mbs + 1) * 4,
+                     "host_table_us": round(host_s / args.steps * 1e6, 2),
+                     "upload_us": round(up, 2), "graph_replay_us": round(gr, 2),
+                     "eager_step_us": round(eager, 2),
+                     "gpu_us_per_step": round(t0.elapsed_time(t1) / args.steps * 1e3, 2),
+                     "wall_us_per_step": round(wall / args.steps * 1e6, 2),
+                     "kv_read_gbps_graph": round(kv_tokens * 2 * row_bytes / (gr * 1e-6) / 1e9, 1),
+                     "slack_tokens": held * bs - sum(bm.length(b) for b in range(B))})
+        print(json.dumps({"block_size": bs, **rows[-1]}), file=sys.stderr, flush=True)
+        step.close()
+        bm.close()
+        del k, v, step
+        torch.cuda.empty_cache()
+    line = {"metric": "serving decode step per block size (host table, upload, graph replay)",
+            "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "dtype": w.dtype, "data": "synthetic",
+            "config": {"workload": w.name, "batch": B, "num_q_heads": hq, "num_kv_heads": hkv,
+                       "head_dim": d, "window": w.window, "seed": args.seed},
+            "results": rows}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -245,6 +359,13 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.serving:
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        serving(args)
         return
     import torch
     if not torch.cuda.is_available():

@@ -387,9 +387,9 @@ PKV_API pkv_block_manager* pkv_bm_create(int64_t num_blocks, int32_t block_size,
 PKV_API void pkv_bm_destroy(pkv_block_manager* bm);
 /* Blocks on the free list (-1 for NULL). */
 PKV_API int64_t pkv_bm_num_free(const pkv_block_manager* bm);
-/* Registers an empty sequence. */
+/* Registers an empty sequence (ids are >= 0; negative ids mark padding rows below). */
 PKV_API int pkv_bm_add(pkv_block_manager* bm, int64_t seq);
-/* Registers `child` sharing every block of `parent` (same length). */
+/* Registers `child` (a new id >= 0) sharing every block of `parent` (same length). */
 PKV_API int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
 /*
  * Extends `seq` by num_tokens >= 0 tokens.  slots_out [host] [num_tokens] int64 or NULL:
@@ -401,6 +401,21 @@ PKV_API int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
  */
 PKV_API int pkv_bm_append(pkv_block_manager* bm, int64_t seq, int32_t num_tokens,
                           int64_t* slots_out, int64_t* copy_out, int32_t* num_copies);
+/*
+ * The host side of one decode step for a fixed-size batch: row i appends one token to
+ * sequence seqs[i] (as pkv_bm_append, rows in order), or is a padding row when seqs[i] < 0.
+ * Then row i of table [n][max_blocks_per_seq] int32 and seq_lens [n] int32 (or NULL) get
+ * the sequence's blocks and new length (padding rows: pad_block everywhere, length 0),
+ * ready for pkv_upload and pkv_paged_attn_decode_ex with k_new/v_new.  slots_out [n] int64
+ * or NULL gets each row's new slot (-1 for padding rows).  copies_out [n][2] int64 gets the
+ * copy-on-write pairs of the step, *num_copies of them, to run (pkv_kv_cache_copy_blocks)
+ * before the decode writes.  All [host].  Everything is checked first: on an error (an id
+ * unknown or listed twice, a sequence over max_blocks_per_seq, too few free blocks)
+ * nothing changes.
+ */
+PKV_API int pkv_bm_decode_step(pkv_block_manager* bm, const int64_t* seqs, int32_t n,
+                               int64_t* slots_out, int64_t* copies_out, int32_t* num_copies,
+                               int32_t* table, int32_t* seq_lens, int32_t pad_block);
 /* Releases `seq` (counts first, then blocks at count 0 back to the free list). */
 PKV_API int pkv_bm_free(pkv_block_manager* bm, int64_t seq);
 /* [host] *len = tokens of `seq`. */

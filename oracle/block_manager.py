@@ -50,13 +50,13 @@ class BlockManagerModel:
         return len(self.free_blocks)
 
     def add(self, seq: int):
-        if seq in self.block_table:
-            raise ManagerError("shape", f"sequence {seq} exists")
+        if seq in self.block_table or (isinstance(seq, int) and seq < 0):
+            raise ManagerError("shape", f"sequence {seq} exists or is negative")
         self.block_table[seq] = []
         self.seq_len[seq] = 0
 
     def fork(self, parent: int, child: int):
-        if parent not in self.block_table or child in self.block_table:
+        if parent not in self.block_table or child in self.block_table or child < 0:
             raise ManagerError("shape", "bad fork")
         self.block_table[child] = list(self.block_table[parent])
         self.seq_len[child] = self.seq_len[parent]
@@ -97,6 +97,39 @@ class BlockManagerModel:
             slots.append(blocks[p // bs] * bs + p % bs)
         self.seq_len[seq] = n + num_tokens
         return slots, copy
+
+    def decode_step(self, seqs, pad_block: int = 0):
+        """One token for each row's sequence in row order; a negative id is a padding row
+        (no sequence: pad_block row, length 0, slot -1).  Returns (rows, lengths, slots,
+        copies).  Nothing changes when any row would fail."""
+        live = [s for s in seqs if s >= 0]
+        if len(set(live)) != len(live) or any(s not in self.block_table for s in live):
+            raise ManagerError("shape", "unknown or repeated sequence")
+        for s in live:          # a row that would need a block past max_blocks_per_seq
+            if self.seq_len[s] % self.block_size == 0 and \
+                    len(self.block_table[s]) + 1 > self.max_blocks_per_seq:
+                raise ManagerError("shape", "sequence longer than max_blocks_per_seq blocks")
+        saved = (list(self.free_blocks), list(self.ref_count),
+                 {k: list(v) for k, v in self.block_table.items()}, dict(self.seq_len))
+        rows, lens, slots, copies = [], [], [], []
+        try:
+            for s in seqs:
+                if s < 0:
+                    rows.append([pad_block] * self.max_blocks_per_seq)
+                    lens.append(0)
+                    slots.append(-1)
+                    continue
+                (slot,), copy = self.append(s, 1)
+                if copy is not None:
+                    copies.append(copy)
+                slots.append(slot)
+                r, l = self.table([s], pad_block)
+                rows.append(r[0])
+                lens.append(l[0])
+        except ManagerError:
+            self.free_blocks, self.ref_count, self.block_table, self.seq_len = saved
+            raise
+        return rows, lens, slots, copies
 
     def free(self, seq: int):
         if seq not in self.block_table:

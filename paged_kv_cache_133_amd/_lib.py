@@ -28,7 +28,8 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_paged_attn_decode_split", "pkv_paged_attn_decode_combine",
            "pkv_paged_attn_decode_append", "pkv_paged_attn_decode_ex", "pkv_paged_attn_varlen",
            "pkv_paged_attn_varlen_ex", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
-           "pkv_bm_add", "pkv_bm_fork", "pkv_bm_append", "pkv_bm_free", "pkv_bm_length",
+           "pkv_bm_add", "pkv_bm_fork", "pkv_bm_append", "pkv_bm_decode_step", "pkv_bm_free",
+           "pkv_bm_length",
            "pkv_bm_ref_count", "pkv_bm_table", "pkv_kv_cache_copy_blocks", "pkv_upload",
            "pkv_graph_begin", "pkv_graph_end", "pkv_graph_launch", "pkv_graph_destroy")
 
@@ -104,6 +105,8 @@ def lib() -> ctypes.CDLL:
     L.pkv_bm_fork.argtypes = [p, i64, i64]
     L.pkv_bm_append.restype = ctypes.c_int
     L.pkv_bm_append.argtypes = [p, i64, i32, p, p, p]
+    L.pkv_bm_decode_step.restype = ctypes.c_int
+    L.pkv_bm_decode_step.argtypes = [p, p, i32, p, p, p, p, p, i32]
     L.pkv_bm_length.restype = ctypes.c_int
     L.pkv_bm_length.argtypes = [p, i64, p]
     L.pkv_bm_ref_count.restype = ctypes.c_int
@@ -523,6 +526,34 @@ class BlockManager:
         _check(lib().pkv_bm_append(self._h, seq, num_tokens, slots.ctypes.data_as(ctypes.c_void_p),
                                    copy.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n)))
         return slots, ((int(copy[0]), int(copy[1])) if n.value else None)
+
+    def decode_step(self, seqs, table=None, seq_lens=None, slots=None, pad_block: int = 0):
+        """One token for each row's sequence (negative id: padding row) and the step's table,
+        lengths and slots (pkv_bm_decode_step).  Arrays may be the caller's (C-contiguous
+        int32 table [n][max_blocks_per_seq] and seq_lens [n], int64 slots [n]).  Returns
+        (table, seq_lens, slots, copies) with copies an int64 [k][2] array of
+        copy-on-write (source, destination) blocks."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        n = ids.shape[0]
+        if table is None:
+            table = np.empty((n, self.max_blocks_per_seq), dtype=np.int32)
+        if seq_lens is None:
+            seq_lens = np.empty(n, dtype=np.int32)
+        if slots is None:
+            slots = np.empty(n, dtype=np.int64)
+        for a, shape, dt in ((table, (n, self.max_blocks_per_seq), np.int32),
+                             (seq_lens, (n,), np.int32), (slots, (n,), np.int64)):
+            if a.dtype != dt or tuple(a.shape) != shape or not a.flags["C_CONTIGUOUS"]:
+                raise ValueError(f"expected a C-contiguous {dt.__name__} array of shape {shape}")
+        copies = np.empty((max(n, 1), 2), dtype=np.int64)
+        k = ctypes.c_int32(0)
+        vp = ctypes.c_void_p
+        _check(lib().pkv_bm_decode_step(self._h, ids.ctypes.data_as(vp), n,
+                                        slots.ctypes.data_as(vp), copies.ctypes.data_as(vp),
+                                        ctypes.byref(k), table.ctypes.data_as(vp),
+                                        seq_lens.ctypes.data_as(vp), pad_block))
+        return table, seq_lens, slots, copies[:k.value]
 
     def free(self, seq: int):
         _check(lib().pkv_bm_free(self._h, seq))

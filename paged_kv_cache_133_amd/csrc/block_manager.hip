@@ -71,6 +71,7 @@ int64_t pkv_bm_num_free(const pkv_block_manager* bm) { return bm ? (int64_t)bm->
 
 int pkv_bm_add(pkv_block_manager* bm, int64_t seq) {
     if (!bm) return bm_fail(PKV_ERR_NULL, "bm_add: NULL manager");
+    if (seq < 0) return bm_fail(PKV_ERR_SHAPE, "bm_add: sequence ids are >= 0 (negative ids mark padding rows)");
     if (bm->seqs.count(seq)) return bm_fail(PKV_ERR_SHAPE, "bm_add: sequence %lld exists", (long long)seq);
     bm->seqs.emplace(seq, pkv_block_manager::Seq());
     return PKV_OK;
@@ -80,7 +81,8 @@ int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child) {
     if (!bm) return bm_fail(PKV_ERR_NULL, "bm_fork: NULL manager");
     auto it = bm->seqs.find(parent);
     if (it == bm->seqs.end()) return bm_fail(PKV_ERR_SHAPE, "bm_fork: no sequence %lld", (long long)parent);
-    if (bm->seqs.count(child)) return bm_fail(PKV_ERR_SHAPE, "bm_fork: sequence %lld exists", (long long)child);
+    if (child < 0 || bm->seqs.count(child))
+        return bm_fail(PKV_ERR_SHAPE, "bm_fork: child id %lld is negative or exists", (long long)child);
     pkv_block_manager::Seq c = it->second;
     for (int32_t blk : c.blocks) ++bm->ref[(size_t)blk];
     bm->seqs.emplace(child, std::move(c));
@@ -132,6 +134,76 @@ int pkv_bm_append(pkv_block_manager* bm, int64_t seq, int32_t num_tokens, int64_
         if (slots_out) slots_out[i] = (int64_t)s.blocks[(size_t)(pos / bs)] * bs + pos % bs;
     }
     s.len = len1;
+    return PKV_OK;
+}
+
+int pkv_bm_decode_step(pkv_block_manager* bm, const int64_t* seqs, int32_t n, int64_t* slots_out,
+                       int64_t* copies_out, int32_t* num_copies, int32_t* table, int32_t* seq_lens,
+                       int32_t pad_block) {
+    if (num_copies) *num_copies = 0;
+    if (!bm) return bm_fail(PKV_ERR_NULL, "bm_decode_step: NULL manager");
+    if (n < 0) return bm_fail(PKV_ERR_SHAPE, "bm_decode_step: negative row count");
+    if (n == 0) return PKV_OK;
+    if (!seqs || !copies_out || !num_copies || !table)
+        return bm_fail(PKV_ERR_NULL, "bm_decode_step: NULL array");
+    // Check everything first so that a failure changes nothing: every id known and listed
+    // once, every sequence within max_blocks_per_seq, and enough free blocks for the new
+    // blocks and the copies on write (a shared block is copied only while another row of
+    // the step, or a sequence outside it, still holds it).
+    const int64_t bs = bm->block_size;
+    std::unordered_map<int64_t, int32_t> seen;
+    std::unordered_map<int32_t, int32_t> dropped;
+    int64_t fresh = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (seqs[i] < 0) continue;
+        auto it = bm->seqs.find(seqs[i]);
+        if (it == bm->seqs.end())
+            return bm_fail(PKV_ERR_SHAPE, "bm_decode_step: no sequence %lld", (long long)seqs[i]);
+        if (seen[seqs[i]]++)
+            return bm_fail(PKV_ERR_SHAPE, "bm_decode_step: sequence %lld listed twice", (long long)seqs[i]);
+        const auto& s = it->second;
+        if (s.len % bs == 0) {
+            if ((int64_t)s.blocks.size() + 1 > bm->max_blocks_per_seq)
+                return bm_fail(PKV_ERR_SHAPE, "bm_decode_step: sequence %lld would exceed max_blocks_per_seq",
+                               (long long)seqs[i]);
+            ++fresh;
+        } else {
+            const int32_t last = s.blocks.back();
+            if (bm->ref[(size_t)last] - dropped[last] > 1) {
+                ++fresh;
+                ++dropped[last];
+            }
+        }
+    }
+    if (fresh > (int64_t)bm->free_list.size())
+        return bm_fail(PKV_ERR_WORKSPACE, "bm_decode_step: kv cache full (%lld blocks needed, %lld free)",
+                       (long long)fresh, (long long)bm->free_list.size());
+    int32_t copies = 0;
+    const int32_t w = bm->max_blocks_per_seq;
+    for (int32_t i = 0; i < n; ++i) {
+        int32_t* row = table + (int64_t)i * w;
+        if (seqs[i] < 0) {                          // padding row
+            if (slots_out) slots_out[i] = -1;
+            std::fill(row, row + w, pad_block);
+            if (seq_lens) seq_lens[i] = 0;
+            continue;
+        }
+        int64_t slot = -1, copy[2];
+        int32_t nc = 0;
+        const int rc = pkv_bm_append(bm, seqs[i], 1, &slot, copy, &nc);
+        if (rc != PKV_OK) return rc;                // not reached: checked above
+        if (nc) {
+            copies_out[2 * copies] = copy[0];
+            copies_out[2 * copies + 1] = copy[1];
+            ++copies;
+        }
+        if (slots_out) slots_out[i] = slot;
+        const auto& s = bm->seqs.at(seqs[i]);
+        std::fill(row, row + w, pad_block);
+        std::copy(s.blocks.begin(), s.blocks.end(), row);
+        if (seq_lens) seq_lens[i] = (int32_t)std::min<int64_t>(s.len, 0x7fffffff);
+    }
+    *num_copies = copies;
     return PKV_OK;
 }
 

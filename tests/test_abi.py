@@ -312,3 +312,27 @@ def test_int8_forms_reject_bad_arguments():
     assert dec(ks=None) == -1
     assert dec(vs=ctypes.c_void_p(0x400004)) == -5
     assert dec(B=0) == 0
+
+
+def test_copy_upload_graph_reject_bad_arguments():
+    lib = _lib().lib()
+    cp = lib.pkv_kv_cache_copy_blocks
+    assert cp(FAKE, 4096, 8, FAKE, -1, None) == -2              # negative pair count
+    assert cp(FAKE, 0, 8, FAKE, 1, None) == -2                  # empty blocks
+    assert cp(FAKE, 4096, 0, FAKE, 1, None) == -2               # empty pool
+    assert cp(FAKE, 6, 8, FAKE, 1, None) == -5                  # not a multiple of 4 bytes
+    assert cp(FAKE, 1 << 40, 1 << 40, FAKE, 1, None) == -2      # pool size overflows
+    assert cp(None, 4096, 8, FAKE, 0, None) == 0                # nothing to copy
+    assert cp(None, 4096, 8, FAKE, 1, None) == -1
+    assert cp(FAKE, 4096, 8, None, 1, None) == -1
+    assert cp(ctypes.c_void_p(0x100002), 4096, 8, FAKE, 1, None) == -5
+    assert lib.pkv_upload(None, None, 0, None) == 0
+    assert lib.pkv_upload(None, FAKE, 8, None) == -1
+    assert lib.pkv_upload(FAKE, None, 8, None) == -1
+    g = ctypes.c_void_p(0x1234)
+    assert lib.pkv_graph_begin(None) == -1                      # the NULL stream cannot capture
+    assert lib.pkv_graph_end(None, ctypes.byref(g)) == -1
+    assert lib.pkv_graph_end(FAKE, None) == -1
+    assert lib.pkv_graph_launch(None, None) == -1
+    assert lib.pkv_graph_destroy(None) == 0
+    assert b"graph" in lib.pkv_last_error()

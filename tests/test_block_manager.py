@@ -68,6 +68,20 @@ def test_random_walk_matches_model(seed, bs):
             sid = rng.choice(sorted(live)) if rng.random() < 0.95 else next_id + 5
             got, want = both(lambda: bm.free(sid), lambda: m.free(sid))
             live.discard(sid)
+        elif r < 0.55:
+            # one decode step over a fixed batch: live rows in random order, padding rows
+            ids = rng.sample(sorted(live), k=rng.randint(1, len(live)))
+            ids += [-1] * rng.randint(0, 3)
+            if rng.random() < 0.05:
+                ids.append(ids[0])                  # a repeated id: refused
+            rng.shuffle(ids)
+            pad = rng.choice([0, -1])
+
+            def c_step():
+                t, ln, sl, cp = bm.decode_step(ids, pad_block=pad)
+                return t.tolist(), ln.tolist(), sl.tolist(), [tuple(x) for x in cp.tolist()]
+
+            got, want = both(c_step, lambda: m.decode_step(ids, pad_block=pad))
         else:
             sid = rng.choice(sorted(live))
             n = rng.choice([0, 1, 1, 1, 2, 3, 7, bs + 1, 3 * bs])
@@ -142,3 +156,39 @@ def test_table_into_caller_arrays():
     assert lens.tolist() == [4, 9]
     with pytest.raises(ValueError):
         bm.table([1, 3], table=np.zeros((2, 4), dtype=np.int32))
+
+
+def test_decode_step_errors_change_nothing():
+    bm = pkv.BlockManager(6, 2, 3)
+    m = BlockManagerModel(6, 2, 3)
+    for x in (bm, m):
+        x.add(0)
+        x.append(0, 3)                              # blocks 5, 4 (one row in 4)
+        x.fork(0, 1)
+        x.add(2)
+        x.append(2, 2)                              # block 3, full
+    state = (bm.num_free, bm.table([0, 1, 2])[0].tolist())
+    for ids, status in (([0, 0], ERR_SHAPE), ([0, 7], ERR_SHAPE), ([1, 0, 2, 2], ERR_SHAPE)):
+        with pytest.raises(PagedKVError) as e:
+            bm.decode_step(ids)
+        assert e.value.status == status
+        with pytest.raises(ManagerError):
+            m.decode_step(ids)
+        assert (bm.num_free, bm.table([0, 1, 2])[0].tolist()) == state
+    # rows 0 and 1 share block 4: the first of them copies it, the second then owns it
+    t, ln, sl, cp = bm.decode_step([-1, 1, 0, 2])
+    rows, lens, slots, copies = m.decode_step([-1, 1, 0, 2])
+    assert t.tolist() == rows and ln.tolist() == lens and sl.tolist() == slots
+    assert [tuple(x) for x in cp.tolist()] == copies == [(4, 2)]
+    assert sl[0] == -1 and ln[0] == 0 and bm.num_free == 1    # blocks 2 (copy) and 1 taken
+    # rows 0 and 1 both start a block now, and one block is free: refused as a whole
+    state = (bm.num_free, bm.table([0, 1, 2])[0].tolist(), bm.length(0))
+    with pytest.raises(PagedKVError) as e:
+        bm.decode_step([0, 1, 2])
+    assert e.value.status == ERR_WORKSPACE
+    assert (bm.num_free, bm.table([0, 1, 2])[0].tolist(), bm.length(0)) == state
+    with pytest.raises(ManagerError) as e2:
+        m.decode_step([0, 1, 2])
+    assert e2.value.kind == "full" and m.seq_len[0] == 4 and m.num_free() == 1
+    with pytest.raises(PagedKVError):
+        bm.add(-3)
