@@ -466,6 +466,39 @@ PKV_API int pkv_graph_launch(void* graph, void* stream);
 /* Destroys a graph handle (NULL is a no-op); no replay of it may still be pending. */
 PKV_API int pkv_graph_destroy(void* graph);
 
+/*
+ * Step runner: a recorded decode step replayed with double-buffered uploads of its host-
+ * built inputs (the table and lengths: "Paged KV Cache and Packed Sequence", 5.3, the copy
+ * of the next step's table overlapping this step's attention).  The caller owns two device
+ * buffers and two pinned host buffers (hipHostMalloc) of `bytes` each, and records graph j
+ * (reading device buffer j) between pkv_runner_capture_begin(r, j, s) and
+ * pkv_runner_capture_end(r, s) on a created stream s.  Then per step:
+ *   h = pkv_runner_host_buffer(r)   [host] blocks until the upload that last read this
+ *                                   buffer has run (two steps back), returns it to fill;
+ *   pkv_runner_launch(r, stream)    the copy stream uploads h to its device buffer once the
+ *                                   replay that last read that buffer is done, and `stream`
+ *                                   (any stream, NULL included) waits for that upload only,
+ *                                   then replays the matching graph.
+ * The runner owns a copy stream (default priority), four events and the two graphs; it
+ * allocates no device memory.  pkv_runner_destroy waits for its pending work first.
+ */
+typedef struct pkv_step_runner pkv_step_runner;
+/* NULL (and pkv_last_error) on NULL or repeated buffers, bytes = 0 or a HIP error. */
+PKV_API pkv_step_runner* pkv_runner_create(void* dev0, void* dev1, const void* host0,
+                                           const void* host1, size_t bytes);
+PKV_API int pkv_runner_destroy(pkv_step_runner* r);
+/* Starts recording graph j (0 or 1) on `stream`; PKV_ERR_SHAPE if j is recorded already or
+ * another capture of this runner is open. */
+PKV_API int pkv_runner_capture_begin(pkv_step_runner* r, int32_t j, void* stream);
+PKV_API int pkv_runner_capture_end(pkv_step_runner* r, void* stream);
+/* The executable graph j (for pkv_graph_launch without an upload), or NULL. */
+PKV_API void* pkv_runner_graph(pkv_step_runner* r, int32_t j);
+/* [host] The host buffer the next pkv_runner_launch uploads, once free; NULL on error. */
+PKV_API void* pkv_runner_host_buffer(pkv_step_runner* r);
+/* Enqueues the next step (upload + replay) as described above; PKV_ERR_SHAPE if its graph
+ * was not recorded. */
+PKV_API int pkv_runner_launch(pkv_step_runner* r, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

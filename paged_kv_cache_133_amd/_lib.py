@@ -31,7 +31,10 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_bm_add", "pkv_bm_fork", "pkv_bm_append", "pkv_bm_decode_step", "pkv_bm_free",
            "pkv_bm_length",
            "pkv_bm_ref_count", "pkv_bm_table", "pkv_kv_cache_copy_blocks", "pkv_upload",
-           "pkv_graph_begin", "pkv_graph_end", "pkv_graph_launch", "pkv_graph_destroy")
+           "pkv_graph_begin", "pkv_graph_end", "pkv_graph_launch", "pkv_graph_destroy",
+           "pkv_runner_create", "pkv_runner_destroy", "pkv_runner_capture_begin",
+           "pkv_runner_capture_end", "pkv_runner_graph", "pkv_runner_host_buffer",
+           "pkv_runner_launch")
 
 
 class PagedKVError(RuntimeError):
@@ -125,6 +128,20 @@ def lib() -> ctypes.CDLL:
     L.pkv_graph_launch.argtypes = [p, p]
     L.pkv_graph_destroy.restype = ctypes.c_int
     L.pkv_graph_destroy.argtypes = [p]
+    L.pkv_runner_create.restype = p
+    L.pkv_runner_create.argtypes = [p, p, p, p, sz]
+    L.pkv_runner_destroy.restype = ctypes.c_int
+    L.pkv_runner_destroy.argtypes = [p]
+    L.pkv_runner_capture_begin.restype = ctypes.c_int
+    L.pkv_runner_capture_begin.argtypes = [p, i32, p]
+    L.pkv_runner_capture_end.restype = ctypes.c_int
+    L.pkv_runner_capture_end.argtypes = [p, p]
+    L.pkv_runner_graph.restype = p
+    L.pkv_runner_graph.argtypes = [p, i32]
+    L.pkv_runner_host_buffer.restype = p
+    L.pkv_runner_host_buffer.argtypes = [p]
+    L.pkv_runner_launch.restype = ctypes.c_int
+    L.pkv_runner_launch.argtypes = [p, p]
     _lib = L
     return L
 

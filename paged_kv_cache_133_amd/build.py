@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 SOURCES = ["api.hip", "write.hip", "norm_rope.hip", "decode.hip", "int8_kv.hip", "mla_attn.hip",
-           "varlen_attn.hip", "gqa_attn.hip", "block_manager.hip"]
+           "varlen_attn.hip", "gqa_attn.hip", "block_manager.hip",
+           "runner.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

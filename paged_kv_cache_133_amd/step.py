@@ -1,17 +1,17 @@
-"""A decode step recorded once and replayed with new host-built tables.
+"""A decode step recorded once and replayed with new host-built tables (pkv_runner_*).
 
 "Paged KV Cache and Packed Sequence", 5.3: the block table changes every step, so the
-recorded step must not hold it; the host builds it (BlockManager.table) into a tensor that
-is copied to the device before each replay, and with two such buffers the copy for the next
-step runs while this step's attention does.  Here:
+recorded step must not hold it; the host builds it (BlockManager.decode_step) into a
+buffer that is copied to the device before each replay, and with two such buffers the copy
+for the next step runs while this step's attention does.  Here:
 
   * two pinned host buffers and two device buffers, each [batch * max_blocks_per_seq +
-    batch] int32 (the table, then seq_lens_kv);
-  * two graphs, graph j recording pkv_paged_attn_decode_ex (write of the new rows and
-    attention) over device buffer j, on a stream of its own;
-  * launch(): the upload of buffer j runs on a copy stream once the graph that last read
-    device buffer j is done, and graph j waits for that upload only, so the upload of step
-    t+1 overlaps the attention of step t when the host runs ahead.
+    batch] int32 (the table, then seq_lens_kv), owned by this object;
+  * two graphs in a native step runner, graph j recording pkv_paged_attn_decode_ex (write
+    of the new rows and attention) over device buffer j;
+  * launch(): one library call that uploads buffer j on the runner's copy stream once the
+    replay that last read device buffer j is done, and replays graph j on the current
+    stream after that upload only.
 
 The batch is fixed at capture; rows without a sequence are padding rows (length 0: output
 0, lse -inf, nothing written, slot -1).  Inputs q, k_new and v_new are the step's own
@@ -23,7 +23,8 @@ import ctypes
 
 import torch
 
-from ._lib import _check, lib, new_decode_workspace, paged_attn_decode_append, upload
+from ._lib import PagedKVError, _check, _stream, lib, new_decode_workspace, \
+    paged_attn_decode_append
 
 
 class GraphDecodeStep:
@@ -35,6 +36,7 @@ class GraphDecodeStep:
         self.device, self.batch, self.mbs = dev, batch, max_blocks_per_seq
         self.max_len = max_blocks_per_seq * bs
         n = batch * max_blocks_per_seq + batch
+        self.nbytes = n * 4
         self.staging = [torch.zeros(n, dtype=torch.int32, pin_memory=True) for _ in range(2)]
         self._host = [s.numpy() for s in self.staging]
         self.dev = [torch.zeros(n, dtype=torch.int32, device=dev) for _ in range(2)]
@@ -45,32 +47,30 @@ class GraphDecodeStep:
         self.lse = torch.zeros(batch, num_q_heads, dtype=torch.float32, device=dev)
         self.slots = torch.zeros(batch, dtype=torch.int64, device=dev)
         self.workspace = new_decode_workspace(batch, num_q_heads, hkv, d, self.max_len, dev)
-        self.main = torch.cuda.Stream(dev)
-        self.copy = torch.cuda.Stream(dev)
-        self._main_h = ctypes.c_void_p(self.main.cuda_stream)
-        self.uploaded = [torch.cuda.Event() for _ in range(2)]
-        self.consumed = [torch.cuda.Event() for _ in range(2)]
-        self.graphs = []
-        self.main.wait_stream(torch.cuda.current_stream(dev))
+        vp = ctypes.c_void_p
+        self._r = lib().pkv_runner_create(vp(self.dev[0].data_ptr()), vp(self.dev[1].data_ptr()),
+                                          vp(self.staging[0].data_ptr()),
+                                          vp(self.staging[1].data_ptr()), self.nbytes)
+        if not self._r:
+            msg = lib().pkv_last_error()
+            raise PagedKVError(-8, msg.decode() if msg else "")
+        cap = torch.cuda.Stream(dev)
+        cap_h = vp(cap.cuda_stream)
+        cap.wait_stream(torch.cuda.current_stream(dev))
         for j in range(2):
             table, lens = self.device_views(j)
-            with torch.cuda.stream(self.main):
-                _check(lib().pkv_graph_begin(self._main_h))
-                g = ctypes.c_void_p()
+            with torch.cuda.stream(cap):
+                _check(lib().pkv_runner_capture_begin(self._r, j, cap_h))
                 try:
                     paged_attn_decode_append(self.q, self.k_new, self.v_new, k_cache, v_cache,
                                              table, lens, self.max_len, softmax_scale,
                                              out=self.out, lse=self.lse,
                                              workspace=self.workspace, slots_out=self.slots,
                                              window=window)
-                except BaseException:
-                    lib().pkv_graph_end(self._main_h, ctypes.byref(g))
-                    lib().pkv_graph_destroy(g)
-                    self.close()
-                    raise
-                _check(lib().pkv_graph_end(self._main_h, ctypes.byref(g)))
-            self.graphs.append(g)
-        self.t = 0
+                finally:
+                    rc = lib().pkv_runner_capture_end(self._r, cap_h)
+                _check(rc)
+        torch.cuda.current_stream(dev).wait_stream(cap)
 
     def device_views(self, j: int):
         cut = self.batch * self.mbs
@@ -80,41 +80,25 @@ class GraphDecodeStep:
         """(table [batch][max_blocks_per_seq], seq_lens [batch]) numpy views of the pinned
         buffer the next launch() uploads; fill both before calling it.  Waits until the
         upload that last read this buffer has run."""
-        j = self.t % 2
-        self.uploaded[j].synchronize()
+        p = lib().pkv_runner_host_buffer(self._r)
+        if not p:
+            _check(-8)
+        j = 0 if p == self.staging[0].data_ptr() else 1
         cut = self.batch * self.mbs
         v = self._host[j]
         return v[:cut].reshape(self.batch, self.mbs), v[cut:]
 
-    def launch(self, timing=None):
-        """Upload the host tables and replay the step; the current stream then waits for
-        it (out, lse and slots are ready for work enqueued on it afterwards).  timing: an
-        optional dict of two timing-event pairs, "upload" (recorded on the copy stream
-        around the upload) and "graph" (on the step's stream around the replay)."""
-        j = self.t % 2
-        cur = torch.cuda.current_stream(self.device)
-        self.copy.wait_event(self.consumed[j])
-        if timing:
-            timing["upload"][0].record(self.copy)
-        with torch.cuda.stream(self.copy):
-            upload(self.dev[j], self.staging[j])
-        if timing:
-            timing["upload"][1].record(self.copy)
-        self.uploaded[j].record(self.copy)
-        self.main.wait_stream(cur)
-        self.main.wait_event(self.uploaded[j])
-        if timing:
-            timing["graph"][0].record(self.main)
-        _check(lib().pkv_graph_launch(self.graphs[j], self._main_h))
-        if timing:
-            timing["graph"][1].record(self.main)
-        self.consumed[j].record(self.main)
-        cur.wait_stream(self.main)
-        self.t += 1
+    def launch(self):
+        """Upload the host tables and replay the step on the current stream."""
+        _check(lib().pkv_runner_launch(self._r, _stream(self.device)))
+
+    def graph(self, j: int):
+        """Executable graph j (replay without an upload: pkv_graph_launch)."""
+        return lib().pkv_runner_graph(self._r, j)
 
     def close(self):
-        for g in getattr(self, "graphs", []):
-            lib().pkv_graph_destroy(g)
-        self.graphs = []
+        if getattr(self, "_r", None):
+            lib().pkv_runner_destroy(self._r)
+            self._r = None
 
     __del__ = close

@@ -336,3 +336,17 @@ def test_copy_upload_graph_reject_bad_arguments():
     assert lib.pkv_graph_launch(None, None) == -1
     assert lib.pkv_graph_destroy(None) == 0
     assert b"graph" in lib.pkv_last_error()
+
+
+def test_runner_rejects_bad_arguments():
+    lib = _lib().lib()
+    assert not lib.pkv_runner_create(None, FAKE, FAKE, FAKE, 64)
+    assert b"runner_create" in lib.pkv_last_error()
+    assert not lib.pkv_runner_create(FAKE, FAKE, FAKE, ctypes.c_void_p(0x200000), 64)   # same device buffer
+    assert not lib.pkv_runner_create(FAKE, ctypes.c_void_p(0x200000), FAKE, ctypes.c_void_p(0x300000), 0)
+    assert lib.pkv_runner_destroy(None) == 0
+    assert lib.pkv_runner_capture_begin(None, 0, FAKE) == -1
+    assert lib.pkv_runner_capture_end(None, FAKE) == -1
+    assert lib.pkv_runner_launch(None, None) == -1
+    assert not lib.pkv_runner_graph(None, 0)
+    assert not lib.pkv_runner_host_buffer(None)

@@ -273,3 +273,41 @@ def test_serving_loop_graph_replays(hq, hkv, d):
     assert copies_seen > 0, "the walk never exercised a copy on write"
     step.close()
     bm.close()
+
+
+def test_runner_capture_errors_and_plain_replays():
+    """The runner refuses a second open capture and a launch of an unrecorded graph; a
+    recorded step replayed many times with eager work between equals the eager call."""
+    import ctypes
+    from paged_kv_cache_133_amd._lib import PagedKVError, _check, lib
+    say("runner capture errors and replays")
+    bs, hq, hkv, d, B, mbs = 16, 8, 2, 128, 3, 8
+    g = torch.Generator(device=DEV).manual_seed(3)
+    k = torch.randn(40, bs, hkv, d, generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn(40, bs, hkv, d, generator=g, device=DEV).to(torch.bfloat16)
+    step = GraphDecodeStep(k.clone(), v.clone(), B, mbs, hq, 0.088)
+    s = torch.cuda.Stream(DEV)
+    sh = ctypes.c_void_p(s.cuda_stream)
+    assert lib().pkv_runner_capture_begin(step._r, 0, sh) == -2       # graph 0 exists
+    assert lib().pkv_runner_capture_begin(step._r, 2, sh) == -2
+    assert lib().pkv_runner_capture_end(step._r, sh) == -2             # none open
+    kk, vv = k.clone(), v.clone()
+    table = torch.arange(B * mbs, dtype=torch.int32).view(B, mbs) + 5
+    for rep, lens in enumerate(([1, 17, 100], [2, 18, 101], [0, 19, 102], [4, 0, 103], [5, 1, 104])):
+        tab, ln = step.host_tables()
+        tab[:] = table.numpy()
+        ln[:] = lens
+        step.q.copy_(torch.randn(B, hq, d, generator=g, device=DEV).to(torch.bfloat16))
+        step.k_new.copy_(torch.randn(B, hkv, d, generator=g, device=DEV).to(torch.bfloat16))
+        step.v_new.copy_(torch.randn(B, hkv, d, generator=g, device=DEV).to(torch.bfloat16))
+        step.launch()
+        out, lse = pkv.paged_attn_decode_append(
+            step.q, step.k_new, step.v_new, kk, vv, table.to(DEV),
+            torch.tensor(lens, dtype=torch.int32, device=DEV), mbs * bs, 0.088,
+            lse=torch.empty(B, hq, dtype=torch.float32, device=DEV))
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(step.out), _bits(out)), rep
+        assert torch.equal(_bits(step.lse), _bits(lse)), rep
+    step.close()
+    with pytest.raises(PagedKVError):
+        _check(lib().pkv_runner_launch(None, None))
