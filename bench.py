@@ -47,6 +47,8 @@ def dominant_kernel(w):
     sources its traffic counters depend on."""
     if w.mode == "mla":
         return "mla_decode_kernel", [CSRC + "mla_attn.hip"] + MFMA_SOURCES
+    if w.q_tokens:      # multi-token decode: the range-streaming kernel
+        return "gqa_stream_kernel", [CSRC + "gqa_attn.hip"] + MFMA_SOURCES
     if w.mode == "varlen":
         return "varlen_kernel<128>", [CSRC + "varlen_attn.hip"] + MFMA_SOURCES
     if w.kv_dtype == "int8":
@@ -243,6 +245,29 @@ def cpu_baseline(case, kv_bytes, min_seconds):
                        f"{med * 1e3:.1f} ms/step")}
 
 
+def step_description(w, path):
+    """What one timed step launches, for the JSON line."""
+    if int8_workload(w):
+        return ("slot_mapping, kv_cache_write_int8 (quantizing write), decode_int8 split pass, "
+                "combine")
+    if w.q_tokens:
+        return ("kv_cache_append (slot_mapping + write of the step's %d rows per sequence), "
+                "decode_mtp range pass, combine" % w.q_tokens)
+    if w.mode == "varlen":
+        return "kv_cache_append (slot_mapping + write), varlen causal attention"
+    if w.mode == "mla":
+        return {"separate": "slot_mapping, kv_cache_write (nope + rope), MLA split pass, combine"}.get(
+            path, "kv_cache_append (nope + rope), MLA split pass, combine")
+    return {"fused": "paged_attn_decode_append: split pass that also writes the new "
+                     "token (slot_mapping + write + split-KV attention), then combine",
+            "append": "kv_cache_append (slot_mapping + write), decode split, combine",
+            "separate": "slot_mapping, kv_cache_write, decode split, combine"}[path]
+
+
+def int8_workload(w):
+    return w.kv_dtype == "int8"
+
+
 def serving(args):
     """--serving: the decode layer of a workload as a serving loop runs it, once per block
     size ("Paged KV Cache and Packed Sequence", 5.3-5.4).  The sequences start at the
@@ -430,6 +455,12 @@ def main():
     need = pkv.decode_workspace_size(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim_v,
                                      case.max_len_after)
     ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+    ws_mtp = None
+    if w.q_tokens:
+        need = int(_lib.lib().pkv_decode_mtp_workspace_size(w.batch, w.q_tokens, w.num_q_heads,
+                                                            w.num_kv_heads, w.head_dim_v,
+                                                            case.max_len_after))
+        ws_mtp = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
     slot_call = _lib.prepare_slot_mapping(table, lb, cu, w.block_size, T, slots)
     fused = args.path == "fused"
     reps = []
@@ -453,6 +484,13 @@ def main():
         else:
             v = case.cache_v if r == 0 else case.cache_v.clone()
             pair = (case.new_k, case.new_v, k, v)
+        if w.q_tokens:
+            write = _lib.prepare_kv_cache_append(*pair, table, lb, cu, case.max_new, slots)
+            attn, combine, _ = _lib.prepare_decode_mtp(case.q, k, v, table, la, w.q_tokens,
+                                                       case.max_len_after, w.scale, out=out,
+                                                       lse=lse, workspace=ws_mtp, window=w.window)
+            reps.append((write, attn, combine))
+            continue
         if w.mode == "varlen":
             write = _lib.prepare_kv_cache_append(*pair, table, lb, cu, case.max_new, slots)
             attn = _lib.prepare_varlen(case.q, k, v, table, cu, la, case.max_new, w.scale,
@@ -554,10 +592,7 @@ def main():
            "kv_tokens": int(case.lens_after.sum()), "max_kv_len": case.max_len_after,
            "pool_replicas": R,
            "path": args.path,
-           "step": {"fused": "paged_attn_decode_append: split pass that also writes the new "
-                             "token (slot_mapping + write + split-KV attention), then combine",
-                    "append": "kv_cache_append (slot_mapping + write), decode split, combine",
-                    "separate": "slot_mapping, kv_cache_write, decode split, combine"}[args.path]}
+           "step": step_description(w, args.path)}
     line = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

@@ -335,8 +335,8 @@ PKV_API int pkv_paged_attn_varlen(void* out, float* lse_out, const void* q,
  * over the cache (slot_mapping_out then unused).  stages as for decode_append; workspace:
  * pkv_decode_workspace_size(...) bytes suffice for any window.  Other arguments, support
  * and preconditions as for pkv_paged_attn_decode_append / pkv_paged_attn_decode.
- * MTP decode (next_n + 1 query tokens per sequence, causal) goes through
- * pkv_paged_attn_varlen(_ex) with n_b = next_n + 1 (skill page, Appendix E).
+ * MTP decode (next_n + 1 query tokens per sequence, causal): pkv_paged_attn_decode_mtp
+ * below, or pkv_paged_attn_varlen(_ex) with n_b = next_n + 1 (skill page, Appendix E).
  */
 PKV_API int pkv_paged_attn_decode_ex(void* out, float* lse_out, const void* q, const void* k_new,
                              const void* v_new, void* k_cache, void* v_cache,
@@ -346,6 +346,38 @@ PKV_API int pkv_paged_attn_decode_ex(void* out, float* lse_out, const void* q, c
                              int32_t head_dim, int32_t block_size, int64_t num_blocks,
                              float softmax_scale, int32_t dtype, int32_t window, int32_t stages,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Multi-token decode (MTP: next_n + 1 = num_q_tokens query tokens per sequence, causal;
+ * "KVCache Optimization Skill", Appendix E, sparse_mode 3 with next_n): sequence b's rows
+ * are q[b * num_q_tokens + i], i < num_q_tokens, the last num_q_tokens of its
+ * seq_lens_kv[b] cached tokens (written beforehand with pkv_kv_cache_write).  Row i sees
+ * keys p <= seq_lens_kv[b] - num_q_tokens + i (and, with window > 0, the `window` most
+ * recent of those).  The same result as pkv_paged_attn_varlen_ex with
+ * cu_seqlens_q[b] = b * num_q_tokens and causal = 1, computed like a decode: each K/V row is
+ * read once per kv head for all the sequence's query tokens and heads.
+ *   q, out [batch * num_q_tokens][num_q_heads][head_dim]; lse_out [batch * num_q_tokens][num_q_heads]
+ *   workspace: pkv_decode_mtp_workspace_size(...) bytes, 16-byte aligned
+ *   stages: 1 = the range pass, 2 = the combine pass, 3 = both (1 then 2 equals 3).
+ * Supported: bf16, head_dim 64 or 128, num_q_tokens * (num_q_heads / num_kv_heads) <= 16,
+ * block_size >= 4 (head_dim 128) / 8 (head_dim 64), batch <= 1024; other shapes return
+ * PKV_ERR_UNSUPPORTED (pkv_paged_attn_varlen_ex covers them).  Device preconditions:
+ * num_q_tokens <= seq_lens_kv[b] <= max_seq_len_kv, or seq_lens_kv[b] = 0 (padding: the
+ * sequence's rows are 0 with lse -inf); table entries as for pkv_paged_attn_decode.
+ */
+PKV_API size_t pkv_decode_mtp_workspace_size(int32_t batch, int32_t num_q_tokens,
+                                             int32_t num_q_heads, int32_t num_kv_heads,
+                                             int32_t head_dim_v, int32_t max_seq_len_kv);
+PKV_API int pkv_paged_attn_decode_mtp(void* out, float* lse_out, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* seq_lens_kv,
+                                      int32_t batch, int32_t num_q_tokens,
+                                      int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                      float softmax_scale, int32_t dtype, int32_t window,
+                                      int32_t stages, void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /* pkv_paged_attn_varlen with the window (causal or not: hi = the row's last visible key). */
 PKV_API int pkv_paged_attn_varlen_ex(void* out, float* lse_out, const void* q,

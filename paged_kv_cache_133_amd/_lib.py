@@ -34,7 +34,7 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_graph_begin", "pkv_graph_end", "pkv_graph_launch", "pkv_graph_destroy",
            "pkv_runner_create", "pkv_runner_destroy", "pkv_runner_capture_begin",
            "pkv_runner_capture_end", "pkv_runner_graph", "pkv_runner_host_buffer",
-           "pkv_runner_launch")
+           "pkv_runner_launch", "pkv_decode_mtp_workspace_size", "pkv_paged_attn_decode_mtp")
 
 
 class PagedKVError(RuntimeError):
@@ -128,6 +128,11 @@ def lib() -> ctypes.CDLL:
     L.pkv_graph_launch.argtypes = [p, p]
     L.pkv_graph_destroy.restype = ctypes.c_int
     L.pkv_graph_destroy.argtypes = [p]
+    L.pkv_decode_mtp_workspace_size.restype = sz
+    L.pkv_decode_mtp_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.pkv_paged_attn_decode_mtp.restype = ctypes.c_int
+    L.pkv_paged_attn_decode_mtp.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                            i32, i32, i64, f32, i32, i32, i32, p, sz, p]
     L.pkv_runner_create.restype = p
     L.pkv_runner_create.argtypes = [p, p, p, p, sz]
     L.pkv_runner_destroy.restype = ctypes.c_int
@@ -459,6 +464,52 @@ def prepare_kv_cache_write(k_new, v_new, k_cache, v_cache, slots):
     args = (_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(slots), slots.shape[0],
             hkv, dk, dv, bs, nb, _dtype_code(k_cache), _stream(k_cache.device))
     return PreparedCall(lib().pkv_kv_cache_write, args, (k_new, v_new, k_cache, v_cache, slots))
+
+
+def _decode_mtp_args(q, k_cache, v_cache, block_table, seq_lens_kv, num_q_tokens,
+                     max_seq_len_kv, softmax_scale, stages, out, lse, workspace, window):
+    """Arguments of pkv_paged_attn_decode_mtp."""
+    _dev(q, k_cache, v_cache, block_table, seq_lens_kv, out, lse, workspace)
+    rows, hq, d = q.shape
+    B = seq_lens_kv.shape[0]
+    if rows != B * num_q_tokens:
+        raise ValueError(f"q has {rows} rows, expected batch * num_q_tokens = {B * num_q_tokens}")
+    nb, bs, hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        need = int(lib().pkv_decode_mtp_workspace_size(B, num_q_tokens, hq, hkv, d, max_seq_len_kv))
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
+    args = (_ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(seq_lens_kv), B, num_q_tokens, block_table.shape[1], max_seq_len_kv, hq, hkv, d,
+            bs, nb, float(softmax_scale), _dtype_code(q), int(window), stages, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(q.device))
+    return args, out, workspace
+
+
+def paged_attn_decode_mtp(q, k_cache, v_cache, block_table, seq_lens_kv, num_q_tokens,
+                          max_seq_len_kv, softmax_scale, out=None, lse=None, workspace=None,
+                          window=0):
+    """Decode of num_q_tokens causal query tokens per sequence (pkv_paged_attn_decode_mtp);
+    q [batch * num_q_tokens][Hq][D].  Returns (out, lse)."""
+    args, out, _ = _decode_mtp_args(q, k_cache, v_cache, block_table, seq_lens_kv, num_q_tokens,
+                                    max_seq_len_kv, softmax_scale, 3, out, lse, workspace, window)
+    _check(lib().pkv_paged_attn_decode_mtp(*args))
+    return out, lse
+
+
+def prepare_decode_mtp(q, k_cache, v_cache, block_table, seq_lens_kv, num_q_tokens,
+                       max_seq_len_kv, softmax_scale, out=None, lse=None, workspace=None, window=0):
+    """(range pass, combine pass) prepared calls of pkv_paged_attn_decode_mtp."""
+    calls = []
+    for stages in (1, 2):
+        args, out, workspace = _decode_mtp_args(q, k_cache, v_cache, block_table, seq_lens_kv,
+                                                num_q_tokens, max_seq_len_kv, softmax_scale,
+                                                stages, out, lse, workspace, window)
+        calls.append(PreparedCall(lib().pkv_paged_attn_decode_mtp, args,
+                                  (q, k_cache, v_cache, block_table, seq_lens_kv, out, lse,
+                                   workspace)))
+    return calls[0], calls[1], out
 
 
 def _varlen_args(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, max_seqlen_q,

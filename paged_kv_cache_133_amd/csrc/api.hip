@@ -270,7 +270,8 @@ int prepare_decode(pkv::DecodeParams& p, pkv::DecodePlan& plan, void* out, float
                    int32_t head_dim_qk, int32_t head_dim_v, int32_t head_dim_rope,
                    int32_t block_size, int64_t num_blocks, float softmax_scale, int32_t dtype,
                    void* workspace, size_t workspace_bytes, bool* nothing_to_do,
-                   int32_t window = 0, bool allow_stream = true, bool byte_rows = false) {
+                   int32_t window = 0, bool allow_stream = true, bool byte_rows = false,
+                   int32_t qn = 0) {
     *nothing_to_do = false;
     if (window < 0) return fail(PKV_ERR_SHAPE, "decode: window must be >= 0 (0: no window)");
     if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "decode: unknown dtype %d", dtype);
@@ -313,7 +314,7 @@ int prepare_decode(pkv::DecodeParams& p, pkv::DecodePlan& plan, void* out, float
     // With a window a sequence's splits cover at most window + 31 keys (they start at the
     // window start rounded down to 32): plan for that length.
     const int32_t plan_len = window > 0 && window < max_seq_len_kv - 31 ? window + 31 : max_seq_len_kv;
-    plan = pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim_v, plan_len, byte_rows);
+    plan = pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim_v, plan_len, byte_rows, qn);
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))
         return fail(PKV_ERR_WORKSPACE, "decode: workspace needs %zu bytes (16-byte aligned), got %zu",
                     plan.ws_bytes, workspace ? workspace_bytes : (size_t)0);
@@ -343,7 +344,8 @@ int prepare_decode(pkv::DecodeParams& p, pkv::DecodePlan& plan, void* out, float
     p.num_blocks = num_blocks;
     p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
     p.window = window;
-    if (allow_stream && pkv::gqa_stream_supported(dtype, group, head_dim_v, p.bs_log2, batch)) {
+    p.qn = qn > 0 ? qn : 1;
+    if (qn > 0 || (allow_stream && pkv::gqa_stream_supported(dtype, group, head_dim_v, p.bs_log2, batch))) {
         p.parts = plan.parts;
         p.ws_o = reinterpret_cast<float*>(ws + plan.st_o_offset);
         p.ws_ml = reinterpret_cast<float*>(ws + plan.st_ml_offset);
@@ -648,6 +650,57 @@ int pkv_paged_attn_decode_ex(void* out, float* lse_out, const void* q, const voi
                           num_kv_heads, head_dim, block_size, num_blocks, softmax_scale, dtype,
                           window, stages, workspace, workspace_bytes, (hipStream_t)stream,
                           "decode_ex");
+}
+
+size_t pkv_decode_mtp_workspace_size(int32_t batch, int32_t num_q_tokens, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim_v, int32_t max_seq_len_kv) {
+    if (batch <= 0 || num_q_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        head_dim_v <= 0 || max_seq_len_kv <= 0 || num_q_heads % num_kv_heads)
+        return 0;
+    return pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim_v, max_seq_len_kv, false,
+                            num_q_tokens).ws_bytes;
+}
+
+int pkv_paged_attn_decode_mtp(void* out, float* lse_out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens_kv, int32_t batch, int32_t num_q_tokens,
+                              int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int64_t num_blocks, float softmax_scale,
+                              int32_t dtype, int32_t window, int32_t stages, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (stages < 1 || stages > 3) return fail(PKV_ERR_SHAPE, "decode_mtp: stages must be 1, 2 or 3");
+    if (num_q_tokens < 1) return fail(PKV_ERR_SHAPE, "decode_mtp: num_q_tokens must be >= 1");
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+        return fail(PKV_ERR_SHAPE, "decode_mtp: num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                    num_q_heads, num_kv_heads);
+    if (dtype != PKV_BF16 && dtype != PKV_F32) return fail(PKV_ERR_DTYPE, "decode_mtp: unknown dtype %d", dtype);
+    const int64_t cols = (int64_t)num_q_tokens * (num_q_heads / num_kv_heads);
+    if (dtype != PKV_BF16 || cols > 16)
+        return fail(PKV_ERR_UNSUPPORTED, "decode_mtp: bf16 with num_q_tokens * (query heads per kv head) <= 16 "
+                    "(got %lld); pkv_paged_attn_varlen_ex covers the rest", (long long)cols);
+    if (!pow2_in(block_size, 1, 256))
+        return fail(PKV_ERR_UNSUPPORTED, "decode_mtp: block_size %d is not a power of two in [1, 256]", block_size);
+    if (!pkv::gqa_stream_shape_supported(head_dim, log2i(block_size), batch))
+        return fail(PKV_ERR_UNSUPPORTED, "decode_mtp: head_dim %d, block_size %d, batch %d not supported "
+                    "(head_dim 64/128, block_size >= 1024 / (2 head_dim), batch <= 1024); "
+                    "pkv_paged_attn_varlen_ex covers the rest", head_dim, block_size, batch);
+    if ((int64_t)batch * num_q_tokens > 0x7fffffffLL) return fail(PKV_ERR_SHAPE, "decode_mtp: too many rows");
+    pkv::DecodeParams p;
+    pkv::DecodePlan plan{};
+    bool idle = false;
+    int rc = prepare_decode(p, plan, out, lse_out, q, nullptr, k_cache, v_cache, nullptr, block_table,
+                            seq_lens_kv, batch, max_blocks_per_seq, max_seq_len_kv, num_q_heads,
+                            num_kv_heads, head_dim, head_dim, 0, block_size, num_blocks, softmax_scale,
+                            dtype, workspace, workspace_bytes, &idle, window, true, false, num_q_tokens);
+    if (rc != PKV_OK || idle) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (stages & 1) {
+        rc = hip_status(pkv::launch_gqa_decode(p, head_dim, s), "decode_mtp launch");
+        if (rc != PKV_OK) return rc;
+    }
+    if ((stages & 2) && needs_combine(p, plan)) return launch_combine_for(p, head_dim, dtype, s);
+    return PKV_OK;
 }
 
 int pkv_kv_cache_write_int8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

@@ -358,7 +358,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
 
 DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t head_dim_v, int32_t max_seq_len_kv, bool byte_rows) {
+                       int32_t head_dim_v, int32_t max_seq_len_kv, bool byte_rows, int32_t qn) {
     DecodePlan pl{};
     const int G = num_q_heads / num_kv_heads;
     // Larger groups carry more partial state per split: use longer splits for them (and
@@ -377,9 +377,9 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
         pl.ws_ml_offset = align256(rows * head_dim_v * sizeof(float));
         pl.ws_bytes = pl.ws_ml_offset + rows * 2 * sizeof(float);
     }
-    if (gqa_mfma_supported(1, G)) {      // the range-streaming layout, if that kernel runs
+    if (gqa_mfma_supported(1, G) || qn > 0) {   // the range-streaming layout, if that kernel runs
         pl.parts = gqa_stream_parts(num_kv_heads);
-        const size_t parts = (size_t)num_kv_heads * pl.parts * 2 * G;
+        const size_t parts = (size_t)num_kv_heads * pl.parts * 2 * G * (qn > 0 ? qn : 1);
         pl.st_o_offset = 0;
         pl.st_ml_offset = align256(parts * head_dim_v * sizeof(float));
         pl.st_pre_offset = align256(pl.st_ml_offset + parts * 2 * sizeof(float));

@@ -32,6 +32,12 @@
 //
 // Append mode reads this step's token from the new rows, and the workgroup whose range
 // holds it writes the kv head's slice to the cache.
+//
+// Multi-token decode (MTP, "KVCache Optimization Skill", Appendix E: next_n + 1 query tokens
+// per sequence, causal): the range kernel takes qn query tokens per sequence, the product
+// columns standing for (token, head) pairs, qn * G <= 16.  Column (i, h) sees keys up to
+// L - qn + i (bottom-right causal, its own token included), so only a sequence's last tile
+// is masked differently per column; every K/V row is still read once per kv head.
 #include "mfma_common.h"
 
 namespace pkv {
@@ -228,6 +234,7 @@ __device__ __forceinline__ int range_of(int x, int T, int P) { return (int)(((in
 // ksa = ks rounded down to a tile; seg counts the sequences with tiles entered so far.
 struct Cursor {
     int b, pre, end, L, ks, ksa, seg;
+    int ks_last;                      // first key the last query token sees (>= ks)
 };
 
 template <int D, bool APPEND>
@@ -246,15 +253,22 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
     const int w = blockIdx.x / p.hkv;
     const int P = p.parts;
     const int G = p.group;
-    const bool valid = n < G;
+    const int qn = max(p.qn, 1);      // query tokens per sequence (1: decode)
+    const int NC = qn * G;            // columns in use: (token, head) pairs
+    const bool valid = n < NC;
+    const int tok = valid ? n / G : 0;
+    const int hcol = n - tok * G;
+    const int back = qn - 1 - tok;    // this column sees keys below L - back
+    auto out_row = [&](int b) { return ((int64_t)b * qn + tok) * p.hq + kvh * G + hcol; };
 
     // Tiles of every sequence and their prefix over the batch (the same in every
-    // workgroup; workgroup 0 also leaves it for the combine).
+    // workgroup; workgroup 0 also leaves it for the combine).  Tiles start at the first
+    // key the first query token sees.
     int total = 0;
     for (int c0 = 0; c0 < p.batch; c0 += 64) {
         const int b = c0 + lane;
         const int L = b < p.batch ? min(p.seq_lens[b], p.len_cap) : 0;
-        const int nt = L > 0 ? (L - window_start32(L, p.window) + kKeys - 1) / kKeys : 0;
+        const int nt = L > 0 ? (L - window_start32(L - qn + 1, p.window) + kKeys - 1) / kKeys : 0;
         int v = nt;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -293,7 +307,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         while (em) {
             const int bb = c0 + __builtin_ctzll(em);
             em &= em - 1;
-            if (valid) store_empty<D>(p, (int64_t)bb * p.hq + kvh * G + n, g);
+            if (valid) store_empty<D>(p, out_row(bb), g);
         }
         if (APPEND) {
             uint64_t mm = __ballot(mine);
@@ -323,7 +337,8 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         c.pre = __builtin_amdgcn_readfirstlane(s_pre[b]);
         c.end = __builtin_amdgcn_readfirstlane(s_pre[b + 1]);
         c.L = __builtin_amdgcn_readfirstlane(s_len[b]);
-        c.ks = window_start(c.L, p.window);
+        c.ks = window_start(c.L - qn + 1, p.window);
+        c.ks_last = window_start(c.L, p.window);
         c.ksa = c.ks & ~(kKeys - 1);
         c.seg = 0;
         return c;
@@ -337,7 +352,8 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
             c.end = __builtin_amdgcn_readfirstlane(s_pre[c.b + 1]);
         } while (x >= c.end);
         c.L = __builtin_amdgcn_readfirstlane(s_len[c.b]);
-        c.ks = window_start(c.L, p.window);
+        c.ks = window_start(c.L - qn + 1, p.window);
+        c.ks_last = window_start(c.L, p.window);
         c.ksa = c.ks & ~(kKeys - 1);
         ++c.seg;
     };
@@ -356,8 +372,8 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
     const int bs_mask = (1 << p.bs_log2) - 1;
     const int32_t last_block = (int32_t)(p.num_blocks - 1);
     uint8_t* const qring = smem + S::kQOff;
-    const int q_bytes = G * C::kRowBytes;
-    const int nq = (q_bytes + 1023) / 1024;
+    const int nq = (NC * C::kRowBytes + 1023) / 1024;
+    const uint8_t* const qbase = reinterpret_cast<const uint8_t*>(p.q);
 
     // Issue side.  The block-table entries of a tile (one per wave load; every wave load
     // lies in one block) are read through the scalar cache one tile before its loads.
@@ -378,9 +394,16 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         const int kb = ic.ksa + (x - ic.pre) * kKeys;
         uint8_t* stage = smem + (u % kStg) * C::kStage;
         if (x == ic.pre || u == 0) {  // first tile of a segment: its query rows first
-            const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(p.q) + ((int64_t)ic.b * p.hq + kvh * G) * D * 2;
+            // LDS row c of the slot is column c: query token c / G, head c % G of the kv
+            // head (bytes past the NC rows re-read the last row).
             uint8_t* qdst = qring + (ic.seg % kStg) * S::kQSlot;
-            for (int j = 0; j < nq; ++j) lds_dma16(qsrc + min(j * 1024 + 16 * lane, q_bytes - 16), qdst + j * 1024);
+            for (int j = 0; j < nq; ++j) {
+                const int byte = j * 1024 + 16 * lane;
+                const int c = min(byte / C::kRowBytes, NC - 1);
+                const int ct = c / G;
+                const int64_t qrow = ((int64_t)ic.b * qn + ct) * p.hq + kvh * G + (c - ct * G);
+                lds_dma16(qbase + qrow * C::kRowBytes + (byte & (C::kRowBytes - 1)), qdst + j * 1024);
+            }
         }
         if (x + 1 < ic.end) {         // full tile: SGPR base per wave load, constant lane offsets
 #pragma unroll
@@ -457,8 +480,11 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 feed(t + kStg - 1);
                 const int kb = cc.ksa + (x0 + t - cc.pre) * kKeys;
-                full = kb >= cc.ks && kb + kKeys <= cc.L;
-                tmax = tile_scores<D>(smem + (t % kStg) * C::kStage, qf, n, g, full, kb, cc.ks, cc.L,
+                // every column sees the whole tile: past the last token's window start and
+                // before the first token's end
+                full = kb >= cc.ks_last && kb + kKeys <= cc.L - (qn - 1);
+                tmax = tile_scores<D>(smem + (t % kStg) * C::kStage, qf, n, g, full, kb,
+                                      window_start(cc.L - back, p.window), cc.L - back,
                                       p.scale_log2, sv);
                 if (__any(must_rescale(st, tmax))) break;
                 tile_pv<D>(smem + (t % kStg) * C::kStage, st, full, sv, p.scale_log2, n, g, oacc);
@@ -472,9 +498,9 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         l_tot += __shfl_xor(l_tot, 32, 64);
         if (valid) {
             if (whole) {
-                store_final<D>(p, (int64_t)cc.b * p.hq + kvh * G + n, g, st.m, l_tot, oacc);
+                store_final<D>(p, out_row(cc.b), g, st.m, l_tot, oacc);
             } else {
-                const int64_t ps = ((int64_t)(kvh * P + w) * 2 + slot) * G + n;
+                const int64_t ps = ((int64_t)(kvh * P + w) * 2 + slot) * NC + n;
                 float* o = p.ws_o + ps * D + 4 * g;
 #pragma unroll
                 for (int dt = 0; dt < C::kDTiles; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = oacc[dt];
@@ -510,20 +536,26 @@ __global__ __launch_bounds__(256) void gqa_stream_combine_kernel(DecodeParams p)
     const int wl = range_of(end - 1, T, P);
     if (wf == wl) return;
     const int G = p.group;
+    const int qn = max(p.qn, 1);
+    const int NC = qn * G;            // columns: (query token, head) pairs
     const int np = wl - wf + 1;
     const int first_slot = range_start(wf, T, P) == pre ? 0 : 1;
-    auto part = [&](int j, int n) {   // partial index of part j (range wf + j), head n
-        return ((int64_t)(kvh * P + wf + j) * 2 + (j == 0 ? first_slot : 0)) * G + n;
+    auto part = [&](int j, int n) {   // partial index of part j (range wf + j), column n
+        return ((int64_t)(kvh * P + wf + j) * 2 + (j == 0 ? first_slot : 0)) * NC + n;
     };
-    for (int i = threadIdx.x; i < np * G; i += blockDim.x) {
-        const int j = i / G, n = i % G;
+    auto row_of = [&](int n) {        // output row of column n
+        const int t = n / G;
+        return ((int64_t)b * qn + t) * p.hq + kvh * G + (n - t * G);
+    };
+    for (int i = threadIdx.x; i < np * NC; i += blockDim.x) {
+        const int j = i / NC, n = i % NC;
         const bool empty = range_start(wf + j, T, P) == range_start(wf + j + 1, T, P);
         const int64_t ps = part(j, n);
         s_w[n][j] = empty ? -INFINITY : p.ws_ml[ps * 2];
         s_l[n][j] = empty ? 0.0f : p.ws_ml[ps * 2 + 1];
     }
     __syncthreads();
-    if (threadIdx.x < G) {
+    if (threadIdx.x < NC) {
         const int n = threadIdx.x;
         float M = -INFINITY;
         for (int j = 0; j < np; ++j) M = fmaxf(M, s_w[n][j]);
@@ -534,11 +566,11 @@ __global__ __launch_bounds__(256) void gqa_stream_combine_kernel(DecodeParams p)
             lsum = fmaf(f, s_l[n][j], lsum);
         }
         s_inv[n] = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-        const int64_t row = (int64_t)b * p.hq + kvh * G + n;
+        const int64_t row = row_of(n);
         if (p.lse) p.lse[row] = lsum > 0.0f ? (M + __log2f(lsum)) * kLn2f : -INFINITY;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < G * (D / 4); i += blockDim.x) {
+    for (int i = threadIdx.x; i < NC * (D / 4); i += blockDim.x) {
         const int n = i / (D / 4);
         const int d = (i % (D / 4)) * 4;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -550,7 +582,7 @@ __global__ __launch_bounds__(256) void gqa_stream_combine_kernel(DecodeParams p)
             acc += f * o;
         }
         const float inv = s_inv[n];
-        const int64_t row = (int64_t)b * p.hq + kvh * G + n;
+        const int64_t row = row_of(n);
         const uint32_t w0 = bf16_bits(acc[0] * inv) | ((uint32_t)bf16_bits(acc[1] * inv) << 16);
         const uint32_t w1 = bf16_bits(acc[2] * inv) | ((uint32_t)bf16_bits(acc[3] * inv) << 16);
         *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * D + d) = make_uint2(w0, w1);
@@ -753,6 +785,11 @@ bool gqa_mfma_supported(int dtype, int group) { return dtype == 1 && group >= 4 
 bool gqa_stream_supported(int dtype, int group, int head_dim, int bs_log2, int batch) {
     const int rpi_log2 = head_dim == 128 ? 2 : 3;    // every wave load within one block
     return gqa_mfma_supported(dtype, group) && bs_log2 >= rpi_log2 && batch <= kStreamMaxBatch;
+}
+
+bool gqa_stream_shape_supported(int head_dim, int bs_log2, int batch) {
+    const int rpi_log2 = head_dim == 128 ? 2 : 3;
+    return (head_dim == 64 || head_dim == 128) && bs_log2 >= rpi_log2 && batch <= kStreamMaxBatch;
 }
 
 int gqa_stream_parts(int num_kv_heads) { return num_kv_heads >= kStreamWgs ? 1 : kStreamWgs / num_kv_heads; }

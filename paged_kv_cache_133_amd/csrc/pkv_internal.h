@@ -114,8 +114,11 @@ struct DecodePlan {
     int32_t parts;
     size_t st_o_offset, st_ml_offset, st_pre_offset;
 };
+// qn > 0: the multi-token decode, which always runs the range-streaming kernel with qn
+// query tokens per sequence; 0: decode (that kernel only for bf16 with 4..16 heads per kv head).
 DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t head_dim_v, int32_t max_seq_len_kv, bool byte_rows = false);
+                       int32_t head_dim_v, int32_t max_seq_len_kv, bool byte_rows = false,
+                       int32_t qn = 0);
 
 struct DecodeParams {
     void* out;
@@ -152,12 +155,17 @@ struct DecodeParams {
     // (window_start below); 0 keeps all of them.  Splits and tiles then start at the
     // window start rounded down to a multiple of 32 keys.
     int32_t window;
+    // Query tokens per sequence (range-streaming kernel only; 1 for decode): q, out and lse
+    // rows are [B * qn][Hq]; token i of sequence b sees keys below seq_lens[b] - qn + 1 + i.
+    int32_t qn;
 };
 // dtype: 0 f32, 1 bf16; head_dim 64 or 128.  bf16 with 4..16 query heads per kv head runs
 // on the matrix cores (launch_gqa_decode: the range-streaming kernel when p.parts > 0,
 // else the per-split one), everything else on the vector ALU.
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, hipStream_t s);
 bool gqa_mfma_supported(int dtype, int group);
+// Head dim, block size and batch the range-streaming kernel takes (any column count <= 16).
+bool gqa_stream_shape_supported(int head_dim, int bs_log2, int batch);
 bool gqa_stream_supported(int dtype, int group, int head_dim, int bs_log2, int batch);
 int gqa_stream_parts(int num_kv_heads);
 hipError_t launch_gqa_decode(const DecodeParams& p, int head_dim, hipStream_t s);

@@ -54,6 +54,7 @@ class Workload:
     description: str = ""
     window: int = 0           # sliding window (keys each query row sees; 0: all)
     kv_dtype: str = ""        # "int8": the cache holds int8 codes + fp32 row scales
+    q_tokens: int = 0         # > 0: every sequence has this many causal query tokens (MTP)
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -97,7 +98,7 @@ MTP_DECODE = Workload("mtp_decode_bf16", "varlen", 32, 32, 8, 128, 128, 0, 16, "
                       1.0 / math.sqrt(128.0), 129,
                       "MTP decode (next_n = 1): B=32, 2 causal query tokens per sequence, "
                       "32 q / 8 kv heads, head_dim 128, bs 16, kv lengths U{512..2048} before "
-                      "the step, bf16")
+                      "the step, bf16", q_tokens=2)
 
 # The headline shape over an INT8 cache (the same lengths as the bf16 headline).
 LLAMA7B_INT8 = Workload("llama7b_mha_int8", "decode", 32, 32, 32, 128, 128, 0, 16, "bf16",

@@ -350,3 +350,36 @@ def test_runner_rejects_bad_arguments():
     assert lib.pkv_runner_launch(None, None) == -1
     assert not lib.pkv_runner_graph(None, 0)
     assert not lib.pkv_runner_host_buffer(None)
+
+
+def test_decode_mtp_rejects():
+    lib = _lib().lib()
+
+    def mtp(**kw):
+        a = dict(out=FAKE, lse=None, q=FAKE, k=FAKE, v=FAKE, table=FAKE, lens=FAKE, B=4, qn=2,
+                 mbs=64, maxlen=1024, hq=32, hkv=8, d=128, bs=16, nb=256, scale=0.088, dtype=1,
+                 window=0, stages=3, ws=FAKE, wsb=1 << 30, stream=None)
+        a.update(kw)
+        return lib.pkv_paged_attn_decode_mtp(a["out"], a["lse"], a["q"], a["k"], a["v"], a["table"],
+                                             a["lens"], a["B"], a["qn"], a["mbs"], a["maxlen"], a["hq"],
+                                             a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["dtype"],
+                                             a["window"], a["stages"], a["ws"], a["wsb"], a["stream"])
+    assert mtp(stages=0) == -2
+    assert mtp(qn=0) == -2
+    assert mtp(hq=30) == -2
+    assert mtp(dtype=0) == -4                 # fp32: varlen covers it
+    assert mtp(dtype=7) == -3
+    assert mtp(qn=5) == -4                    # 20 columns
+    assert mtp(bs=2) == -4                    # below one wave load of rows
+    assert mtp(d=96) == -4
+    assert mtp(B=2000) == -4
+    assert mtp(bs=24) == -4
+    assert mtp(window=-1) == -2
+    assert mtp(scale=0.0) == -6
+    assert mtp(out=None) == -1
+    assert mtp(ws=FAKE, wsb=16) == -7
+    assert mtp(maxlen=2000) == -2             # > mbs * bs
+    need = lib.pkv_decode_mtp_workspace_size(4, 2, 32, 8, 128, 1024)
+    assert need > lib.pkv_decode_mtp_workspace_size(4, 1, 32, 8, 128, 1024) > 0
+    assert lib.pkv_decode_mtp_workspace_size(4, 0, 32, 8, 128, 1024) == 0
+    assert mtp(wsb=need - 1) == -7
