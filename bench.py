@@ -430,7 +430,8 @@ def main():
         # The INT8 pools: every row of the bf16 pool quantized by the library's writer.
         nbs = case.num_blocks * w.block_size
         pool_i8 = {n: torch.empty(case.cache_k.shape, dtype=torch.int8, device=dev) for n in ("k", "v")}
-        pool_sc = {n: torch.empty(case.cache_k.shape[:3], dtype=torch.float32, device=dev)
+        nb_, bs_, hkv_ = case.cache_k.shape[:3]
+        pool_sc = {n: torch.empty((nb_, hkv_, bs_), dtype=torch.float32, device=dev)
                    for n in ("k", "v")}
         pkv.kv_cache_write_int8(case.cache_k.reshape(nbs, w.num_kv_heads, w.head_dim),
                                 case.cache_v.reshape(nbs, w.num_kv_heads, w.head_dim_v),

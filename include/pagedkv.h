@@ -136,7 +136,9 @@ PKV_API int pkv_kv_cache_append(const void* k_new, const void* v_new, void* k_ca
  *   s = max|x| / 127,  q = round_half_even(x / s) clamped to [-127, 127]  (IEEE fp32 divisions;
  *   a zero row has s = 0 and zero codes),  x ~ q * s.
  * Caches: codes k_cache, v_cache [num_blocks][block_size][num_kv_heads][head_dim] int8 and
- * scales k_scale, v_scale [num_blocks][block_size][num_kv_heads] fp32.
+ * scales k_scale, v_scale [num_blocks][num_kv_heads][block_size] fp32: the scale of slot
+ * (block P, offset o) and kv head h is at (P * num_kv_heads + h) * block_size + o, so a
+ * block's scales of one head are adjacent (the decode reads a run of tokens' scales at once).
  *
  * pkv_kv_cache_write_int8: quantize k_new, v_new [num_tokens][num_kv_heads][head_dim]
  * (dtype f32 or bf16) row by row and store codes and scales at slot_mapping[t] (int64;

@@ -255,13 +255,21 @@ def kv_rmsnorm_rope_cache(kv: torch.Tensor, gamma: torch.Tensor, cos: torch.Tens
                                            _dtype_code(kv), _stream(kv.device)))
 
 
+def _scale_shape(k_scale, v_scale, nb, hkv, bs):
+    for s in (k_scale, v_scale):
+        if tuple(s.shape) != (nb, hkv, bs) or s.dtype != torch.float32:
+            raise ValueError(f"INT8 scale arrays are float32 [num_blocks, num_kv_heads, "
+                             f"block_size] = {(nb, hkv, bs)}, got {tuple(s.shape)} {s.dtype}")
+
+
 def kv_cache_write_int8(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
                         v_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
                         slot_mapping: torch.Tensor):
     """Quantize and write one step's K/V rows into the INT8 cache (see
-    pkv_kv_cache_write_int8).  Caches [nb, bs, Hkv, D] int8, scales [nb, bs, Hkv] fp32."""
+    pkv_kv_cache_write_int8).  Caches [nb, bs, Hkv, D] int8, scales [nb, Hkv, bs] fp32."""
     _dev(k_new, v_new, k_cache, v_cache, k_scale, v_scale, slot_mapping)
     nb, bs, hkv, d = k_cache.shape
+    _scale_shape(k_scale, v_scale, nb, hkv, bs)
     _check(lib().pkv_kv_cache_write_int8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                          _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping),
                                          slot_mapping.shape[0], hkv, d, bs, nb, _dtype_code(k_new),
@@ -273,6 +281,7 @@ def _decode_int8_args(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_le
     _dev(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens_kv, out, lse, workspace)
     B, hq, d = q.shape
     nb, bs, hkv, _ = k_cache.shape
+    _scale_shape(k_scale, v_scale, nb, hkv, bs)
     if out is None:
         out = torch.empty((B, hq, d), dtype=q.dtype, device=q.device)
     if workspace is None:

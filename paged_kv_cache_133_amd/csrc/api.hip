@@ -737,6 +737,7 @@ int pkv_kv_cache_write_int8(const void* k_new, const void* v_new, void* k_cache,
     p.num_tokens = num_tokens;
     p.num_slots = num_blocks * block_size;
     p.hkv = num_kv_heads;
+    p.bs_log2 = log2i(block_size);
     return hip_status(pkv::launch_kv_write_int8(p, dtype, head_dim, (hipStream_t)stream),
                       "kv_cache_write_int8 launch");
 }

@@ -4,7 +4,8 @@
 // not the scheme.  The one taken: symmetric int8 codes with one fp32 scale per (token, kv
 // head) row, s = max|x| / 127 and q = round_half_even(x / s) (IEEE fp32 divisions; a zero
 // row has s = 0 and zero codes).  The caches hold the codes [nb][bs][Hkv][D] int8 and the
-// scales [nb][bs][Hkv] fp32, one pair for K and one for V.
+// scales [nb][Hkv][bs] fp32 (a block's scales of one head side by side), one pair for K
+// and one for V.
 //
 // Decode is bound by HBM bytes, and int8 rows are half the bf16 bytes (plus 4 bytes of
 // scale per row): the same split-KV schedule as decode_split_kernel on the vector ALU.
@@ -14,10 +15,10 @@
 //    query; the row's K scale multiplies the finished dot product;
 //  * V codes are widened once per token and shared by the group's heads; the row's V scale
 //    is folded into the softmax weight: o += (p s_v) q_v, l += p;
-//  * the 64 scales of a 32-token step (K and V) come in one 4-byte-per-lane load and reach
-//    the lanes of each token through LDS, each row of lanes taking consecutive tokens so
-//    that it reads its scales in one access (a scale load per token row cost a sixth of the
-//    kernel's time, shuffles per token most of that);
+//  * each row of lanes takes NJ consecutive tokens of a step, so with blocks of at least NJ
+//    tokens their K (V) scales are NJ adjacent floats of one block and head: one load per
+//    row, issued with the code loads (scales laid out per (token, head) cost a sixth of
+//    the kernel's time: every token's scale was a separate access);
 //  * splits are twice as long as for bf16 rows, for the same bytes per workgroup.
 // Keys below the window start are not loaded; the new token is written beforehand by the
 // quantizing write (the attention reads the same codes later steps will).
@@ -75,6 +76,7 @@ __global__ __launch_bounds__(256) void kv_write_int8_kernel(QuantWriteParams p) 
 #pragma unroll
     for (int s = 1; s < kLpr; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 64));
     if (!live || slot < 0 || slot >= p.num_slots) return;
+    const int64_t sc_idx = (((slot >> p.bs_log2) * p.hkv + h) << p.bs_log2) | (slot & ((1 << p.bs_log2) - 1));
     const float sc = __fdiv_rn(amax, 127.0f);
     uint32_t w[2] = {0u, 0u};
     if (sc > 0.0f) {
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void kv_write_int8_kernel(QuantWriteParams p) 
     }
     uint8_t* dst = reinterpret_cast<uint8_t*>(which ? p.v_cache : p.k_cache) + (slot * p.hkv + h) * D + c * 8;
     *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-    if (c == 0) (which ? p.v_scale : p.k_scale)[slot * p.hkv + h] = sc;
+    if (c == 0) (which ? p.v_scale : p.k_scale)[sc_idx] = sc;
 }
 
 // ------------------------------------------------------------------ int8 decode
@@ -96,10 +98,10 @@ __global__ __launch_bounds__(256) void decode_int8_kernel(DecodeParams p) {
     constexpr int LPT = D / EPL;                      // lanes per token row
     constexpr int TPW = 64 / LPT;                     // tokens per wave load
     constexpr int NJ = kStepTokensI8 / TPW;           // loads per step (each of K, V)
+    static_assert(NJ == 2 || NJ == 4, "a row of lanes takes 2 or 4 tokens per step");
     __shared__ float sm_m[kWavesI8][GP];
     __shared__ float sm_l[kWavesI8][GP];
     __shared__ float sm_o[kWavesI8][GP][D];
-    __shared__ __attribute__((aligned(16))) float sm_sc[kWavesI8][2 * kStepTokensI8];   // a step's K, V scales
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -171,20 +173,10 @@ __global__ __launch_bounds__(256) void decode_int8_kernel(DecodeParams p) {
     for (int base = w0; base < w1; base += kStepTokensI8) {
         const int32_t tbl_next = load_table(base + kStepTokensI8);
         const int blk0 = base >> p.bs_log2;
-        // Scales of the step's 32 tokens in one load (lane i < 32: the K scale of token
-        // base + i; lane 32 + i: its V scale), through this wave's LDS slots to the lanes of
-        // row r, which take tokens NJ r .. NJ r + NJ - 1 and read their NJ scales at once.
-        {
-            const int tk = base + (lane & 31);
-            int32_t phys = __shfl(tbl, (tk >> p.bs_log2) - blk0, 64);
-            phys = min(max(phys, 0), last_block);
-            const int64_t slot = ((int64_t)phys << p.bs_log2) | (tk & bs_mask);
-            const float* sp = lane < 32 ? p.k_scale : p.v_scale;
-            sm_sc[wave][lane] = (tk >= ks && tk < w1) ? sp[slot * p.hkv + kvh] : 0.0f;
-        }
         u32x4 kr[NJ], vr[NJ];
         float ksc[NJ], vsc[NJ];
         bool valid[NJ];
+        int64_t sbase[NJ];            // scale index of each token: ((block, head), offset)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int tok = base + row * NJ + j;
@@ -192,6 +184,7 @@ __global__ __launch_bounds__(256) void decode_int8_kernel(DecodeParams p) {
             int32_t phys = __shfl(tbl, (tok >> p.bs_log2) - blk0, 64);
             phys = min(max(phys, 0), last_block);
             const int64_t slot = ((int64_t)phys << p.bs_log2) | (tok & bs_mask);
+            sbase[j] = (((int64_t)phys * p.hkv + kvh) << p.bs_log2) | (tok & bs_mask);
             kr[j] = u32x4{0u, 0u, 0u, 0u};
             vr[j] = u32x4{0u, 0u, 0u, 0u};
             if (valid[j]) {
@@ -199,19 +192,32 @@ __global__ __launch_bounds__(256) void decode_int8_kernel(DecodeParams p) {
                 vr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + slot * slot_stride));
             }
         }
-        // The row's NJ consecutive K and V scales (written by this wave above; LDS accesses
-        // of one wave complete in order).
-        if constexpr (NJ == 4) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(&sm_sc[wave][row * NJ]);
-            const f32x4 c = *reinterpret_cast<const f32x4*>(&sm_sc[wave][kStepTokensI8 + row * NJ]);
+        // The row's NJ consecutive K and V scales: one aligned load each when a block holds
+        // at least NJ tokens (the row's first token is a multiple of NJ), else per token.
+        // Tokens outside [ks, w1) get scale 0 (their rows are zero and their weights 0).
+        if ((1 << p.bs_log2) >= NJ) {
+            if constexpr (NJ == 4) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(p.k_scale + sbase[0]);
+                const f32x4 c = *reinterpret_cast<const f32x4*>(p.v_scale + sbase[0]);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) { ksc[j] = a[j]; vsc[j] = c[j]; }
+                for (int j = 0; j < NJ; ++j) { ksc[j] = a[j]; vsc[j] = c[j]; }
+            } else {
+                const float2 a = *reinterpret_cast<const float2*>(p.k_scale + sbase[0]);
+                const float2 c = *reinterpret_cast<const float2*>(p.v_scale + sbase[0]);
+                ksc[0] = a.x; ksc[1] = a.y;
+                vsc[0] = c.x; vsc[1] = c.y;
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                ksc[j] = sm_sc[wave][row * NJ + j];
-                vsc[j] = sm_sc[wave][kStepTokensI8 + row * NJ + j];
+                ksc[j] = p.k_scale[sbase[j]];
+                vsc[j] = p.v_scale[sbase[j]];
             }
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            ksc[j] = valid[j] ? ksc[j] : 0.0f;
+            vsc[j] = valid[j] ? vsc[j] : 0.0f;
         }
         // K codes as bf16 pairs; V codes widened once for all heads of the group.
         uint32_t kb[NJ][8];

@@ -70,11 +70,12 @@ struct QuantWriteParams {
     const void* v_new;
     int8_t* k_cache;         // [nb * bs][Hkv][D]
     int8_t* v_cache;
-    float* k_scale;          // [nb * bs][Hkv]
+    float* k_scale;          // [nb][Hkv][bs]: a block's scales of one head are contiguous
     float* v_scale;
     const int64_t* slots;
     int64_t num_tokens, num_slots;
     int32_t hkv;
+    int32_t bs_log2;
 };
 hipError_t launch_kv_write_int8(const QuantWriteParams& p, int in_dtype, int head_dim, hipStream_t s);
 

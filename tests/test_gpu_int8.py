@@ -33,8 +33,8 @@ def test_int8_write_bit_exact(dtype, hkv, d, bs):
     slots[12] = nb * bs
     kc = torch.randint(-128, 128, (nb, bs, hkv, d), generator=g, dtype=torch.int8)
     vc = torch.randint(-128, 128, (nb, bs, hkv, d), generator=g, dtype=torch.int8)
-    ks = torch.randn(nb, bs, hkv, generator=g)
-    vs = torch.randn(nb, bs, hkv, generator=g)
+    ks = torch.randn(nb, hkv, bs, generator=g)     # [block][kv head][offset]
+    vs = torch.randn(nb, hkv, bs, generator=g)
     say(f"int8 write {dtype} hkv={hkv} d={d} bs={bs}")
     dk, dv, dks, dvs = kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV)
     pkv.kv_cache_write_int8(k_new.to(DEV), v_new.to(DEV), dk, dv, dks, dvs, slots.to(DEV))
@@ -44,11 +44,12 @@ def test_int8_write_bit_exact(dtype, hkv, d, bs):
     for new, cache, scale, gc, gs in ((k_new, kc, ks, dk, dks), (v_new, vc, vs, dv, dvs)):
         q, s = oracle.quantize_rows(host(new))                     # [T, hkv, d], [T, hkv]
         exp_c = cache.numpy().reshape(nb * bs, hkv, d).copy()
-        exp_s = scale.numpy().reshape(nb * bs, hkv).copy()
+        exp_s = scale.permute(0, 2, 1).numpy().reshape(nb * bs, hkv).copy()   # per slot
         exp_c[sl] = q[ok]
         exp_s[sl] = s[ok]
         assert np.array_equal(gc.cpu().numpy().reshape(nb * bs, hkv, d), exp_c)
-        assert np.array_equal(gs.cpu().numpy().reshape(nb * bs, hkv).view(np.uint32), exp_s.view(np.uint32))
+        got_s = gs.cpu().permute(0, 2, 1).contiguous().numpy().reshape(nb * bs, hkv)
+        assert np.array_equal(got_s.view(np.uint32), exp_s.view(np.uint32))
 
 
 def _int8_case(Hq, Hkv, D, bs, L, seed):
@@ -60,8 +61,10 @@ def _int8_case(Hq, Hkv, D, bs, L, seed):
     nb = c.num_blocks
     kq, ksc = oracle.quantize_rows(host(c.cache_k))
     vq, vsc = oracle.quantize_rows(host(c.cache_v))
+    # scales per (slot, kv head) from the oracle, stored [block][kv head][offset]
     dev = {"kc": torch.from_numpy(kq).to(DEV), "vc": torch.from_numpy(vq).to(DEV),
-           "ks": torch.from_numpy(ksc).to(DEV), "vs": torch.from_numpy(vsc).to(DEV)}
+           "ks": torch.from_numpy(ksc).permute(0, 2, 1).contiguous().to(DEV),
+           "vs": torch.from_numpy(vsc).permute(0, 2, 1).contiguous().to(DEV)}
     table = c.table_tensor(DEV)
     slots = pkv.slot_mapping(table, c.lens_before_tensor(DEV), c.cu_q_tensor(DEV), bs, c.num_tokens)
     pkv.kv_cache_write_int8(c.new_k, c.new_v, dev["kc"], dev["vc"], dev["ks"], dev["vs"], slots)
@@ -79,7 +82,8 @@ def _int8_case(Hq, Hkv, D, bs, L, seed):
     vsc = vsc.reshape(nb * bs, Hkv)
     vsc[sl] = ns
     assert np.array_equal(dev["kc"].cpu().numpy().reshape(nb * bs, Hkv, D), kq)
-    assert np.array_equal(dev["vs"].cpu().numpy().reshape(nb * bs, Hkv), vsc)
+    assert np.array_equal(dev["vs"].cpu().permute(0, 2, 1).contiguous().numpy().reshape(nb * bs, Hkv), vsc)
+    assert np.array_equal(dev["ks"].cpu().permute(0, 2, 1).contiguous().numpy().reshape(nb * bs, Hkv), ksc)
     kdeq = oracle.dequantize_rows(kq, ksc).reshape(nb, bs, Hkv, D)
     vdeq = oracle.dequantize_rows(vq, vsc).reshape(nb, bs, Hkv, D)
     return c, dev, table, kdeq, vdeq

@@ -142,7 +142,8 @@ def test_padding_rows_int8():
     q = torch.randn(B, hq, d, generator=g).to(torch.bfloat16)
     say("padding rows int8")
     lse = torch.full((B, hq), 7.0, dtype=torch.float32, device=DEV)
-    out, _ = pkv.paged_attn_decode_int8(q.to(DEV), kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV),
+    blockwise = lambda s: s.permute(0, 2, 1).contiguous().to(DEV)   # [block][kv head][offset]  # noqa: E731
+    out, _ = pkv.paged_attn_decode_int8(q.to(DEV), kc.to(DEV), vc.to(DEV), blockwise(ks), blockwise(vs),
                                         table.to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV),
                                         mbs * bs, d ** -0.5, lse=lse)
     torch.cuda.synchronize()
