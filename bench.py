@@ -152,7 +152,12 @@ def algorithmic_bytes(case):
     e = w.elem_bytes
     Lp = visible_keys(case)[0]                     # keys some row of the sequence sees
     B, T = w.batch, case.num_tokens
-    if w.mode == "mla":
+    if w.mode == "mla" and w.kv_dtype == "int8":
+        row = w.head_dim + w.head_dim_rope + 8      # nope and rope codes + their two scales
+        kv = int(Lp.sum()) * row
+        # the quantizing writer reads the new rows in the query dtype, writes codes and scales
+        new_rows = (T * (w.head_dim + w.head_dim_rope) * e + T * row) // 2
+    elif w.mode == "mla":
         row = w.head_dim + w.head_dim_rope          # nope read once (key and value) + rope
         new_rows = T * (w.head_dim + w.head_dim_rope) * e
         kv = int(Lp.sum()) * row * e
@@ -207,15 +212,25 @@ def cpu_baseline(case, kv_bytes, min_seconds):
          "new_k": host(c.new_k), "new_v": host(c.new_v), "new_rope": host(c.new_rope),
          "block_size": c.w.block_size, "num_blocks": c.num_blocks, "scale": c.w.scale}
     int8 = c.w.kv_dtype == "int8"
+    mla = c.w.mode == "mla"
     if int8:
         # the oracle's own quantization of the pools (outside the timed step)
         pk, sk = oracle.quantize_rows(h["cache_k"])
-        pv, sv = oracle.quantize_rows(h["cache_v"])
+        pv, sv = oracle.quantize_rows(h["cache_rope" if mla else "cache_v"])
 
     def int8_step():
         # slot_mapping, quantize and write the new rows, attend over the dequantized pools
         slots = oracle.slot_mapping(h["block_table"], h["lens_before"], h["cu_q"],
                                     h["block_size"], h["num_blocks"])
+        if mla:   # nope (key and value) and rope, each with its own scales
+            deq = []
+            for pool, scale, new in ((pk, sk, h["new_k"]), (pv, sv, h["new_rope"])):
+                qn, sn = oracle.quantize_rows(new)
+                deq.append(oracle.dequantize_rows(oracle.kv_write(pool, qn, slots),
+                                                  oracle.kv_write(scale, sn, slots)))
+            return oracle.paged_attention(oracle.widen(h["q"]), deq[0], deq[0], h["block_table"],
+                                          h["cu_q"], h["lens_after"], h["scale"], False,
+                                          q_rope=oracle.widen(h["q_rope"]), k_rope=deq[1])
         caches = []
         for pool, scale, new in ((pk, sk, h["new_k"]), (pv, sv, h["new_v"])):
             qn, sn = oracle.quantize_rows(new)
@@ -247,6 +262,9 @@ def cpu_baseline(case, kv_bytes, min_seconds):
 
 def step_description(w, path):
     """What one timed step launches, for the JSON line."""
+    if int8_workload(w) and w.mode == "mla":
+        return ("slot_mapping, kv_cache_write_int8_mla (quantizing write of nope and rope), "
+                "decode_mla_int8 split pass, combine")
     if int8_workload(w):
         return ("slot_mapping, kv_cache_write_int8 (quantizing write), decode_int8 split pass, "
                 "combine")
@@ -426,7 +444,18 @@ def main():
     case = wl.make_workload_case(w, seed=args.seed, device=dev)
     kv_bytes, split_bytes, step_bytes = algorithmic_bytes(case)
     int8 = w.kv_dtype == "int8"
-    if int8:
+    if int8 and w.mode == "mla":
+        # The INT8 latent pools: nope and rope rows of the bf16 pools quantized by the writer.
+        nbs = case.num_blocks * w.block_size
+        nb_, bs_ = case.cache_k.shape[:2]
+        pool_i8 = {"k": torch.empty((nb_, bs_, 512), dtype=torch.int8, device=dev),
+                   "v": torch.empty((nb_, bs_, 64), dtype=torch.int8, device=dev)}
+        pool_sc = {n: torch.empty((nb_, bs_), dtype=torch.float32, device=dev) for n in ("k", "v")}
+        pkv.kv_cache_write_int8_mla(case.cache_k.reshape(nbs, 512), case.cache_rope.reshape(nbs, 64),
+                                    pool_i8["k"], pool_i8["v"], pool_sc["k"], pool_sc["v"],
+                                    torch.arange(nbs, dtype=torch.int64, device=dev))
+        pool_bytes = sum(t.numel() * t.element_size() for t in (*pool_i8.values(), *pool_sc.values()))
+    elif int8:
         # The INT8 pools: every row of the bf16 pool quantized by the library's writer.
         nbs = case.num_blocks * w.block_size
         pool_i8 = {n: torch.empty(case.cache_k.shape, dtype=torch.int8, device=dev) for n in ("k", "v")}
@@ -467,6 +496,17 @@ def main():
     reps = []
     slot_first = args.path == "separate" or int8
     for r in range(R):
+        if int8 and mla:
+            nc, rc, ns, rs = (pool_i8["k"], pool_i8["v"], pool_sc["k"], pool_sc["v"]) if r == 0 else (
+                pool_i8["k"].clone(), pool_i8["v"].clone(), pool_sc["k"].clone(), pool_sc["v"].clone())
+            write = _lib.prepare_kv_cache_write_int8_mla(case.new_k.reshape(T, 512),
+                                                         case.new_rope.reshape(T, 64), nc, rc, ns,
+                                                         rs, slots)
+            split, combine, _ = _lib.prepare_decode_mla_int8(case.q, case.q_rope, nc, rc, ns, rs,
+                                                             table, la, case.max_len_after, w.scale,
+                                                             out=out, lse=lse, workspace=ws)
+            reps.append((write, split, combine))
+            continue
         if int8:
             ki8, vi8, ksc, vsc = (pool_i8["k"], pool_i8["v"], pool_sc["k"], pool_sc["v"]) if r == 0 else (
                 pool_i8["k"].clone(), pool_i8["v"].clone(), pool_sc["k"].clone(), pool_sc["v"].clone())

@@ -168,6 +168,36 @@ PKV_API int pkv_paged_attn_decode_int8(void* out, float* lse_out, const void* q,
                                size_t workspace_bytes, void* stream);
 
 /*
+ * INT8 MLA latent cache: the 512-wide nope row and the 64-wide rope row of each token are
+ * quantized separately by the scheme above (one fp32 scale each per token):
+ *   nope_codes [num_blocks][block_size][512] int8, rope_codes [num_blocks][block_size][64]
+ *   int8, nope_scale and rope_scale [num_blocks][block_size] fp32 (one kv head: slot order).
+ * pkv_kv_cache_write_int8_mla: quantize kv_nope [num_tokens][512] and k_rope
+ * [num_tokens][64] (f32 or bf16) into them at slot_mapping (slots outside the pool are
+ * skipped); all arrays 16-byte aligned.
+ * pkv_paged_attn_decode_mla_int8: the MLA-absorbed decode of pkv_paged_attn_decode over
+ * these caches: score = scale * (s_nope * (q . codes_nope) + s_rope * (q_rope . codes_rope)),
+ * out = sum softmax * s_nope * codes_nope; bf16 q, q_rope and out; block_size >= 4 (a power
+ * of two); num_q_heads, workspace (pkv_decode_workspace_size with 1 kv head and head_dim_v
+ * 512), stages and preconditions as for the MLA form of pkv_paged_attn_decode /
+ * pkv_paged_attn_decode_split / _combine (stages 1, 2, 3).
+ */
+PKV_API int pkv_kv_cache_write_int8_mla(const void* kv_nope, const void* k_rope, void* nope_codes,
+                                        void* rope_codes, float* nope_scale, float* rope_scale,
+                                        const int64_t* slot_mapping, int64_t num_tokens,
+                                        int32_t block_size, int64_t num_blocks, int32_t dtype,
+                                        void* stream);
+PKV_API int pkv_paged_attn_decode_mla_int8(void* out, float* lse_out, const void* q, const void* q_rope,
+                                           const void* nope_codes, const void* rope_codes,
+                                           const float* nope_scale, const float* rope_scale,
+                                           const int32_t* block_table, const int32_t* seq_lens_kv,
+                                           int32_t batch, int32_t max_blocks_per_seq,
+                                           int32_t max_seq_len_kv, int32_t num_q_heads,
+                                           int32_t block_size, int64_t num_blocks,
+                                           float softmax_scale, int32_t stages, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
+/*
  * The MLA latent row normalised, rotated and written in one launch: the fused writer the
  * pages place in front of the MLA cache (npu_kv_rmsnorm_rope_cache, keyed by slot_mapping;
  * "KVCache Optimization Skill", Mode 3 and its cache-write fusion note), which they name

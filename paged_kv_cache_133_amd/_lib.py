@@ -34,7 +34,8 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_graph_begin", "pkv_graph_end", "pkv_graph_launch", "pkv_graph_destroy",
            "pkv_runner_create", "pkv_runner_destroy", "pkv_runner_capture_begin",
            "pkv_runner_capture_end", "pkv_runner_graph", "pkv_runner_host_buffer",
-           "pkv_runner_launch", "pkv_decode_mtp_workspace_size", "pkv_paged_attn_decode_mtp")
+           "pkv_runner_launch", "pkv_decode_mtp_workspace_size", "pkv_paged_attn_decode_mtp",
+           "pkv_kv_cache_write_int8_mla", "pkv_paged_attn_decode_mla_int8")
 
 
 class PagedKVError(RuntimeError):
@@ -128,6 +129,11 @@ def lib() -> ctypes.CDLL:
     L.pkv_graph_launch.argtypes = [p, p]
     L.pkv_graph_destroy.restype = ctypes.c_int
     L.pkv_graph_destroy.argtypes = [p]
+    L.pkv_kv_cache_write_int8_mla.restype = ctypes.c_int
+    L.pkv_kv_cache_write_int8_mla.argtypes = [p, p, p, p, p, p, p, i64, i32, i64, i32, p]
+    L.pkv_paged_attn_decode_mla_int8.restype = ctypes.c_int
+    L.pkv_paged_attn_decode_mla_int8.argtypes = [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
+                                                 i32, i64, f32, i32, p, sz, p]
     L.pkv_decode_mtp_workspace_size.restype = sz
     L.pkv_decode_mtp_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     L.pkv_paged_attn_decode_mtp.restype = ctypes.c_int
@@ -167,6 +173,16 @@ def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return PKV_BF16
     raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _batch_rows(B, block_table, seq_lens_kv, q_rope=None):
+    """Host-side guard: one table row and one length per sequence (the library cannot see
+    device array sizes; a mismatch would read past a tensor's end)."""
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens_kv.shape[0] != B:
+        raise ValueError(f"block_table {tuple(block_table.shape)} and seq_lens_kv "
+                         f"{tuple(seq_lens_kv.shape)} need one row per sequence (batch {B})")
+    if q_rope is not None and q_rope.shape[0] != B:
+        raise ValueError(f"q_rope has {q_rope.shape[0]} rows, expected {B}")
 
 
 def _dev(*ts):
@@ -280,6 +296,7 @@ def _decode_int8_args(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_le
                       max_seq_len_kv, softmax_scale, stages, out, lse, workspace, window):
     _dev(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens_kv, out, lse, workspace)
     B, hq, d = q.shape
+    _batch_rows(B, block_table, seq_lens_kv)
     nb, bs, hkv, _ = k_cache.shape
     _scale_shape(k_scale, v_scale, nb, hkv, bs)
     if out is None:
@@ -344,6 +361,7 @@ def _decode_args(q, k_cache, v_cache, block_table, seq_lens_kv, max_seq_len_kv, 
                  q_rope, k_rope_cache, out, lse, workspace):
     _dev(q, k_cache, v_cache, block_table, seq_lens_kv, q_rope, k_rope_cache, out, lse, workspace)
     B, hq, dqk = q.shape
+    _batch_rows(B, block_table, seq_lens_kv, q_rope)
     nb, bs, hkv, _ = k_cache.shape
     dv = v_cache.shape[-1]
     dr = q_rope.shape[-1] if q_rope is not None else 0
@@ -415,6 +433,7 @@ def _decode_append_args(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens
     _dev(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv, out, lse, workspace,
          slots_out)
     B, hq, d = q.shape
+    _batch_rows(B, block_table, seq_lens_kv)
     nb, bs, hkv, _ = k_cache.shape
     if out is None:
         out = torch.empty((B, hq, d), dtype=q.dtype, device=q.device)
@@ -475,12 +494,93 @@ def prepare_kv_cache_write(k_new, v_new, k_cache, v_cache, slots):
     return PreparedCall(lib().pkv_kv_cache_write, args, (k_new, v_new, k_cache, v_cache, slots))
 
 
+def kv_cache_write_int8_mla(kv_nope, k_rope, nope_codes, rope_codes, nope_scale, rope_scale,
+                            slot_mapping):
+    """Quantize and write MLA latent rows into the INT8 latent cache
+    (pkv_kv_cache_write_int8_mla): codes [nb, bs, 512] / [nb, bs, 64] int8, scales [nb, bs]."""
+    _dev(kv_nope, k_rope, nope_codes, rope_codes, nope_scale, rope_scale, slot_mapping)
+    nb, bs = nope_codes.shape[0], nope_codes.shape[1]
+    _mla_int8_shapes(nope_codes, rope_codes, nope_scale, rope_scale)
+    _check(lib().pkv_kv_cache_write_int8_mla(_ptr(kv_nope), _ptr(k_rope), _ptr(nope_codes),
+                                             _ptr(rope_codes), _ptr(nope_scale), _ptr(rope_scale),
+                                             _ptr(slot_mapping), slot_mapping.shape[0], bs, nb,
+                                             _dtype_code(kv_nope), _stream(kv_nope.device)))
+
+
+def _mla_int8_shapes(nope_codes, rope_codes, nope_scale, rope_scale):
+    nb, bs = nope_codes.shape[0], nope_codes.shape[1]
+    want = ((nope_codes, (nb, bs, 512), torch.int8), (rope_codes, (nb, bs, 64), torch.int8),
+            (nope_scale, (nb, bs), torch.float32), (rope_scale, (nb, bs), torch.float32))
+    for t, shape, dt in want:
+        if tuple(t.shape) != shape or t.dtype != dt:
+            raise ValueError(f"INT8 MLA cache arrays: expected {shape} {dt}, got {tuple(t.shape)} {t.dtype}")
+
+
+def _decode_mla_int8_args(q, q_rope, nope_codes, rope_codes, nope_scale, rope_scale, block_table,
+                          seq_lens_kv, max_seq_len_kv, softmax_scale, stages, out, lse, workspace):
+    _dev(q, q_rope, nope_codes, rope_codes, nope_scale, rope_scale, block_table, seq_lens_kv, out,
+         lse, workspace)
+    _mla_int8_shapes(nope_codes, rope_codes, nope_scale, rope_scale)
+    B, hq, _ = q.shape
+    _batch_rows(B, block_table, seq_lens_kv)
+    nb, bs = nope_codes.shape[0], nope_codes.shape[1]
+    if out is None:
+        out = torch.empty((B, hq, 512), dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = new_decode_workspace(B, hq, 1, 512, max_seq_len_kv, q.device)
+    args = (_ptr(out), _ptr(lse), _ptr(q), _ptr(q_rope), _ptr(nope_codes), _ptr(rope_codes),
+            _ptr(nope_scale), _ptr(rope_scale), _ptr(block_table), _ptr(seq_lens_kv), B,
+            block_table.shape[1], max_seq_len_kv, hq, bs, nb, float(softmax_scale), stages,
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device))
+    return args, out, workspace
+
+
+def paged_attn_decode_mla_int8(q, q_rope, nope_codes, rope_codes, nope_scale, rope_scale,
+                               block_table, seq_lens_kv, max_seq_len_kv, softmax_scale, out=None,
+                               lse=None, workspace=None):
+    """MLA-absorbed decode over the INT8 latent cache (pkv_paged_attn_decode_mla_int8)."""
+    args, out, _ = _decode_mla_int8_args(q, q_rope, nope_codes, rope_codes, nope_scale, rope_scale,
+                                         block_table, seq_lens_kv, max_seq_len_kv, softmax_scale,
+                                         3, out, lse, workspace)
+    _check(lib().pkv_paged_attn_decode_mla_int8(*args))
+    return out, lse
+
+
+def prepare_decode_mla_int8(q, q_rope, nope_codes, rope_codes, nope_scale, rope_scale, block_table,
+                            seq_lens_kv, max_seq_len_kv, softmax_scale, out=None, lse=None,
+                            workspace=None):
+    """(split pass, combine pass) prepared calls of pkv_paged_attn_decode_mla_int8."""
+    calls = []
+    for stages in (1, 2):
+        args, out, workspace = _decode_mla_int8_args(q, q_rope, nope_codes, rope_codes, nope_scale,
+                                                     rope_scale, block_table, seq_lens_kv,
+                                                     max_seq_len_kv, softmax_scale, stages, out,
+                                                     lse, workspace)
+        calls.append(PreparedCall(lib().pkv_paged_attn_decode_mla_int8, args,
+                                  (q, q_rope, nope_codes, rope_codes, nope_scale, rope_scale,
+                                   block_table, seq_lens_kv, out, lse, workspace)))
+    return calls[0], calls[1], out
+
+
+def prepare_kv_cache_write_int8_mla(kv_nope, k_rope, nope_codes, rope_codes, nope_scale, rope_scale,
+                                    slots):
+    _dev(kv_nope, k_rope, nope_codes, rope_codes, nope_scale, rope_scale, slots)
+    _mla_int8_shapes(nope_codes, rope_codes, nope_scale, rope_scale)
+    nb, bs = nope_codes.shape[0], nope_codes.shape[1]
+    args = (_ptr(kv_nope), _ptr(k_rope), _ptr(nope_codes), _ptr(rope_codes), _ptr(nope_scale),
+            _ptr(rope_scale), _ptr(slots), slots.shape[0], bs, nb, _dtype_code(kv_nope),
+            _stream(kv_nope.device))
+    return PreparedCall(lib().pkv_kv_cache_write_int8_mla, args,
+                        (kv_nope, k_rope, nope_codes, rope_codes, nope_scale, rope_scale, slots))
+
+
 def _decode_mtp_args(q, k_cache, v_cache, block_table, seq_lens_kv, num_q_tokens,
                      max_seq_len_kv, softmax_scale, stages, out, lse, workspace, window):
     """Arguments of pkv_paged_attn_decode_mtp."""
     _dev(q, k_cache, v_cache, block_table, seq_lens_kv, out, lse, workspace)
     rows, hq, d = q.shape
     B = seq_lens_kv.shape[0]
+    _batch_rows(B, block_table, seq_lens_kv)
     if rows != B * num_q_tokens:
         raise ValueError(f"q has {rows} rows, expected batch * num_q_tokens = {B * num_q_tokens}")
     nb, bs, hkv, _ = k_cache.shape

@@ -391,7 +391,8 @@ int run_mla_decode(void* out, float* lse_out, const void* q, const void* q_rope,
                    int32_t num_kv_heads, int32_t head_dim_qk, int32_t head_dim_v,
                    int32_t head_dim_rope, int32_t block_size, int64_t num_blocks,
                    float softmax_scale, int32_t dtype, void* workspace, size_t workspace_bytes,
-                   int stages, hipStream_t s) {
+                   int stages, hipStream_t s, const float* nope_scale = nullptr,
+                   const float* rope_scale = nullptr) {
     if (num_kv_heads != 1 || head_dim_qk != 512 || head_dim_v != 512 || head_dim_rope != 64)
         return fail(PKV_ERR_UNSUPPORTED,
                     "decode (MLA): needs 1 kv head, head_dim_qk = head_dim_v = 512, head_dim_rope = 64");
@@ -435,6 +436,8 @@ int run_mla_decode(void* out, float* lse_out, const void* q, const void* q_rope,
     p.len_cap = max_seq_len_kv;
     p.num_blocks = num_blocks;
     p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+    p.k_scale = nope_scale;
+    p.r_scale = rope_scale;
     int rc = PKV_OK;
     if (stages & 1) {
         rc = hip_status(pkv::launch_mla_decode(p, s), "decode (MLA) launch");
@@ -701,6 +704,70 @@ int pkv_paged_attn_decode_mtp(void* out, float* lse_out, const void* q, const vo
     }
     if ((stages & 2) && needs_combine(p, plan)) return launch_combine_for(p, head_dim, dtype, s);
     return PKV_OK;
+}
+
+int pkv_kv_cache_write_int8_mla(const void* kv_nope, const void* k_rope, void* nope_codes,
+                                void* rope_codes, float* nope_scale, float* rope_scale,
+                                const int64_t* slot_mapping, int64_t num_tokens, int32_t block_size,
+                                int64_t num_blocks, int32_t dtype, void* stream) {
+    if (dtype != PKV_F32 && dtype != PKV_BF16)
+        return fail(PKV_ERR_DTYPE, "kv_cache_write_int8_mla: unknown input dtype %d", dtype);
+    if (num_tokens < 0 || num_blocks <= 0)
+        return fail(PKV_ERR_SHAPE, "kv_cache_write_int8_mla: num_blocks must be positive (num_tokens >= 0)");
+    if (!pow2_in(block_size, 1, 256))
+        return fail(PKV_ERR_UNSUPPORTED, "kv_cache_write_int8_mla: block_size %d is not a power of two in [1, 256]",
+                    block_size);
+    if (num_tokens > 0x7fffffffLL) return fail(PKV_ERR_SHAPE, "kv_cache_write_int8_mla: too many tokens");
+    if (num_tokens == 0) return PKV_OK;
+    if (!kv_nope || !k_rope || !nope_codes || !rope_codes || !nope_scale || !rope_scale || !slot_mapping)
+        return fail(PKV_ERR_NULL, "kv_cache_write_int8_mla: NULL pointer argument");
+    if (!aligned16(kv_nope) || !aligned16(k_rope) || !aligned16(nope_codes) || !aligned16(rope_codes) ||
+        !aligned16(nope_scale) || !aligned16(rope_scale))
+        return fail(PKV_ERR_ALIGN, "kv_cache_write_int8_mla: all arrays must be 16-byte aligned");
+    if (nope_codes == rope_codes || nope_scale == rope_scale)
+        return fail(PKV_ERR_SHAPE, "kv_cache_write_int8_mla: nope and rope arrays must differ");
+    pkv::QuantWriteParams p{};
+    p.k_new = kv_nope;
+    p.v_new = k_rope;
+    p.k_cache = static_cast<int8_t*>(nope_codes);
+    p.v_cache = static_cast<int8_t*>(rope_codes);
+    p.k_scale = nope_scale;
+    p.v_scale = rope_scale;
+    p.slots = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.num_slots = num_blocks * block_size;
+    p.hkv = 1;
+    p.bs_log2 = log2i(block_size);
+    return hip_status(pkv::launch_kv_write_int8_mla(p, dtype, (hipStream_t)stream),
+                      "kv_cache_write_int8_mla launch");
+}
+
+int pkv_paged_attn_decode_mla_int8(void* out, float* lse_out, const void* q, const void* q_rope,
+                                   const void* nope_codes, const void* rope_codes,
+                                   const float* nope_scale, const float* rope_scale,
+                                   const int32_t* block_table, const int32_t* seq_lens_kv, int32_t batch,
+                                   int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                                   int32_t num_q_heads, int32_t block_size, int64_t num_blocks,
+                                   float softmax_scale, int32_t stages, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (stages < 1 || stages > 3) return fail(PKV_ERR_SHAPE, "decode_mla_int8: stages must be 1, 2 or 3");
+    if (!q_rope || !rope_codes) return fail(PKV_ERR_NULL, "decode_mla_int8: q_rope and rope_codes are required");
+    bool mla = false;
+    int rc = check_decode_common(q_rope, rope_codes, PKV_BF16, batch, num_q_heads, 1, 512, 512, 64,
+                                 max_blocks_per_seq, max_seq_len_kv, block_size, num_blocks,
+                                 softmax_scale, &mla);
+    if (rc != PKV_OK) return rc;
+    if (block_size < 4)
+        return fail(PKV_ERR_UNSUPPORTED, "decode_mla_int8: block_size %d (needs >= 4: a 4-key group's scales are one load)",
+                    block_size);
+    if (batch == 0) return PKV_OK;
+    if (!nope_scale || !rope_scale) return fail(PKV_ERR_NULL, "decode_mla_int8: NULL scale array");
+    if (!aligned16(nope_scale) || !aligned16(rope_scale))
+        return fail(PKV_ERR_ALIGN, "decode_mla_int8: scale arrays must be 16-byte aligned");
+    return run_mla_decode(out, lse_out, q, q_rope, nope_codes, nope_codes, rope_codes, block_table,
+                          seq_lens_kv, batch, max_blocks_per_seq, max_seq_len_kv, num_q_heads, 1, 512,
+                          512, 64, block_size, num_blocks, softmax_scale, PKV_BF16, workspace,
+                          workspace_bytes, stages, (hipStream_t)stream, nope_scale, rope_scale);
 }
 
 int pkv_kv_cache_write_int8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

@@ -47,7 +47,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void kv_write_int8_kernel(QuantWriteParams p) {
     constexpr int kLpr = D / 8;                       // lanes per row
     constexpr int kRpw = 64 / kLpr;                   // rows per wave
-    const int which = blockIdx.y;
+    const int which = p.which_base + blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRpw + lane / kLpr;
     const int c = lane % kLpr;
@@ -329,6 +329,22 @@ hipError_t launch_kv_write_int8(const QuantWriteParams& p, int in_dtype, int hea
         if (head_dim == 64) hipLaunchKernelGGL((kv_write_int8_kernel<float, 64>), grid, dim3(256), 0, s, p);
         else hipLaunchKernelGGL((kv_write_int8_kernel<float, 128>), grid, dim3(256), 0, s, p);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_write_int8_mla(const QuantWriteParams& p, int in_dtype, hipStream_t s) {
+    QuantWriteParams q = p;
+    const int64_t rows = p.num_tokens;                                  // one kv head
+    const dim3 gn((unsigned)((rows + 3) / 4), 1);                       // 512 wide: one row per wave
+    const dim3 gr((unsigned)((rows + 31) / 32), 1);                     // 64 wide: eight per wave
+    q.which_base = 0;
+    if (in_dtype == 1) hipLaunchKernelGGL((kv_write_int8_kernel<bf16_t, 512>), gn, dim3(256), 0, s, q);
+    else hipLaunchKernelGGL((kv_write_int8_kernel<float, 512>), gn, dim3(256), 0, s, q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    q.which_base = 1;
+    if (in_dtype == 1) hipLaunchKernelGGL((kv_write_int8_kernel<bf16_t, 64>), gr, dim3(256), 0, s, q);
+    else hipLaunchKernelGGL((kv_write_int8_kernel<float, 64>), gr, dim3(256), 0, s, q);
     return hipGetLastError();
 }
 

@@ -20,6 +20,14 @@
 //    which after the first tiles almost never happens.  Full tiles skip the masking.
 // One wave per SIMD: O^T lives in VGPRs (the rescale multiplies it in place) and Q^T in
 // the accumulation registers.
+//
+// Over the INT8 cache (codes with one fp32 scale per token for nope and one for rope) the
+// products are the same, over bf16 copies of the codes (exact: |q| <= 127): the codes of a
+// tile (512 + 64 bytes per key) and its keys' scales reach LDS by direct loads two tiles
+// ahead; each wave converts the eight keys it loaded into one of two bf16 buffers laid out
+// like a bf16 stage, before the tile's barrier.  Scores keep the nope and rope sums apart
+// and weigh them per key with the two scales; the nope scale is folded into the weight of
+// the value sum (P' = bf16(p s_nope)), while l sums the rounded p.
 #include "mfma_common.h"
 
 namespace pkv {
@@ -52,9 +60,42 @@ __device__ __forceinline__ int mla_row(int g, int r) { return (g & 2) * 4 + (g &
 // Physical 16-byte chunk of rope chunk c in rope row r.
 __device__ __forceinline__ int rope_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
+// LDS of the INT8 form: three stages of codes as loaded (32 nope rows of 512 bytes, then per
+// wave 1 KiB: its 8 rope rows of 64 bytes, the 8 nope scales, the 8 rope scales, padding),
+// two bf16 buffers (a bf16 stage plus the tile's 32 nope and 32 rope scales), the table.
+struct MlaI8Cfg {
+    static constexpr int kCodeStages = 3;
+    static constexpr int kNopeCodes = kKeys * 512;
+    static constexpr int kAux = 1024;
+    static constexpr int kCodeStage = kNopeCodes + MlaCfg::kWaves * kAux;
+    static constexpr int kBuf = MlaCfg::kStage + 2 * kKeys * 4;
+    static constexpr int kBufOff = kCodeStages * kCodeStage;
+    static constexpr int kTabOff = kBufOff + 2 * kBuf;
+    static constexpr int kSmem = kTabOff + 2 * kTabEntries * 4;
+    static constexpr int kDma = 5;                          // wave loads per tile: 4 nope + 1 rope and scales
+    static_assert(kSmem <= 160 * 1024, "LDS");
+    static_assert(kBuf % 16 == 0, "buffer alignment");
+};
+
+// Code k of a dword as float.
+__device__ __forceinline__ float code_of(uint32_t w, int k) { return (float)(int)(int8_t)(w >> (8 * k)); }
+// 16 codes as 16 bf16 (exact), codes 0-7 in lo, 8-15 in hi.
+__device__ __forceinline__ void codes_to_bf16(u32x4 v, u32x4& lo, u32x4& hi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t a = pack_bf16(code_of(v[i], 0), code_of(v[i], 1));
+        const uint32_t b = pack_bf16(code_of(v[i], 2), code_of(v[i], 3));
+        if (i < 2) { lo[2 * i] = a; lo[2 * i + 1] = b; }
+        else { hi[2 * i - 4] = a; hi[2 * i - 3] = b; }
+    }
+}
+
+template <bool I8>
 __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams p) {
     using C = MlaCfg;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[C::kSmem];
+    using I = MlaI8Cfg;
+    constexpr int kTabOff = I8 ? I::kTabOff : kStages * C::kStage;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[I8 ? I::kSmem : C::kSmem];
 
     const int tid = threadIdx.x;
     const int wid = tid >> 6;
@@ -73,7 +114,7 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
     {
         auto nsplits = [&](int, int len) { return len > 0 ? (len + p.split_tokens - 1) / p.split_tokens : 1; };
         if (!find_item<C::kThreads>(unit, p.batch, p.seq_lens, p.len_cap, nsplits,
-                                    reinterpret_cast<int32_t*>(smem + kStages * C::kStage), b, split))
+                                    reinterpret_cast<int32_t*>(smem + kTabOff), b, split))
             return;
         b = __builtin_amdgcn_readfirstlane(b);          // the same in every lane
         split = __builtin_amdgcn_readfirstlane(split);
@@ -114,7 +155,7 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
     }
 
     TableChunks<C::kThreads> tab;
-    tab.lds = reinterpret_cast<int32_t*>(smem + kStages * C::kStage);
+    tab.lds = reinterpret_cast<int32_t*>(smem + kTabOff);
     tab.row = p.table + (int64_t)b * p.mbs;
     tab.k_begin = k_begin;
     tab.k_end = k_end;
@@ -151,6 +192,46 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
     auto issue_tile = [&](int u) {
         const int kb = k_begin + u * kKeys;
         const int chunk = u / kChunkTiles;
+        if constexpr (I8) {
+            // Wave w loads the codes of keys 8 w .. 8 w + 7: their nope rows (4 loads of two
+            // rows) and one load whose lanes 0-31 take the 8 rope rows, 32-33 the 8 nope
+            // scales, 34-35 the 8 rope scales (scales are in slot order per block, and a
+            // group of 4 keys lies in one block), the others re-read lane 32's bytes.
+            uint8_t* cs = smem + (u % I::kCodeStages) * I::kCodeStage;
+            uint8_t* aux = cs + I::kNopeCodes + wid_u * I::kAux;
+            const uint8_t* ncodes = reinterpret_cast<const uint8_t*>(p.k_cache);
+            const uint8_t* rcodes = reinterpret_cast<const uint8_t*>(p.k_rope);
+            const uint8_t* nsc = reinterpret_cast<const uint8_t*>(p.k_scale);
+            const uint8_t* rsc = reinterpret_cast<const uint8_t*>(p.r_scale);
+            const int32_t entry = next_entry;
+            if (u + 1 < ntiles && fast_tile(u + 1)) next_entry = entry_of(u + 1);
+            const int q = lane >= 32 && lane < 36 ? lane - 32 : 0;
+            if (fast_tile(u)) {
+                const int key0 = kb + 8 * wid_u;
+                const int32_t blk = min(max(entry, 0), tab.last_block);
+                const uint64_t slot0 = ((uint64_t)(uint32_t)blk << p.bs_log2) | (uint32_t)(key0 & bs_mask);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    lds_dma16_s(ncodes + slot0 * 512u + j * 1024, (uint32_t)lane * 16u, cs + (8 * wid_u) * 512 + j * 1024);
+                const uint8_t* src = lane < 32 ? rcodes + slot0 * 64u + lane * 16
+                                               : ((q & 2) ? rsc : nsc) + slot0 * 4u + (q & 1) * 16;
+                lds_dma16(src, aux);
+                return;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int key = min(kb + 8 * wid + 2 * j + (lane >> 5), k_end - 1);
+                const uint64_t slot = ((uint64_t)tab.block_of(key, chunk) << p.bs_log2) | (uint32_t)(key & bs_mask);
+                lds_dma16(ncodes + slot * 512u + (lane & 31) * 16, cs + (8 * wid_u + 2 * j) * 512);
+            }
+            // keys past the range: their rope row and scales come from the last key (its
+            // 4-key group for the scales); their weights are 0
+            const int key = lane < 32 ? min(kb + 8 * wid + (lane >> 2), k_end - 1)
+                                      : min(kb + 8 * wid + 4 * (q & 1), (k_end - 1) & ~3);
+            const uint64_t slot = ((uint64_t)tab.block_of(key, chunk) << p.bs_log2) | (uint32_t)(key & bs_mask);
+            lds_dma16(lane < 32 ? rcodes + slot * 64u + (lane & 3) * 16 : ((q & 2) ? rsc : nsc) + slot * 4u, aux);
+            return;
+        }
         uint8_t* stage = smem + (u % kStages) * C::kStage;
         const int32_t entry = next_entry;
         if (u + 1 < ntiles && fast_tile(u + 1)) next_entry = entry_of(u + 1);
@@ -197,6 +278,36 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
 #pragma unroll
     for (int h = 0; h < 2; ++h) v_off[h] = (16 * h + mla_row(g, n >> 2)) * C::kNopeRow + 8 * (n & 3);
 
+    // INT8: this wave's keys of tile t, codes -> bf16 buffer t & 1 (it reads only what it
+    // loaded itself, so its own load counter is the only wait), scales beside them.
+    auto convert = [&](int t) {
+        const uint8_t* cs = smem + (t % I::kCodeStages) * I::kCodeStage;
+        uint8_t* bf = smem + I::kBufOff + (t & 1) * I::kBuf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {          // nope: 8 rows x 32 chunks of 16 codes
+            const int ci = lane + 64 * i;
+            const int r = 8 * wid_u + (ci >> 5);
+            const int c16 = ci & 31;
+            u32x4 lo, hi;
+            codes_to_bf16(*reinterpret_cast<const u32x4*>(cs + r * 512 + c16 * 16), lo, hi);
+            *reinterpret_cast<u32x4*>(bf + r * C::kNopeRow + c16 * 32) = lo;
+            *reinterpret_cast<u32x4*>(bf + r * C::kNopeRow + c16 * 32 + 16) = hi;
+        }
+        const uint8_t* aux = cs + I::kNopeCodes + wid_u * I::kAux;
+        if (lane < 32) {                       // rope: row 8 w + lane / 4, dims 16 (lane % 4) ..
+            const int r = 8 * wid_u + (lane >> 2);
+            const int c4 = lane & 3;
+            u32x4 lo, hi;
+            codes_to_bf16(*reinterpret_cast<const u32x4*>(aux + lane * 16), lo, hi);
+            *reinterpret_cast<u32x4*>(bf + C::kRopeBase + r * 128 + rope_chunk(r, 2 * c4) * 16) = lo;
+            *reinterpret_cast<u32x4*>(bf + C::kRopeBase + r * 128 + rope_chunk(r, 2 * c4 + 1) * 16) = hi;
+        } else if (lane < 48) {                // scales: 8 nope, then 8 rope
+            const int qq = lane - 32;
+            const float sc = *reinterpret_cast<const float*>(aux + 512 + qq * 4);
+            *reinterpret_cast<float*>(bf + C::kStage + ((qq >> 3) * kKeys + 8 * wid_u + (qq & 7)) * 4) = sc;
+        }
+    };
+
     RowState st;
     f32x4 oacc[C::kDTiles];
 #pragma unroll
@@ -206,17 +317,19 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
     // them and sets keys past the range (and all keys of heads past num_q_heads) to -inf.
     // Entry (h, r) of lane (g, n) is key 16 h + mla_row(g, r) of the tile.  Returns the
     // head's max over the tile (scaled, log2 units).
-    auto scores = [&](int t, bool full, float* sv) -> float {
-        const uint8_t* stage = smem + (t % kStages) * C::kStage;
-        f32x4 sacc[2];
+    auto scores = [&](int t, bool full, float* sv, float* sn) -> float {
+        const uint8_t* stage = I8 ? smem + I::kBufOff + (t & 1) * I::kBuf : smem + (t % kStages) * C::kStage;
+        f32x4 sacc[2], racc[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             sacc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+            racc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < C::kSteps; ++s) {
                 const uint8_t* src = s < 16 ? stage + k_off[h] + 64 * s : stage + rope_off[h][s - 16];
                 const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(src));
-                sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], sacc[h], 0, 0, 0);
+                if (I8 && s >= 16) racc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], racc[h], 0, 0, 0);
+                else sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], sacc[h], 0, 0, 0);
             }
         }
         // Keep six K reads in flight ahead of the products (left alone, the compiler
@@ -228,6 +341,15 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
+        if constexpr (I8) {   // per key: s_nope * (q_nope . codes) + s_rope * (q_rope . codes)
+            const float* scn = reinterpret_cast<const float*>(stage + C::kStage);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int key = 16 * (e >> 2) + mla_row(g, e & 3);
+                sn[e] = scn[key];
+                sacc[e >> 2][e & 3] = sn[e] * sacc[e >> 2][e & 3] + scn[kKeys + key] * racc[e >> 2][e & 3];
+            }
+        }
         float tmax;
         if (full) {
 #pragma unroll
@@ -241,6 +363,7 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
             for (int e = 0; e < 8; ++e) {
                 const int key = kb + 16 * (e >> 2) + mla_row(g, e & 3);
                 sv[e] = (valid && key < k_end) ? sacc[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
+                if (I8 && sv[e] == -INFINITY) sn[e] = 0.0f;   // no stale scale reaches P'
                 tmax = fmaxf(tmax, sv[e]);
             }
         }
@@ -249,16 +372,17 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
 
     // P^T of tile t against the running max (k-slot 8 g + 4 h + r is entry (h, r); the sum
     // adds the rounded weights), then O^T += V^T . P^T.
-    auto probs_pv = [&](int t, bool full, const float* sv) {
+    auto probs_pv = [&](int t, bool full, const float* sv, const float* sn) {
         u32x4 pw;
         if (full) {
             const float mneg = -st.m;
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const uint32_t w = pack_bf16(fast_exp2(__builtin_fmaf(sv[e], p.scale_log2, mneg)),
-                                             fast_exp2(__builtin_fmaf(sv[e + 1], p.scale_log2, mneg)));
+                const float e0 = fast_exp2(__builtin_fmaf(sv[e], p.scale_log2, mneg));
+                const float e1 = fast_exp2(__builtin_fmaf(sv[e + 1], p.scale_log2, mneg));
+                const uint32_t w = pack_bf16(e0, e1);
                 st.l = dot2_bf16(w, kOnesBf16x2, st.l);
-                pw[e >> 1] = w;
+                pw[e >> 1] = I8 ? pack_bf16(e0 * sn[e], e1 * sn[e + 1]) : w;
             }
         } else {
 #pragma unroll
@@ -267,11 +391,11 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
                 const float e1 = sv[e + 1] == -INFINITY ? 0.0f : fast_exp2(sv[e + 1] - st.m);
                 const uint32_t w = pack_bf16(e0, e1);
                 st.l = dot2_bf16(w, kOnesBf16x2, st.l);
-                pw[e >> 1] = w;
+                pw[e >> 1] = I8 ? pack_bf16(e0 * sn[e], e1 * sn[e + 1]) : w;
             }
         }
         const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
-        const uint8_t* stage = smem + (t % kStages) * C::kStage;
+        const uint8_t* stage = I8 ? smem + I::kBufOff + (t & 1) * I::kBuf : smem + (t % kStages) * C::kStage;
         const uint8_t* v0 = stage + v_off[0];
         const uint8_t* v1 = stage + v_off[1];
 #pragma unroll
@@ -301,8 +425,9 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
         if (u % kChunkTiles == kChunkTiles / 2 && tab.exists(c + 1)) tab.store(c + 1, treg);
         issue_tile(u);
     };
+    constexpr int kAhead = I8 ? I::kCodeStages - 1 : kStages - 1;   // tiles issued ahead
 #pragma unroll
-    for (int u = 0; u < kStages - 1; ++u) feed(u);
+    for (int u = 0; u < kAhead; ++u) feed(u);
 
     // Tile t: wait for its loads, barrier (tile t visible, the stage of tile t - 1 free,
     // staged table entries visible), issue tile t + 3 (two waves before their scores, two
@@ -311,20 +436,32 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
     // slack leaves the loop to rescale O^T, so that inside the loop the accumulators are
     // only touched by the products.
     int t = 0;
-    float sv[8];
+    float sv[8], sn[8];
     float tmax = 0.0f;
     bool full = false;
     while (t < ntiles) {
         for (; t < ntiles; ++t) {
-            wait_tile<C::kDma>(min(ntiles - 1 - t, kStages - 2));
-            block_sync();
-            if (wid_u < 2) feed(t + kStages - 1);
-            full = k_begin + (t + 1) * kKeys <= k_end;
-            tmax = scores(t, full, sv);
-            if (wid_u >= 2) feed(t + kStages - 1);
+            if constexpr (I8) {
+                // This wave's codes of tile t (tile t + 1 may stay in flight), into bf16;
+                // the barrier publishes buffer t & 1 and frees the code stage of tile t - 1
+                // (converted) and buffer (t + 1) & 1 (read by tile t - 1) for reuse.
+                wait_tile<I::kDma>(min(ntiles - 1 - t, 1));
+                convert(t);
+                block_sync();
+                feed(t + kAhead);
+                full = k_begin + (t + 1) * kKeys <= k_end;
+                tmax = scores(t, full, sv, sn);
+            } else {
+                wait_tile<C::kDma>(min(ntiles - 1 - t, kStages - 2));
+                block_sync();
+                if (wid_u < 2) feed(t + kStages - 1);
+                full = k_begin + (t + 1) * kKeys <= k_end;
+                tmax = scores(t, full, sv, sn);
+                if (wid_u >= 2) feed(t + kStages - 1);
+            }
             const bool grow = tmax > st.m + kRescaleSlack || (st.m == -INFINITY && tmax != -INFINITY);
             if (__any(grow)) break;
-            probs_pv(t, full, sv);
+            probs_pv(t, full, sv, sn);
         }
         if (t >= ntiles) break;
         {
@@ -336,7 +473,7 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
             for (int dt = 0; dt < C::kDTiles; ++dt) oacc[dt] *= alpha;
             st.m = mnew;
         }
-        probs_pv(t, full, sv);
+        probs_pv(t, full, sv, sn);
         ++t;
     }
 
@@ -398,7 +535,8 @@ hipError_t launch_mla_decode(const MfmaParams& p, hipStream_t s) {
     const int64_t hgs = mla_head_groups(p.hq);
     const int64_t units = ((int64_t)p.batch * p.max_splits + 7) / 8 * 8;
     const dim3 grid((unsigned)(hgs * units));
-    hipLaunchKernelGGL(mla_decode_kernel, grid, dim3(MlaCfg::kThreads), 0, s, p);
+    if (p.k_scale) hipLaunchKernelGGL(mla_decode_kernel<true>, grid, dim3(MlaCfg::kThreads), 0, s, p);
+    else hipLaunchKernelGGL(mla_decode_kernel<false>, grid, dim3(MlaCfg::kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -76,8 +76,12 @@ struct QuantWriteParams {
     int64_t num_tokens, num_slots;
     int32_t hkv;
     int32_t bs_log2;
+    int32_t which_base;      // 0: blockIdx.y picks K (0) or V (1); 1: the launch writes V only
 };
 hipError_t launch_kv_write_int8(const QuantWriteParams& p, int in_dtype, int head_dim, hipStream_t s);
+// The MLA latent cache: k_new/k_cache/k_scale are the 512-wide nope rows, v_new/v_cache/
+// v_scale the 64-wide rope rows (one kv head), each quantized with its own scale.
+hipError_t launch_kv_write_int8_mla(const QuantWriteParams& p, int in_dtype, hipStream_t s);
 
 // RMSNorm + RoPE + write of the MLA latent row (one wave per token).
 struct NormRopeParams {
@@ -214,6 +218,10 @@ struct MfmaParams {
     int32_t window;          // varlen: > 0 keeps each row's `window` most recent visible keys
     int64_t num_blocks;
     float scale_log2;
+    // MLA over the INT8 cache (else null): k_cache / k_rope hold int8 codes, these their
+    // fp32 scales [nb][1][bs] (nope, rope).
+    const float* k_scale;
+    const float* r_scale;
 };
 // MLA decode: Dqk = 512 + Dr 64, Dv = 512, bf16.  Returns the launch status.
 DecodePlan plan_mla(int32_t batch, int32_t num_q_heads, int32_t head_dim_v, int32_t max_seq_len_kv);

@@ -383,3 +383,41 @@ def test_decode_mtp_rejects():
     assert need > lib.pkv_decode_mtp_workspace_size(4, 1, 32, 8, 128, 1024) > 0
     assert lib.pkv_decode_mtp_workspace_size(4, 0, 32, 8, 128, 1024) == 0
     assert mtp(wsb=need - 1) == -7
+
+
+def test_int8_mla_forms_reject_bad_arguments():
+    lib = _lib().lib()
+    F2 = ctypes.c_void_p(0x200000)
+
+    def dec(**kw):
+        a = dict(out=FAKE, lse=None, q=FAKE, qr=FAKE, nc=FAKE, rc=F2, ns=FAKE, rs=F2, table=FAKE,
+                 lens=FAKE, B=2, mbs=8, maxlen=128, hq=128, bs=16, nb=64, scale=0.04, stages=3,
+                 ws=FAKE, wsb=1 << 30, stream=None)
+        a.update(kw)
+        return lib.pkv_paged_attn_decode_mla_int8(a["out"], a["lse"], a["q"], a["qr"], a["nc"], a["rc"],
+                                                  a["ns"], a["rs"], a["table"], a["lens"], a["B"], a["mbs"],
+                                                  a["maxlen"], a["hq"], a["bs"], a["nb"], a["scale"],
+                                                  a["stages"], a["ws"], a["wsb"], a["stream"])
+    assert dec(stages=0) == -2
+    assert dec(qr=None) == -1
+    assert dec(bs=2, maxlen=16) == -4           # a 4-key group's scales must be one load
+    assert dec(bs=24) == -4
+    assert dec(ns=None) == -1
+    assert dec(rs=ctypes.c_void_p(0x200004)) == -5
+    assert dec(scale=-1.0) == -6
+    assert dec(maxlen=4096) == -2
+    assert dec(ws=FAKE, wsb=16, mbs=256, maxlen=4096) == -7   # several splits: a workspace is needed
+    assert dec(B=0) == 0
+
+    def wr(**kw):
+        a = dict(n=FAKE, r=F2, nc=FAKE, rc=F2, ns=FAKE, rs=F2, slots=FAKE, T=3, bs=16, nb=8, dtype=1)
+        a.update(kw)
+        return lib.pkv_kv_cache_write_int8_mla(a["n"], a["r"], a["nc"], a["rc"], a["ns"], a["rs"],
+                                               a["slots"], a["T"], a["bs"], a["nb"], a["dtype"], None)
+    assert wr(dtype=5) == -3
+    assert wr(T=-1) == -2
+    assert wr(T=0, n=None) == 0
+    assert wr(slots=None) == -1
+    assert wr(rc=FAKE) == -2                    # nope and rope codes must differ
+    assert wr(ns=ctypes.c_void_p(0x100004)) == -5
+    assert wr(bs=3) == -4

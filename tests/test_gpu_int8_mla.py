@@ -1,0 +1,153 @@
+"""GPU parity of the INT8 MLA latent cache against the oracle, through the C ABI: the
+quantizing writer bit for bit (nope and rope rows each with their own scale, other bytes
+unchanged, out-of-pool slots skipped), and the MLA-absorbed decode over the codes against
+fp64 attention over the exactly dequantized rows (key = nope || rope, value = nope).  Needs an
+MI355X."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_133_amd as pkv
+from oracle import oracle
+from paged_kv_cache_133_amd import _lib
+from paged_kv_cache_133_amd import workloads as wl
+from tests.gpu_common import LSE_ABS_MFMA, say
+from tests.helpers import host
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.mark.parametrize("dtype,bs", [("bf16", 16), ("f32", 4), ("bf16", 128)])
+def test_int8_mla_write_bit_exact(dtype, bs):
+    td = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    g = torch.Generator().manual_seed(bs)
+    T, nb = 37, 12
+    nope = (torch.randn(T, 512, generator=g) * torch.rand(T, 1, generator=g) * 20).to(td)
+    rope = (torch.randn(T, 64, generator=g) * 3).to(td)
+    nope[5] = 0                                          # zero row: scale 0, zero codes
+    slots = torch.randperm(nb * bs, generator=g)[:T].to(torch.int64)
+    slots[3], slots[9] = -1, nb * bs                     # skipped
+    nc = torch.randint(-128, 128, (nb, bs, 512), generator=g, dtype=torch.int8)
+    rc = torch.randint(-128, 128, (nb, bs, 64), generator=g, dtype=torch.int8)
+    ns = torch.randn(nb, bs, generator=g)
+    rs = torch.randn(nb, bs, generator=g)
+    say(f"int8 mla write {dtype} bs={bs}")
+    d = [t.to(DEV) for t in (nc, rc, ns, rs)]
+    pkv.kv_cache_write_int8_mla(nope.to(DEV), rope.to(DEV), *d, slots.to(DEV))
+    torch.cuda.synchronize()
+    ok = ((slots >= 0) & (slots < nb * bs)).numpy()
+    sl = slots.numpy()[ok]
+    for new, codes, scales, gc, gs, w in ((nope, nc, ns, d[0], d[2], 512), (rope, rc, rs, d[1], d[3], 64)):
+        q, s = oracle.quantize_rows(host(new))           # [T, w], [T]
+        exp_c = codes.numpy().reshape(nb * bs, w).copy()
+        exp_s = scales.numpy().reshape(nb * bs).copy()
+        exp_c[sl] = q[ok]
+        exp_s[sl] = s[ok]
+        assert np.array_equal(gc.cpu().numpy().reshape(nb * bs, w), exp_c)
+        assert np.array_equal(gs.cpu().numpy().reshape(nb * bs).view(np.uint32), exp_s.view(np.uint32))
+
+
+def _int8_mla_case(hq, bs, L, seed):
+    """An MLA case whose pools are the oracle's quantization of a bf16 pool, with the step's
+    new rows written by the GPU's quantizing writer.  A length of 0 marks a padding row: the
+    case still gives it one row (q has one row per sequence), and the lengths the kernel gets
+    (returned) say 0 there.  Returns the case, the device arrays, the dequantized pools (fp64)
+    and the lengths."""
+    w = wl.custom(mode="mla", batch=len(L), num_q_heads=hq, num_kv_heads=1, head_dim=512,
+                  head_dim_rope=64, block_size=bs, dtype="bf16")
+    c = wl.make_case(w, np.maximum(np.array(L) - 1, 0), [1] * len(L), seed=seed, device=DEV,
+                     poison=False)
+    lens = np.where(np.array(L) > 0, c.lens_after, 0).astype(np.int32)
+    nb = c.num_blocks
+    nq, nsc = oracle.quantize_rows(host(c.cache_k).reshape(nb, bs, 512))
+    rq, rsc = oracle.quantize_rows(host(c.cache_rope).reshape(nb, bs, 64))
+    dev = {"nc": torch.from_numpy(nq).to(DEV), "rc": torch.from_numpy(rq).to(DEV),
+           "ns": torch.from_numpy(nsc).to(DEV), "rs": torch.from_numpy(rsc).to(DEV)}
+    table = c.table_tensor(DEV)
+    if c.num_tokens:
+        slots = pkv.slot_mapping(table, c.lens_before_tensor(DEV), c.cu_q_tensor(DEV), bs, c.num_tokens)
+        pkv.kv_cache_write_int8_mla(c.new_k.reshape(-1, 512), c.new_rope.reshape(-1, 64), dev["nc"],
+                                    dev["rc"], dev["ns"], dev["rs"], slots)
+        torch.cuda.synchronize()
+        sl = slots.cpu().numpy()
+        a, b = oracle.quantize_rows(host(c.new_k).reshape(-1, 512))
+        nq.reshape(nb * bs, 512)[sl] = a
+        nsc.reshape(nb * bs)[sl] = b
+        a, b = oracle.quantize_rows(host(c.new_rope).reshape(-1, 64))
+        rq.reshape(nb * bs, 64)[sl] = a
+        rsc.reshape(nb * bs)[sl] = b
+    assert np.array_equal(dev["nc"].cpu().numpy(), nq) and np.array_equal(dev["rs"].cpu().numpy(), rsc)
+    kdeq = oracle.dequantize_rows(nq, nsc).reshape(nb, bs, 1, 512)
+    rdeq = oracle.dequantize_rows(rq, rsc).reshape(nb, bs, 1, 64)
+    return c, dev, table, kdeq, rdeq, lens
+
+
+def _check(c, out, lse, kdeq, rdeq, lens_all, rows=None):
+    idx = np.arange(c.w.batch) if rows is None else np.asarray(rows)
+    lens = lens_all[idx]
+    live = idx[lens > 0]
+    got = out.float().cpu().numpy()
+    got_lse = lse.cpu().numpy()
+    for b in idx[lens == 0]:                            # padding rows: 0 and -inf
+        assert (got[b] == 0).all() and np.isneginf(got_lse[b]).all()
+    if len(live) == 0:
+        return 0.0
+    cu = np.arange(len(live) + 1, dtype=np.int32)
+    o, ol = oracle.paged_attention(oracle.widen(host(c.q))[live], kdeq, kdeq, c.block_table[live], cu,
+                                   lens_all[live], c.w.scale, False,
+                                   q_rope=oracle.widen(host(c.q_rope))[live], k_rope=rdeq)
+    err = float(np.abs(got[live] - o).max())
+    assert err <= 2e-2, f"max-abs error {err:.3e}"
+    lerr = float(np.abs(got_lse[live] - ol).max())
+    assert lerr <= LSE_ABS_MFMA, f"lse error {lerr:.3e}"
+    return err
+
+
+@pytest.mark.parametrize("hq,bs", [(128, 16), (64, 4), (16, 128), (32, 8)])
+def test_int8_mla_decode_parity(hq, bs):
+    L = [0, 1, 31, 32, 33, bs - 1 if bs > 1 else 2, 700, 2600]
+    say(f"int8 mla decode hq={hq} bs={bs} L={L}")
+    c, dev, table, kdeq, rdeq, lens = _int8_mla_case(hq, bs, L, seed=hq + bs)
+    assert c.q.shape[0] == len(L)
+    lse = torch.full((len(L), hq), 3.0, dtype=torch.float32, device=DEV)
+    out, _ = pkv.paged_attn_decode_mla_int8(c.q, c.q_rope, dev["nc"], dev["rc"], dev["ns"], dev["rs"],
+                                            table, torch.from_numpy(lens).to(DEV), c.max_len_after,
+                                            c.w.scale, lse=lse)
+    torch.cuda.synchronize()
+    say(f"  max-abs error {_check(c, out, lse, kdeq, rdeq, lens):.3e}")
+
+
+def test_int8_mla_two_passes_equal_one():
+    c, dev, table, kdeq, rdeq, lens = _int8_mla_case(128, 64, [3000, 5, 1400, 64, 65], seed=4)
+    la = torch.from_numpy(lens).to(DEV)
+    args = (c.q, c.q_rope, dev["nc"], dev["rc"], dev["ns"], dev["rs"], table, la, c.max_len_after, c.w.scale)
+    lse1 = torch.empty((5, 128), dtype=torch.float32, device=DEV)
+    out1, _ = pkv.paged_attn_decode_mla_int8(*args, lse=lse1)
+    lse2 = torch.empty_like(lse1)
+    first, second, out2 = _lib.prepare_decode_mla_int8(*args, lse=lse2)
+    first()
+    second()
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
+    _check(c, out1, lse1, kdeq, rdeq, lens)
+
+
+def test_int8_mla_full_workload_sampled():
+    """The MLA workload's shape at full size (64 sequences of U{2048..8192}, 128 heads, bs
+    128) over the INT8 latent cache; the oracle checks four sequences."""
+    w = wl.WORKLOADS["mla_absorbed_bf16"]
+    L, _ = wl.sample_lengths(w, 0)
+    Lp = [int(x) + 1 for x in L]
+    say("int8 mla full-size workload (sampled sequences)")
+    c, dev, table, kdeq, rdeq, lens = _int8_mla_case(128, 128, Lp, seed=0)
+    lse = torch.empty((len(Lp), 128), dtype=torch.float32, device=DEV)
+    out, _ = pkv.paged_attn_decode_mla_int8(c.q, c.q_rope, dev["nc"], dev["rc"], dev["ns"], dev["rs"],
+                                            table, torch.from_numpy(lens).to(DEV), c.max_len_after,
+                                            c.w.scale, lse=lse)
+    torch.cuda.synchronize()
+    order = np.argsort(c.lens_after)
+    rows = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 3})
+    say(f"  max-abs error {_check(c, out, lse, kdeq, rdeq, lens, rows=rows):.3e}")

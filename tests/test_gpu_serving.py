@@ -42,7 +42,11 @@ def test_copy_blocks(shape, dtype):
     else:
         pool = torch.randn(shape, generator=g).to(dtype)
     nb = shape[0]
-    pairs = [(1, 0), (5, 7), (nb - 1, 3), (2, 2), (-1, 4), (6, nb), (8, nb - 2)]
+    # destinations distinct and never a source (the documented precondition); plus a
+    # same-block pair and two pairs outside the pool, which are skipped
+    pairs = [(1, 0), (5, 7), (nb - 1, 3), (2, 2), (-1, 6), (6, nb), (8, 4)]
+    dst = [t for s_, t in pairs if 0 <= s_ < nb and 0 <= t < nb and s_ != t]
+    assert len(set(dst)) == len(dst) and not set(dst) & {s_ for s_, t in pairs}
     say(f"copy_blocks {shape} {dtype}")
     d = pool.to(DEV)
     pkv.kv_cache_copy_blocks(d, torch.tensor(pairs, dtype=torch.int64, device=DEV))
