@@ -51,9 +51,11 @@ def dominant_kernel(w):
         return "gqa_stream_kernel", [CSRC + "gqa_attn.hip"] + MFMA_SOURCES
     if w.mode == "varlen":
         return "varlen_kernel<128>", [CSRC + "varlen_attn.hip"] + MFMA_SOURCES
-    if w.kv_dtype == "int8":
-        return "decode_int8_kernel", [CSRC + "int8_kv.hip", CSRC + "pkv_device.h"]
     group = w.num_q_heads // w.num_kv_heads
+    if w.kv_dtype == "int8":
+        if group > 4:   # the range-streaming kernel over the codes
+            return "gqa_stream_kernel", [CSRC + "gqa_attn.hip"] + MFMA_SOURCES
+        return "decode_int8_kernel", [CSRC + "int8_kv.hip", CSRC + "pkv_device.h"]
     if w.dtype == "bf16" and 4 <= group <= 16:
         rows_per_wave_load = 1024 // (2 * w.head_dim)
         name = ("gqa_stream_kernel" if w.block_size >= rows_per_wave_load and w.batch <= 1024
@@ -266,8 +268,9 @@ def step_description(w, path):
         return ("slot_mapping, kv_cache_write_int8_mla (quantizing write of nope and rope), "
                 "decode_mla_int8 split pass, combine")
     if int8_workload(w):
-        return ("slot_mapping, kv_cache_write_int8 (quantizing write), decode_int8 split pass, "
-                "combine")
+        kind = "range pass" if w.num_q_heads // w.num_kv_heads > 4 else "split pass"
+        return ("slot_mapping, kv_cache_write_int8 (quantizing write), decode_int8 %s, "
+                "combine" % kind)
     if w.q_tokens:
         return ("kv_cache_append (slot_mapping + write of the step's %d rows per sequence), "
                 "decode_mtp range pass, combine" % w.q_tokens)

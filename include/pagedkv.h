@@ -153,10 +153,11 @@ PKV_API int pkv_kv_cache_write_int8(const void* k_new, const void* v_new, void* 
 
 /*
  * Decode over the INT8 caches: as pkv_paged_attn_decode_ex without the new-token write (write
- * it first with pkv_kv_cache_write_int8), with bf16 q and out, 1..4 query heads per kv head,
- * head_dim 64 or 128.  score = scale * s_k * (q . q_k), out = sum softmax * s_v * q_v, in fp32.
- * window, stages and workspace as for pkv_paged_attn_decode_ex (pkv_decode_workspace_size
- * bytes suffice).
+ * it first with pkv_kv_cache_write_int8), with bf16 q and out, head_dim 64 or 128, and 1..16
+ * query heads per kv head; with 5..16 of them block_size must be at least 1024 / head_dim
+ * (8 or 16) and batch at most 1024, else PKV_ERR_UNSUPPORTED.  score = scale * s_k * (q . q_k),
+ * out = sum softmax * s_v * q_v, accumulated in fp32.  window, stages and workspace as for
+ * pkv_paged_attn_decode_ex (pkv_decode_workspace_size bytes suffice).
  */
 PKV_API int pkv_paged_attn_decode_int8(void* out, float* lse_out, const void* q, const void* k_cache,
                                const void* v_cache, const float* k_scale, const float* v_scale,

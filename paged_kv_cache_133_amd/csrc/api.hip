@@ -817,9 +817,17 @@ int pkv_paged_attn_decode_int8(void* out, float* lse_out, const void* q, const v
                                int64_t num_blocks, float softmax_scale, int32_t window, int32_t stages,
                                void* workspace, size_t workspace_bytes, void* stream) {
     if (stages < 1 || stages > 3) return fail(PKV_ERR_SHAPE, "decode_int8: stages must be 1, 2 or 3");
-    if (num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 && num_q_heads / num_kv_heads > 4)
-        return fail(PKV_ERR_UNSUPPORTED, "decode_int8: %d query heads per kv head (max 4)",
-                    num_q_heads / num_kv_heads);
+    // 1..4 query heads per kv head: the split kernel; 5..16: the range-streaming kernel, whose
+    // code loads need blocks of at least 1024 / head_dim keys.
+    const int group = num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 ? num_q_heads / num_kv_heads : 0;
+    const bool ranges = group > 4;
+    if (ranges && (group > 16 || (head_dim != 64 && head_dim != 128) || block_size <= 0 ||
+                   (block_size & (block_size - 1)) || block_size < 1024 / head_dim ||
+                   !pkv::gqa_stream_supported(PKV_BF16, group, head_dim, log2i(block_size), batch)))
+        return fail(PKV_ERR_UNSUPPORTED,
+                    "decode_int8: %d query heads per kv head needs at most 16, head_dim 64 or 128, "
+                    "block_size >= %d and batch <= 1024 (got head_dim %d, block_size %d, batch %d)",
+                    group, head_dim == 64 ? 16 : 8, head_dim, block_size, batch);
     pkv::DecodeParams p;
     pkv::DecodePlan plan{};
     bool idle = false;
@@ -827,8 +835,9 @@ int pkv_paged_attn_decode_int8(void* out, float* lse_out, const void* q, const v
     int rc = prepare_decode(p, plan, out, lse_out, q, nullptr, k_cache, v_cache, nullptr, block_table,
                             seq_lens_kv, batch, max_blocks_per_seq, max_seq_len_kv, num_q_heads,
                             num_kv_heads, head_dim, head_dim, 0, block_size, num_blocks, softmax_scale,
-                            PKV_BF16, workspace, workspace_bytes, &idle, window, false, true);
+                            PKV_BF16, workspace, workspace_bytes, &idle, window, ranges, true);
     if (rc != PKV_OK || idle) return rc;
+    if (ranges != (p.parts > 0)) return fail(PKV_ERR_UNSUPPORTED, "decode_int8: no kernel for this shape");
     if (!k_scale || !v_scale) return fail(PKV_ERR_NULL, "decode_int8: NULL scale array");
     if (!aligned16(k_scale) || !aligned16(v_scale))
         return fail(PKV_ERR_ALIGN, "decode_int8: scale arrays must be 16-byte aligned");

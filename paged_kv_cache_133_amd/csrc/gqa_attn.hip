@@ -61,6 +61,18 @@ struct GqaCfg {
     static_assert(2 * kDma < 64, "vmcnt range");
 };
 
+// 16 int8 codes as 16 bf16 (exact: |q| <= 127), codes 0-7 in lo, 8-15 in hi.
+__device__ __forceinline__ void codes_to_bf16(u32x4 v, u32x4& lo, u32x4& hi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float c0 = (float)(int)(int8_t)(v[i]), c1 = (float)(int)(int8_t)(v[i] >> 8);
+        const float c2 = (float)(int)(int8_t)(v[i] >> 16), c3 = (float)(int)(int8_t)(v[i] >> 24);
+        const uint32_t a = pack_bf16(c0, c1), b = pack_bf16(c2, c3);
+        if (i < 2) { lo[2 * i] = a; lo[2 * i + 1] = b; }
+        else { hi[2 * i - 4] = a; hi[2 * i - 3] = b; }
+    }
+}
+
 // ------------------------------------------------------------------ per-tile math
 // Scores of the tile in `stage`: full tiles keep the raw S^T entries; a tile that is not
 // wholly inside the key range [k_lo, k_end) scales them and sets keys outside it to -inf.
@@ -69,7 +81,7 @@ struct GqaCfg {
 template <int D>
 __device__ __forceinline__ float tile_scores(const uint8_t* stage, const bf16x8_t* qf, int n, int g,
                                              bool full, int kb, int k_lo, int k_end, float scale_log2,
-                                             float* sv) {
+                                             float* sv, const float* kscale = nullptr) {
     using C = GqaCfg<D>;
     f32x4 sacc[2];
 #pragma unroll
@@ -85,6 +97,12 @@ __device__ __forceinline__ float tile_scores(const uint8_t* stage, const bf16x8_
     }
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * C::kSteps, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * C::kSteps, 0);
+    if (kscale) {   // INT8 codes: the dot products times each key's K scale
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(kscale + 4 * g);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(kscale + 16 + 4 * g);
+        sacc[0] *= s0;
+        sacc[1] *= s1;
+    }
     float tmax;
     if (full) {
 #pragma unroll
@@ -106,17 +124,28 @@ __device__ __forceinline__ float tile_scores(const uint8_t* stage, const bf16x8_
 // P^T of the tile against the running max, then O^T += V^T . P^T (V half of `stage`).
 template <int D>
 __device__ __forceinline__ void tile_pv(const uint8_t* stage, RowState& st, bool full, const float* sv,
-                                        float scale_log2, int n, int g, f32x4* oacc) {
+                                        float scale_log2, int n, int g, f32x4* oacc,
+                                        const float* vscale = nullptr) {
     using C = GqaCfg<D>;
+    // INT8 codes: each key's V scale goes into its weight for the value sum (P' = p s_v; the
+    // masked keys' stale scales never reach it), while l sums the rounded p.
+    float vs[8];
+    if (vscale) {
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(vscale + 4 * g);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(vscale + 16 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { vs[e] = s0[e]; vs[4 + e] = s1[e]; }
+    }
     u32x4 pw;
     if (full) {
         const float mneg = -st.m;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-            const uint32_t w = pack_bf16(fast_exp2(__builtin_fmaf(sv[e], scale_log2, mneg)),
-                                         fast_exp2(__builtin_fmaf(sv[e + 1], scale_log2, mneg)));
+            const float e0 = fast_exp2(__builtin_fmaf(sv[e], scale_log2, mneg));
+            const float e1 = fast_exp2(__builtin_fmaf(sv[e + 1], scale_log2, mneg));
+            const uint32_t w = pack_bf16(e0, e1);
             st.l = dot2_bf16(w, kOnesBf16x2, st.l);
-            pw[e >> 1] = w;
+            pw[e >> 1] = vscale ? pack_bf16(e0 * vs[e], e1 * vs[e + 1]) : w;
         }
     } else {
 #pragma unroll
@@ -125,7 +154,9 @@ __device__ __forceinline__ void tile_pv(const uint8_t* stage, RowState& st, bool
             const float e1 = sv[e + 1] == -INFINITY ? 0.0f : fast_exp2(sv[e + 1] - st.m);
             const uint32_t w = pack_bf16(e0, e1);
             st.l = dot2_bf16(w, kOnesBf16x2, st.l);
-            pw[e >> 1] = w;
+            pw[e >> 1] = vscale ? pack_bf16(sv[e] == -INFINITY ? 0.0f : e0 * vs[e],
+                                            sv[e + 1] == -INFINITY ? 0.0f : e1 * vs[e + 1])
+                                : w;
         }
     }
     const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
@@ -215,14 +246,26 @@ constexpr int kStreamStages = 3;       // LDS stages: two tiles in flight while 
 constexpr int kStreamMaxBatch = 1024;  // sequences whose tile prefix fits LDS
 constexpr int kStreamWgs = 512;        // workgroups per launch (all kv heads): 2 per CU
 
-template <int D>
+// LDS of the range kernel.  bf16 caches: kStreamStages tile stages.  INT8 caches: as many
+// stages of codes as loaded (K rows of D bytes, V rows, then 1 KiB whose first 256 bytes are
+// the tile's 32 K and 32 V scales) and one bf16 tile the wave converts them into.
+template <int D, bool I8 = false>
 struct StreamCfg {
     using C = GqaCfg<D>;
+    static constexpr int kCodeHalf = kKeys * D;                       // K (or V) codes of a tile
+    static constexpr int kCodeStage = 2 * kCodeHalf + 1024;
+    static constexpr int kCodeRpi = 1024 / D;                         // code rows per wave load: 8 or 16
+    static constexpr int kCodeDmaHalf = kKeys / kCodeRpi;             // wave loads per half: 4 or 2
+    static constexpr int kDma = I8 ? 2 * kCodeDmaHalf + 1 : C::kDma;  // wave loads per tile
+    static constexpr int kStagesBytes = I8 ? kStreamStages * kCodeStage + C::kStage
+                                           : kStreamStages * C::kStage;
+    static constexpr int kBufOff = kStreamStages * kCodeStage;        // INT8: the bf16 tile
     static constexpr int kQSlot = 16 * C::kRowBytes;                  // one segment's query rows
-    static constexpr int kQOff = kStreamStages * C::kStage;
+    static constexpr int kQOff = kStagesBytes;
     static constexpr int kPreOff = kQOff + kStreamStages * kQSlot;    // [batch + 1] first tile
     static constexpr int kLenOff = kPreOff + (kStreamMaxBatch + 1) * 4 + 12;  // [batch] lengths
     static constexpr int kSmem = kLenOff + kStreamMaxBatch * 4;
+    static_assert(2 * kDma < 64, "vmcnt range");
 };
 
 // Start of range w of P over T tiles, and the range that holds tile x.
@@ -237,10 +280,11 @@ struct Cursor {
     int ks_last;                      // first key the last query token sees (>= ks)
 };
 
-template <int D, bool APPEND>
+template <int D, bool APPEND, bool I8 = false>
 __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
+    static_assert(!(APPEND && I8), "the INT8 cache is written beforehand by the quantizing writer");
     using C = GqaCfg<D>;
-    using S = StreamCfg<D>;
+    using S = StreamCfg<D, I8>;
     constexpr int kStg = kStreamStages;
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::kSmem];
     int32_t* s_pre = reinterpret_cast<int32_t*>(smem + S::kPreOff);
@@ -369,6 +413,14 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         lchunk[j] = (uint32_t)swz<C::kRowChunks, C::kRowShift>(j * C::kRpi + lrow, lane % C::kRowChunks) * 16u;
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k_cache) + kvh * D * 2;
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v_cache) + kvh * D * 2;
+    // INT8: code rows of D bytes (this kv head's slice of a slot of hkv D bytes), 16 bytes
+    // per lane, kept in the order loaded (the conversion applies the swizzle).
+    const uint32_t crow_bytes = (uint32_t)(p.hkv * D);
+    const int crow = lane / (D / 16);
+    const uint32_t cchunk = (uint32_t)(lane % (D / 16)) * 16u;
+    const uint32_t cvoff = (uint32_t)crow * crow_bytes + cchunk;
+    const uint8_t* kcodes = reinterpret_cast<const uint8_t*>(p.k_cache) + kvh * D;
+    const uint8_t* vcodes = reinterpret_cast<const uint8_t*>(p.v_cache) + kvh * D;
     const int bs_mask = (1 << p.bs_log2) - 1;
     const int32_t last_block = (int32_t)(p.num_blocks - 1);
     uint8_t* const qring = smem + S::kQOff;
@@ -392,7 +444,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
     auto issue = [&](int u) {         // loads of local tile u (prep(u) done)
         const int x = x0 + u;
         const int kb = ic.ksa + (x - ic.pre) * kKeys;
-        uint8_t* stage = smem + (u % kStg) * C::kStage;
+        uint8_t* stage = smem + (u % kStg) * (I8 ? S::kCodeStage : C::kStage);
         if (x == ic.pre || u == 0) {  // first tile of a segment: its query rows first
             // LDS row c of the slot is column c: query token c / G, head c % G of the kv
             // head (bytes past the NC rows re-read the last row).
@@ -404,6 +456,51 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
                 const int64_t qrow = ((int64_t)ic.b * qn + ct) * p.hq + kvh * G + (c - ct * G);
                 lds_dma16(qbase + qrow * C::kRowBytes + (byte & (C::kRowBytes - 1)), qdst + j * 1024);
             }
+        }
+        if constexpr (I8) {
+            // Codes: wave load j of a half takes rows j kCodeRpi .. (one block: blocks hold
+            // at least kCodeRpi keys; its entry is pe[2 j]).  Then one load of the scales:
+            // lanes 0-7 the K scales of keys 4 i .. 4 i + 3, lanes 8-15 the V scales (a run
+            // of 4 in the [block][kv head][offset] layout), the others re-read lane 0's.
+            const int L = ic.L;
+            const bool whole = x + 1 < ic.end;
+            const int64_t last_slot = ((int64_t)min(max(pe_last, 0), last_block) << p.bs_log2) | ((L - 1) & bs_mask);
+#pragma unroll
+            for (int j = 0; j < S::kCodeDmaHalf; ++j) {
+                const uint32_t blk = (uint32_t)min(max(pe[2 * j], 0), last_block);
+                const int key0 = kb + j * S::kCodeRpi;
+                if (whole) {
+                    const uint64_t off = (uint64_t)(((uint64_t)blk << p.bs_log2) | (uint32_t)(key0 & bs_mask)) * crow_bytes;
+                    lds_dma16_s(kcodes + off, cvoff, stage + j * 1024);
+                    lds_dma16_s(vcodes + off, cvoff, stage + S::kCodeHalf + j * 1024);
+                } else {              // rows past the end re-read the last key
+                    const int key = key0 + crow;
+                    const int64_t slot = key < L ? (((int64_t)blk << p.bs_log2) | (key & bs_mask)) : last_slot;
+                    lds_dma16(kcodes + slot * crow_bytes + cchunk, stage + j * 1024);
+                    lds_dma16(vcodes + slot * crow_bytes + cchunk, stage + S::kCodeHalf + j * 1024);
+                }
+            }
+            {
+                const int gi = lane < 16 ? (lane & 7) : 0;      // 4-key group of this lane
+                // its block's entry pe[4 gi / kRpi], by a tree of selects on the index bits
+                // (a chain of equality selects becomes a scratch-memory lookup)
+                const int e_idx = (4 * gi) / C::kRpi;
+                int32_t tv[C::kDmaHalf];
+#pragma unroll
+                for (int jj = 0; jj < C::kDmaHalf; ++jj) tv[jj] = pe[jj];
+#pragma unroll
+                for (int lv = 1; lv < C::kDmaHalf; lv <<= 1)
+#pragma unroll
+                    for (int jj = 0; jj + lv < C::kDmaHalf; jj += 2 * lv) tv[jj] = (e_idx & lv) ? tv[jj + lv] : tv[jj];
+                const int32_t e = tv[0];
+                const int key = kb + 4 * gi;
+                const int64_t slot = key < L ? (((int64_t)min(max(e, 0), last_block) << p.bs_log2) | (key & bs_mask))
+                                             : ((int64_t)min(max(pe_last, 0), last_block) << p.bs_log2) | (((L - 1) & ~3) & bs_mask);
+                const int64_t sidx = (((slot >> p.bs_log2) * p.hkv + kvh) << p.bs_log2) | (slot & bs_mask);
+                const float* sc = (lane >= 8 && lane < 16) ? p.v_scale : p.k_scale;
+                lds_dma16(sc + sidx, stage + 2 * S::kCodeHalf);
+            }
+            return;
         }
         if (x + 1 < ic.end) {         // full tile: SGPR base per wave load, constant lane offsets
 #pragma unroll
@@ -443,6 +540,40 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < kStg - 1; ++u) feed(u);
 
+    // INT8: the codes of tile t (this wave's own loads) into the bf16 tile, logical 16-byte
+    // chunk c of row r at physical chunk swz(r, c) as the products read it; LDS accesses of
+    // one wave complete in order, so the previous tile's reads of it are done first.
+    // The bf16 tile the products read, and (INT8) the tile's K and V scales.
+    auto tile_of = [&](int t) -> const uint8_t* {
+        return I8 ? smem + S::kBufOff : smem + (t % kStg) * C::kStage;
+    };
+    auto kscale_of = [&](int t) -> const float* {
+        return I8 ? reinterpret_cast<const float*>(smem + (t % kStg) * S::kCodeStage + 2 * S::kCodeHalf) : nullptr;
+    };
+    auto vscale_of = [&](int t) -> const float* {
+        return I8 ? reinterpret_cast<const float*>(smem + (t % kStg) * S::kCodeStage + 2 * S::kCodeHalf) + kKeys
+                  : nullptr;
+    };
+    auto convert = [&](int t) {
+        const uint8_t* cs = smem + (t % kStg) * S::kCodeStage;
+        uint8_t* bf = smem + S::kBufOff;
+        constexpr int kUnits = kKeys * D / 16;            // 16-code units per half
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < kUnits / 64; ++i) {
+                const int ui = lane + 64 * i;
+                const int r = ui / (D / 16);
+                const int u16 = ui % (D / 16);
+                u32x4 lo, hi;
+                codes_to_bf16(*reinterpret_cast<const u32x4*>(cs + h * S::kCodeHalf + r * D + u16 * 16), lo, hi);
+                uint8_t* row = bf + h * C::kHalf + r * C::kRowBytes;
+                *reinterpret_cast<u32x4*>(row + swz<C::kRowChunks, C::kRowShift>(r, 2 * u16) * 16) = lo;
+                *reinterpret_cast<u32x4*>(row + swz<C::kRowChunks, C::kRowShift>(r, 2 * u16 + 1) * 16) = hi;
+            }
+        }
+    };
+
     // Consume side: one segment (the part of a sequence inside the range) at a time.
     Cursor cc = cursor_at(b0);
     int t = 0;
@@ -451,7 +582,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         const int tend = min(cc.end, x1) - x0;         // local end of the segment
         const bool whole = cc.pre >= x0 && cc.end <= x1;
         const int slot = t == 0 ? 0 : 1;               // partial state: first or last segment
-        wait_tile<C::kDma>(min(ntw - 1 - t, kStg - 2));
+        wait_tile<S::kDma>(min(ntw - 1 - t, kStg - 2));
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         // This segment's query rows (Q^T fragments: k-step s covers dims 32 s .. 32 s + 31;
         // lane (g, n) holds 8 of them of head n, zero for columns past G).
@@ -476,22 +607,23 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         // touched by products.
         while (t < tend) {
             for (; t < tend; ++t) {
-                wait_tile<C::kDma>(min(ntw - 1 - t, kStg - 2));
+                wait_tile<S::kDma>(min(ntw - 1 - t, kStg - 2));
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 feed(t + kStg - 1);
+                if constexpr (I8) convert(t);
                 const int kb = cc.ksa + (x0 + t - cc.pre) * kKeys;
                 // every column sees the whole tile: past the last token's window start and
                 // before the first token's end
                 full = kb >= cc.ks_last && kb + kKeys <= cc.L - (qn - 1);
-                tmax = tile_scores<D>(smem + (t % kStg) * C::kStage, qf, n, g, full, kb,
+                tmax = tile_scores<D>(tile_of(t), qf, n, g, full, kb,
                                       window_start(cc.L - back, p.window), cc.L - back,
-                                      p.scale_log2, sv);
+                                      p.scale_log2, sv, kscale_of(t));
                 if (__any(must_rescale(st, tmax))) break;
-                tile_pv<D>(smem + (t % kStg) * C::kStage, st, full, sv, p.scale_log2, n, g, oacc);
+                tile_pv<D>(tile_of(t), st, full, sv, p.scale_log2, n, g, oacc, vscale_of(t));
             }
             if (t >= tend) break;
             rescale<D>(st, tmax, oacc);
-            tile_pv<D>(smem + (t % kStg) * C::kStage, st, full, sv, p.scale_log2, n, g, oacc);
+            tile_pv<D>(tile_of(t), st, full, sv, p.scale_log2, n, g, oacc, vscale_of(t));
             ++t;
         }
         float l_tot = st.l + __shfl_xor(st.l, 16, 64);
@@ -793,6 +925,13 @@ bool gqa_stream_shape_supported(int head_dim, int bs_log2, int batch) {
 }
 
 int gqa_stream_parts(int num_kv_heads) { return num_kv_heads >= kStreamWgs ? 1 : kStreamWgs / num_kv_heads; }
+
+hipError_t launch_gqa_decode_int8(const DecodeParams& p, int head_dim, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)p.hkv * p.parts));
+    if (head_dim == 64) hipLaunchKernelGGL((gqa_stream_kernel<64, false, true>), grid, dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((gqa_stream_kernel<128, false, true>), grid, dim3(64), 0, s, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_gqa_decode(const DecodeParams& p, int head_dim, hipStream_t s) {
     if (p.parts > 0) {

@@ -349,6 +349,7 @@ hipError_t launch_kv_write_int8_mla(const QuantWriteParams& p, int in_dtype, hip
 }
 
 hipError_t launch_decode_int8(const DecodeParams& p, int head_dim, hipStream_t s) {
+    if (p.parts > 0) return launch_gqa_decode_int8(p, head_dim, s);
     const dim3 grid((unsigned)((int64_t)p.hkv * p.batch * p.max_splits));
     const int gp = p.group <= 1 ? 1 : (p.group <= 2 ? 2 : 4);
     if (head_dim == 64) {

@@ -175,8 +175,12 @@ bool gqa_stream_supported(int dtype, int group, int head_dim, int bs_log2, int b
 int gqa_stream_parts(int num_kv_heads);
 hipError_t launch_gqa_decode(const DecodeParams& p, int head_dim, hipStream_t s);
 hipError_t launch_gqa_stream_combine(const DecodeParams& p, int head_dim, hipStream_t s);
-// Decode over the INT8 caches (p.k_scale / p.v_scale set): bf16 queries and output,
-// 1..4 query heads per kv head, split-KV with the generic combine.
+// The range-streaming kernel over INT8 codes (p.parts > 0, p.k_scale / p.v_scale set,
+// blocks of at least 1024 / head_dim keys); its combine is launch_gqa_stream_combine.
+hipError_t launch_gqa_decode_int8(const DecodeParams& p, int head_dim, hipStream_t s);
+// Decode over the INT8 caches (p.k_scale / p.v_scale set): bf16 queries and output.
+// 1..4 query heads per kv head: split-KV with the generic combine; p.parts > 0 (5..16):
+// launch_gqa_decode_int8.
 hipError_t launch_decode_int8(const DecodeParams& p, int head_dim, hipStream_t s);
 
 // Merge of split partials (second launch of a split decode).

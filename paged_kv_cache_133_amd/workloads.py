@@ -107,6 +107,13 @@ LLAMA7B_INT8 = Workload("llama7b_mha_int8", "decode", 32, 32, 32, 128, 128, 0, 1
                         "scale per token and head): B=32, 32 heads, head_dim 128, bs 16, kv "
                         "lengths U{512..2048}, bf16 queries", kv_dtype="int8")
 
+# The long-context GQA shape over an INT8 cache (the same lengths as the bf16 one).
+GQA_LONG_INT8 = Workload("gqa_long_int8", "decode", 64, 64, 8, 128, 128, 0, 128, "bf16",
+                         1.0 / math.sqrt(128.0), 257,
+                         "GQA long-context decode over an INT8 KV cache (codes + fp32 scale per "
+                         "token and head): B=64, 64 q / 8 kv heads, head_dim 128, bs 128, kv "
+                         "lengths log-uniform [1024, 32768], bf16 queries", kv_dtype="int8")
+
 # The MLA shape over an INT8 latent cache (the same lengths as the bf16 MLA workload).
 MLA_INT8 = Workload("mla_absorbed_int8", "mla", 64, 128, 1, 512, 512, 64, 128, "bf16",
                     1.0 / math.sqrt(576.0), 65,
@@ -115,7 +122,7 @@ MLA_INT8 = Workload("mla_absorbed_int8", "mla", 64, 128, 1, 512, 512, 64, 128, "
                     "queries", kv_dtype="int8")
 
 WORKLOADS = {w.name: w for w in (TINY, LLAMA7B, GQA_LONG, MLA, VARLEN, SWA_DECODE, MTP_DECODE,
-                                 LLAMA7B_INT8, MLA_INT8)}
+                                 LLAMA7B_INT8, GQA_LONG_INT8, MLA_INT8)}
 
 
 def sample_lengths(w: Workload, seed: int) -> tuple[np.ndarray, np.ndarray]:
@@ -126,7 +133,7 @@ def sample_lengths(w: Workload, seed: int) -> tuple[np.ndarray, np.ndarray]:
         return np.array([37, 130], np.int64), np.ones(2, np.int64)
     if w.name in (LLAMA7B.name, "llama7b_mha_int8"):
         return rng.integers(512, 2048, size=B, endpoint=True), np.ones(B, np.int64)
-    if w.name == GQA_LONG.name:
+    if w.name in (GQA_LONG.name, "gqa_long_int8"):
         u = rng.uniform(math.log(1024.0), math.log(32768.0), size=B)
         return np.clip(np.round(np.exp(u)), 1024, 32768).astype(np.int64), np.ones(B, np.int64)
     if w.name in (MLA.name, "mla_absorbed_int8"):

@@ -8,8 +8,9 @@ import torch
 
 import paged_kv_cache_133_amd as pkv
 from oracle import oracle
+from paged_kv_cache_133_amd import _lib
 from paged_kv_cache_133_amd import workloads as wl
-from tests.gpu_common import say
+from tests.gpu_common import LSE_ABS_MFMA, say
 from tests.helpers import host
 
 pytestmark = pytest.mark.gpu
@@ -98,13 +99,26 @@ def _check(c, out, lse, kdeq, vdeq, window, rows=None):
     got = out.float().cpu().numpy()[idx]
     err = np.abs(got - o).max()
     assert err <= 2e-2, f"max-abs error {err:.3e}"
-    lerr = (np.abs(lse.cpu().numpy()[idx] - ol) / np.maximum(1.0, np.abs(ol))).max()
-    assert lerr <= 1e-4, f"lse error {lerr:.3e}"
+    _check_lse(c, lse.cpu().numpy()[idx], ol)
     return err
 
 
+def _check_lse(c, got, ol):
+    """1..4 query heads per kv head: the split kernel sums fp32 weights (relative 1e-4);
+    5..16: the matrix-core kernel sums bf16-rounded weights (absolute LSE_ABS_MFMA)."""
+    if c.w.num_q_heads // c.w.num_kv_heads > 4:
+        lerr = np.abs(got - ol).max()
+        assert lerr <= LSE_ABS_MFMA, f"lse error {lerr:.3e}"
+    else:
+        lerr = (np.abs(got - ol) / np.maximum(1.0, np.abs(ol))).max()
+        assert lerr <= 1e-4, f"lse error {lerr:.3e}"
+
+
 @pytest.mark.parametrize("shape", [(32, 32, 128, 16), (8, 2, 64, 1), (16, 4, 128, 128),
-                                   (4, 1, 128, 32), (12, 4, 64, 64)],
+                                   (4, 1, 128, 32), (12, 4, 64, 64),
+                                   # 5..16 query heads per kv head: the range-streaming kernel
+                                   (32, 4, 128, 16), (64, 4, 64, 16), (40, 8, 128, 8),
+                                   (16, 2, 128, 128), (48, 4, 64, 32)],
                          ids=lambda s: "hq%d_hkv%d_d%d_bs%d" % s)
 @pytest.mark.parametrize("window", [0, 100])
 def test_int8_decode(shape, window):
@@ -135,3 +149,88 @@ def test_int8_headline_workload_sampled():
                                         lse=lse)
     torch.cuda.synchronize()
     _check(c, out, lse, kdeq, vdeq, 0, rows=list(range(0, 32, 4)))
+
+
+@pytest.mark.parametrize("shape", [(32, 4, 128, 16), (64, 4, 64, 16), (12, 4, 128, 32)],
+                         ids=lambda s: "hq%d_hkv%d_d%d_bs%d" % s)
+def test_int8_decode_padding_rows(shape):
+    """Rows with seq_lens_kv = 0 (padding): output 0 and lse -inf; the others as the oracle
+    says (both kernels: 12:4 the split one, 8 and 16 per kv head the range one)."""
+    Hq, Hkv, D, bs = shape
+    L = [40, 700, 9, 2100, 64, 33]
+    say(f"int8 decode padding rows {shape}")
+    c, dev, table, kdeq, vdeq = _int8_case(Hq, Hkv, D, bs, L, seed=Hq + D)
+    lens = c.lens_after_tensor(DEV).clone()
+    pad = [0, 3]
+    lens[pad] = 0
+    lse = torch.full((len(L), Hq), 7.0, dtype=torch.float32, device=DEV)
+    out, _ = pkv.paged_attn_decode_int8(c.q, dev["kc"], dev["vc"], dev["ks"], dev["vs"], table,
+                                        lens, c.max_len_after, c.w.scale, lse=lse)
+    torch.cuda.synchronize()
+    got, got_lse = out.float().cpu(), lse.cpu()
+    for b in pad:
+        assert (got[b] == 0).all() and torch.isneginf(got_lse[b]).all()
+    _check(c, out, lse, kdeq, vdeq, 0, rows=[1, 2, 4, 5])
+
+
+def test_int8_two_passes_equal_one_ranges():
+    """The range pass and the combine as two calls give the one-call result bit for bit
+    (8 query heads per kv head)."""
+    L = [3000, 5, 1400, 64, 65, 2222, 1, 800]
+    c, dev, table, kdeq, vdeq = _int8_case(32, 4, 128, 16, L, seed=11)
+    la = c.lens_after_tensor(DEV)
+    args = (c.q, dev["kc"], dev["vc"], dev["ks"], dev["vs"], table, la, c.max_len_after, c.w.scale)
+    lse1 = torch.empty((len(L), 32), dtype=torch.float32, device=DEV)
+    out1, _ = pkv.paged_attn_decode_int8(*args, lse=lse1)
+    lse2 = torch.empty_like(lse1)
+    first, second, out2 = _lib.prepare_decode_int8(*args, lse=lse2)
+    first()
+    second()
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
+    _check(c, out1, lse1, kdeq, vdeq, 0)
+
+
+def test_int8_gqa_long_workload_sampled():
+    """The long-context GQA workload over the INT8 cache at full size (B = 64, 64 q / 8 kv
+    heads, bs 128, lengths log-uniform [1024, 32768]).  The pool is seeded random codes and
+    scales (quantizing 600M elements on the host would take minutes; the writer has its own
+    bit-exact tests); the oracle dequantizes the blocks of four sequences and checks them."""
+    w = wl.WORKLOADS["gqa_long_int8"]
+    L, _ = wl.sample_lengths(w, 0)
+    say("int8 gqa_long workload (sampled sequences)")
+    c = wl.make_case(w, L, [1] * w.batch, seed=0, device=DEV, poison=False)
+    nb, bs, hkv, d = c.cache_k.shape
+    gen = torch.Generator(device=DEV).manual_seed(1234)
+    codes = [torch.randint(-127, 128, (nb, bs, hkv, d), generator=gen, device=DEV, dtype=torch.int8)
+             for _ in range(2)]
+    scales = [torch.rand((nb, hkv, bs), generator=gen, device=DEV) * 0.03 + 1e-3 for _ in range(2)]
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=DEV)
+    out, _ = pkv.paged_attn_decode_int8(c.q, codes[0], codes[1], scales[0], scales[1],
+                                        c.table_tensor(DEV), c.lens_after_tensor(DEV),
+                                        c.max_len_after, c.w.scale, lse=lse)
+    torch.cuda.synchronize()
+    order = np.argsort(c.lens_after)
+    rows = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 3})
+    # a compact pool of the sampled sequences' blocks, the table renumbered into it
+    used = [c.block_table[b][:(int(c.lens_after[b]) + bs - 1) // bs] for b in rows]
+    blocks = np.concatenate(used).astype(np.int64)
+    sel = torch.from_numpy(blocks).to(DEV)
+    deq = []
+    for cd, sc in zip(codes, scales):
+        q8 = cd[sel].cpu().numpy()                                   # [n, bs, hkv, d]
+        s32 = sc[sel].permute(0, 2, 1).contiguous().cpu().numpy()    # [n, bs, hkv]
+        deq.append(oracle.dequantize_rows(q8, s32))
+    table = np.zeros((len(rows), max(len(u) for u in used)), np.int32)
+    k = 0
+    for i, u in enumerate(used):
+        table[i, :len(u)] = np.arange(k, k + len(u))
+        k += len(u)
+    cu = np.arange(len(rows) + 1, dtype=np.int32)
+    o, ol = oracle.paged_attention(oracle.widen(host(c.q))[rows], deq[0], deq[1], table, cu,
+                                   c.lens_after[rows], c.w.scale, False)
+    err = float(np.abs(out.float().cpu().numpy()[rows] - o).max())
+    assert err <= 2e-2, f"max-abs error {err:.3e}"
+    _check_lse(c, lse.cpu().numpy()[rows], ol)
+    say(f"  max-abs error {err:.3e}")
