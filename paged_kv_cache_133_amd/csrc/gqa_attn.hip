@@ -243,6 +243,7 @@ __device__ __forceinline__ void append_row(const DecodeParams& p, int b, int kvh
 
 // ================================================================== range-streaming kernel
 constexpr int kStreamStages = 3;       // LDS stages: two tiles in flight while one is used
+constexpr int kStreamCodeStages = 3;   // INT8 code stages (tiles of half the bytes)
 constexpr int kStreamMaxBatch = 1024;  // sequences whose tile prefix fits LDS
 constexpr int kStreamWgs = 512;        // workgroups per launch (all kv heads): 2 per CU
 
@@ -257,12 +258,12 @@ struct StreamCfg {
     static constexpr int kCodeRpi = 1024 / D;                         // code rows per wave load: 8 or 16
     static constexpr int kCodeDmaHalf = kKeys / kCodeRpi;             // wave loads per half: 4 or 2
     static constexpr int kDma = I8 ? 2 * kCodeDmaHalf + 1 : C::kDma;  // wave loads per tile
-    static constexpr int kStagesBytes = I8 ? kStreamStages * kCodeStage + C::kStage
-                                           : kStreamStages * C::kStage;
-    static constexpr int kBufOff = kStreamStages * kCodeStage;        // INT8: the bf16 tile
+    static constexpr int kStages = I8 ? kStreamCodeStages : kStreamStages;
+    static constexpr int kStagesBytes = I8 ? kStages * kCodeStage + C::kStage : kStages * C::kStage;
+    static constexpr int kBufOff = kStages * kCodeStage;              // INT8: the bf16 tile
     static constexpr int kQSlot = 16 * C::kRowBytes;                  // one segment's query rows
     static constexpr int kQOff = kStagesBytes;
-    static constexpr int kPreOff = kQOff + kStreamStages * kQSlot;    // [batch + 1] first tile
+    static constexpr int kPreOff = kQOff + kStages * kQSlot;          // [batch + 1] first tile
     static constexpr int kLenOff = kPreOff + (kStreamMaxBatch + 1) * 4 + 12;  // [batch] lengths
     static constexpr int kSmem = kLenOff + kStreamMaxBatch * 4;
     static_assert(2 * kDma < 64, "vmcnt range");
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
     static_assert(!(APPEND && I8), "the INT8 cache is written beforehand by the quantizing writer");
     using C = GqaCfg<D>;
     using S = StreamCfg<D, I8>;
-    constexpr int kStg = kStreamStages;
+    constexpr int kStg = S::kStages;
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::kSmem];
     int32_t* s_pre = reinterpret_cast<int32_t*>(smem + S::kPreOff);
     int32_t* s_len = reinterpret_cast<int32_t*>(smem + S::kLenOff);
@@ -557,16 +558,24 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
     auto convert = [&](int t) {
         const uint8_t* cs = smem + (t % kStg) * S::kCodeStage;
         uint8_t* bf = smem + S::kBufOff;
-        constexpr int kUnits = kKeys * D / 16;            // 16-code units per half
+        constexpr int kUnits = kKeys * D / 16 / 64;       // 16-code units per lane and half
+        // All reads first: a store to the bf16 tile may alias a later read as far as the
+        // compiler knows, so interleaved it would wait out each read's latency.
+        u32x4 raw[2][kUnits];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < kUnits; ++i)
+                raw[h][i] = *reinterpret_cast<const u32x4*>(cs + h * S::kCodeHalf + (lane + 64 * i) * 16);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int i = 0; i < kUnits / 64; ++i) {
+            for (int i = 0; i < kUnits; ++i) {
                 const int ui = lane + 64 * i;
                 const int r = ui / (D / 16);
                 const int u16 = ui % (D / 16);
                 u32x4 lo, hi;
-                codes_to_bf16(*reinterpret_cast<const u32x4*>(cs + h * S::kCodeHalf + r * D + u16 * 16), lo, hi);
+                codes_to_bf16(raw[h][i], lo, hi);
                 uint8_t* row = bf + h * C::kHalf + r * C::kRowBytes;
                 *reinterpret_cast<u32x4*>(row + swz<C::kRowChunks, C::kRowShift>(r, 2 * u16) * 16) = lo;
                 *reinterpret_cast<u32x4*>(row + swz<C::kRowChunks, C::kRowShift>(r, 2 * u16 + 1) * 16) = hi;

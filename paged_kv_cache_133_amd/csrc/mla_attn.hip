@@ -283,28 +283,37 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
     auto convert = [&](int t) {
         const uint8_t* cs = smem + (t % I::kCodeStages) * I::kCodeStage;
         uint8_t* bf = smem + I::kBufOff + (t & 1) * I::kBuf;
+        // All reads first: a store to the bf16 buffer may alias a later read as far as the
+        // compiler knows, so interleaved it would wait out each read's latency.
+        const uint8_t* aux = cs + I::kNopeCodes + wid_u * I::kAux;
+        u32x4 raw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ci = lane + 64 * i;
+            raw[i] = *reinterpret_cast<const u32x4*>(cs + (8 * wid_u + (ci >> 5)) * 512 + (ci & 31) * 16);
+        }
+        const u32x4 rraw = *reinterpret_cast<const u32x4*>(aux + (lane & 31) * 16);
+        const float sc_in = *reinterpret_cast<const float*>(aux + 512 + ((lane - 32) & 15) * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {          // nope: 8 rows x 32 chunks of 16 codes
             const int ci = lane + 64 * i;
             const int r = 8 * wid_u + (ci >> 5);
             const int c16 = ci & 31;
             u32x4 lo, hi;
-            codes_to_bf16(*reinterpret_cast<const u32x4*>(cs + r * 512 + c16 * 16), lo, hi);
+            codes_to_bf16(raw[i], lo, hi);
             *reinterpret_cast<u32x4*>(bf + r * C::kNopeRow + c16 * 32) = lo;
             *reinterpret_cast<u32x4*>(bf + r * C::kNopeRow + c16 * 32 + 16) = hi;
         }
-        const uint8_t* aux = cs + I::kNopeCodes + wid_u * I::kAux;
         if (lane < 32) {                       // rope: row 8 w + lane / 4, dims 16 (lane % 4) ..
             const int r = 8 * wid_u + (lane >> 2);
             const int c4 = lane & 3;
             u32x4 lo, hi;
-            codes_to_bf16(*reinterpret_cast<const u32x4*>(aux + lane * 16), lo, hi);
+            codes_to_bf16(rraw, lo, hi);
             *reinterpret_cast<u32x4*>(bf + C::kRopeBase + r * 128 + rope_chunk(r, 2 * c4) * 16) = lo;
             *reinterpret_cast<u32x4*>(bf + C::kRopeBase + r * 128 + rope_chunk(r, 2 * c4 + 1) * 16) = hi;
         } else if (lane < 48) {                // scales: 8 nope, then 8 rope
             const int qq = lane - 32;
-            const float sc = *reinterpret_cast<const float*>(aux + 512 + qq * 4);
-            *reinterpret_cast<float*>(bf + C::kStage + ((qq >> 3) * kKeys + 8 * wid_u + (qq & 7)) * 4) = sc;
+            *reinterpret_cast<float*>(bf + C::kStage + ((qq >> 3) * kKeys + 8 * wid_u + (qq & 7)) * 4) = sc_in;
         }
     };
 
