@@ -254,7 +254,10 @@ size_t pkv_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num
         return 0;
     if (num_kv_heads == 1 && head_dim_v == 512)   // the MLA-absorbed shape
         return pkv::plan_mla(batch, num_q_heads, head_dim_v, max_seq_len_kv).ws_bytes;
-    return pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim_v, max_seq_len_kv).ws_bytes;
+    // the larger of the bf16 and INT8 plans (INT8 runs more ranges per kv head)
+    const size_t a = pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim_v, max_seq_len_kv).ws_bytes;
+    const size_t b = pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim_v, max_seq_len_kv, true).ws_bytes;
+    return a > b ? a : b;
 }
 
 }  // extern "C"

@@ -243,13 +243,20 @@ __device__ __forceinline__ void append_row(const DecodeParams& p, int b, int kvh
 
 // ================================================================== range-streaming kernel
 constexpr int kStreamStages = 3;       // LDS stages: two tiles in flight while one is used
-constexpr int kStreamCodeStages = 3;   // INT8 code stages (tiles of half the bytes)
+constexpr int kStreamCodeStages = 2;   // INT8 code stages: one tile in flight while one is used
 constexpr int kStreamMaxBatch = 1024;  // sequences whose tile prefix fits LDS
 constexpr int kStreamWgs = 512;        // workgroups per launch (all kv heads): 2 per CU
+constexpr int kStreamWgsI8 = 1024;     // INT8: 4 per CU, one wave on every SIMD
+// bf16 in the INT8 layout (two stages, query rows in registers, 4 per CU): 4 % faster on the
+// 32K-context GQA shape, but the merge of 4 times as many ranges makes the two-token MTP
+// step slower; off.
+constexpr bool kStreamCompactBf16 = false;
 
-// LDS of the range kernel.  bf16 caches: kStreamStages tile stages.  INT8 caches: as many
-// stages of codes as loaded (K rows of D bytes, V rows, then 1 KiB whose first 256 bytes are
-// the tile's 32 K and 32 V scales) and one bf16 tile the wave converts them into.
+// LDS of the range kernel.  bf16 caches: kStreamStages tile stages, a ring of query rows per
+// stage, the tile prefix and the lengths.  INT8 caches (under 40 KiB, for four workgroups per
+// CU): stages of codes as loaded (K rows of D bytes, V rows, then 1 KiB whose first 256 bytes
+// are the tile's 32 K and 32 V scales), one bf16 tile the wave converts them into, and the
+// tile prefix; the query rows stay in registers and the lengths are read from memory.
 template <int D, bool I8 = false>
 struct StreamCfg {
     using C = GqaCfg<D>;
@@ -258,14 +265,16 @@ struct StreamCfg {
     static constexpr int kCodeRpi = 1024 / D;                         // code rows per wave load: 8 or 16
     static constexpr int kCodeDmaHalf = kKeys / kCodeRpi;             // wave loads per half: 4 or 2
     static constexpr int kDma = I8 ? 2 * kCodeDmaHalf + 1 : C::kDma;  // wave loads per tile
-    static constexpr int kStages = I8 ? kStreamCodeStages : kStreamStages;
+    static constexpr bool kCompact = I8 || kStreamCompactBf16;   // Q in registers, no lengths
+    static constexpr int kStages = kCompact ? kStreamCodeStages : kStreamStages;
     static constexpr int kStagesBytes = I8 ? kStages * kCodeStage + C::kStage : kStages * C::kStage;
     static constexpr int kBufOff = kStages * kCodeStage;              // INT8: the bf16 tile
-    static constexpr int kQSlot = 16 * C::kRowBytes;                  // one segment's query rows
+    static constexpr int kQSlot = kCompact ? 0 : 16 * C::kRowBytes;   // one segment's query rows
     static constexpr int kQOff = kStagesBytes;
     static constexpr int kPreOff = kQOff + kStages * kQSlot;          // [batch + 1] first tile
     static constexpr int kLenOff = kPreOff + (kStreamMaxBatch + 1) * 4 + 12;  // [batch] lengths
-    static constexpr int kSmem = kLenOff + kStreamMaxBatch * 4;
+    static constexpr int kSmem = kLenOff + (kCompact ? 0 : kStreamMaxBatch * 4);
+    static_assert(!kCompact || kSmem <= 40 * 1024, "four workgroups per CU");
     static_assert(2 * kDma < 64, "vmcnt range");
 };
 
@@ -289,7 +298,13 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
     constexpr int kStg = S::kStages;
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::kSmem];
     int32_t* s_pre = reinterpret_cast<int32_t*>(smem + S::kPreOff);
-    int32_t* s_len = reinterpret_cast<int32_t*>(smem + S::kLenOff);
+    int32_t* s_len = reinterpret_cast<int32_t*>(smem + S::kLenOff);   // bf16 only
+    // Visible length of sequence b: per lane, and (b uniform) in SGPRs.
+    auto lane_len = [&](int b) { return S::kCompact ? min(p.seq_lens[b], p.len_cap) : s_len[b]; };
+    auto uni_len = [&](int b) {
+        return S::kCompact ? min(uniform_load(p.seq_lens + b), p.len_cap)
+                           : __builtin_amdgcn_readfirstlane(s_len[b]);
+    };
 
     const int lane = threadIdx.x;
     const int n = lane & 15;          // head column of this lane; A-operand row
@@ -322,7 +337,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         }
         if (b < p.batch) {
             s_pre[b] = total + v - nt;
-            s_len[b] = L;
+            if constexpr (!S::kCompact) s_len[b] = L;
             if (blockIdx.x == 0) p.tile_prefix[b] = total + v - nt;
         }
         total += __shfl(v, 63, 64);
@@ -344,7 +359,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         bool empty = false, mine = false;
         if (b < p.batch) {
             const int e = s_pre[b + 1];
-            empty = s_len[b] <= 0;
+            empty = lane_len(b) <= 0;
             mine = e > s_pre[b] && e - 1 >= x0 && e - 1 < x1;
             if (APPEND && empty && p.slots_out && w == 0 && kvh == 0) p.slots_out[b] = -1;
         }
@@ -359,7 +374,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
             while (mm) {
                 const int bb = c0 + __builtin_ctzll(mm);
                 mm &= mm - 1;
-                append_row<D>(p, bb, kvh, __builtin_amdgcn_readfirstlane(s_len[bb]), lane);
+                append_row<D>(p, bb, kvh, uni_len(bb), lane);
             }
         }
     }
@@ -381,7 +396,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         c.b = b;
         c.pre = __builtin_amdgcn_readfirstlane(s_pre[b]);
         c.end = __builtin_amdgcn_readfirstlane(s_pre[b + 1]);
-        c.L = __builtin_amdgcn_readfirstlane(s_len[b]);
+        c.L = uni_len(b);
         c.ks = window_start(c.L - qn + 1, p.window);
         c.ks_last = window_start(c.L, p.window);
         c.ksa = c.ks & ~(kKeys - 1);
@@ -396,7 +411,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
             c.pre = c.end;
             c.end = __builtin_amdgcn_readfirstlane(s_pre[c.b + 1]);
         } while (x >= c.end);
-        c.L = __builtin_amdgcn_readfirstlane(s_len[c.b]);
+        c.L = uni_len(c.b);
         c.ks = window_start(c.L - qn + 1, p.window);
         c.ks_last = window_start(c.L, p.window);
         c.ksa = c.ks & ~(kKeys - 1);
@@ -425,6 +440,11 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
     const int bs_mask = (1 << p.bs_log2) - 1;
     const int32_t last_block = (int32_t)(p.num_blocks - 1);
     uint8_t* const qring = smem + S::kQOff;
+    // INT8: the query fragments of the segment whose first tile was issued last.  With two
+    // stages that tile is issued one tile ahead, and the consume side takes the fragments
+    // at the segment's start, before it issues the next tile.
+    static_assert(!S::kCompact || kStg == 2, "one query register set");
+    u32x4 qnext[C::kSteps];
     const int nq = (NC * C::kRowBytes + 1023) / 1024;
     const uint8_t* const qbase = reinterpret_cast<const uint8_t*>(p.q);
 
@@ -446,7 +466,16 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         const int x = x0 + u;
         const int kb = ic.ksa + (x - ic.pre) * kKeys;
         uint8_t* stage = smem + (u % kStg) * (I8 ? S::kCodeStage : C::kStage);
-        if (x == ic.pre || u == 0) {  // first tile of a segment: its query rows first
+        if ((x == ic.pre || u == 0) && S::kCompact) {   // first tile of a segment: its query rows first
+            // into register set seg % kStg (lane (g, n): column n's 16-byte pieces g, 4 + g,
+            // ...; columns past NC re-read the last one)
+            const int c = min(n, NC - 1);
+            const int ct = c / G;
+            const int64_t qrow = ((int64_t)ic.b * qn + ct) * p.hq + kvh * G + (c - ct * G);
+            const uint8_t* src = qbase + qrow * C::kRowBytes + 16 * g;
+#pragma unroll
+            for (int s = 0; s < C::kSteps; ++s) qnext[s] = ld16(src + 64 * s);
+        } else if (x == ic.pre || u == 0) {
             // LDS row c of the slot is column c: query token c / G, head c % G of the kv
             // head (bytes past the NC rows re-read the last row).
             uint8_t* qdst = qring + (ic.seg % kStg) * S::kQSlot;
@@ -596,7 +625,11 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         // This segment's query rows (Q^T fragments: k-step s covers dims 32 s .. 32 s + 31;
         // lane (g, n) holds 8 of them of head n, zero for columns past G).
         bf16x8_t qf[C::kSteps];
-        {
+        if constexpr (S::kCompact) {
+#pragma unroll
+            for (int s = 0; s < C::kSteps; ++s)
+                qf[s] = __builtin_bit_cast(bf16x8_t, valid ? qnext[s] : u32x4{0u, 0u, 0u, 0u});
+        } else {
             const uint8_t* qs = qring + (cc.seg % kStg) * S::kQSlot + n * C::kRowBytes;
 #pragma unroll
             for (int s = 0; s < C::kSteps; ++s) {
@@ -659,12 +692,10 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
 // its last segment unless the sequence starts exactly at the range start; ranges are
 // empty when there are fewer tiles than ranges).  The (m, l) of all parts are staged in
 // LDS with one round of loads, then every o element is read once.
-constexpr int kCombineMaxParts = kStreamWgs;
-
-template <int D>
+template <int D, int MAXP>
 __global__ __launch_bounds__(256) void gqa_stream_combine_kernel(DecodeParams p) {
-    __shared__ float s_w[16][kCombineMaxParts];   // m, then the weight e^(m - M)
-    __shared__ float s_l[16][kCombineMaxParts];
+    __shared__ float s_w[16][MAXP];   // m, then the weight e^(m - M)
+    __shared__ float s_l[16][MAXP];
     __shared__ float s_inv[16];
     const int b = blockIdx.x / p.hkv;
     const int kvh = blockIdx.x % p.hkv;
@@ -933,7 +964,10 @@ bool gqa_stream_shape_supported(int head_dim, int bs_log2, int batch) {
     return (head_dim == 64 || head_dim == 128) && bs_log2 >= rpi_log2 && batch <= kStreamMaxBatch;
 }
 
-int gqa_stream_parts(int num_kv_heads) { return num_kv_heads >= kStreamWgs ? 1 : kStreamWgs / num_kv_heads; }
+int gqa_stream_parts(int num_kv_heads, bool int8) {
+    const int wgs = int8 || kStreamCompactBf16 ? kStreamWgsI8 : kStreamWgs;
+    return num_kv_heads >= wgs ? 1 : wgs / num_kv_heads;
+}
 
 hipError_t launch_gqa_decode_int8(const DecodeParams& p, int head_dim, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)p.hkv * p.parts));
@@ -967,8 +1001,14 @@ hipError_t launch_gqa_decode(const DecodeParams& p, int head_dim, hipStream_t s)
 
 hipError_t launch_gqa_stream_combine(const DecodeParams& p, int head_dim, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)p.batch * p.hkv));
-    if (head_dim == 64) hipLaunchKernelGGL((gqa_stream_combine_kernel<64>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((gqa_stream_combine_kernel<128>), grid, dim3(256), 0, s, p);
+    // at most kStreamWgs (kStreamWgsI8) parts per kv head
+    if (p.parts <= kStreamWgs) {
+        if (head_dim == 64) hipLaunchKernelGGL((gqa_stream_combine_kernel<64, kStreamWgs>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gqa_stream_combine_kernel<128, kStreamWgs>), grid, dim3(256), 0, s, p);
+    } else {
+        if (head_dim == 64) hipLaunchKernelGGL((gqa_stream_combine_kernel<64, kStreamWgsI8>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gqa_stream_combine_kernel<128, kStreamWgsI8>), grid, dim3(256), 0, s, p);
+    }
     return hipGetLastError();
 }
 
