@@ -92,8 +92,11 @@ __global__ __launch_bounds__(256) void kv_write_int8_kernel(QuantWriteParams p) 
 }
 
 // ------------------------------------------------------------------ int8 decode
+// Register budget: one query head per kv head fits 128 VGPRs (4 waves per SIMD, 77 -> 74 us
+// on the Llama-7B INT8 step); four fit 256 without accumulation registers (2 waves).
 template <int D, int GP>
-__global__ __launch_bounds__(256) void decode_int8_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP == 1 ? 4 : 2)))
+void decode_int8_kernel(DecodeParams p) {
     constexpr int EPL = 16;                           // codes per lane per load
     constexpr int LPT = D / EPL;                      // lanes per token row
     constexpr int TPW = 64 / LPT;                     // tokens per wave load
