@@ -300,6 +300,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     }
 }
 
+// Four output values of one row: bf16 (one 8-byte store) or fp32 (one 16-byte store).
+__device__ __forceinline__ void store_out4(bf16_t* out, int64_t idx, float a, float b, float c, float d) {
+    const uint32_t w0 = f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    const uint32_t w1 = f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+    *reinterpret_cast<uint2*>(out + idx) = make_uint2(w0, w1);
+}
+__device__ __forceinline__ void store_out4(float* out, int64_t idx, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(out + idx) = make_float4(a, b, c, d);
+}
+
+// One workgroup per (sequence, query head) row: wave 0 reduces the splits' (m, l) with lane
+// shuffles, then every thread merges four value columns (16-byte partial loads).
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     extern __shared__ float sm_w[];   // [max_splits] weights
@@ -311,24 +323,39 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     const int ns = L > 0 ? (L - window_start32(L, p.window) + p.split_tokens - 1) / p.split_tokens : 0;
     if (ns <= 1) return;   // the split kernel wrote this row directly
     const float* ml = p.ws_ml + bh * p.max_splits * 2;
-    if (threadIdx.x == 0) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
         float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+        for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
         float lsum = 0.0f;
-        for (int s = 0; s < ns; ++s) {
+        for (int s = lane; s < ns; s += 64) {
             const float w = fast_exp2(ml[2 * s] - M);
             sm_w[s] = w;
             lsum = fmaf(w, ml[2 * s + 1], lsum);
         }
-        sm_inv = 1.0f / lsum;
-        sm_lse = (M + __log2f(lsum)) * kLn2;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o, 64);
+        if (lane == 0) {
+            sm_inv = 1.0f / lsum;
+            sm_lse = (M + __log2f(lsum)) * kLn2;
+        }
     }
     __syncthreads();
     const float* o = p.ws_o + bh * p.max_splits * p.dim;
-    for (int d = threadIdx.x; d < p.dim; d += blockDim.x) {
-        float acc = 0.0f;
-        for (int s = 0; s < ns; ++s) acc = fmaf(sm_w[s], o[(int64_t)s * p.dim + d], acc);
-        store_out<T>(p.out, bh * p.dim + d, acc * sm_inv);
+    const float inv = sm_inv;
+    for (int d = 4 * threadIdx.x; d < p.dim; d += 4 * blockDim.x) {
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int s = 0; s < ns; ++s) {
+            const float w = sm_w[s];
+            const float4 v = *reinterpret_cast<const float4*>(o + (int64_t)s * p.dim + d);
+            acc.x = fmaf(w, v.x, acc.x);
+            acc.y = fmaf(w, v.y, acc.y);
+            acc.z = fmaf(w, v.z, acc.z);
+            acc.w = fmaf(w, v.w, acc.w);
+        }
+        store_out4(reinterpret_cast<T*>(p.out), bh * p.dim + d, acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
     if (p.lse && threadIdx.x == 0) p.lse[bh] = sm_lse;
 }
@@ -399,7 +426,8 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, hipStre
 
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)p.batch * p.hq));
-    const int threads = p.dim >= 256 ? 256 : (p.dim >= 128 ? 128 : 64);
+    // four value columns per thread (dims are multiples of 4: 64, 128, 512)
+    const int threads = p.dim >= 1024 ? 256 : (p.dim >= 512 ? 128 : 64);
     const size_t shm = (size_t)p.max_splits * sizeof(float);
     if (dtype == 1) hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(threads), shm, s, p);
     else hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(threads), shm, s, p);
