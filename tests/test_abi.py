@@ -304,12 +304,15 @@ def test_int8_forms_reject_bad_arguments():
         return L.pkv_paged_attn_decode_int8(a["out"], a["lse"], a["q"], a["kc"], a["vc"], a["ks"], a["vs"],
                                             a["t"], a["lens"], a["B"], a["mbs"], a["mx"], a["hq"],
                                             a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["win"],
-                                            a["st"], FAKE, 1 << 30, None)
+                                            a["st"], FAKE, a.get("wsb", 1 << 30), None)
     assert dec(hq=34, hkv=2) == -4               # more than 16 query heads per kv head
     assert dec(hq=16, hkv=2, bs=4) == -4         # 8 per kv head: blocks of fewer than 8 keys
     assert dec(hq=16, hkv=2, d=64, bs=8) == -4   # ... of fewer than 16 keys at head_dim 64
     assert dec(hq=16, hkv=2, B=1025, mbs=1) == -4    # ... more than 1024 sequences
     assert dec(hq=10, hkv=2, d=96) == -4
+    # 8 query heads per kv head (the range kernel's partial states): a too-small workspace
+    # is refused before any launch
+    assert dec(B=64, hq=64, hkv=8, bs=128, mbs=256, mx=32768, nb=16384, wsb=4096) == -7
     assert dec(st=0) == -2
     assert dec(win=-1) == -2
     assert dec(d=96) == -4
