@@ -243,7 +243,7 @@ __device__ __forceinline__ void append_row(const DecodeParams& p, int b, int kvh
 
 // ================================================================== range-streaming kernel
 constexpr int kStreamStages = 3;       // LDS stages: two tiles in flight while one is used
-constexpr int kStreamCodeStages = 2;   // INT8 code stages: one tile in flight while one is used
+constexpr int kStreamCodeStages = 2;   // stages of the compact (INT8) layout: one tile in flight
 constexpr int kStreamMaxBatch = 1024;  // sequences whose tile prefix fits LDS
 constexpr int kStreamWgs = 512;        // workgroups per launch (all kv heads): 2 per CU
 constexpr int kStreamWgsI8 = 1024;     // INT8: 4 per CU, one wave on every SIMD

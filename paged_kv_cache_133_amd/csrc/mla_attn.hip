@@ -528,8 +528,11 @@ DecodePlan plan_mla(int32_t batch, int32_t num_q_heads, int32_t head_dim_v, int3
     const int64_t hgs = mla_head_groups(num_q_heads);
     auto nsplits = [&](int sp) { return (int64_t)(max_seq_len_kv + sp - 1) / sp; };
     // A split's partial state is Hq x Dv fp32 (256 KiB at 128 x 512): long splits keep that
-    // traffic small; shorten them only while the grid would leave compute units idle.
-    int split = 1024;
+    // traffic small; shorten them only while the grid would leave compute units idle.  With
+    // one workgroup per CU the time also depends on how the units pack onto the CUs: on 64
+    // sequences of 2K-8K keys a sweep of 512..2048 measured 1536 best (167.8 us; 1024: 182.8,
+    // 1280: 201.3, 1792: 185.6, 2048: 200.7).
+    int split = 1536;
     while (split > 256 && batch * hgs * nsplits(split) < 512) split /= 2;
     pl.split_tokens = split;
     pl.max_splits = (int32_t)(max_seq_len_kv > 0 ? nsplits(split) : 1);
