@@ -243,14 +243,10 @@ __device__ __forceinline__ void append_row(const DecodeParams& p, int b, int kvh
 
 // ================================================================== range-streaming kernel
 constexpr int kStreamStages = 3;       // LDS stages: two tiles in flight while one is used
-constexpr int kStreamCodeStages = 2;   // stages of the compact (INT8) layout: one tile in flight
+constexpr int kStreamCodeStages = 2;   // INT8 code stages: one tile in flight while one is used
 constexpr int kStreamMaxBatch = 1024;  // sequences whose tile prefix fits LDS
 constexpr int kStreamWgs = 512;        // workgroups per launch (all kv heads): 2 per CU
 constexpr int kStreamWgsI8 = 1024;     // INT8: 4 per CU, one wave on every SIMD
-// bf16 in the INT8 layout (two stages, query rows in registers, 4 per CU): 4 % faster on the
-// 32K-context GQA shape, but the merge of 4 times as many ranges makes the two-token MTP
-// step slower; off.
-constexpr bool kStreamCompactBf16 = false;
 
 // LDS of the range kernel.  bf16 caches: kStreamStages tile stages, a ring of query rows per
 // stage, the tile prefix and the lengths.  INT8 caches (under 40 KiB, for four workgroups per
@@ -265,7 +261,7 @@ struct StreamCfg {
     static constexpr int kCodeRpi = 1024 / D;                         // code rows per wave load: 8 or 16
     static constexpr int kCodeDmaHalf = kKeys / kCodeRpi;             // wave loads per half: 4 or 2
     static constexpr int kDma = I8 ? 2 * kCodeDmaHalf + 1 : C::kDma;  // wave loads per tile
-    static constexpr bool kCompact = I8 || kStreamCompactBf16;   // Q in registers, no lengths
+    static constexpr bool kCompact = I8;                          // Q in registers, no lengths
     static constexpr int kStages = kCompact ? kStreamCodeStages : kStreamStages;
     static constexpr int kStagesBytes = I8 ? kStages * kCodeStage + C::kStage : kStages * C::kStage;
     static constexpr int kBufOff = kStages * kCodeStage;              // INT8: the bf16 tile
@@ -298,7 +294,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
     constexpr int kStg = S::kStages;
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::kSmem];
     int32_t* s_pre = reinterpret_cast<int32_t*>(smem + S::kPreOff);
-    int32_t* s_len = reinterpret_cast<int32_t*>(smem + S::kLenOff);   // bf16 only
+    int32_t* s_len = S::kCompact ? nullptr : reinterpret_cast<int32_t*>(smem + S::kLenOff);
     // Visible length of sequence b: per lane, and (b uniform) in SGPRs.
     auto lane_len = [&](int b) { return S::kCompact ? min(p.seq_lens[b], p.len_cap) : s_len[b]; };
     auto uni_len = [&](int b) {
@@ -965,7 +961,7 @@ bool gqa_stream_shape_supported(int head_dim, int bs_log2, int batch) {
 }
 
 int gqa_stream_parts(int num_kv_heads, bool int8) {
-    const int wgs = int8 || kStreamCompactBf16 ? kStreamWgsI8 : kStreamWgs;
+    const int wgs = int8 ? kStreamWgsI8 : kStreamWgs;
     return num_kv_heads >= wgs ? 1 : wgs / num_kv_heads;
 }
 
