@@ -405,7 +405,8 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
         pl.ws_bytes = pl.ws_ml_offset + rows * 2 * sizeof(float);
     }
     if (gqa_mfma_supported(1, G) || qn > 0) {   // the range-streaming layout, if that kernel runs
-        pl.parts = gqa_stream_parts(num_kv_heads, byte_rows && G > 4);
+        const bool compact = byte_rows ? G > 4 : max_seq_len_kv >= kStreamCompactMinKeys;
+        pl.parts = gqa_stream_parts(num_kv_heads, compact);
         const size_t parts = (size_t)num_kv_heads * pl.parts * 2 * G * (qn > 0 ? qn : 1);
         pl.st_o_offset = 0;
         pl.st_ml_offset = align256(parts * head_dim_v * sizeof(float));

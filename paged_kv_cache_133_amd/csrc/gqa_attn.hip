@@ -243,17 +243,18 @@ __device__ __forceinline__ void append_row(const DecodeParams& p, int b, int kvh
 
 // ================================================================== range-streaming kernel
 constexpr int kStreamStages = 3;       // LDS stages: two tiles in flight while one is used
-constexpr int kStreamCodeStages = 2;   // INT8 code stages: one tile in flight while one is used
+constexpr int kStreamCodeStages = 2;   // compact layout: one tile in flight while one is used
 constexpr int kStreamMaxBatch = 1024;  // sequences whose tile prefix fits LDS
 constexpr int kStreamWgs = 512;        // workgroups per launch (all kv heads): 2 per CU
-constexpr int kStreamWgsI8 = 1024;     // INT8: 4 per CU, one wave on every SIMD
+constexpr int kStreamWgsCompact = 1024;  // compact layout: 4 per CU, one wave on every SIMD
 
-// LDS of the range kernel.  bf16 caches: kStreamStages tile stages, a ring of query rows per
-// stage, the tile prefix and the lengths.  INT8 caches (under 40 KiB, for four workgroups per
-// CU): stages of codes as loaded (K rows of D bytes, V rows, then 1 KiB whose first 256 bytes
-// are the tile's 32 K and 32 V scales), one bf16 tile the wave converts them into, and the
-// tile prefix; the query rows stay in registers and the lengths are read from memory.
-template <int D, bool I8 = false>
+// LDS of the range kernel.  Default layout (bf16): kStreamStages tile stages, a ring of query
+// rows per stage, the tile prefix and the lengths.  Compact layout (under 40 KiB, for four
+// workgroups per CU; INT8 always, bf16 on long contexts): two stages (INT8: of codes as
+// loaded, K rows of D bytes, V rows, then 1 KiB whose first 256 bytes are the tile's 32 K
+// and 32 V scales, plus one bf16 tile the wave converts them into) and the tile prefix; the
+// query rows stay in registers and the lengths are read from memory.
+template <int D, bool I8 = false, bool COMPACT = I8>
 struct StreamCfg {
     using C = GqaCfg<D>;
     static constexpr int kCodeHalf = kKeys * D;                       // K (or V) codes of a tile
@@ -261,7 +262,8 @@ struct StreamCfg {
     static constexpr int kCodeRpi = 1024 / D;                         // code rows per wave load: 8 or 16
     static constexpr int kCodeDmaHalf = kKeys / kCodeRpi;             // wave loads per half: 4 or 2
     static constexpr int kDma = I8 ? 2 * kCodeDmaHalf + 1 : C::kDma;  // wave loads per tile
-    static constexpr bool kCompact = I8;                          // Q in registers, no lengths
+    static constexpr bool kCompact = COMPACT;                     // Q in registers, no lengths
+    static_assert(COMPACT || !I8, "INT8 runs in the compact layout");
     static constexpr int kStages = kCompact ? kStreamCodeStages : kStreamStages;
     static constexpr int kStagesBytes = I8 ? kStages * kCodeStage + C::kStage : kStages * C::kStage;
     static constexpr int kBufOff = kStages * kCodeStage;              // INT8: the bf16 tile
@@ -286,11 +288,11 @@ struct Cursor {
     int ks_last;                      // first key the last query token sees (>= ks)
 };
 
-template <int D, bool APPEND, bool I8 = false>
+template <int D, bool APPEND, bool I8 = false, bool COMPACT = I8>
 __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
     static_assert(!(APPEND && I8), "the INT8 cache is written beforehand by the quantizing writer");
     using C = GqaCfg<D>;
-    using S = StreamCfg<D, I8>;
+    using S = StreamCfg<D, I8, COMPACT>;
     constexpr int kStg = S::kStages;
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::kSmem];
     int32_t* s_pre = reinterpret_cast<int32_t*>(smem + S::kPreOff);
@@ -960,8 +962,8 @@ bool gqa_stream_shape_supported(int head_dim, int bs_log2, int batch) {
     return (head_dim == 64 || head_dim == 128) && bs_log2 >= rpi_log2 && batch <= kStreamMaxBatch;
 }
 
-int gqa_stream_parts(int num_kv_heads, bool int8) {
-    const int wgs = int8 ? kStreamWgsI8 : kStreamWgs;
+int gqa_stream_parts(int num_kv_heads, bool compact) {
+    const int wgs = compact ? kStreamWgsCompact : kStreamWgs;
     return num_kv_heads >= wgs ? 1 : wgs / num_kv_heads;
 }
 
@@ -975,12 +977,24 @@ hipError_t launch_gqa_decode_int8(const DecodeParams& p, int head_dim, hipStream
 hipError_t launch_gqa_decode(const DecodeParams& p, int head_dim, hipStream_t s) {
     if (p.parts > 0) {
         const dim3 grid((unsigned)((int64_t)p.hkv * p.parts));
+        // the plan chose the compact layout when it planned more than kStreamWgs ranges
+        const bool compact = (int64_t)p.hkv * p.parts > kStreamWgs;
         if (head_dim == 64) {
-            if (p.k_new) hipLaunchKernelGGL((gqa_stream_kernel<64, true>), grid, dim3(64), 0, s, p);
-            else hipLaunchKernelGGL((gqa_stream_kernel<64, false>), grid, dim3(64), 0, s, p);
+            if (compact) {
+                if (p.k_new) hipLaunchKernelGGL((gqa_stream_kernel<64, true, false, true>), grid, dim3(64), 0, s, p);
+                else hipLaunchKernelGGL((gqa_stream_kernel<64, false, false, true>), grid, dim3(64), 0, s, p);
+            } else {
+                if (p.k_new) hipLaunchKernelGGL((gqa_stream_kernel<64, true>), grid, dim3(64), 0, s, p);
+                else hipLaunchKernelGGL((gqa_stream_kernel<64, false>), grid, dim3(64), 0, s, p);
+            }
         } else {
-            if (p.k_new) hipLaunchKernelGGL((gqa_stream_kernel<128, true>), grid, dim3(64), 0, s, p);
-            else hipLaunchKernelGGL((gqa_stream_kernel<128, false>), grid, dim3(64), 0, s, p);
+            if (compact) {
+                if (p.k_new) hipLaunchKernelGGL((gqa_stream_kernel<128, true, false, true>), grid, dim3(64), 0, s, p);
+                else hipLaunchKernelGGL((gqa_stream_kernel<128, false, false, true>), grid, dim3(64), 0, s, p);
+            } else {
+                if (p.k_new) hipLaunchKernelGGL((gqa_stream_kernel<128, true>), grid, dim3(64), 0, s, p);
+                else hipLaunchKernelGGL((gqa_stream_kernel<128, false>), grid, dim3(64), 0, s, p);
+            }
         }
         return hipGetLastError();
     }
@@ -997,13 +1011,13 @@ hipError_t launch_gqa_decode(const DecodeParams& p, int head_dim, hipStream_t s)
 
 hipError_t launch_gqa_stream_combine(const DecodeParams& p, int head_dim, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)p.batch * p.hkv));
-    // at most kStreamWgs (kStreamWgsI8) parts per kv head
+    // at most kStreamWgs (compact layout: kStreamWgsCompact) parts per kv head
     if (p.parts <= kStreamWgs) {
         if (head_dim == 64) hipLaunchKernelGGL((gqa_stream_combine_kernel<64, kStreamWgs>), grid, dim3(256), 0, s, p);
         else hipLaunchKernelGGL((gqa_stream_combine_kernel<128, kStreamWgs>), grid, dim3(256), 0, s, p);
     } else {
-        if (head_dim == 64) hipLaunchKernelGGL((gqa_stream_combine_kernel<64, kStreamWgsI8>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((gqa_stream_combine_kernel<128, kStreamWgsI8>), grid, dim3(256), 0, s, p);
+        if (head_dim == 64) hipLaunchKernelGGL((gqa_stream_combine_kernel<64, kStreamWgsCompact>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gqa_stream_combine_kernel<128, kStreamWgsCompact>), grid, dim3(256), 0, s, p);
     }
     return hipGetLastError();
 }

@@ -172,8 +172,11 @@ bool gqa_mfma_supported(int dtype, int group);
 // Head dim, block size and batch the range-streaming kernel takes (any column count <= 16).
 bool gqa_stream_shape_supported(int head_dim, int bs_log2, int batch);
 bool gqa_stream_supported(int dtype, int group, int head_dim, int bs_log2, int batch);
-// Ranges per kv head: bf16 2 workgroups per CU, INT8 (5..16 query heads per kv head) 4.
-int gqa_stream_parts(int num_kv_heads, bool int8);
+// Ranges per kv head: 2 workgroups per CU, or 4 in the compact layout (INT8 with 5..16 query
+// heads per kv head, and bf16 when the planned length is at least kStreamCompactMinKeys:
+// the merge of twice the ranges pays off only on long contexts).
+int gqa_stream_parts(int num_kv_heads, bool compact);
+constexpr int32_t kStreamCompactMinKeys = 8192;
 hipError_t launch_gqa_decode(const DecodeParams& p, int head_dim, hipStream_t s);
 hipError_t launch_gqa_stream_combine(const DecodeParams& p, int head_dim, hipStream_t s);
 // The range-streaming kernel over INT8 codes (p.parts > 0, p.k_scale / p.v_scale set,

@@ -25,6 +25,10 @@ CASES = [
     (16, 2, 128, 256, [5000, 6, 4100, 257, 255, 256]),
     (32, 4, 128, 2, [300, 2, 3, 77]),                                  # blocks < one wave load
     (16, 4, 64, 4, [129, 1, 64, 500]),                                 # D 64: 8 rows per wave load
+    # longest sequence >= 8192 keys: the compact layout (two stages, 4 workgroups per CU)
+    (32, 4, 128, 16, [8200, 1, 33, 9000, 31, 64]),                     # G 8
+    (64, 4, 64, 32, [8192, 5, 3000, 1, 8300]),                         # G 16, D 64
+    (16, 4, 128, 128, [12000, 2, 7, 100, 129]),                        # G 4, large blocks
 ]
 
 
@@ -46,7 +50,7 @@ def test_gqa_mfma_decode(case):
     say(f"  max-abs error {err:.3e}")
 
 
-@pytest.mark.parametrize("case", CASES[:5], ids=lambda s: "hq%d_hkv%d_d%d_bs%d" % s[:4])
+@pytest.mark.parametrize("case", CASES[:5] + CASES[-3:], ids=lambda s: "hq%d_hkv%d_d%d_bs%d" % s[:4])
 def test_gqa_mfma_decode_append(case):
     """Write-and-attend in one pass: pool bytes, slots, outputs and lse as the oracle's."""
     Hq, Hkv, D, bs, L = case

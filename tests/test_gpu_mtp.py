@@ -50,6 +50,21 @@ SHAPES = [  # hq, hkv, d, bs, qn  (columns qn * hq / hkv)
 ]
 
 
+def test_mtp_decode_long_context():
+    """A sequence of more than 8192 keys puts the MTP decode in the compact layout (query
+    fragments of (token, head) columns in registers)."""
+    hq, hkv, d, bs, qn = 32, 8, 128, 16, 2
+    w = wl.custom(mode="varlen", batch=5, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                  block_size=bs, dtype="bf16")
+    L = [9000, 30, 1, 4000, 8191]
+    say(f"mtp long context L={L}")
+    c = wl.make_case(w, L, [qn] * len(L), seed=77, device=DEV)
+    g = mtp_step(c, qn)
+    o = oracle_step(c, causal=True)
+    compare_writes(c, g, o)
+    compare_outputs(c, g, o, tokens=o["tokens"], label="mtp long context")
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "hq%d_hkv%d_d%d_bs%d_qn%d" % s)
 @pytest.mark.parametrize("window", [0, 100])
 def test_mtp_decode_parity(shape, window):
