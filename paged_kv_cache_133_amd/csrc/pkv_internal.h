@@ -176,7 +176,7 @@ bool gqa_stream_supported(int dtype, int group, int head_dim, int bs_log2, int b
 // heads per kv head, and bf16 when the planned length is at least kStreamCompactMinKeys:
 // the merge of twice the ranges pays off only on long contexts).
 int gqa_stream_parts(int num_kv_heads, bool compact);
-constexpr int32_t kStreamCompactMinKeys = 8192;
+constexpr int32_t kStreamCompactMinKeys = 4096;
 hipError_t launch_gqa_decode(const DecodeParams& p, int head_dim, hipStream_t s);
 hipError_t launch_gqa_stream_combine(const DecodeParams& p, int head_dim, hipStream_t s);
 // The range-streaming kernel over INT8 codes (p.parts > 0, p.k_scale / p.v_scale set,

@@ -34,6 +34,22 @@ def test_decode_window(shape, window):
     compare_outputs(c, g, o, tokens=o["tokens"], label=f"window {window} {shape}")
 
 
+@pytest.mark.parametrize("shape", [(32, 4, 128, 16, "bf16"), (64, 4, 64, 32, "bf16")],
+                         ids=lambda s: "hq%d_hkv%d_d%d_bs%d_%s" % s)
+@pytest.mark.parametrize("window", [4096, 5000])
+def test_decode_window_long(shape, window):
+    """Windows of 4096+ keys over sequences to 9000: the range kernel's compact layout."""
+    Hq, Hkv, D, bs, dtype = shape
+    w = wl.custom(batch=5, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs, dtype=dtype)
+    L = [9000, 40, 5000, 4100, 1]
+    say(f"decode window {window} long: {shape}")
+    c = wl.make_case(w, np.array(L) - 1, [1] * len(L), seed=window + D, device=DEV)
+    g = gpu_step(c, window=window)
+    o = oracle_step(c, window=window)
+    compare_writes(c, g, o)
+    compare_outputs(c, g, o, tokens=o["tokens"], label=f"window {window} long {shape}")
+
+
 @pytest.mark.parametrize("shape", SHAPES[1:4], ids=lambda s: "hq%d_hkv%d_d%d_bs%d_%s" % s)
 def test_decode_append_window(shape):
     """Write-and-attend with a window: pool bytes, slots, outputs and lse as the oracle's."""
