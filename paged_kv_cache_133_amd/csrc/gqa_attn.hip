@@ -243,7 +243,7 @@ __device__ __forceinline__ void append_row(const DecodeParams& p, int b, int kvh
 
 // ================================================================== range-streaming kernel
 constexpr int kStreamStages = 3;       // LDS stages: two tiles in flight while one is used
-constexpr int kStreamCodeStages = 2;   // compact layout: one tile in flight while one is used
+constexpr int kStreamCompactStages = 2;   // compact layout: one tile in flight while one is used
 constexpr int kStreamMaxBatch = 1024;  // sequences whose tile prefix fits LDS
 constexpr int kStreamWgs = 512;        // workgroups per launch (all kv heads): 2 per CU
 constexpr int kStreamWgsCompact = 1024;  // compact layout: 4 per CU, one wave on every SIMD
@@ -264,7 +264,7 @@ struct StreamCfg {
     static constexpr int kDma = I8 ? 2 * kCodeDmaHalf + 1 : C::kDma;  // wave loads per tile
     static constexpr bool kCompact = COMPACT;                     // Q in registers, no lengths
     static_assert(COMPACT || !I8, "INT8 runs in the compact layout");
-    static constexpr int kStages = kCompact ? kStreamCodeStages : kStreamStages;
+    static constexpr int kStages = kCompact ? kStreamCompactStages : kStreamStages;
     static constexpr int kStagesBytes = I8 ? kStages * kCodeStage + C::kStage : kStages * C::kStage;
     static constexpr int kBufOff = kStages * kCodeStage;              // INT8: the bf16 tile
     static constexpr int kQSlot = kCompact ? 0 : 16 * C::kRowBytes;   // one segment's query rows
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
     const int bs_mask = (1 << p.bs_log2) - 1;
     const int32_t last_block = (int32_t)(p.num_blocks - 1);
     uint8_t* const qring = smem + S::kQOff;
-    // INT8: the query fragments of the segment whose first tile was issued last.  With two
+    // Compact layout: the query fragments of the segment whose first tile was issued last.  With two
     // stages that tile is issued one tile ahead, and the consume side takes the fragments
     // at the segment's start, before it issues the next tile.
     static_assert(!S::kCompact || kStg == 2, "one query register set");
