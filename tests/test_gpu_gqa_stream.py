@@ -104,3 +104,16 @@ def test_gqa_mfma_split_and_combine_equal_decode():
     torch.cuda.synchronize()
     assert torch.equal(g["out"].view(torch.int16), out2.view(torch.int16))
     assert torch.equal(g["lse"], lse2)
+
+
+def test_gqa_compact_many_short_sequences():
+    """The compact layout (one sequence of 5000 keys) with 400 sequences of 1..70 keys:
+    many one- and two-tile segments per range; every row checked, writes included."""
+    rng = np.random.default_rng(8)
+    L = [int(x) for x in rng.integers(1, 71, size=400)] + [5000]
+    say(f"gqa compact layout, many short sequences (B={len(L)})")
+    c = _case(32, 4, 128, 16, L, seed=13)
+    g = gpu_step(c)
+    o = oracle_step(c)
+    compare_writes(c, g, o)
+    compare_outputs(c, g, o, tokens=o["tokens"], label="compact many short")

@@ -234,3 +234,18 @@ def test_int8_gqa_long_workload_sampled():
     assert err <= 2e-2, f"max-abs error {err:.3e}"
     _check_lse(c, lse.cpu().numpy()[rows], ol)
     say(f"  max-abs error {err:.3e}")
+
+
+def test_int8_ranges_many_short_sequences():
+    """300 sequences of 1..70 keys and one of 6000 at 8 query heads per kv head: ranges hold
+    many one- and two-tile segments in a row, so the next segment's query fragments are
+    issued while the previous segment is still in use; every row checked."""
+    rng = np.random.default_rng(5)
+    L = [int(x) for x in rng.integers(1, 71, size=300)] + [6000]
+    say(f"int8 ranges, many short sequences (B={len(L)})")
+    c, dev, table, kdeq, vdeq = _int8_case(32, 4, 128, 16, L, seed=21)
+    lse = torch.empty((len(L), 32), dtype=torch.float32, device=DEV)
+    out, _ = pkv.paged_attn_decode_int8(c.q, dev["kc"], dev["vc"], dev["ks"], dev["vs"], table,
+                                        c.lens_after_tensor(DEV), c.max_len_after, c.w.scale, lse=lse)
+    torch.cuda.synchronize()
+    say(f"  max-abs error {_check(c, out, lse, kdeq, vdeq, 0):.3e}")
