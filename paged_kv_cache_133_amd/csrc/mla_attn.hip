@@ -132,9 +132,19 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
         }
         return;
     }
-    const int k_begin = split * p.split_tokens;
+    // The sequence's ns = ceil(L / split_tokens) splits (the count the merge uses) share its
+    // tiles evenly, so that its units are of one size for the longest-first order; if an
+    // even share could leave the last split empty they keep split_tokens keys each.
+    int split_keys = p.split_tokens;
+    {
+        const int tiles = (L + kKeys - 1) / kKeys;
+        const int ns = (L + p.split_tokens - 1) / p.split_tokens;
+        const int even = (tiles + ns - 1) / ns;
+        if ((int64_t)(ns - 1) * even < tiles) split_keys = even * kKeys;
+    }
+    const int k_begin = split * split_keys;
     if (k_begin >= L) return;
-    const int k_end = min(L, k_begin + p.split_tokens);
+    const int k_end = min(L, k_begin + split_keys);
     const int ntiles = (k_end - k_begin + kKeys - 1) / kKeys;
 
     const int head = hg * C::kHeads + wid * 16 + n;
@@ -530,8 +540,8 @@ DecodePlan plan_mla(int32_t batch, int32_t num_q_heads, int32_t head_dim_v, int3
     // A split's partial state is Hq x Dv fp32 (256 KiB at 128 x 512): long splits keep that
     // traffic small; shorten them only while the grid would leave compute units idle.  With
     // one workgroup per CU the time also depends on how the units pack onto the CUs: on 64
-    // sequences of 2K-8K keys a sweep of 512..2048 measured 1536 best (167.8 us; 1024: 182.8,
-    // 1280: 201.3, 1792: 185.6, 2048: 200.7).
+    // sequences of 2K-8K keys (splits of a sequence evenly sized) a sweep measured 1536 best
+    // (163.3 us; 1024: 177.8, 1280: 197.6, 2048: 190.2).
     int split = 1536;
     while (split > 256 && batch * hgs * nsplits(split) < 512) split /= 2;
     pl.split_tokens = split;
