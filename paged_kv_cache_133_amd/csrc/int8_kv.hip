@@ -119,7 +119,17 @@ void decode_int8_kernel(DecodeParams p) {
     const int L = min(p.seq_lens[b], p.len_cap);
     const int ks = window_start(L, p.window);
     const int ksa = ks & ~(kStepTokensI8 - 1);
-    const int t0 = ksa + split * p.split_tokens;
+    // The sequence's nsplit splits (the count the merge uses) share its steps evenly, in whole
+    // steps per wave, unless that could leave the last split empty.
+    int split_keys = p.split_tokens;
+    {
+        const int steps = (L - ksa + kStepTokensI8 - 1) / kStepTokensI8;
+        const int ns = max((L - ksa + p.split_tokens - 1) / p.split_tokens, 1);
+        const int per_wave_steps = ((steps + ns - 1) / ns + kWavesI8 - 1) / kWavesI8;
+        const int even = per_wave_steps * kWavesI8 * kStepTokensI8;
+        if (even > 0 && (int64_t)(ns - 1) * even < L - ksa) split_keys = even;
+    }
+    const int t0 = ksa + split * split_keys;
     if (L <= 0) {   // no visible key: output 0, lse -inf
         if (split == 0) {
             for (int i = threadIdx.x; i < p.group * D; i += blockDim.x) {
@@ -131,9 +141,9 @@ void decode_int8_kernel(DecodeParams p) {
         return;
     }
     if (t0 >= L) return;
-    const int t1 = min(L, t0 + p.split_tokens);
+    const int t1 = min(L, t0 + split_keys);
     const int nsplit = (L - ksa + p.split_tokens - 1) / p.split_tokens;
-    const int per_wave = p.split_tokens / kWavesI8;
+    const int per_wave = split_keys / kWavesI8;
     const int w0 = t0 + wave * per_wave;
     const int w1 = min(t1, w0 + per_wave);
     const int bs_mask = (1 << p.bs_log2) - 1;
