@@ -136,10 +136,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int32_t last_block = (int32_t)(p.num_blocks - 1);
     const int32_t* trow = p.table + (int64_t)b * p.mbs;
 
-    // Append mode: this step's token sits at L - 1; its K/V come from the new rows.
-    const int pos_new = APPEND ? L - 1 : -1;
+    // Append mode: this step's token sits at L - 1; its K/V come from the new rows.  A row
+    // longer than the length bound (a broken precondition) appends nothing: its slot is
+    // reported as -1 and it attends to its first len_cap cached keys, as without append.
+    const bool app = APPEND && p.seq_lens[b] <= p.len_cap;
+    const int pos_new = app ? L - 1 : -1;
     const int64_t new_off = ((int64_t)b * p.hkv + kvh) * D * EB;
-    if (APPEND && pos_new >= t0 && pos_new < t1) {
+    if (APPEND && !app && split == 0 && p.slots_out && kvh == 0 && threadIdx.x == 0)
+        p.slots_out[b] = -1;
+    if (app && pos_new >= t0 && pos_new < t1) {
         int32_t phys = trow[pos_new >> p.bs_log2];
         phys = min(max(phys, 0), last_block);
         const int64_t slot = ((int64_t)phys << p.bs_log2) | (pos_new & bs_mask);

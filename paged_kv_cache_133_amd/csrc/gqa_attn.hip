@@ -224,9 +224,15 @@ __device__ __forceinline__ void store_empty(const DecodeParams& p, int64_t row, 
 
 // The kv head's slice of sequence b's new K and V rows to its slot (append mode), by the
 // first 2 kRowChunks lanes.
+// A row longer than the length bound (a broken precondition) appends nothing: its slot is
+// reported as -1 (the lookup of the new key, `new_key`, then never matches either).
 template <int D>
 __device__ __forceinline__ void append_row(const DecodeParams& p, int b, int kvh, int L, int lane) {
     using C = GqaCfg<D>;
+    if (uniform_load(p.seq_lens + b) > p.len_cap) {
+        if (p.slots_out && kvh == 0 && lane == 0) p.slots_out[b] = -1;
+        return;
+    }
     if (lane >= 2 * C::kRowChunks) return;
     const int32_t* trow = p.table + (int64_t)b * p.mbs;
     const int32_t phys = min(max(trow[(L - 1) >> p.bs_log2], 0), (int32_t)(p.num_blocks - 1));
@@ -286,7 +292,16 @@ __device__ __forceinline__ int range_of(int x, int T, int P) { return (int)(((in
 struct Cursor {
     int b, pre, end, L, ks, ksa, seg;
     int ks_last;                      // first key the last query token sees (>= ks)
+    int new_key;                      // append mode: key read from the new rows (L - 1), else INT_MAX
 };
+
+// Append mode: the key of sequence b that comes from the new rows, L - 1, unless the row is
+// longer than the length bound; INT_MAX (no key) otherwise and outside append mode.
+template <bool APPEND>
+__device__ __forceinline__ int new_key_of(const DecodeParams& p, int b, int L) {
+    if (!APPEND) return INT_MAX;
+    return uniform_load(p.seq_lens + b) <= p.len_cap ? L - 1 : INT_MAX;
+}
 
 template <int D, bool APPEND, bool I8 = false, bool COMPACT = I8>
 __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
@@ -399,6 +414,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         c.ks_last = window_start(c.L, p.window);
         c.ksa = c.ks & ~(kKeys - 1);
         c.seg = 0;
+        c.new_key = new_key_of<APPEND>(p, b, c.L);
         return c;
     };
     // Move c to the sequence that holds tile x (x never moves back).
@@ -413,6 +429,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         c.ks = window_start(c.L - qn + 1, p.window);
         c.ks_last = window_start(c.L, p.window);
         c.ksa = c.ks & ~(kKeys - 1);
+        c.new_key = new_key_of<APPEND>(p, c.b, c.L);
         ++c.seg;
     };
 
@@ -550,7 +567,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
                                              : last_slot;
                 const uint8_t* ks = kbase + slot * row_bytes + lchunk[j];
                 const uint8_t* vs = vbase + slot * row_bytes + lchunk[j];
-                if (APPEND && key >= L - 1) {
+                if (APPEND && key >= ic.new_key) {
                     ks = reinterpret_cast<const uint8_t*>(p.k_new) + new_off + lchunk[j];
                     vs = reinterpret_cast<const uint8_t*>(p.v_new) + new_off + lchunk[j];
                 }
@@ -809,6 +826,7 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
     const uint32_t row_bytes = (uint32_t)(p.hkv * D * 2);            // one cache slot
     const int64_t new_off = ((int64_t)b * p.hkv + kvh) * D * 2;      // this head's new rows
 
+    const int new_key = new_key_of<APPEND>(p, b, L);                  // INT_MAX: none
     if (APPEND && L - 1 >= k_begin && L - 1 < k_end) append_row<D>(p, b, kvh, L, lane);
 
     // Q^T fragments: k-step s covers dims 32 s .. 32 s + 31; this lane holds 8 of them of
@@ -851,7 +869,7 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
     const bool fast_rows = p.bs_log2 >= 5;
     auto fast_tile = [&](int u) {
         const int kb = k_begin + u * kKeys;
-        return fast_rows && kb + kKeys <= k_end && !(APPEND && kb + kKeys > L - 1);
+        return fast_rows && kb + kKeys <= k_end && !(APPEND && kb + kKeys > new_key);
     };
     auto entry_of = [&](int u) { return uniform_load(trow + ((k_begin + u * kKeys) >> p.bs_log2)); };
     int32_t next_entry = fast_tile(0) ? entry_of(0) : 0;
@@ -878,7 +896,7 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
             const uint64_t slot = ((uint64_t)tab.block_of(key, chunk) << p.bs_log2) | (uint32_t)(key & bs_mask);
             const uint8_t* ks = kbase + slot * row_bytes + lchunk[j];
             const uint8_t* vs = vbase + slot * row_bytes + lchunk[j];
-            if (APPEND && key == L - 1) {
+            if (APPEND && key == new_key) {
                 ks = reinterpret_cast<const uint8_t*>(p.k_new) + new_off + lchunk[j];
                 vs = reinterpret_cast<const uint8_t*>(p.v_new) + new_off + lchunk[j];
             }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
+
 namespace pkv {
 
 constexpr int kWave = 64;

@@ -51,8 +51,8 @@ def test_decode_parity_small(shape):
 
 @pytest.mark.parametrize("name", ["tiny_gqa_f32", "llama7b_mha_bf16"])
 def test_decode_parity_full_workload(name):
-    """The full-size workload in the launch configuration the bench times; every output
-    row is checked."""
+    """The full-size workload through slot_mapping + kv_cache_write + paged_attn_decode
+    (the bench's `separate` path); every output row is checked."""
     w = wl.WORKLOADS[name]
     say(f"decode parity full: {name}")
     c = wl.make_workload_case(w, seed=0, device=DEV)
@@ -63,19 +63,49 @@ def test_decode_parity_full_workload(name):
     say(f"  max-abs error {err:.3e}")
 
 
-def test_decode_parity_gqa_long_sampled():
-    """GQA 64/8, lengths up to 32K: the whole batch runs on the GPU; the oracle checks the
-    longest, the shortest and two other sequences in full."""
+def test_decode_parity_gqa_long_full():
+    """GQA 64/8, lengths up to 32K, every one of the 64 sequences against the oracle."""
     w = wl.GQA_LONG
-    say("decode parity gqa_long (sampled sequences)")
+    say("decode parity gqa_long (all rows)")
     c = wl.make_workload_case(w, seed=0, device=DEV)
     g = gpu_step(c)
-    order = np.argsort(c.lens_after)
-    rows = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 5})
-    o = oracle_step(c, rows=rows)
+    o = oracle_step(c)
     compare_writes(c, g, o)
     err = compare_outputs(c, g, o, tokens=o["tokens"], label="gqa_long")
-    say(f"  rows {rows} lens {c.lens_after[rows].tolist()} max-abs error {err:.3e}")
+    say(f"  {w.batch} rows, lens {int(c.lens_after.min())}..{int(c.lens_after.max())}, "
+        f"max-abs error {err:.3e}")
+
+
+def _append_full(name, seed=0):
+    """One step of a full-size workload through paged_attn_decode_append (the bench's
+    default, fused path: write folded into the split pass, then the combine) against the
+    oracle's slot_mapping + write + attention: slots exactly, both whole pools byte for
+    byte, every output row."""
+    import paged_kv_cache_133_amd as pkv
+    w = wl.WORKLOADS[name]
+    say(f"decode_append full workload: {name} seed {seed}")
+    c = wl.make_workload_case(w, seed=seed, device=DEV)
+    o = oracle_step(c)
+    k, v = c.cache_k.clone(), c.cache_v.clone()
+    T = c.num_tokens
+    slots = torch.full((T,), -5, dtype=torch.int64, device=DEV)
+    lse = torch.empty((T, w.num_q_heads), dtype=torch.float32, device=DEV)
+    out, _ = pkv.paged_attn_decode_append(c.q, c.new_k, c.new_v, k, v, c.table_tensor(DEV),
+                                          c.lens_after_tensor(DEV), c.max_len_after, w.scale,
+                                          lse=lse, slots_out=slots)
+    torch.cuda.synchronize()
+    g = {"slots": slots, "cache_k": k, "cache_v": v, "out": out, "lse": lse}
+    compare_writes(c, g, o)
+    err = compare_outputs(c, g, o, tokens=o["tokens"], label=f"decode_append {name}")
+    say(f"  {w.batch} rows, max-abs error {err:.3e}")
+
+
+def test_decode_append_full_workload_llama7b():
+    _append_full("llama7b_mha_bf16")
+
+
+def test_decode_append_full_workload_gqa_long():
+    _append_full("gqa_long_bf16")
 
 
 def test_decode_other_seeds_llama7b():
@@ -242,3 +272,51 @@ def test_decode_append_matches_oracle(shape):
     assert torch.equal(out.view(torch.int16) if dt == "bf16" else out.view(torch.int32),
                        ref["out"].view(torch.int16) if dt == "bf16" else ref["out"].view(torch.int32))
     assert torch.equal(lse, ref["lse"])
+
+
+@pytest.mark.parametrize("shape", [(8, 8, 128, 16, "bf16"), (4, 1, 64, 16, "f32"),
+                                   (16, 2, 128, 16, "bf16"), (16, 2, 128, 2, "bf16")],
+                         ids=lambda s: "hq%d_hkv%d_d%d_bs%d_%s" % s)
+def test_decode_append_overlength_row_writes_nothing(shape):
+    """A row whose length exceeds max_seq_len_kv (a broken precondition) appends nothing in
+    the fused write-and-attend call: its slot is reported as -1, the pools keep their bytes
+    there, and it attends to its first max_seq_len_kv cached keys, exactly as the plain
+    decode does.  The other rows are written and attended as usual."""
+    import paged_kv_cache_133_amd as pkv
+    from oracle import oracle
+    from tests.helpers import case_numpy, host
+    Hq, Hkv, D, bs, dt = shape
+    w = wl.custom(batch=3, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                  dtype=dt)
+    L = [99, 299, 49]            # L' = 100, 300, 50
+    cap = 200                    # row 1 is over the bound
+    say(f"decode_append over-length row: {shape}")
+    c = wl.make_case(w, L, [1] * 3, seed=91, device=DEV)
+    h = case_numpy(c)
+    all_slots = oracle.slot_mapping(h["block_table"], h["lens_before"], h["cu_q"],
+                                    h["block_size"], h["num_blocks"])
+    keep = np.array([0, 2])
+    ref_k = oracle.kv_write(h["cache_k"], h["new_k"][keep], all_slots[keep])
+    ref_v = oracle.kv_write(h["cache_v"], h["new_v"][keep], all_slots[keep])
+    k, v = c.cache_k.clone(), c.cache_v.clone()
+    table, la = c.table_tensor(DEV), c.lens_after_tensor(DEV)
+    slots = torch.full((3,), -9, dtype=torch.int64, device=DEV)
+    out, _ = pkv.paged_attn_decode_append(c.q, c.new_k, c.new_v, k, v, table, la, cap, w.scale,
+                                          slots_out=slots)
+    torch.cuda.synchronize()
+    exp_slots = all_slots.copy()
+    exp_slots[1] = -1
+    assert np.array_equal(slots.cpu().numpy(), exp_slots)
+    assert host(k).tobytes() == ref_k.tobytes()
+    assert host(v).tobytes() == ref_v.tobytes()
+    # the plain decode over the written pools with the same bound: the same bits
+    plain, _ = pkv.paged_attn_decode(c.q, k, v, table, la, cap, w.scale)
+    torch.cuda.synchronize()
+    ity = torch.int16 if dt == "bf16" else torch.int32
+    assert torch.equal(out.view(ity), plain.view(ity))
+    # and the oracle over those pools, row 1 cut to its first `cap` keys
+    lens = np.minimum(c.lens_after, cap).astype(np.int32)
+    ref_out, _ = oracle.paged_attention(h["q"], ref_k, ref_v, c.block_table,
+                                        np.arange(4, dtype=np.int32), lens, w.scale, False)
+    err = float(np.abs(out.float().cpu().numpy().astype(np.float64) - ref_out).max())
+    assert err <= {"f32": 1e-5, "bf16": 2e-2}[dt], err
