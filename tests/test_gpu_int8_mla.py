@@ -135,19 +135,17 @@ def test_int8_mla_two_passes_equal_one():
     _check(c, out1, lse1, kdeq, rdeq, lens)
 
 
-def test_int8_mla_full_workload_sampled():
+def test_int8_mla_full_workload():
     """The MLA workload's shape at full size (64 sequences of U{2048..8192}, 128 heads, bs
-    128) over the INT8 latent cache; the oracle checks four sequences."""
+    128) over the INT8 latent cache; the oracle checks every sequence."""
     w = wl.WORKLOADS["mla_absorbed_bf16"]
     L, _ = wl.sample_lengths(w, 0)
     Lp = [int(x) + 1 for x in L]
-    say("int8 mla full-size workload (sampled sequences)")
+    say("int8 mla full-size workload (all rows)")
     c, dev, table, kdeq, rdeq, lens = _int8_mla_case(128, 128, Lp, seed=0)
     lse = torch.empty((len(Lp), 128), dtype=torch.float32, device=DEV)
     out, _ = pkv.paged_attn_decode_mla_int8(c.q, c.q_rope, dev["nc"], dev["rc"], dev["ns"], dev["rs"],
                                             table, torch.from_numpy(lens).to(DEV), c.max_len_after,
                                             c.w.scale, lse=lse)
     torch.cuda.synchronize()
-    order = np.argsort(c.lens_after)
-    rows = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 3})
-    say(f"  max-abs error {_check(c, out, lse, kdeq, rdeq, lens, rows=rows):.3e}")
+    say(f"  max-abs error {_check(c, out, lse, kdeq, rdeq, lens):.3e}")
