@@ -3,36 +3,51 @@
 TEST INFRASTRUCTURE ONLY: the tests may import this module; the product path never does,
 and it shares no code with the library's manager.
 
-It follows "Paged KV Cache and Packed Sequence" (hotelren.com source note):
-  * 2.1: a pool of num_blocks physical blocks; the free list starts as 0 .. num_blocks-1
-    and a block is taken with a pop from its end; a per-block reference count; per
-    sequence a list of physical blocks; a request that finds the free list empty fails
-    with "kv cache full";
+Behaviour it follows ("Paged KV Cache and Packed Sequence", hotelren.com source note):
+  * 2.1: a pool of num_blocks physical blocks, all spare at the start; a spare block is
+    handed out last-in first-out (the spare ids form a stack that starts as 0 at the bottom
+    up to num_blocks - 1 on top); each block counts the sequences that hold it; each
+    sequence owns an ordered list of physical blocks; a request that needs more spare
+    blocks than there are fails (a "full" error);
   * 2.1: a sequence of n tokens holds ceil(n / block_size) blocks; 2.2: token position p
     lives at offset p % block_size of logical block p // block_size, and the flat index of
-    the row is physical_block * block_size + offset; a decode step takes a new block only
+    its row is physical_block * block_size + offset; a decode step takes a new block only
     when its token is the first of a logical block the sequence does not hold yet;
   * 2.2: the table handed to the kernels is fixed-width (max_blocks_per_seq per sequence);
-  * 5.2: sequences sharing a prefix share its blocks (count > 1); releasing a sequence
-    first lowers the count of each of its blocks and puts a block back on the free list
-    only when its count reaches zero.
+  * 5.2: sequences that share a prefix share its blocks (a holder count above one);
+    releasing a sequence lowers the count of each of its blocks, and a block becomes
+    spare again only when no holder remains.
 
 Readings where the pages are silent:
   * fork(parent, child) is how a prefix comes to be shared (beam search, parallel
     sampling): the child gets the parent's block list and every count goes up by one;
   * copy on write: a sequence about to write into a partly filled last block that is
-    shared takes a fresh block for it instead (the writer's count on the old block is
-    dropped) and reports (old, new) so that the rows already there are copied first;
+    shared takes a fresh block for it instead (its hold on the old block is dropped) and
+    reports (old, new) so that the rows already there are copied first;
   * a failed request changes nothing (the fresh blocks are counted before any is taken);
-  * released blocks go back on the free list in the order the sequence holds them.
+  * blocks released together become spare in the order the sequence held them (the last
+    one ends on top of the stack).
 """
 from __future__ import annotations
+
+from dataclasses import dataclass, field
 
 
 class ManagerError(RuntimeError):
     def __init__(self, kind: str, message: str):
         super().__init__(message)
-        self.kind = kind          # "shape" (bad id / too long) or "full" (free list short)
+        self.kind = kind          # "shape" (bad id / too long) or "full" (too few spare)
+
+
+@dataclass
+class SeqRecord:
+    blocks: list = field(default_factory=list)   # physical ids in logical order
+    length: int = 0                              # tokens held
+
+
+def blocks_for(tokens: int, block_size: int) -> int:
+    """Blocks that hold `tokens` tokens: ceil(tokens / block_size)."""
+    return (tokens + block_size - 1) // block_size
 
 
 class BlockManagerModel:
@@ -41,76 +56,124 @@ class BlockManagerModel:
             raise ManagerError("shape", "sizes must be positive")
         self.block_size = block_size
         self.max_blocks_per_seq = max_blocks_per_seq
-        self.free_blocks = list(range(num_blocks))
-        self.ref_count = [0] * num_blocks
-        self.block_table = {}      # seq id -> list of physical blocks
-        self.seq_len = {}          # seq id -> tokens held
+        self._spare = [i for i in range(num_blocks)]   # stack: the top is the last element
+        self._holders = [0 for _ in range(num_blocks)]  # sequences holding each block
+        self._seqs: dict = {}                           # seq id -> SeqRecord
 
+    # ------------------------------------------------------------------ read access
     def num_free(self) -> int:
-        return len(self.free_blocks)
+        return len(self._spare)
 
-    def add(self, seq: int):
-        if seq in self.block_table or (isinstance(seq, int) and seq < 0):
-            raise ManagerError("shape", f"sequence {seq} exists or is negative")
-        self.block_table[seq] = []
-        self.seq_len[seq] = 0
+    def spare_ids(self) -> list:
+        """Spare block ids, bottom of the stack first."""
+        return list(self._spare)
 
-    def fork(self, parent: int, child: int):
-        if parent not in self.block_table or child in self.block_table or child < 0:
-            raise ManagerError("shape", "bad fork")
-        self.block_table[child] = list(self.block_table[parent])
-        self.seq_len[child] = self.seq_len[parent]
-        for blk in self.block_table[child]:
-            self.ref_count[blk] += 1
+    def holders(self, blk: int) -> int:
+        return self._holders[blk]
 
-    def _take(self) -> int:
-        blk = self.free_blocks.pop()
-        self.ref_count[blk] += 1
+    def holder_counts(self) -> list:
+        return list(self._holders)
+
+    def sequences(self) -> list:
+        return list(self._seqs)
+
+    def blocks_of(self, seq) -> list:
+        return list(self._record(seq).blocks)
+
+    def length_of(self, seq) -> int:
+        return self._record(seq).length
+
+    def _record(self, seq) -> SeqRecord:
+        rec = self._seqs.get(seq)
+        if rec is None:
+            raise ManagerError("shape", f"no sequence {seq}")
+        return rec
+
+    # ------------------------------------------------------------------ ownership
+    def _grab(self) -> int:
+        """The spare block on top of the stack, now held once."""
+        blk = self._spare.pop()
+        self._holders[blk] = 1
         return blk
 
-    def append(self, seq: int, num_tokens: int):
-        """Returns (slots of the new tokens, (old, new) block copy or None)."""
-        if seq not in self.block_table or num_tokens < 0:
-            raise ManagerError("shape", "bad append")
-        blocks, n = self.block_table[seq], self.seq_len[seq]
+    def _release(self, blocks) -> None:
+        """Drop one hold on each block; the ones left with no holder become spare, in the
+        order given."""
+        emptied = []
+        for blk in blocks:
+            self._holders[blk] -= 1
+            if self._holders[blk] == 0:
+                emptied.append(blk)
+        self._spare.extend(emptied)
+
+    # ------------------------------------------------------------------ operations
+    def add(self, seq):
+        if seq in self._seqs or (isinstance(seq, int) and seq < 0):
+            raise ManagerError("shape", f"sequence {seq} exists or is negative")
+        self._seqs[seq] = SeqRecord()
+
+    def fork(self, parent, child):
+        if parent not in self._seqs or child in self._seqs or child < 0:
+            raise ManagerError("shape", "bad fork")
+        src = self._seqs[parent]
+        self._seqs[child] = SeqRecord(list(src.blocks), src.length)
+        for blk in src.blocks:
+            self._holders[blk] += 1
+
+    def _plan(self, rec: SeqRecord, num_tokens: int):
+        """(logical blocks that need a fresh id, whether the first of them replaces a shared
+        partly filled last block) for appending num_tokens tokens to rec."""
         bs = self.block_size
+        total = blocks_for(rec.length + num_tokens, bs)
+        if total > self.max_blocks_per_seq:
+            raise ManagerError("shape", "sequence longer than max_blocks_per_seq blocks")
+        fresh = list(range(len(rec.blocks), total))
+        partial = rec.length % bs != 0
+        shared_tail = partial and self._holders[rec.blocks[-1]] > 1
+        if shared_tail:
+            fresh.insert(0, len(rec.blocks) - 1)
+        return fresh, shared_tail
+
+    def append(self, seq, num_tokens: int):
+        """Slots of num_tokens new tokens of `seq`, and the (old, new) block copy a copy on
+        write needs (or None)."""
+        if seq not in self._seqs or num_tokens < 0:
+            raise ManagerError("shape", "bad append")
+        rec = self._seqs[seq]
         if num_tokens == 0:
             return [], None
-        held_after = -(-(n + num_tokens) // bs)
-        if held_after > self.max_blocks_per_seq:
-            raise ManagerError("shape", "sequence longer than max_blocks_per_seq blocks")
-        cow = n % bs != 0 and self.ref_count[blocks[-1]] > 1
-        fresh = held_after - len(blocks) + (1 if cow else 0)
-        if fresh > len(self.free_blocks):
-            raise ManagerError("full", "kv cache full")
+        fresh, shared_tail = self._plan(rec, num_tokens)
+        if len(fresh) > len(self._spare):
+            raise ManagerError("full", f"{len(fresh)} blocks needed, {len(self._spare)} spare")
         copy = None
-        if cow:
-            old = blocks[-1]
-            new = self._take()
-            self.ref_count[old] -= 1
-            blocks[-1] = new
-            copy = (old, new)
-        slots = []
-        for p in range(n, n + num_tokens):
-            if p // bs == len(blocks):          # first token of a block not held yet
-                blocks.append(self._take())
-            slots.append(blocks[p // bs] * bs + p % bs)
-        self.seq_len[seq] = n + num_tokens
-        return slots, copy
+        for j in fresh:
+            blk = self._grab()
+            if j < len(rec.blocks):                  # the shared tail: move the writer off it
+                old = rec.blocks[j]
+                self._holders[old] -= 1
+                rec.blocks[j] = blk
+                copy = (old, blk)
+            else:
+                rec.blocks.append(blk)
+        assert copy is not None or not shared_tail
+        bs = self.block_size
+        first = rec.length
+        rec.length += num_tokens
+        return [rec.blocks[p // bs] * bs + p % bs for p in range(first, rec.length)], copy
 
     def decode_step(self, seqs, pad_block: int = 0):
         """One token for each row's sequence in row order; a negative id is a padding row
         (no sequence: pad_block row, length 0, slot -1).  Returns (rows, lengths, slots,
         copies).  Nothing changes when any row would fail."""
         live = [s for s in seqs if s >= 0]
-        if len(set(live)) != len(live) or any(s not in self.block_table for s in live):
+        if len(set(live)) != len(live) or any(s not in self._seqs for s in live):
             raise ManagerError("shape", "unknown or repeated sequence")
         for s in live:          # a row that would need a block past max_blocks_per_seq
-            if self.seq_len[s] % self.block_size == 0 and \
-                    len(self.block_table[s]) + 1 > self.max_blocks_per_seq:
+            rec = self._seqs[s]
+            if blocks_for(rec.length + 1, self.block_size) > self.max_blocks_per_seq:
                 raise ManagerError("shape", "sequence longer than max_blocks_per_seq blocks")
-        saved = (list(self.free_blocks), list(self.ref_count),
-                 {k: list(v) for k, v in self.block_table.items()}, dict(self.seq_len))
+        snapshot = (list(self._spare), list(self._holders),
+                    {k: SeqRecord(list(r.blocks), r.length) for k, r in self._seqs.items()})
         rows, lens, slots, copies = [], [], [], []
         try:
             for s in seqs:
@@ -123,32 +186,24 @@ class BlockManagerModel:
                 if copy is not None:
                     copies.append(copy)
                 slots.append(slot)
-                r, l = self.table([s], pad_block)
+                r, n = self.table([s], pad_block)
                 rows.append(r[0])
-                lens.append(l[0])
+                lens.append(n[0])
         except ManagerError:
-            self.free_blocks, self.ref_count, self.block_table, self.seq_len = saved
+            self._spare, self._holders, self._seqs = snapshot
             raise
         return rows, lens, slots, copies
 
-    def free(self, seq: int):
-        if seq not in self.block_table:
-            raise ManagerError("shape", f"no sequence {seq}")
-        blocks = self.block_table.pop(seq)
-        del self.seq_len[seq]
-        for blk in blocks:
-            self.ref_count[blk] -= 1
-        for blk in blocks:
-            if self.ref_count[blk] == 0:
-                self.free_blocks.append(blk)
+    def free(self, seq):
+        rec = self._record(seq)
+        del self._seqs[seq]
+        self._release(rec.blocks)
 
     def table(self, seqs, pad_block: int = 0):
         """Fixed-width rows (blocks, then pad_block) and the lengths."""
         rows, lens = [], []
         for s in seqs:
-            if s not in self.block_table:
-                raise ManagerError("shape", f"no sequence {s}")
-            blocks = self.block_table[s]
-            rows.append(blocks + [pad_block] * (self.max_blocks_per_seq - len(blocks)))
-            lens.append(self.seq_len[s])
+            rec = self._record(s)
+            rows.append(list(rec.blocks) + [pad_block] * (self.max_blocks_per_seq - len(rec.blocks)))
+            lens.append(rec.length)
         return rows, lens

@@ -36,10 +36,10 @@ def compare_state(bm, m, live, pad):
     rows, mlens = m.table(ids, pad_block=pad)
     assert table.tolist() == [list(r) for r in rows] if ids else table.size == 0
     assert lens.tolist() == mlens
-    for b in range(len(m.ref_count)):
-        assert bm.ref_count(b) == m.ref_count[b]
+    for b in range(len(m.holder_counts())):
+        assert bm.ref_count(b) == m.holders(b)
     for s in ids:
-        assert bm.length(s) == m.seq_len[s]
+        assert bm.length(s) == m.length_of(s)
 
 
 @pytest.mark.parametrize("seed", range(8))
@@ -189,6 +189,6 @@ def test_decode_step_errors_change_nothing():
     assert (bm.num_free, bm.table([0, 1, 2])[0].tolist(), bm.length(0)) == state
     with pytest.raises(ManagerError) as e2:
         m.decode_step([0, 1, 2])
-    assert e2.value.kind == "full" and m.seq_len[0] == 4 and m.num_free() == 1
+    assert e2.value.kind == "full" and m.length_of(0) == 4 and m.num_free() == 1
     with pytest.raises(PagedKVError):
         bm.add(-3)

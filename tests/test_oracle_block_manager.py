@@ -7,7 +7,7 @@ import random
 
 import pytest
 
-from oracle.block_manager import BlockManagerModel, ManagerError
+from oracle.block_manager import BlockManagerModel, ManagerError, SeqRecord
 
 
 def check_invariants(m, live):
@@ -15,15 +15,15 @@ def check_invariants(m, live):
     cover the pool; each sequence holds ceil(len / block_size) blocks."""
     holders = {}
     for s in live:
-        blocks = m.block_table[s]
+        blocks = m.blocks_of(s)
         assert len(blocks) == len(set(blocks))
-        assert len(blocks) == -(-m.seq_len[s] // m.block_size)
+        assert len(blocks) == -(-m.length_of(s) // m.block_size)
         for b in blocks:
             holders[b] = holders.get(b, 0) + 1
-    assert len(m.free_blocks) == len(set(m.free_blocks))
-    assert not set(m.free_blocks) & set(holders)
-    assert len(m.free_blocks) + len(holders) == len(m.ref_count)
-    for b, c in enumerate(m.ref_count):
+    assert len(m.spare_ids()) == len(set(m.spare_ids()))
+    assert not set(m.spare_ids()) & set(holders)
+    assert len(m.spare_ids()) + len(holders) == len(m.holder_counts())
+    for b, c in enumerate(m.holder_counts()):
         assert c == holders.get(b, 0), (b, c, holders.get(b, 0))
 
 
@@ -33,7 +33,7 @@ def pin_pages_37_tokens(cls):
     m = cls(64, 16, 8)
     m.add(0)
     slots, _ = m.append(0, 37)
-    blocks = m.block_table[0]
+    blocks = m.blocks_of(0)
     assert len(blocks) == 3 and m.num_free() == 61
     assert slots[:16] == [blocks[0] * 16 + i for i in range(16)]
     assert slots[36] == blocks[2] * 16 + 4
@@ -78,13 +78,13 @@ def pin_full_changes_nothing(cls):
     with pytest.raises(ManagerError) as e:
         m.append(1, 1)
     assert e.value.kind == "full"
-    assert m.seq_len[1] == 4 and m.num_free() == 0 and m.block_table[1] == [1, 0]
+    assert m.length_of(1) == 4 and m.num_free() == 0 and m.blocks_of(1) == [1, 0]
     m2 = cls(3, 2, 4)
     m2.add(1)
     m2.append(1, 2)
     with pytest.raises(ManagerError):
         m2.append(1, 5)                                   # needs 3 more, 2 free
-    assert m2.num_free() == 2 and m2.seq_len[1] == 2 and m2.ref_count == [0, 0, 1]
+    assert m2.num_free() == 2 and m2.length_of(1) == 2 and m2.holder_counts() == [0, 0, 1]
 
 
 def pin_too_long(cls):
@@ -93,7 +93,7 @@ def pin_too_long(cls):
     m.append(0, 8)
     with pytest.raises(ManagerError) as e:
         m.append(0, 1)
-    assert e.value.kind == "shape" and m.seq_len[0] == 8 and m.num_free() == 14
+    assert e.value.kind == "shape" and m.length_of(0) == 8 and m.num_free() == 14
 
 
 def pin_shared_prefix_release(cls):
@@ -103,11 +103,11 @@ def pin_shared_prefix_release(cls):
     m.add(0)
     m.append(0, 8)
     m.fork(0, 1)
-    assert [m.ref_count[b] for b in m.block_table[0]] == [2, 2]
+    assert [m.holders(b) for b in m.blocks_of(0)] == [2, 2]
     m.free(0)
-    assert m.num_free() == 6 and [m.ref_count[b] for b in m.block_table[1]] == [1, 1]
+    assert m.num_free() == 6 and [m.holders(b) for b in m.blocks_of(1)] == [1, 1]
     m.free(1)
-    assert m.num_free() == 8 and m.ref_count == [0] * 8
+    assert m.num_free() == 8 and m.holder_counts() == [0] * 8
 
 
 def pin_copy_on_write(cls):
@@ -118,13 +118,13 @@ def pin_copy_on_write(cls):
     m.fork(0, 1)
     slots, copy = m.append(1, 1)
     assert copy == (6, 5) and slots == [5 * 4 + 2]
-    assert m.block_table[1] == [7, 5] and m.block_table[0] == [7, 6]
-    assert m.ref_count[6] == 1 and m.ref_count[7] == 2
+    assert m.blocks_of(1) == [7, 5] and m.blocks_of(0) == [7, 6]
+    assert m.holders(6) == 1 and m.holders(7) == 2
     slots, copy = m.append(0, 1)                          # block 6 no longer shared
     assert copy is None and slots == [6 * 4 + 2]
     m.fork(0, 2)                                          # block 6 shared again, 3 rows
     assert m.append(0, 1) == ([4 * 4 + 3], (6, 4))        # the writer moves to block 4
-    assert m.block_table[2] == [7, 6] and m.ref_count[6] == 1
+    assert m.blocks_of(2) == [7, 6] and m.holders(6) == 1
     m3 = cls(8, 4, 4)
     m3.add(0)
     m3.append(0, 8)
@@ -199,51 +199,41 @@ def test_model_pin(pin):
 
 # ----------------------------------------------------------------------------- mutants
 class FifoFreeList(BlockManagerModel):
-    def _take(self):
-        blk = self.free_blocks.pop(0)
-        self.ref_count[blk] += 1
+    def _grab(self):
+        blk = self._spare.pop(0)
+        self._holders[blk] = 1
         return blk
 
 
 class FreeIgnoresCounts(BlockManagerModel):
     def free(self, seq):
-        blocks = self.block_table.pop(seq)
-        del self.seq_len[seq]
-        for blk in blocks:
-            self.ref_count[blk] = max(self.ref_count[blk] - 1, 0)
-            if blk not in self.free_blocks:
-                self.free_blocks.append(blk)
+        rec = self._record(seq)
+        del self._seqs[seq]
+        for blk in rec.blocks:
+            self._holders[blk] = max(self._holders[blk] - 1, 0)
+            if blk not in self._spare:
+                self._spare.append(blk)
 
 
 class ForkKeepsCounts(BlockManagerModel):
     def fork(self, parent, child):
-        self.block_table[child] = list(self.block_table[parent])
-        self.seq_len[child] = self.seq_len[parent]
+        src = self._seqs[parent]
+        self._seqs[child] = SeqRecord(list(src.blocks), src.length)
 
 
 class NoCopyOnWrite(BlockManagerModel):
-    def append(self, seq, num_tokens):
-        saved = self.ref_count
-        blocks = self.block_table.get(seq)
-        if blocks and self.seq_len[seq] % self.block_size:
-            self.ref_count = list(saved)
-            self.ref_count[blocks[-1]] = 1              # looks unshared to the check
-            last = blocks[-1]
-            try:
-                out = super().append(seq, num_tokens)
-            finally:
-                self.ref_count[last] = saved[last]
-            return out
-        return super().append(seq, num_tokens)
+    def _plan(self, rec, num_tokens):
+        fresh, shared_tail = super()._plan(rec, num_tokens)
+        return (fresh[1:] if shared_tail else fresh), False
 
 
 class EagerNextBlock(BlockManagerModel):
     """Takes the next block when a block's last row is written."""
     def append(self, seq, num_tokens):
         slots, copy = super().append(seq, num_tokens)
-        n = self.seq_len[seq]
-        if num_tokens and n % self.block_size == 0 and self.free_blocks:
-            self.block_table[seq].append(self._take())
+        rec = self._seqs[seq]
+        if num_tokens and rec.length % self.block_size == 0 and self._spare:
+            rec.blocks.append(self._grab())
         return slots, copy
 
 
@@ -259,8 +249,8 @@ class FailureLeaksBlocks(BlockManagerModel):
         try:
             return super().append(seq, num_tokens)
         except ManagerError as e:
-            if e.kind == "full" and self.free_blocks:
-                self.block_table[seq].append(self._take())
+            if e.kind == "full" and self._spare:
+                self._seqs[seq].blocks.append(self._grab())
             raise
 
 
