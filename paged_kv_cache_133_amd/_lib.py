@@ -259,9 +259,10 @@ def prepare_kv_cache_append(k_new, v_new, k_cache, v_cache, block_table, lens_be
 
 def kv_rmsnorm_rope_cache(kv: torch.Tensor, gamma: torch.Tensor, cos: torch.Tensor,
                           sin: torch.Tensor, cache_nope: torch.Tensor, cache_rope: torch.Tensor,
-                          slot_mapping: torch.Tensor, eps: float = 1e-6):
+                          slot_mapping: torch.Tensor, eps: float):
     """RMSNorm + RoPE + write of the MLA latent row (see pkv_kv_rmsnorm_rope_cache).
-    kv [T, Dn + Dr], gamma [Dn], cos/sin [T, Dr/2] fp32, caches [nb, bs, 1, Dn/Dr]."""
+    kv [T, Dn + Dr], gamma [Dn], cos/sin [T, Dr/2] fp32, caches [nb, bs, 1, Dn/Dr].
+    eps (the RMSNorm epsilon) has no default: the caller states the model's value."""
     _dev(kv, gamma, cos, sin, cache_nope, cache_rope, slot_mapping)
     nb, bs, _, dn = cache_nope.shape
     dr = cache_rope.shape[-1]
