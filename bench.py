@@ -76,7 +76,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=5.0,
                     help="minimum wall time of the CPU-oracle sample")
     ap.add_argument("--no-kernel-events", action="store_true",
-                    help="omit the per-kernel HIP events inside the timed region")
+                    help="skip the second timed region (the dominant kernel alone) and the roofline")
     ap.add_argument("--path", choices=("fused", "append", "separate"), default="fused",
                     help="fused: decode_append (write folded into the split pass), combine; "
                          "append: kv_cache_append (slot_mapping + write), split, combine; "
@@ -86,6 +86,9 @@ def parse():
                          "replayed with double-buffered table uploads, per block size")
     ap.add_argument("--block-sizes", default="16,32,64,128",
                     help="block sizes of the --serving sweep")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only measure the practical HBM read ceiling (pkv_stream_read over "
+                         "0.7-4 GB at several grid sizes) and a device copy")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for counter scaling)")
     return ap.parse_args()
@@ -100,11 +103,14 @@ def kernel_source_hash(sources) -> str:
 
 
 def read_traffic(workload: str, kernel: str, sources):
-    """HBM bytes per launch of the dominant kernel from the committed counter summary,
-    or None if the summary is missing or was taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel.split('<')[0]}_{workload}.txt")
+    """(HBM bytes per launch of the dominant kernel, where the figure comes from): the
+    committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE runs, scaled by a copy
+    of known size), or (None, reason) if it is missing or was taken on other kernel sources.
+    The counters are not read in this run."""
+    rel = os.path.join("profiles", f"traffic_{kernel.split('<')[0]}_{workload}.txt")
+    path = os.path.join(ROOT, rel)
     if not os.path.exists(path):
-        return None
+        return None, f"no counter summary {rel}"
     vals = {}
     with open(path) as f:
         for line in f:
@@ -112,11 +118,11 @@ def read_traffic(workload: str, kernel: str, sources):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
     if vals.get("kernel_source_sha256_16") != kernel_source_hash(sources):
-        return None
+        return None, f"{rel} was taken on other kernel sources"
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals["hbm_bytes_per_launch"]), f"committed counter summary {rel}"
     except (KeyError, ValueError):
-        return None
+        return None, f"{rel} holds no hbm_bytes_per_launch"
 
 
 def visible_keys(case):
@@ -193,11 +199,69 @@ def calibrate_copy(mib: int):
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
 
 
+def read_ceiling(launches: int = 20):
+    """--read-ceiling: pkv_stream_read (16-byte non-temporal loads, grid-stride) over 0.7,
+    1.5 and 4 GB at 1K-16K workgroups, rotating over a 4 GiB buffer so that no launch finds
+    its bytes in the 256 MB Infinity Cache, and a torch device copy of 1 GiB; events at the
+    two ends of each run of launches.  Prints one JSON line."""
+    import torch
+    from paged_kv_cache_133_amd import _lib
+    _lib.lib()
+    dev = torch.device("cuda:0")
+    total = 4 << 30
+    buf = torch.zeros(total, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    rows = []
+    for size in (700_000_000, 1_500_000_000, total):
+        size -= size % 4096
+        nrot = max(1, total // size)
+        for grid in (1024, 2048, 4096, 8192, 16384):
+            calls = [_lib.prepare_stream_read(buf[r * size:(r + 1) * size], sink, grid)
+                     for r in range(nrot)]
+            for i in range(3):
+                calls[i % nrot]()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(launches):
+                calls[i % nrot]()
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / launches
+            rows.append({"bytes": size, "grid": grid, "us_per_launch": round(us, 2),
+                         "GB_per_s": round(size / (us * 1e-6) / 1e9, 1)})
+    del buf
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(launches):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / launches
+    best = max(rows, key=lambda r: r["GB_per_s"])
+    print(json.dumps({"read_ceiling_GB_per_s": best["GB_per_s"], "best": best,
+                      "frac_of_8TBps": round(best["GB_per_s"] / PEAK_HBM_GBPS, 4),
+                      "copy_1GiB": {"us_per_copy": round(us, 2),
+                                    "GB_per_s_read_plus_write": round(2 * n / (us * 1e-6) / 1e9, 1)},
+                      "runs": rows}), flush=True)
+
+
 def cpu_baseline(case, kv_bytes, min_seconds):
-    """The fp64 oracle on this host: the whole step (slot_mapping, writes, attention) on
-    host copies of the same inputs, repeated until min_seconds of wall time."""
+    """The fp64 oracle on this host, on host copies of the same inputs.  One step is
+    slot_mapping, the in-place cache writes of the step's rows, then attention for every
+    sequence; the pools are copied to the host once, outside the timing (writing the same
+    rows to the same slots again changes nothing).  INT8 workloads also quantize the new
+    rows and dequantize the pools, as the oracle computes them.  Timed with all of the
+    oracle's threads (median of at least 3 runs, at least min_seconds in all), then with
+    one thread, on the whole step when that takes under ~10 s, else on every k-th
+    sequence (the KV bytes of those sequences over their time)."""
     from oracle import oracle
-    from paged_kv_cache_133_amd import workloads as wl  # noqa: F401
     import numpy as np
     import torch
 
@@ -208,58 +272,78 @@ def cpu_baseline(case, kv_bytes, min_seconds):
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
     c = case
+    w = c.w
     h = {"block_table": c.block_table, "lens_before": c.lens_before, "cu_q": c.cu_q,
          "lens_after": c.lens_after, "cache_k": host(c.cache_k), "cache_v": host(c.cache_v),
          "cache_rope": host(c.cache_rope), "q": host(c.q), "q_rope": host(c.q_rope),
-         "new_k": host(c.new_k), "new_v": host(c.new_v), "new_rope": host(c.new_rope),
-         "block_size": c.w.block_size, "num_blocks": c.num_blocks, "scale": c.w.scale}
-    int8 = c.w.kv_dtype == "int8"
-    mla = c.w.mode == "mla"
+         "new_k": host(c.new_k), "new_v": host(c.new_v), "new_rope": host(c.new_rope)}
+    int8 = w.kv_dtype == "int8"
+    mla = w.mode == "mla"
+    causal = w.mode == "varlen"
     if int8:
         # the oracle's own quantization of the pools (outside the timed step)
         pk, sk = oracle.quantize_rows(h["cache_k"])
         pv, sv = oracle.quantize_rows(h["cache_rope" if mla else "cache_v"])
+        pools = [(pk, sk, h["new_k"]), (pv, sv, h["new_rope" if mla else "new_v"])]
+    else:
+        pools = [(h["cache_k"], h["new_k"]), (h["cache_rope" if mla else "cache_v"],
+                                               h["new_rope" if mla else "new_v"])]
 
-    def int8_step():
-        # slot_mapping, quantize and write the new rows, attend over the dequantized pools
+    def step(rows, threads):
         slots = oracle.slot_mapping(h["block_table"], h["lens_before"], h["cu_q"],
-                                    h["block_size"], h["num_blocks"])
-        if mla:   # nope (key and value) and rope, each with its own scales
-            deq = []
-            for pool, scale, new in ((pk, sk, h["new_k"]), (pv, sv, h["new_rope"])):
+                                    w.block_size, c.num_blocks)
+        if int8:
+            caches = []
+            for codes, scales, new in pools:
                 qn, sn = oracle.quantize_rows(new)
-                deq.append(oracle.dequantize_rows(oracle.kv_write(pool, qn, slots),
-                                                  oracle.kv_write(scale, sn, slots)))
-            return oracle.paged_attention(oracle.widen(h["q"]), deq[0], deq[0], h["block_table"],
-                                          h["cu_q"], h["lens_after"], h["scale"], False,
-                                          q_rope=oracle.widen(h["q_rope"]), k_rope=deq[1])
-        caches = []
-        for pool, scale, new in ((pk, sk, h["new_k"]), (pv, sv, h["new_v"])):
-            qn, sn = oracle.quantize_rows(new)
-            codes = oracle.kv_write(pool, qn, slots)
-            scales = oracle.kv_write(scale, sn, slots)
-            caches.append(oracle.dequantize_rows(codes, scales))
-        return oracle.paged_attention(oracle.widen(h["q"]), caches[0], caches[1], h["block_table"],
-                                      h["cu_q"], h["lens_after"], h["scale"], False,
-                                      window=c.w.window)
+                oracle.kv_write_into(codes, qn, slots)
+                oracle.kv_write_into(scales, sn, slots)
+                caches.append(oracle.dequantize_rows(codes, scales))
+            q = oracle.widen(h["q"])
+            q_rope = oracle.widen(h["q_rope"]) if mla else None
+        else:
+            for pool, new in pools:
+                oracle.kv_write_into(pool, new, slots)
+            caches = [p for p, _ in pools]
+            q, q_rope = h["q"], h["q_rope"]
+        k = caches[0]
+        v, rope = (k, caches[1]) if mla else (caches[1], None)
+        tok = np.concatenate([np.arange(c.cu_q[b], c.cu_q[b + 1]) for b in rows]).astype(np.int64)
+        n = c.cu_q[rows + 1] - c.cu_q[rows]
+        cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        oracle.paged_attention(q[tok], k, v, c.block_table[rows], cu, c.lens_after[rows], w.scale,
+                               causal, q_rope=q_rope[tok] if q_rope is not None else None,
+                               k_rope=rope, threads=threads, window=w.window)
 
+    all_rows = np.arange(w.batch)
+    threads = oracle.max_threads()
     times = []
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        if int8:
-            int8_step()
-        else:
-            oracle.decode_step(h, causal=(c.w.mode == "varlen"), window=c.w.window)
+        step(all_rows, threads)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start >= min_seconds and len(times) >= 3:
             break
     med = statistics.median(times)
-    return {"value": round(kv_bytes / med / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
+    # one thread: the whole step, or every k-th sequence so that it takes ~10 s at most
+    keys = visible_keys(c)[0].astype(np.float64)
+    k_every = max(1, int(np.ceil(med * threads / 10.0)))
+    rows1 = all_rows[::k_every]
+    t1 = time.perf_counter()
+    step(rows1, 1)
+    t1 = time.perf_counter() - t1
+    bytes1 = kv_bytes * float(keys[rows1].sum() / keys.sum())
+    sample1 = ("the whole step" if k_every == 1 else
+               f"the step's writes and the attention of one sequence in {k_every} "
+               f"({len(rows1)} of {w.batch}, {bytes1 / 1e6:.1f} MB of KV)")
+    return {"value": round(kv_bytes / med / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": (f"whole {c.w.name} step (slot_mapping, K/V writes, fp64 attention over "
-                       f"all {c.w.batch} sequences), median of {len(times)} runs, "
-                       f"{med * 1e3:.1f} ms/step")}
+            "sample": (f"whole {w.name} step (slot_mapping, in-place K/V writes, fp64 attention "
+                       f"over all {w.batch} sequences; pools copied to the host once, outside "
+                       f"the timing), median of {len(times)} runs, {med * 1e3:.1f} ms/step"),
+            "value_1_thread": round(bytes1 / t1 / 1e9, 4),
+            "sample_1_thread": f"{sample1}: {t1 * 1e3:.1f} ms"}
 
 
 def step_description(w, path):
@@ -426,6 +510,9 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
+    if args.read_ceiling:
+        read_ceiling()
+        return
     if args.serving:
         import torch
         if not torch.cuda.is_available():
@@ -562,33 +649,25 @@ def main():
         reps.append((write, split, combine))
     torch.cuda.synchronize()
 
-    events = not args.no_kernel_events
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)] if events else None
-
-    def step(i, with_events):
+    def step(i):
         write, attn, combine = reps[i % R]
         if slot_first:
             slot_call()
         if write is not None:
             write()
-        if with_events:
-            ev[i][0].record()
         attn()
-        if with_events:
-            ev[i][1].record()
         if combine is not None:
             combine()
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
     # Timed region: K whole steps, events only at its two ends.
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(args.steps):
-        step(i, False)
+        step(i)
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
@@ -597,28 +676,37 @@ def main():
 
     roofline = None
     flops = algorithmic_flops(case)
-    if events:
-        # Second pass of the same K steps with a pair of HIP events around every launch of
-        # the dominant kernel, recorded on the stream it runs on (torch's current stream).
+    if not args.no_kernel_events:
+        # The dominant kernel's launch time: a second timed region of K launches of that
+        # kernel alone, back to back over the rotated pools, on the stream the library
+        # launches on (torch's current stream), events only at the two ends.  (Events
+        # around every launch add their own overhead to each duration.)
+        for i in range(2):
+            reps[i % R][1]()
+        k0 = torch.cuda.Event(enable_timing=True)
+        k1 = torch.cuda.Event(enable_timing=True)
+        k0.record()
         for i in range(args.steps):
-            step(i, True)
+            reps[i % R][1]()
+        k1.record()
         torch.cuda.synchronize()
-        durs = [a.elapsed_time(b) for a, b in ev]
-        split_ms = statistics.mean(durs)
+        split_ms = k0.elapsed_time(k1) / args.steps
         gbps = split_bytes / (split_ms * 1e-3) / 1e9
         tflops = flops / (split_ms * 1e-3) / 1e12
         # The bound is whichever resource the launch would saturate first at peak.
         mfma_bound = flops / (PEAK_BF16_TFLOPS * 1e12) > split_bytes / (PEAK_HBM_GBPS * 1e9)
         kname, ksources = dominant_kernel(w)
-        traffic = read_traffic(w.name, kname, ksources)
+        traffic, traffic_src = read_traffic(w.name, kname, ksources)
         if mfma_bound:
             roofline = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
         else:
             roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
                         "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}
-        roofline.update({"traffic": traffic, "kernel": kname,
+        roofline.update({"traffic": traffic, "traffic_source": traffic_src, "kernel": kname,
                          "kernel_us": round(split_ms * 1e3, 2),
+                         "kernel_us_method": (f"{args.steps} launches of the kernel alone, back "
+                                              "to back on its stream, HIP events at the two ends"),
                          "algorithmic_bytes_per_launch": split_bytes,
                          "algorithmic_flops_per_launch": flops,
                          "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),

@@ -497,6 +497,17 @@ PKV_API int pkv_bm_table(const pkv_block_manager* bm, const int64_t* seqs, int32
                          int32_t* table, int32_t* seq_lens, int32_t pad_block);
 
 /*
+ * Measurement aid (not part of the decode path): reads `bytes` bytes from the device buffer
+ * `src` with 16-byte non-temporal loads, `grid` workgroups of 256 threads striding over it,
+ * and writes (almost never) one word to `sink`.  Its bandwidth is the practical HBM read
+ * ceiling the HBM-bound kernels are compared with, next to the 8 TB/s vendor figure; "Paged
+ * KV Cache and Packed Sequence", 5.4, times memory movement beside the kernel the same way.
+ *   src 16-byte aligned, bytes a positive multiple of 16, sink [1] uint32, grid in [1, 65536].
+ */
+PKV_API int pkv_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t grid,
+                            void* stream);
+
+/*
  * Copies whole blocks inside one cache array: for i < num_pairs, block pairs[2i] of
  * pool [num_blocks][block_bytes] is copied to block pairs[2i+1] (the copy-on-write pairs
  * of pkv_bm_append; call once per cache array: K, V, and the scale arrays of an INT8

@@ -126,14 +126,20 @@ def slot_mapping(block_table, lens_before, cu_new, block_size: int, num_blocks: 
 def kv_write(cache: np.ndarray, rows: np.ndarray, slots) -> np.ndarray:
     """Return a copy of `cache` ([nb, bs, ...]) with rows[t] written at slots[t]."""
     out = np.array(cache, copy=True, order="C")
+    kv_write_into(out, rows, slots)
+    return out
+
+
+def kv_write_into(cache: np.ndarray, rows: np.ndarray, slots) -> None:
+    """Write rows[t] at slots[t] of `cache` ([nb, bs, ...], C-contiguous) in place."""
+    assert cache.flags["C_CONTIGUOUS"] and cache.flags["WRITEABLE"]
     rows = np.ascontiguousarray(rows)
     s = _c(slots, np.int64)
-    num_slots = out.shape[0] * out.shape[1]
-    row_bytes = out.nbytes // num_slots if num_slots else 0
-    assert rows.dtype == out.dtype and rows.nbytes == len(s) * row_bytes
+    num_slots = cache.shape[0] * cache.shape[1]
+    row_bytes = cache.nbytes // num_slots if num_slots else 0
+    assert rows.dtype == cache.dtype and rows.nbytes == len(s) * row_bytes
     if len(s):
-        _check(lib().orc_kv_write(_ptr(out), num_slots, row_bytes, _ptr(rows), _ptr(s), len(s)))
-    return out
+        _check(lib().orc_kv_write(_ptr(cache), num_slots, row_bytes, _ptr(rows), _ptr(s), len(s)))
 
 
 def kv_write_contiguous(cache: np.ndarray, newkv: np.ndarray, seqlen, token_offset) -> np.ndarray:

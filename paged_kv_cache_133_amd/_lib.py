@@ -26,7 +26,8 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_decode_workspace_size", "pkv_paged_attn_decode_int8",
            "pkv_paged_attn_decode",
            "pkv_paged_attn_decode_split", "pkv_paged_attn_decode_combine",
-           "pkv_paged_attn_decode_append", "pkv_paged_attn_decode_ex", "pkv_paged_attn_varlen",
+           "pkv_paged_attn_decode_append",
+           "pkv_paged_attn_decode_ex", "pkv_paged_attn_varlen",
            "pkv_paged_attn_varlen_ex", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
            "pkv_bm_add", "pkv_bm_fork", "pkv_bm_append", "pkv_bm_decode_step", "pkv_bm_free",
            "pkv_bm_length",
@@ -35,7 +36,7 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_runner_create", "pkv_runner_destroy", "pkv_runner_capture_begin",
            "pkv_runner_capture_end", "pkv_runner_graph", "pkv_runner_host_buffer",
            "pkv_runner_launch", "pkv_decode_mtp_workspace_size", "pkv_paged_attn_decode_mtp",
-           "pkv_kv_cache_write_int8_mla", "pkv_paged_attn_decode_mla_int8")
+           "pkv_kv_cache_write_int8_mla", "pkv_paged_attn_decode_mla_int8", "pkv_stream_read")
 
 
 class PagedKVError(RuntimeError):
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.pkv_paged_attn_decode_append.restype = ctypes.c_int
     L.pkv_paged_attn_decode_append.argtypes = [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
                                                i32, i32, i32, i64, f32, i32, i32, p, sz, p]
+    L.pkv_stream_read.restype = ctypes.c_int
+    L.pkv_stream_read.argtypes = [p, i64, p, i32, p]
     L.pkv_paged_attn_decode_ex.restype = ctypes.c_int
     L.pkv_paged_attn_decode_ex.argtypes = [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
                                            i32, i32, i32, i64, f32, i32, i32, i32, p, sz, p]
@@ -460,6 +463,13 @@ def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seq
                                        workspace, slots_out, window)
     _check(lib().pkv_paged_attn_decode_ex(*args))
     return out, lse
+
+
+def prepare_stream_read(src: torch.Tensor, sink: torch.Tensor, grid: int):
+    """pkv_stream_read over all of `src` (a measurement aid: the HBM read ceiling)."""
+    _dev(src, sink)
+    args = (_ptr(src), src.numel() * src.element_size(), _ptr(sink), int(grid), _stream(src.device))
+    return PreparedCall(lib().pkv_stream_read, args, (src, sink))
 
 
 def prepare_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,

@@ -105,6 +105,15 @@ int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_cache, void
     return hip_status(pkv::launch_kv_write(p, (hipStream_t)stream), "kv_cache_write launch");
 }
 
+int pkv_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t grid, void* stream) {
+    if (!src || !sink) return fail(PKV_ERR_NULL, "stream_read: NULL src or sink");
+    if (!aligned16(src) || reinterpret_cast<uintptr_t>(sink) % 4)
+        return fail(PKV_ERR_ALIGN, "stream_read: src must be 16-byte and sink 4-byte aligned");
+    if (bytes <= 0 || bytes % 16) return fail(PKV_ERR_SHAPE, "stream_read: bytes must be a positive multiple of 16");
+    if (grid < 1 || grid > 65536) return fail(PKV_ERR_SHAPE, "stream_read: grid must be in [1, 65536]");
+    return hip_status(pkv::launch_stream_read(src, bytes, sink, grid, (hipStream_t)stream), "stream_read launch");
+}
+
 int pkv_kv_cache_copy_blocks(void* pool, int64_t block_bytes, int64_t num_blocks,
                              const int64_t* pairs, int32_t num_pairs, void* stream) {
     if (num_pairs < 0 || block_bytes <= 0 || num_blocks <= 0)

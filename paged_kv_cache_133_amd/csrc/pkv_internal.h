@@ -62,6 +62,7 @@ struct CopyBlocksParams {
     int32_t num_pairs;
 };
 hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t s);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, hipStream_t s);
 
 // Quantizing write of the INT8 cache: per (token, kv head) row, s = max|x| / 127 and
 // q = round_half_even(x / s) into the int8 caches and the fp32 scale arrays.

@@ -167,7 +167,28 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksParams p) {
     }
 }
 
+// Measurement aid: the practical HBM read ceiling the HBM-bound kernels are compared with.
+// Grid-stride 16-byte non-temporal loads over n16 vectors; the XOR of every word is stored
+// only if it equals a constant, so the loads cannot be dropped and (almost) nothing is
+// written.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                          uint32_t* sink) {
+    uint32_t acc = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+        const u32x4 v = __builtin_nontemporal_load(src + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, hipStream_t s) {
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                       static_cast<const u32x4*>(src), bytes / 16, sink);
+    return hipGetLastError();
+}
 
 hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t s) {
     const bool v16 = p.block_bytes % 16 == 0 && reinterpret_cast<uintptr_t>(p.pool) % 16 == 0;
