@@ -381,6 +381,35 @@ PKV_API int pkv_paged_attn_decode_ex(void* out, float* lse_out, const void* q, c
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): pkv_paged_attn_decode_append (both
+ * passes, stages = 3) with no workspace argument.  The split pass keeps its partial states
+ * in a fixed array inside the library, PKV_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, which
+ * each GPU the library runs on holds until the process ends.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine); the caller still owns q, the new rows, the
+ * caches, the table, the lengths, out, lse_out and slot_mapping_out.
+ *   - A batch whose partial states exceed the array (pkv_decode_workspace_size(...) above
+ *     PKV_NOALLOC_SCRATCH_BYTES; the Llama-7B decode layer with 32 sequences of up to 2K
+ *     tokens needs about 4.3 MB) returns PKV_ERR_WORKSPACE before anything is enqueued.
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap on a GPU (two
+ *     streams, two host threads) race and give undefined results; calls ordered on one
+ *     stream are safe.  Nothing in the array needs clearing between calls.
+ *   - The stream must belong to the current device (its copy of the array is looked up once,
+ *     on the first call on that device).
+ * Arguments, support, preconditions and results as for pkv_paged_attn_decode_append.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+PKV_API int pkv_paged_attn_decode_append_noalloc(void* out, float* lse_out, const void* q,
+                                         const void* k_new, const void* v_new, void* k_cache,
+                                         void* v_cache, const int32_t* block_table,
+                                         const int32_t* seq_lens_kv, int64_t* slot_mapping_out,
+                                         int32_t batch, int32_t max_blocks_per_seq,
+                                         int32_t max_seq_len_kv, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t block_size, int64_t num_blocks,
+                                         float softmax_scale, int32_t dtype, void* stream);
+
+/*
  * Multi-token decode (MTP: next_n + 1 = num_q_tokens query tokens per sequence, causal;
  * "KVCache Optimization Skill", Appendix E, sparse_mode 3 with next_n): sequence b's rows
  * are q[b * num_q_tokens + i], i < num_q_tokens, the last num_q_tokens of its

@@ -26,7 +26,7 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_decode_workspace_size", "pkv_paged_attn_decode_int8",
            "pkv_paged_attn_decode",
            "pkv_paged_attn_decode_split", "pkv_paged_attn_decode_combine",
-           "pkv_paged_attn_decode_append",
+           "pkv_paged_attn_decode_append", "pkv_paged_attn_decode_append_noalloc",
            "pkv_paged_attn_decode_ex", "pkv_paged_attn_varlen",
            "pkv_paged_attn_varlen_ex", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
            "pkv_bm_add", "pkv_bm_fork", "pkv_bm_append", "pkv_bm_decode_step", "pkv_bm_free",
@@ -90,6 +90,9 @@ def lib() -> ctypes.CDLL:
                                                i32, i32, i32, i64, f32, i32, i32, p, sz, p]
     L.pkv_stream_read.restype = ctypes.c_int
     L.pkv_stream_read.argtypes = [p, i64, p, i32, p]
+    L.pkv_paged_attn_decode_append_noalloc.restype = ctypes.c_int
+    L.pkv_paged_attn_decode_append_noalloc.argtypes = [p, p, p, p, p, p, p, p, p, p, i32, i32,
+                                                       i32, i32, i32, i32, i32, i64, f32, i32, p]
     L.pkv_paged_attn_decode_ex.restype = ctypes.c_int
     L.pkv_paged_attn_decode_ex.argtypes = [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
                                            i32, i32, i32, i64, f32, i32, i32, i32, p, sz, p]
@@ -462,6 +465,23 @@ def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seq
                                        seq_lens_kv, max_seq_len_kv, softmax_scale, 3, out, lse,
                                        workspace, slots_out, window)
     _check(lib().pkv_paged_attn_decode_ex(*args))
+    return out, lse
+
+
+def paged_attn_decode_append_noalloc(q, k_new, v_new, k_cache, v_cache, block_table,
+                                     seq_lens_kv, max_seq_len_kv, softmax_scale, out, lse=None,
+                                     slots_out=None):
+    """pkv_paged_attn_decode_append_noalloc: the write-and-attend decode step with the partial
+    states in the library's fixed per-GPU scratch (no workspace; `out` is the caller's)."""
+    _dev(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv, out, lse, slots_out)
+    B, hq, d = q.shape
+    _batch_rows(B, block_table, seq_lens_kv)
+    nb, bs, hkv, _ = k_cache.shape
+    _check(lib().pkv_paged_attn_decode_append_noalloc(
+        _ptr(out), _ptr(lse), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_table), _ptr(seq_lens_kv), _ptr(slots_out), B, block_table.shape[1],
+        max_seq_len_kv, hq, hkv, d, bs, nb, float(softmax_scale), _dtype_code(q),
+        _stream(q.device)))
     return out, lse
 
 

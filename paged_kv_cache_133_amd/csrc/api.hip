@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/pagedkv.h"
 #include "pkv_internal.h"
 
@@ -665,6 +667,75 @@ int pkv_paged_attn_decode_ex(void* out, float* lse_out, const void* q, const voi
                           num_kv_heads, head_dim, block_size, num_blocks, softmax_scale, dtype,
                           window, stages, workspace, workspace_bytes, (hipStream_t)stream,
                           "decode_ex");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ allocation-free decode step
+// The split pass's partial states of pkv_paged_attn_decode_append_noalloc live in this
+// fixed array instead of a caller workspace: one copy per GPU the library runs on, held
+// until the process ends, shared by every call on that GPU (calls that overlap on one GPU
+// race).  Nothing in it has to start at zero: the split pass writes every partial state
+// and tile prefix the combine reads, in each call.
+static __device__ __align__(256) uint8_t scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current GPU's copy of `scratch`, looked up once per device with
+// that device current.  In host code the array's name only identifies the symbol; it is
+// never a device address.
+int scratch_on_current_device(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "decode_append_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PKV_ERR_UNSUPPORTED, "decode_append_noalloc: device %d (at most %d devices)", dev,
+                    kMaxDevices);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "decode_append_noalloc: hipGetSymbolAddress(scratch)");
+        if (!p) return fail(PKV_ERR_HIP, "decode_append_noalloc: no device address for the scratch array");
+        g_scratch_ptr[dev].store(p, std::memory_order_release);   // the same value from any racer
+    }
+    *ptr = p;
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attn_decode_append_noalloc(void* out, float* lse_out, const void* q,
+                                         const void* k_new, const void* v_new, void* k_cache,
+                                         void* v_cache, const int32_t* block_table,
+                                         const int32_t* seq_lens_kv, int64_t* slot_mapping_out,
+                                         int32_t batch, int32_t max_blocks_per_seq,
+                                         int32_t max_seq_len_kv, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t block_size, int64_t num_blocks,
+                                         float softmax_scale, int32_t dtype, void* stream) {
+    if (!k_new || !v_new) return fail(PKV_ERR_NULL, "decode_append_noalloc: NULL k_new or v_new");
+    void* ws = nullptr;
+    int rc = scratch_on_current_device(&ws);
+    if (rc != PKV_OK) return rc;
+    rc = run_decode_mha(out, lse_out, q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
+                        slot_mapping_out, batch, max_blocks_per_seq, max_seq_len_kv, num_q_heads,
+                        num_kv_heads, head_dim, block_size, num_blocks, softmax_scale, dtype, 0, 3,
+                        ws, (size_t)PKV_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream,
+                        "decode_append_noalloc");
+    if (rc == PKV_ERR_WORKSPACE) {   // every other argument was accepted before this check
+        const size_t need = pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len_kv).ws_bytes;
+        return fail(PKV_ERR_WORKSPACE,
+                    "decode_append_noalloc: this batch needs %zu bytes of partial states; the fixed "
+                    "scratch holds %zu (use pkv_paged_attn_decode_append with a workspace, or fewer "
+                    "sequences, heads or a smaller max_seq_len_kv)",
+                    need, (size_t)PKV_NOALLOC_SCRATCH_BYTES);
+    }
+    return rc;
 }
 
 size_t pkv_decode_mtp_workspace_size(int32_t batch, int32_t num_q_tokens, int32_t num_q_heads,
