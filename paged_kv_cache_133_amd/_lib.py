@@ -15,7 +15,10 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+# PKV_LIBRARY_PATH names another build of the library (the host-sanitizer test loads a
+# host-only ASan/UBSan build this way); by default the one built next to this file.
+LIB_PATH = (os.environ.get("PKV_LIBRARY_PATH")
+            or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so"))
 
 PKV_F32, PKV_BF16 = 0, 1
 STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_SHAPE", -3: "PKV_ERR_DTYPE",

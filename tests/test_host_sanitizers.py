@@ -1,0 +1,110 @@
+"""Host code under AddressSanitizer and UndefinedBehaviorSanitizer, on the CPU.
+
+The library is rebuilt with its host code (C-ABI argument checks, the block manager
+with its hash map, vectors and reference counts, the step runner's host objects) under
+-fsanitize=address,undefined (`-Xarch_host`: the GPU code is compiled as usual and never
+run here), and the C oracle is compiled with the same sanitizers; both use the LLVM
+sanitizer runtime, preloaded into a child Python.  The child then runs the block-manager random walk against the model, the
+ABI argument checks, and the oracle's pins.  Any sanitizer report aborts the child and
+fails this test.  ("Paged KV Cache and Packed Sequence", 5.2, names the bugs this
+catches: overwrites, leaks and reference counts released wrongly.)  No GPU is used: none
+of the tests the child runs launches a kernel."""
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "paged_kv_cache_133_amd", "csrc")
+HOST_SOURCES = ["api", "write", "norm_rope", "decode", "int8_kv", "mla_attn", "varlen_attn",
+                "gqa_attn", "block_manager", "runner"]
+SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+       "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def _tool(path):
+    return path if os.path.exists(path) else None
+
+
+HIPCC = _tool("/opt/rocm/bin/hipcc") or shutil.which("hipcc")
+CLANG = _tool("/opt/rocm/llvm/bin/clang") or shutil.which("clang")
+
+
+def _runtime():
+    hits = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+    return hits[0] if hits else None
+
+
+pytestmark = pytest.mark.skipif(not (HIPCC and CLANG and _runtime()),
+                                reason="needs hipcc, clang and the LLVM ASan runtime")
+
+
+def _run(cmd, **kw):
+    r = subprocess.run(cmd, capture_output=True, text=True, **kw)
+    assert r.returncode == 0, f"{' '.join(cmd[:3])}...: {r.stderr[-3000:]}"
+    return r
+
+
+@pytest.fixture(scope="module")
+def sanitized(tmp_path_factory):
+    out = tmp_path_factory.mktemp("sanitize")
+    objs = []
+    procs = []
+    for name in HOST_SOURCES:
+        obj = str(out / f"{name}.o")
+        objs.append(obj)
+        procs.append(subprocess.Popen(
+            [HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+             "-fno-omit-frame-pointer", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             *SAN, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, f"{name}.hip"),
+             "-o", obj], stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+    for p in procs:
+        _, err = p.communicate()
+        assert p.returncode == 0, err[-3000:]
+    lib = str(out / "libpagedkv_hostsan.so")
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *SAN, *objs, "-o", lib])
+    orc = str(out / "liboracle_san.so")
+    _run([CLANG, "-O1", "-g", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-fno-omit-frame-pointer",
+          "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+          os.path.join(ROOT, "oracle", "pkv_oracle.c"), "-o", orc, "-lm"])
+    return lib, orc
+
+
+def _child(lib, orc, tests):
+    env = dict(os.environ)
+    libomp = os.path.join(os.path.dirname(CLANG), "..", "lib")
+    env.update({
+        "LD_PRELOAD": _runtime(),
+        "LD_LIBRARY_PATH": os.path.abspath(libomp) + ":" + env.get("LD_LIBRARY_PATH", ""),
+        # Python itself is not instrumented and keeps objects to the end: no leak check;
+        # any other report aborts the child.
+        "ASAN_OPTIONS": "detect_leaks=0:abort_on_error=1:halt_on_error=1",
+        "UBSAN_OPTIONS": "halt_on_error=1:print_stacktrace=1",
+        "PKV_LIBRARY_PATH": lib,
+        "PKV_ORACLE_LIB_OVERRIDE": orc,
+        "HIP_VISIBLE_DEVICES": "",
+    })
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        "-m", "not gpu", *tests], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=900)
+    tail = (r.stdout[-2500:] + "\n" + r.stderr[-2500:])
+    assert r.returncode == 0, tail
+    assert "ERROR: AddressSanitizer" not in r.stderr and "runtime error:" not in r.stderr, tail
+    return r.stdout
+
+
+def test_block_manager_and_abi_under_sanitizers(sanitized):
+    lib, orc = sanitized
+    out = _child(lib, orc, ["tests/test_block_manager.py", "tests/test_abi.py"])
+    assert " passed" in out
+
+
+def test_oracle_pins_under_sanitizers(sanitized):
+    lib, orc = sanitized
+    out = _child(lib, orc, ["tests/test_oracle_index.py", "tests/test_oracle_attention.py",
+                            "tests/test_oracle_int8.py", "tests/test_oracle_sizes_pack.py",
+                            "tests/test_oracle_block_manager.py"])
+    assert " passed" in out
