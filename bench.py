@@ -352,9 +352,12 @@ def step_description(w, path):
         return ("slot_mapping, kv_cache_write_int8_mla (quantizing write of nope and rope), "
                 "decode_mla_int8 split pass, combine")
     if int8_workload(w):
-        kind = "range pass" if w.num_q_heads // w.num_kv_heads > 4 else "split pass"
-        return ("slot_mapping, kv_cache_write_int8 (quantizing write), decode_int8 %s, "
-                "combine" % kind)
+        if w.num_q_heads // w.num_kv_heads > 4:
+            return "slot_mapping, kv_cache_write_int8 (quantizing write), decode_int8 range pass, combine"
+        if path == "fused":
+            return ("paged_attn_decode_int8_append: split pass that also quantizes and writes the "
+                    "new token (slot_mapping + quantizing write + split-KV attention), then combine")
+        return "slot_mapping, kv_cache_write_int8 (quantizing write), decode_int8 split pass, combine"
     if w.q_tokens:
         return ("kv_cache_append (slot_mapping + write of the step's %d rows per sequence), "
                 "decode_mtp range pass, combine" % w.q_tokens)
@@ -584,7 +587,10 @@ def main():
     slot_call = _lib.prepare_slot_mapping(table, lb, cu, w.block_size, T, slots)
     fused = args.path == "fused"
     reps = []
-    slot_first = args.path == "separate" or int8
+    # INT8 with 1..4 query heads per kv head: the quantizing write folds into the split pass
+    # (the fused path); otherwise slot_mapping and the quantizing write run first.
+    int8_fused = int8 and not w.mode == "mla" and fused and w.num_q_heads // w.num_kv_heads <= 4
+    slot_first = args.path == "separate" or (int8 and not int8_fused)
     for r in range(R):
         if int8 and mla:
             nc, rc, ns, rs = (pool_i8["k"], pool_i8["v"], pool_sc["k"], pool_sc["v"]) if r == 0 else (
@@ -600,6 +606,13 @@ def main():
         if int8:
             ki8, vi8, ksc, vsc = (pool_i8["k"], pool_i8["v"], pool_sc["k"], pool_sc["v"]) if r == 0 else (
                 pool_i8["k"].clone(), pool_i8["v"].clone(), pool_sc["k"].clone(), pool_sc["v"].clone())
+            if int8_fused:
+                split, combine, _ = _lib.prepare_decode_int8_append(
+                    case.q, case.new_k, case.new_v, ki8, vi8, ksc, vsc, table, la,
+                    case.max_len_after, w.scale, out=out, lse=lse, workspace=ws, slots_out=slots,
+                    window=w.window)
+                reps.append((None, split, combine))
+                continue
             write = _lib.prepare_kv_cache_write_int8(case.new_k, case.new_v, ki8, vi8, ksc, vsc, slots)
             split, combine, _ = _lib.prepare_decode_int8(case.q, ki8, vi8, ksc, vsc, table, la,
                                                          case.max_len_after, w.scale, out=out,

@@ -39,7 +39,8 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_runner_create", "pkv_runner_destroy", "pkv_runner_capture_begin",
            "pkv_runner_capture_end", "pkv_runner_graph", "pkv_runner_host_buffer",
            "pkv_runner_launch", "pkv_decode_mtp_workspace_size", "pkv_paged_attn_decode_mtp",
-           "pkv_kv_cache_write_int8_mla", "pkv_paged_attn_decode_mla_int8", "pkv_stream_read")
+           "pkv_kv_cache_write_int8_mla", "pkv_paged_attn_decode_mla_int8", "pkv_stream_read",
+           "pkv_paged_attn_decode_int8_append")
 
 
 class PagedKVError(RuntimeError):
@@ -78,6 +79,9 @@ def lib() -> ctypes.CDLL:
     L.pkv_paged_attn_decode_int8.restype = ctypes.c_int
     L.pkv_paged_attn_decode_int8.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32,
                                              i32, i32, i64, f32, i32, i32, p, sz, p]
+    L.pkv_paged_attn_decode_int8_append.restype = ctypes.c_int
+    L.pkv_paged_attn_decode_int8_append.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p, i32, i32, i32,
+                                                    i32, i32, i32, i32, i64, f32, i32, i32, p, sz, p]
     L.pkv_kv_rmsnorm_rope_cache.restype = ctypes.c_int
     L.pkv_kv_rmsnorm_rope_cache.argtypes = [p, p, p, p, p, p, p, i64, i32, i32, i32, i64, f32, i32, p]
     L.pkv_decode_workspace_size.restype = sz
@@ -342,6 +346,57 @@ def prepare_decode_int8(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_
         calls.append(PreparedCall(lib().pkv_paged_attn_decode_int8, args,
                                   (q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens_kv,
                                    out, lse, workspace)))
+    return calls[0], calls[1], out
+
+
+def _decode_int8_append_args(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table,
+                             seq_lens_kv, max_seq_len_kv, softmax_scale, stages, out, lse,
+                             workspace, slots_out, window):
+    _dev(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens_kv, out, lse,
+         workspace, slots_out)
+    B, hq, d = q.shape
+    _batch_rows(B, block_table, seq_lens_kv)
+    nb, bs, hkv, _ = k_cache.shape
+    _scale_shape(k_scale, v_scale, nb, hkv, bs)
+    if tuple(k_new.shape) != (B, hkv, d) or tuple(v_new.shape) != (B, hkv, d):
+        raise ValueError(f"k_new/v_new must be [{B}, {hkv}, {d}]")
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = new_decode_workspace(B, hq, hkv, d, max_seq_len_kv, q.device)
+    args = (_ptr(out), _ptr(lse), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+            _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens_kv), _ptr(slots_out), B,
+            block_table.shape[1], max_seq_len_kv, hq, hkv, d, bs, nb, float(softmax_scale),
+            int(window), stages, _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(q.device))
+    return args, out, workspace
+
+
+def paged_attn_decode_int8_append(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table,
+                                  seq_lens_kv, max_seq_len_kv, softmax_scale, out=None, lse=None,
+                                  workspace=None, slots_out=None, window=0):
+    """Quantize, write and attend to this step's token in one pass over the INT8 cache (see
+    pkv_paged_attn_decode_int8_append).  Returns (out, lse)."""
+    args, out, _ = _decode_int8_append_args(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                                            block_table, seq_lens_kv, max_seq_len_kv,
+                                            softmax_scale, 3, out, lse, workspace, slots_out, window)
+    _check(lib().pkv_paged_attn_decode_int8_append(*args))
+    return out, lse
+
+
+def prepare_decode_int8_append(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table,
+                               seq_lens_kv, max_seq_len_kv, softmax_scale, out=None, lse=None,
+                               workspace=None, slots_out=None, window=0):
+    """(split pass with the folded write, combine pass) prepared calls."""
+    calls = []
+    for stages in (1, 2):
+        args, out, workspace = _decode_int8_append_args(q, k_new, v_new, k_cache, v_cache, k_scale,
+                                                        v_scale, block_table, seq_lens_kv,
+                                                        max_seq_len_kv, softmax_scale, stages, out,
+                                                        lse, workspace, slots_out, window)
+        calls.append(PreparedCall(lib().pkv_paged_attn_decode_int8_append, args,
+                                  (q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table,
+                                   seq_lens_kv, out, lse, workspace, slots_out)))
     return calls[0], calls[1], out
 
 

@@ -892,25 +892,37 @@ int pkv_kv_cache_write_int8(const void* k_new, const void* v_new, void* k_cache,
                       "kv_cache_write_int8 launch");
 }
 
-int pkv_paged_attn_decode_int8(void* out, float* lse_out, const void* q, const void* k_cache,
-                               const void* v_cache, const float* k_scale, const float* v_scale,
-                               const int32_t* block_table, const int32_t* seq_lens_kv, int32_t batch,
-                               int32_t max_blocks_per_seq, int32_t max_seq_len_kv, int32_t num_q_heads,
-                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                               int64_t num_blocks, float softmax_scale, int32_t window, int32_t stages,
-                               void* workspace, size_t workspace_bytes, void* stream) {
-    if (stages < 1 || stages > 3) return fail(PKV_ERR_SHAPE, "decode_int8: stages must be 1, 2 or 3");
+}  // extern "C"
+
+namespace {
+
+// Decode over the INT8 caches; with k_new / v_new (bf16, 1..4 query heads per kv head) the
+// step's token is quantized, written and attended in the same pass.
+int run_decode_int8(void* out, float* lse_out, const void* q, const void* k_new, const void* v_new,
+                    void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                    const int32_t* block_table, const int32_t* seq_lens_kv, int64_t* slot_mapping_out,
+                    int32_t batch, int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int64_t num_blocks, float softmax_scale, int32_t window, int32_t stages,
+                    void* workspace, size_t workspace_bytes, void* stream, const char* who) {
+    if (stages < 1 || stages > 3) return fail(PKV_ERR_SHAPE, "%s: stages must be 1, 2 or 3", who);
     // 1..4 query heads per kv head: the split kernel; 5..16: the range-streaming kernel, whose
     // code loads need blocks of at least 1024 / head_dim keys.
     const int group = num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 ? num_q_heads / num_kv_heads : 0;
     const bool ranges = group > 4;
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return fail(PKV_ERR_NULL, "%s: k_new and v_new must be given together or not at all", who);
+    if (k_new && ranges)
+        return fail(PKV_ERR_UNSUPPORTED,
+                    "%s: the write folded into the pass takes 1..4 query heads per kv head (got %d); "
+                    "write with pkv_kv_cache_write_int8, then pkv_paged_attn_decode_int8", who, group);
     if (ranges && (group > 16 || (head_dim != 64 && head_dim != 128) || block_size <= 0 ||
                    (block_size & (block_size - 1)) || block_size < 1024 / head_dim ||
                    !pkv::gqa_stream_supported(PKV_BF16, group, head_dim, log2i(block_size), batch)))
         return fail(PKV_ERR_UNSUPPORTED,
-                    "decode_int8: %d query heads per kv head needs at most 16, head_dim 64 or 128, "
+                    "%s: %d query heads per kv head needs at most 16, head_dim 64 or 128, "
                     "block_size >= %d and batch <= 1024 (got head_dim %d, block_size %d, batch %d)",
-                    group, head_dim == 64 ? 16 : 8, head_dim, block_size, batch);
+                    who, group, head_dim == 64 ? 16 : 8, head_dim, block_size, batch);
     pkv::DecodeParams p;
     pkv::DecodePlan plan{};
     bool idle = false;
@@ -920,12 +932,25 @@ int pkv_paged_attn_decode_int8(void* out, float* lse_out, const void* q, const v
                             num_kv_heads, head_dim, head_dim, 0, block_size, num_blocks, softmax_scale,
                             PKV_BF16, workspace, workspace_bytes, &idle, window, ranges, true);
     if (rc != PKV_OK || idle) return rc;
-    if (ranges != (p.parts > 0)) return fail(PKV_ERR_UNSUPPORTED, "decode_int8: no kernel for this shape");
-    if (!k_scale || !v_scale) return fail(PKV_ERR_NULL, "decode_int8: NULL scale array");
+    if (ranges != (p.parts > 0)) return fail(PKV_ERR_UNSUPPORTED, "%s: no kernel for this shape", who);
+    if (!k_scale || !v_scale) return fail(PKV_ERR_NULL, "%s: NULL scale array", who);
     if (!aligned16(k_scale) || !aligned16(v_scale))
-        return fail(PKV_ERR_ALIGN, "decode_int8: scale arrays must be 16-byte aligned");
+        return fail(PKV_ERR_ALIGN, "%s: scale arrays must be 16-byte aligned", who);
     p.k_scale = k_scale;
     p.v_scale = v_scale;
+    if (k_new) {
+        if (!aligned16(k_new) || !aligned16(v_new))
+            return fail(PKV_ERR_ALIGN, "%s: k_new and v_new must be 16-byte aligned", who);
+        if (k_cache == v_cache || k_scale == v_scale)
+            return fail(PKV_ERR_SHAPE, "%s: the K and V caches (and their scales) must differ", who);
+        p.k_new = k_new;
+        p.v_new = v_new;
+        p.k_cache_w = k_cache;
+        p.v_cache_w = v_cache;
+        p.k_scale_w = k_scale;
+        p.v_scale_w = v_scale;
+        p.slots_out = slot_mapping_out;
+    }
     hipStream_t s = (hipStream_t)stream;
     if (stages & 1) {
         rc = hip_status(pkv::launch_decode_int8(p, head_dim, s), "decode_int8 split launch");
@@ -933,6 +958,43 @@ int pkv_paged_attn_decode_int8(void* out, float* lse_out, const void* q, const v
     }
     if ((stages & 2) && needs_combine(p, plan)) return launch_combine_for(p, head_dim, PKV_BF16, s);
     return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attn_decode_int8(void* out, float* lse_out, const void* q, const void* k_cache,
+                               const void* v_cache, const float* k_scale, const float* v_scale,
+                               const int32_t* block_table, const int32_t* seq_lens_kv, int32_t batch,
+                               int32_t max_blocks_per_seq, int32_t max_seq_len_kv, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, float softmax_scale, int32_t window, int32_t stages,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    return run_decode_int8(out, lse_out, q, nullptr, nullptr, const_cast<void*>(k_cache),
+                           const_cast<void*>(v_cache), const_cast<float*>(k_scale),
+                           const_cast<float*>(v_scale), block_table, seq_lens_kv, nullptr, batch,
+                           max_blocks_per_seq, max_seq_len_kv, num_q_heads, num_kv_heads, head_dim,
+                           block_size, num_blocks, softmax_scale, window, stages, workspace,
+                           workspace_bytes, stream, "decode_int8");
+}
+
+int pkv_paged_attn_decode_int8_append(void* out, float* lse_out, const void* q, const void* k_new,
+                                      const void* v_new, void* k_cache, void* v_cache, float* k_scale,
+                                      float* v_scale, const int32_t* block_table,
+                                      const int32_t* seq_lens_kv, int64_t* slot_mapping_out,
+                                      int32_t batch, int32_t max_blocks_per_seq,
+                                      int32_t max_seq_len_kv, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int64_t num_blocks, float softmax_scale, int32_t window,
+                                      int32_t stages, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+    if (!k_new || !v_new) return fail(PKV_ERR_NULL, "decode_int8_append: NULL k_new or v_new");
+    return run_decode_int8(out, lse_out, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                           block_table, seq_lens_kv, slot_mapping_out, batch, max_blocks_per_seq,
+                           max_seq_len_kv, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                           softmax_scale, window, stages, workspace, workspace_bytes, stream,
+                           "decode_int8_append");
 }
 
 int pkv_paged_attn_varlen(void* out, float* lse_out, const void* q, const int32_t* cu_seqlens_q,

@@ -94,7 +94,13 @@ __global__ __launch_bounds__(256) void kv_write_int8_kernel(QuantWriteParams p) 
 // ------------------------------------------------------------------ int8 decode
 // Register budget: one query head per kv head fits 128 VGPRs (4 waves per SIMD, 77 -> 74 us
 // on the Llama-7B INT8 step); four fit 256 without accumulation registers (2 waves).
-template <int D, int GP>
+// APPEND (the write folded into the pass, as in decode_split_kernel): the token at
+// seq_lens[b] - 1 comes from the bf16 rows k_new / v_new [B][Hkv][D]; the wave whose keys
+// hold it quantizes it as the writer does (the same operations, so the same codes and scale
+// bit for bit) and stores the codes and scales at its slot (reported in slots_out) before
+// its loop, which then reads it back like any cached token.  A row longer than the length
+// bound writes nothing (slot -1) and attends to its first len_cap cached keys.
+template <int D, int GP, bool APPEND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP == 1 ? 4 : 2)))
 void decode_int8_kernel(DecodeParams p) {
     constexpr int EPL = 16;                           // codes per lane per load
@@ -130,6 +136,10 @@ void decode_int8_kernel(DecodeParams p) {
         if (even > 0 && (int64_t)(ns - 1) * even < L - ksa) split_keys = even;
     }
     const int t0 = ksa + split * split_keys;
+    const bool app = APPEND && p.seq_lens[b] <= p.len_cap;
+    const int pos_new = app ? L - 1 : -1;
+    if (APPEND && !app && split == 0 && p.slots_out && kvh == 0 && threadIdx.x == 0)
+        p.slots_out[b] = -1;
     if (L <= 0) {   // no visible key: output 0, lse -inf
         if (split == 0) {
             for (int i = threadIdx.x; i < p.group * D; i += blockDim.x) {
@@ -172,6 +182,39 @@ void decode_int8_kernel(DecodeParams p) {
 
     const int64_t slot_stride = (int64_t)p.hkv * D;               // bytes per cache row
     const int64_t head_off = (int64_t)kvh * D + col * EPL;
+    // Append: the wave whose keys hold the new token quantizes its K and V rows (two values
+    // per lane), stores the codes and scales at its slot and waits for those stores; its loop
+    // then reads the token back like any cached one.  No other wave touches that token.
+    if (APPEND && pos_new >= w0 && pos_new < w1) {
+        const int32_t phys = min(max(trow[pos_new >> p.bs_log2], 0), last_block);
+        const int64_t slot = ((int64_t)phys << p.bs_log2) | (pos_new & bs_mask);
+        const int64_t sc_idx = (((int64_t)phys * p.hkv + kvh) << p.bs_log2) | (pos_new & bs_mask);
+        const int64_t src_off = (((int64_t)b * p.hkv + kvh) * D + 2 * (lane % (D / 2))) * 2;
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const uint32_t pair = *reinterpret_cast<const uint32_t*>(
+                reinterpret_cast<const uint8_t*>(which ? p.v_new : p.k_new) + src_off);
+            const float x0 = bf16_lo(pair), x1 = bf16_hi(pair);
+            float amax = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+            for (int sft = 1; sft < D / 2; sft <<= 1) amax = fmaxf(amax, __shfl_xor(amax, sft, 64));
+            const float sc = __fdiv_rn(amax, 127.0f);
+            uint32_t w = 0u;
+            if (sc > 0.0f) {
+                const float q0 = fminf(fmaxf(rintf(__fdiv_rn(x0, sc)), -127.0f), 127.0f);
+                const float q1 = fminf(fmaxf(rintf(__fdiv_rn(x1, sc)), -127.0f), 127.0f);
+                w = ((uint32_t)(int)q0 & 0xffu) | (((uint32_t)(int)q1 & 0xffu) << 8);
+            }
+            if (lane < D / 2) {
+                uint8_t* dst = reinterpret_cast<uint8_t*>(which ? p.v_cache_w : p.k_cache_w) +
+                               slot * slot_stride + (int64_t)kvh * D + 2 * lane;
+                *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
+                if (lane == 0) (which ? p.v_scale_w : p.k_scale_w)[sc_idx] = sc;
+            }
+        }
+        if (p.slots_out && kvh == 0 && lane == 0) p.slots_out[b] = slot;
+        __threadfence_block();   // the stores complete before this wave's loads of the token
+    }
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k_cache) + head_off;
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v_cache) + head_off;
 
@@ -361,18 +404,24 @@ hipError_t launch_kv_write_int8_mla(const QuantWriteParams& p, int in_dtype, hip
     return hipGetLastError();
 }
 
+template <int D, bool APPEND>
+void launch_decode_int8_d(const DecodeParams& p, dim3 grid, hipStream_t s) {
+    const int gp = p.group <= 1 ? 1 : (p.group <= 2 ? 2 : 4);
+    if (gp == 1) hipLaunchKernelGGL((decode_int8_kernel<D, 1, APPEND>), grid, dim3(256), 0, s, p);
+    else if (gp == 2) hipLaunchKernelGGL((decode_int8_kernel<D, 2, APPEND>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((decode_int8_kernel<D, 4, APPEND>), grid, dim3(256), 0, s, p);
+}
+
 hipError_t launch_decode_int8(const DecodeParams& p, int head_dim, hipStream_t s) {
     if (p.parts > 0) return launch_gqa_decode_int8(p, head_dim, s);
     const dim3 grid((unsigned)((int64_t)p.hkv * p.batch * p.max_splits));
-    const int gp = p.group <= 1 ? 1 : (p.group <= 2 ? 2 : 4);
+    const bool append = p.k_new != nullptr;
     if (head_dim == 64) {
-        if (gp == 1) hipLaunchKernelGGL((decode_int8_kernel<64, 1>), grid, dim3(256), 0, s, p);
-        else if (gp == 2) hipLaunchKernelGGL((decode_int8_kernel<64, 2>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((decode_int8_kernel<64, 4>), grid, dim3(256), 0, s, p);
+        if (append) launch_decode_int8_d<64, true>(p, grid, s);
+        else launch_decode_int8_d<64, false>(p, grid, s);
     } else {
-        if (gp == 1) hipLaunchKernelGGL((decode_int8_kernel<128, 1>), grid, dim3(256), 0, s, p);
-        else if (gp == 2) hipLaunchKernelGGL((decode_int8_kernel<128, 2>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((decode_int8_kernel<128, 4>), grid, dim3(256), 0, s, p);
+        if (append) launch_decode_int8_d<128, true>(p, grid, s);
+        else launch_decode_int8_d<128, false>(p, grid, s);
     }
     return hipGetLastError();
 }

@@ -154,9 +154,13 @@ struct DecodeParams {
     // [B + 1] it leaves for its combine; ws_o / ws_ml then hold its partial states.
     int32_t parts;
     int32_t* tile_prefix;
-    // INT8 caches (launch_decode_int8): one fp32 scale per (slot, kv head) row, else null.
+    // INT8 caches (launch_decode_int8): one fp32 scale per (slot, kv head) row, else null;
+    // in append mode (k_new set, 1..4 query heads per kv head) the writable views of the
+    // code caches (k_cache_w / v_cache_w) and of the scales below take the new token.
     const float* k_scale;
     const float* v_scale;
+    float* k_scale_w;
+    float* v_scale_w;
     // Sliding window (band): > 0 keeps the `window` most recent keys of each sequence
     // (window_start below); 0 keeps all of them.  Splits and tiles then start at the
     // window start rounded down to a multiple of 32 keys.

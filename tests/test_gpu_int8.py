@@ -249,3 +249,95 @@ def test_int8_ranges_many_short_sequences():
                                         c.lens_after_tensor(DEV), c.max_len_after, c.w.scale, lse=lse)
     torch.cuda.synchronize()
     say(f"  max-abs error {_check(c, out, lse, kdeq, vdeq, 0):.3e}")
+
+
+def _code_pools(c):
+    """Two device copies of the INT8 pools (codes, [block][kv head][offset] scales): the
+    oracle's quantization of the case's bf16 pools."""
+    kq, ksc = oracle.quantize_rows(host(c.cache_k))
+    vq, vsc = oracle.quantize_rows(host(c.cache_v))
+    one = lambda: {"kc": torch.from_numpy(kq).to(DEV), "vc": torch.from_numpy(vq).to(DEV),  # noqa: E731
+                   "ks": torch.from_numpy(ksc).permute(0, 2, 1).contiguous().to(DEV),
+                   "vs": torch.from_numpy(vsc).permute(0, 2, 1).contiguous().to(DEV)}
+    return one(), one()
+
+
+@pytest.mark.parametrize("shape", [(32, 32, 128, 16), (8, 2, 64, 1), (16, 4, 128, 128),
+                                   (4, 1, 128, 32), (12, 4, 64, 64)],
+                         ids=lambda s: "hq%d_hkv%d_d%d_bs%d" % s)
+@pytest.mark.parametrize("window", [0, 100])
+def test_int8_decode_append(shape, window):
+    """Quantize, write and attend to the step's token in one pass: the slots, the written codes
+    and scales (whole pools) and the outputs equal slot_mapping + the quantizing write +
+    decode_int8 bit for bit, and the output matches the oracle over the dequantized pools."""
+    Hq, Hkv, D, bs = shape
+    L = [1, 31, 32, 33, 300, 1500, 3000]
+    say(f"int8 decode_append {shape} window {window}")
+    w = wl.custom(batch=len(L), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                  dtype="bf16")
+    c = wl.make_case(w, np.array(L) - 1, [1] * len(L), seed=Hq * 5 + bs + window, device=DEV,
+                     poison=False)
+    a, s = _code_pools(c)
+    table, la = c.table_tensor(DEV), c.lens_after_tensor(DEV)
+    B = len(L)
+    slots_a = torch.full((B,), -2, dtype=torch.int64, device=DEV)
+    lse_a = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    out_a, _ = pkv.paged_attn_decode_int8_append(c.q, c.new_k, c.new_v, a["kc"], a["vc"], a["ks"],
+                                                 a["vs"], table, la, c.max_len_after, w.scale,
+                                                 lse=lse_a, slots_out=slots_a, window=window)
+    slots_s = pkv.slot_mapping(table, c.lens_before_tensor(DEV), c.cu_q_tensor(DEV), bs, B)
+    pkv.kv_cache_write_int8(c.new_k, c.new_v, s["kc"], s["vc"], s["ks"], s["vs"], slots_s)
+    lse_s = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    out_s, _ = pkv.paged_attn_decode_int8(c.q, s["kc"], s["vc"], s["ks"], s["vs"], table, la,
+                                          c.max_len_after, w.scale, lse=lse_s, window=window)
+    torch.cuda.synchronize()
+    assert torch.equal(slots_a, slots_s)
+    for key in ("kc", "vc"):
+        assert torch.equal(a[key], s[key]), key
+    for key in ("ks", "vs"):
+        assert torch.equal(a[key].view(torch.int32), s[key].view(torch.int32)), key
+    assert torch.equal(out_a.view(torch.int16), out_s.view(torch.int16))
+    assert torch.equal(lse_a.view(torch.int32), lse_s.view(torch.int32))
+    nb = c.num_blocks
+    kdeq = oracle.dequantize_rows(a["kc"].cpu().numpy().reshape(nb * bs, Hkv, D),
+                                  a["ks"].cpu().permute(0, 2, 1).contiguous().numpy().reshape(nb * bs, Hkv))
+    vdeq = oracle.dequantize_rows(a["vc"].cpu().numpy().reshape(nb * bs, Hkv, D),
+                                  a["vs"].cpu().permute(0, 2, 1).contiguous().numpy().reshape(nb * bs, Hkv))
+    err = _check(c, out_a, lse_a, kdeq.reshape(nb, bs, Hkv, D), vdeq.reshape(nb, bs, Hkv, D), window)
+    say(f"  max-abs error {err:.3e}")
+
+
+def test_int8_decode_append_headline_and_overlength_row():
+    """The INT8 headline workload (B = 32, 32 heads, lengths 513..2049) through the fused
+    call the bench times, against the separate write + decode bit for bit; then a row over
+    the length bound: nothing written for it (slot -1) and the same output as decode_int8."""
+    w = wl.WORKLOADS["llama7b_mha_int8"]
+    L, _ = wl.sample_lengths(w, 0)
+    Lp = np.asarray(L) + 1
+    say("int8 decode_append headline")
+    wc = wl.custom(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                   head_dim=w.head_dim, block_size=w.block_size, dtype="bf16")
+    c = wl.make_case(wc, Lp - 1, [1] * w.batch, seed=0, device=DEV, poison=False)
+    table, la = c.table_tensor(DEV), c.lens_after_tensor(DEV)
+    for cap in (c.max_len_after, int(np.sort(Lp)[-2])):     # the second bound cuts the longest row
+        a, s = _code_pools(c)
+        slots_a = torch.full((w.batch,), -2, dtype=torch.int64, device=DEV)
+        out_a, _ = pkv.paged_attn_decode_int8_append(c.q, c.new_k, c.new_v, a["kc"], a["vc"], a["ks"],
+                                                     a["vs"], table, la, cap, w.scale,
+                                                     slots_out=slots_a)
+        slots_s = pkv.slot_mapping(table, c.lens_before_tensor(DEV), c.cu_q_tensor(DEV),
+                                   w.block_size, w.batch)
+        over = la > cap
+        slots_s[over] = -1
+        keep = ~over
+        pkv.kv_cache_write_int8(c.new_k[keep], c.new_v[keep], s["kc"], s["vc"], s["ks"], s["vs"],
+                                slots_s[keep])
+        out_s, _ = pkv.paged_attn_decode_int8(c.q, s["kc"], s["vc"], s["ks"], s["vs"], table, la, cap,
+                                              w.scale)
+        torch.cuda.synchronize()
+        say(f"  bound {cap}: {int(over.sum())} rows over it")
+        assert torch.equal(slots_a, slots_s)
+        for key in ("kc", "vc", "ks", "vs"):
+            assert torch.equal(a[key].view(torch.int8) if key in ("kc", "vc") else a[key].view(torch.int32),
+                               s[key].view(torch.int8) if key in ("kc", "vc") else s[key].view(torch.int32)), key
+        assert torch.equal(out_a.view(torch.int16), out_s.view(torch.int16))
