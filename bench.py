@@ -364,8 +364,10 @@ def step_description(w, path):
     if w.mode == "varlen":
         return "kv_cache_append (slot_mapping + write), varlen causal attention"
     if w.mode == "mla":
-        return {"separate": "slot_mapping, kv_cache_write (nope + rope), MLA split pass, combine"}.get(
-            path, "kv_cache_append (nope + rope), MLA split pass, combine")
+        return {"separate": "slot_mapping, kv_cache_write (nope + rope), MLA split pass, combine",
+                "append": "kv_cache_append (nope + rope), MLA split pass, combine"}.get(
+            path, "paged_attn_decode_mla_append: MLA split pass that also writes the new latent "
+                  "row (slot_mapping + write of nope and rope + split-KV attention), then combine")
     return {"fused": "paged_attn_decode_append: split pass that also writes the new "
                      "token (slot_mapping + write + split-KV attention), then combine",
             "append": "kv_cache_append (slot_mapping + write), decode split, combine",
@@ -640,6 +642,14 @@ def main():
             attn = _lib.prepare_varlen(case.q, k, v, table, cu, la, case.max_new, w.scale,
                                        causal=True, out=out, lse=lse, window=w.window)
             reps.append((write, attn, None))
+            continue
+        if fused and mla:
+            split, combine, _ = _lib.prepare_decode_mla_append(case.q, case.q_rope, case.new_k,
+                                                               case.new_rope, k, rope, table, la,
+                                                               case.max_len_after, w.scale,
+                                                               out=out, lse=lse, workspace=ws,
+                                                               slots_out=slots)
+            reps.append((None, split, combine))
             continue
         if fused and not mla:
             split, combine, _ = _lib.prepare_decode_append(case.q, case.new_k, case.new_v, k, v,

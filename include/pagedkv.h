@@ -352,6 +352,28 @@ PKV_API int pkv_paged_attn_decode_append(void* out, float* lse_out, const void* 
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * The MLA-absorbed decode step with the cache write folded into the pass: for each
+ * sequence b, the step's latent row (nope_new[b] [512], rope_new[b] [64], bf16) is the key
+ * and value at position seq_lens_kv[b] - 1, read from those rows, and stored at its slot of
+ * cache_nope / cache_rope (reported in slot_mapping_out [batch], or -1 for a row longer than
+ * max_seq_len_kv, which writes nothing).  Equal to pkv_kv_cache_append of the two rows
+ * followed by pkv_paged_attn_decode with q_rope ("KVCache Optimization Skill", Mode 3 and
+ * 3.6: write by slot_mapping, then attention reads kv_len + 1 tokens).
+ *   q_nope [batch][num_q_heads][512], q_rope [batch][num_q_heads][64], out like q_nope;
+ *   cache_nope [nb][bs][1][512], cache_rope [nb][bs][1][64]; stages and workspace as for
+ *   pkv_paged_attn_decode_append (pkv_decode_workspace_size(batch, Hq, 1, 512, max) bytes).
+ */
+PKV_API int pkv_paged_attn_decode_mla_append(void* out, float* lse_out, const void* q_nope,
+                                     const void* q_rope, const void* nope_new,
+                                     const void* rope_new, void* cache_nope, void* cache_rope,
+                                     const int32_t* block_table, const int32_t* seq_lens_kv,
+                                     int64_t* slot_mapping_out, int32_t batch,
+                                     int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                                     int32_t num_q_heads, int32_t block_size, int64_t num_blocks,
+                                     float softmax_scale, int32_t stages, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * Packed varlen attention over the paged cache: sequence b owns query rows
  * [cu_seqlens_q[b], cu_seqlens_q[b+1]) of the packed stream (n_b rows) and
  * seq_lens_kv[b] = L'_b cached tokens, its own new rows included (they were written

@@ -9,6 +9,7 @@ from ._lib import (BlockManager, CapturedStep, PagedKVError, decode_workspace_si
                    kv_cache_write_int8_mla, paged_attn_decode_mla_int8,
                    kv_rmsnorm_rope_cache, lib, new_decode_workspace, paged_attn_decode,
                    paged_attn_decode_int8, paged_attn_decode_int8_append, paged_attn_decode_append,
+                   paged_attn_decode_mla_append,
                    paged_attn_decode_append_noalloc, paged_attn_decode_mtp,
                    paged_attn_varlen,
                    slot_mapping, upload, version)

@@ -40,7 +40,7 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_runner_capture_end", "pkv_runner_graph", "pkv_runner_host_buffer",
            "pkv_runner_launch", "pkv_decode_mtp_workspace_size", "pkv_paged_attn_decode_mtp",
            "pkv_kv_cache_write_int8_mla", "pkv_paged_attn_decode_mla_int8", "pkv_stream_read",
-           "pkv_paged_attn_decode_int8_append")
+           "pkv_paged_attn_decode_int8_append", "pkv_paged_attn_decode_mla_append")
 
 
 class PagedKVError(RuntimeError):
@@ -79,6 +79,9 @@ def lib() -> ctypes.CDLL:
     L.pkv_paged_attn_decode_int8.restype = ctypes.c_int
     L.pkv_paged_attn_decode_int8.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32,
                                              i32, i32, i64, f32, i32, i32, p, sz, p]
+    L.pkv_paged_attn_decode_mla_append.restype = ctypes.c_int
+    L.pkv_paged_attn_decode_mla_append.argtypes = [p, p, p, p, p, p, p, p, p, p, p, i32, i32, i32,
+                                                   i32, i32, i64, f32, i32, p, sz, p]
     L.pkv_paged_attn_decode_int8_append.restype = ctypes.c_int
     L.pkv_paged_attn_decode_int8_append.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p, i32, i32, i32,
                                                     i32, i32, i32, i32, i64, f32, i32, i32, p, sz, p]
@@ -397,6 +400,56 @@ def prepare_decode_int8_append(q, k_new, v_new, k_cache, v_cache, k_scale, v_sca
         calls.append(PreparedCall(lib().pkv_paged_attn_decode_int8_append, args,
                                   (q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table,
                                    seq_lens_kv, out, lse, workspace, slots_out)))
+    return calls[0], calls[1], out
+
+
+def _decode_mla_append_args(q, q_rope, nope_new, rope_new, cache_nope, cache_rope, block_table,
+                            seq_lens_kv, max_seq_len_kv, softmax_scale, stages, out, lse, workspace,
+                            slots_out):
+    _dev(q, q_rope, nope_new, rope_new, cache_nope, cache_rope, block_table, seq_lens_kv, out, lse,
+         workspace, slots_out)
+    B, hq, dn = q.shape
+    _batch_rows(B, block_table, seq_lens_kv, q_rope)
+    nb, bs = cache_nope.shape[:2]
+    if nope_new.numel() != B * 512 or rope_new.numel() != B * 64:
+        raise ValueError(f"nope_new / rope_new must hold {B} rows of 512 / 64")
+    if out is None:
+        out = torch.empty((B, hq, dn), dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = new_decode_workspace(B, hq, 1, dn, max_seq_len_kv, q.device)
+    args = (_ptr(out), _ptr(lse), _ptr(q), _ptr(q_rope), _ptr(nope_new), _ptr(rope_new),
+            _ptr(cache_nope), _ptr(cache_rope), _ptr(block_table), _ptr(seq_lens_kv),
+            _ptr(slots_out), B, block_table.shape[1], max_seq_len_kv, hq, bs, nb,
+            float(softmax_scale), stages, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(q.device))
+    return args, out, workspace
+
+
+def paged_attn_decode_mla_append(q, q_rope, nope_new, rope_new, cache_nope, cache_rope,
+                                 block_table, seq_lens_kv, max_seq_len_kv, softmax_scale, out=None,
+                                 lse=None, workspace=None, slots_out=None):
+    """MLA decode step that also writes the step's latent rows (see
+    pkv_paged_attn_decode_mla_append).  Returns (out, lse)."""
+    args, out, _ = _decode_mla_append_args(q, q_rope, nope_new, rope_new, cache_nope, cache_rope,
+                                           block_table, seq_lens_kv, max_seq_len_kv, softmax_scale,
+                                           3, out, lse, workspace, slots_out)
+    _check(lib().pkv_paged_attn_decode_mla_append(*args))
+    return out, lse
+
+
+def prepare_decode_mla_append(q, q_rope, nope_new, rope_new, cache_nope, cache_rope, block_table,
+                              seq_lens_kv, max_seq_len_kv, softmax_scale, out=None, lse=None,
+                              workspace=None, slots_out=None):
+    """(split pass with the folded write, combine pass) prepared calls."""
+    calls = []
+    for stages in (1, 2):
+        args, out, workspace = _decode_mla_append_args(q, q_rope, nope_new, rope_new, cache_nope,
+                                                       cache_rope, block_table, seq_lens_kv,
+                                                       max_seq_len_kv, softmax_scale, stages, out,
+                                                       lse, workspace, slots_out)
+        calls.append(PreparedCall(lib().pkv_paged_attn_decode_mla_append, args,
+                                  (q, q_rope, nope_new, rope_new, cache_nope, cache_rope,
+                                   block_table, seq_lens_kv, out, lse, workspace, slots_out)))
     return calls[0], calls[1], out
 
 

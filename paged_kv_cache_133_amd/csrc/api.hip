@@ -406,7 +406,8 @@ int run_mla_decode(void* out, float* lse_out, const void* q, const void* q_rope,
                    int32_t head_dim_rope, int32_t block_size, int64_t num_blocks,
                    float softmax_scale, int32_t dtype, void* workspace, size_t workspace_bytes,
                    int stages, hipStream_t s, const float* nope_scale = nullptr,
-                   const float* rope_scale = nullptr) {
+                   const float* rope_scale = nullptr, const void* nope_new = nullptr,
+                   const void* rope_new = nullptr, int64_t* slots_out = nullptr) {
     if (num_kv_heads != 1 || head_dim_qk != 512 || head_dim_v != 512 || head_dim_rope != 64)
         return fail(PKV_ERR_UNSUPPORTED,
                     "decode (MLA): needs 1 kv head, head_dim_qk = head_dim_v = 512, head_dim_rope = 64");
@@ -452,6 +453,13 @@ int run_mla_decode(void* out, float* lse_out, const void* q, const void* q_rope,
     p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
     p.k_scale = nope_scale;
     p.r_scale = rope_scale;
+    if (nope_new) {   // append: the new latent rows are attended and written in the pass
+        p.k_new = nope_new;
+        p.rope_new = rope_new;
+        p.k_cache_w = const_cast<void*>(k_cache);
+        p.rope_w = const_cast<void*>(k_rope_cache);
+        p.slots_out = slots_out;
+    }
     int rc = PKV_OK;
     if (stages & 1) {
         rc = hip_status(pkv::launch_mla_decode(p, s), "decode (MLA) launch");
@@ -587,6 +595,33 @@ int pkv_paged_attn_decode_combine(void* out, float* lse_out, const void* q, cons
     rc = prepare_decode(p, plan, PKV_DECODE_ARGS, &idle);
     if (rc != PKV_OK || idle || !needs_combine(p, plan)) return rc;
     return launch_combine_for(p, head_dim_v, dtype, (hipStream_t)stream);
+}
+
+int pkv_paged_attn_decode_mla_append(void* out, float* lse_out, const void* q_nope,
+                                     const void* q_rope, const void* nope_new,
+                                     const void* rope_new, void* cache_nope, void* cache_rope,
+                                     const int32_t* block_table, const int32_t* seq_lens_kv,
+                                     int64_t* slot_mapping_out, int32_t batch,
+                                     int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                                     int32_t num_q_heads, int32_t block_size, int64_t num_blocks,
+                                     float softmax_scale, int32_t stages, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    if (stages < 1 || stages > 3) return fail(PKV_ERR_SHAPE, "decode_mla_append: stages must be 1, 2 or 3");
+    if (!nope_new || !rope_new) return fail(PKV_ERR_NULL, "decode_mla_append: NULL new rows");
+    if (!q_rope || !cache_rope) return fail(PKV_ERR_NULL, "decode_mla_append: NULL q_rope or cache_rope");
+    if (!aligned16(nope_new) || !aligned16(rope_new))
+        return fail(PKV_ERR_ALIGN, "decode_mla_append: the new rows must be 16-byte aligned");
+    if (cache_nope == cache_rope) return fail(PKV_ERR_SHAPE, "decode_mla_append: the two caches must differ");
+    bool mla = false;
+    int rc = check_decode_common(q_rope, cache_rope, PKV_BF16, batch, num_q_heads, 1, 512, 512, 64,
+                                 max_blocks_per_seq, max_seq_len_kv, block_size, num_blocks,
+                                 softmax_scale, &mla);
+    if (rc != PKV_OK) return rc;
+    return run_mla_decode(out, lse_out, q_nope, q_rope, cache_nope, cache_nope, cache_rope, block_table,
+                          seq_lens_kv, batch, max_blocks_per_seq, max_seq_len_kv, num_q_heads, 1,
+                          512, 512, 64, block_size, num_blocks, softmax_scale, PKV_BF16, workspace,
+                          workspace_bytes, stages, (hipStream_t)stream, nullptr, nullptr, nope_new,
+                          rope_new, slot_mapping_out);
 }
 
 #undef PKV_DECODE_ARGS

@@ -92,7 +92,11 @@ __device__ __forceinline__ void codes_to_bf16(u32x4 v, u32x4& lo, u32x4& hi) {
     }
 }
 
-template <bool I8>
+// APPEND (bf16): the key at seq_lens[b] - 1 is the step's new latent row, read from
+// p.k_new / p.rope_new instead of the cache; head group 0 of the split that holds it also
+// stores it at its slot (reported in slots_out).  A row longer than the length bound writes
+// nothing (slot -1) and attends to its first len_cap cached keys.
+template <bool I8, bool APPEND = false>
 __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams p) {
     using C = MlaCfg;
     using I = MlaI8Cfg;
@@ -143,9 +147,27 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
         if ((int64_t)(ns - 1) * even < tiles) split_keys = even * kKeys;
     }
     const int k_begin = split * split_keys;
+    // Append: the new token's key (INT_MAX: none), and its write by head group 0 of the
+    // split that holds it (one nope row of 1 KiB by wave 0, one rope row by wave 1).
+    const bool app = APPEND && p.seq_lens[b] <= p.len_cap;
+    const int new_key = app ? L - 1 : INT_MAX;
+    if (APPEND && !app && split == 0 && hg == 0 && p.slots_out && tid == 0) p.slots_out[b] = -1;
     if (k_begin >= L) return;
     const int k_end = min(L, k_begin + split_keys);
     const int ntiles = (k_end - k_begin + kKeys - 1) / kKeys;
+    if (APPEND && hg == 0 && new_key >= k_begin && new_key < k_end && wid < 2) {
+        const int32_t phys = min(max(p.table[(int64_t)b * p.mbs + (new_key >> p.bs_log2)], 0),
+                                 (int32_t)(p.num_blocks - 1));
+        const int64_t slot = ((int64_t)phys << p.bs_log2) | (new_key & ((1 << p.bs_log2) - 1));
+        if (wid == 0) {
+            st16(reinterpret_cast<uint8_t*>(p.k_cache_w) + slot * 1024 + lane * 16,
+                 ld16(reinterpret_cast<const uint8_t*>(p.k_new) + (int64_t)b * 1024 + lane * 16));
+            if (p.slots_out && lane == 0) p.slots_out[b] = slot;
+        } else if (lane < 8) {
+            st16(reinterpret_cast<uint8_t*>(p.rope_w) + slot * 128 + lane * 16,
+                 ld16(reinterpret_cast<const uint8_t*>(p.rope_new) + (int64_t)b * 128 + lane * 16));
+        }
+    }
 
     const int head = hg * C::kHeads + wid * 16 + n;
     const bool valid = head < p.hq;
@@ -198,7 +220,9 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
     const bool fast_rows = p.bs_log2 >= 3;
     const uint32_t rope_voff = (uint32_t)((lane >> 3) * 128 + rope_chunk(rope_r, lane & 7) * 16);
     // The table entry of the next tile is read one tile ahead, off the critical path.
-    auto fast_tile = [&](int u) { return fast_rows && k_begin + (u + 1) * kKeys <= k_end; };
+    auto fast_tile = [&](int u) {
+        return fast_rows && k_begin + (u + 1) * kKeys <= k_end && !(APPEND && k_begin + (u + 1) * kKeys > new_key);
+    };
     auto entry_of = [&](int u) { return uniform_load(tab.row + ((k_begin + u * kKeys + 8 * wid_u) >> p.bs_log2)); };
     int32_t next_entry = fast_tile(0) ? entry_of(0) : 0;
     auto issue_tile = [&](int u) {
@@ -264,13 +288,18 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
             const int r = wid * (kKeys / C::kWaves) + j;
             const int key = min(kb + r, k_end - 1);
             const uint32_t blk = __builtin_amdgcn_readfirstlane(tab.block_of(key, chunk));
-            lds_dma16(nope_src + ((uint64_t)blk * nope_block + (uint32_t)(key & bs_mask) * 1024u),
-                      stage + r * C::kNopeRow);
+            const uint8_t* src = nope_src + ((uint64_t)blk * nope_block + (uint32_t)(key & bs_mask) * 1024u);
+            if (APPEND && key == new_key)
+                src = reinterpret_cast<const uint8_t*>(p.k_new) + (int64_t)b * 1024 + lane * 16;
+            lds_dma16(src, stage + r * C::kNopeRow);
         }
         const int key = min(kb + rope_r, k_end - 1);
         const uint32_t blk = tab.block_of(key, chunk);
-        lds_dma16(rope_src + ((uint64_t)blk * rope_block + (uint32_t)(key & bs_mask) * 128u),
-                  stage + C::kRopeBase + wid * 1024);
+        const uint8_t* src = rope_src + ((uint64_t)blk * rope_block + (uint32_t)(key & bs_mask) * 128u);
+        if (APPEND && key == new_key)
+            src = reinterpret_cast<const uint8_t*>(p.rope_new) + (int64_t)b * 128 +
+                  rope_chunk(rope_r, lane & 7) * 16;
+        lds_dma16(src, stage + C::kRopeBase + wid * 1024);
     };
 
     // S^T reads: A-operand row n of key half h is LDS row 16 h + mla_row(n / 4, n % 4);
@@ -559,8 +588,9 @@ hipError_t launch_mla_decode(const MfmaParams& p, hipStream_t s) {
     const int64_t hgs = mla_head_groups(p.hq);
     const int64_t units = ((int64_t)p.batch * p.max_splits + 7) / 8 * 8;
     const dim3 grid((unsigned)(hgs * units));
-    if (p.k_scale) hipLaunchKernelGGL(mla_decode_kernel<true>, grid, dim3(MlaCfg::kThreads), 0, s, p);
-    else hipLaunchKernelGGL(mla_decode_kernel<false>, grid, dim3(MlaCfg::kThreads), 0, s, p);
+    if (p.k_scale) hipLaunchKernelGGL((mla_decode_kernel<true>), grid, dim3(MlaCfg::kThreads), 0, s, p);
+    else if (p.k_new) hipLaunchKernelGGL((mla_decode_kernel<false, true>), grid, dim3(MlaCfg::kThreads), 0, s, p);
+    else hipLaunchKernelGGL((mla_decode_kernel<false>), grid, dim3(MlaCfg::kThreads), 0, s, p);
     return hipGetLastError();
 }
 

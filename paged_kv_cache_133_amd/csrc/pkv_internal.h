@@ -235,6 +235,13 @@ struct MfmaParams {
     // fp32 scales [nb][1][bs] (nope, rope).
     const float* k_scale;
     const float* r_scale;
+    // MLA append (bf16; else null): the step's latent rows nope [B][512] and rope [B][64],
+    // attended at position seq_lens[b] - 1 and written there through the writable views.
+    const void* k_new;
+    const void* rope_new;
+    void* k_cache_w;
+    void* rope_w;
+    int64_t* slots_out;      // [B] or null
 };
 // MLA decode: Dqk = 512 + Dr 64, Dv = 512, bf16.  Returns the launch status.
 DecodePlan plan_mla(int32_t batch, int32_t num_q_heads, int32_t head_dim_v, int32_t max_seq_len_kv);

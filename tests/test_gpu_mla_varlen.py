@@ -43,6 +43,88 @@ def test_mla_full_workload():
         f"max-abs error {err:.3e}")
 
 
+def _mla_append(c, cap=None):
+    """pkv_paged_attn_decode_mla_append on fresh copies of the case's pools."""
+    k, rope = c.cache_k.clone(), c.cache_rope.clone()
+    B = c.w.batch
+    slots = torch.full((B,), -5, dtype=torch.int64, device=DEV)
+    lse = torch.empty((B, c.w.num_q_heads), dtype=torch.float32, device=DEV)
+    out, _ = pkv.paged_attn_decode_mla_append(c.q, c.q_rope, c.new_k, c.new_rope, k, rope,
+                                              c.table_tensor(DEV), c.lens_after_tensor(DEV),
+                                              c.max_len_after if cap is None else cap,
+                                              c.w.scale, lse=lse, slots_out=slots)
+    torch.cuda.synchronize()
+    return {"slots": slots, "cache_k": k, "cache_v": k, "cache_rope": rope, "out": out,
+            "lse": lse}
+
+
+@pytest.mark.parametrize("hq,bs", [(128, 128), (64, 16), (32, 1), (16, 32)])
+def test_mla_decode_append_parity_small(hq, bs):
+    """The latent write folded into the MLA split pass: the slots, both written pools and
+    the outputs equal the oracle's slot_mapping + write + attention, and they equal the
+    separate write + decode bit for bit (the new key sits on a tile edge in some rows)."""
+    w = wl.custom(mode="mla", batch=6, num_q_heads=hq, num_kv_heads=1, head_dim=512,
+                  head_dim_rope=64, block_size=bs, dtype="bf16")
+    L = [0, 31, 32, 63, max(bs - 1, 3), 2600]
+    say(f"mla append parity: hq={hq} bs={bs} L={L}")
+    c = wl.make_case(w, L, [1] * 6, seed=hq * 7 + bs, device=DEV)
+    g = _mla_append(c)
+    o = oracle_step(c)
+    compare_writes(c, g, o)
+    err = compare_outputs(c, g, o, tokens=o["tokens"], label=f"mla append hq={hq} bs={bs}")
+    say(f"  max-abs error {err:.3e}")
+    ref = gpu_step(c)
+    assert torch.equal(g["out"].view(torch.int16), ref["out"].view(torch.int16))
+    assert torch.equal(g["lse"], ref["lse"])
+
+
+def test_mla_decode_append_full_workload():
+    """B = 64, 128 heads, lengths U{2048..8192} through the fused MLA step: every row against
+    the oracle, the slots exactly, both pools byte for byte."""
+    say("mla append full workload (all rows)")
+    c = wl.make_workload_case(wl.MLA, seed=0, device=DEV)
+    g = _mla_append(c)
+    o = oracle_step(c)
+    compare_writes(c, g, o)
+    err = compare_outputs(c, g, o, tokens=o["tokens"], label="mla append full")
+    say(f"  max-abs error {err:.3e}")
+
+
+def test_mla_decode_append_overlength_row_writes_nothing():
+    """A row longer than max_seq_len_kv writes nothing (slot -1, pools unchanged there) and
+    attends to its first max_seq_len_kv keys, like the plain MLA decode with that bound."""
+    from oracle import oracle
+    from tests.helpers import case_numpy, host
+    w = wl.custom(mode="mla", batch=3, num_q_heads=64, num_kv_heads=1, head_dim=512,
+                  head_dim_rope=64, block_size=16, dtype="bf16")
+    cap = 200
+    say("mla append over-length row")
+    c = wl.make_case(w, [99, 299, 49], [1] * 3, seed=93, device=DEV)
+    h = case_numpy(c)
+    all_slots = oracle.slot_mapping(h["block_table"], h["lens_before"], h["cu_q"],
+                                    h["block_size"], h["num_blocks"])
+    keep = np.array([0, 2])
+    ref_k = oracle.kv_write(h["cache_k"], h["new_k"][keep], all_slots[keep])
+    ref_r = oracle.kv_write(h["cache_rope"], h["new_rope"][keep], all_slots[keep])
+    g = _mla_append(c, cap=cap)
+    exp_slots = all_slots.copy()
+    exp_slots[1] = -1
+    assert np.array_equal(g["slots"].cpu().numpy(), exp_slots)
+    assert host(g["cache_k"]).tobytes() == ref_k.tobytes()
+    assert host(g["cache_rope"]).tobytes() == ref_r.tobytes()
+    plain, _ = pkv.paged_attn_decode(c.q, g["cache_k"], g["cache_k"], c.table_tensor(DEV),
+                                     c.lens_after_tensor(DEV), cap, w.scale, q_rope=c.q_rope,
+                                     k_rope_cache=g["cache_rope"])
+    torch.cuda.synchronize()
+    assert torch.equal(g["out"].view(torch.int16), plain.view(torch.int16))
+    lens = np.minimum(c.lens_after, cap).astype(np.int32)
+    ref_out, _ = oracle.paged_attention(h["q"], ref_k, ref_k, c.block_table,
+                                        np.arange(4, dtype=np.int32), lens, w.scale, False,
+                                        q_rope=h["q_rope"], k_rope=ref_r)
+    err = float(np.abs(g["out"].float().cpu().numpy().astype(np.float64) - ref_out).max())
+    assert err <= 2e-2, err
+
+
 def test_mla_split_and_combine_equal_decode():
     w = wl.custom(mode="mla", batch=3, num_q_heads=128, num_kv_heads=1, head_dim=512,
                   head_dim_rope=64, block_size=128, dtype="bf16")
