@@ -38,6 +38,7 @@ constexpr int kTabEntries = kChunkKeys + 16;    // entries per chunk buffer (>= 
 // s_waitcnt immediate (gfx9 layout): vmcnt in bits 3:0 and 15:14, expcnt in 6:4,
 // lgkmcnt in 11:8; expcnt and lgkmcnt at their maxima do not wait.
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x402;             // VALU and transcendental
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 

@@ -179,11 +179,8 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
 #pragma unroll
     for (int mt = 0; mt < C::kMTiles; ++mt) oacc[mt] = f32x16{};
 
-    // Scores of tile t: full tiles keep the raw S^T entries; boundary tiles scale them and
-    // set keys past the range or past a row's last visible position to -inf.  Returns the
-    // row's max over the tile (scaled, log2 units).  Entry r of a lane is key
-    // 8 (r / 4) + 4 lhalf + r % 4 of the tile.
-    auto scores = [&](int t, bool full, float* sv) -> float {
+    // S^T of tile t (its K reads and products; the caller places the scheduling hints).
+    auto mma_scores = [&](int t) -> f32x16 {
         const uint8_t* stage = smem + (t % kStages) * C::kStage;
         f32x16 sacc = f32x16{};
         const uint8_t* krow = stage + lrow * C::kRowBytes;
@@ -193,10 +190,12 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
             const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(krow + pos));
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc, 0, 0, 0);
         }
-        // All K reads of the tile in flight before the products (left alone, the compiler
-        // issues each read just before its product and waits out the LDS latency).
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::kSteps, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, C::kSteps, 0);
+        return sacc;
+    };
+    // The row's max over tile t (scaled, log2 units).  Full tiles keep the raw S^T entries;
+    // boundary tiles scale them and set keys past the range or past a row's last visible
+    // position to -inf.  Entry r of a lane is key 8 (r / 4) + 4 lhalf + r % 4 of the tile.
+    auto row_max = [&](int t, bool full, const f32x16& sacc, float* sv) -> float {
         float tmax;
         if (full) {
 #pragma unroll
@@ -219,61 +218,14 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
         return max_xor32(tmax);
     };
 
-    // P^T of tile t against the running max (B-operand layout: k-slot j of k-step ks is
-    // entry 8 ks + j; the sum adds the rounded weights), then O^T += V^T . P^T with V^T
-    // from the row-major V tile by transposing reads.
-    auto probs_pv = [&](int t, bool full, const float* sv) {
-        u32x4 pw[2];
-        if (full) {
-            const float mneg = -st.m;
+    // O^T += V^T . P^T of one tile (the V^T operands read by transposing LDS reads).
+    auto mma_values = [&](bf16x8_t (*va)[2], const u32x4* pw) {
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const uint32_t w = pack_bf16(fast_exp2(__builtin_fmaf(sv[r], p.scale_log2, mneg)),
-                                             fast_exp2(__builtin_fmaf(sv[r + 1], p.scale_log2, mneg)));
-                st.l = dot2_bf16(w, kOnesBf16x2, st.l);
-                pw[r >> 3][(r & 7) >> 1] = w;
-            }
-        } else {
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float e0 = sv[r] == -INFINITY ? 0.0f : fast_exp2(sv[r] - st.m);
-                const float e1 = sv[r + 1] == -INFINITY ? 0.0f : fast_exp2(sv[r + 1] - st.m);
-                const uint32_t w = pack_bf16(e0, e1);
-                st.l = dot2_bf16(w, kOnesBf16x2, st.l);
-                pw[r >> 3][(r & 7) >> 1] = w;
-            }
-        }
-        const uint8_t* vbuf = smem + (t % kStages) * C::kStage + C::kHalf;
-        const int grp = lane >> 4;
-        const int kk = lane & 15;
-#pragma unroll
-        for (int mt = 0; mt < C::kMTiles; ++mt) {
-            const int d0 = 32 * mt + 16 * (grp & 1) + 4 * (kk & 3);
-            const int cv = (d0 * 2) >> 4, w = (d0 * 2) & 15;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int t0 = 16 * ks + 4 * (grp >> 1) + (kk >> 2);
-                const int plo = swz<C::kRowChunks, C::kRowShift>(t0, cv) * 16 + w;
-                const int phi = swz<C::kRowChunks, C::kRowShift>(t0 + 8, cv) * 16 + w;
-                // Assemble the operand from whole dwords: extracting the 16-bit elements
-                // one by one made the compiler keep only the first dword of each read.
-                const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(vbuf + t0 * C::kRowBytes + plo));
-                const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(vbuf + (t0 + 8) * C::kRowBytes + phi));
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            for (int mt = 0; mt < C::kMTiles; ++mt)
                 oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    a, __builtin_bit_cast(bf16x8_t, pw[ks]), oacc[mt], 0, 0, 0);
-            }
-        }
-        // Eight transposing reads (four products) in flight ahead of the products.
-        constexpr int kPv = 2 * C::kMTiles;
-        constexpr int kAhead = kPv < 4 ? kPv : 4;
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kAhead, 0);
-#pragma unroll
-        for (int i = 0; i < kPv - kAhead; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAhead, 0);
+                    va[mt][ks], __builtin_bit_cast(bf16x8_t, pw[ks]), oacc[mt], 0, 0, 0);
     };
 
     // Table chunks and the loads of tile u (issued kStages - 1 tiles ahead).
@@ -287,28 +239,24 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
 #pragma unroll
     for (int u = 0; u < kStages - 1; ++u) feed(u);
 
-    // Tile t: wait for its loads, barrier (tile t visible, the stage of tile t - 1 free,
-    // staged table entries visible), issue tile t + 3, scores, then P and O.  A tile that
-    // raises some row's max by more than the slack leaves the loop to rescale O^T, so that
-    // inside the loop the accumulators are only touched by the products.
-    int t = 0;
-    float sv[16];
-    float tmax = 0.0f;
-    bool full = false;
-    while (t < ntiles) {
-        for (; t < ntiles; ++t) {
-            wait_tile<C::kDma>(min(ntiles - 1 - t, kStages - 2));
-            block_sync();
-            feed(t + kStages - 1);
-            full = kstart + t * kKeys >= full_lo && kstart + t * kKeys + kKeys <= full_end;
-            tmax = scores(t, full, sv);
-            const bool grow = tmax > st.m + kRescaleSlack || (st.m == -INFINITY && tmax != -INFINITY);
-            if (__any(grow)) break;
-            probs_pv(t, full, sv);
-        }
-        if (t >= ntiles) break;
-        {
-            const bool grow = tmax > st.m + kRescaleSlack || (st.m == -INFINITY && tmax != -INFINITY);
+    // Software pipeline, one tile apart: iteration t takes the max of S^T(t) (computed in
+    // iteration t - 1) and rescales O^T if some row's max grew past the slack; then, after
+    // the barrier that makes tile t + 1 visible and frees the stage of tile t - 1 (tile
+    // t + 3 is issued into it), the products of S^T(t + 1) are interleaved with the
+    // exponentials of P^T(t), and O^T += V^T . P^T(t) follows.  The last iteration
+    // computes a throw-away S^T on a stage nobody writes any more, which keeps that region
+    // one straight-line block for the scheduler.
+    wait_tile<C::kDma>(min(ntiles - 1, kStages - 2));
+    block_sync();
+    f32x16 s_cur = mma_scores(0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::kSteps, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, C::kSteps, 0);
+    for (int t = 0; t < ntiles; ++t) {
+        const bool full = kstart + t * kKeys >= full_lo && kstart + t * kKeys + kKeys <= full_end;
+        float sv[16];
+        const float tmax = row_max(t, full, s_cur, sv);
+        const bool grow = tmax > st.m + kRescaleSlack || (st.m == -INFINITY && tmax != -INFINITY);
+        if (__any(grow)) {
             const float mnew = grow ? tmax : st.m;
             const float alpha = !grow ? 1.0f : (st.m == -INFINITY ? 0.0f : fast_exp2(st.m - mnew));
             st.l *= alpha;
@@ -316,8 +264,59 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
             for (int mt = 0; mt < C::kMTiles; ++mt) oacc[mt] *= alpha;
             st.m = mnew;
         }
-        probs_pv(t, full, sv);
-        ++t;
+        if (t + 1 < ntiles) {
+            wait_tile<C::kDma>(min(ntiles - 2 - t, kStages - 3));
+            block_sync();
+            feed(t + kStages - 1);
+        }
+        // S^T(t + 1) interleaved with the exponentials of P^T(t) and the V reads of tile t,
+        // step by step (each step a scheduling region of its own, so that the compiler
+        // cannot gather the products at one end): step i issues product i of S^T(t + 1)
+        // (if any), exponential pair i of P^T(t) and the transposing reads of V^T operand i.  The
+        // K reads of all steps go first.  Then the P . V products.
+        const uint8_t* kst = smem + ((t + 1) % kStages) * C::kStage + lrow * C::kRowBytes;
+        bf16x8_t ka[C::kSteps];
+#pragma unroll
+        for (int i = 0; i < C::kSteps; ++i)
+            ka[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
+                        kst + swz<C::kRowChunks, C::kRowShift>(lrow, 2 * i + lhalf) * 16));
+        __builtin_amdgcn_sched_barrier(0);
+        const float sc = full ? p.scale_log2 : 1.0f;
+        const float mneg = st.m == -INFINITY ? 0.0f : -st.m;
+        const uint8_t* vbuf = smem + (t % kStages) * C::kStage + C::kHalf;
+        const int grp = lane >> 4;
+        const int kk = lane & 15;
+        f32x16 s_next = f32x16{};
+        u32x4 pw[2];
+        bf16x8_t va[C::kMTiles][2];
+        constexpr int kPipeSteps = C::kSteps > 8 ? C::kSteps : 8;   // >= 8 exponential pairs
+        static_assert(2 * C::kMTiles <= kPipeSteps, "steps cover the V operands");
+#pragma unroll
+        for (int i = 0; i < kPipeSteps; ++i) {
+            if (i < C::kSteps)
+                s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[i], s_next, 0, 0, 0);
+            if (i < 8) {
+                const int r = 2 * i;
+                const uint32_t w = pack_bf16(fast_exp2(__builtin_fmaf(sv[r], sc, mneg)),
+                                             fast_exp2(__builtin_fmaf(sv[r + 1], sc, mneg)));
+                st.l = dot2_bf16(w, kOnesBf16x2, st.l);
+                pw[r >> 3][(r & 7) >> 1] = w;
+            }
+            if (i < 2 * C::kMTiles) {
+                const int mt = i >> 1, ks = i & 1;
+                const int d0 = 32 * mt + 16 * (grp & 1) + 4 * (kk & 3);
+                const int cv = (d0 * 2) >> 4, w = (d0 * 2) & 15;
+                const int t0 = 16 * ks + 4 * (grp >> 1) + (kk >> 2);
+                const int plo = swz<C::kRowChunks, C::kRowShift>(t0, cv) * 16 + w;
+                const int phi = swz<C::kRowChunks, C::kRowShift>(t0 + 8, cv) * 16 + w;
+                const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(vbuf + t0 * C::kRowBytes + plo));
+                const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(vbuf + (t0 + 8) * C::kRowBytes + phi));
+                va[mt][ks] = __builtin_bit_cast(bf16x8_t, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mma_values(va, pw);
+        s_cur = s_next;
     }
 
     // ---------------------------------------------------------------- epilogue
