@@ -86,6 +86,9 @@ def parse():
                          "replayed with double-buffered table uploads, per block size")
     ap.add_argument("--block-sizes", default="16,32,64,128",
                     help="block sizes of the --serving sweep")
+    ap.add_argument("--table-capacity", type=float, default=1.0,
+                    help="--serving: max_blocks_per_seq as this multiple of what the longest "
+                         "sequence reaches during the run (the recorded step's length bound)")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="only measure the practical HBM read ceiling (pkv_stream_read over "
                          "0.7-4 GB at several grid sizes) and a device copy")
@@ -384,9 +387,10 @@ def serving(args):
     workload's lengths, their blocks taken from the host block manager one block per
     sequence in turn (so that neighbouring blocks belong to different sequences, as under
     continuous batching).  A loop step is pkv_bm_decode_step writing the next table into a
-    pinned buffer (host time) and one pkv_runner_launch (upload on the copy stream, replay
-    of the recorded write-and-attend step).  Timed beside it, each back to back on one
-    stream: the table upload alone, the replay alone, and the same step run eagerly.
+    pinned buffer (host time) and one pkv_runner_launch (replay of the recorded step: the
+    table copy kernel, then write-and-attend).  Timed beside it, each back to back on one
+    stream: the table copy kernel alone, the replay alone, and the same step (without the
+    copy) run eagerly.
     Prints one JSON line with a row per block size."""
     import numpy as np
     import torch
@@ -423,7 +427,7 @@ def serving(args):
     rows = []
     for bs in [int(x) for x in args.block_sizes.split(",")]:
         final = L0 + total + 2
-        mbs = int(math.ceil(final.max() / bs))
+        mbs = int(math.ceil(final.max() / bs * args.table_capacity))
         nb = int(sum(math.ceil(x / bs) for x in final)) + 8
         k = torch.randn(nb, bs, hkv, d, generator=gen, device=dev).to(w.torch_dtype)
         v = torch.randn(nb, bs, hkv, d, generator=gen, device=dev).to(w.torch_dtype)
@@ -470,7 +474,7 @@ def serving(args):
         # pieces alone, on the tables of the last step (lengths stay put: the same slot is
         # rewritten each time)
         j_last = (K + args.warmup - 1) % 2
-        up = timed(lambda: _lib._check(_lib.lib().pkv_upload(
+        up = timed(lambda: _lib._check(_lib.lib().pkv_upload_kernel(
             ctypes.c_void_p(step.dev[j_last].data_ptr()),
             ctypes.c_void_p(step.staging[j_last].data_ptr()), step.nbytes, cur())), K)
         graph = step.graph(j_last)
@@ -484,6 +488,7 @@ def serving(args):
         kv_tokens = tokens_before + B * (K + 1) / 2.0
         held = sum(math.ceil(bm.length(b) / bs) for b in range(B))
         rows.append({"block_size": bs, "max_blocks_per_seq": mbs,
+                     "table_capacity": args.table_capacity,
                      "table_bytes": step.nbytes,
                      "host_table_us": round(host_s / K * 1e6, 2),
                      "upload_us": round(up, 2), "graph_replay_us": round(gr, 2),

@@ -617,20 +617,19 @@ PKV_API int pkv_graph_launch(void* graph, void* stream);
 PKV_API int pkv_graph_destroy(void* graph);
 
 /*
- * Step runner: a recorded decode step replayed with double-buffered uploads of its host-
- * built inputs (the table and lengths: "Paged KV Cache and Packed Sequence", 5.3, the copy
- * of the next step's table overlapping this step's attention).  The caller owns two device
- * buffers and two pinned host buffers (hipHostMalloc) of `bytes` each, and records graph j
- * (reading device buffer j) between pkv_runner_capture_begin(r, j, s) and
- * pkv_runner_capture_end(r, s) on a created stream s.  Then per step:
- *   h = pkv_runner_host_buffer(r)   [host] blocks until the upload that last read this
+ * Step runner: a recorded decode step replayed with double-buffered host-built inputs (the
+ * table and lengths: "Paged KV Cache and Packed Sequence", 5.3, the host filling the next
+ * step's table while this step runs).  The caller owns two device buffers and two pinned
+ * host buffers (hipHostMalloc) of `bytes` each (a multiple of 4, all 16-byte aligned), and
+ * records graph j (reading device buffer j) between pkv_runner_capture_begin(r, j, s) and
+ * pkv_runner_capture_end(r, s) on a created stream s; capture_begin records, as the
+ * graph's first node, a copy kernel of host buffer j into device buffer j.  Then per step:
+ *   h = pkv_runner_host_buffer(r)   [host] blocks until the replay that last read this
  *                                   buffer has run (two steps back), returns it to fill;
- *   pkv_runner_launch(r, stream)    the copy stream uploads h to its device buffer once the
- *                                   replay that last read that buffer is done, and `stream`
- *                                   (any stream, NULL included) waits for that upload only,
- *                                   then replays the matching graph.
- * The runner owns a copy stream (default priority), four events and the two graphs; it
- * allocates no device memory.  pkv_runner_destroy waits for its pending work first.
+ *   pkv_runner_launch(r, stream)    replays the matching graph on `stream` (any stream, NULL
+ *                                   included): the copy, then the recorded step.
+ * The runner owns two events and the two graphs; it allocates no device memory and uses
+ * no stream of its own.  pkv_runner_destroy waits for its pending work first.
  */
 typedef struct pkv_step_runner pkv_step_runner;
 /* NULL (and pkv_last_error) on NULL or repeated buffers, bytes = 0 or a HIP error. */
@@ -643,11 +642,16 @@ PKV_API int pkv_runner_capture_begin(pkv_step_runner* r, int32_t j, void* stream
 PKV_API int pkv_runner_capture_end(pkv_step_runner* r, void* stream);
 /* The executable graph j (for pkv_graph_launch without an upload), or NULL. */
 PKV_API void* pkv_runner_graph(pkv_step_runner* r, int32_t j);
-/* [host] The host buffer the next pkv_runner_launch uploads, once free; NULL on error. */
+/* [host] The host buffer the next pkv_runner_launch copies in, once free; NULL on error. */
 PKV_API void* pkv_runner_host_buffer(pkv_step_runner* r);
-/* Enqueues the next step (upload + replay) as described above; PKV_ERR_SHAPE if its graph
- * was not recorded. */
+/* Enqueues the next step (copy + recorded step, one graph replay) as described above;
+ * PKV_ERR_SHAPE if its graph was not recorded. */
 PKV_API int pkv_runner_launch(pkv_step_runner* r, void* stream);
+/* The copy the runner records: `bytes` (a multiple of 4) from pinned host memory src_host
+ * (hipHostMalloc; read through its device view) to device memory dst, both 16-byte
+ * aligned, by a kernel on `stream` (so that a graph records it as a kernel node, and it
+ * needs no copy engine).  PKV_ERR_HIP if src_host has no device view (not pinned). */
+PKV_API int pkv_upload_kernel(void* dst, const void* src_host, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

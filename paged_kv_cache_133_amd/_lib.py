@@ -38,7 +38,7 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_graph_begin", "pkv_graph_end", "pkv_graph_launch", "pkv_graph_destroy",
            "pkv_runner_create", "pkv_runner_destroy", "pkv_runner_capture_begin",
            "pkv_runner_capture_end", "pkv_runner_graph", "pkv_runner_host_buffer",
-           "pkv_runner_launch", "pkv_decode_mtp_workspace_size", "pkv_paged_attn_decode_mtp",
+           "pkv_runner_launch", "pkv_upload_kernel", "pkv_decode_mtp_workspace_size", "pkv_paged_attn_decode_mtp",
            "pkv_kv_cache_write_int8_mla", "pkv_paged_attn_decode_mla_int8", "pkv_stream_read",
            "pkv_paged_attn_decode_int8_append", "pkv_paged_attn_decode_mla_append")
 
@@ -169,6 +169,8 @@ def lib() -> ctypes.CDLL:
     L.pkv_runner_host_buffer.argtypes = [p]
     L.pkv_runner_launch.restype = ctypes.c_int
     L.pkv_runner_launch.argtypes = [p, p]
+    L.pkv_upload_kernel.restype = ctypes.c_int
+    L.pkv_upload_kernel.argtypes = [p, p, sz, p]
     _lib = L
     return L
 

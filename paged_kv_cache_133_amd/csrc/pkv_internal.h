@@ -63,6 +63,10 @@ struct CopyBlocksParams {
 };
 hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t s);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, hipStream_t s);
+// bytes (a multiple of 4; both ends 16-byte aligned) from pinned host memory, addressed by
+// its device view (hipHostGetDevicePointer), into dst, by a kernel (so that a graph can
+// record it as a kernel node).
+hipError_t launch_host_copy(void* dst, const void* src_dev_view, int64_t bytes, hipStream_t s);
 
 // Quantizing write of the INT8 cache: per (token, kv head) row, s = max|x| / 127 and
 // q = round_half_even(x / s) into the int8 caches and the fp32 scale arrays.

@@ -182,7 +182,30 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
     if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
+// Copy of n4 int32 words from pinned host memory (its device view) into device memory: one
+// 16-byte word per thread where the two ends allow it, 4-byte words for the tail.
+__global__ __launch_bounds__(256) void host_copy_kernel(const uint32_t* __restrict__ src,
+                                                        uint32_t* __restrict__ dst, int64_t n4) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t n16 = n4 / 4;
+    if (i < n16) {
+        reinterpret_cast<u32x4*>(dst)[i] = reinterpret_cast<const u32x4*>(src)[i];
+    } else if (i < n16 + (n4 & 3)) {
+        const int64_t k = 4 * n16 + (i - n16);
+        dst[k] = src[k];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_host_copy(void* dst, const void* src_dev_view, int64_t bytes, hipStream_t s) {
+    const int64_t n4 = bytes / 4;
+    const int64_t threads = n4 / 4 + (n4 & 3);
+    const unsigned grid = (unsigned)((threads + 255) / 256);
+    hipLaunchKernelGGL(host_copy_kernel, dim3(grid), dim3(256), 0, s,
+                       static_cast<const uint32_t*>(src_dev_view), static_cast<uint32_t*>(dst), n4);
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, hipStream_t s) {
     hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(256), 0, s,

@@ -2,16 +2,15 @@
 
 "Paged KV Cache and Packed Sequence", 5.3: the block table changes every step, so the
 recorded step must not hold it; the host builds it (BlockManager.decode_step) into a
-buffer that is copied to the device before each replay, and with two such buffers the copy
-for the next step runs while this step's attention does.  Here:
+buffer that is copied to the device at the start of each replay, and with two such buffers
+the host fills the next one while this step runs.  Here:
 
   * two pinned host buffers and two device buffers, each [batch * max_blocks_per_seq +
     batch] int32 (the table, then seq_lens_kv), owned by this object;
-  * two graphs in a native step runner, graph j recording pkv_paged_attn_decode_ex (write
-    of the new rows and attention) over device buffer j;
-  * launch(): one library call that uploads buffer j on the runner's copy stream once the
-    replay that last read device buffer j is done, and replays graph j on the current
-    stream after that upload only.
+  * two graphs in a native step runner, graph j recording a copy kernel (pinned host
+    buffer j -> device buffer j) and pkv_paged_attn_decode_append (write of the new rows
+    and attention) over device buffer j;
+  * launch(): one library call that replays graph j on the current stream.
 
 The batch is fixed at capture; rows without a sequence are padding rows (length 0: output
 0, lse -inf, nothing written, slot -1).  Inputs q, k_new and v_new are the step's own
@@ -78,8 +77,8 @@ class GraphDecodeStep:
 
     def host_tables(self):
         """(table [batch][max_blocks_per_seq], seq_lens [batch]) numpy views of the pinned
-        buffer the next launch() uploads; fill both before calling it.  Waits until the
-        upload that last read this buffer has run."""
+        buffer the next launch() copies in; fill both before calling it.  Waits until the
+        replay that last read this buffer (two steps back) has run."""
         p = lib().pkv_runner_host_buffer(self._r)
         if not p:
             _check(-8)
@@ -89,11 +88,11 @@ class GraphDecodeStep:
         return v[:cut].reshape(self.batch, self.mbs), v[cut:]
 
     def launch(self):
-        """Upload the host tables and replay the step on the current stream."""
+        """Replay the step on the current stream: the table copy, then write-and-attend."""
         _check(lib().pkv_runner_launch(self._r, _stream(self.device)))
 
     def graph(self, j: int):
-        """Executable graph j (replay without an upload: pkv_graph_launch)."""
+        """Executable graph j (its table copy and the step; pkv_graph_launch)."""
         return lib().pkv_runner_graph(self._r, j)
 
     def close(self):
