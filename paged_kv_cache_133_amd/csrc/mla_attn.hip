@@ -588,9 +588,8 @@ hipError_t launch_mla_decode(const MfmaParams& p, hipStream_t s) {
     const int64_t hgs = mla_head_groups(p.hq);
     const int64_t units = ((int64_t)p.batch * p.max_splits + 7) / 8 * 8;
     const dim3 grid((unsigned)(hgs * units));
-    if (p.k_scale) hipLaunchKernelGGL((mla_decode_kernel<true>), grid, dim3(MlaCfg::kThreads), 0, s, p);
-    else if (p.k_new) hipLaunchKernelGGL((mla_decode_kernel<false, true>), grid, dim3(MlaCfg::kThreads), 0, s, p);
-    else hipLaunchKernelGGL((mla_decode_kernel<false>), grid, dim3(MlaCfg::kThreads), 0, s, p);
+    if (!p.k_scale) return launch_mla_wide(p, s);   // bf16: one workgroup for 128 heads
+    hipLaunchKernelGGL((mla_decode_kernel<true>), grid, dim3(MlaCfg::kThreads), 0, s, p);
     return hipGetLastError();
 }
 
