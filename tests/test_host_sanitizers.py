@@ -19,8 +19,10 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "paged_kv_cache_133_amd", "csrc")
-HOST_SOURCES = ["api", "write", "norm_rope", "decode", "int8_kv", "mla_attn", "varlen_attn",
-                "gqa_attn", "block_manager", "runner"]
+sys.path.insert(0, ROOT)
+from paged_kv_cache_133_amd.build import SOURCES  # noqa: E402  (every source of the library)
+
+HOST_SOURCES = [os.path.splitext(src)[0] for src in SOURCES]
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=undefined"]
 
