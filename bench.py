@@ -47,7 +47,7 @@ def dominant_kernel(w):
     sources its traffic counters depend on."""
     if w.mode == "mla":
         if w.kv_dtype == "int8":
-            return "mla_decode_kernel", [CSRC + "mla_attn.hip"] + MFMA_SOURCES
+            return "mla_int8_kernel", [CSRC + "mla_attn.hip"] + MFMA_SOURCES
         return "mla_wide_kernel", [CSRC + "mla_wide.hip"] + MFMA_SOURCES
     if w.q_tokens:      # multi-token decode: the range-streaming kernel
         return "gqa_stream_kernel", [CSRC + "gqa_attn.hip"] + MFMA_SOURCES

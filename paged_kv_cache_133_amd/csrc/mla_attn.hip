@@ -1,33 +1,28 @@
-// MLA-absorbed decode over the paged cache with MFMA for gfx950 ("KVCache Optimization
-// Skill", Mode 3: key = cache_nope || cache_rope, value = cache_nope, rope passed
-// separately): all query heads of a sequence share one latent head, so a tile of keys
-// read once serves every head.
+// MLA-absorbed decode over the paged INT8 cache with MFMA for gfx950 ("KVCache
+// Optimization Skill", Mode 3: key = cache_nope || cache_rope, value = cache_nope, rope
+// passed separately; the cache holds int8 codes with one fp32 scale per token for nope and
+// one for rope).  The bf16 cache runs mla_wide_kernel.
 //
 // A workgroup of four waves owns 64 heads (16 per wave) of one (sequence, split) and walks
-// its keys in tiles of 32 (the tile pipeline of mfma_common.h), each wave over the whole
-// 576-wide contraction, with v_mfma_f32_16x16x32_bf16.  The two head groups of 128 heads
-// are launched onto the same XCD so that the second read of a K tile comes from its L2.
-//  * S^T (16 keys x 16 heads, two per tile) = K . Q^T: K rows from LDS as the A operand,
-//    Q^T of the wave's 16 heads in registers as the B operand (72 registers);
+// its keys in tiles of 32, each wave over the whole 576-wide contraction, with
+// v_mfma_f32_16x16x32_bf16 over bf16 copies of the codes (exact: |q| <= 127).  The two
+// head groups of 128 heads are launched onto the same XCD so that the second read of a tile
+// comes from its L2.
+//  * the codes of a tile (512 + 64 bytes per key) and its keys' scales reach LDS by direct
+//    loads two tiles ahead; each wave converts the eight keys it loaded into one of two
+//    bf16 buffers (32 nope rows of 1024 bytes padded to 1056, then 32 rope rows of 128
+//    bytes with their chunks XOR-swizzled by row) before the tile's barrier;
+//  * S^T (16 keys x 16 heads, two per tile) = K . Q^T: K rows from the buffer as the A
+//    operand, Q^T of the wave's 16 heads in the accumulation registers as B (72); the nope
+//    and rope sums are kept apart and weighed per key with the two scales;
 //  * lane (g, n) (g = lane / 16) holds 8 keys of head n: the head's max and sum take two
-//    cross-lane steps, and P^T (bf16) is the B operand of the next product with k-slot
+//    cross-lane steps, and P'^T = bf16(p s_nope) (the nope scale folded into the value
+//    weight; l sums the rounded p) is the B operand of the next product with k-slot
 //    8 g + 4 h + r standing for accumulator entry r of key half h;
-//  * O^T (512 x 16 heads, 128 registers) += V^T . P^T, the A operand built by two
-//    ds_read_b64_tr_b16 per product (four keys at one value column per lane and read)
-//    from the nope part of the same LDS rows;
-//  * O^T keeps one head per lane column, so the online-softmax rescale is lane-local; it
-//    is applied only when a head's max grows by more than 2^8 (P <= 256 in between),
-//    which after the first tiles almost never happens.  Full tiles skip the masking.
-// One wave per SIMD: O^T lives in VGPRs (the rescale multiplies it in place) and Q^T in
-// the accumulation registers.
-//
-// Over the INT8 cache (codes with one fp32 scale per token for nope and one for rope) the
-// products are the same, over bf16 copies of the codes (exact: |q| <= 127): the codes of a
-// tile (512 + 64 bytes per key) and its keys' scales reach LDS by direct loads two tiles
-// ahead; each wave converts the eight keys it loaded into one of two bf16 buffers laid out
-// like a bf16 stage, before the tile's barrier.  Scores keep the nope and rope sums apart
-// and weigh them per key with the two scales; the nope scale is folded into the weight of
-// the value sum (P' = bf16(p s_nope)), while l sums the rounded p.
+//  * O^T (512 x 16 heads, 128 registers) += V^T . P'^T, the A operand built by two
+//    ds_read_b64_tr_b16 per product from the nope part of the same buffer rows;
+//  * the online-softmax rescale is lane-local and applied only when a head's max grows by
+//    more than 2^8 (P <= 256 in between).  Full tiles skip the masking.
 #include "mfma_common.h"
 
 namespace pkv {
@@ -40,19 +35,16 @@ struct MlaCfg {
     static constexpr int kWaves = 4;
     static constexpr int kThreads = kWaves * 64;
     static constexpr int kHeads = kWaves * 16;              // query heads per workgroup
-    // LDS stage: 32 nope rows of 1024 bytes padded to 1056 (one wave load each), then 32
-    // rope rows of 128 bytes (eight per wave load) with their chunks XOR-swizzled by row.
+    // bf16 stage: 32 nope rows of 1024 bytes padded to 1056, then 32 rope rows of 128
+    // bytes with their chunks XOR-swizzled by row.
     // The 32-byte padding was measured on gfx950 to serve both the 16-byte K reads and the
     // 8-byte transposing V reads of the products without bank conflicts (a probe of the two
     // read patterns: 191 and 161 B/clk per CU, against 112 and 112 with 16-byte padding).
     static constexpr int kNopeRow = 1024 + 32;
     static constexpr int kRopeBase = kKeys * kNopeRow;
     static constexpr int kStage = kRopeBase + kKeys * 128;
-    static constexpr int kDma = kKeys / kWaves + 1;         // wave loads per tile: 8 nope + 1 rope
     static constexpr int kSteps = 576 / 32;                 // S^T k-steps (16 nope, 2 rope)
     static constexpr int kDTiles = 512 / 16;                // 16-row tiles of O^T
-    static constexpr int kSmem = kStages * kStage + 2 * kTabEntries * 4;
-    static_assert(kSmem <= 160 * 1024, "LDS");
     static_assert(kKeys * 128 == kWaves * 1024, "one rope load per wave");
 };
 
@@ -92,16 +84,11 @@ __device__ __forceinline__ void codes_to_bf16(u32x4 v, u32x4& lo, u32x4& hi) {
     }
 }
 
-// APPEND (bf16): the key at seq_lens[b] - 1 is the step's new latent row, read from
-// p.k_new / p.rope_new instead of the cache; head group 0 of the split that holds it also
-// stores it at its slot (reported in slots_out).  A row longer than the length bound writes
-// nothing (slot -1) and attends to its first len_cap cached keys.
-template <bool I8, bool APPEND = false>
-__global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams p) {
+__global__ __launch_bounds__(MlaCfg::kThreads) void mla_int8_kernel(MfmaParams p) {
     using C = MlaCfg;
     using I = MlaI8Cfg;
-    constexpr int kTabOff = I8 ? I::kTabOff : kStages * C::kStage;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[I8 ? I::kSmem : C::kSmem];
+    constexpr int kTabOff = I::kTabOff;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[I::kSmem];
 
     const int tid = threadIdx.x;
     const int wid = tid >> 6;
@@ -147,28 +134,9 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
         if ((int64_t)(ns - 1) * even < tiles) split_keys = even * kKeys;
     }
     const int k_begin = split * split_keys;
-    // Append: the new token's key (INT_MAX: none), and its write by head group 0 of the
-    // split that holds it (one nope row of 1 KiB by wave 0, one rope row by wave 1).
-    const bool app = APPEND && p.seq_lens[b] <= p.len_cap;
-    const int new_key = app ? L - 1 : INT_MAX;
-    if (APPEND && !app && split == 0 && hg == 0 && p.slots_out && tid == 0) p.slots_out[b] = -1;
     if (k_begin >= L) return;
     const int k_end = min(L, k_begin + split_keys);
     const int ntiles = (k_end - k_begin + kKeys - 1) / kKeys;
-    if (APPEND && hg == 0 && new_key >= k_begin && new_key < k_end && wid < 2) {
-        const int32_t phys = min(max(p.table[(int64_t)b * p.mbs + (new_key >> p.bs_log2)], 0),
-                                 (int32_t)(p.num_blocks - 1));
-        const int64_t slot = ((int64_t)phys << p.bs_log2) | (new_key & ((1 << p.bs_log2) - 1));
-        if (wid == 0) {
-            st16(reinterpret_cast<uint8_t*>(p.k_cache_w) + slot * 1024 + lane * 16,
-                 ld16(reinterpret_cast<const uint8_t*>(p.k_new) + (int64_t)b * 1024 + lane * 16));
-            if (p.slots_out && lane == 0) p.slots_out[b] = slot;
-        } else if (lane < 8) {
-            st16(reinterpret_cast<uint8_t*>(p.rope_w) + slot * 128 + lane * 16,
-                 ld16(reinterpret_cast<const uint8_t*>(p.rope_new) + (int64_t)b * 128 + lane * 16));
-        }
-    }
-
     const int head = hg * C::kHeads + wid * 16 + n;
     const bool valid = head < p.hq;
     const int64_t row = (int64_t)b * p.hq + min(head, p.hq - 1);
@@ -208,98 +176,57 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
     // 16-byte chunk; the row's slot is the same for the whole wave) and rope rows
     // 8 w .. 8 w + 7 (one load, lane = row 8 w + lane / 8, physical chunk lane % 8).
     const int bs_mask = (1 << p.bs_log2) - 1;
-    const uint32_t nope_block = (uint32_t)(1024u << p.bs_log2);   // bytes per block
-    const uint32_t rope_block = (uint32_t)(128u << p.bs_log2);
-    const uint8_t* nope_src = reinterpret_cast<const uint8_t*>(p.k_cache) + lane * 16;
-    const int rope_r = wid * 8 + (lane >> 3);
-    const uint8_t* rope_src = reinterpret_cast<const uint8_t*>(p.k_rope) + rope_chunk(rope_r, lane & 7) * 16;
     // Full tiles with blocks of at least 8 keys: the wave's 8 rows are consecutive slots of
     // one block, found with one scalar read of the block table; every load then uses that
     // row base in SGPRs and a constant offset per lane.
     const int wid_u = __builtin_amdgcn_readfirstlane(wid);
     const bool fast_rows = p.bs_log2 >= 3;
-    const uint32_t rope_voff = (uint32_t)((lane >> 3) * 128 + rope_chunk(rope_r, lane & 7) * 16);
     // The table entry of the next tile is read one tile ahead, off the critical path.
     auto fast_tile = [&](int u) {
-        return fast_rows && k_begin + (u + 1) * kKeys <= k_end && !(APPEND && k_begin + (u + 1) * kKeys > new_key);
+        return fast_rows && k_begin + (u + 1) * kKeys <= k_end;
     };
     auto entry_of = [&](int u) { return uniform_load(tab.row + ((k_begin + u * kKeys + 8 * wid_u) >> p.bs_log2)); };
     int32_t next_entry = fast_tile(0) ? entry_of(0) : 0;
     auto issue_tile = [&](int u) {
         const int kb = k_begin + u * kKeys;
         const int chunk = u / kChunkTiles;
-        if constexpr (I8) {
-            // Wave w loads the codes of keys 8 w .. 8 w + 7: their nope rows (4 loads of two
-            // rows) and one load whose lanes 0-31 take the 8 rope rows, 32-33 the 8 nope
-            // scales, 34-35 the 8 rope scales (scales are in slot order per block, and a
-            // group of 4 keys lies in one block), the others re-read lane 32's bytes.
-            uint8_t* cs = smem + (u % I::kCodeStages) * I::kCodeStage;
-            uint8_t* aux = cs + I::kNopeCodes + wid_u * I::kAux;
-            const uint8_t* ncodes = reinterpret_cast<const uint8_t*>(p.k_cache);
-            const uint8_t* rcodes = reinterpret_cast<const uint8_t*>(p.k_rope);
-            const uint8_t* nsc = reinterpret_cast<const uint8_t*>(p.k_scale);
-            const uint8_t* rsc = reinterpret_cast<const uint8_t*>(p.r_scale);
-            const int32_t entry = next_entry;
-            if (u + 1 < ntiles && fast_tile(u + 1)) next_entry = entry_of(u + 1);
-            const int q = lane >= 32 && lane < 36 ? lane - 32 : 0;
-            if (fast_tile(u)) {
-                const int key0 = kb + 8 * wid_u;
-                const int32_t blk = min(max(entry, 0), tab.last_block);
-                const uint64_t slot0 = ((uint64_t)(uint32_t)blk << p.bs_log2) | (uint32_t)(key0 & bs_mask);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    lds_dma16_s(ncodes + slot0 * 512u + j * 1024, (uint32_t)lane * 16u, cs + (8 * wid_u) * 512 + j * 1024);
-                const uint8_t* src = lane < 32 ? rcodes + slot0 * 64u + lane * 16
-                                               : ((q & 2) ? rsc : nsc) + slot0 * 4u + (q & 1) * 16;
-                lds_dma16(src, aux);
-                return;
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int key = min(kb + 8 * wid + 2 * j + (lane >> 5), k_end - 1);
-                const uint64_t slot = ((uint64_t)tab.block_of(key, chunk) << p.bs_log2) | (uint32_t)(key & bs_mask);
-                lds_dma16(ncodes + slot * 512u + (lane & 31) * 16, cs + (8 * wid_u + 2 * j) * 512);
-            }
-            // keys past the range: their rope row and scales come from the last key (its
-            // 4-key group for the scales); their weights are 0
-            const int key = lane < 32 ? min(kb + 8 * wid + (lane >> 2), k_end - 1)
-                                      : min(kb + 8 * wid + 4 * (q & 1), (k_end - 1) & ~3);
-            const uint64_t slot = ((uint64_t)tab.block_of(key, chunk) << p.bs_log2) | (uint32_t)(key & bs_mask);
-            lds_dma16(lane < 32 ? rcodes + slot * 64u + (lane & 3) * 16 : ((q & 2) ? rsc : nsc) + slot * 4u, aux);
-            return;
-        }
-        uint8_t* stage = smem + (u % kStages) * C::kStage;
+        // Wave w loads the codes of keys 8 w .. 8 w + 7: their nope rows (4 loads of two
+        // rows) and one load whose lanes 0-31 take the 8 rope rows, 32-33 the 8 nope
+        // scales, 34-35 the 8 rope scales (scales are in slot order per block, and a
+        // group of 4 keys lies in one block), the others re-read lane 32's bytes.
+        uint8_t* cs = smem + (u % I::kCodeStages) * I::kCodeStage;
+        uint8_t* aux = cs + I::kNopeCodes + wid_u * I::kAux;
+        const uint8_t* ncodes = reinterpret_cast<const uint8_t*>(p.k_cache);
+        const uint8_t* rcodes = reinterpret_cast<const uint8_t*>(p.k_rope);
+        const uint8_t* nsc = reinterpret_cast<const uint8_t*>(p.k_scale);
+        const uint8_t* rsc = reinterpret_cast<const uint8_t*>(p.r_scale);
         const int32_t entry = next_entry;
         if (u + 1 < ntiles && fast_tile(u + 1)) next_entry = entry_of(u + 1);
+        const int q = lane >= 32 && lane < 36 ? lane - 32 : 0;
         if (fast_tile(u)) {
             const int key0 = kb + 8 * wid_u;
             const int32_t blk = min(max(entry, 0), tab.last_block);
             const uint64_t slot0 = ((uint64_t)(uint32_t)blk << p.bs_log2) | (uint32_t)(key0 & bs_mask);
-            const uint8_t* nb = reinterpret_cast<const uint8_t*>(p.k_cache) + slot0 * 1024u;
 #pragma unroll
-            for (int j = 0; j < kKeys / C::kWaves; ++j)
-                lds_dma16_s(nb + j * 1024, (uint32_t)lane * 16u, stage + (8 * wid_u + j) * C::kNopeRow);
-            lds_dma16_s(reinterpret_cast<const uint8_t*>(p.k_rope) + slot0 * 128u, rope_voff,
-                        stage + C::kRopeBase + wid_u * 1024);
+            for (int j = 0; j < 4; ++j)
+                lds_dma16_s(ncodes + slot0 * 512u + j * 1024, (uint32_t)lane * 16u, cs + (8 * wid_u) * 512 + j * 1024);
+            const uint8_t* src = lane < 32 ? rcodes + slot0 * 64u + lane * 16
+                                           : ((q & 2) ? rsc : nsc) + slot0 * 4u + (q & 1) * 16;
+            lds_dma16(src, aux);
             return;
         }
 #pragma unroll
-        for (int j = 0; j < kKeys / C::kWaves; ++j) {
-            const int r = wid * (kKeys / C::kWaves) + j;
-            const int key = min(kb + r, k_end - 1);
-            const uint32_t blk = __builtin_amdgcn_readfirstlane(tab.block_of(key, chunk));
-            const uint8_t* src = nope_src + ((uint64_t)blk * nope_block + (uint32_t)(key & bs_mask) * 1024u);
-            if (APPEND && key == new_key)
-                src = reinterpret_cast<const uint8_t*>(p.k_new) + (int64_t)b * 1024 + lane * 16;
-            lds_dma16(src, stage + r * C::kNopeRow);
+        for (int j = 0; j < 4; ++j) {
+            const int key = min(kb + 8 * wid + 2 * j + (lane >> 5), k_end - 1);
+            const uint64_t slot = ((uint64_t)tab.block_of(key, chunk) << p.bs_log2) | (uint32_t)(key & bs_mask);
+            lds_dma16(ncodes + slot * 512u + (lane & 31) * 16, cs + (8 * wid_u + 2 * j) * 512);
         }
-        const int key = min(kb + rope_r, k_end - 1);
-        const uint32_t blk = tab.block_of(key, chunk);
-        const uint8_t* src = rope_src + ((uint64_t)blk * rope_block + (uint32_t)(key & bs_mask) * 128u);
-        if (APPEND && key == new_key)
-            src = reinterpret_cast<const uint8_t*>(p.rope_new) + (int64_t)b * 128 +
-                  rope_chunk(rope_r, lane & 7) * 16;
-        lds_dma16(src, stage + C::kRopeBase + wid * 1024);
+        // keys past the range: their rope row and scales come from the last key (its
+        // 4-key group for the scales); their weights are 0
+        const int key = lane < 32 ? min(kb + 8 * wid + (lane >> 2), k_end - 1)
+                                  : min(kb + 8 * wid + 4 * (q & 1), (k_end - 1) & ~3);
+        const uint64_t slot = ((uint64_t)tab.block_of(key, chunk) << p.bs_log2) | (uint32_t)(key & bs_mask);
+        lds_dma16(lane < 32 ? rcodes + slot * 64u + (lane & 3) * 16 : ((q & 2) ? rsc : nsc) + slot * 4u, aux);
     };
 
     // S^T reads: A-operand row n of key half h is LDS row 16 h + mla_row(n / 4, n % 4);
@@ -368,7 +295,7 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
     // Entry (h, r) of lane (g, n) is key 16 h + mla_row(g, r) of the tile.  Returns the
     // head's max over the tile (scaled, log2 units).
     auto scores = [&](int t, bool full, float* sv, float* sn) -> float {
-        const uint8_t* stage = I8 ? smem + I::kBufOff + (t & 1) * I::kBuf : smem + (t % kStages) * C::kStage;
+        const uint8_t* stage = smem + I::kBufOff + (t & 1) * I::kBuf;
         f32x4 sacc[2], racc[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -378,7 +305,7 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
             for (int s = 0; s < C::kSteps; ++s) {
                 const uint8_t* src = s < 16 ? stage + k_off[h] + 64 * s : stage + rope_off[h][s - 16];
                 const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(src));
-                if (I8 && s >= 16) racc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], racc[h], 0, 0, 0);
+                if (s >= 16) racc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], racc[h], 0, 0, 0);
                 else sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], sacc[h], 0, 0, 0);
             }
         }
@@ -391,14 +318,13 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
-        if constexpr (I8) {   // per key: s_nope * (q_nope . codes) + s_rope * (q_rope . codes)
-            const float* scn = reinterpret_cast<const float*>(stage + C::kStage);
+        // per key: s_nope * (q_nope . codes) + s_rope * (q_rope . codes)
+        const float* scn = reinterpret_cast<const float*>(stage + C::kStage);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int key = 16 * (e >> 2) + mla_row(g, e & 3);
-                sn[e] = scn[key];
-                sacc[e >> 2][e & 3] = sn[e] * sacc[e >> 2][e & 3] + scn[kKeys + key] * racc[e >> 2][e & 3];
-            }
+        for (int e = 0; e < 8; ++e) {
+            const int key = 16 * (e >> 2) + mla_row(g, e & 3);
+            sn[e] = scn[key];
+            sacc[e >> 2][e & 3] = sn[e] * sacc[e >> 2][e & 3] + scn[kKeys + key] * racc[e >> 2][e & 3];
         }
         float tmax;
         if (full) {
@@ -413,7 +339,7 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
             for (int e = 0; e < 8; ++e) {
                 const int key = kb + 16 * (e >> 2) + mla_row(g, e & 3);
                 sv[e] = (valid && key < k_end) ? sacc[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
-                if (I8 && sv[e] == -INFINITY) sn[e] = 0.0f;   // no stale scale reaches P'
+                if (sv[e] == -INFINITY) sn[e] = 0.0f;   // no stale scale reaches P'
                 tmax = fmaxf(tmax, sv[e]);
             }
         }
@@ -432,7 +358,7 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
                 const float e1 = fast_exp2(__builtin_fmaf(sv[e + 1], p.scale_log2, mneg));
                 const uint32_t w = pack_bf16(e0, e1);
                 st.l = dot2_bf16(w, kOnesBf16x2, st.l);
-                pw[e >> 1] = I8 ? pack_bf16(e0 * sn[e], e1 * sn[e + 1]) : w;
+                pw[e >> 1] = pack_bf16(e0 * sn[e], e1 * sn[e + 1]);
             }
         } else {
 #pragma unroll
@@ -441,11 +367,11 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
                 const float e1 = sv[e + 1] == -INFINITY ? 0.0f : fast_exp2(sv[e + 1] - st.m);
                 const uint32_t w = pack_bf16(e0, e1);
                 st.l = dot2_bf16(w, kOnesBf16x2, st.l);
-                pw[e >> 1] = I8 ? pack_bf16(e0 * sn[e], e1 * sn[e + 1]) : w;
+                pw[e >> 1] = pack_bf16(e0 * sn[e], e1 * sn[e + 1]);
             }
         }
         const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
-        const uint8_t* stage = I8 ? smem + I::kBufOff + (t & 1) * I::kBuf : smem + (t % kStages) * C::kStage;
+        const uint8_t* stage = smem + I::kBufOff + (t & 1) * I::kBuf;
         const uint8_t* v0 = stage + v_off[0];
         const uint8_t* v1 = stage + v_off[1];
 #pragma unroll
@@ -467,7 +393,7 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
     };
 
-    // Table chunks and the loads of tile u (issued kStages - 1 tiles ahead).
+    // Table chunks and the loads of tile u (issued kAhead tiles ahead).
     auto feed = [&](int u) {
         if (u >= ntiles) return;
         const int c = u / kChunkTiles;
@@ -475,14 +401,13 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
         if (u % kChunkTiles == kChunkTiles / 2 && tab.exists(c + 1)) tab.store(c + 1, treg);
         issue_tile(u);
     };
-    constexpr int kAhead = I8 ? I::kCodeStages - 1 : kStages - 1;   // tiles issued ahead
+    constexpr int kAhead = I::kCodeStages - 1;   // tiles issued ahead
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) feed(u);
 
-    // Tile t: wait for its loads, barrier (tile t visible, the stage of tile t - 1 free,
-    // staged table entries visible), issue tile t + 3 (two waves before their scores, two
-    // after, so that the four waves do not queue their 36 loads on the compute unit at
-    // once), scores, then P and O.  A tile that raises some head's max by more than the
+    // Tile t: wait for this wave's codes, convert them, barrier (buffer t & 1 complete, the
+    // code stage of tile t - 1 free, staged table entries visible), issue tile t + 2,
+    // scores, then P and O.  A tile that raises some head's max by more than the
     // slack leaves the loop to rescale O^T, so that inside the loop the accumulators are
     // only touched by the products.
     int t = 0;
@@ -491,24 +416,15 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_decode_kernel(MfmaParams
     bool full = false;
     while (t < ntiles) {
         for (; t < ntiles; ++t) {
-            if constexpr (I8) {
-                // This wave's codes of tile t (tile t + 1 may stay in flight), into bf16;
-                // the barrier publishes buffer t & 1 and frees the code stage of tile t - 1
-                // (converted) and buffer (t + 1) & 1 (read by tile t - 1) for reuse.
-                wait_tile<I::kDma>(min(ntiles - 1 - t, 1));
-                convert(t);
-                block_sync();
-                feed(t + kAhead);
-                full = k_begin + (t + 1) * kKeys <= k_end;
-                tmax = scores(t, full, sv, sn);
-            } else {
-                wait_tile<C::kDma>(min(ntiles - 1 - t, kStages - 2));
-                block_sync();
-                if (wid_u < 2) feed(t + kStages - 1);
-                full = k_begin + (t + 1) * kKeys <= k_end;
-                tmax = scores(t, full, sv, sn);
-                if (wid_u >= 2) feed(t + kStages - 1);
-            }
+            // This wave's codes of tile t (tile t + 1 may stay in flight), into bf16; the
+            // barrier publishes buffer t & 1 and frees the code stage of tile t - 1
+            // (converted) and buffer (t + 1) & 1 (read by tile t - 1) for reuse.
+            wait_tile<I::kDma>(min(ntiles - 1 - t, 1));
+            convert(t);
+            block_sync();
+            feed(t + kAhead);
+            full = k_begin + (t + 1) * kKeys <= k_end;
+            tmax = scores(t, full, sv, sn);
             const bool grow = tmax > st.m + kRescaleSlack || (st.m == -INFINITY && tmax != -INFINITY);
             if (__any(grow)) break;
             probs_pv(t, full, sv, sn);
@@ -584,12 +500,12 @@ DecodePlan plan_mla(int32_t batch, int32_t num_q_heads, int32_t head_dim_v, int3
 }
 
 hipError_t launch_mla_decode(const MfmaParams& p, hipStream_t s) {
+    if (!p.k_scale) return launch_mla_wide(p, s);   // bf16: one workgroup for 128 heads
     // ids: (unit / 8, head group, unit % 8) with units = batch * max_splits rounded up to 8
     const int64_t hgs = mla_head_groups(p.hq);
     const int64_t units = ((int64_t)p.batch * p.max_splits + 7) / 8 * 8;
     const dim3 grid((unsigned)(hgs * units));
-    if (!p.k_scale) return launch_mla_wide(p, s);   // bf16: one workgroup for 128 heads
-    hipLaunchKernelGGL((mla_decode_kernel<true>), grid, dim3(MlaCfg::kThreads), 0, s, p);
+    hipLaunchKernelGGL(mla_int8_kernel, grid, dim3(MlaCfg::kThreads), 0, s, p);
     return hipGetLastError();
 }
 
