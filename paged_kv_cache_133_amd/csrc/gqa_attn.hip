@@ -128,7 +128,7 @@ __device__ __forceinline__ void tile_pv(const uint8_t* stage, RowState& st, bool
                                         const float* vscale = nullptr) {
     using C = GqaCfg<D>;
     // INT8 codes: each key's V scale goes into its weight for the value sum (P' = p s_v; the
-    // masked keys' stale scales never reach it), while l sums the rounded p.
+    // masked keys' stale scales never reach it), while l sums the fp32 p.
     float vs[8];
     if (vscale) {
         const f32x4 s0 = *reinterpret_cast<const f32x4*>(vscale + 4 * g);
@@ -143,20 +143,18 @@ __device__ __forceinline__ void tile_pv(const uint8_t* stage, RowState& st, bool
         for (int e = 0; e < 8; e += 2) {
             const float e0 = fast_exp2(__builtin_fmaf(sv[e], scale_log2, mneg));
             const float e1 = fast_exp2(__builtin_fmaf(sv[e + 1], scale_log2, mneg));
-            const uint32_t w = pack_bf16(e0, e1);
-            st.l = dot2_bf16(w, kOnesBf16x2, st.l);
-            pw[e >> 1] = vscale ? pack_bf16(e0 * vs[e], e1 * vs[e + 1]) : w;
+            st.l += e0 + e1;
+            pw[e >> 1] = vscale ? pack_bf16(e0 * vs[e], e1 * vs[e + 1]) : pack_bf16(e0, e1);
         }
     } else {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
             const float e0 = sv[e] == -INFINITY ? 0.0f : fast_exp2(sv[e] - st.m);
             const float e1 = sv[e + 1] == -INFINITY ? 0.0f : fast_exp2(sv[e + 1] - st.m);
-            const uint32_t w = pack_bf16(e0, e1);
-            st.l = dot2_bf16(w, kOnesBf16x2, st.l);
+            st.l += e0 + e1;
             pw[e >> 1] = vscale ? pack_bf16(sv[e] == -INFINITY ? 0.0f : e0 * vs[e],
                                             sv[e + 1] == -INFINITY ? 0.0f : e1 * vs[e + 1])
-                                : w;
+                                : pack_bf16(e0, e1);
         }
     }
     const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);

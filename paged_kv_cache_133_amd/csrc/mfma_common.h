@@ -28,7 +28,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2f = 0.69314718055994530942f;
 constexpr float kRescaleSlack = 8.0f;           // log2 units a row max may grow before rescaling
-constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // bf16 pair (1, 1)
 constexpr int kKeys = 32;                       // keys per tile
 constexpr int kStages = 4;                      // LDS stages of the tile pipeline
 constexpr int kChunkTiles = 32;                 // tiles per staged chunk of the block table

@@ -17,7 +17,7 @@
 //    and rope sums are kept apart and weighed per key with the two scales;
 //  * lane (g, n) (g = lane / 16) holds 8 keys of head n: the head's max and sum take two
 //    cross-lane steps, and P'^T = bf16(p s_nope) (the nope scale folded into the value
-//    weight; l sums the rounded p) is the B operand of the next product with k-slot
+//    weight; l sums the fp32 p) is the B operand of the next product with k-slot
 //    8 g + 4 h + r standing for accumulator entry r of key half h;
 //  * O^T (512 x 16 heads, 128 registers) += V^T . P'^T, the A operand built by two
 //    ds_read_b64_tr_b16 per product from the nope part of the same buffer rows;
@@ -346,8 +346,8 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_int8_kernel(MfmaParams p
         return max_xor32(max_xor16(tmax));
     };
 
-    // P^T of tile t against the running max (k-slot 8 g + 4 h + r is entry (h, r); the sum
-    // adds the rounded weights), then O^T += V^T . P^T.
+    // P^T of tile t against the running max (k-slot 8 g + 4 h + r is entry (h, r); l adds
+    // the fp32 weights, the products take them rounded), then O^T += V^T . P^T.
     auto probs_pv = [&](int t, bool full, const float* sv, const float* sn) {
         u32x4 pw;
         if (full) {
@@ -356,8 +356,7 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_int8_kernel(MfmaParams p
             for (int e = 0; e < 8; e += 2) {
                 const float e0 = fast_exp2(__builtin_fmaf(sv[e], p.scale_log2, mneg));
                 const float e1 = fast_exp2(__builtin_fmaf(sv[e + 1], p.scale_log2, mneg));
-                const uint32_t w = pack_bf16(e0, e1);
-                st.l = dot2_bf16(w, kOnesBf16x2, st.l);
+                st.l += e0 + e1;
                 pw[e >> 1] = pack_bf16(e0 * sn[e], e1 * sn[e + 1]);
             }
         } else {
@@ -365,8 +364,7 @@ __global__ __launch_bounds__(MlaCfg::kThreads) void mla_int8_kernel(MfmaParams p
             for (int e = 0; e < 8; e += 2) {
                 const float e0 = sv[e] == -INFINITY ? 0.0f : fast_exp2(sv[e] - st.m);
                 const float e1 = sv[e + 1] == -INFINITY ? 0.0f : fast_exp2(sv[e + 1] - st.m);
-                const uint32_t w = pack_bf16(e0, e1);
-                st.l = dot2_bf16(w, kOnesBf16x2, st.l);
+                st.l += e0 + e1;
                 pw[e >> 1] = pack_bf16(e0 * sn[e], e1 * sn[e + 1]);
             }
         }

@@ -364,10 +364,10 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
             else s_ev = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], s_ev, 0, 0, 0);
             if (s < 8) {   // exponential pair s of P^T(t)
                 const int i = 2 * s;
-                const uint32_t w = pack_bf16(fast_exp2(__builtin_fmaf(s_cur[i], sc, mneg)),
-                                             fast_exp2(__builtin_fmaf(s_cur[i + 1], sc, mneg)));
-                st.l = dot2_bf16(w, kOnesBf16x2, st.l);
-                pw[i >> 3][(i & 7) >> 1] = w;
+                const float e0 = fast_exp2(__builtin_fmaf(s_cur[i], sc, mneg));
+                const float e1 = fast_exp2(__builtin_fmaf(s_cur[i + 1], sc, mneg));
+                st.l += e0 + e1;
+                pw[i >> 3][(i & 7) >> 1] = pack_bf16(e0, e1);
             }
             __builtin_amdgcn_sched_barrier(0);
         }

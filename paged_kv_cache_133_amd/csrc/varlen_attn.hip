@@ -297,10 +297,10 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
                 s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[i], s_next, 0, 0, 0);
             if (i < 8) {
                 const int r = 2 * i;
-                const uint32_t w = pack_bf16(fast_exp2(__builtin_fmaf(sv[r], sc, mneg)),
-                                             fast_exp2(__builtin_fmaf(sv[r + 1], sc, mneg)));
-                st.l = dot2_bf16(w, kOnesBf16x2, st.l);
-                pw[r >> 3][(r & 7) >> 1] = w;
+                const float e0 = fast_exp2(__builtin_fmaf(sv[r], sc, mneg));
+                const float e1 = fast_exp2(__builtin_fmaf(sv[r + 1], sc, mneg));
+                st.l += e0 + e1;
+                pw[r >> 3][(r & 7) >> 1] = pack_bf16(e0, e1);
             }
             if (i < 2 * C::kMTiles) {
                 const int mt = i >> 1, ks = i & 1;

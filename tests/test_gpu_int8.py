@@ -10,7 +10,7 @@ import paged_kv_cache_133_amd as pkv
 from oracle import oracle
 from paged_kv_cache_133_amd import _lib
 from paged_kv_cache_133_amd import workloads as wl
-from tests.gpu_common import LSE_ABS_MFMA, say
+from tests.gpu_common import LSE_REL, lse_error, say
 from tests.helpers import host
 
 pytestmark = pytest.mark.gpu
@@ -104,14 +104,9 @@ def _check(c, out, lse, kdeq, vdeq, window, rows=None):
 
 
 def _check_lse(c, got, ol):
-    """1..4 query heads per kv head: the split kernel sums fp32 weights (relative 1e-4);
-    5..16: the matrix-core kernel sums bf16-rounded weights (absolute LSE_ABS_MFMA)."""
-    if c.w.num_q_heads // c.w.num_kv_heads > 4:
-        lerr = np.abs(got - ol).max()
-        assert lerr <= LSE_ABS_MFMA, f"lse error {lerr:.3e}"
-    else:
-        lerr = (np.abs(got - ol) / np.maximum(1.0, np.abs(ol))).max()
-        assert lerr <= 1e-4, f"lse error {lerr:.3e}"
+    """Both INT8 kernels (1..4 and 5..16 query heads per kv head) sum fp32 weights."""
+    lerr = lse_error(got, ol)
+    assert lerr <= LSE_REL, f"lse error {lerr:.3e}"
 
 
 @pytest.mark.parametrize("shape", [(32, 32, 128, 16), (8, 2, 64, 1), (16, 4, 128, 128),

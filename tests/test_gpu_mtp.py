@@ -10,7 +10,7 @@ import torch
 import paged_kv_cache_133_amd as pkv
 from paged_kv_cache_133_amd import _lib
 from paged_kv_cache_133_amd import workloads as wl
-from tests.gpu_common import ATOL, compare_outputs, compare_writes, oracle_step, say
+from tests.gpu_common import ATOL, compare_outputs, compare_writes, oracle_step, say, LSE_REL, lse_error
 
 pytestmark = pytest.mark.gpu
 
@@ -100,7 +100,8 @@ def test_mtp_two_pass_equals_one_and_matches_varlen():
                                      w.scale, causal=True, lse=lse_v)
     torch.cuda.synchronize()
     assert float((out_v.float() - one["out"].float()).abs().max()) <= ATOL["bf16"]
-    assert float((lse_v - one["lse"]).abs().max()) <= 4e-3
+    # two kernels, each within LSE_REL of the exact value
+    assert lse_error(lse_v.cpu().numpy(), one["lse"].cpu().numpy()) <= 2 * LSE_REL
 
 
 def test_mtp_padding_rows():
