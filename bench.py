@@ -46,8 +46,6 @@ def dominant_kernel(w):
     """The attention kernel a workload's step runs (the library's dispatch rule) and the
     sources its traffic counters depend on."""
     if w.mode == "mla":
-        if w.kv_dtype == "int8":
-            return "mla_int8_kernel", [CSRC + "mla_attn.hip"] + MFMA_SOURCES
         return "mla_wide_kernel", [CSRC + "mla_wide.hip"] + MFMA_SOURCES
     if w.q_tokens:      # multi-token decode: the range-streaming kernel
         return "gqa_stream_kernel", [CSRC + "gqa_attn.hip"] + MFMA_SOURCES

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.hip", "write.hip", "norm_rope.hip", "decode.hip", "int8_kv.hip", "mla_attn.hip", "mla_wide.hip",
+SOURCES = ["api.hip", "write.hip", "norm_rope.hip", "decode.hip", "int8_kv.hip", "mla_wide.hip",
            "varlen_attn.hip", "gqa_attn.hip", "block_manager.hip",
            "runner.hip"]
 ARCH = "gfx950"
@@ -28,7 +28,6 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={
 # The MFMA attention kernels keep their accumulators in ordinary VGPRs: with the default
 # choice (AGPRs) the online-softmax rescale copies every accumulator out and back each tile.
 EXTRA = {"varlen_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "mla_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "mla_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "gqa_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 

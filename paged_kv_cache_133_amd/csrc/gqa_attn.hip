@@ -61,18 +61,6 @@ struct GqaCfg {
     static_assert(2 * kDma < 64, "vmcnt range");
 };
 
-// 16 int8 codes as 16 bf16 (exact: |q| <= 127), codes 0-7 in lo, 8-15 in hi.
-__device__ __forceinline__ void codes_to_bf16(u32x4 v, u32x4& lo, u32x4& hi) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float c0 = (float)(int)(int8_t)(v[i]), c1 = (float)(int)(int8_t)(v[i] >> 8);
-        const float c2 = (float)(int)(int8_t)(v[i] >> 16), c3 = (float)(int)(int8_t)(v[i] >> 24);
-        const uint32_t a = pack_bf16(c0, c1), b = pack_bf16(c2, c3);
-        if (i < 2) { lo[2 * i] = a; lo[2 * i + 1] = b; }
-        else { hi[2 * i - 4] = a; hi[2 * i - 3] = b; }
-    }
-}
-
 // ------------------------------------------------------------------ per-tile math
 // Scores of the tile in `stage`: full tiles keep the raw S^T entries; a tile that is not
 // wholly inside the key range [k_lo, k_end) scales them and sets keys outside it to -inf.

@@ -67,6 +67,20 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds_base) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m0) : "memory");
 }
 
+// x, opaque to the compiler: per-lane values derived from it inside a loop are computed
+// there, where they are needed, instead of being hoisted out and held in registers (or
+// spilled) across the whole loop.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// 4 bytes per lane from src into LDS at lds_base + 4 * lane, as lds_dma16.
+__device__ __forceinline__ void lds_dma4(const void* src, uint8_t* lds_base) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_base;
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(src), "{m0}"(m0) : "memory");
+}
+
 // The same with a wave-uniform 64-bit base in SGPRs and a 32-bit offset per lane (the
 // saddr form), for loads whose addresses differ from lane to lane only by constants.
 // s_nop 4: an SGPR or M0 written by a VALU instruction needs five wait states before a
@@ -112,6 +126,25 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
 }
 
+// 8 int8 codes (two dwords) as 8 bf16 (exact: |code| <= 127).
+__device__ __forceinline__ u32x4 codes8_to_bf16(uint32_t x, uint32_t y) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t v = i ? y : x;
+        const float c0 = (float)(int)(int8_t)(v), c1 = (float)(int)(int8_t)(v >> 8);
+        const float c2 = (float)(int)(int8_t)(v >> 16), c3 = (float)(int)(int8_t)(v >> 24);
+        r[2 * i] = pack_bf16(c0, c1);
+        r[2 * i + 1] = pack_bf16(c2, c3);
+    }
+    return r;
+}
+// 16 int8 codes as 16 bf16, codes 0-7 in lo, 8-15 in hi.
+__device__ __forceinline__ void codes_to_bf16(u32x4 v, u32x4& lo, u32x4& hi) {
+    lo = codes8_to_bf16(v[0], v[1]);
+    hi = codes8_to_bf16(v[2], v[3]);
+}
+
 // ------------------------------------------------------------------ block-table chunks
 // Chunk c holds the entries of keys [k_begin + 1024 c, k_begin + 1024 (c + 1)) in LDS
 // buffer c & 1.  Entries are loaded into registers when the chunk before it starts to
@@ -138,9 +171,25 @@ struct TableChunks {
         for (int j = 0; j < kRegs; ++j)
             if (tid + j * NT < kTabEntries) dst[tid + j * NT] = min(max(regs[j], 0), last_block);
     }
-    // Physical block of key (all keys of one tile lie in one chunk).
+    // Chunk c's entries straight into LDS buffer c & 1, without registers: four loads of 64
+    // entries per wave of a 4-wave workgroup (a range starts on a tile, so a chunk spans at
+    // most 1024 entries); entries past the chunk's last repeat it.  Completion is waited for
+    // with the wave's load counter like the tile loads, and published by the barriers
+    // before the chunk is used.
+    __device__ void load_lds(int c, int wave) const {
+        static_assert(NT == 256 && 16 * 64 <= kTabEntries, "four waves, 1024 entries");
+        const int e0 = first_entry(c);
+        const int e1 = (min(k_end, k_begin + (c + 1) * kChunkKeys) - 1) >> bs_log2;
+        uint8_t* dst = reinterpret_cast<uint8_t*>(lds + (c & 1) * kTabEntries);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int blk = 4 * j + wave;
+            lds_dma4(row + min(e0 + 64 * blk + (int)(threadIdx.x & 63), e1), dst + blk * 256);
+        }
+    }
+    // Physical block of key (all keys of one tile lie in one chunk), clamped into the pool.
     __device__ uint32_t block_of(int key, int chunk) const {
-        return (uint32_t)lds[(chunk & 1) * kTabEntries + (key >> bs_log2) - first_entry(chunk)];
+        return (uint32_t)min(max(lds[(chunk & 1) * kTabEntries + (key >> bs_log2) - first_entry(chunk)], 0), last_block);
     }
 };
 

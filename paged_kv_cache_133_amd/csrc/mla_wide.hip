@@ -1,7 +1,7 @@
-// MLA-absorbed decode over the paged bf16 cache, one workgroup per (sequence, split) for
-// all 128 query heads ("KVCache Optimization Skill", Mode 3: key = cache_nope ||
-// cache_rope, value = cache_nope, one latent head shared by every query head): each K/V
-// tile goes from HBM into LDS once and serves every head.
+// MLA-absorbed decode over the paged cache, one workgroup per (sequence, split) for all
+// 128 query heads ("KVCache Optimization Skill", Mode 3: key = cache_nope || cache_rope,
+// value = cache_nope, one latent head shared by every query head): each K/V tile goes
+// from HBM into LDS once and serves every head.
 //
 // Four waves, one per SIMD, 32 heads each, v_mfma_f32_32x32x16_bf16 for both products:
 //  * S^T (32 keys x 32 heads) = K . Q^T over the 576-wide contraction (36 k-steps): K rows
@@ -18,11 +18,22 @@
 // anything else reads it (the rare rescale, the epilogue) and the wait states after a
 // VALU write of an operand are spelled out.
 //
-// LDS stage: 32 nope rows of 1024 bytes padded to 1040, key k in row
+// bf16 stage of a tile: 32 nope rows of 1024 bytes padded to 1040, key k in row
 // (k & 16) | 4 (k & 3) | ((k >> 2) & 3), so that the 16 lanes of a K read hit 16 different
 // bank groups and the four rows of a transposing read (keys 4 h + a, a = 0..3, of a
 // 16-key group) sit 16 banks apart; then 32 rope rows of 128 bytes (key k in row k), their
-// 16-byte chunks XOR-swizzled by row.  Four stages, the tile pipeline of mfma_common.h.
+// 16-byte chunks XOR-swizzled by row.
+//  * bf16 cache: four stages, filled straight from HBM (the tile pipeline of mfma_common.h);
+//  * INT8 cache (codes with one fp32 scale per key for the nope part and one for the rope
+//    part): the codes reach one of two code stages by direct loads three tiles ahead; each
+//    wave converts the keys it loaded itself into one of three bf16 stages (the codes
+//    exactly, the scales beside them) two tiles ahead, among the value products, so that
+//    the tile's one barrier publishes them.  A key's score weighs the nope and rope sums by
+//    their own scales, s = s_nope (q . nope) + s_rope (q . rope), in one accumulator: the
+//    nope products, times s_nope / s_rope', then the rope products added, times s_rope'
+//    (s_rope' = s_rope, raised to s_nope 2^-60 and to 2^-126 where it is smaller: the ratio
+//    stays finite, and the rope term moves by at most 2^-60 of the nope scale); the nope
+//    scale goes into the value weight (P' = bf16(p s_nope)) while l adds p.
 #include "mfma_common.h"
 
 namespace pkv {
@@ -48,6 +59,24 @@ struct WideCfg {
     static_assert(3 * kThreads + 24 <= 2 * kTabEntries, "work-order scratch fits the table area");
 };
 
+// INT8 LDS: two code stages (32 nope rows of 512 codes, then per wave 1 KiB: its 8 rope
+// rows of 64 codes, its 8 nope and 8 rope scales), three bf16 stages each followed by three
+// per-key factors of the tile (s_nope, s_nope / s_rope', s_rope'), the table.
+struct WideI8Cfg {
+    static constexpr int kCodeStages = 2;
+    static constexpr int kNopeCodes = kKeys * 512;
+    static constexpr int kAux = 1024;
+    static constexpr int kCodeStage = kNopeCodes + WideCfg::kWaves * kAux;
+    static constexpr int kBufs = 3;
+    static constexpr int kBuf = WideCfg::kStage + 3 * kKeys * 4;
+    static constexpr int kBufOff = kCodeStages * kCodeStage;
+    static constexpr int kTabOff = kBufOff + kBufs * kBuf;
+    static constexpr int kSmem = kTabOff + 2 * kTabEntries * 4;
+    static constexpr int kDma = 5;                          // wave loads per tile: 4 nope + 1 rope and scales
+    static_assert(kSmem <= 160 * 1024, "LDS");
+    static_assert(kBuf % 16 == 0 && kCodeStage % 16 == 0, "alignment");
+};
+
 // LDS nope row of key k of a tile.
 __device__ __forceinline__ int wide_row(int k) { return (k & 16) | ((k & 3) << 2) | ((k >> 2) & 3); }
 // Physical 16-byte chunk of rope chunk c in rope row r (an involution).
@@ -71,14 +100,18 @@ __device__ __forceinline__ int wide_rope_chunk(int r, int c) { return c ^ ((r >>
 // Cycles for an MFMA result written by inline assembly to be readable by anything else.
 __device__ __forceinline__ void wait_mfma_result() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
-// APPEND: the key at seq_lens[b] - 1 is the step's new latent row, read from p.k_new /
-// p.rope_new instead of the cache; the split that holds it also stores it at its slot
-// (reported in slots_out).  A row longer than the length bound writes nothing (slot -1)
-// and attends to its first len_cap cached keys.
-template <bool APPEND>
+// APPEND (bf16 only): the key at seq_lens[b] - 1 is the step's new latent row, read from
+// p.k_new / p.rope_new instead of the cache; the split that holds it also stores it at its
+// slot (reported in slots_out).  A row longer than the length bound writes nothing (slot
+// -1) and attends to its first len_cap cached keys.
+// I8: p.k_cache / p.k_rope hold int8 codes, p.k_scale / p.r_scale their scales [nb][bs].
+template <bool APPEND, bool I8>
 __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams p) {
+    static_assert(!(APPEND && I8), "the INT8 form has no append mode");
     using C = WideCfg;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[C::kSmem];
+    using W8 = WideI8Cfg;
+    constexpr int kTabOff = I8 ? W8::kTabOff : C::kTabOff;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[I8 ? W8::kSmem : C::kSmem];
 
     const int tid = threadIdx.x;
     const int wid = tid >> 6;
@@ -97,7 +130,7 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
     {
         auto nsplits = [&](int, int len) { return len > 0 ? (len + p.split_tokens - 1) / p.split_tokens : 1; };
         if (!find_item<C::kThreads>(unit, p.batch, p.seq_lens, p.len_cap, nsplits,
-                                    reinterpret_cast<int32_t*>(smem + C::kTabOff), b, split))
+                                    reinterpret_cast<int32_t*>(smem + kTabOff), b, split))
             return;
         b = __builtin_amdgcn_readfirstlane(b);
         split = __builtin_amdgcn_readfirstlane(split);
@@ -159,26 +192,41 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
     }
 
     TableChunks<C::kThreads> tab;
-    tab.lds = reinterpret_cast<int32_t*>(smem + C::kTabOff);
+    tab.lds = reinterpret_cast<int32_t*>(smem + kTabOff);
     tab.row = p.table + (int64_t)b * p.mbs;
     tab.k_begin = k_begin;
     tab.k_end = k_end;
     tab.bs_log2 = p.bs_log2;
     tab.tid = tid;
     tab.last_block = (int32_t)(p.num_blocks - 1);
-    int32_t treg[TableChunks<C::kThreads>::kRegs];
-    tab.load(0, treg);
-    tab.store(0, treg);
+    const int wid_u = __builtin_amdgcn_readfirstlane(wid);
+    tab.load_lds(0, wid_u);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     block_sync();
 
-    // Loads of one tile: wave w fills the nope rows of keys 8 w .. 8 w + 7 (one load per
-    // row, lane = 16-byte chunk) and their rope rows (one load: lane = row 8 w + lane / 8,
-    // physical chunk lane % 8).
-    const int wid_u = __builtin_amdgcn_readfirstlane(wid);
+    // The bf16 stage of tile t (what the products read).  INT8: the offset (t % 3 stages)
+    // is put in a scalar register explicitly; left to itself the compiler spent vector
+    // registers on it and spilled.
+    auto stage_of = [&](int t) -> uint8_t* {
+        if constexpr (I8) return smem + __builtin_amdgcn_readfirstlane(W8::kBufOff + (t % W8::kBufs) * W8::kBuf);
+        else return smem + (t % kStages) * C::kStage;
+    };
+    auto code_stage = [&](int u) -> uint8_t* {
+        return smem + __builtin_amdgcn_readfirstlane((u % W8::kCodeStages) * W8::kCodeStage);
+    };
+
+    // Loads of one tile.  bf16: wave w fills the nope rows of keys 8 w .. 8 w + 7 (one load
+    // per row, lane = 16-byte chunk) and their rope rows (one load: lane = row 8 w + lane / 8,
+    // physical chunk lane % 8).  INT8: wave w loads the codes of keys 8 w .. 8 w + 7 into
+    // code stage u % 2: their nope rows (4 loads of two rows) and one load whose lanes 0-31
+    // take the 8 rope rows, 32-33 the 8 nope scales and 34-35 the 8 rope scales (a block's
+    // scales are in slot order, and an aligned group of 4 keys lies in one block); the
+    // other lanes re-read lane 32's bytes.
     const int bs_mask = (1 << p.bs_log2) - 1;
     const uint8_t* nope_g = reinterpret_cast<const uint8_t*>(p.k_cache);
     const uint8_t* rope_g = reinterpret_cast<const uint8_t*>(p.k_rope);
+    const uint8_t* nsc_g = reinterpret_cast<const uint8_t*>(p.k_scale);
+    const uint8_t* rsc_g = reinterpret_cast<const uint8_t*>(p.r_scale);
     const int rope_r = 8 * wid_u + (lane >> 3);
     const int rope_c = wide_rope_chunk(rope_r, lane & 7);
     const uint32_t rope_voff = (uint32_t)((lane >> 3) * 128 + rope_c * 16);
@@ -191,46 +239,125 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
     };
     auto entry_of = [&](int u) { return uniform_load(tab.row + ((k_begin + u * kKeys + 8 * wid_u) >> p.bs_log2)); };
     int32_t next_entry = fast_tile(0) ? entry_of(0) : 0;
+    // INT8, fast tile: load j (< 4: nope rows 8 w + 2 j and 8 w + 2 j + 1; 4: rope rows and
+    // scales) from the wave's first slot.
+    auto code_load = [&](int u, uint64_t slot0, int j) {
+        uint8_t* cs = code_stage(u);
+        if (j < 4) {
+            lds_dma16_s(nope_g + slot0 * 512u + j * 1024, (uint32_t)lane * 16u, cs + (8 * wid_u + 2 * j) * 512);
+        } else {
+            const int ln = opaque(lane), q = ln >= 32 && ln < 36 ? ln - 32 : 0;
+            const uint8_t* src = ln < 32 ? rope_g + (slot0 * 64u + (uint32_t)(ln * 16))
+                                         : ((q & 2) ? rsc_g : nsc_g) + (slot0 * 4u + (uint32_t)((q & 1) * 16));
+            lds_dma16(src, cs + W8::kNopeCodes + wid_u * W8::kAux);
+        }
+    };
     auto issue_tile = [&](int u) {
         const int kb = k_begin + u * kKeys;
         const int chunk = u / kChunkTiles;
-        uint8_t* stage = smem + (u % kStages) * C::kStage;
         const int32_t entry = next_entry;
         if (u + 1 < ntiles && fast_tile(u + 1)) next_entry = entry_of(u + 1);
         if (fast_tile(u)) {
             const int key0 = kb + 8 * wid_u;
             const int32_t blk = min(max(entry, 0), tab.last_block);
             const uint64_t slot0 = ((uint64_t)(uint32_t)blk << p.bs_log2) | (uint32_t)(key0 & bs_mask);
-            const uint8_t* nb = nope_g + slot0 * 1024u;
+            if constexpr (I8) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                lds_dma16_s(nb + j * 1024, (uint32_t)lane * 16u, stage + wide_row(8 * wid_u + j) * C::kNopeRow);
-            lds_dma16_s(rope_g + slot0 * 128u, rope_voff, stage + C::kRopeBase + wid_u * 1024);
+                for (int j = 0; j < 5; ++j) code_load(u, slot0, j);
+            } else {
+                uint8_t* stage = stage_of(u);
+                const uint8_t* nb = nope_g + slot0 * 1024u;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    lds_dma16_s(nb + j * 1024, (uint32_t)lane * 16u, stage + wide_row(8 * wid_u + j) * C::kNopeRow);
+                lds_dma16_s(rope_g + slot0 * 128u, rope_voff, stage + C::kRopeBase + wid_u * 1024);
+            }
             return;
         }
+        const int ln = opaque(lane);   // per-lane addresses are computed here, not hoisted
+        if constexpr (I8) {
+            // keys past the range: their rows and scales come from the last key (its 4-key
+            // group for the scales); the conversion gives them scale 0
+            uint8_t* cs = code_stage(u);
+            const int q = ln >= 32 && ln < 36 ? ln - 32 : 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int key = min(kb + 8 * wid_u + j, k_end - 1);
-            const uint32_t blk = __builtin_amdgcn_readfirstlane(tab.block_of(key, chunk));
-            const uint8_t* src = nope_g + (((uint64_t)blk << p.bs_log2) | (uint32_t)(key & bs_mask)) * 1024u + lane * 16;
+            for (int j = 0; j < 4; ++j) {
+                const int key = min(kb + 8 * wid_u + 2 * j + (ln >> 5), k_end - 1);
+                const uint64_t slot = ((uint64_t)tab.block_of(key, chunk) << p.bs_log2) | (uint32_t)(key & bs_mask);
+                lds_dma16(nope_g + (slot * 512u + (uint32_t)((ln & 31) * 16)), cs + (8 * wid_u + 2 * j) * 512);
+            }
+            const int key = ln < 32 ? min(kb + 8 * wid_u + (ln >> 2), k_end - 1)
+                                    : min(kb + 8 * wid_u + 4 * (q & 1), (k_end - 1) & ~3);
+            const uint64_t slot = ((uint64_t)tab.block_of(key, chunk) << p.bs_log2) | (uint32_t)(key & bs_mask);
+            lds_dma16(ln < 32 ? rope_g + (slot * 64u + (uint32_t)((ln & 3) * 16)) : ((q & 2) ? rsc_g : nsc_g) + slot * 4u,
+                      cs + W8::kNopeCodes + wid_u * W8::kAux);
+        } else {
+            uint8_t* stage = stage_of(u);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int key = min(kb + 8 * wid_u + j, k_end - 1);
+                const uint32_t blk = __builtin_amdgcn_readfirstlane(tab.block_of(key, chunk));
+                const uint8_t* src = nope_g + (((uint64_t)blk << p.bs_log2) | (uint32_t)(key & bs_mask)) * 1024u + lane * 16;
+                if (APPEND && key == new_key)
+                    src = reinterpret_cast<const uint8_t*>(p.k_new) + (int64_t)b * 1024 + lane * 16;
+                lds_dma16(src, stage + wide_row(8 * wid_u + j) * C::kNopeRow);
+            }
+            const int key = min(kb + rope_r, k_end - 1);
+            const uint32_t blk = tab.block_of(key, chunk);
+            const uint8_t* src = rope_g + (((uint64_t)blk << p.bs_log2) | (uint32_t)(key & bs_mask)) * 128u + rope_c * 16;
             if (APPEND && key == new_key)
-                src = reinterpret_cast<const uint8_t*>(p.k_new) + (int64_t)b * 1024 + lane * 16;
-            lds_dma16(src, stage + wide_row(8 * wid_u + j) * C::kNopeRow);
+                src = reinterpret_cast<const uint8_t*>(p.rope_new) + (int64_t)b * 128 + rope_c * 16;
+            lds_dma16(src, stage + C::kRopeBase + wid_u * 1024);
         }
-        const int key = min(kb + rope_r, k_end - 1);
-        const uint32_t blk = tab.block_of(key, chunk);
-        const uint8_t* src = rope_g + (((uint64_t)blk << p.bs_log2) | (uint32_t)(key & bs_mask)) * 128u + rope_c * 16;
-        if (APPEND && key == new_key)
-            src = reinterpret_cast<const uint8_t*>(p.rope_new) + (int64_t)b * 128 + rope_c * 16;
-        lds_dma16(src, stage + C::kRopeBase + wid_u * 1024);
     };
-    // Table chunks and the loads of tile u.
+    // The next table chunk (as the loads of a chunk's first tile are issued; it is used 32
+    // tiles later) and the loads of tile u.
+    auto next_chunk = [&](int u) {
+        const int c = u / kChunkTiles;
+        if (u % kChunkTiles == 0 && tab.exists(c + 1)) tab.load_lds(c + 1, wid_u);
+    };
     auto feed = [&](int u) {
         if (u >= ntiles) return;
-        const int c = u / kChunkTiles;
-        if (u % kChunkTiles == 0 && tab.exists(c + 1)) tab.load(c + 1, treg);
-        if (u % kChunkTiles == kChunkTiles / 2 && tab.exists(c + 1)) tab.store(c + 1, treg);
+        next_chunk(u);
         issue_tile(u);
+    };
+
+    // INT8 conversion of this wave's keys of tile u (code stage u % 2 -> bf16 stage u % 3),
+    // in ten pieces of one LDS read and one write: piece j < 8 is the nope row of key
+    // 8 w + j (lane = 8 codes), 8 the rope rows (lane = row 8 w + lane / 8, 8 codes), 9 the
+    // factors of the 8 keys (lanes 0-7; keys past the range get s_nope = 0, so that no
+    // stale scale reaches a weight, and a finite score).  The wave reads only what it
+    // loaded itself, so its own load counter is the only wait.
+    auto conv_read = [&](int u, int j) -> u32x2 {
+        const uint8_t* cs = code_stage(u);
+        const uint8_t* aux = cs + W8::kNopeCodes + wid_u * W8::kAux;
+        if (j < 8) return *reinterpret_cast<const u32x2*>(cs + (8 * wid_u + j) * 512 + lane * 8);
+        const int ln = opaque(lane);   // (pieces 8 and 9: addresses computed here, not hoisted)
+        if (j == 8) return *reinterpret_cast<const u32x2*>(aux + ln * 8);
+        const uint32_t* sc = reinterpret_cast<const uint32_t*>(aux + 512) + (ln & 7);
+        return u32x2{sc[0], sc[8]};
+    };
+    // wide_row(8 w + j) = wide_row(8 w) + 4 (j % 4) + j / 4 (disjoint bit fields)
+    const int conv_nope = wide_row(8 * wid_u) * C::kNopeRow + lane * 16;
+    auto conv_write = [&](int u, int j, u32x2 c) {
+        uint8_t* bf = stage_of(u);
+        if (j < 8) {
+            *reinterpret_cast<u32x4*>(bf + conv_nope + (4 * (j & 3) + (j >> 2)) * C::kNopeRow) = codes8_to_bf16(c[0], c[1]);
+        } else if (j == 8) {
+            const int ln = opaque(lane);
+            const int r = 8 * wid_u + (ln >> 3);
+            *reinterpret_cast<u32x4*>(bf + C::kRopeBase + r * 128 + wide_rope_chunk(r, ln & 7) * 16) =
+                codes8_to_bf16(c[0], c[1]);
+        } else if (lane < 8) {
+            const int key = 8 * wid_u + opaque(lane);
+            const bool in = k_begin + u * kKeys + key < k_end;
+            const float sn = in ? __uint_as_float(c[0]) : 0.0f;
+            const float srp = fmaxf(fmaxf(in ? __uint_as_float(c[1]) : 0.0f, sn * 0x1p-60f), 0x1p-126f);
+            float* f = reinterpret_cast<float*>(bf + C::kStage) + key;
+            f[0] = sn;
+            f[kKeys] = sn / srp;
+            f[2 * kKeys] = srp;
+        }
     };
 
     // Per-lane LDS offsets inside a stage.  K read of k-step s < 32: nope row of key l % 32,
@@ -255,24 +382,62 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
         const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(base + 2 * C::kNopeRow));
         return __builtin_bit_cast(bf16x8_t, u32x4{lo[0], lo[1], hi[0], hi[1]});
     };
+    // INT8: factor n (0: s_nope, 1: s_nope / s_rope', 2: s_rope') of this lane's keys
+    // 8 q + 4 h .. + 3.
+    auto scales4 = [&](const uint8_t* stage, int n, int q) -> f32x4 {
+        return *reinterpret_cast<const f32x4*>(stage + C::kStage + (n * kKeys + 8 * q + 4 * h) * 4);
+    };
 
     RowState st;
     f32x16 oacc[16];
 #pragma unroll
     for (int ct = 0; ct < 16; ++ct) oacc[ct] = f32x16{};
 
-    // Prologue: tiles 0..2 issued, tile 0 in LDS, S^T(0).
+    // Prologue.  bf16: tiles 0..2 issued, tile 0 in LDS.  INT8: tiles 0 and 1 loaded and
+    // converted, tile 2 issued (into the code stage of tile 0, read above).  Then S^T(0).
+    if constexpr (I8) {
+        feed(0);
+        feed(1);
 #pragma unroll
-    for (int u = 0; u < kStages - 1; ++u) feed(u);
-    wait_tile<C::kDma>(min(ntiles - 1, kStages - 2));
+        for (int u = 0; u < 2; ++u) {
+            if (u == 0 && ntiles > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(W8::kDma));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            if (u < ntiles) {
+#pragma unroll
+                for (int j = 0; j < 10; ++j) conv_write(u, j, conv_read(u, j));
+            }
+        }
+        feed(2);
+    } else {
+#pragma unroll
+        for (int u = 0; u < kStages - 1; ++u) feed(u);
+        wait_tile<C::kDma>(min(ntiles - 1, kStages - 2));
+    }
     block_sync();
     f32x16 s_cur;
     {
-        const uint8_t* stage = smem;
+        const uint8_t* stage = stage_of(0);
         s_cur = f32x16{};
 #pragma unroll
-        for (int s = 0; s < 36; ++s)
+        for (int s = 0; s < (I8 ? 32 : 36); ++s)
             s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(stage, s), qf[s], s_cur, 0, 0, 0);
+        if constexpr (I8) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 r = scales4(stage, 1, q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s_cur[4 * q + e] *= r[e];
+            }
+#pragma unroll
+            for (int s = 32; s < 36; ++s)
+                s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(stage, s), qf[s], s_cur, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 r = scales4(stage, 2, q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s_cur[4 * q + e] *= r[e];
+            }
+        }
     }
 
     for (int t = 0; t < ntiles; ++t) {
@@ -317,19 +482,19 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
             }
             st.m = mnew;
         }
-        // Tile t + 3 goes into the stage of tile t - 1 once the barrier has freed it; the
-        // loads of a fast tile are spread over the value products below (one per product),
-        // others are issued here at once.
-        const int u = t + kStages - 1;
+        // Tile t + 3 goes into the stage of tile t - 1 (INT8: the code stage of tile t + 1,
+        // which this wave has converted) once the barrier has freed it; the loads of a fast
+        // tile are spread over the products below (one per product), others are issued here
+        // at once.  INT8: the barrier also publishes the bf16 stage of tile t + 1, converted
+        // during tile t - 1.
+        const int u = t + 3;
         bool spread = false;
         uint64_t slot_u = 0;
         if (t + 1 < ntiles) {
-            wait_tile<C::kDma>(min(ntiles - 2 - t, kStages - 3));
+            if constexpr (!I8) wait_tile<C::kDma>(min(ntiles - 2 - t, kStages - 3));
             block_sync();
             if (u < ntiles) {
-                const int c = u / kChunkTiles;
-                if (u % kChunkTiles == 0 && tab.exists(c + 1)) tab.load(c + 1, treg);
-                if (u % kChunkTiles == kChunkTiles / 2 && tab.exists(c + 1)) tab.store(c + 1, treg);
+                if constexpr (!I8) next_chunk(u);
                 if (fast_tile(u)) {
                     const int32_t entry = next_entry;
                     if (u + 1 < ntiles && fast_tile(u + 1)) next_entry = entry_of(u + 1);
@@ -341,42 +506,57 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
                 }
             }
         }
-        uint8_t* ustage = smem + (u % kStages) * C::kStage;
         // S^T(t + 1) (on a stage no load writes any more when t + 1 = ntiles: a throw-away
         // result that keeps this region straight-line), interleaved step by step with the
         // exponentials of P^T(t); each step a scheduling region of its own.
-        const uint8_t* kst = smem + ((t + 1) % kStages) * C::kStage;
+        const uint8_t* kst = stage_of(t + 1);
+        const uint8_t* vst = stage_of(t);
         const float sc = full ? p.scale_log2 : 1.0f;
         const float mneg = st.m == -INFINITY ? 0.0f : -st.m;
         bf16x8_t kring[C::kKRing];
 #pragma unroll
         for (int s = 0; s < C::kKRing; ++s) kring[s] = k_operand(kst, s);
+        f32x4 vsc;   // INT8: the nope scales of tile t (the value weights) of 4 keys
+        if constexpr (I8) vsc = scales4(vst, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        // two accumulation chains (even and odd k-steps), so that consecutive products do
-        // not wait for each other's result
+        // bf16: two accumulation chains (even and odd k-steps), so that consecutive products
+        // do not wait for each other's result.  INT8: the 32 nope k-steps in one chain here;
+        // its rope k-steps follow among the value products.
+        constexpr int kSteps = I8 ? 32 : 36;
         f32x16 s_ev = f32x16{}, s_od = f32x16{};
         u32x4 pw[2];
 #pragma unroll
-        for (int s = 0; s < 36; ++s) {
+        for (int s = 0; s < kSteps; ++s) {
             const bf16x8_t ka = kring[s % C::kKRing];
-            if (s + C::kKRing < 36) kring[s % C::kKRing] = k_operand(kst, s + C::kKRing);
-            if (s & 1) s_od = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], s_od, 0, 0, 0);
+            if (s + C::kKRing < kSteps) kring[s % C::kKRing] = k_operand(kst, s + C::kKRing);
+            if (!I8 && (s & 1)) s_od = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], s_od, 0, 0, 0);
             else s_ev = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], s_ev, 0, 0, 0);
             if (s < 8) {   // exponential pair s of P^T(t)
                 const int i = 2 * s;
                 const float e0 = fast_exp2(__builtin_fmaf(s_cur[i], sc, mneg));
                 const float e1 = fast_exp2(__builtin_fmaf(s_cur[i + 1], sc, mneg));
                 st.l += e0 + e1;
-                pw[i >> 3][(i & 7) >> 1] = pack_bf16(e0, e1);
+                if constexpr (I8) {
+                    pw[i >> 3][(i & 7) >> 1] = pack_bf16(e0 * vsc[i & 3], e1 * vsc[(i & 3) + 1]);
+                    if (s % 2 == 1 && s < 7) vsc = scales4(vst, 0, s / 2 + 1);
+                } else {
+                    pw[i >> 3][(i & 7) >> 1] = pack_bf16(e0, e1);
+                }
             }
+            if (I8 && spread && s >= 8 && s < 13) code_load(u, slot_u, s - 8);
             __builtin_amdgcn_sched_barrier(0);
         }
         // O^T += V^T . P^T(t): 32 products, the transposing reads kVRing products ahead.
-        const uint8_t* vst = smem + (t % kStages) * C::kStage;
+        // INT8, among them: the scores of tile t + 1 completed (products 0-14: the nope sums
+        // times s_nope / s_rope', the four rope products, times s_rope'), then this wave's
+        // conversion of tile t + 2 (16-27).
         bf16x8_t vring[C::kVRing];
 #pragma unroll
         for (int m = 0; m < C::kVRing; ++m) vring[m] = v_operand(vst, m);
         __builtin_amdgcn_sched_barrier(0);
+        f32x4 ksc[2];
+        bf16x8_t rk[2];
+        u32x2 craw[2];
 #pragma unroll
         for (int m = 0; m < 32; ++m) {
             const bf16x8_t va = vring[m % C::kVRing];
@@ -384,14 +564,50 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
             const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw[m >> 4]);
             // s_nop 2: its operands may have just been written by VALU instructions
             asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(oacc[m & 15]) : "v"(va), "v"(pb));
-            if (spread && m < 8)
-                lds_dma16_s(nope_g + (slot_u + m) * 1024u, (uint32_t)lane * 16u,
-                            ustage + wide_row(8 * wid_u + m) * C::kNopeRow);
-            if (spread && m == 8)
-                lds_dma16_s(rope_g + slot_u * 128u, rope_voff, ustage + C::kRopeBase + wid_u * 1024);
+            if constexpr (I8) {
+                if (m < 16) {
+                    // the nope sums times s_nope / s_rope' (products 1-2), the rope products
+                    // (3, 5, 7, 9), times s_rope' (12, 14); factors of 8 keys, two operands
+                    // in flight
+                    if (m == 1 || m == 2 || m == 12 || m == 14) {
+                        const int i0 = m == 1 || m == 12 ? 0 : 8;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) s_ev[i0 + e] *= ksc[e >> 2][e & 3];
+                    }
+                    if (m == 0 || m == 1 || m == 10 || m == 12) {
+                        const int n = m < 10 ? 1 : 2, q = m == 0 || m == 10 ? 0 : 2;
+                        ksc[0] = scales4(kst, n, q);
+                        ksc[1] = scales4(kst, n, q + 1);
+                    }
+                    if (m >= 3 && m <= 9 && (m & 1))
+                        s_ev = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rk[((m - 3) >> 1) & 1], qf[32 + ((m - 3) >> 1)], s_ev, 0, 0, 0);
+                    if (m == 1 || m == 2 || m == 3 || m == 5) {
+                        const int i = m <= 2 ? m - 1 : (m - 3) / 2 + 2;   // rope k-step 32 + i
+                        rk[i & 1] = k_operand(kst, 32 + i);
+                    }
+                } else if (t + 2 < ntiles) {
+                    const int j = m - 16;     // piece j read at product 16 + j, converted at 18 + j
+                    if (j == 0) {             // this wave's codes of tile t + 2 (tile t + 3's may fly)
+                        if (t + 3 < ntiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(W8::kDma));
+                        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+                    }
+                    if (j >= 2 && j < 12) conv_write(t + 2, j - 2, craw[j & 1]);
+                    if (j < 10) craw[j & 1] = conv_read(t + 2, j);
+                }
+                // after the wait above, so that the wait does not cover these loads
+                if (m == 28 && u < ntiles) next_chunk(u);
+            } else {
+                uint8_t* ustage = stage_of(u);
+                if (spread && m < 8)
+                    lds_dma16_s(nope_g + (slot_u + m) * 1024u, (uint32_t)lane * 16u,
+                                ustage + wide_row(8 * wid_u + m) * C::kNopeRow);
+                if (spread && m == 8)
+                    lds_dma16_s(rope_g + slot_u * 128u, rope_voff, ustage + C::kRopeBase + wid_u * 1024);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
-        s_cur = s_ev + s_od;
+        if constexpr (I8) s_cur = s_ev;
+        else s_cur = s_ev + s_od;
     }
 
     // ---------------------------------------------------------------- epilogue
@@ -436,17 +652,39 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
 
 }  // namespace
 
-int32_t mla_wide_head_groups(int32_t num_q_heads) {
+int32_t mla_head_groups(int32_t num_q_heads) {
     return (num_q_heads + WideCfg::kHeads - 1) / WideCfg::kHeads;
 }
 
-hipError_t launch_mla_wide(const MfmaParams& p, hipStream_t s) {
+DecodePlan plan_mla(int32_t batch, int32_t num_q_heads, int32_t head_dim_v, int32_t max_seq_len_kv) {
+    DecodePlan pl{};
+    const int64_t groups64 = (num_q_heads + 63) / 64;   // the scale the threshold below was set at
+    auto nsplits = [&](int sp) { return (int64_t)(max_seq_len_kv + sp - 1) / sp; };
+    // A split's partial state is Hq x Dv fp32 (256 KiB at 128 x 512): long splits keep that
+    // traffic small; shorten them only while the grid would leave compute units idle.  With
+    // one workgroup per CU the time also depends on how the units pack onto the CUs: on 64
+    // sequences of 2K-8K keys (splits of a sequence evenly sized) a sweep of the bf16 kernel
+    // measured 1536 best (131 us; 512: 165, 768: 151, 1024: 159, 2048: 146).
+    int split = 1536;
+    while (split > 256 && batch * groups64 * nsplits(split) < 512) split /= 2;
+    pl.split_tokens = split;
+    pl.max_splits = (int32_t)(max_seq_len_kv > 0 ? nsplits(split) : 1);
+    if (pl.max_splits <= 1) return pl;
+    const size_t rows = (size_t)batch * num_q_heads * pl.max_splits;
+    pl.ws_o_offset = 0;
+    pl.ws_ml_offset = (rows * head_dim_v * sizeof(float) + 255) & ~(size_t)255;
+    pl.ws_bytes = pl.ws_ml_offset + rows * 2 * sizeof(float);
+    return pl;
+}
+
+hipError_t launch_mla_decode(const MfmaParams& p, hipStream_t s) {
     // ids: (unit / 8, head group, unit % 8) with units = batch * max_splits rounded up to 8
-    const int64_t hgs = mla_wide_head_groups(p.hq);
+    const int64_t hgs = mla_head_groups(p.hq);
     const int64_t units = ((int64_t)p.batch * p.max_splits + 7) / 8 * 8;
     const dim3 grid((unsigned)(hgs * units));
-    if (p.k_new) hipLaunchKernelGGL((mla_wide_kernel<true>), grid, dim3(WideCfg::kThreads), 0, s, p);
-    else hipLaunchKernelGGL((mla_wide_kernel<false>), grid, dim3(WideCfg::kThreads), 0, s, p);
+    if (p.k_scale) hipLaunchKernelGGL((mla_wide_kernel<false, true>), grid, dim3(WideCfg::kThreads), 0, s, p);
+    else if (p.k_new) hipLaunchKernelGGL((mla_wide_kernel<true, false>), grid, dim3(WideCfg::kThreads), 0, s, p);
+    else hipLaunchKernelGGL((mla_wide_kernel<false, false>), grid, dim3(WideCfg::kThreads), 0, s, p);
     return hipGetLastError();
 }
 

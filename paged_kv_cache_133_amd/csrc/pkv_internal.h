@@ -247,13 +247,11 @@ struct MfmaParams {
     void* rope_w;
     int64_t* slots_out;      // [B] or null
 };
-// MLA decode: Dqk = 512 + Dr 64, Dv = 512, bf16.  Returns the launch status.
+// MLA decode: Dqk = 512 + Dr 64, Dv = 512, bf16 queries over the bf16 or the INT8 latent
+// cache; one workgroup per (sequence, split, group of 128 heads).  Returns the launch status.
 DecodePlan plan_mla(int32_t batch, int32_t num_q_heads, int32_t head_dim_v, int32_t max_seq_len_kv);
 int32_t mla_head_groups(int32_t num_q_heads);
 hipError_t launch_mla_decode(const MfmaParams& p, hipStream_t s);
-// The bf16 MLA decode with all 128 heads of a unit in one workgroup (same plan).
-hipError_t launch_mla_wide(const MfmaParams& p, hipStream_t s);
-int32_t mla_wide_head_groups(int32_t num_q_heads);
 // Varlen chunk: head_dim 64 or 128, bf16.
 hipError_t launch_varlen(const MfmaParams& p, int head_dim, hipStream_t s);
 int32_t varlen_tokens_per_block(int32_t group);
