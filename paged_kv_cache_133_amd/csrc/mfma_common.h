@@ -126,7 +126,8 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
 }
 
-// 8 int8 codes (two dwords) as 8 bf16 (exact: |code| <= 127).
+// 8 int8 codes (two dwords) as 8 bf16 (exact: |code| <= 127).  (A byte-permute form, fp32
+// 2^23 + (c + 128) minus 2^23 + 128, takes more instructions and measured slower.)
 __device__ __forceinline__ u32x4 codes8_to_bf16(uint32_t x, uint32_t y) {
     u32x4 r;
 #pragma unroll

@@ -27,8 +27,8 @@
 //  * INT8 cache (codes with one fp32 scale per key for the nope part and one for the rope
 //    part): the codes reach one of two code stages by direct loads three tiles ahead; each
 //    wave converts the keys it loaded itself into one of three bf16 stages (the codes
-//    exactly, the scales beside them) two tiles ahead, among the value products, so that
-//    the tile's one barrier publishes them.  A key's score weighs the nope and rope sums by
+//    exactly, the scales beside them) one tile ahead, just before the tile's one barrier,
+//    which publishes them.  A key's score weighs the nope and rope sums by
 //    their own scales, s = s_nope (q . nope) + s_rope (q . rope), in one accumulator: the
 //    nope products, times s_nope / s_rope', then the rope products added, times s_rope'
 //    (s_rope' = s_rope, raised to s_nope 2^-60 and to 2^-126 where it is smaller: the ratio
@@ -360,6 +360,16 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
         }
     };
 
+    // All reads first: a store to the bf16 stage may alias a later read as far as the
+    // compiler knows, so interleaved, every read would wait out the one before it.
+    auto convert = [&](int u) {
+        u32x2 c[10];
+#pragma unroll
+        for (int j = 0; j < 10; ++j) c[j] = conv_read(u, j);
+#pragma unroll
+        for (int j = 0; j < 10; ++j) conv_write(u, j, c[j]);
+    };
+
     // Per-lane LDS offsets inside a stage.  K read of k-step s < 32: nope row of key l % 32,
     // bytes 32 s + 16 h; rope k-step 32 + i: rope chunk 2 i + h of that key.  Transposing
     // read of V (k-step ks, read rd, value tile ct): lane (G = lane / 16, a = lane / 4 % 4,
@@ -393,20 +403,14 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
 #pragma unroll
     for (int ct = 0; ct < 16; ++ct) oacc[ct] = f32x16{};
 
-    // Prologue.  bf16: tiles 0..2 issued, tile 0 in LDS.  INT8: tiles 0 and 1 loaded and
-    // converted, tile 2 issued (into the code stage of tile 0, read above).  Then S^T(0).
+    // Prologue.  bf16: tiles 0..2 issued, tile 0 in LDS.  INT8: tiles 0..2 issued, tile 0
+    // converted (tile 2 into its code stage once read).  Then S^T(0).
     if constexpr (I8) {
         feed(0);
         feed(1);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            if (u == 0 && ntiles > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(W8::kDma));
-            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-            if (u < ntiles) {
-#pragma unroll
-                for (int j = 0; j < 10; ++j) conv_write(u, j, conv_read(u, j));
-            }
-        }
+        if (ntiles > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(W8::kDma));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        convert(0);
         feed(2);
     } else {
 #pragma unroll
@@ -483,15 +487,26 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
             st.m = mnew;
         }
         // Tile t + 3 goes into the stage of tile t - 1 (INT8: the code stage of tile t + 1,
-        // which this wave has converted) once the barrier has freed it; the loads of a fast
-        // tile are spread over the products below (one per product), others are issued here
-        // at once.  INT8: the barrier also publishes the bf16 stage of tile t + 1, converted
-        // during tile t - 1.
+        // converted just before) once the barrier has freed it; the loads of a fast tile are
+        // spread over the products below (one per product), others are issued here at once.
+        // INT8: this wave converts its keys of tile t + 1 into bf16 stage (t + 1) % 3 here,
+        // where no operand reads compete for LDS (among the products, the conversion's
+        // stores cost three times as much), and the barrier publishes it; the wait lets the
+        // codes of tile t + 2, and a table chunk issued after them, stay in flight.
         const int u = t + 3;
         bool spread = false;
         uint64_t slot_u = 0;
         if (t + 1 < ntiles) {
-            if constexpr (!I8) wait_tile<C::kDma>(min(ntiles - 2 - t, kStages - 3));
+            if constexpr (I8) {
+                const int v = t + 2;
+                if (v >= ntiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+                else if (v % kChunkTiles == 0 && tab.exists(v / kChunkTiles + 1))
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(W8::kDma + 4));
+                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(W8::kDma));
+                convert(t + 1);
+            } else {
+                wait_tile<C::kDma>(min(ntiles - 2 - t, kStages - 3));
+            }
             block_sync();
             if (u < ntiles) {
                 if constexpr (!I8) next_chunk(u);
@@ -543,20 +558,17 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
                     pw[i >> 3][(i & 7) >> 1] = pack_bf16(e0, e1);
                 }
             }
-            if (I8 && spread && s >= 8 && s < 13) code_load(u, slot_u, s - 8);
             __builtin_amdgcn_sched_barrier(0);
         }
         // O^T += V^T . P^T(t): 32 products, the transposing reads kVRing products ahead.
         // INT8, among them: the scores of tile t + 1 completed (products 0-14: the nope sums
-        // times s_nope / s_rope', the four rope products, times s_rope'), then this wave's
-        // conversion of tile t + 2 (16-27).
+        // times s_nope / s_rope', the four rope products, times s_rope').
         bf16x8_t vring[C::kVRing];
 #pragma unroll
         for (int m = 0; m < C::kVRing; ++m) vring[m] = v_operand(vst, m);
         __builtin_amdgcn_sched_barrier(0);
         f32x4 ksc[2];
         bf16x8_t rk[2];
-        u32x2 craw[2];
 #pragma unroll
         for (int m = 0; m < 32; ++m) {
             const bf16x8_t va = vring[m % C::kVRing];
@@ -585,17 +597,10 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
                         const int i = m <= 2 ? m - 1 : (m - 3) / 2 + 2;   // rope k-step 32 + i
                         rk[i & 1] = k_operand(kst, 32 + i);
                     }
-                } else if (t + 2 < ntiles) {
-                    const int j = m - 16;     // piece j read at product 16 + j, converted at 18 + j
-                    if (j == 0) {             // this wave's codes of tile t + 2 (tile t + 3's may fly)
-                        if (t + 3 < ntiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(W8::kDma));
-                        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-                    }
-                    if (j >= 2 && j < 12) conv_write(t + 2, j - 2, craw[j & 1]);
-                    if (j < 10) craw[j & 1] = conv_read(t + 2, j);
                 }
-                // after the wait above, so that the wait does not cover these loads
-                if (m == 28 && u < ntiles) next_chunk(u);
+                // the codes of tile t + 3 (products 16-20), then a table chunk (21)
+                if (spread && m >= 16 && m < 21) code_load(u, slot_u, m - 16);
+                if (m == 21 && u < ntiles) next_chunk(u);
             } else {
                 uint8_t* ustage = stage_of(u);
                 if (spread && m < 8)
