@@ -105,7 +105,7 @@ def _check(c, out, lse, kdeq, rdeq, lens_all, rows=None):
     return err
 
 
-@pytest.mark.parametrize("hq,bs", [(128, 16), (64, 4), (16, 128), (32, 8)])
+@pytest.mark.parametrize("hq,bs", [(128, 16), (64, 4), (16, 128), (32, 8), (192, 32)])
 def test_int8_mla_decode_parity(hq, bs):
     L = [0, 1, 31, 32, 33, bs - 1 if bs > 1 else 2, 700, 2600]
     say(f"int8 mla decode hq={hq} bs={bs} L={L}")

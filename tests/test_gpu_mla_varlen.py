@@ -14,7 +14,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.mark.parametrize("hq,bs", [(128, 128), (64, 16), (32, 1), (96, 64), (16, 32)])
+# 160 and 256 heads: two workgroups (head groups of 128) per (sequence, split)
+@pytest.mark.parametrize("hq,bs", [(128, 128), (64, 16), (32, 1), (96, 64), (16, 32), (160, 16), (256, 64)])
 def test_mla_decode_parity_small(hq, bs):
     w = wl.custom(mode="mla", batch=5, num_q_heads=hq, num_kv_heads=1, head_dim=512,
                   head_dim_rope=64, block_size=bs, dtype="bf16")
