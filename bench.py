@@ -91,7 +91,8 @@ def parse():
                          "sequence reaches during the run (the recorded step's length bound)")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="only measure the practical HBM read ceiling (pkv_stream_read over "
-                         "0.7-4 GB at several grid sizes) and a device copy")
+                         "0.7-4 GB at several grid sizes), a device copy, and the read floor "
+                         "of the headline decode's access pattern (pkv_gather_read)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for counter scaling)")
     return ap.parse_args()
@@ -247,12 +248,55 @@ def read_ceiling(launches: int = 20):
     b.record()
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / launches
+    del src, dst
     best = max(rows, key=lambda r: r["GB_per_s"])
     print(json.dumps({"read_ceiling_GB_per_s": best["GB_per_s"], "best": best,
                       "frac_of_8TBps": round(best["GB_per_s"] / PEAK_HBM_GBPS, 4),
                       "copy_1GiB": {"us_per_copy": round(us, 2),
                                     "GB_per_s_read_plus_write": round(2 * n / (us * 1e-6) / 1e9, 1)},
+                      "gather": gather_floor(launches=launches),
                       "runs": rows}), flush=True)
+
+
+def gather_floor(launches: int = 20, replicas: int = 3):
+    """The read floor of the headline decode's own access pattern: pkv_gather_read over the
+    llama7b_mha_bf16 case (seed 0; the same table, lengths after the step and pools, rotated
+    over `replicas` copies) reads exactly the K/V rows the decode reads, with no arithmetic.
+    Slices of 512 B (the rows of the pair of heads one decode workgroup reads) and splits of
+    256 rows are the decode's own pattern; other slices and splits show how much of the floor
+    is the pattern's."""
+    import torch
+    from paged_kv_cache_133_amd import _lib
+    from paged_kv_cache_133_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    w = wl.LLAMA7B
+    case = wl.make_workload_case(w, seed=0, device=dev)
+    table = case.table_tensor(dev)
+    la = case.lens_after_tensor(dev)
+    pools = [(case.cache_k, case.cache_v)] + [(case.cache_k.clone(), case.cache_v.clone())
+                                              for _ in range(replicas - 1)]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    row = w.num_kv_heads * w.head_dim * case.cache_k.element_size()
+    kv_bytes = int(la.sum().item()) * row * 2
+    runs = []
+    for slice_bytes, split in ((512, 256), (256, 256), (256, 128), (256, 512), (1024, 128),
+                               (2048, 64), (row, 16)):
+        calls = [_lib.prepare_gather_read(k, v, table, la, case.max_len_after, slice_bytes, split,
+                                          sink) for k, v in pools]
+        for i in range(2 * replicas):
+            calls[i % replicas]()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(launches):
+            calls[i % replicas]()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / launches
+        runs.append({"slice_bytes": slice_bytes, "split_tokens": split, "us_per_launch": round(us, 2),
+                     "GB_per_s": round(kv_bytes / (us * 1e-6) / 1e9, 1)})
+    return {"workload": w.name, "kv_read_bytes": kv_bytes, "decode_pattern": runs[0],
+            "best": max(runs, key=lambda r: r["GB_per_s"]), "runs": runs}
 
 
 def cpu_baseline(case, kv_bytes, min_seconds):

@@ -582,6 +582,27 @@ PKV_API int pkv_stream_read(const void* src, int64_t bytes, uint32_t* sink, int3
                             void* stream);
 
 /*
+ * Measurement aid (not part of the decode path): the read floor of a paged decode's own
+ * access pattern.  Reads, with no arithmetic, the bytes a decode over the same arguments
+ * reads: rows p in [0, min(seq_lens[b], max_seq_len_kv)) of sequence b from both caches,
+ * row = block_table[b][p / block_size] * block_size + p % block_size ("Paged KV Cache and
+ * Packed Sequence", 2.2), one workgroup per (slice of slice_bytes of a row, sequence, split
+ * of split_tokens rows), and writes (almost never) one word to `sink`.  With slice_bytes =
+ * one head's row and split_tokens = the decode's split it is the decode's own pattern.
+ *   k_cache, v_cache [num_blocks][block_size][row_bytes] (16-byte aligned), block_table
+ *   [batch][max_blocks_per_seq] int32, seq_lens [batch] int32, sink [1] uint32, all device.
+ *   row_bytes a multiple of slice_bytes, slice_bytes a positive multiple of 16, block_size
+ *   a power of two in [1, 256], split_tokens in [1, 1024], max_seq_len_kv in
+ *   [0, max_blocks_per_seq * block_size]; lengths are clamped to it and table entries to
+ *   [0, num_blocks).  batch 0 or max_seq_len_kv 0: PKV_OK, nothing enqueued.
+ */
+PKV_API int pkv_gather_read(const void* k_cache, const void* v_cache, const int32_t* block_table,
+                            const int32_t* seq_lens, int32_t batch, int32_t max_blocks_per_seq,
+                            int32_t max_seq_len_kv, int32_t block_size, int64_t num_blocks,
+                            int32_t row_bytes, int32_t slice_bytes, int32_t split_tokens,
+                            uint32_t* sink, void* stream);
+
+/*
  * Copies whole blocks inside one cache array: for i < num_pairs, block pairs[2i] of
  * pool [num_blocks][block_bytes] is copied to block pairs[2i+1] (the copy-on-write pairs
  * of pkv_bm_append; call once per cache array: K, V, and the scale arrays of an INT8

@@ -40,7 +40,8 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_runner_capture_end", "pkv_runner_graph", "pkv_runner_host_buffer",
            "pkv_runner_launch", "pkv_upload_kernel", "pkv_decode_mtp_workspace_size", "pkv_paged_attn_decode_mtp",
            "pkv_kv_cache_write_int8_mla", "pkv_paged_attn_decode_mla_int8", "pkv_stream_read",
-           "pkv_paged_attn_decode_int8_append", "pkv_paged_attn_decode_mla_append")
+           "pkv_paged_attn_decode_int8_append", "pkv_paged_attn_decode_mla_append",
+           "pkv_gather_read")
 
 
 class PagedKVError(RuntimeError):
@@ -100,6 +101,8 @@ def lib() -> ctypes.CDLL:
                                                i32, i32, i32, i64, f32, i32, i32, p, sz, p]
     L.pkv_stream_read.restype = ctypes.c_int
     L.pkv_stream_read.argtypes = [p, i64, p, i32, p]
+    L.pkv_gather_read.restype = ctypes.c_int
+    L.pkv_gather_read.argtypes = [p, p, p, p, i32, i32, i32, i32, i64, i32, i32, i32, p, p]
     L.pkv_paged_attn_decode_append_noalloc.restype = ctypes.c_int
     L.pkv_paged_attn_decode_append_noalloc.argtypes = [p, p, p, p, p, p, p, p, p, p, i32, i32,
                                                        i32, i32, i32, i32, i32, i64, f32, i32, p]
@@ -603,6 +606,21 @@ def prepare_stream_read(src: torch.Tensor, sink: torch.Tensor, grid: int):
     _dev(src, sink)
     args = (_ptr(src), src.numel() * src.element_size(), _ptr(sink), int(grid), _stream(src.device))
     return PreparedCall(lib().pkv_stream_read, args, (src, sink))
+
+
+def prepare_gather_read(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                        seq_lens: torch.Tensor, max_seq_len_kv: int, slice_bytes: int,
+                        split_tokens: int, sink: torch.Tensor):
+    """pkv_gather_read: the K/V rows a decode over these arguments reads, read with no
+    arithmetic (a measurement aid: the read floor of the decode's access pattern).  Caches
+    [nb, bs, ...] contiguous; a row is everything after the block-size dimension."""
+    _dev(k_cache, v_cache, block_table, seq_lens, sink)
+    nb, bs = k_cache.shape[:2]
+    row_bytes = k_cache[0, 0].numel() * k_cache.element_size()
+    args = (_ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+            block_table.shape[0], block_table.shape[1], int(max_seq_len_kv), bs, nb, row_bytes,
+            int(slice_bytes), int(split_tokens), _ptr(sink), _stream(k_cache.device))
+    return PreparedCall(lib().pkv_gather_read, args, (k_cache, v_cache, block_table, seq_lens, sink))
 
 
 def prepare_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,

@@ -116,6 +116,45 @@ int pkv_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t grid
     return hip_status(pkv::launch_stream_read(src, bytes, sink, grid, (hipStream_t)stream), "stream_read launch");
 }
 
+int pkv_gather_read(const void* k_cache, const void* v_cache, const int32_t* block_table,
+                    const int32_t* seq_lens, int32_t batch, int32_t max_blocks_per_seq,
+                    int32_t max_seq_len_kv, int32_t block_size, int64_t num_blocks,
+                    int32_t row_bytes, int32_t slice_bytes, int32_t split_tokens,
+                    uint32_t* sink, void* stream) {
+    if (batch < 0 || max_blocks_per_seq < 1 || num_blocks < 1)
+        return fail(PKV_ERR_SHAPE, "gather_read: batch >= 0, max_blocks_per_seq >= 1, num_blocks >= 1");
+    if (!pow2_in(block_size, 1, 256))
+        return fail(PKV_ERR_UNSUPPORTED, "gather_read: block_size must be a power of two in [1, 256]");
+    if (slice_bytes < 16 || slice_bytes % 16 || row_bytes < slice_bytes || row_bytes % slice_bytes)
+        return fail(PKV_ERR_SHAPE, "gather_read: slice_bytes a positive multiple of 16 dividing row_bytes");
+    if (split_tokens < 1 || split_tokens > 1024)
+        return fail(PKV_ERR_SHAPE, "gather_read: split_tokens must be in [1, 1024]");
+    if (max_seq_len_kv < 0 || (int64_t)max_seq_len_kv > (int64_t)max_blocks_per_seq * block_size)
+        return fail(PKV_ERR_SHAPE, "gather_read: max_seq_len_kv must be in [0, max_blocks_per_seq * block_size]");
+    if (num_blocks > INT64_MAX / ((int64_t)block_size * row_bytes))
+        return fail(PKV_ERR_SHAPE, "gather_read: cache size overflows");
+    if (batch == 0 || max_seq_len_kv == 0) return PKV_OK;
+    if (!k_cache || !v_cache || !block_table || !seq_lens || !sink)
+        return fail(PKV_ERR_NULL, "gather_read: NULL pointer argument");
+    if (!aligned16(k_cache) || !aligned16(v_cache) || reinterpret_cast<uintptr_t>(sink) % 4)
+        return fail(PKV_ERR_ALIGN, "gather_read: caches must be 16-byte and sink 4-byte aligned");
+    pkv::GatherReadParams p{};
+    p.k = static_cast<const uint8_t*>(k_cache);
+    p.v = static_cast<const uint8_t*>(v_cache);
+    p.table = block_table;
+    p.seq_lens = seq_lens;
+    p.sink = sink;
+    p.num_blocks = num_blocks;
+    p.batch = batch;
+    p.mbs = max_blocks_per_seq;
+    p.bs_log2 = log2i(block_size);
+    p.len_cap = max_seq_len_kv;
+    p.row_bytes = row_bytes;
+    p.slice_bytes = slice_bytes;
+    p.split_tokens = split_tokens;
+    return hip_status(pkv::launch_gather_read(p, (hipStream_t)stream), "gather_read launch");
+}
+
 int pkv_kv_cache_copy_blocks(void* pool, int64_t block_bytes, int64_t num_blocks,
                              const int64_t* pairs, int32_t num_pairs, void* stream) {
     if (num_pairs < 0 || block_bytes <= 0 || num_blocks <= 0)

@@ -63,6 +63,20 @@ struct CopyBlocksParams {
 };
 hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t s);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, hipStream_t s);
+// The decode's K/V reads without arithmetic: one workgroup per (slice of slice_bytes of a
+// row, sequence, split of split_tokens rows); lengths clamped to [0, len_cap], table entries
+// to [0, num_blocks).  split_tokens in [1, 1024], slice_bytes a multiple of 16 dividing
+// row_bytes, len_cap <= mbs * 2^bs_log2.
+struct GatherReadParams {
+    const uint8_t* k;
+    const uint8_t* v;
+    const int32_t* table;      // [batch][mbs]
+    const int32_t* seq_lens;   // [batch]
+    uint32_t* sink;
+    int64_t num_blocks;
+    int32_t batch, mbs, bs_log2, len_cap, row_bytes, slice_bytes, split_tokens;
+};
+hipError_t launch_gather_read(const GatherReadParams& p, hipStream_t s);
 // bytes (a multiple of 4; both ends 16-byte aligned) from pinned host memory, addressed by
 // its device view (hipHostGetDevicePointer), into dst, by a kernel (so that a graph can
 // record it as a kernel node).

@@ -182,6 +182,52 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
     if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
+// Measurement aid: the read floor of a paged decode's own access pattern.  Workgroup
+// (slice, sequence, split) reads rows [split * split_tokens, +split_tokens) of both caches,
+// clamped to the sequence's length, through the block table (row = entry * bs + offset),
+// slice_bytes of each row; the split's table entries are staged in LDS first.  Eight
+// 16-byte loads of each cache per thread are in flight between uses, as in the decode.
+constexpr int kGatherEntries = 1040;   // table entries of one split: split_tokens / bs + 2
+__global__ __launch_bounds__(256) void gather_read_kernel(GatherReadParams p) {
+    constexpr int U = 8;
+    __shared__ int32_t tab[kGatherEntries];
+    const int nslices = p.row_bytes / p.slice_bytes;
+    const int id = blockIdx.x;
+    const int slice = id % nslices;
+    const int b = (id / nslices) % p.batch;
+    const int split = id / (nslices * p.batch);
+    const int L = min(max(p.seq_lens[b], 0), p.len_cap);
+    const int t0 = split * p.split_tokens;
+    if (t0 >= L) return;
+    const int t1 = min(L, t0 + p.split_tokens);
+    const int blk0 = t0 >> p.bs_log2;
+    const int nblk = ((t1 - 1) >> p.bs_log2) - blk0 + 1;
+    const int32_t last = (int32_t)(p.num_blocks - 1);
+    for (int i = threadIdx.x; i < nblk; i += blockDim.x)
+        tab[i] = min(max(p.table[(int64_t)b * p.mbs + blk0 + i], 0), last);
+    __syncthreads();
+    const int chunks = p.slice_bytes / 16;
+    const int n = (t1 - t0) * chunks;
+    const int64_t col = (int64_t)slice * p.slice_bytes;
+    const int bs_mask = (1 << p.bs_log2) - 1;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int e = threadIdx.x; e < n; e += (int)blockDim.x * U) {
+        u32x4 kr[U], vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int eu = min(e + (int)blockDim.x * u, n - 1);
+            const int tok = t0 + eu / chunks;
+            const int64_t row = ((int64_t)tab[(tok >> p.bs_log2) - blk0] << p.bs_log2) | (tok & bs_mask);
+            const int64_t off = row * p.row_bytes + col + (int64_t)(eu % chunks) * 16;
+            kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.k + off));
+            vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.v + off));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= kr[u] ^ vr[u];
+    }
+    if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u) p.sink[0] = acc.z;
+}
+
 // Copy of n4 int32 words from pinned host memory (its device view) into device memory: one
 // 16-byte word per thread where the two ends allow it, 4-byte words for the tail.
 __global__ __launch_bounds__(256) void host_copy_kernel(const uint32_t* __restrict__ src,
@@ -210,6 +256,15 @@ hipError_t launch_host_copy(void* dst, const void* src_dev_view, int64_t bytes, 
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, hipStream_t s) {
     hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(256), 0, s,
                        static_cast<const u32x4*>(src), bytes / 16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_read(const GatherReadParams& p, hipStream_t s) {
+    const int64_t nsplit = ((int64_t)p.len_cap + p.split_tokens - 1) / p.split_tokens;
+    const int64_t grid = (int64_t)(p.row_bytes / p.slice_bytes) * p.batch * nsplit;
+    if (grid <= 0) return hipSuccess;
+    if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(gather_read_kernel, dim3((unsigned)grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -428,3 +428,30 @@ def test_int8_mla_forms_reject_bad_arguments():
     assert wr(rc=FAKE) == -2                    # nope and rope codes must differ
     assert wr(ns=ctypes.c_void_p(0x100004)) == -5
     assert wr(bs=3) == -4
+
+
+def test_gather_read_rejects_bad_arguments():
+    lib = _lib().lib()
+    g = lib.pkv_gather_read
+
+    def call(**kw):
+        a = dict(k=FAKE, v=FAKE, table=FAKE, lens=FAKE, B=2, mbs=4, maxlen=64, bs=16, nb=32,
+                 row=256, slice=256, split=256, sink=FAKE)
+        a.update(kw)
+        return g(a["k"], a["v"], a["table"], a["lens"], a["B"], a["mbs"], a["maxlen"], a["bs"],
+                 a["nb"], a["row"], a["slice"], a["split"], a["sink"], None)
+
+    assert call(B=-1) == -2
+    assert call(mbs=0) == -2
+    assert call(nb=0) == -2
+    assert call(bs=12) == -4
+    assert call(slice=8) == -2                   # not a multiple of 16
+    assert call(row=384, slice=256) == -2        # does not divide the row
+    assert call(split=0) == -2
+    assert call(split=2048) == -2
+    assert call(maxlen=65) == -2                 # beyond max_blocks_per_seq * block_size
+    assert call(B=0) == 0 and call(maxlen=0) == 0
+    assert call(k=None) == -1
+    assert call(sink=None) == -1
+    assert call(v=ctypes.c_void_p(0x100008)) == -5
+    assert b"gather_read" in lib.pkv_last_error()
