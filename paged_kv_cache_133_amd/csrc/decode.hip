@@ -416,10 +416,11 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t head_dim_v, int32_t max_seq_len_kv, bool byte_rows, int32_t qn) {
     DecodePlan pl{};
     const int G = num_q_heads / num_kv_heads;
-    // Larger groups carry more partial state per split: use longer splits for them (and
-    // twice as long over one-byte INT8 rows, for the same bytes per workgroup).
+    // Larger groups carry more partial state per split: use longer splits for them.  Over
+    // one-byte INT8 rows: 256 keys when a workgroup reads a pair of kv heads' contiguous rows
+    // (one query head per kv head), else twice the bf16 split (the same bytes per workgroup).
     int split = G <= 2 ? 256 : G <= 4 ? 512 : 1024;
-    if (byte_rows) split *= 2;
+    if (byte_rows) split = int8_head_group(G, num_kv_heads) > 1 ? 256 : split * 2;
     const int64_t pairs = (int64_t)batch * num_kv_heads;
     auto nsplits = [&](int sp) { return (int64_t)(max_seq_len_kv + sp - 1) / sp; };
     // Keep at least ~4 workgroups per compute unit in flight on long sequences.

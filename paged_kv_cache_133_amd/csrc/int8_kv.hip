@@ -19,7 +19,9 @@
 //    tokens their K (V) scales are NJ adjacent floats of one block and head: one load per
 //    row, issued with the code loads (scales laid out per (token, head) cost a sixth of
 //    the kernel's time: every token's scale was a separate access);
-//  * splits are twice as long as for bf16 rows, for the same bytes per workgroup.
+//  * with one query head per kv head a workgroup takes a pair of adjacent kv heads, whose
+//    rows of a token are one contiguous piece, over splits of 256 keys; otherwise splits
+//    are twice as long as for bf16 rows, for the same bytes per workgroup.
 // Keys below the window start are not loaded; the new token is written beforehand by the
 // quantizing write (the attention reads the same codes later steps will).
 #include "pkv_device.h"
@@ -100,26 +102,35 @@ __global__ __launch_bounds__(256) void kv_write_int8_kernel(QuantWriteParams p) 
 // bit for bit) and stores the codes and scales at its slot (reported in slots_out) before
 // its loop, which then reads it back like any cached token.  A row longer than the length
 // bound writes nothing (slot -1) and attends to its first len_cap cached keys.
-template <int D, int GP, bool APPEND>
+// HP adjacent kv heads per workgroup (HP > 1 only with one query head per kv head): a
+// token's HP head rows are one contiguous piece of HP * D bytes, read by HP * D / 16 lanes;
+// each row of lanes still takes NJ consecutive tokens, so a step is kStepTokensI8 / HP
+// tokens and the loads in flight per lane stay the same.
+template <int D, int GP, bool APPEND, int HP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GP == 1 ? 4 : 2)))
 void decode_int8_kernel(DecodeParams p) {
+    static_assert(HP == 1 || GP == 1, "head groups only with one query head per kv head");
     constexpr int EPL = 16;                           // codes per lane per load
-    constexpr int LPT = D / EPL;                      // lanes per token row
-    constexpr int TPW = 64 / LPT;                     // tokens per wave load
-    constexpr int NJ = kStepTokensI8 / TPW;           // loads per step (each of K, V)
+    constexpr int LPT = D / EPL;                      // lanes per head row
+    constexpr int LPR = LPT * HP;                     // lanes per token (HP head rows)
+    constexpr int NJ = kStepTokensI8 / (64 / LPT);    // loads per step (each of K, V)
+    constexpr int STEP = kStepTokensI8 / HP;          // tokens per step
     static_assert(NJ == 2 || NJ == 4, "a row of lanes takes 2 or 4 tokens per step");
-    __shared__ float sm_m[kWavesI8][GP];
-    __shared__ float sm_l[kWavesI8][GP];
-    __shared__ float sm_o[kWavesI8][GP][D];
+    static_assert(LPR <= 64 && (64 / LPR) * NJ == STEP, "bad head grouping");
+    __shared__ float sm_m[kWavesI8][GP * HP];
+    __shared__ float sm_l[kWavesI8][GP * HP];
+    __shared__ float sm_o[kWavesI8][GP * HP][D];
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int row = lane / LPT;
+    const int row = lane / LPR;
+    const int hs = (lane / LPT) % HP;   // which head of the workgroup's HP
     const int col = lane % LPT;
 
     int id = blockIdx.x;
-    const int kvh = id % p.hkv;
-    id /= p.hkv;
+    const int kvp = id % (p.hkv / HP);
+    const int kvh = kvp * HP + hs;
+    id /= p.hkv / HP;
     const int b = id % p.batch;
     const int split = id / p.batch;
     const int L = min(p.seq_lens[b], p.len_cap);
@@ -138,12 +149,12 @@ void decode_int8_kernel(DecodeParams p) {
     const int t0 = ksa + split * split_keys;
     const bool app = APPEND && p.seq_lens[b] <= p.len_cap;
     const int pos_new = app ? L - 1 : -1;
-    if (APPEND && !app && split == 0 && p.slots_out && kvh == 0 && threadIdx.x == 0)
+    if (APPEND && !app && split == 0 && p.slots_out && kvp == 0 && threadIdx.x == 0)
         p.slots_out[b] = -1;
     if (L <= 0) {   // no visible key: output 0, lse -inf
         if (split == 0) {
-            for (int i = threadIdx.x; i < p.group * D; i += blockDim.x) {
-                const int h = kvh * p.group + i / D;
+            for (int i = threadIdx.x; i < HP * p.group * D; i += blockDim.x) {
+                const int h = kvp * HP * p.group + i / D;
                 reinterpret_cast<uint16_t*>(p.out)[((int64_t)b * p.hq + h) * D + i % D] = 0;
                 if (p.lse && i % D == 0) p.lse[(int64_t)b * p.hq + h] = -INFINITY;
             }
@@ -183,13 +194,17 @@ void decode_int8_kernel(DecodeParams p) {
     const int64_t slot_stride = (int64_t)p.hkv * D;               // bytes per cache row
     const int64_t head_off = (int64_t)kvh * D + col * EPL;
     // Append: the wave whose keys hold the new token quantizes its K and V rows (two values
-    // per lane), stores the codes and scales at its slot and waits for those stores; its loop
-    // then reads the token back like any cached one.  No other wave touches that token.
+    // per lane; the HP heads' rows one after another), stores the codes and scales at its
+    // slot and waits for those stores; its loop then reads the token back like any cached
+    // one.  No other wave touches that token.
     if (APPEND && pos_new >= w0 && pos_new < w1) {
         const int32_t phys = min(max(trow[pos_new >> p.bs_log2], 0), last_block);
         const int64_t slot = ((int64_t)phys << p.bs_log2) | (pos_new & bs_mask);
-        const int64_t sc_idx = (((int64_t)phys * p.hkv + kvh) << p.bs_log2) | (pos_new & bs_mask);
-        const int64_t src_off = (((int64_t)b * p.hkv + kvh) * D + 2 * (lane % (D / 2))) * 2;
+#pragma unroll
+        for (int hh = 0; hh < HP; ++hh) {
+        const int kvw = kvp * HP + hh;   // the head whose row is written
+        const int64_t sc_idx = (((int64_t)phys * p.hkv + kvw) << p.bs_log2) | (pos_new & bs_mask);
+        const int64_t src_off = (((int64_t)b * p.hkv + kvw) * D + 2 * (lane % (D / 2))) * 2;
 #pragma unroll
         for (int which = 0; which < 2; ++which) {
             const uint32_t pair = *reinterpret_cast<const uint32_t*>(
@@ -207,12 +222,13 @@ void decode_int8_kernel(DecodeParams p) {
             }
             if (lane < D / 2) {
                 uint8_t* dst = reinterpret_cast<uint8_t*>(which ? p.v_cache_w : p.k_cache_w) +
-                               slot * slot_stride + (int64_t)kvh * D + 2 * lane;
+                               slot * slot_stride + (int64_t)kvw * D + 2 * lane;
                 *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
                 if (lane == 0) (which ? p.v_scale_w : p.k_scale_w)[sc_idx] = sc;
             }
         }
-        if (p.slots_out && kvh == 0 && lane == 0) p.slots_out[b] = slot;
+        }
+        if (p.slots_out && kvp == 0 && lane == 0) p.slots_out[b] = slot;
         __threadfence_block();   // the stores complete before this wave's loads of the token
     }
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k_cache) + head_off;
@@ -221,13 +237,13 @@ void decode_int8_kernel(DecodeParams p) {
     // Table entries of the blocks a step touches: lane i holds entry (first block + i).
     auto load_table = [&](int base) -> int32_t {
         const int blk0 = base >> p.bs_log2;
-        const int nblk = ((min(base + kStepTokensI8, w1) - 1) >> p.bs_log2) - blk0 + 1;
+        const int nblk = ((min(base + STEP, w1) - 1) >> p.bs_log2) - blk0 + 1;
         return (base < w1 && lane < nblk) ? trow[blk0 + lane] : 0;
     };
 
     int32_t tbl = load_table(w0);
-    for (int base = w0; base < w1; base += kStepTokensI8) {
-        const int32_t tbl_next = load_table(base + kStepTokensI8);
+    for (int base = w0; base < w1; base += STEP) {
+        const int32_t tbl_next = load_table(base + STEP);
         const int blk0 = base >> p.bs_log2;
         u32x4 kr[NJ], vr[NJ];
         float ksc[NJ], vsc[NJ];
@@ -327,36 +343,37 @@ void decode_int8_kernel(DecodeParams p) {
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
         if (g >= p.group) break;
-        const float mw = cross_row_max<LPT>(m[g]);
+        const float mw = cross_row_max<LPR>(m[g]);
         const float f = (m[g] == -INFINITY) ? 0.0f : fast_exp2(m[g] - mw);
-        const float lw = cross_row_sum<LPT>(l[g] * f);
+        const float lw = cross_row_sum<LPR>(l[g] * f);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[g][e] = cross_row_sum<LPT>(o[g][e] * f);
+        for (int e = 0; e < EPL; ++e) o[g][e] = cross_row_sum<LPR>(o[g][e] * f);
         if (row == 0) {
+            const int gi = g * HP + hs;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) sm_o[wave][g][col * EPL + e] = o[g][e];
+            for (int e = 0; e < EPL; ++e) sm_o[wave][gi][col * EPL + e] = o[g][e];
             if (col == 0) {
-                sm_m[wave][g] = mw;
-                sm_l[wave][g] = lw;
+                sm_m[wave][gi] = mw;
+                sm_l[wave][gi] = lw;
             }
         }
     }
     __syncthreads();
 
-    for (int i = threadIdx.x; i < p.group * D; i += blockDim.x) {
-        const int g = i / D;
+    for (int i = threadIdx.x; i < HP * p.group * D; i += blockDim.x) {
+        const int gi = i / D;   // g * HP + head of the group
         const int d = i % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWavesI8; ++w) M = fmaxf(M, sm_m[w][g]);
+        for (int w = 0; w < kWavesI8; ++w) M = fmaxf(M, sm_m[w][gi]);
         float acc = 0.0f, lsum = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWavesI8; ++w) {
-            const float f = (sm_m[w][g] == -INFINITY) ? 0.0f : fast_exp2(sm_m[w][g] - M);
-            acc = fmaf(f, sm_o[w][g][d], acc);
-            lsum = fmaf(f, sm_l[w][g], lsum);
+            const float f = (sm_m[w][gi] == -INFINITY) ? 0.0f : fast_exp2(sm_m[w][gi] - M);
+            acc = fmaf(f, sm_o[w][gi][d], acc);
+            lsum = fmaf(f, sm_l[w][gi], lsum);
         }
-        const int h = kvh * p.group + g;
+        const int h = (kvp * HP + gi % HP) * p.group + gi / HP;
         const int64_t bh = (int64_t)b * p.hq + h;
         if (nsplit == 1) {
             reinterpret_cast<uint16_t*>(p.out)[bh * D + d] = f32_to_bf16(acc / lsum);
@@ -373,6 +390,12 @@ void decode_int8_kernel(DecodeParams p) {
 }
 
 }  // namespace
+
+int int8_head_group(int32_t group, int32_t num_kv_heads) {
+    // Pairs: on the Llama-7B INT8 step 72.3 -> 69.6 us with 256-key splits (groups of 4
+    // with 8-token steps: 76; pairs over 128 or 512 keys: 73.8, 71.3).
+    return group == 1 && num_kv_heads % 2 == 0 ? 2 : 1;
+}
 
 hipError_t launch_kv_write_int8(const QuantWriteParams& p, int in_dtype, int head_dim, hipStream_t s) {
     const int rpw = 64 / (head_dim / 8);
@@ -407,14 +430,17 @@ hipError_t launch_kv_write_int8_mla(const QuantWriteParams& p, int in_dtype, hip
 template <int D, bool APPEND>
 void launch_decode_int8_d(const DecodeParams& p, dim3 grid, hipStream_t s) {
     const int gp = p.group <= 1 ? 1 : (p.group <= 2 ? 2 : 4);
-    if (gp == 1) hipLaunchKernelGGL((decode_int8_kernel<D, 1, APPEND>), grid, dim3(256), 0, s, p);
-    else if (gp == 2) hipLaunchKernelGGL((decode_int8_kernel<D, 2, APPEND>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((decode_int8_kernel<D, 4, APPEND>), grid, dim3(256), 0, s, p);
+    const int hp = int8_head_group(p.group, p.hkv);
+    if (hp == 2) hipLaunchKernelGGL((decode_int8_kernel<D, 1, APPEND, 2>), grid, dim3(256), 0, s, p);
+    else if (gp == 1) hipLaunchKernelGGL((decode_int8_kernel<D, 1, APPEND, 1>), grid, dim3(256), 0, s, p);
+    else if (gp == 2) hipLaunchKernelGGL((decode_int8_kernel<D, 2, APPEND, 1>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((decode_int8_kernel<D, 4, APPEND, 1>), grid, dim3(256), 0, s, p);
 }
 
 hipError_t launch_decode_int8(const DecodeParams& p, int head_dim, hipStream_t s) {
     if (p.parts > 0) return launch_gqa_decode_int8(p, head_dim, s);
-    const dim3 grid((unsigned)((int64_t)p.hkv * p.batch * p.max_splits));
+    const int hp = int8_head_group(p.group, p.hkv);
+    const dim3 grid((unsigned)((int64_t)(p.hkv / hp) * p.batch * p.max_splits));
     const bool append = p.k_new != nullptr;
     if (head_dim == 64) {
         if (append) launch_decode_int8_d<64, true>(p, grid, s);

@@ -209,6 +209,10 @@ hipError_t launch_gqa_decode_int8(const DecodeParams& p, int head_dim, hipStream
 // 1..4 query heads per kv head: split-KV with the generic combine; p.parts > 0 (5..16):
 // launch_gqa_decode_int8.
 hipError_t launch_decode_int8(const DecodeParams& p, int head_dim, hipStream_t s);
+// Kv heads per workgroup of the INT8 split-KV decode: with one query head per kv head and
+// an even number of kv heads, a pair of adjacent heads, whose rows of a token are one
+// contiguous piece; else 1.  The plan sizes the splits for it.
+int int8_head_group(int32_t group, int32_t num_kv_heads);
 
 // Merge of split partials (second launch of a split decode).
 struct CombineParams {
