@@ -23,6 +23,10 @@ SHAPES = [
     (32, 2, 128, 256, "bf16"),
     (2, 1, 128, 32, "f32"),
     (16, 16, 64, 64, "bf16"),
+    # one query head per kv head, odd head counts: one kv head per workgroup (even counts
+    # take adjacent pairs)
+    (5, 5, 128, 8, "bf16"),
+    (3, 3, 64, 16, "f32"),
 ]
 
 
@@ -245,7 +249,8 @@ def test_workspace_reuse():
 
 
 @pytest.mark.parametrize("shape", [(32, 32, 128, 16, "bf16"), (8, 2, 64, 1, "f32"),
-                                   (16, 2, 128, 128, "bf16"), (4, 1, 128, 32, "f32")],
+                                   (16, 2, 128, 128, "bf16"), (4, 1, 128, 32, "f32"),
+                                   (6, 6, 128, 1, "f32"), (5, 5, 64, 16, "bf16")],
                          ids=lambda s: "hq%d_hkv%d_d%d_bs%d_%s" % s)
 def test_decode_append_matches_oracle(shape):
     """Write-and-attend in one pass: the written pool, the slots and the outputs equal the
@@ -275,7 +280,8 @@ def test_decode_append_matches_oracle(shape):
 
 
 @pytest.mark.parametrize("shape", [(8, 8, 128, 16, "bf16"), (4, 1, 64, 16, "f32"),
-                                   (16, 2, 128, 16, "bf16"), (16, 2, 128, 2, "bf16")],
+                                   (16, 2, 128, 16, "bf16"), (16, 2, 128, 2, "bf16"),
+                                   (3, 3, 128, 16, "bf16")],
                          ids=lambda s: "hq%d_hkv%d_d%d_bs%d_%s" % s)
 def test_decode_append_overlength_row_writes_nothing(shape):
     """A row whose length exceeds max_seq_len_kv (a broken precondition) appends nothing in

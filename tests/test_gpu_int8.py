@@ -111,6 +111,8 @@ def _check_lse(c, got, ol):
 
 @pytest.mark.parametrize("shape", [(32, 32, 128, 16), (8, 2, 64, 1), (16, 4, 128, 128),
                                    (4, 1, 128, 32), (12, 4, 64, 64),
+                                   # MHA: kv head pairs (even counts) and single heads
+                                   (6, 6, 64, 1), (3, 3, 128, 16),
                                    # 5..16 query heads per kv head: the range-streaming kernel
                                    (32, 4, 128, 16), (64, 4, 64, 16), (40, 8, 128, 8),
                                    (16, 2, 128, 128), (48, 4, 64, 32)],
@@ -258,7 +260,8 @@ def _code_pools(c):
 
 
 @pytest.mark.parametrize("shape", [(32, 32, 128, 16), (8, 2, 64, 1), (16, 4, 128, 128),
-                                   (4, 1, 128, 32), (12, 4, 64, 64)],
+                                   (4, 1, 128, 32), (12, 4, 64, 64), (6, 6, 64, 1),
+                                   (3, 3, 128, 16)],
                          ids=lambda s: "hq%d_hkv%d_d%d_bs%d" % s)
 @pytest.mark.parametrize("window", [0, 100])
 def test_int8_decode_append(shape, window):

@@ -17,7 +17,7 @@ DEV = "cuda:0"
 LENS = [1, 31, 32, 33, 300, 1500, 3000]     # after the step
 # (Hq, Hkv, D, block_size, dtype): VALU (fp32 GQA, bf16 MHA), range streaming, per split
 SHAPES = [(4, 1, 64, 16, "f32"), (8, 8, 128, 16, "bf16"), (32, 4, 128, 16, "bf16"),
-          (32, 4, 128, 2, "bf16"), (48, 4, 64, 128, "bf16")]
+          (32, 4, 128, 2, "bf16"), (48, 4, 64, 128, "bf16"), (5, 5, 64, 16, "bf16")]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "hq%d_hkv%d_d%d_bs%d_%s" % s)
