@@ -435,7 +435,7 @@ DecodePlan plan_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
     }
     if (gqa_mfma_supported(1, G) || qn > 0) {   // the range-streaming layout, if that kernel runs
         const bool compact = byte_rows ? G > 4 : max_seq_len_kv >= kStreamCompactMinKeys;
-        pl.parts = gqa_stream_parts(num_kv_heads, compact);
+        pl.parts = gqa_stream_parts(num_kv_heads, compact, byte_rows);
         const size_t parts = (size_t)num_kv_heads * pl.parts * 2 * G * (qn > 0 ? qn : 1);
         pl.st_o_offset = 0;
         pl.st_ml_offset = align256(parts * head_dim_v * sizeof(float));

@@ -239,13 +239,18 @@ constexpr int kStreamCompactStages = 2;   // compact layout: one tile in flight 
 constexpr int kStreamMaxBatch = 1024;  // sequences whose tile prefix fits LDS
 constexpr int kStreamWgs = 512;        // workgroups per launch (all kv heads): 2 per CU
 constexpr int kStreamWgsCompact = 1024;  // compact layout: 4 per CU, one wave on every SIMD
+// INT8: the wave's instructions (the code conversion above all), not the memory, set the
+// pace, so time falls with the waves per CU: a bf16 buffer of one half tile (K, then V)
+// leaves room for 5 workgroups per CU.
+constexpr int kStreamWgsI8 = 1280;
 
 // LDS of the range kernel.  Default layout (bf16): kStreamStages tile stages, a ring of query
 // rows per stage, the tile prefix and the lengths.  Compact layout (under 40 KiB, for four
 // workgroups per CU; INT8 always, bf16 on long contexts): two stages (INT8: of codes as
 // loaded, K rows of D bytes, V rows, then 1 KiB whose first 256 bytes are the tile's 32 K
-// and 32 V scales, plus one bf16 tile the wave converts them into) and the tile prefix; the
-// query rows stay in registers and the lengths are read from memory.
+// and 32 V scales, plus a bf16 half tile the wave converts the K codes, then the V codes
+// into: under 32 KiB, five workgroups per CU) and the tile prefix; the query rows stay in
+// registers and the lengths are read from memory.
 template <int D, bool I8 = false, bool COMPACT = I8>
 struct StreamCfg {
     using C = GqaCfg<D>;
@@ -257,14 +262,15 @@ struct StreamCfg {
     static constexpr bool kCompact = COMPACT;                     // Q in registers, no lengths
     static_assert(COMPACT || !I8, "INT8 runs in the compact layout");
     static constexpr int kStages = kCompact ? kStreamCompactStages : kStreamStages;
-    static constexpr int kStagesBytes = I8 ? kStages * kCodeStage + C::kStage : kStages * C::kStage;
+    static constexpr int kPerCu = (I8 ? kStreamWgsI8 : kCompact ? kStreamWgsCompact : kStreamWgs) / 256;
+    static constexpr int kStagesBytes = I8 ? kStages * kCodeStage + C::kHalf : kStages * C::kStage;
     static constexpr int kBufOff = kStages * kCodeStage;              // INT8: the bf16 tile
     static constexpr int kQSlot = kCompact ? 0 : 16 * C::kRowBytes;   // one segment's query rows
     static constexpr int kQOff = kStagesBytes;
     static constexpr int kPreOff = kQOff + kStages * kQSlot;          // [batch + 1] first tile
     static constexpr int kLenOff = kPreOff + (kStreamMaxBatch + 1) * 4 + 12;  // [batch] lengths
     static constexpr int kSmem = kLenOff + (kCompact ? 0 : kStreamMaxBatch * 4);
-    static_assert(!kCompact || kSmem <= 40 * 1024, "four workgroups per CU");
+    static_assert(kSmem <= 160 * 1024 / kPerCu, "the workgroups of a CU share its LDS");
     static_assert(2 * kDma < 64, "vmcnt range");
 };
 
@@ -578,6 +584,11 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
     auto tile_of = [&](int t) -> const uint8_t* {
         return I8 ? smem + S::kBufOff : smem + (t % kStg) * C::kStage;
     };
+    // The tile whose V half the value product reads: INT8 converts V into the same buffer
+    // as K, so its "stage" starts one half before the buffer (only its V half is read).
+    auto vtile_of = [&](int t) -> const uint8_t* {
+        return I8 ? smem + S::kBufOff - C::kHalf : smem + (t % kStg) * C::kStage;
+    };
     auto kscale_of = [&](int t) -> const float* {
         return I8 ? reinterpret_cast<const float*>(smem + (t % kStg) * S::kCodeStage + 2 * S::kCodeHalf) : nullptr;
     };
@@ -585,31 +596,27 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         return I8 ? reinterpret_cast<const float*>(smem + (t % kStg) * S::kCodeStage + 2 * S::kCodeHalf) + kKeys
                   : nullptr;
     };
-    auto convert = [&](int t) {
-        const uint8_t* cs = smem + (t % kStg) * S::kCodeStage;
+    // Half h (0: K, 1: V) of tile t's codes into the bf16 half-tile buffer; the V half
+    // overwrites K after the scores have read it (same wave, LDS in order).
+    auto convert = [&](int t, int h) {
+        const uint8_t* cs = smem + (t % kStg) * S::kCodeStage + h * S::kCodeHalf;
         uint8_t* bf = smem + S::kBufOff;
         constexpr int kUnits = kKeys * D / 16 / 64;       // 16-code units per lane and half
         // All reads first: a store to the bf16 tile may alias a later read as far as the
         // compiler knows, so interleaved it would wait out each read's latency.
-        u32x4 raw[2][kUnits];
+        u32x4 raw[kUnits];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int i = 0; i < kUnits; ++i) raw[i] = *reinterpret_cast<const u32x4*>(cs + (lane + 64 * i) * 16);
 #pragma unroll
-            for (int i = 0; i < kUnits; ++i)
-                raw[h][i] = *reinterpret_cast<const u32x4*>(cs + h * S::kCodeHalf + (lane + 64 * i) * 16);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int i = 0; i < kUnits; ++i) {
-                const int ui = lane + 64 * i;
-                const int r = ui / (D / 16);
-                const int u16 = ui % (D / 16);
-                u32x4 lo, hi;
-                codes_to_bf16(raw[h][i], lo, hi);
-                uint8_t* row = bf + h * C::kHalf + r * C::kRowBytes;
-                *reinterpret_cast<u32x4*>(row + swz<C::kRowChunks, C::kRowShift>(r, 2 * u16) * 16) = lo;
-                *reinterpret_cast<u32x4*>(row + swz<C::kRowChunks, C::kRowShift>(r, 2 * u16 + 1) * 16) = hi;
-            }
+        for (int i = 0; i < kUnits; ++i) {
+            const int ui = lane + 64 * i;
+            const int r = ui / (D / 16);
+            const int u16 = ui % (D / 16);
+            u32x4 lo, hi;
+            codes_to_bf16(raw[i], lo, hi);
+            uint8_t* row = bf + r * C::kRowBytes;
+            *reinterpret_cast<u32x4*>(row + swz<C::kRowChunks, C::kRowShift>(r, 2 * u16) * 16) = lo;
+            *reinterpret_cast<u32x4*>(row + swz<C::kRowChunks, C::kRowShift>(r, 2 * u16 + 1) * 16) = hi;
         }
     };
 
@@ -653,7 +660,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
                 wait_tile<S::kDma>(min(ntw - 1 - t, kStg - 2));
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 feed(t + kStg - 1);
-                if constexpr (I8) convert(t);
+                if constexpr (I8) convert(t, 0);
                 const int kb = cc.ksa + (x0 + t - cc.pre) * kKeys;
                 // every column sees the whole tile: past the last token's window start and
                 // before the first token's end
@@ -662,11 +669,13 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
                                       window_start(cc.L - back, p.window), cc.L - back,
                                       p.scale_log2, sv, kscale_of(t));
                 if (__any(must_rescale(st, tmax))) break;
-                tile_pv<D>(tile_of(t), st, full, sv, p.scale_log2, n, g, oacc, vscale_of(t));
+                if constexpr (I8) convert(t, 1);
+                tile_pv<D>(vtile_of(t), st, full, sv, p.scale_log2, n, g, oacc, vscale_of(t));
             }
             if (t >= tend) break;
             rescale<D>(st, tmax, oacc);
-            tile_pv<D>(tile_of(t), st, full, sv, p.scale_log2, n, g, oacc, vscale_of(t));
+            if constexpr (I8) convert(t, 1);
+            tile_pv<D>(vtile_of(t), st, full, sv, p.scale_log2, n, g, oacc, vscale_of(t));
             ++t;
         }
         float l_tot = st.l + __shfl_xor(st.l, 16, 64);
@@ -966,9 +975,10 @@ bool gqa_stream_shape_supported(int head_dim, int bs_log2, int batch) {
     return (head_dim == 64 || head_dim == 128) && bs_log2 >= rpi_log2 && batch <= kStreamMaxBatch;
 }
 
-int gqa_stream_parts(int num_kv_heads, bool compact) {
-    const int wgs = compact ? kStreamWgsCompact : kStreamWgs;
-    return num_kv_heads >= wgs ? 1 : wgs / num_kv_heads;
+int gqa_stream_parts(int num_kv_heads, bool compact, bool int8) {
+    const int wgs = int8 ? kStreamWgsI8 : compact ? kStreamWgsCompact : kStreamWgs;
+    // at most kStreamWgsCompact parts per kv head (the combine's bound)
+    return num_kv_heads >= wgs ? 1 : min(wgs / num_kv_heads, kStreamWgsCompact);
 }
 
 hipError_t launch_gqa_decode_int8(const DecodeParams& p, int head_dim, hipStream_t s) {

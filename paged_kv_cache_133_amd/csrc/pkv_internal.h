@@ -195,10 +195,10 @@ bool gqa_mfma_supported(int dtype, int group);
 // Head dim, block size and batch the range-streaming kernel takes (any column count <= 16).
 bool gqa_stream_shape_supported(int head_dim, int bs_log2, int batch);
 bool gqa_stream_supported(int dtype, int group, int head_dim, int bs_log2, int batch);
-// Ranges per kv head: 2 workgroups per CU, or 4 in the compact layout (INT8 with 5..16 query
-// heads per kv head, and bf16 when the planned length is at least kStreamCompactMinKeys:
-// the merge of twice the ranges pays off only on long contexts).
-int gqa_stream_parts(int num_kv_heads, bool compact);
+// Ranges per kv head: 2 workgroups per CU, or 4 in the compact layout (bf16 when the planned
+// length is at least kStreamCompactMinKeys: the merge of twice the ranges pays off only on
+// long contexts), or 5 over INT8 codes (5..16 query heads per kv head).
+int gqa_stream_parts(int num_kv_heads, bool compact, bool int8);
 constexpr int32_t kStreamCompactMinKeys = 4096;
 hipError_t launch_gqa_decode(const DecodeParams& p, int head_dim, hipStream_t s);
 hipError_t launch_gqa_stream_combine(const DecodeParams& p, int head_dim, hipStream_t s);
