@@ -465,8 +465,14 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         const int kb = ic.ksa + (x0 + u - ic.pre) * kKeys;
         const int32_t* trow = p.table + (int64_t)ic.b * p.mbs;
         const int last_idx = (ic.L - 1) >> p.bs_log2;
+        if (p.bs_log2 >= 5) {         // the tile lies in one block: one entry
+            const int32_t e = uniform_load(trow + min(kb >> p.bs_log2, last_idx));
 #pragma unroll
-        for (int j = 0; j < C::kDmaHalf; ++j) pe[j] = uniform_load(trow + min((kb + j * C::kRpi) >> p.bs_log2, last_idx));
+            for (int j = 0; j < C::kDmaHalf; ++j) pe[j] = e;
+        } else {
+#pragma unroll
+            for (int j = 0; j < C::kDmaHalf; ++j) pe[j] = uniform_load(trow + min((kb + j * C::kRpi) >> p.bs_log2, last_idx));
+        }
         pe_last = uniform_load(trow + last_idx);
     };
     auto issue = [&](int u) {         // loads of local tile u (prep(u) done)
@@ -501,6 +507,26 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
             // of 4 in the [block][kv head][offset] layout), the others re-read lane 0's.
             const int L = ic.L;
             const bool whole = x + 1 < ic.end;
+            if (whole && p.bs_log2 >= 5) {
+                // Blocks of at least 32 keys: the tile (keys from a multiple of 32) lies in
+                // one block, so one row base serves every wave load and the 32 scales are
+                // one run of the block's.
+                const uint32_t blk = (uint32_t)min(max(pe[0], 0), last_block);
+                const uint64_t row0 = ((uint64_t)blk << p.bs_log2) | (uint32_t)(kb & bs_mask);
+                const uint8_t* kc = kcodes + row0 * crow_bytes;
+                const uint8_t* vc = vcodes + row0 * crow_bytes;
+#pragma unroll
+                for (int j = 0; j < S::kCodeDmaHalf; ++j) {
+                    const uint64_t off = (uint64_t)(j * S::kCodeRpi) * crow_bytes;
+                    lds_dma16_s(kc + off, cvoff, stage + j * 1024);
+                    lds_dma16_s(vc + off, cvoff, stage + S::kCodeHalf + j * 1024);
+                }
+                const int gi = lane < 16 ? (lane & 7) : 0;
+                const int64_t sidx = ((((int64_t)blk * p.hkv + kvh) << p.bs_log2) | (kb & bs_mask)) + 4 * gi;
+                const float* sc = (lane >= 8 && lane < 16) ? p.v_scale : p.k_scale;
+                lds_dma16(sc + sidx, stage + 2 * S::kCodeHalf);
+                return;
+            }
             const int64_t last_slot = ((int64_t)min(max(pe_last, 0), last_block) << p.bs_log2) | ((L - 1) & bs_mask);
 #pragma unroll
             for (int j = 0; j < S::kCodeDmaHalf; ++j) {
