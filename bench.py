@@ -638,9 +638,9 @@ def main():
     slot_call = _lib.prepare_slot_mapping(table, lb, cu, w.block_size, T, slots)
     fused = args.path == "fused"
     reps = []
-    # INT8 with 1..4 query heads per kv head: the quantizing write folds into the split pass
-    # (the fused path); otherwise slot_mapping and the quantizing write run first.
-    int8_fused = int8 and not w.mode == "mla" and fused and w.num_q_heads // w.num_kv_heads <= 4
+    # INT8 (MHA/GQA): the quantizing write folds into the attention pass (the fused path);
+    # INT8 MLA: slot_mapping and the quantizing write run first.
+    int8_fused = int8 and not w.mode == "mla" and fused
     slot_first = args.path == "separate" or (int8 and not int8_fused)
     for r in range(R):
         if int8 and mla:

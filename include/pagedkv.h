@@ -169,16 +169,16 @@ PKV_API int pkv_paged_attn_decode_int8(void* out, float* lse_out, const void* q,
                                size_t workspace_bytes, void* stream);
 
 /*
- * The INT8 decode step with the quantizing write folded into the pass (1..4 query heads per
- * kv head): for each sequence b, the step's bf16 rows k_new[b], v_new[b] [batch][Hkv][head_dim]
+ * The INT8 decode step with the quantizing write folded into the pass: for each sequence b, the step's bf16 rows k_new[b], v_new[b] [batch][Hkv][head_dim]
  * are quantized exactly as pkv_kv_cache_write_int8 does (the same codes and scales, bit for
  * bit), stored at logical position seq_lens_kv[b] - 1 (its slot in slot_mapping_out [batch],
  * or -1 for a row longer than max_seq_len_kv, which writes nothing), and attended to with
  * the other seq_lens_kv[b] - 1 cached tokens.  Equal to slot_mapping + pkv_kv_cache_write_int8
  * + pkv_paged_attn_decode_int8, in one pass ("KVCache Optimization Skill", 3.6: write by
  * slot_mapping, then attention reads kv_len + 1 tokens; Layer 3 notes on the quantized cache).
- * 5..16 query heads per kv head return PKV_ERR_UNSUPPORTED (write first, then decode_int8).
- * Other arguments, stages, workspace and preconditions as for pkv_paged_attn_decode_int8.
+ * Any of 1..16 query heads per kv head (with 5..16 the range that holds a sequence's last
+ * key writes it before reading it back).  Other arguments, stages, workspace and
+ * preconditions as for pkv_paged_attn_decode_int8.
  */
 PKV_API int pkv_paged_attn_decode_int8_append(void* out, float* lse_out, const void* q,
                                       const void* k_new, const void* v_new, void* k_cache,

@@ -986,10 +986,6 @@ int run_decode_int8(void* out, float* lse_out, const void* q, const void* k_new,
     const bool ranges = group > 4;
     if ((k_new == nullptr) != (v_new == nullptr))
         return fail(PKV_ERR_NULL, "%s: k_new and v_new must be given together or not at all", who);
-    if (k_new && ranges)
-        return fail(PKV_ERR_UNSUPPORTED,
-                    "%s: the write folded into the pass takes 1..4 query heads per kv head (got %d); "
-                    "write with pkv_kv_cache_write_int8, then pkv_paged_attn_decode_int8", who, group);
     if (ranges && (group > 16 || (head_dim != 64 && head_dim != 128) || block_size <= 0 ||
                    (block_size & (block_size - 1)) || block_size < 1024 / head_dim ||
                    !pkv::gqa_stream_supported(PKV_BF16, group, head_dim, log2i(block_size), batch)))

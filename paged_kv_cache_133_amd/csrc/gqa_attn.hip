@@ -233,6 +233,47 @@ __device__ __forceinline__ void append_row(const DecodeParams& p, int b, int kvh
     if (p.slots_out && kvh == 0 && lane == 0) p.slots_out[b] = slot;
 }
 
+// INT8 form: the kv head's slices of the new bf16 K and V rows quantized as the writer does
+// (s = max|x| / 127, q = round_half_even(x / s), the same fp32 operations, so the same codes
+// and scale bit for bit) and stored at the slot with their scales; two values per lane.
+// The caller waits for the stores before any load of that key.
+template <int D>
+__device__ __forceinline__ void append_row_i8(const DecodeParams& p, int b, int kvh, int L, int lane) {
+    if (uniform_load(p.seq_lens + b) > p.len_cap) {
+        if (p.slots_out && kvh == 0 && lane == 0) p.slots_out[b] = -1;
+        return;
+    }
+    const int32_t* trow = p.table + (int64_t)b * p.mbs;
+    const int32_t phys = min(max(trow[(L - 1) >> p.bs_log2], 0), (int32_t)(p.num_blocks - 1));
+    const int off_in_block = (L - 1) & ((1 << p.bs_log2) - 1);
+    const int64_t slot = ((int64_t)phys << p.bs_log2) | off_in_block;
+    const int64_t sc_idx = (((int64_t)phys * p.hkv + kvh) << p.bs_log2) | off_in_block;
+    const int64_t src_off = (((int64_t)b * p.hkv + kvh) * D + 2 * (lane % (D / 2))) * 2;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const uint32_t pair = *reinterpret_cast<const uint32_t*>(
+            reinterpret_cast<const uint8_t*>(which ? p.v_new : p.k_new) + src_off);
+        const float x0 = bf16_lo(pair), x1 = bf16_hi(pair);
+        float amax = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+        for (int sft = 1; sft < D / 2; sft <<= 1) amax = fmaxf(amax, __shfl_xor(amax, sft, 64));
+        const float sc = __fdiv_rn(amax, 127.0f);
+        uint32_t w = 0u;
+        if (sc > 0.0f) {
+            const float q0 = fminf(fmaxf(rintf(__fdiv_rn(x0, sc)), -127.0f), 127.0f);
+            const float q1 = fminf(fmaxf(rintf(__fdiv_rn(x1, sc)), -127.0f), 127.0f);
+            w = ((uint32_t)(int)q0 & 0xffu) | (((uint32_t)(int)q1 & 0xffu) << 8);
+        }
+        if (lane < D / 2) {
+            uint8_t* dst = reinterpret_cast<uint8_t*>(which ? p.v_cache_w : p.k_cache_w) +
+                           slot * (int64_t)p.hkv * D + (int64_t)kvh * D + 2 * lane;
+            *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
+            if (lane == 0) (which ? p.v_scale_w : p.k_scale_w)[sc_idx] = sc;
+        }
+    }
+    if (p.slots_out && kvh == 0 && lane == 0) p.slots_out[b] = slot;
+}
+
 // ================================================================== range-streaming kernel
 constexpr int kStreamStages = 3;       // LDS stages: two tiles in flight while one is used
 constexpr int kStreamCompactStages = 2;   // compact layout: one tile in flight while one is used
@@ -297,7 +338,6 @@ __device__ __forceinline__ int new_key_of(const DecodeParams& p, int b, int L) {
 
 template <int D, bool APPEND, bool I8 = false, bool COMPACT = I8>
 __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
-    static_assert(!(APPEND && I8), "the INT8 cache is written beforehand by the quantizing writer");
     using C = GqaCfg<D>;
     using S = StreamCfg<D, I8, COMPACT>;
     constexpr int kStg = S::kStages;
@@ -379,10 +419,14 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
             while (mm) {
                 const int bb = c0 + __builtin_ctzll(mm);
                 mm &= mm - 1;
-                append_row<D>(p, bb, kvh, uni_len(bb), lane);
+                if constexpr (I8) append_row_i8<D>(p, bb, kvh, uni_len(bb), lane);
+                else append_row<D>(p, bb, kvh, uni_len(bb), lane);
             }
         }
     }
+    // INT8: the new codes are read back from the cache by this range's last tile of the
+    // sequence (bf16 reads the new rows instead), so the stores complete first.
+    if constexpr (APPEND && I8) __threadfence_block();
     if (ntw <= 0) return;
 
     // The sequence that holds tile x0 (the first with tiles past x0).
@@ -1009,8 +1053,13 @@ int gqa_stream_parts(int num_kv_heads, bool compact, bool int8) {
 
 hipError_t launch_gqa_decode_int8(const DecodeParams& p, int head_dim, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)p.hkv * p.parts));
-    if (head_dim == 64) hipLaunchKernelGGL((gqa_stream_kernel<64, false, true>), grid, dim3(64), 0, s, p);
-    else hipLaunchKernelGGL((gqa_stream_kernel<128, false, true>), grid, dim3(64), 0, s, p);
+    if (p.k_new) {
+        if (head_dim == 64) hipLaunchKernelGGL((gqa_stream_kernel<64, true, true>), grid, dim3(64), 0, s, p);
+        else hipLaunchKernelGGL((gqa_stream_kernel<128, true, true>), grid, dim3(64), 0, s, p);
+    } else {
+        if (head_dim == 64) hipLaunchKernelGGL((gqa_stream_kernel<64, false, true>), grid, dim3(64), 0, s, p);
+        else hipLaunchKernelGGL((gqa_stream_kernel<128, false, true>), grid, dim3(64), 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -261,7 +261,11 @@ def _code_pools(c):
 
 @pytest.mark.parametrize("shape", [(32, 32, 128, 16), (8, 2, 64, 1), (16, 4, 128, 128),
                                    (4, 1, 128, 32), (12, 4, 64, 64), (6, 6, 64, 1),
-                                   (3, 3, 128, 16)],
+                                   (3, 3, 128, 16),
+                                   # 5..16 query heads per kv head: the range-streaming kernel
+                                   # writes the new key before its last tile reads it back
+                                   (32, 4, 128, 16), (64, 4, 64, 16), (40, 8, 128, 8),
+                                   (16, 2, 128, 128)],
                          ids=lambda s: "hq%d_hkv%d_d%d_bs%d" % s)
 @pytest.mark.parametrize("window", [0, 100])
 def test_int8_decode_append(shape, window):
@@ -339,3 +343,39 @@ def test_int8_decode_append_headline_and_overlength_row():
             assert torch.equal(a[key].view(torch.int8) if key in ("kc", "vc") else a[key].view(torch.int32),
                                s[key].view(torch.int8) if key in ("kc", "vc") else s[key].view(torch.int32)), key
         assert torch.equal(out_a.view(torch.int16), out_s.view(torch.int16))
+
+
+@pytest.mark.parametrize("shape", [(32, 4, 128, 16), (16, 2, 128, 128)], ids=lambda s: "hq%d_hkv%d_d%d_bs%d" % s)
+def test_int8_decode_append_ranges_overlength_row(shape):
+    """The range-streaming form of the fused call with a length bound that cuts the longest
+    row: nothing is written for it (slot -1), the other rows are, and the outputs equal the
+    separate write + decode_int8 under the same bound bit for bit."""
+    Hq, Hkv, D, bs = shape
+    L = np.array([7, 300, 2999, 1500, 64, 1100, 33, 2048])
+    say(f"int8 decode_append ranges over-length {shape}")
+    w = wl.custom(batch=len(L), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                  dtype="bf16")
+    c = wl.make_case(w, L - 1, [1] * len(L), seed=Hq + bs, device=DEV, poison=False)
+    table, la = c.table_tensor(DEV), c.lens_after_tensor(DEV)
+    B = len(L)
+    cap = int(np.sort(L)[-2])
+    a, s = _code_pools(c)
+    slots_a = torch.full((B,), -2, dtype=torch.int64, device=DEV)
+    out_a, _ = pkv.paged_attn_decode_int8_append(c.q, c.new_k, c.new_v, a["kc"], a["vc"], a["ks"],
+                                                 a["vs"], table, la, cap, w.scale, slots_out=slots_a)
+    slots_s = pkv.slot_mapping(table, c.lens_before_tensor(DEV), c.cu_q_tensor(DEV), bs, B)
+    over = la > cap
+    slots_s[over] = -1
+    keep = ~over
+    pkv.kv_cache_write_int8(c.new_k[keep], c.new_v[keep], s["kc"], s["vc"], s["ks"], s["vs"],
+                            slots_s[keep])
+    out_s, _ = pkv.paged_attn_decode_int8(c.q, s["kc"], s["vc"], s["ks"], s["vs"], table, la, cap,
+                                          w.scale)
+    torch.cuda.synchronize()
+    assert int(over.sum()) == 1
+    assert torch.equal(slots_a, slots_s)
+    for key in ("kc", "vc"):
+        assert torch.equal(a[key], s[key]), key
+    for key in ("ks", "vs"):
+        assert torch.equal(a[key].view(torch.int32), s[key].view(torch.int32)), key
+    assert torch.equal(out_a.view(torch.int16), out_s.view(torch.int16))
