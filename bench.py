@@ -396,15 +396,20 @@ def cpu_baseline(case, kv_bytes, min_seconds):
 def step_description(w, path):
     """What one timed step launches, for the JSON line."""
     if int8_workload(w) and w.mode == "mla":
+        if path == "fused":
+            return ("paged_attn_decode_mla_int8_append: MLA split pass that also quantizes and "
+                    "writes the new latent row (slot_mapping + quantizing write of nope and rope "
+                    "+ split-KV attention), then combine")
         return ("slot_mapping, kv_cache_write_int8_mla (quantizing write of nope and rope), "
                 "decode_mla_int8 split pass, combine")
     if int8_workload(w):
-        if w.num_q_heads // w.num_kv_heads > 4:
-            return "slot_mapping, kv_cache_write_int8 (quantizing write), decode_int8 range pass, combine"
+        ranges = w.num_q_heads // w.num_kv_heads > 4
         if path == "fused":
-            return ("paged_attn_decode_int8_append: split pass that also quantizes and writes the "
-                    "new token (slot_mapping + quantizing write + split-KV attention), then combine")
-        return "slot_mapping, kv_cache_write_int8 (quantizing write), decode_int8 split pass, combine"
+            return ("paged_attn_decode_int8_append: %s pass that also quantizes and writes the "
+                    "new token (slot_mapping + quantizing write + attention), then combine"
+                    % ("range" if ranges else "split"))
+        return ("slot_mapping, kv_cache_write_int8 (quantizing write), decode_int8 %s pass, combine"
+                % ("range" if ranges else "split"))
     if w.q_tokens:
         return ("kv_cache_append (slot_mapping + write of the step's %d rows per sequence), "
                 "decode_mtp range pass, combine" % w.q_tokens)
@@ -638,14 +643,21 @@ def main():
     slot_call = _lib.prepare_slot_mapping(table, lb, cu, w.block_size, T, slots)
     fused = args.path == "fused"
     reps = []
-    # INT8 (MHA/GQA): the quantizing write folds into the attention pass (the fused path);
-    # INT8 MLA: slot_mapping and the quantizing write run first.
-    int8_fused = int8 and not w.mode == "mla" and fused
+    # INT8: the quantizing write folds into the attention pass (the fused path); the
+    # separate path runs slot_mapping and the quantizing writer first.
+    int8_fused = int8 and fused
     slot_first = args.path == "separate" or (int8 and not int8_fused)
     for r in range(R):
         if int8 and mla:
             nc, rc, ns, rs = (pool_i8["k"], pool_i8["v"], pool_sc["k"], pool_sc["v"]) if r == 0 else (
                 pool_i8["k"].clone(), pool_i8["v"].clone(), pool_sc["k"].clone(), pool_sc["v"].clone())
+            if int8_fused:
+                split, combine, _ = _lib.prepare_decode_mla_int8_append(
+                    case.q, case.q_rope, case.new_k.reshape(T, 512), case.new_rope.reshape(T, 64),
+                    nc, rc, ns, rs, table, la, case.max_len_after, w.scale, out=out, lse=lse,
+                    workspace=ws, slots_out=slots)
+                reps.append((None, split, combine))
+                continue
             write = _lib.prepare_kv_cache_write_int8_mla(case.new_k.reshape(T, 512),
                                                          case.new_rope.reshape(T, 64), nc, rc, ns,
                                                          rs, slots)

@@ -222,6 +222,30 @@ PKV_API int pkv_paged_attn_decode_mla_int8(void* out, float* lse_out, const void
                                            size_t workspace_bytes, void* stream);
 
 /*
+ * The MLA-absorbed decode step over the INT8 latent cache with the quantizing write folded
+ * into the pass: for each sequence b the step's bf16 latent rows nope_new[b] [batch][512] and
+ * rope_new[b] [batch][64] are quantized exactly as pkv_kv_cache_write_int8_mla does (the same
+ * codes and scales, bit for bit), stored at logical position seq_lens_kv[b] - 1 (its slot in
+ * slot_mapping_out [batch], or -1 for a row longer than max_seq_len_kv, which writes nothing),
+ * and attended to with the other seq_lens_kv[b] - 1 cached tokens.  Equal to slot_mapping +
+ * pkv_kv_cache_write_int8_mla + pkv_paged_attn_decode_mla_int8, in one pass ("KVCache
+ * Optimization Skill", 3.6: write by slot_mapping, then attention reads kv_len + 1 tokens;
+ * Mode 3, the compressed latent cache).  The caches and scales are written; the nope and rope
+ * arrays must be distinct.  Other arguments, stages, workspace and preconditions as for
+ * pkv_paged_attn_decode_mla_int8.
+ */
+PKV_API int pkv_paged_attn_decode_mla_int8_append(void* out, float* lse_out, const void* q,
+                                          const void* q_rope, const void* nope_new,
+                                          const void* rope_new, void* nope_codes, void* rope_codes,
+                                          float* nope_scale, float* rope_scale,
+                                          const int32_t* block_table, const int32_t* seq_lens_kv,
+                                          int64_t* slot_mapping_out, int32_t batch,
+                                          int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                                          int32_t num_q_heads, int32_t block_size,
+                                          int64_t num_blocks, float softmax_scale, int32_t stages,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The MLA latent row normalised, rotated and written in one launch: the fused writer the
  * pages place in front of the MLA cache (npu_kv_rmsnorm_rope_cache, keyed by slot_mapping;
  * "KVCache Optimization Skill", Mode 3 and its cache-write fusion note), which they name

@@ -7,6 +7,7 @@ to its C ABI (include/pagedkv.h).  Calls raise if the library is missing.
 from ._lib import (BlockManager, CapturedStep, PagedKVError, decode_workspace_size,  # noqa: F401
                    kv_cache_append, kv_cache_copy_blocks, kv_cache_write, kv_cache_write_int8,
                    kv_cache_write_int8_mla, paged_attn_decode_mla_int8,
+                   paged_attn_decode_mla_int8_append,
                    kv_rmsnorm_rope_cache, lib, new_decode_workspace, paged_attn_decode,
                    paged_attn_decode_int8, paged_attn_decode_int8_append, paged_attn_decode_append,
                    paged_attn_decode_mla_append,

@@ -41,7 +41,7 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_runner_launch", "pkv_upload_kernel", "pkv_decode_mtp_workspace_size", "pkv_paged_attn_decode_mtp",
            "pkv_kv_cache_write_int8_mla", "pkv_paged_attn_decode_mla_int8", "pkv_stream_read",
            "pkv_paged_attn_decode_int8_append", "pkv_paged_attn_decode_mla_append",
-           "pkv_gather_read")
+           "pkv_gather_read", "pkv_paged_attn_decode_mla_int8_append")
 
 
 class PagedKVError(RuntimeError):
@@ -153,6 +153,9 @@ def lib() -> ctypes.CDLL:
     L.pkv_paged_attn_decode_mla_int8.restype = ctypes.c_int
     L.pkv_paged_attn_decode_mla_int8.argtypes = [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
                                                  i32, i64, f32, i32, p, sz, p]
+    L.pkv_paged_attn_decode_mla_int8_append.restype = ctypes.c_int
+    L.pkv_paged_attn_decode_mla_int8_append.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p, p, i32,
+                                                        i32, i32, i32, i32, i64, f32, i32, p, sz, p]
     L.pkv_decode_mtp_workspace_size.restype = sz
     L.pkv_decode_mtp_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     L.pkv_paged_attn_decode_mtp.restype = ctypes.c_int
@@ -721,6 +724,64 @@ def prepare_decode_mla_int8(q, q_rope, nope_codes, rope_codes, nope_scale, rope_
         calls.append(PreparedCall(lib().pkv_paged_attn_decode_mla_int8, args,
                                   (q, q_rope, nope_codes, rope_codes, nope_scale, rope_scale,
                                    block_table, seq_lens_kv, out, lse, workspace)))
+    return calls[0], calls[1], out
+
+
+def _decode_mla_int8_append_args(q, q_rope, nope_new, rope_new, nope_codes, rope_codes, nope_scale,
+                                 rope_scale, block_table, seq_lens_kv, max_seq_len_kv, softmax_scale,
+                                 stages, out, lse, workspace, slots_out):
+    _dev(q, q_rope, nope_new, rope_new, nope_codes, rope_codes, nope_scale, rope_scale, block_table,
+         seq_lens_kv, out, lse, workspace, slots_out)
+    _mla_int8_shapes(nope_codes, rope_codes, nope_scale, rope_scale)
+    B, hq, _ = q.shape
+    _batch_rows(B, block_table, seq_lens_kv)
+    if nope_new.dtype != torch.bfloat16 or rope_new.dtype != torch.bfloat16:
+        raise ValueError("the new latent rows must be bf16")
+    if tuple(nope_new.shape[-1:]) != (512,) or tuple(rope_new.shape[-1:]) != (64,) or \
+            nope_new.numel() != B * 512 or rope_new.numel() != B * 64:
+        raise ValueError("nope_new must hold [B, 512] and rope_new [B, 64] values")
+    nb, bs = nope_codes.shape[0], nope_codes.shape[1]
+    if out is None:
+        out = torch.empty((B, hq, 512), dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = new_decode_workspace(B, hq, 1, 512, max_seq_len_kv, q.device)
+    args = (_ptr(out), _ptr(lse), _ptr(q), _ptr(q_rope), _ptr(nope_new), _ptr(rope_new),
+            _ptr(nope_codes), _ptr(rope_codes), _ptr(nope_scale), _ptr(rope_scale),
+            _ptr(block_table), _ptr(seq_lens_kv), _ptr(slots_out), B, block_table.shape[1],
+            max_seq_len_kv, hq, bs, nb, float(softmax_scale), stages, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(q.device))
+    return args, out, workspace
+
+
+def paged_attn_decode_mla_int8_append(q, q_rope, nope_new, rope_new, nope_codes, rope_codes,
+                                      nope_scale, rope_scale, block_table, seq_lens_kv,
+                                      max_seq_len_kv, softmax_scale, out=None, lse=None,
+                                      workspace=None, slots_out=None):
+    """MLA decode over the INT8 latent cache that also quantizes and writes the step's latent
+    rows (pkv_paged_attn_decode_mla_int8_append).  Returns (out, lse)."""
+    args, out, _ = _decode_mla_int8_append_args(q, q_rope, nope_new, rope_new, nope_codes,
+                                                rope_codes, nope_scale, rope_scale, block_table,
+                                                seq_lens_kv, max_seq_len_kv, softmax_scale, 3, out,
+                                                lse, workspace, slots_out)
+    _check(lib().pkv_paged_attn_decode_mla_int8_append(*args))
+    return out, lse
+
+
+def prepare_decode_mla_int8_append(q, q_rope, nope_new, rope_new, nope_codes, rope_codes,
+                                   nope_scale, rope_scale, block_table, seq_lens_kv,
+                                   max_seq_len_kv, softmax_scale, out=None, lse=None,
+                                   workspace=None, slots_out=None):
+    """(split pass with the folded quantizing write, combine pass) prepared calls."""
+    calls = []
+    for stages in (1, 2):
+        args, out, workspace = _decode_mla_int8_append_args(
+            q, q_rope, nope_new, rope_new, nope_codes, rope_codes, nope_scale, rope_scale,
+            block_table, seq_lens_kv, max_seq_len_kv, softmax_scale, stages, out, lse, workspace,
+            slots_out)
+        calls.append(PreparedCall(lib().pkv_paged_attn_decode_mla_int8_append, args,
+                                  (q, q_rope, nope_new, rope_new, nope_codes, rope_codes,
+                                   nope_scale, rope_scale, block_table, seq_lens_kv, out, lse,
+                                   workspace, slots_out)))
     return calls[0], calls[1], out
 
 

@@ -497,6 +497,8 @@ int run_mla_decode(void* out, float* lse_out, const void* q, const void* q_rope,
         p.rope_new = rope_new;
         p.k_cache_w = const_cast<void*>(k_cache);
         p.rope_w = const_cast<void*>(k_rope_cache);
+        p.k_scale_w = const_cast<float*>(nope_scale);   // INT8: the scales it writes
+        p.r_scale_w = const_cast<float*>(rope_scale);
         p.slots_out = slots_out;
     }
     int rc = PKV_OK;
@@ -925,6 +927,41 @@ int pkv_paged_attn_decode_mla_int8(void* out, float* lse_out, const void* q, con
                           seq_lens_kv, batch, max_blocks_per_seq, max_seq_len_kv, num_q_heads, 1, 512,
                           512, 64, block_size, num_blocks, softmax_scale, PKV_BF16, workspace,
                           workspace_bytes, stages, (hipStream_t)stream, nope_scale, rope_scale);
+}
+
+int pkv_paged_attn_decode_mla_int8_append(void* out, float* lse_out, const void* q, const void* q_rope,
+                                          const void* nope_new, const void* rope_new,
+                                          void* nope_codes, void* rope_codes, float* nope_scale,
+                                          float* rope_scale, const int32_t* block_table,
+                                          const int32_t* seq_lens_kv, int64_t* slot_mapping_out,
+                                          int32_t batch, int32_t max_blocks_per_seq,
+                                          int32_t max_seq_len_kv, int32_t num_q_heads,
+                                          int32_t block_size, int64_t num_blocks, float softmax_scale,
+                                          int32_t stages, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+    const char* who = "decode_mla_int8_append";
+    if (stages < 1 || stages > 3) return fail(PKV_ERR_SHAPE, "%s: stages must be 1, 2 or 3", who);
+    if (!q_rope || !rope_codes) return fail(PKV_ERR_NULL, "%s: q_rope and rope_codes are required", who);
+    bool mla = false;
+    int rc = check_decode_common(q_rope, rope_codes, PKV_BF16, batch, num_q_heads, 1, 512, 512, 64,
+                                 max_blocks_per_seq, max_seq_len_kv, block_size, num_blocks,
+                                 softmax_scale, &mla);
+    if (rc != PKV_OK) return rc;
+    if (block_size < 4)
+        return fail(PKV_ERR_UNSUPPORTED, "%s: block_size %d (needs >= 4: a 4-key group's scales are one load)",
+                    who, block_size);
+    if (batch == 0) return PKV_OK;
+    if (!nope_new || !rope_new) return fail(PKV_ERR_NULL, "%s: NULL new rows", who);
+    if (!nope_scale || !rope_scale) return fail(PKV_ERR_NULL, "%s: NULL scale array", who);
+    if (!aligned16(nope_scale) || !aligned16(rope_scale) || !aligned16(nope_new) || !aligned16(rope_new))
+        return fail(PKV_ERR_ALIGN, "%s: scale arrays and new rows must be 16-byte aligned", who);
+    if (nope_codes == rope_codes || nope_scale == rope_scale)
+        return fail(PKV_ERR_SHAPE, "%s: the nope and rope arrays must differ", who);
+    return run_mla_decode(out, lse_out, q, q_rope, nope_codes, nope_codes, rope_codes, block_table,
+                          seq_lens_kv, batch, max_blocks_per_seq, max_seq_len_kv, num_q_heads, 1, 512,
+                          512, 64, block_size, num_blocks, softmax_scale, PKV_BF16, workspace,
+                          workspace_bytes, stages, (hipStream_t)stream, nope_scale, rope_scale,
+                          nope_new, rope_new, slot_mapping_out);
 }
 
 int pkv_kv_cache_write_int8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

@@ -97,17 +97,51 @@ __device__ __forceinline__ int wide_rope_chunk(int r, int c) { return c ^ ((r >>
     PKV_RS10("23") PKV_RS10("24") PKV_RS1("250") PKV_RS1("251") PKV_RS1("252") PKV_RS1("253")         \
     PKV_RS1("254") PKV_RS1("255")
 
+// One latent row quantized as the INT8 writer does it: s = max|x| / 127, q = round half to
+// even of x / s clamped to [-127, 127] (fp32 divisions; a zero row has s = 0 and zero codes).
+// G lanes hold 8 bf16 values each (src: 16 bytes); lanes that `store` write their 8 codes at
+// dst and lane 0 the scale.  The max is exact in any order, so the codes and the scale equal
+// the writer's bit for bit.
+template <int G>
+__device__ __forceinline__ void quant_row8(const uint8_t* src, uint8_t* dst, float* scale, int lane,
+                                           bool store) {
+    const u32x4 v = ld16(src);
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[2 * i] = bf16_lo(v[i]); x[2 * i + 1] = bf16_hi(v[i]); }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+    for (int sft = 1; sft < G; sft <<= 1) amax = fmaxf(amax, __shfl_xor(amax, sft, 64));
+    const float sc = __fdiv_rn(amax, 127.0f);
+    uint32_t w[2] = {0u, 0u};
+    if (sc > 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float qf = fminf(fmaxf(rintf(__fdiv_rn(x[i], sc)), -127.0f), 127.0f);
+            w[i >> 2] |= ((uint32_t)(int)qf & 0xffu) << (8 * (i & 3));
+        }
+    }
+    if (store) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+        if (lane == 0) *scale = sc;
+    }
+}
+
 // Cycles for an MFMA result written by inline assembly to be readable by anything else.
 __device__ __forceinline__ void wait_mfma_result() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
-// APPEND (bf16 only): the key at seq_lens[b] - 1 is the step's new latent row, read from
+// APPEND: the key at seq_lens[b] - 1 is the step's new latent row.  bf16: read from
 // p.k_new / p.rope_new instead of the cache; the split that holds it also stores it at its
-// slot (reported in slots_out).  A row longer than the length bound writes nothing (slot
-// -1) and attends to its first len_cap cached keys.
+// slot (reported in slots_out).  INT8: every workgroup of the split that holds it quantizes
+// the row as the writer does (the same codes and scales, bit for bit; the workgroups of
+// other head groups store the same bytes) and stores it before its first load, which then
+// reads it back like any cached key.  A row longer than the length bound writes nothing
+// (slot -1) and attends to its first len_cap cached keys.
 // I8: p.k_cache / p.k_rope hold int8 codes, p.k_scale / p.r_scale their scales [nb][bs].
 template <bool APPEND, bool I8>
 __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams p) {
-    static_assert(!(APPEND && I8), "the INT8 form has no append mode");
     using C = WideCfg;
     using W8 = WideI8Cfg;
     constexpr int kTabOff = I8 ? W8::kTabOff : C::kTabOff;
@@ -164,7 +198,25 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
     if (k_begin >= L) return;
     const int k_end = min(L, k_begin + split_keys);
     const int ntiles = (k_end - k_begin + kKeys - 1) / kKeys;
-    if (APPEND && hg == 0 && new_key >= k_begin && new_key < k_end && wid < 2) {
+    if (APPEND && I8 && new_key >= k_begin && new_key < k_end && wid < 2) {
+        const int32_t phys = min(max(p.table[(int64_t)b * p.mbs + (new_key >> p.bs_log2)], 0),
+                                 (int32_t)(p.num_blocks - 1));
+        const int64_t slot = ((int64_t)phys << p.bs_log2) | (new_key & ((1 << p.bs_log2) - 1));
+        if (wid == 0) {        // nope: 8 values per lane
+            quant_row8<64>(reinterpret_cast<const uint8_t*>(p.k_new) + (int64_t)b * 1024 + lane * 16,
+                           reinterpret_cast<uint8_t*>(p.k_cache_w) + slot * 512 + lane * 8,
+                           p.k_scale_w + slot, lane, true);
+            if (hg == 0 && p.slots_out && lane == 0) p.slots_out[b] = slot;
+        } else {               // rope: lanes 0-7, 8 values each
+            const int l8 = lane & 7;
+            quant_row8<8>(reinterpret_cast<const uint8_t*>(p.rope_new) + (int64_t)b * 128 + l8 * 16,
+                          reinterpret_cast<uint8_t*>(p.rope_w) + slot * 64 + l8 * 8,
+                          p.r_scale_w + slot, l8, lane < 8);
+        }
+        // the stores complete before the loads below (the wait and barrier after the first
+        // table chunk's load cover them)
+    }
+    if (APPEND && !I8 && hg == 0 && new_key >= k_begin && new_key < k_end && wid < 2) {
         const int32_t phys = min(max(p.table[(int64_t)b * p.mbs + (new_key >> p.bs_log2)], 0),
                                  (int32_t)(p.num_blocks - 1));
         const int64_t slot = ((int64_t)phys << p.bs_log2) | (new_key & ((1 << p.bs_log2) - 1));
@@ -235,7 +287,7 @@ __global__ __launch_bounds__(WideCfg::kThreads) void mla_wide_kernel(MfmaParams 
     const bool fast_rows = p.bs_log2 >= 3;
     auto fast_tile = [&](int u) {
         const int kb = k_begin + u * kKeys;
-        return fast_rows && kb + kKeys <= k_end && !(APPEND && new_key >= kb && new_key < kb + kKeys);
+        return fast_rows && kb + kKeys <= k_end && !(APPEND && !I8 && new_key >= kb && new_key < kb + kKeys);
     };
     auto entry_of = [&](int u) { return uniform_load(tab.row + ((k_begin + u * kKeys + 8 * wid_u) >> p.bs_log2)); };
     int32_t next_entry = fast_tile(0) ? entry_of(0) : 0;
@@ -687,7 +739,8 @@ hipError_t launch_mla_decode(const MfmaParams& p, hipStream_t s) {
     const int64_t hgs = mla_head_groups(p.hq);
     const int64_t units = ((int64_t)p.batch * p.max_splits + 7) / 8 * 8;
     const dim3 grid((unsigned)(hgs * units));
-    if (p.k_scale) hipLaunchKernelGGL((mla_wide_kernel<false, true>), grid, dim3(WideCfg::kThreads), 0, s, p);
+    if (p.k_scale && p.k_new) hipLaunchKernelGGL((mla_wide_kernel<true, true>), grid, dim3(WideCfg::kThreads), 0, s, p);
+    else if (p.k_scale) hipLaunchKernelGGL((mla_wide_kernel<false, true>), grid, dim3(WideCfg::kThreads), 0, s, p);
     else if (p.k_new) hipLaunchKernelGGL((mla_wide_kernel<true, false>), grid, dim3(WideCfg::kThreads), 0, s, p);
     else hipLaunchKernelGGL((mla_wide_kernel<false, false>), grid, dim3(WideCfg::kThreads), 0, s, p);
     return hipGetLastError();

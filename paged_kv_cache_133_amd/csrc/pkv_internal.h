@@ -257,12 +257,15 @@ struct MfmaParams {
     // fp32 scales [nb][1][bs] (nope, rope).
     const float* k_scale;
     const float* r_scale;
-    // MLA append (bf16; else null): the step's latent rows nope [B][512] and rope [B][64],
-    // attended at position seq_lens[b] - 1 and written there through the writable views.
+    // MLA append (else null): the step's bf16 latent rows nope [B][512] and rope [B][64],
+    // attended at position seq_lens[b] - 1 and written there through the writable views
+    // (INT8: quantized, codes into k_cache_w / rope_w and scales into the scale views).
     const void* k_new;
     const void* rope_new;
     void* k_cache_w;
     void* rope_w;
+    float* k_scale_w;
+    float* r_scale_w;
     int64_t* slots_out;      // [B] or null
 };
 // MLA decode: Dqk = 512 + Dr 64, Dv = 512, bf16 queries over the bf16 or the INT8 latent

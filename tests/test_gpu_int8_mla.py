@@ -149,3 +149,61 @@ def test_int8_mla_full_workload():
                                             c.w.scale, lse=lse)
     torch.cuda.synchronize()
     say(f"  max-abs error {_check(c, out, lse, kdeq, rdeq, lens):.3e}")
+
+
+def _int8_mla_pools(c):
+    """Two device copies of the INT8 latent pools: the oracle's quantization of the case's
+    bf16 pools (the step's rows not yet written)."""
+    nb, bs = c.num_blocks, c.w.block_size
+    nq, nsc = oracle.quantize_rows(host(c.cache_k).reshape(nb, bs, 512))
+    rq, rsc = oracle.quantize_rows(host(c.cache_rope).reshape(nb, bs, 64))
+    one = lambda: {"nc": torch.from_numpy(nq).to(DEV), "rc": torch.from_numpy(rq).to(DEV),  # noqa: E731
+                   "ns": torch.from_numpy(nsc).to(DEV), "rs": torch.from_numpy(rsc).to(DEV)}
+    return one(), one()
+
+
+@pytest.mark.parametrize("hq,bs,cut", [(128, 16, False), (64, 4, False), (192, 32, False),
+                                       (128, 128, False), (128, 64, True)])
+def test_int8_mla_decode_append(hq, bs, cut):
+    """Quantize, write and attend to the step's latent row in one pass: the slots, the whole
+    code and scale pools and the outputs equal slot_mapping + the quantizing writer +
+    decode_mla_int8 bit for bit; the output matches the oracle over the written pools.  With
+    `cut`, the length bound excludes the longest row: it writes nothing (slot -1)."""
+    L = np.array([1, 31, 32, 33, 700, 2600, 1500, 64])
+    say(f"int8 mla decode_append hq={hq} bs={bs} cut={cut}")
+    w = wl.custom(mode="mla", batch=len(L), num_q_heads=hq, num_kv_heads=1, head_dim=512,
+                  head_dim_rope=64, block_size=bs, dtype="bf16")
+    c = wl.make_case(w, L - 1, [1] * len(L), seed=hq + bs + cut, device=DEV, poison=False)
+    table, la = c.table_tensor(DEV), c.lens_after_tensor(DEV)
+    B = len(L)
+    cap = int(np.sort(L)[-2]) if cut else c.max_len_after
+    a, s = _int8_mla_pools(c)
+    nope_new, rope_new = c.new_k.reshape(B, 512), c.new_rope.reshape(B, 64)
+    slots_a = torch.full((B,), -2, dtype=torch.int64, device=DEV)
+    lse_a = torch.empty((B, hq), dtype=torch.float32, device=DEV)
+    out_a, _ = pkv.paged_attn_decode_mla_int8_append(c.q, c.q_rope, nope_new, rope_new, a["nc"], a["rc"],
+                                                     a["ns"], a["rs"], table, la, cap, w.scale,
+                                                     lse=lse_a, slots_out=slots_a)
+    slots_s = pkv.slot_mapping(table, c.lens_before_tensor(DEV), c.cu_q_tensor(DEV), bs, B)
+    over = la > cap
+    slots_s[over] = -1
+    keep = ~over
+    pkv.kv_cache_write_int8_mla(nope_new[keep], rope_new[keep], s["nc"], s["rc"], s["ns"], s["rs"],
+                                slots_s[keep])
+    lse_s = torch.empty((B, hq), dtype=torch.float32, device=DEV)
+    out_s, _ = pkv.paged_attn_decode_mla_int8(c.q, c.q_rope, s["nc"], s["rc"], s["ns"], s["rs"], table,
+                                              la, cap, w.scale, lse=lse_s)
+    torch.cuda.synchronize()
+    assert int(over.sum()) == (1 if cut else 0)
+    assert torch.equal(slots_a, slots_s)
+    for key in ("nc", "rc"):
+        assert torch.equal(a[key], s[key]), key
+    for key in ("ns", "rs"):
+        assert torch.equal(a[key].view(torch.int32), s[key].view(torch.int32)), key
+    assert torch.equal(out_a.view(torch.int16), out_s.view(torch.int16))
+    assert torch.equal(lse_a.view(torch.int32), lse_s.view(torch.int32))
+    if not cut:
+        nb = c.num_blocks
+        kdeq = oracle.dequantize_rows(a["nc"].cpu().numpy(), a["ns"].cpu().numpy()).reshape(nb, bs, 1, 512)
+        rdeq = oracle.dequantize_rows(a["rc"].cpu().numpy(), a["rs"].cpu().numpy()).reshape(nb, bs, 1, 64)
+        say(f"  max-abs error {_check(c, out_a, lse_a, kdeq, rdeq, c.lens_after.astype(np.int32)):.3e}")
