@@ -330,54 +330,39 @@ __device__ __forceinline__ void store_out4(float* out, int64_t idx, float a, flo
     *reinterpret_cast<float4*>(out + idx) = make_float4(a, b, c, d);
 }
 
-// One workgroup per (sequence, query head) row: wave 0 reduces the splits' (m, l) with lane
-// shuffles, then every thread merges four value columns (16-byte partial loads).
+// dim / 4 threads per (sequence, query head) row, 256 / (dim / 4) rows per workgroup.  Each
+// thread folds the row's split (m, l) pairs itself (the same few values for the whole row:
+// one cache line, no barrier) and merges its four value columns, the split partials read
+// with 16-byte loads.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-    extern __shared__ float sm_w[];   // [max_splits] weights
-    __shared__ float sm_inv;
-    __shared__ float sm_lse;
-    const int64_t bh = blockIdx.x;
+    const int tpr = p.dim / 4;
+    const int64_t bh = (int64_t)blockIdx.x * (blockDim.x / tpr) + threadIdx.x / tpr;
+    if (bh >= (int64_t)p.batch * p.hq) return;
+    const int d = 4 * (threadIdx.x % tpr);
     const int b = (int)(bh / p.hq);
     const int L = min(p.seq_lens[b], p.len_cap);
     const int ns = L > 0 ? (L - window_start32(L, p.window) + p.split_tokens - 1) / p.split_tokens : 0;
     if (ns <= 1) return;   // the split kernel wrote this row directly
     const float* ml = p.ws_ml + bh * p.max_splits * 2;
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        float M = -INFINITY;
-        for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-        float lsum = 0.0f;
-        for (int s = lane; s < ns; s += 64) {
-            const float w = fast_exp2(ml[2 * s] - M);
-            sm_w[s] = w;
-            lsum = fmaf(w, ml[2 * s + 1], lsum);
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o, 64);
-        if (lane == 0) {
-            sm_inv = 1.0f / lsum;
-            sm_lse = (M + __log2f(lsum)) * kLn2;
-        }
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+    const float* o = p.ws_o + bh * p.max_splits * p.dim + d;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float lsum = 0.0f;
+#pragma unroll 4
+    for (int s = 0; s < ns; ++s) {
+        const float w = fast_exp2(ml[2 * s] - M);
+        lsum = fmaf(w, ml[2 * s + 1], lsum);
+        const float4 v = *reinterpret_cast<const float4*>(o + (int64_t)s * p.dim);
+        acc.x = fmaf(w, v.x, acc.x);
+        acc.y = fmaf(w, v.y, acc.y);
+        acc.z = fmaf(w, v.z, acc.z);
+        acc.w = fmaf(w, v.w, acc.w);
     }
-    __syncthreads();
-    const float* o = p.ws_o + bh * p.max_splits * p.dim;
-    const float inv = sm_inv;
-    for (int d = 4 * threadIdx.x; d < p.dim; d += 4 * blockDim.x) {
-        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        for (int s = 0; s < ns; ++s) {
-            const float w = sm_w[s];
-            const float4 v = *reinterpret_cast<const float4*>(o + (int64_t)s * p.dim + d);
-            acc.x = fmaf(w, v.x, acc.x);
-            acc.y = fmaf(w, v.y, acc.y);
-            acc.z = fmaf(w, v.z, acc.z);
-            acc.w = fmaf(w, v.w, acc.w);
-        }
-        store_out4(reinterpret_cast<T*>(p.out), bh * p.dim + d, acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    }
-    if (p.lse && threadIdx.x == 0) p.lse[bh] = sm_lse;
+    const float inv = 1.0f / lsum;
+    store_out4(reinterpret_cast<T*>(p.out), bh * p.dim + d, acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if (p.lse && d == 0) p.lse[bh] = (M + __log2f(lsum)) * kLn2;
 }
 
 template <typename T, int D, bool APPEND>
@@ -455,12 +440,14 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, hipStre
 }
 
 hipError_t launch_combine(const CombineParams& p, int dtype, hipStream_t s) {
-    const dim3 grid((unsigned)((int64_t)p.batch * p.hq));
-    // four value columns per thread (dims are multiples of 4: 64, 128, 512)
-    const int threads = p.dim >= 1024 ? 256 : (p.dim >= 512 ? 128 : 64);
-    const size_t shm = (size_t)p.max_splits * sizeof(float);
-    if (dtype == 1) hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(threads), shm, s, p);
-    else hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(threads), shm, s, p);
+    // four value columns per thread; the head dims (64, 128, 512) divide 1024, so whole rows
+    // fill a workgroup of 256 threads
+    if (p.dim % 4 || 1024 % p.dim) return hipErrorInvalidValue;
+    const int rows_per_wg = 1024 / p.dim;
+    const int64_t rows = (int64_t)p.batch * p.hq;
+    const dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
+    if (dtype == 1) hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
