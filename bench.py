@@ -11,10 +11,14 @@ already resident in HBM.  --path append / separate time the same step as three /
 launches (kv_cache_append or slot_mapping + kv_cache_write, split, combine).  Several copies of the K/V pool are rotated so that each step
 reads a pool that left the 256 MB Infinity Cache long ago.
 
+Before the W warm-up steps, whole steps run untimed for at least --settle-ms (200 ms) of
+wall time, until the GPU clock has settled; then exactly K steps are timed, HIP events
+only at the two ends of the timed region.
+
 Prints one JSON line: KV-read GB/s (value), µs per step, the roofline of the dominant
-kernel (the split-KV attention pass, timed with HIP events around each of its launches
-on the stream it runs on, in a second pass of the same steps so the events do not
-perturb the step time) and the fp64 CPU oracle timed on this host as a baseline.
+kernel (the split-KV attention pass: K launches of it alone, back to back on the stream
+it runs on, HIP events at the two ends, after the timed steps) and the fp64 CPU oracle
+timed on this host as a baseline.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--seed S]
   python bench.py --calibrate-copy MIB     # plain copy of known size, for counter scaling
@@ -69,6 +73,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed whole steps for at least this long before the warm-up steps")
     ap.add_argument("--workload", default="llama7b_mha_bf16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--replicas", type=int, default=0, help="K/V pool copies rotated (0: auto)")
@@ -743,8 +749,19 @@ def main():
         if combine is not None:
             combine()
 
+    # Clock settling: from idle the GPU's clock takes tens of milliseconds to reach its
+    # steady level under this load (measured: a few warm-up steps leave the long-context
+    # and varlen steps 15-20 % slower than a settled run), so whole steps run untimed for
+    # at least --settle-ms of wall time before the W warm-up steps.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            step(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
-        step(i)
+        step(settle_steps + i)
     torch.cuda.synchronize()
     # Timed region: K whole steps, events only at its two ends.
     t0 = torch.cuda.Event(enable_timing=True)
@@ -811,6 +828,8 @@ def main():
            "step": step_description(w, args.path)}
     line = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+            "settle": {"ms": args.settle_ms, "steps": settle_steps,
+                       "what": "untimed whole steps before the warm-up, until the GPU clock has settled"},
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": w.dtype, "data": "synthetic", "config": cfg,
             "us_per_step": round(us_step, 2),

@@ -345,20 +345,26 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     const int ns = L > 0 ? (L - window_start32(L, p.window) + p.split_tokens - 1) / p.split_tokens : 0;
     if (ns <= 1) return;   // the split kernel wrote this row directly
     const float* ml = p.ws_ml + bh * p.max_splits * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
     const float* o = p.ws_o + bh * p.max_splits * p.dim + d;
+    // One pass, the running max rescaling what is merged so far: a split's (m, l) and its
+    // values are read together, with no wait for the other splits' maxima first.  (Every
+    // split here has at least one key; a max of -inf would still weigh 0, not NaN.)
+    float M = -INFINITY;
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float lsum = 0.0f;
 #pragma unroll 4
     for (int s = 0; s < ns; ++s) {
-        const float w = fast_exp2(ml[2 * s] - M);
-        lsum = fmaf(w, ml[2 * s + 1], lsum);
+        const float ms = ml[2 * s], ls = ml[2 * s + 1];
         const float4 v = *reinterpret_cast<const float4*>(o + (int64_t)s * p.dim);
-        acc.x = fmaf(w, v.x, acc.x);
-        acc.y = fmaf(w, v.y, acc.y);
-        acc.z = fmaf(w, v.z, acc.z);
-        acc.w = fmaf(w, v.w, acc.w);
+        const float mn = fmaxf(M, ms);
+        const float a = M == -INFINITY ? 0.0f : fast_exp2(M - mn);
+        const float w = ms == -INFINITY ? 0.0f : fast_exp2(ms - mn);
+        M = mn;
+        lsum = fmaf(w, ls, lsum * a);
+        acc.x = fmaf(w, v.x, acc.x * a);
+        acc.y = fmaf(w, v.y, acc.y * a);
+        acc.z = fmaf(w, v.z, acc.z * a);
+        acc.w = fmaf(w, v.w, acc.w * a);
     }
     const float inv = 1.0f / lsum;
     store_out4(reinterpret_cast<T*>(p.out), bh * p.dim + d, acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
