@@ -209,7 +209,26 @@ def calibrate_copy(mib: int):
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
 
 
-def read_ceiling(launches: int = 20):
+def settle_clock(ms: float, buf=None):
+    """Untimed HBM reads (pkv_stream_read over 1 GiB, or `buf`) for at least `ms` of wall
+    time: from idle the GPU's clock takes tens of milliseconds to settle under load."""
+    import torch
+    from paged_kv_cache_133_amd import _lib
+    if ms <= 0:
+        return
+    dev = torch.device("cuda:0")
+    if buf is None:
+        buf = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    call = _lib.prepare_stream_read(buf, sink, 2048)
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
+
+
+def read_ceiling(launches: int = 20, settle_ms: float = 200.0):
     """--read-ceiling: pkv_stream_read (16-byte non-temporal loads, grid-stride) over 0.7,
     1.5 and 4 GB at 1K-16K workgroups, rotating over a 4 GiB buffer so that no launch finds
     its bytes in the 256 MB Infinity Cache, and a torch device copy of 1 GiB; events at the
@@ -221,6 +240,7 @@ def read_ceiling(launches: int = 20):
     total = 4 << 30
     buf = torch.zeros(total, dtype=torch.uint8, device=dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    settle_clock(settle_ms, buf)
     rows = []
     for size in (700_000_000, 1_500_000_000, total):
         size -= size % 4096
@@ -507,6 +527,7 @@ def serving(args):
             bm.decode_step(ids, table=tab, seq_lens=lens)
             step.launch()
 
+        settle_clock(args.settle_ms)
         for _ in range(args.warmup):
             loop_step()
         torch.cuda.synchronize()
@@ -576,7 +597,7 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
     if args.read_ceiling:
-        read_ceiling()
+        read_ceiling(settle_ms=args.settle_ms)
         return
     if args.serving:
         import torch
