@@ -521,6 +521,36 @@ PKV_API int pkv_paged_attn_varlen_ex(void* out, float* lse_out, const void* q,
                              void* stream);
 
 /*
+ * One packed chunk with its cache write folded into the attention pass ("KVCache
+ * Optimization Skill", 3.6: the step's K/V are written by slot, then attention reads the
+ * cached tokens and the new ones; "Paged KV Cache and Packed Sequence", 4.1).  Sequence b's
+ * n_b new rows k_new/v_new[cu_seqlens_q[b] + i] are stored at logical position
+ * pos = seq_lens_kv[b] - n_b + i, slot block_table[b][pos / block_size] * block_size +
+ * pos % block_size (the slot rule of pkv_kv_cache_append with lens_before = seq_lens_kv -
+ * n_b: -1 for pos < 0 or pos >= max_blocks_per_seq * block_size, nothing written for a slot
+ * outside [0, num_blocks * block_size)); the slot goes to slot_mapping_out[cu_seqlens_q[b] + i]
+ * when slot_mapping_out is not NULL.  The attention is pkv_paged_attn_varlen_ex over the
+ * cache after those writes, the new keys read from k_new/v_new instead of back from the
+ * cache.  For valid inputs the result equals pkv_kv_cache_append followed by
+ * pkv_paged_attn_varlen_ex bit for bit (out, lse, both caches, slots), in one launch.
+ *   k_new, v_new [total_q][num_kv_heads][head_dim], q's dtype, 16-byte aligned, distinct
+ *           from the caches
+ *   slot_mapping_out [total_q] int64 or NULL
+ * Other arguments, support and preconditions as for pkv_paged_attn_varlen_ex; the written
+ * slots must not be read as cached keys by any row of the call (distinct positions in
+ * blocks no other sequence reads, as copy on write ensures).
+ */
+PKV_API int pkv_paged_attn_varlen_append(void* out, float* lse_out, const void* q, const void* k_new,
+                                 const void* v_new, const int32_t* cu_seqlens_q,
+                                 const int32_t* seq_lens_kv, void* k_cache, void* v_cache,
+                                 const int32_t* block_table, int32_t batch, int64_t total_q,
+                                 int32_t max_seqlen_q, int32_t max_blocks_per_seq,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int64_t num_blocks, float softmax_scale,
+                                 int32_t causal, int32_t window, int32_t dtype,
+                                 int64_t* slot_mapping_out, void* stream);
+
+/*
  * ---------------------------------------------------------------- block management
  * Host block manager of one cache pool ("Paged KV Cache and Packed Sequence", 2.1-2.2,
  * 5.2 and 5.3).  [host] only: no call touches the GPU.  A manager owns num_blocks

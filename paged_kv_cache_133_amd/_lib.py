@@ -41,7 +41,8 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_runner_launch", "pkv_upload_kernel", "pkv_decode_mtp_workspace_size", "pkv_paged_attn_decode_mtp",
            "pkv_kv_cache_write_int8_mla", "pkv_paged_attn_decode_mla_int8", "pkv_stream_read",
            "pkv_paged_attn_decode_int8_append", "pkv_paged_attn_decode_mla_append",
-           "pkv_gather_read", "pkv_paged_attn_decode_mla_int8_append")
+           "pkv_gather_read", "pkv_paged_attn_decode_mla_int8_append",
+           "pkv_paged_attn_varlen_append")
 
 
 class PagedKVError(RuntimeError):
@@ -115,6 +116,9 @@ def lib() -> ctypes.CDLL:
     L.pkv_paged_attn_varlen_ex.restype = ctypes.c_int
     L.pkv_paged_attn_varlen_ex.argtypes = [p, p, p, p, p, p, p, p, i32, i64, i32, i32, i32, i32,
                                            i32, i32, i64, f32, i32, i32, i32, p]
+    L.pkv_paged_attn_varlen_append.restype = ctypes.c_int
+    L.pkv_paged_attn_varlen_append.argtypes = [p, p, p, p, p, p, p, p, p, p, i32, i64, i32, i32,
+                                               i32, i32, i32, i32, i64, f32, i32, i32, i32, p, p]
     L.pkv_bm_create.restype = p
     L.pkv_bm_create.argtypes = [i64, i32, i32]
     L.pkv_bm_destroy.restype = None
@@ -878,6 +882,56 @@ def prepare_varlen(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, 
                              max_seqlen_q, softmax_scale, causal, out, lse, window)
     return PreparedCall(lib().pkv_paged_attn_varlen_ex, args,
                         (q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, out, lse))
+
+
+def _varlen_append_args(q, k_new, v_new, k_cache, v_cache, block_table, cu_seqlens_q,
+                        seq_lens_kv, max_seqlen_q, softmax_scale, causal, out, lse, window,
+                        slots_out):
+    """Arguments of pkv_paged_attn_varlen_append."""
+    _dev(q, k_new, v_new, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_kv, out, lse,
+         slots_out)
+    T, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (T, hkv, d) or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {q.dtype} tensor of shape {(T, hkv, d)}")
+    if slots_out is not None and (tuple(slots_out.shape) != (T,) or slots_out.dtype != torch.int64):
+        raise ValueError(f"slots_out must be int64 of shape {(T,)}")
+    if out is None:
+        out = torch.empty_like(q)
+    args = (_ptr(out), _ptr(lse), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cu_seqlens_q),
+            _ptr(seq_lens_kv), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            seq_lens_kv.shape[0], T, max_seqlen_q, block_table.shape[1], hq, hkv, d, bs, nb,
+            float(softmax_scale), int(bool(causal)), int(window), _dtype_code(q),
+            _ptr(slots_out), _stream(q.device))
+    return args, out
+
+
+def paged_attn_varlen_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                             k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             block_table: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                             seq_lens_kv: torch.Tensor, max_seqlen_q: int, softmax_scale: float,
+                             causal: bool = True, out: Optional[torch.Tensor] = None,
+                             lse: Optional[torch.Tensor] = None, window: int = 0,
+                             slots_out: Optional[torch.Tensor] = None):
+    """The chunk's cache write folded into the varlen pass (pkv_paged_attn_varlen_append):
+    new rows at positions seq_lens_kv[b] - n_b + i, then attention over every key."""
+    args, out = _varlen_append_args(q, k_new, v_new, k_cache, v_cache, block_table,
+                                    cu_seqlens_q, seq_lens_kv, max_seqlen_q, softmax_scale,
+                                    causal, out, lse, window, slots_out)
+    _check(lib().pkv_paged_attn_varlen_append(*args))
+    return out, lse
+
+
+def prepare_varlen_append(q, k_new, v_new, k_cache, v_cache, block_table, cu_seqlens_q,
+                          seq_lens_kv, max_seqlen_q, softmax_scale, causal=True, out=None,
+                          lse=None, window=0, slots_out=None):
+    args, out = _varlen_append_args(q, k_new, v_new, k_cache, v_cache, block_table,
+                                    cu_seqlens_q, seq_lens_kv, max_seqlen_q, softmax_scale,
+                                    causal, out, lse, window, slots_out)
+    return PreparedCall(lib().pkv_paged_attn_varlen_append, args,
+                        (q, k_new, v_new, k_cache, v_cache, block_table, cu_seqlens_q,
+                         seq_lens_kv, out, lse, slots_out))
 
 
 # ---------------------------------------------------------------------- block management

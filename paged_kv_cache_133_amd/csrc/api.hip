@@ -1117,13 +1117,19 @@ int pkv_paged_attn_varlen(void* out, float* lse_out, const void* q, const int32_
                                     softmax_scale, causal, 0, dtype, stream);
 }
 
-int pkv_paged_attn_varlen_ex(void* out, float* lse_out, const void* q, const int32_t* cu_seqlens_q,
-                             const int32_t* seq_lens_kv, const void* k_cache, const void* v_cache,
-                             const int32_t* block_table, int32_t batch, int64_t total_q,
-                             int32_t max_seqlen_q, int32_t max_blocks_per_seq, int32_t num_q_heads,
-                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                             int64_t num_blocks, float softmax_scale, int32_t causal, int32_t window,
-                             int32_t dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pkv_paged_attn_varlen_ex, and with k_new / v_new given its append form.
+int varlen_impl(void* out, float* lse_out, const void* q, const int32_t* cu_seqlens_q,
+                const int32_t* seq_lens_kv, const void* k_cache, const void* v_cache,
+                const int32_t* block_table, int32_t batch, int64_t total_q,
+                int32_t max_seqlen_q, int32_t max_blocks_per_seq, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int64_t num_blocks, float softmax_scale, int32_t causal, int32_t window,
+                int32_t dtype, const void* k_new, const void* v_new, int64_t* slot_mapping_out,
+                void* stream) {
     if (window < 0) return fail(PKV_ERR_SHAPE, "varlen: window must be >= 0 (0: no window)");
     if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_DTYPE, "varlen: unknown dtype %d", dtype);
     if (batch < 0 || total_q < 0 || max_seqlen_q < 0)
@@ -1147,6 +1153,12 @@ int pkv_paged_attn_varlen_ex(void* out, float* lse_out, const void* q, const int
         return fail(PKV_ERR_NULL, "varlen: NULL pointer argument");
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return fail(PKV_ERR_ALIGN, "varlen: out, q and caches must be 16-byte aligned");
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return fail(PKV_ERR_NULL, "varlen_append: k_new and v_new must both be given");
+    if (k_new && (!aligned16(k_new) || !aligned16(v_new)))
+        return fail(PKV_ERR_ALIGN, "varlen_append: k_new and v_new must be 16-byte aligned");
+    if (k_new && (k_new == k_cache || v_new == v_cache || k_new == v_cache || v_new == k_cache))
+        return fail(PKV_ERR_SHAPE, "varlen_append: the new rows must not be the caches");
     const int tpb = pkv::varlen_tokens_per_block(group);
     const int64_t qblocks = (max_seqlen_q + tpb - 1) / tpb;
     if ((int64_t)num_kv_heads * qblocks * batch > 0x7fffffffLL)
@@ -1173,7 +1185,46 @@ int pkv_paged_attn_varlen_ex(void* out, float* lse_out, const void* q, const int
     p.window = window;
     p.num_blocks = num_blocks;
     p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.k_cache_w = const_cast<void*>(k_cache);
+    p.v_cache_w = const_cast<void*>(v_cache);
+    p.slots_out = slot_mapping_out;
     return hip_status(pkv::launch_varlen(p, head_dim, (hipStream_t)stream), "varlen launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attn_varlen_ex(void* out, float* lse_out, const void* q, const int32_t* cu_seqlens_q,
+                             const int32_t* seq_lens_kv, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, int32_t batch, int64_t total_q,
+                             int32_t max_seqlen_q, int32_t max_blocks_per_seq, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int64_t num_blocks, float softmax_scale, int32_t causal, int32_t window,
+                             int32_t dtype, void* stream) {
+    return varlen_impl(out, lse_out, q, cu_seqlens_q, seq_lens_kv, k_cache, v_cache, block_table, batch,
+                       total_q, max_seqlen_q, max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim,
+                       block_size, num_blocks, softmax_scale, causal, window, dtype, nullptr, nullptr,
+                       nullptr, stream);
+}
+
+int pkv_paged_attn_varlen_append(void* out, float* lse_out, const void* q, const void* k_new,
+                                 const void* v_new, const int32_t* cu_seqlens_q,
+                                 const int32_t* seq_lens_kv, void* k_cache, void* v_cache,
+                                 const int32_t* block_table, int32_t batch, int64_t total_q,
+                                 int32_t max_seqlen_q, int32_t max_blocks_per_seq,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int64_t num_blocks, float softmax_scale,
+                                 int32_t causal, int32_t window, int32_t dtype,
+                                 int64_t* slot_mapping_out, void* stream) {
+    if (batch > 0 && total_q > 0 && max_seqlen_q > 0 && (!k_new || !v_new))
+        return fail(PKV_ERR_NULL, "varlen_append: NULL pointer argument");
+    return varlen_impl(out, lse_out, q, cu_seqlens_q, seq_lens_kv, k_cache, v_cache, block_table, batch,
+                       total_q, max_seqlen_q, max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim,
+                       block_size, num_blocks, softmax_scale, causal, window, dtype, k_new, v_new,
+                       slot_mapping_out, stream);
 }
 
 }  // extern "C"

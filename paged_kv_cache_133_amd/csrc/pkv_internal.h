@@ -264,6 +264,10 @@ struct MfmaParams {
     const void* rope_new;
     void* k_cache_w;
     void* rope_w;
+    // Varlen append (else null): the step's new K/V rows [T][Hkv][D] (v_new), attended at
+    // positions seq_lens[b] - n_b + i and written there through k_cache_w / v_cache_w.
+    const void* v_new;
+    void* v_cache_w;
     float* k_scale_w;
     float* r_scale_w;
     int64_t* slots_out;      // [B] or null

@@ -15,6 +15,12 @@
 //    applied only when a row's max grows by more than 2^8 (P <= 256 in between), which
 //    after the first tiles almost never happens.  Tiles that every row of the workgroup
 //    sees whole skip the masking.
+// Append mode (the chunk's cache write folded into the pass, "KVCache Optimization Skill",
+// 3.6: write by slot, then attend over the cached tokens and the new ones): the n_b new
+// K/V rows of sequence b sit at positions seq_lens[b] - n_b + i; every workgroup reads
+// keys from there on out of the new rows themselves (their packed rows have the cache
+// slot's row layout), and the workgroup of a query block stores its tokens' rows of its
+// kv head at their slots, which no workgroup of the launch reads back.
 #include "mfma_common.h"
 
 namespace pkv {
@@ -41,8 +47,8 @@ struct VarCfg {
     static_assert(kDma * 1024 * kWaves == kStage, "tile");
 };
 
-template <int D>
-__global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams p) {
+template <int D, bool APPEND>
+__device__ __forceinline__ void varlen_body(const MfmaParams& p) {
     using C = VarCfg<D>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::kSmem];
 
@@ -61,9 +67,10 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
     int b, qb;
     {
         int j;
+        // (append mode: a sequence with new rows but no visible key still stores its slots)
         auto qblocks = [&](int s, int len) {
             const int n = p.cu_q[s + 1] - p.cu_q[s];
-            return (n > 0 && len > 0) ? (n + tpb - 1) / tpb : 0;
+            return (n > 0 && (APPEND || len > 0)) ? (n + tpb - 1) / tpb : 0;
         };
         if (!find_item<C::kThreads>(blockIdx.x / p.hkv, p.batch, p.seq_lens, p.len_cap, qblocks,
                                     reinterpret_cast<int32_t*>(smem + kStages * C::kStage), b, j))
@@ -75,7 +82,77 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
     const int nq = p.cu_q[b + 1] - q0;
     const int L = min(p.seq_lens[b], p.len_cap);
     const int i_first = qb * tpb;
-    if (i_first >= nq || nq <= 0 || L <= 0) return;
+    if (i_first >= nq || nq <= 0) return;
+    const uint32_t row_bytes = (uint32_t)(p.hkv * D * 2);             // one cache slot
+    // Append mode: new keys start at new_start (seq_lens[b] - n_b, before the length bound);
+    // this workgroup stores the rows of its tokens for its kv head (slot rule of
+    // pkv_kv_cache_append: no slot past the table's capacity, none outside the pool).
+    // The first kWrDefer 16-byte pieces of each thread go by direct loads into the last
+    // tile stage (free until the loop issues its first load there) and are stored once
+    // the query rows are in, so that their latency hides under the query loads; any
+    // further pieces (fewer than four query heads per kv head: more tokens per
+    // workgroup) are copied at once.
+    const int new_start = APPEND ? p.seq_lens[b] - nq : INT_MAX;
+    constexpr int kWrDefer = C::kStage / 16 / C::kThreads;
+    constexpr int kRowChunks = D * 2 / 16;
+    constexpr int kRowsPerPass = C::kThreads / kRowChunks;
+    uint8_t* const wr_buf = smem + (kStages - 1) * C::kStage;
+    int32_t wr_entry[kWrDefer];       // staged piece d: its block-table entry (read now, used later)
+    const int wr_rows = APPEND ? 2 * min(nq - i_first, tpb) : 0;
+    const int bs_mask_w = (1 << p.bs_log2) - 1;
+    // Piece k of this thread: row r = tid / kRowChunks + k kRowsPerPass (K of token
+    // i_first + r / 2 if r is even, else V), 16 bytes at chunk tid % kRowChunks.
+    auto piece_pos = [&](int r) { return (int64_t)new_start + i_first + (r >> 1); };
+    auto piece_off = [&]() { return (int64_t)kvh * D * 2 + (tid % kRowChunks) * 16; };
+    auto piece_src = [&](int r) {
+        return reinterpret_cast<const uint8_t*>((r & 1) ? p.v_new : p.k_new) + (int64_t)(q0 + i_first + (r >> 1)) * row_bytes + piece_off();
+    };
+    // The slot of a piece (the rule of pkv_kv_cache_append) from its table entry; the
+    // kv head 0 workgroup reports it for K pieces of chunk 0, and stores outside the pool
+    // are skipped.
+    auto piece_store = [&](int r, int32_t entry, const u32x4& val) {
+        const int64_t pos = piece_pos(r);
+        const int64_t slot = (pos >= 0 && pos < p.len_cap) ? (((int64_t)entry << p.bs_log2) | (pos & bs_mask_w)) : -1;
+        if ((r & 1) == 0 && kvh == 0 && tid % kRowChunks == 0 && p.slots_out) p.slots_out[q0 + i_first + (r >> 1)] = slot;
+        if (slot < 0 || slot >= (p.num_blocks << p.bs_log2)) return;
+        st16(reinterpret_cast<uint8_t*>((r & 1) ? p.v_cache_w : p.k_cache_w) + slot * row_bytes + piece_off(), val);
+    };
+    auto piece_entry = [&](int r) -> int32_t {
+        const int64_t pos = piece_pos(r);
+        return (pos >= 0 && pos < p.len_cap) ? p.table[(int64_t)b * p.mbs + (pos >> p.bs_log2)] : 0;
+    };
+    if constexpr (APPEND) {
+#pragma unroll
+        for (int d = 0; d < kWrDefer; ++d) {
+            const int r = tid / kRowChunks + d * kRowsPerPass;
+            wr_entry[d] = 0;
+            if (r < wr_rows) {
+                lds_dma16(piece_src(r), wr_buf + (d * C::kThreads + (tid & ~63)) * 16);
+                wr_entry[d] = piece_entry(r);
+            }
+        }
+        for (int r = tid / kRowChunks + kWrDefer * kRowsPerPass; r < wr_rows; r += kRowsPerPass)
+            piece_store(r, piece_entry(r), ld16(piece_src(r)));
+    }
+    // The staged pieces to their slots (after a wait for the direct loads and a barrier).
+    auto store_staged = [&]() {
+        if constexpr (APPEND) {
+#pragma unroll
+            for (int d = 0; d < kWrDefer; ++d) {
+                const int r = tid / kRowChunks + d * kRowsPerPass;
+                if (r < wr_rows)
+                    piece_store(r, wr_entry[d], *reinterpret_cast<const u32x4*>(wr_buf + (d * C::kThreads + tid) * 16));
+            }
+        }
+    };
+    if (L <= 0) {
+        if constexpr (APPEND) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            block_sync();
+            store_staged();
+        }
+        return;
+    }
     const int i_last = min(nq, i_first + tpb) - 1;
     const int i = i_first + wid * tw + lrow / G;
     const bool valid = (lrow < tw * G) && (i < nq);
@@ -117,13 +194,13 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
     // them, placed inside the loop, would also wait for the tile loads issued there.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     block_sync();
+    store_staged();
 
     // Loads of one tile: wave load J = wid * kDma + j fills LDS slots 64 J .. 64 J + 63
     // of the stage; the first half of the stage is the K tile, the second the V tile.
     // Slot q of a half is row q / kRowChunks, physical chunk q % kRowChunks, which holds
     // logical chunk swz(row, physical chunk) of that row.
     const int bs_mask = (1 << p.bs_log2) - 1;
-    const uint32_t row_bytes = (uint32_t)(p.hkv * D * 2);             // one cache slot
     const uint32_t block_bytes = row_bytes << p.bs_log2;
     const bool v_part = wid >= C::kWaves / 2;                         // uniform per wave
     const uint8_t* cache = reinterpret_cast<const uint8_t*>(v_part ? p.v_cache : p.k_cache) + kvh * D * 2;
@@ -133,6 +210,8 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
     const int wid_u = __builtin_amdgcn_readfirstlane(wid);
     const bool fast_rows = p.bs_log2 >= 4;
     const uint8_t* cache_u = reinterpret_cast<const uint8_t*>(wid_u >= C::kWaves / 2 ? p.v_cache : p.k_cache) + kvh * D * 2;
+    // append mode: this kv head's slice of the new rows of the wave's half (K or V)
+    const uint8_t* new_u = reinterpret_cast<const uint8_t*>(wid_u >= C::kWaves / 2 ? p.v_new : p.k_new) + kvh * D * 2;
     uint32_t fast_voff[C::kDma];
 #pragma unroll
     for (int j = 0; j < C::kDma; ++j) {
@@ -142,7 +221,14 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
                        (uint32_t)swz<C::kRowChunks, C::kRowShift>(r, q % C::kRowChunks) * 16u;
     }
     // The table entry of the next tile is read one tile ahead, off the critical path.
-    auto fast_tile = [&](int u) { return fast_rows && kstart + (u + 1) * kKeys <= k_end; };
+    // Append mode: a full tile of new keys is 32 consecutive new rows (one base, the same
+    // lane offsets); a tile with both kinds of key takes the per-row path.
+    auto fast_tile = [&](int u) {
+        return fast_rows && kstart + (u + 1) * kKeys <= k_end && !(APPEND && kstart + (u + 1) * kKeys > new_start);
+    };
+    auto new_tile = [&](int u) {
+        return APPEND && kstart + u * kKeys >= new_start && kstart + (u + 1) * kKeys <= k_end;
+    };
     auto entry_of = [&](int u) { return uniform_load(tab.row + ((kstart + u * kKeys + 16 * (wid_u & 1)) >> p.bs_log2)); };
     int32_t next_entry = fast_tile(0) ? entry_of(0) : 0;
     auto issue_tile = [&](int u) {
@@ -160,6 +246,13 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
             for (int j = 0; j < C::kDma; ++j) lds_dma16_s(sb, fast_voff[j], stage + (wid_u * C::kDma + j) * 1024);
             return;
         }
+        if (new_tile(u)) {
+            const int key0 = kb + 16 * (wid_u & 1);
+            const uint8_t* sb = new_u + (int64_t)(q0 + key0 - new_start) * row_bytes;
+#pragma unroll
+            for (int j = 0; j < C::kDma; ++j) lds_dma16_s(sb, fast_voff[j], stage + (wid_u * C::kDma + j) * 1024);
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < C::kDma; ++j) {
             const int J = wid * C::kDma + j;
@@ -170,6 +263,9 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
             const uint32_t blk = tab.block_of(key, chunk);
             const uint8_t* src = cache + ((uint64_t)blk * block_bytes +
                                           (uint32_t)(key & bs_mask) * row_bytes + (uint32_t)c * 16u);
+            if (APPEND && key >= new_start)
+                src = reinterpret_cast<const uint8_t*>(v_part ? p.v_new : p.k_new) + kvh * D * 2 +
+                      (int64_t)(q0 + key - new_start) * row_bytes + c * 16;
             lds_dma16(src, stage + J * 1024);
         }
     };
@@ -337,14 +433,30 @@ __global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams 
     if (p.lse && lhalf == 0) p.lse[out_row] = l_tot > 0.0f ? (st.m + __log2f(l_tot)) * kLn2f : -INFINITY;
 }
 
+// The plain pass, and the append pass held to two waves per SIMD (its writes' registers
+// would otherwise take it past 256 and halve the waves per SIMD).
+template <int D>
+__global__ __launch_bounds__(VarCfg<D>::kThreads) void varlen_kernel(MfmaParams p) {
+    varlen_body<D, false>(p);
+}
+template <int D>
+__global__ __launch_bounds__(VarCfg<D>::kThreads, 2) void varlen_append_kernel(MfmaParams p) {
+    varlen_body<D, true>(p);
+}
+
 }  // namespace
 
 int32_t varlen_tokens_per_block(int32_t group) { return VarCfg<128>::kWaves * (32 / group); }
 
 hipError_t launch_varlen(const MfmaParams& p, int head_dim, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)p.hkv * p.q_blocks * p.batch));
-    if (head_dim == 64) hipLaunchKernelGGL(varlen_kernel<64>, grid, dim3(VarCfg<64>::kThreads), 0, s, p);
-    else hipLaunchKernelGGL(varlen_kernel<128>, grid, dim3(VarCfg<128>::kThreads), 0, s, p);
+    if (p.k_new) {
+        if (head_dim == 64) hipLaunchKernelGGL(varlen_append_kernel<64>, grid, dim3(VarCfg<64>::kThreads), 0, s, p);
+        else hipLaunchKernelGGL(varlen_append_kernel<128>, grid, dim3(VarCfg<128>::kThreads), 0, s, p);
+    } else {
+        if (head_dim == 64) hipLaunchKernelGGL(varlen_kernel<64>, grid, dim3(VarCfg<64>::kThreads), 0, s, p);
+        else hipLaunchKernelGGL(varlen_kernel<128>, grid, dim3(VarCfg<128>::kThreads), 0, s, p);
+    }
     return hipGetLastError();
 }
 
