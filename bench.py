@@ -165,7 +165,7 @@ def algorithmic_flops(case):
     return pairs * w.num_q_heads * 2 * (w.head_dim + w.head_dim_rope + w.head_dim_v)
 
 
-def algorithmic_bytes(case):
+def algorithmic_bytes(case, path="fused"):
     """(kv_read, split_kernel, step) algorithmic bytes of one step."""
     w = case.w
     e = w.elem_bytes
@@ -194,6 +194,10 @@ def algorithmic_bytes(case):
     out_bytes = T * w.num_q_heads * w.head_dim_v * e
     table = 4 * int((-(-Lp // w.block_size)).sum())
     split = kv + q_bytes + out_bytes + table + 4 * B
+    if w.mode == "varlen" and path == "fused":
+        # the fused pass also stores the chunk's new rows (its reads of them replace cache
+        # reads already counted in kv); the decode passes' one row per sequence is left out
+        split += new_rows
     # slot_mapping: table entry, L_b, cu; slot written; write: new rows read + written
     step = split + 2 * new_rows + 4 * B * 3 + 8 * T
     return kv, split, step
@@ -622,7 +626,7 @@ def main():
     w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     case = wl.make_workload_case(w, seed=args.seed, device=dev)
-    kv_bytes, split_bytes, step_bytes = algorithmic_bytes(case)
+    kv_bytes, split_bytes, step_bytes = algorithmic_bytes(case, args.path)
     int8 = w.kv_dtype == "int8"
     if int8 and w.mode == "mla":
         # The INT8 latent pools: nope and rope rows of the bf16 pools quantized by the writer.
