@@ -442,6 +442,9 @@ def step_description(w, path):
         return ("slot_mapping, kv_cache_write_int8 (quantizing write), decode_int8 %s pass, combine"
                 % ("range" if ranges else "split"))
     if w.q_tokens:
+        if path == "fused":
+            return ("paged_attn_decode_mtp_append: range pass that also writes the step's %d rows "
+                    "per sequence (slot_mapping + write + attention), then combine" % w.q_tokens)
         return ("kv_cache_append (slot_mapping + write of the step's %d rows per sequence), "
                 "decode_mtp range pass, combine" % w.q_tokens)
     if w.mode == "varlen":
@@ -726,6 +729,14 @@ def main():
         else:
             v = case.cache_v if r == 0 else case.cache_v.clone()
             pair = (case.new_k, case.new_v, k, v)
+        if w.q_tokens and fused:
+            attn, combine, _ = _lib.prepare_decode_mtp_append(case.q, case.new_k, case.new_v, k, v,
+                                                              table, la, w.q_tokens,
+                                                              case.max_len_after, w.scale, out=out,
+                                                              lse=lse, workspace=ws_mtp,
+                                                              window=w.window, slots_out=slots)
+            reps.append((None, attn, combine))
+            continue
         if w.q_tokens:
             write = _lib.prepare_kv_cache_append(*pair, table, lb, cu, case.max_new, slots)
             attn, combine, _ = _lib.prepare_decode_mtp(case.q, k, v, table, la, w.q_tokens,

@@ -510,6 +510,30 @@ PKV_API int pkv_paged_attn_decode_mtp(void* out, float* lse_out, const void* q,
                                       int32_t stages, void* workspace, size_t workspace_bytes,
                                       void* stream);
 
+/*
+ * MTP decode with the step's cache write folded into the pass ("KVCache Optimization
+ * Skill", 3.6 and Appendix E): sequence b's num_q_tokens new K/V rows
+ * k_new/v_new[b * num_q_tokens + i] are stored at positions seq_lens_kv[b] - num_q_tokens + i
+ * (the query tokens' own positions) and read from k_new/v_new by the attention, which is
+ * pkv_paged_attn_decode_mtp over the cache after those writes; for valid inputs, equal bit
+ * for bit to pkv_kv_cache_append (lens_before = seq_lens_kv - num_q_tokens) followed by
+ * pkv_paged_attn_decode_mtp, in one attention launch.  The slot of row b * num_q_tokens + i
+ * goes to slot_mapping_out[b * num_q_tokens + i] when it is not NULL; a sequence longer
+ * than max_seq_len_kv writes nothing (slots -1), as for pkv_paged_attn_decode_append.
+ *   k_new, v_new [batch * num_q_tokens][num_kv_heads][head_dim], 16-byte aligned
+ * stages (1 the range pass with the writes, 2 the combine, 3 both), workspace, support and
+ * other preconditions as for pkv_paged_attn_decode_mtp.
+ */
+PKV_API int pkv_paged_attn_decode_mtp_append(void* out, float* lse_out, const void* q, const void* k_new,
+                                     const void* v_new, void* k_cache, void* v_cache,
+                                     const int32_t* block_table, const int32_t* seq_lens_kv,
+                                     int32_t batch, int32_t num_q_tokens, int32_t max_blocks_per_seq,
+                                     int32_t max_seq_len_kv, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int64_t num_blocks, float softmax_scale, int32_t dtype,
+                                     int32_t window, int32_t stages, void* workspace,
+                                     size_t workspace_bytes, int64_t* slot_mapping_out, void* stream);
+
 /* pkv_paged_attn_varlen with the window (causal or not: hi = the row's last visible key). */
 PKV_API int pkv_paged_attn_varlen_ex(void* out, float* lse_out, const void* q,
                              const int32_t* cu_seqlens_q, const int32_t* seq_lens_kv,

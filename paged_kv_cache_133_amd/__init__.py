@@ -12,5 +12,6 @@ from ._lib import (BlockManager, CapturedStep, PagedKVError, decode_workspace_si
                    paged_attn_decode_int8, paged_attn_decode_int8_append, paged_attn_decode_append,
                    paged_attn_decode_mla_append,
                    paged_attn_decode_append_noalloc, paged_attn_decode_mtp,
+                   paged_attn_decode_mtp_append,
                    paged_attn_varlen, paged_attn_varlen_append,
                    slot_mapping, upload, version)

@@ -42,7 +42,7 @@ EXPORTS = ("pkv_version", "pkv_last_error", "pkv_slot_mapping", "pkv_kv_cache_wr
            "pkv_kv_cache_write_int8_mla", "pkv_paged_attn_decode_mla_int8", "pkv_stream_read",
            "pkv_paged_attn_decode_int8_append", "pkv_paged_attn_decode_mla_append",
            "pkv_gather_read", "pkv_paged_attn_decode_mla_int8_append",
-           "pkv_paged_attn_varlen_append")
+           "pkv_paged_attn_varlen_append", "pkv_paged_attn_decode_mtp_append")
 
 
 class PagedKVError(RuntimeError):
@@ -165,6 +165,10 @@ def lib() -> ctypes.CDLL:
     L.pkv_paged_attn_decode_mtp.restype = ctypes.c_int
     L.pkv_paged_attn_decode_mtp.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
                                             i32, i32, i64, f32, i32, i32, i32, p, sz, p]
+    L.pkv_paged_attn_decode_mtp_append.restype = ctypes.c_int
+    L.pkv_paged_attn_decode_mtp_append.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
+                                                   i32, i32, i32, i32, i64, f32, i32, i32, i32, p,
+                                                   sz, p, p]
     L.pkv_runner_create.restype = p
     L.pkv_runner_create.argtypes = [p, p, p, p, sz]
     L.pkv_runner_destroy.restype = ctypes.c_int
@@ -845,6 +849,55 @@ def prepare_decode_mtp(q, k_cache, v_cache, block_table, seq_lens_kv, num_q_toke
         calls.append(PreparedCall(lib().pkv_paged_attn_decode_mtp, args,
                                   (q, k_cache, v_cache, block_table, seq_lens_kv, out, lse,
                                    workspace)))
+    return calls[0], calls[1], out
+
+
+def _decode_mtp_append_args(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
+                            num_q_tokens, max_seq_len_kv, softmax_scale, stages, out, lse,
+                            workspace, window, slots_out):
+    """Arguments of pkv_paged_attn_decode_mtp_append."""
+    args, out, workspace = _decode_mtp_args(q, k_cache, v_cache, block_table, seq_lens_kv,
+                                            num_q_tokens, max_seq_len_kv, softmax_scale, stages,
+                                            out, lse, workspace, window)
+    _dev(k_new, v_new, slots_out)
+    rows = q.shape[0]
+    hkv, d = k_cache.shape[2], k_cache.shape[3]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (rows, hkv, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a {q.dtype} tensor of shape {(rows, hkv, d)}")
+    if slots_out is not None and (tuple(slots_out.shape) != (rows,) or slots_out.dtype != torch.int64):
+        raise ValueError(f"slots_out must be int64 of shape {(rows,)}")
+    # (out, lse, q, k_cache, v_cache, table, lens, ...) -> (out, lse, q, k_new, v_new, k_cache, ...)
+    args = args[:3] + (_ptr(k_new), _ptr(v_new)) + args[3:-1] + (_ptr(slots_out), args[-1])
+    return args, out, workspace
+
+
+def paged_attn_decode_mtp_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
+                                 num_q_tokens, max_seq_len_kv, softmax_scale, out=None, lse=None,
+                                 workspace=None, window=0, slots_out=None):
+    """MTP decode with the step's rows written in the pass (pkv_paged_attn_decode_mtp_append);
+    k_new, v_new [batch * num_q_tokens][Hkv][D].  Returns (out, lse)."""
+    args, out, _ = _decode_mtp_append_args(q, k_new, v_new, k_cache, v_cache, block_table,
+                                           seq_lens_kv, num_q_tokens, max_seq_len_kv,
+                                           softmax_scale, 3, out, lse, workspace, window, slots_out)
+    _check(lib().pkv_paged_attn_decode_mtp_append(*args))
+    return out, lse
+
+
+def prepare_decode_mtp_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
+                              num_q_tokens, max_seq_len_kv, softmax_scale, out=None, lse=None,
+                              workspace=None, window=0, slots_out=None):
+    """(range pass with the writes, combine pass) prepared calls of
+    pkv_paged_attn_decode_mtp_append."""
+    calls = []
+    for stages in (1, 2):
+        args, out, workspace = _decode_mtp_append_args(q, k_new, v_new, k_cache, v_cache,
+                                                       block_table, seq_lens_kv, num_q_tokens,
+                                                       max_seq_len_kv, softmax_scale, stages, out,
+                                                       lse, workspace, window, slots_out)
+        calls.append(PreparedCall(lib().pkv_paged_attn_decode_mtp_append, args,
+                                  (q, k_new, v_new, k_cache, v_cache, block_table, seq_lens_kv,
+                                   out, lse, workspace, slots_out)))
     return calls[0], calls[1], out
 
 

@@ -823,14 +823,16 @@ size_t pkv_decode_mtp_workspace_size(int32_t batch, int32_t num_q_tokens, int32_
                             num_q_tokens).ws_bytes;
 }
 
-int pkv_paged_attn_decode_mtp(void* out, float* lse_out, const void* q, const void* k_cache,
-                              const void* v_cache, const int32_t* block_table,
-                              const int32_t* seq_lens_kv, int32_t batch, int32_t num_q_tokens,
-                              int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
-                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                              int32_t block_size, int64_t num_blocks, float softmax_scale,
-                              int32_t dtype, int32_t window, int32_t stages, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+// pkv_paged_attn_decode_mtp, and with k_new / v_new given its append form.
+static int mtp_impl(void* out, float* lse_out, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* block_table,
+                    const int32_t* seq_lens_kv, int32_t batch, int32_t num_q_tokens,
+                    int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int64_t num_blocks, float softmax_scale,
+                    int32_t dtype, int32_t window, int32_t stages, void* workspace,
+                    size_t workspace_bytes, const void* k_new, const void* v_new,
+                    int64_t* slot_mapping_out, void* stream) {
     if (stages < 1 || stages > 3) return fail(PKV_ERR_SHAPE, "decode_mtp: stages must be 1, 2 or 3");
     if (num_q_tokens < 1) return fail(PKV_ERR_SHAPE, "decode_mtp: num_q_tokens must be >= 1");
     if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
@@ -856,6 +858,18 @@ int pkv_paged_attn_decode_mtp(void* out, float* lse_out, const void* q, const vo
                             num_kv_heads, head_dim, head_dim, 0, block_size, num_blocks, softmax_scale,
                             dtype, workspace, workspace_bytes, &idle, window, true, false, num_q_tokens);
     if (rc != PKV_OK || idle) return rc;
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return fail(PKV_ERR_NULL, "decode_mtp_append: k_new and v_new must both be given");
+    if (k_new) {
+        if (!aligned16(k_new) || !aligned16(v_new))
+            return fail(PKV_ERR_ALIGN, "decode_mtp_append: k_new and v_new must be 16-byte aligned");
+        if (k_cache == v_cache) return fail(PKV_ERR_SHAPE, "decode_mtp_append: k_cache and v_cache must differ");
+        p.k_new = k_new;
+        p.v_new = v_new;
+        p.k_cache_w = const_cast<void*>(k_cache);
+        p.v_cache_w = const_cast<void*>(v_cache);
+        p.slots_out = slot_mapping_out;
+    }
     hipStream_t s = (hipStream_t)stream;
     if (stages & 1) {
         rc = hip_status(pkv::launch_gqa_decode(p, head_dim, s), "decode_mtp launch");
@@ -863,6 +877,36 @@ int pkv_paged_attn_decode_mtp(void* out, float* lse_out, const void* q, const vo
     }
     if ((stages & 2) && needs_combine(p, plan)) return launch_combine_for(p, head_dim, dtype, s);
     return PKV_OK;
+}
+
+int pkv_paged_attn_decode_mtp(void* out, float* lse_out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens_kv, int32_t batch, int32_t num_q_tokens,
+                              int32_t max_blocks_per_seq, int32_t max_seq_len_kv,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int64_t num_blocks, float softmax_scale,
+                              int32_t dtype, int32_t window, int32_t stages, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    return mtp_impl(out, lse_out, q, k_cache, v_cache, block_table, seq_lens_kv, batch, num_q_tokens,
+                    max_blocks_per_seq, max_seq_len_kv, num_q_heads, num_kv_heads, head_dim, block_size,
+                    num_blocks, softmax_scale, dtype, window, stages, workspace, workspace_bytes, nullptr,
+                    nullptr, nullptr, stream);
+}
+
+int pkv_paged_attn_decode_mtp_append(void* out, float* lse_out, const void* q, const void* k_new,
+                                     const void* v_new, void* k_cache, void* v_cache,
+                                     const int32_t* block_table, const int32_t* seq_lens_kv,
+                                     int32_t batch, int32_t num_q_tokens, int32_t max_blocks_per_seq,
+                                     int32_t max_seq_len_kv, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int64_t num_blocks, float softmax_scale, int32_t dtype,
+                                     int32_t window, int32_t stages, void* workspace,
+                                     size_t workspace_bytes, int64_t* slot_mapping_out, void* stream) {
+    if (batch > 0 && (!k_new || !v_new)) return fail(PKV_ERR_NULL, "decode_mtp_append: NULL pointer argument");
+    return mtp_impl(out, lse_out, q, k_cache, v_cache, block_table, seq_lens_kv, batch, num_q_tokens,
+                    max_blocks_per_seq, max_seq_len_kv, num_q_heads, num_kv_heads, head_dim, block_size,
+                    num_blocks, softmax_scale, dtype, window, stages, workspace, workspace_bytes, k_new,
+                    v_new, slot_mapping_out, stream);
 }
 
 int pkv_kv_cache_write_int8_mla(const void* kv_nope, const void* k_rope, void* nope_codes,

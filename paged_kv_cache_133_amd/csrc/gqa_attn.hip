@@ -208,29 +208,35 @@ __device__ __forceinline__ void store_empty(const DecodeParams& p, int64_t row, 
     if (p.lse && g == 0) p.lse[row] = -INFINITY;
 }
 
-// The kv head's slice of sequence b's new K and V rows to its slot (append mode), by the
-// first 2 kRowChunks lanes.
-// A row longer than the length bound (a broken precondition) appends nothing: its slot is
-// reported as -1 (the lookup of the new key, `new_key`, then never matches either).
+// The kv head's slices of sequence b's qn new K and V rows (rows b qn + i of k_new / v_new,
+// positions L - qn + i) to their slots (append mode), by the first 2 kRowChunks lanes.
+// A row longer than the length bound (a broken precondition) appends nothing: its slots are
+// reported as -1 (the lookups of the new keys, from `new_key` on, then never match either).
 template <int D>
-__device__ __forceinline__ void append_row(const DecodeParams& p, int b, int kvh, int L, int lane) {
+__device__ __forceinline__ void append_row(const DecodeParams& p, int b, int kvh, int L, int lane, int qn = 1) {
     using C = GqaCfg<D>;
     if (uniform_load(p.seq_lens + b) > p.len_cap) {
-        if (p.slots_out && kvh == 0 && lane == 0) p.slots_out[b] = -1;
+        if (p.slots_out && kvh == 0 && lane < qn) p.slots_out[(int64_t)b * qn + lane] = -1;
         return;
     }
     if (lane >= 2 * C::kRowChunks) return;
     const int32_t* trow = p.table + (int64_t)b * p.mbs;
-    const int32_t phys = min(max(trow[(L - 1) >> p.bs_log2], 0), (int32_t)(p.num_blocks - 1));
-    const int64_t slot = ((int64_t)phys << p.bs_log2) | ((L - 1) & ((1 << p.bs_log2) - 1));
     const int which = lane / C::kRowChunks;
     const int64_t off = (int64_t)(lane % C::kRowChunks) * 16;
-    const int64_t new_off = ((int64_t)b * p.hkv + kvh) * D * 2;
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(which ? p.v_new : p.k_new) + new_off;
-    uint8_t* dst = reinterpret_cast<uint8_t*>(which ? p.v_cache_w : p.k_cache_w) + slot * (int64_t)p.hkv * D * 2 +
-                   (int64_t)kvh * D * 2;
-    st16(dst + off, ld16(src + off));
-    if (p.slots_out && kvh == 0 && lane == 0) p.slots_out[b] = slot;
+    for (int i = 0; i < qn; ++i) {
+        const int pos = L - qn + i;
+        int64_t slot = -1;
+        if (pos >= 0) {
+            const int32_t phys = min(max(trow[pos >> p.bs_log2], 0), (int32_t)(p.num_blocks - 1));
+            slot = ((int64_t)phys << p.bs_log2) | (pos & ((1 << p.bs_log2) - 1));
+            const int64_t new_off = (((int64_t)b * qn + i) * p.hkv + kvh) * D * 2;
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(which ? p.v_new : p.k_new) + new_off;
+            uint8_t* dst = reinterpret_cast<uint8_t*>(which ? p.v_cache_w : p.k_cache_w) +
+                           slot * (int64_t)p.hkv * D * 2 + (int64_t)kvh * D * 2;
+            st16(dst + off, ld16(src + off));
+        }
+        if (p.slots_out && kvh == 0 && lane == 0) p.slots_out[(int64_t)b * qn + i] = slot;
+    }
 }
 
 // INT8 form: the kv head's slices of the new bf16 K and V rows quantized as the writer does
@@ -325,15 +331,16 @@ __device__ __forceinline__ int range_of(int x, int T, int P) { return (int)(((in
 struct Cursor {
     int b, pre, end, L, ks, ksa, seg;
     int ks_last;                      // first key the last query token sees (>= ks)
-    int new_key;                      // append mode: key read from the new rows (L - 1), else INT_MAX
+    int new_key;                      // append mode: first key read from the new rows (L - qn), else INT_MAX
 };
 
-// Append mode: the key of sequence b that comes from the new rows, L - 1, unless the row is
-// longer than the length bound; INT_MAX (no key) otherwise and outside append mode.
+// Append mode: the first key of sequence b that comes from the new rows, L - qn (qn new
+// rows per sequence: 1 for decode), unless the row is longer than the length bound; INT_MAX
+// (no key) otherwise and outside append mode.
 template <bool APPEND>
-__device__ __forceinline__ int new_key_of(const DecodeParams& p, int b, int L) {
+__device__ __forceinline__ int new_key_of(const DecodeParams& p, int b, int L, int qn = 1) {
     if (!APPEND) return INT_MAX;
-    return uniform_load(p.seq_lens + b) <= p.len_cap ? L - 1 : INT_MAX;
+    return uniform_load(p.seq_lens + b) <= p.len_cap ? L - qn : INT_MAX;
 }
 
 template <int D, bool APPEND, bool I8 = false, bool COMPACT = I8>
@@ -406,7 +413,8 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
             const int e = s_pre[b + 1];
             empty = lane_len(b) <= 0;
             mine = e > s_pre[b] && e - 1 >= x0 && e - 1 < x1;
-            if (APPEND && empty && p.slots_out && w == 0 && kvh == 0) p.slots_out[b] = -1;
+            if (APPEND && empty && p.slots_out && w == 0 && kvh == 0)
+                for (int i = 0; i < qn; ++i) p.slots_out[(int64_t)b * qn + i] = -1;
         }
         uint64_t em = w == 0 ? __ballot(empty) : 0ull;
         while (em) {
@@ -420,7 +428,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
                 const int bb = c0 + __builtin_ctzll(mm);
                 mm &= mm - 1;
                 if constexpr (I8) append_row_i8<D>(p, bb, kvh, uni_len(bb), lane);
-                else append_row<D>(p, bb, kvh, uni_len(bb), lane);
+                else append_row<D>(p, bb, kvh, uni_len(bb), lane, qn);
             }
         }
     }
@@ -450,7 +458,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         c.ks_last = window_start(c.L, p.window);
         c.ksa = c.ks & ~(kKeys - 1);
         c.seg = 0;
-        c.new_key = new_key_of<APPEND>(p, b, c.L);
+        c.new_key = new_key_of<APPEND>(p, b, c.L, qn);
         return c;
     };
     // Move c to the sequence that holds tile x (x never moves back).
@@ -465,7 +473,7 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
         c.ks = window_start(c.L - qn + 1, p.window);
         c.ks_last = window_start(c.L, p.window);
         c.ksa = c.ks & ~(kKeys - 1);
-        c.new_key = new_key_of<APPEND>(p, c.b, c.L);
+        c.new_key = new_key_of<APPEND>(p, c.b, c.L, qn);
         ++c.seg;
     };
 
@@ -609,7 +617,8 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
             }
             return;
         }
-        if (x + 1 < ic.end) {         // full tile: SGPR base per wave load, constant lane offsets
+        // full tile with no new key: SGPR base per wave load, constant lane offsets
+        if (x + 1 < ic.end && !(APPEND && kb + kKeys > ic.new_key)) {
 #pragma unroll
             for (int j = 0; j < C::kDmaHalf; ++j) {
                 const uint32_t blk = (uint32_t)min(max(pe[j], 0), last_block);
@@ -618,10 +627,9 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
                 lds_dma16_s(kbase + off, voff, stage + j * 1024);
                 lds_dma16_s(vbase + off, voff, stage + C::kHalf + j * 1024);
             }
-        } else {                      // last tile of its sequence: rows past the end re-read the last key
+        } else {                      // last tile (or one with new keys): rows past the end re-read the last key
             const int L = ic.L;
             const int64_t last_slot = ((int64_t)min(max(pe_last, 0), last_block) << p.bs_log2) | ((L - 1) & bs_mask);
-            const int64_t new_off = ((int64_t)ic.b * p.hkv + kvh) * D * 2;
 #pragma unroll
             for (int j = 0; j < C::kDmaHalf; ++j) {
                 const int key = kb + j * C::kRpi + lrow;
@@ -629,7 +637,8 @@ __global__ __launch_bounds__(64) void gqa_stream_kernel(DecodeParams p) {
                                              : last_slot;
                 const uint8_t* ks = kbase + slot * row_bytes + lchunk[j];
                 const uint8_t* vs = vbase + slot * row_bytes + lchunk[j];
-                if (APPEND && key >= ic.new_key) {
+                if (APPEND && key >= ic.new_key) {   // new row b qn + (key - new_key), the last for keys past the end
+                    const int64_t new_off = (((int64_t)ic.b * qn + (min(key, L - 1) - ic.new_key)) * p.hkv + kvh) * D * 2;
                     ks = reinterpret_cast<const uint8_t*>(p.k_new) + new_off + lchunk[j];
                     vs = reinterpret_cast<const uint8_t*>(p.v_new) + new_off + lchunk[j];
                 }
