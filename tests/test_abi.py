@@ -49,6 +49,7 @@ def test_version():
 
 
 FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: every call below fails on the host
+FAKE2 = ctypes.c_void_p(0x500000)  # a second fake buffer (new rows distinct from the caches)
 
 
 def decode(L, **kw):
@@ -455,3 +456,51 @@ def test_gather_read_rejects_bad_arguments():
     assert call(sink=None) == -1
     assert call(v=ctypes.c_void_p(0x100008)) == -5
     assert b"gather_read" in lib.pkv_last_error()
+
+
+def test_varlen_append_rejects():
+    lib = _lib().lib()
+
+    def va(**kw):
+        a = dict(out=FAKE, lse=None, q=FAKE, kn=FAKE2, vn=FAKE2, cu=FAKE, lens=FAKE, k=FAKE, v=FAKE,
+                 t=FAKE, B=2, T=8, maxq=4, mbs=4, hq=4, hkv=1, d=64, bs=16, nb=32, scale=0.125,
+                 causal=1, window=0, dtype=1, slots=None)
+        a.update(kw)
+        return lib.pkv_paged_attn_varlen_append(a["out"], a["lse"], a["q"], a["kn"], a["vn"], a["cu"],
+                                                a["lens"], a["k"], a["v"], a["t"], a["B"], a["T"],
+                                                a["maxq"], a["mbs"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                                a["nb"], a["scale"], a["causal"], a["window"],
+                                                a["dtype"], a["slots"], None)
+    assert va(kn=None) == -1
+    assert va(vn=None) == -1
+    assert va(kn=ctypes.c_void_p(0x200008)) == -5
+    assert va(kn=FAKE) == -2                  # the new rows are the K cache
+    assert va(dtype=4) == -3
+    assert va(window=-1) == -2
+    assert va(bs=3) == -4
+    assert va(B=0, out=None, q=None, kn=None, vn=None) == 0
+
+
+def test_decode_mtp_append_rejects():
+    lib = _lib().lib()
+    kc, vc = ctypes.c_void_p(0x300000), ctypes.c_void_p(0x400000)
+
+    def ma(**kw):
+        a = dict(out=FAKE, lse=None, q=FAKE, kn=FAKE2, vn=FAKE2, k=kc, v=vc, table=FAKE, lens=FAKE,
+                 B=4, qn=2, mbs=64, maxlen=1024, hq=32, hkv=8, d=128, bs=16, nb=256, scale=0.088,
+                 dtype=1, window=0, stages=3, ws=FAKE, wsb=1 << 30, slots=None)
+        a.update(kw)
+        return lib.pkv_paged_attn_decode_mtp_append(a["out"], a["lse"], a["q"], a["kn"], a["vn"],
+                                                    a["k"], a["v"], a["table"], a["lens"], a["B"],
+                                                    a["qn"], a["mbs"], a["maxlen"], a["hq"], a["hkv"],
+                                                    a["d"], a["bs"], a["nb"], a["scale"], a["dtype"],
+                                                    a["window"], a["stages"], a["ws"], a["wsb"],
+                                                    a["slots"], None)
+    assert ma(kn=None) == -1
+    assert ma(vn=None) == -1
+    assert ma(kn=ctypes.c_void_p(0x200008)) == -5
+    assert ma(v=kc) == -2                     # one pool for K and V
+    assert ma(stages=0) == -2
+    assert ma(qn=5) == -4                     # 20 columns
+    assert ma(dtype=0) == -4
+    assert ma(out=None) == -1
